@@ -1,0 +1,160 @@
+"""Python access to the CPU oracle (liboracle.so).  TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may
+import this package.  The HIP library neither imports nor links it.
+
+The oracle computes C = A*B for CSR inputs by Gustavson's row-wise method
+with a per-thread dense accumulator (gMAGNUS page, §II-B, Eq. 1, Algorithm 1)
+and returns, per entry, the Neumaier-compensated fp64 value, the sum of the
+absolute values of its terms and the number of terms.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C, OpenMP, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        vp = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.oracle_row_products.restype = i64
+        lib.oracle_row_products.argtypes = [i64, i64, vp, vp, vp, vp]
+        lib.oracle_symbolic.restype = ctypes.c_int
+        lib.oracle_symbolic.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_int]
+        lib.oracle_numeric.restype = ctypes.c_int
+        lib.oracle_numeric.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                       vp, vp, vp, vp, vp, ctypes.c_int]
+        lib.oracle_prune_colnorm.restype = i64
+        lib.oracle_prune_colnorm.argtypes = [i64, i64, vp, vp, vp, ctypes.c_float, vp,
+                                             vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+@dataclass
+class OracleResult:
+    row_ptr: np.ndarray   # int64, local to the row range (row_ptr[0] == 0)
+    col: np.ndarray       # int32
+    val: np.ndarray       # float64 (compensated sum)
+    mag: np.ndarray       # float64, sum of |terms|
+    terms: np.ndarray     # int32, number of products summed
+    r0: int
+    r1: int
+
+
+def row_products(A, B, r0: int = 0, r1: int | None = None) -> np.ndarray:
+    """Per-row intermediate-product counts P_i of A*B (int64)."""
+    lib = _load()
+    r1 = A.m if r1 is None else r1
+    arp, acol, brp = _c(A.row_ptr, np.int32), _c(A.col, np.int32), _c(B.row_ptr, np.int32)
+    out = np.zeros(r1 - r0, dtype=np.int64)
+    lib.oracle_row_products(r0, r1, _p(arp), _p(acol), _p(brp), _p(out))
+    return out
+
+
+def symbolic(A, B, r0: int = 0, r1: int | None = None, nthreads: int = 0) -> np.ndarray:
+    """nnz of each row of A*B in [r0, r1) (int64)."""
+    lib = _load()
+    r1 = A.m if r1 is None else r1
+    assert A.n == B.m
+    arp, acol = _c(A.row_ptr, np.int32), _c(A.col, np.int32)
+    brp, bcol = _c(B.row_ptr, np.int32), _c(B.col, np.int32)
+    cnt = np.zeros(r1 - r0, dtype=np.int64)
+    rc = lib.oracle_symbolic(r0, r1, B.n, _p(arp), _p(acol), _p(brp), _p(bcol), _p(cnt), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle_symbolic failed (%d)" % rc)
+    return cnt
+
+
+def spgemm(A, B, r0: int = 0, r1: int | None = None, nthreads: int = 0,
+           rows: np.ndarray | None = None) -> OracleResult:
+    """C = A*B on rows [r0, r1) of A (or on the listed rows, in that order)."""
+    lib = _load()
+    assert A.n == B.m
+    f32 = A.val.dtype == np.float32
+    assert B.val.dtype == A.val.dtype
+    vdt = np.float32 if f32 else np.float64
+    arp, acol, aval = _c(A.row_ptr, np.int32), _c(A.col, np.int32), _c(A.val, vdt)
+    brp, bcol, bval = _c(B.row_ptr, np.int32), _c(B.col, np.int32), _c(B.val, vdt)
+    if rows is not None:
+        # Build a row-gathered copy of A so that the listed rows become rows
+        # [0, len(rows)) of a smaller matrix; the arithmetic is unchanged.
+        rows = np.asarray(rows, dtype=np.int64)
+        starts = arp[rows].astype(np.int64)
+        lens = arp[rows + 1].astype(np.int64) - starts
+        rp = np.zeros(rows.shape[0] + 1, dtype=np.int64)
+        np.cumsum(lens, out=rp[1:])
+        idx = np.repeat(starts - rp[:-1], lens) + np.arange(int(rp[-1]), dtype=np.int64)
+        arp, acol, aval = _c(rp, np.int32), _c(acol[idx], np.int32), _c(aval[idx], vdt)
+        r0, r1 = 0, rows.shape[0]
+    r1 = (arp.shape[0] - 1) if r1 is None else r1
+    cnt = np.zeros(r1 - r0, dtype=np.int64)
+    rc = lib.oracle_symbolic(r0, r1, B.n, _p(arp), _p(acol), _p(brp), _p(bcol), _p(cnt), nthreads)
+    if rc != 0:
+        raise MemoryError("oracle_symbolic failed (%d)" % rc)
+    crp = np.zeros(r1 - r0 + 1, dtype=np.int64)
+    np.cumsum(cnt, out=crp[1:])
+    nnz = int(crp[-1])
+    col = np.empty(nnz, dtype=np.int32)
+    val = np.empty(nnz, dtype=np.float64)
+    mag = np.empty(nnz, dtype=np.float64)
+    terms = np.empty(nnz, dtype=np.int32)
+    rc = lib.oracle_numeric(r0, r1, B.n, _p(arp), _p(acol), _p(aval), _p(brp), _p(bcol),
+                            _p(bval), 1 if f32 else 0, _p(crp), _p(col), _p(val), _p(mag),
+                            _p(terms), nthreads)
+    if rc != 0:
+        raise RuntimeError("oracle_numeric failed (%d)" % rc)
+    return OracleResult(crp, col, val, mag, terms, r0, r1)
+
+
+def prune_colnorm(m: int, n: int, row_ptr, col, val, threshold: float = 1e-4,
+                  keep: np.ndarray | None = None):
+    """Markov-clustering prune (keep c >= threshold, compared in fp32) and
+    column renormalisation (divide by the fp64 sum of the kept column).
+    Returns (row_ptr int64, col int32, val float64)."""
+    lib = _load()
+    rp, cc, vv = _c(row_ptr, np.int64), _c(col, np.int32), _c(val, np.float64)
+    kk = None if keep is None else _c(keep, np.int8)
+    nnz = cc.shape[0]
+    orp = np.zeros(m + 1, dtype=np.int64)
+    oc = np.empty(nnz, dtype=np.int32)
+    ov = np.empty(nnz, dtype=np.float64)
+    w = lib.oracle_prune_colnorm(m, n, _p(rp), _p(cc), _p(vv), ctypes.c_float(threshold),
+                                 _p(kk), _p(orp), _p(oc), _p(ov))
+    if w < 0:
+        raise MemoryError("oracle_prune_colnorm failed")
+    return orp, oc[:w].copy(), ov[:w].copy()

@@ -1,0 +1,193 @@
+/*
+ * CPU oracle for C = A*B on CSR matrices.  TEST INFRASTRUCTURE ONLY: see
+ * oracle.h for the contract and for who may call it.
+ *
+ * Method: Gustavson's row-wise formulation (gMAGNUS page, §II-B, Eq. 1 and
+ * Algorithm 1; Ocean page, §2): row i of C is the sum of the rows B[k,:]
+ * scaled by A[i,k].  Each thread owns a dense accumulator over all columns of
+ * C, a row stamp per column telling whether the column was touched by the
+ * current row, and a list of touched columns, which is sorted before the row
+ * is written (SortAndWrite).  Nothing here is blocked, fused or reordered
+ * beyond that: products are visited in the stored order of A[i,:] and then of
+ * B[k,:].
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC oracle.c
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <omp.h>
+#include <stdlib.h>
+#include <string.h>
+
+int64_t oracle_row_products(int64_t r0, int64_t r1, const int32_t *a_rp,
+                                 const int32_t *a_col, const int32_t *b_rp,
+                                 int64_t *P) {
+  int64_t total = 0;
+  for (int64_t i = r0; i < r1; ++i) {
+    int64_t p = 0;
+    for (int64_t j = a_rp[i]; j < a_rp[i + 1]; ++j) {
+      int32_t k = a_col[j];
+      p += (int64_t)b_rp[k + 1] - (int64_t)b_rp[k];
+    }
+    P[i - r0] = p;
+    total += p;
+  }
+  return total;
+}
+
+int oracle_symbolic(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
+                    const int32_t *a_col, const int32_t *b_rp,
+                    const int32_t *b_col, int64_t *cnt, int nthreads) {
+  int failed = 0;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+  {
+    int64_t *mark = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+    if (!mark) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+      for (int64_t c = 0; c < n; ++c) mark[c] = -1;
+    }
+    /* Every thread takes part in the work-sharing loop, also one whose
+     * allocation failed, so that the loop's implicit barrier is reached. */
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t i = r0; i < r1; ++i) {
+      if (!mark) continue;
+      {
+        int64_t count = 0;
+        for (int64_t j = a_rp[i]; j < a_rp[i + 1]; ++j) {
+          int32_t k = a_col[j];
+          for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) {
+            int32_t c = b_col[b];
+            if (mark[c] != i) {
+              mark[c] = i;
+              ++count;
+            }
+          }
+        }
+        cnt[i - r0] = count;
+      }
+    }
+    free(mark);
+  }
+  return failed ? -1 : 0;
+}
+
+static int cmp_i32(const void *x, const void *y) {
+  int32_t a = *(const int32_t *)x, b = *(const int32_t *)y;
+  return (a > b) - (a < b);
+}
+
+int oracle_numeric(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
+                   const int32_t *a_col, const void *a_val, const int32_t *b_rp,
+                   const int32_t *b_col, const void *b_val, int val_is_f32,
+                   const int64_t *c_rp, int32_t *c_col, double *c_val,
+                   double *c_mag, int32_t *c_terms, int nthreads) {
+  int status = 0;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const double *ad = (const double *)a_val, *bd = (const double *)b_val;
+  const float *af = (const float *)a_val, *bf = (const float *)b_val;
+#pragma omp parallel num_threads(nthreads)
+  {
+    size_t nn = (size_t)(n > 0 ? n : 1);
+    double *acc = (double *)malloc(sizeof(double) * nn);  /* running sum    */
+    double *cmp = (double *)malloc(sizeof(double) * nn);  /* compensation   */
+    double *mag = (double *)malloc(sizeof(double) * nn);  /* sum of |terms| */
+    int32_t *terms = (int32_t *)malloc(sizeof(int32_t) * nn);
+    int64_t *mark = (int64_t *)malloc(sizeof(int64_t) * nn);
+    int32_t *touched = (int32_t *)malloc(sizeof(int32_t) * nn);
+    int ok = acc && cmp && mag && terms && mark && touched;
+    if (!ok) {
+#pragma omp critical
+      status = -1;
+    } else {
+      for (int64_t c = 0; c < n; ++c) mark[c] = -1;
+    }
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t i = r0; i < r1; ++i) {
+      if (!ok) continue;
+      {
+        int64_t nt = 0;
+        for (int64_t j = a_rp[i]; j < a_rp[i + 1]; ++j) {
+          int32_t k = a_col[j];
+          double a = val_is_f32 ? (double)af[j] : ad[j];
+          for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) {
+            int32_t c = b_col[b];
+            double p = a * (val_is_f32 ? (double)bf[b] : bd[b]);
+            if (mark[c] != i) {
+              mark[c] = i;
+              acc[c] = 0.0;
+              cmp[c] = 0.0;
+              mag[c] = 0.0;
+              terms[c] = 0;
+              touched[nt++] = c;
+            }
+            /* Neumaier's compensated addition of p into (acc, cmp). */
+            double s = acc[c];
+            double t = s + p;
+            if (fabs(s) >= fabs(p))
+              cmp[c] += (s - t) + p;
+            else
+              cmp[c] += (p - t) + s;
+            acc[c] = t;
+            mag[c] += fabs(p);
+            terms[c] += 1;
+          }
+        }
+        int64_t base = c_rp[i - r0];
+        if (c_rp[i - r0 + 1] - base != nt) {
+#pragma omp critical
+          status = -2;
+          continue;
+        }
+        qsort(touched, (size_t)nt, sizeof(int32_t), cmp_i32);
+        for (int64_t e = 0; e < nt; ++e) {
+          int32_t c = touched[e];
+          c_col[base + e] = c;
+          c_val[base + e] = acc[c] + cmp[c];
+          if (c_mag) c_mag[base + e] = mag[c];
+          if (c_terms) c_terms[base + e] = terms[c];
+        }
+      }
+    }
+    free(acc);
+    free(cmp);
+    free(mag);
+    free(terms);
+    free(mark);
+    free(touched);
+  }
+  return status;
+}
+
+int64_t oracle_prune_colnorm(int64_t m, int64_t n, const int64_t *c_rp,
+                             const int32_t *c_col, const double *c_val,
+                             float threshold, const int8_t *keep,
+                             int64_t *out_rp, int32_t *out_col,
+                             double *out_val) {
+  double *colsum = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+  if (!colsum) return -1;
+  int64_t w = 0;
+  out_rp[0] = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t e = c_rp[i]; e < c_rp[i + 1]; ++e) {
+      int k;
+      if (keep && keep[e] >= 0)
+        k = keep[e];
+      else
+        k = ((float)c_val[e] >= threshold);
+      if (k) {
+        out_col[w] = c_col[e];
+        out_val[w] = c_val[e];
+        colsum[c_col[e]] += c_val[e];
+        ++w;
+      }
+    }
+    out_rp[i + 1] = w;
+  }
+  for (int64_t e = 0; e < w; ++e) out_val[e] = out_val[e] / colsum[out_col[e]];
+  free(colsum);
+  return w;
+}

@@ -1,0 +1,71 @@
+/*
+ * CPU oracle for sparse general matrix-matrix multiplication, C = A*B, CSR.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this library; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no source with the HIP library.
+ *
+ * What it computes (gMAGNUS page, §II-B, Eq. 1 and Algorithm 1):
+ *   C[i, j] = sum over stored pairs A[i,k], B[k,j] of A[i,k] * B[k,j].
+ * An entry (i, j) exists iff at least one stored pair meets (structural
+ * definition: a computed 0.0 is kept).  Columns of each row of C are emitted
+ * sorted ascending without duplicates (the SortAndWrite step of Algorithm 1).
+ *
+ * Arithmetic: each product is rounded once to fp64 (inputs in fp32 are
+ * widened first, so their products are exact), then summed in fp64 with
+ * Neumaier compensation, so the returned value is close to the exact sum.
+ * The library is compiled with -ffp-contract=off.
+ *
+ * Index conventions: row pointers of A and B are int32, column indices int32.
+ * Rows are processed in [r0, r1); per-row outputs are indexed i - r0.
+ */
+#ifndef SPGEMM_ORACLE_H
+#define SPGEMM_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* P[i - r0] = number of intermediate products of row i, the sum over k in
+ * A[i,:] of nnz(B[k,:]) (stored zeros counted).  Returns the total. */
+int64_t oracle_row_products(int64_t r0, int64_t r1, const int32_t *a_rp,
+                            const int32_t *a_col, const int32_t *b_rp,
+                            int64_t *P);
+
+/* cnt[i - r0] = nnz(C[i,:]) = |union over k in A[i,:] of cols(B[k,:])|.
+ * n = number of columns of B.  Returns 0, or -1 on allocation failure. */
+int oracle_symbolic(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
+                    const int32_t *a_col, const int32_t *b_rp,
+                    const int32_t *b_col, int64_t *cnt, int nthreads);
+
+/* Fills rows [r0, r1) of C at the local offsets c_rp[0..r1-r0] (c_rp[0] may
+ * be nonzero; row i occupies [c_rp[i-r0], c_rp[i-r0+1]) ).
+ * val_is_f32: 0 -> a_val/b_val are double, 1 -> float.
+ * c_val: compensated fp64 value.  c_mag (optional): sum of |A[i,k]*B[k,j]|,
+ * the natural scale for a summation-order tolerance.  c_terms (optional):
+ * number of products summed into the entry.
+ * Returns 0, -1 on allocation failure, -2 if a row's size disagrees with c_rp.
+ */
+int oracle_numeric(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
+                   const int32_t *a_col, const void *a_val, const int32_t *b_rp,
+                   const int32_t *b_col, const void *b_val, int val_is_f32,
+                   const int64_t *c_rp, int32_t *c_col, double *c_val,
+                   double *c_mag, int32_t *c_terms, int nthreads);
+
+/* One Markov-clustering prune + column renormalisation (Trident page, §5.7):
+ * keep entry (i,j) iff (float)c_val >= threshold (compared in fp32; keep[]
+ * overrides the decision where keep[e] is 0 or 1, and is ignored where it is
+ * -1 or keep == NULL); then divide every kept entry by the fp64 sum of the
+ * kept entries of its column.  Output arrays are sized by the caller at
+ * nnz(C); out_rp has m+1 entries.  Returns the number of kept entries. */
+int64_t oracle_prune_colnorm(int64_t m, int64_t n, const int64_t *c_rp,
+                             const int32_t *c_col, const double *c_val,
+                             float threshold, const int8_t *keep,
+                             int64_t *out_rp, int32_t *out_col,
+                             double *out_val);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
