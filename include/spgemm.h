@@ -1,0 +1,186 @@
+/*
+ * spgemm.h -- C ABI of libspgemm.so: sparse general matrix-matrix product
+ * C = A * B on CSR matrices, for one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * Method (gMAGNUS page, "gMAGNUS: Fast SpGEMM on GPUs for Irregular Matrices
+ * via Hierarchical Multisplit", §III, Algorithm 3):
+ *   - rows whose intermediate product fits an on-chip accumulator ("light"
+ *     rows, §II-B, §III-A) are computed row by row (Gustavson, Eq. 1) with LDS
+ *     hash accumulators, binned by size (§III-E);
+ *   - "heavy" rows are expanded by an outer product into an intermediate
+ *     matrix C-hat (§III-B, Eq. 2), split by a hierarchical multisplit into
+ *     column-range chunks (§III-C), and every chunk is accumulated entirely in
+ *     LDS (dense accumulator for heavy chunks, hash for light ones, §III-E);
+ *   - chunk count and levels come from C's column count and the LDS size
+ *     (§III-D, Eq. 4-7).
+ * The two-phase interface (symbolic computes C.rowPtr and nnz(C), numeric
+ * fills C.col and C.val) follows §II-B of the same page and the
+ * symbolic/numeric split described in §2 of the Ocean page.
+ *
+ * Conventions shared by every entry point
+ *   - All matrix arrays are DEVICE pointers on the current HIP device; every
+ *     size and count is a host integer.  `stream` is a hipStream_t passed as
+ *     void* (NULL = the legacy default stream).
+ *   - CSR: row_ptr (rows+1 entries, int32), col (nnz, int32), val (nnz, float
+ *     or double per `dtype`).  Inputs must be canonical: row_ptr[0] == 0,
+ *     row_ptr non-decreasing, 0 <= col < ncols, columns strictly increasing
+ *     within a row.  opts->validate checks this on the device.
+ *   - Output C is canonical CSR; an entry exists iff at least one stored
+ *     pair A[i,k], B[k,j] exists (a computed 0.0 is kept).
+ *   - Nothing is thrown across the ABI; every call returns spgemm_status.
+ *   - Calls on one plan are not thread-safe; distinct plans are independent.
+ */
+#ifndef SPGEMM_H
+#define SPGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spgemm_status {
+  SPGEMM_OK = 0,
+  SPGEMM_ERR_INVALID_ARG = -1,    /* null pointer, negative size, bad dtype  */
+  SPGEMM_ERR_INVALID_CSR = -2,    /* opts->validate found a non-canonical input */
+  SPGEMM_ERR_INDEX_OVERFLOW = -3, /* int32 C.row_ptr requested, nnz(C) > INT32_MAX,
+                                     or a size exceeds the int32 index range */
+  SPGEMM_ERR_OOM = -4,            /* device allocation failed; C untouched   */
+  SPGEMM_ERR_HIP = -5,            /* HIP runtime error; see spgemm_last_error */
+  SPGEMM_ERR_STATE = -6,          /* call order violated or plan in error state */
+  SPGEMM_ERR_INTERNAL = -7        /* a device-side capacity check tripped    */
+} spgemm_status;
+
+typedef enum spgemm_dtype { SPGEMM_F32 = 0, SPGEMM_F64 = 1 } spgemm_dtype;
+
+/* Optional device allocator: return a device pointer of at least `bytes`
+ * usable in stream order on `stream`, or NULL on failure.  With alloc == NULL
+ * the library uses hipMallocAsync / hipFreeAsync on the plan's stream. */
+typedef void *(*spgemm_alloc_fn)(size_t bytes, void *stream, void *ctx);
+typedef void (*spgemm_free_fn)(void *ptr, void *stream, void *ctx);
+
+/* Tuning and override knobs.  Zero-initialise, then set what you need; a zero
+ * field means "automatic". */
+typedef struct spgemm_options {
+  int64_t lds_budget;           /* s_LM in bytes (gMAGNUS §III-D); 0 = LDS per
+                                   work group of the device (160 KiB on gfx950) */
+  int64_t heavy_threshold;      /* tau; 0 = derived from s_LM (Eq. 4 reading)   */
+  int64_t dense_width;          /* final chunk width W (power of two); 0 = derived */
+  int64_t mem_budget;           /* bytes for the heavy intermediate; 0 = all free */
+  int32_t max_chunks_per_level; /* n_chunksMax (power of two >= 2); 0 = 32       */
+  int32_t rowptr64;             /* 1: C.row_ptr is int64, else int32            */
+  int32_t validate;             /* 1: check A and B are canonical CSR           */
+  int32_t single_stream;        /* 1: light and heavy work on the caller's stream */
+  spgemm_alloc_fn alloc;        /* optional allocator (see above)               */
+  spgemm_free_fn free;
+  void *alloc_ctx;
+  int64_t reserved[8];
+} spgemm_options;
+
+/* Parameters chosen by GetMagnusParams (gMAGNUS §III-D, Eq. 4-7). */
+typedef struct spgemm_params {
+  int64_t tau;              /* heavy threshold: a row/chunk is heavy iff its
+                               element count exceeds tau                      */
+  int64_t n_dense;          /* max dense accumulator width for numeric        */
+  int64_t dense_width;      /* W = floor_pow2(n_dense): final chunk width     */
+  int64_t chunks_required;  /* next_pow2(ceil(ncols / W)), at least 1         */
+  int32_t chunks_max;       /* n_chunksMax                                    */
+  int32_t levels;           /* multisplit levels (0 when chunks_required == 1) */
+  int32_t v_chunks[8];      /* chunks per row at each level                   */
+  int64_t level_width[8];   /* column width of a chunk after each level       */
+} spgemm_params;
+
+typedef struct spgemm_stats {
+  int64_t products;           /* P = sum_i sum_{k in A_i} nnz(B_k); flops = 2P */
+  int64_t max_row_products;
+  int64_t light_rows;         /* rows with 0 < P_i <= tau                      */
+  int64_t heavy_rows;         /* rows with P_i > tau                           */
+  int64_t heavy_products;     /* P_h = nnz(C-hat)                              */
+  int64_t heavy_a_nnz;        /* nnz of A restricted to heavy rows             */
+  int64_t nnz_c;
+  spgemm_params params;
+  int64_t level_elems[8];     /* elements entering each multisplit level       */
+  int64_t final_chunks;       /* non-empty chunks accumulated                  */
+  int64_t dense_chunks;       /* of which in a dense LDS accumulator           */
+  int64_t lds_hash_products;  /* products summed in LDS hash tables            */
+  int64_t lds_dense_products; /* products summed in LDS dense accumulators     */
+  int64_t global_products;    /* products summed in global memory (always 0)   */
+  int64_t batches;            /* heavy-row batches                             */
+  double ms_plan, ms_symbolic, ms_numeric; /* host wall time of each call      */
+} spgemm_stats;
+
+typedef struct spgemm_plan_s *spgemm_plan_t;
+typedef struct spgemm_prune_s *spgemm_prune_t;
+
+/* GetMagnusParams on the host; needs no GPU.  (gMAGNUS §III-D, Eq. 4-7.)
+ * ncols = number of columns of C; lds_bytes = s_LM; val_bytes / col_bytes =
+ * s_C.val / s_C.col; max_chunks_per_level = n_chunksMax (0 = 32);
+ * dense_width = W override (0 = derived).  Where the printed formulas are
+ * ambiguous, the readings taken are stated beside the code (params.cpp).
+ * Errors: INVALID_ARG for non-positive sizes or a non-power-of-two
+ * max_chunks_per_level / dense_width. */
+spgemm_status spgemm_compute_params(int64_t ncols, int64_t lds_bytes,
+                                    int32_t val_bytes, int32_t col_bytes,
+                                    int32_t max_chunks_per_level,
+                                    int64_t dense_width, spgemm_params *out);
+
+/* Plan C = A * B (A: m x k, B: k x n).  Validates arguments, queries the
+ * device, computes the parameters, counts intermediate products per row,
+ * splits rows into light and heavy and bins them (gMAGNUS Algorithm 3,
+ * setup phase).  Blocks once to read back the heavy count.  A and B are
+ * borrowed until spgemm_destroy and must not change meanwhile.
+ * Errors: INVALID_ARG, INDEX_OVERFLOW (nnz > INT32_MAX in an input),
+ * INVALID_CSR (with validate), OOM, HIP.  On error *out is NULL. */
+spgemm_status spgemm_plan(spgemm_plan_t *out, int64_t m, int64_t k, int64_t n,
+                          const int32_t *dA_row_ptr, const int32_t *dA_col,
+                          const void *dA_val, int64_t nnzA,
+                          const int32_t *dB_row_ptr, const int32_t *dB_col,
+                          const void *dB_val, int64_t nnzB, spgemm_dtype dtype,
+                          const spgemm_options *opts, void *stream);
+
+/* Symbolic phase: writes C.row_ptr (m+1 entries, int32, or int64 with
+ * opts->rowptr64) into the caller's device buffer and returns nnz(C) on the
+ * host (blocks once).  Heavy rows are expanded, multisplit and counted here;
+ * the reordered intermediate is kept for numeric.
+ * Errors: STATE (not planned, or already run), INDEX_OVERFLOW, OOM, HIP. */
+spgemm_status spgemm_symbolic(spgemm_plan_t p, void *dC_row_ptr,
+                              int64_t *nnzC);
+
+/* Numeric phase: fills C.col (nnz(C) int32) and C.val (nnz(C), dtype),
+ * columns sorted within each row.  Asynchronous on the plan's stream.
+ * Errors: STATE (symbolic not run), HIP. */
+spgemm_status spgemm_numeric(spgemm_plan_t p, int32_t *dC_col, void *dC_val);
+
+spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats *out);
+
+/* Frees the plan's workspace (stream-ordered on the plan's stream). */
+void spgemm_destroy(spgemm_plan_t p);
+
+const char *spgemm_status_string(spgemm_status s);
+/* Last error message of a plan, or of the calling thread when p == NULL. */
+const char *spgemm_last_error(spgemm_plan_t p);
+
+/* One Markov-clustering prune + column renormalisation of C (Trident page,
+ * "Communication-Avoiding SpGEMM via Trident Partitioning", §5.7): keep
+ * entries with C[i,j] >= threshold (compared in the value type), then divide
+ * each kept entry by the fp64 sum of its column's kept entries, rounding once
+ * to the value type.
+ * Count call: computes the kept-entry row pointers into dOut_row_ptr (m+1;
+ * int64 if out_rowptr64 else int32), the column sums, and returns the kept
+ * count on the host (blocks once).  Fill call: writes dOut_col / dOut_val.
+ * C is read through dC_row_ptr (int64 if c_rowptr64 else int32).
+ * Errors: INVALID_ARG, INDEX_OVERFLOW, OOM, HIP, STATE. */
+spgemm_status spgemm_prune_colnorm_count(
+    spgemm_prune_t *out, int64_t m, int64_t n, const void *dC_row_ptr,
+    int32_t c_rowptr64, const int32_t *dC_col, const void *dC_val,
+    spgemm_dtype dtype, double threshold, void *dOut_row_ptr,
+    int32_t out_rowptr64, int64_t *nnzOut, void *stream);
+spgemm_status spgemm_prune_colnorm_fill(spgemm_prune_t p, int32_t *dOut_col,
+                                        void *dOut_val);
+void spgemm_prune_destroy(spgemm_prune_t p);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPGEMM_H */

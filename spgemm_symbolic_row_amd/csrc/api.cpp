@@ -1,0 +1,831 @@
+// Host orchestration of the C ABI (include/spgemm.h): the gMAGNUS end-to-end
+// schedule (gMAGNUS page, §III-A, Algorithm 3) on one GPU.
+//
+//   plan      setup phase: validation, parameters (§III-D), intermediate
+//             products per row (InterOffsets), light/heavy split and size
+//             bins; one host sync to learn the bin sizes.
+//   symbolic  light rows: LDS hash symbolic per bin (light stream);
+//             heavy rows: masked CSR->CSC, outer product, multisplit levels,
+//             chunk symbolic (heavy stream); then C.rowPtr by a scan and one
+//             sync for nnz(C).
+//   numeric   light rows and heavy chunks accumulated in LDS, written sorted.
+//
+// Light and heavy work run on two internal streams forked from, and joined
+// back into, the caller's stream with events.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/spgemm.h"
+#include "internal.hpp"
+
+using namespace sg;
+
+namespace {
+
+struct Error {
+  spgemm_status st;
+  std::string msg;
+};
+
+thread_local std::string g_thread_error;
+
+#define HIP_CHECK(expr)                                                            \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      throw Error{SPGEMM_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)}; \
+  } while (0)
+
+inline void check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) throw Error{SPGEMM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e)};
+}
+
+int64_t next_pow2(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p *= 2;
+  return p;
+}
+int log2_exact(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+double now_ms() {
+  return std::chrono::duration<double, std::milli>(
+             std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
+int tpr_for(int64_t cap) {
+  if (cap <= 256) return 64;
+  if (cap <= 512) return 128;
+  if (cap <= 1024) return 256;
+  if (cap <= 2048) return 512;
+  return 1024;
+}
+
+// Size classes of the LDS hash accumulators: caps 32, 64, ... below tau, then
+// tau itself.  Symbolic tables hold keys only (4 bytes a slot); numeric
+// tables hold (key, value) pairs and must also fit the sort of
+// next_pow2(cap) entries.  Both lists share their caps, so a bin index found
+// from an element count is valid in either.
+void make_bins(int64_t tau, int64_t lds, int val_bytes, std::vector<BinCfg>* sym,
+               std::vector<BinCfg>* num) {
+  std::vector<int64_t> caps;
+  for (int64_t c = 32; c < tau; c *= 2) caps.push_back(c);
+  caps.push_back(tau);
+  for (int64_t cap : caps) {
+    const int tpr = tpr_for(cap);
+    const int rpb = tpr >= 256 ? 1 : 256 / tpr;
+    BinCfg s{};
+    s.cap = (int32_t)cap;
+    s.tpr = tpr;
+    s.rpb = rpb;
+    s.T = (int32_t)std::max<int64_t>(next_pow2(2 * cap), tpr);
+    s.spt = s.T / tpr;
+    s.N = (int32_t)next_pow2(cap);
+    s.lds = (size_t)rpb * s.T * 4 + rpb * 4;
+    if ((int64_t)s.lds > lds)
+      throw Error{SPGEMM_ERR_INVALID_ARG, "symbolic hash table does not fit the LDS budget"};
+    sym->push_back(s);
+
+    BinCfg n = s;
+    const int slot = 4 + val_bytes;
+    const int64_t N = next_pow2(cap);
+    int64_t T = std::max<int64_t>(next_pow2(2 * cap), tpr);
+    const int64_t extra = (int64_t)(tpr * rpb / 64) * 4;
+    while (T > tpr && (int64_t)rpb * T * slot + extra > lds) T -= tpr;
+    if (T < N || T <= cap || T / tpr > 24)
+      throw Error{SPGEMM_ERR_INVALID_ARG, "numeric hash table does not fit the LDS budget"};
+    n.T = (int32_t)T;
+    n.spt = (int32_t)(T / tpr);
+    n.N = (int32_t)N;
+    n.lds = (size_t)rpb * T * slot + extra;
+    num->push_back(n);
+  }
+}
+
+}  // namespace
+
+struct spgemm_plan_s {
+  // inputs
+  int64_t m = 0, k = 0, n = 0, nnzA = 0, nnzB = 0;
+  const int32_t *arp = nullptr, *acol = nullptr, *brp = nullptr, *bcol = nullptr;
+  const void *aval = nullptr, *bval = nullptr;
+  bool f64 = true;
+  spgemm_options opts{};
+  hipStream_t stream = nullptr, sl = nullptr, sh = nullptr;
+  hipEvent_t evFork = nullptr, evL = nullptr, evH = nullptr;
+  int device = 0;
+  int64_t lds = 0, tau = 0;
+  spgemm_params params{};
+  int state = 0;  // 0 planned, 1 symbolic done, 2 numeric done, -1 failed
+  std::string err;
+  std::vector<void*> allocs;
+  std::vector<BinCfg> symBins, numBins;
+  int NS = 0;  // number of hash bins
+  // device arrays
+  int32_t *dSymCaps = nullptr;
+  int64_t *rowP = nullptr, *cnt = nullptr, *stats = nullptr, *cRowOff = nullptr, *scanTmp = nullptr;
+  int32_t *scanA = nullptr, *rowOrder = nullptr, *numOrder = nullptr, *errWord = nullptr;
+  int32_t *binCnt = nullptr, *binFill = nullptr, *binStart = nullptr;
+  uint8_t *rowBin = nullptr, *numKey = nullptr;
+  // pinned host mirrors
+  int64_t* hStats = nullptr;   // kNumStats + 8
+  int32_t* hBins = nullptr;    // 128
+  // host copies
+  std::vector<int32_t> rowBinStart, numBinStart, fcBinStart;
+  // heavy path
+  int64_t h = 0, Ph = 0, nAh = 0;
+  const int32_t* xheavy = nullptr;
+  int32_t *bufCol[2] = {nullptr, nullptr};
+  void* bufVal[2] = {nullptr, nullptr};
+  int64_t nfc = 0, lastFirst = 0, nreq = 1;
+  int64_t* fcOff = nullptr;
+  int32_t *fcCnt = nullptr, *fcRow = nullptr, *fcSlot = nullptr, *fcOrder = nullptr;
+  int8_t* fcBuf = nullptr;
+  int32_t* slotNnz = nullptr;
+  int64_t* slotOff = nullptr;
+  int64_t nnzC = 0;
+  spgemm_stats st{};
+};
+
+namespace {
+
+void* plan_alloc(spgemm_plan_t p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) bytes = 16;
+  bytes = (bytes + 255) & ~size_t(255);
+  void* ptr = nullptr;
+  if (p->opts.alloc) {
+    ptr = p->opts.alloc(bytes, (void*)s, p->opts.alloc_ctx);
+  } else if (hipMallocAsync(&ptr, bytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    ptr = nullptr;
+  }
+  if (!ptr)
+    throw Error{SPGEMM_ERR_OOM, "device allocation of " + std::to_string(bytes) + " bytes failed"};
+  p->allocs.push_back(ptr);
+  return ptr;
+}
+template <typename T>
+T* alloc_n(spgemm_plan_t p, int64_t n, hipStream_t s) {
+  return (T*)plan_alloc(p, (size_t)std::max<int64_t>(n, 1) * sizeof(T), s);
+}
+
+void release(spgemm_plan_t p) {
+  for (void* ptr : p->allocs) {
+    if (p->opts.alloc) {
+      if (p->opts.free) p->opts.free(ptr, (void*)p->stream, p->opts.alloc_ctx);
+    } else {
+      (void)hipFreeAsync(ptr, p->stream);
+    }
+  }
+  p->allocs.clear();
+}
+
+void fork(spgemm_plan_t p) {
+  if (p->sl == p->stream) return;
+  HIP_CHECK(hipEventRecord(p->evFork, p->stream));
+  HIP_CHECK(hipStreamWaitEvent(p->sl, p->evFork, 0));
+  HIP_CHECK(hipStreamWaitEvent(p->sh, p->evFork, 0));
+}
+void join(spgemm_plan_t p) {
+  if (p->sl == p->stream) return;
+  HIP_CHECK(hipEventRecord(p->evL, p->sl));
+  HIP_CHECK(hipEventRecord(p->evH, p->sh));
+  HIP_CHECK(hipStreamWaitEvent(p->stream, p->evL, 0));
+  HIP_CHECK(hipStreamWaitEvent(p->stream, p->evH, 0));
+}
+
+void check_device_errors(spgemm_plan_t p, int32_t word) {
+  if (word & kErrCsr) throw Error{SPGEMM_ERR_INVALID_CSR, "input is not canonical CSR"};
+  if (word & kErrHashFull) throw Error{SPGEMM_ERR_INTERNAL, "an LDS hash table overflowed"};
+  if (word & kErrRowsPerBlock)
+    throw Error{SPGEMM_ERR_INTERNAL, "multisplit work group met more rows than sized for"};
+  if (word & kErrCountMismatch)
+    throw Error{SPGEMM_ERR_INTERNAL, "numeric and symbolic sizes disagree"};
+  (void)p;
+}
+
+int32_t read_err(spgemm_plan_t p, hipStream_t s) {
+  HIP_CHECK(hipMemcpyAsync(p->hBins + 120, p->errWord, 4, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  return p->hBins[120];
+}
+
+RowArgs row_args(spgemm_plan_t p) {
+  return RowArgs{p->arp, p->acol, p->aval, p->brp, p->bcol, p->bval, p->scanA, p->rowP};
+}
+
+// ------------------------------------------------------------------ plan
+void do_plan(spgemm_plan_t p) {
+  const double t0 = now_ms();
+  HIP_CHECK(hipGetDevice(&p->device));
+  int ldsDev = 0;
+  HIP_CHECK(hipDeviceGetAttribute(&ldsDev, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device));
+  p->lds = p->opts.lds_budget ? p->opts.lds_budget : ldsDev;
+  if (p->lds > ldsDev || p->lds < 4096)
+    throw Error{SPGEMM_ERR_INVALID_ARG, "lds_budget must lie in [4096, LDS per work group]"};
+  const int vb = p->f64 ? 8 : 4;
+  spgemm_status ps = spgemm_compute_params(p->n, p->lds, vb, 4, p->opts.max_chunks_per_level,
+                                           p->opts.dense_width, &p->params);
+  if (ps != SPGEMM_OK) throw Error{ps, "parameter selection failed"};
+  p->tau = p->params.tau;
+  if (p->opts.heavy_threshold) {
+    if (p->opts.heavy_threshold < 1 || p->opts.heavy_threshold > p->params.tau)
+      throw Error{SPGEMM_ERR_INVALID_ARG, "heavy_threshold must lie in [1, LDS-derived tau]"};
+    p->tau = p->opts.heavy_threshold;
+  }
+  if ((int64_t)dense_num_lds(p->f64, p->params.dense_width) > ldsDev ||
+      p->params.dense_width > 32768)
+    throw Error{SPGEMM_ERR_INVALID_ARG, "dense width does not fit the LDS"};
+  make_bins(p->tau, p->lds, vb, &p->symBins, &p->numBins);
+  p->NS = (int)p->symBins.size();
+  if (p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
+
+  static bool attrs = false;
+  if (!attrs) {
+    light_set_attributes();
+    heavy_set_attributes();
+    attrs = true;
+  }
+  if (!p->opts.alloc) {
+    // Keep freed workspace in the stream-ordered pool for the next product
+    // instead of returning it to the driver at every synchronisation.
+    static int poolDevice = -1;
+    if (poolDevice != p->device) {
+      hipMemPool_t pool;
+      if (hipDeviceGetDefaultMemPool(&pool, p->device) == hipSuccess) {
+        uint64_t thr = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+      }
+      (void)hipGetLastError();
+      poolDevice = p->device;
+    }
+  }
+
+  if (p->opts.single_stream) {
+    p->sl = p->sh = p->stream;
+  } else {
+    HIP_CHECK(hipStreamCreateWithFlags(&p->sl, hipStreamNonBlocking));
+    HIP_CHECK(hipStreamCreateWithFlags(&p->sh, hipStreamNonBlocking));
+    HIP_CHECK(hipEventCreateWithFlags(&p->evFork, hipEventDisableTiming));
+    HIP_CHECK(hipEventCreateWithFlags(&p->evL, hipEventDisableTiming));
+    HIP_CHECK(hipEventCreateWithFlags(&p->evH, hipEventDisableTiming));
+  }
+  HIP_CHECK(hipHostMalloc((void**)&p->hStats, sizeof(int64_t) * 32, hipHostMallocDefault));
+  HIP_CHECK(hipHostMalloc((void**)&p->hBins, sizeof(int32_t) * 128, hipHostMallocDefault));
+
+  hipStream_t s = p->stream;
+  const int64_t m = p->m;
+  p->errWord = alloc_n<int32_t>(p, 4, s);
+  p->stats = alloc_n<int64_t>(p, kNumStats, s);
+  launch_fill_i32(p->errWord, 0, 4, s);
+  launch_fill_i64(p->stats, 0, kNumStats, s);
+
+  if (p->opts.validate) {
+    launch_validate(p->m, p->k, p->nnzA, p->arp, p->acol, p->errWord, s);
+    launch_validate(p->k, p->n, p->nnzB, p->brp, p->bcol, p->errWord, s);
+    check_launch("validate");
+    check_device_errors(p, read_err(p, s));
+  }
+
+  std::vector<int32_t> caps(p->NS);
+  for (int b = 0; b < p->NS; ++b) caps[b] = p->symBins[b].cap;
+  p->dSymCaps = alloc_n<int32_t>(p, 64, s);
+  std::memcpy(p->hBins, caps.data(), sizeof(int32_t) * p->NS);
+  HIP_CHECK(hipMemcpyAsync(p->dSymCaps, p->hBins, sizeof(int32_t) * p->NS, hipMemcpyHostToDevice, s));
+  // The copy reads pinned memory that is rewritten below; wait for it.
+  HIP_CHECK(hipStreamSynchronize(s));
+
+  p->rowP = alloc_n<int64_t>(p, m, s);
+  p->cnt = alloc_n<int64_t>(p, m, s);
+  p->scanA = alloc_n<int32_t>(p, p->nnzA, s);
+  p->rowBin = alloc_n<uint8_t>(p, m, s);
+  p->rowOrder = alloc_n<int32_t>(p, m, s);
+  p->binCnt = alloc_n<int32_t>(p, 64, s);
+  p->binFill = alloc_n<int32_t>(p, 64, s);
+  p->binStart = alloc_n<int32_t>(p, 65, s);
+  launch_fill_i64(p->cnt, 0, m, s);
+  launch_row_info(m, p->arp, p->acol, p->brp, p->bcol, p->tau, p->dSymCaps, p->NS, p->rowP,
+                  p->scanA, p->rowBin, p->stats, s);
+  const int nkeys = p->NS + 2;  // 0 empty, 1..NS hash bins, NS+1 heavy
+  launch_bin_sort(p->rowBin, m, nkeys, p->binCnt, p->binFill, p->binStart, p->rowOrder, s);
+  check_launch("plan kernels");
+  HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (nkeys + 1), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  p->rowBinStart.assign(p->hBins, p->hBins + nkeys + 1);
+  p->st.products = p->hStats[kStatProducts];
+  p->st.heavy_products = p->Ph = p->hStats[kStatHeavyProducts];
+  p->st.heavy_a_nnz = p->nAh = p->hStats[kStatHeavyANnz];
+  p->st.max_row_products = p->hStats[kStatMaxRowProducts];
+  p->st.heavy_rows = p->h = p->hStats[kStatHeavyRows];
+  p->st.light_rows = p->hStats[kStatLightRows];
+  p->st.params = p->params;
+  p->st.params.tau = p->tau;
+  p->xheavy = p->rowOrder + p->rowBinStart[p->NS + 1];
+  p->nreq = p->params.chunks_required;
+  p->st.ms_plan = now_ms() - t0;
+}
+
+// -------------------------------------------------------------- symbolic
+void heavy_symbolic(spgemm_plan_t p) {
+  hipStream_t s = p->sh;
+  const int64_t h = p->h, Ph = p->Ph, nE = p->nAh;
+  const bool f64 = p->f64;
+  const size_t vb = f64 ? 8 : 4;
+  const int64_t W = p->params.dense_width;
+  int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(std::max<int64_t>({h, nE, p->k, 1}) + 1), s);
+
+  // C-hat row pointers: scan of the heavy rows' product counts.
+  int64_t* hP = alloc_n<int64_t>(p, h, s);
+  int64_t* chatRowPtr = alloc_n<int64_t>(p, h + 1, s);
+  launch_gather_i64(p->rowP, p->xheavy, h, hP, s);
+  launch_scan_i64(hP, h, chatRowPtr, tmp, s);
+
+  // Masked CSR -> CSC of A restricted to the heavy rows.
+  int32_t* colCnt = alloc_n<int32_t>(p, p->k, s);
+  int64_t* colPtr = alloc_n<int64_t>(p, p->k + 1, s);
+  int64_t* colFill = alloc_n<int64_t>(p, p->k, s);
+  int32_t* cscRow = alloc_n<int32_t>(p, nE, s);
+  int32_t* cscCol = alloc_n<int32_t>(p, nE, s);
+  void* cscVal = plan_alloc(p, std::max<int64_t>(nE, 1) * vb, s);
+  launch_fill_i32(colCnt, 0, p->k, s);
+  launch_csc_count(h, p->xheavy, p->arp, p->acol, colCnt, s);
+  launch_scan_i32(colCnt, p->k, colPtr, tmp, s);
+  launch_copy_i64(colFill, colPtr, p->k, s);
+  launch_csc_fill(h, p->xheavy, p->arp, p->acol, p->aval, f64, colFill, cscRow, cscCol, cscVal, s);
+
+  // Flattened element offsets of the CSC entries and their C-hat segments.
+  int64_t* nb = alloc_n<int64_t>(p, nE, s);
+  int64_t* entryOff = alloc_n<int64_t>(p, nE + 1, s);
+  int64_t* cursor = alloc_n<int64_t>(p, h, s);
+  int64_t* segBase = alloc_n<int64_t>(p, nE, s);
+  launch_entry_products(nE, cscCol, p->brp, nb, s);
+  launch_scan_i64(nb, nE, entryOff, tmp, s);
+  launch_copy_i64(cursor, chatRowPtr, h, s);
+  launch_seg_base(nE, cscRow, nb, cursor, segBase, s);
+
+  // Outer product into buffer 0.
+  const int L = p->params.levels;
+  p->bufCol[0] = alloc_n<int32_t>(p, Ph, s);
+  p->bufVal[0] = plan_alloc(p, std::max<int64_t>(Ph, 1) * vb, s);
+  if (L > 0) {
+    p->bufCol[1] = alloc_n<int32_t>(p, Ph, s);
+    p->bufVal[1] = plan_alloc(p, std::max<int64_t>(Ph, 1) * vb, s);
+  }
+  launch_outer_product(f64, Ph, entryOff, nE, cscCol, cscVal, segBase, p->brp, p->bcol, p->bval,
+                       p->bufCol[0], p->bufVal[0], s);
+  check_launch("outer product");
+
+  struct Piece {
+    int64_t first, n;
+    const int64_t* newOff;
+    const int32_t *newCnt, *newRow, *newSlot;
+    int8_t buf;
+  };
+  std::vector<Piece> pieces;
+  bool completed = (L == 0);
+  int64_t R = h, E = Ph;
+  const int64_t* rowPtr = chatRowPtr;
+  const int32_t *inRow = nullptr, *inSlot = nullptr;
+  int cur = 0;
+  for (int l = 0; l < L; ++l) {
+    p->st.level_elems[l] = E;
+    const int v = p->params.v_chunks[l];
+    const int64_t w = p->params.level_width[l];
+    const int shift = log2_exact(w);
+    const int64_t Q = R * v;
+    if (Q >= INT32_MAX) throw Error{SPGEMM_ERR_INDEX_OVERFLOW, "too many chunks in one level"};
+    const bool last = (l == L - 1);
+    int32_t* counts = alloc_n<int32_t>(p, Q, s);
+    int32_t* inv = alloc_n<int32_t>(p, Q, s);
+    int32_t* newCnt = alloc_n<int32_t>(p, Q, s);
+    int32_t* newRow = alloc_n<int32_t>(p, Q, s);
+    int32_t* newSlot = alloc_n<int32_t>(p, Q, s);
+    int64_t* newOff = alloc_n<int64_t>(p, Q + 1, s);
+    int64_t* cur64 = alloc_n<int64_t>(p, Q, s);
+    int32_t* ctr = alloc_n<int32_t>(p, 2, s);
+    int64_t* ltmp = alloc_n<int64_t>(p, scan_tmp_elems(Q) + 1, s);
+    launch_fill_i32(counts, 0, Q, s);
+    launch_fill_i32(newCnt, 0, Q, s);
+    launch_fill_i32(ctr, 0, 2, s);
+    int32_t blockElems;
+    int maxRows;
+    multisplit_geometry(f64, p->tau, v, &blockElems, &maxRows);
+    launch_histogram(E, blockElems, rowPtr, R, p->bufCol[cur], shift, v, maxRows, counts,
+                     p->errWord, s);
+    launch_partition(Q, counts, p->tau, last, v, inRow, inSlot, (int32_t)(w / W), inv, newCnt,
+                     newRow, newSlot, ctr, s);
+    launch_scan_i32(newCnt, Q, newOff, ltmp, s);
+    launch_copy_i64(cur64, newOff, Q, s);
+    const int out = 1 - cur;
+    launch_multisplit(f64, E, blockElems, rowPtr, R, p->bufCol[cur], p->bufVal[cur], shift, v,
+                      (int32_t)(w - 1), maxRows, inv, cur64, p->bufCol[out], p->bufVal[out],
+                      p->errWord, s);
+    check_launch("multisplit level");
+    HIP_CHECK(hipMemcpyAsync(p->hBins + 100, ctr, 8, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    const int64_t nH = p->hBins[100], nL = p->hBins[101];
+    int64_t nextE = 0;
+    if (nH > 0) {
+      HIP_CHECK(hipMemcpyAsync(p->hStats + 16, newOff + nH, 8, hipMemcpyDeviceToHost, s));
+      HIP_CHECK(hipStreamSynchronize(s));
+      nextE = p->hStats[16];
+    }
+    pieces.push_back(Piece{Q - nL, nL, newOff, newCnt, newRow, newSlot, (int8_t)out});
+    if (last) completed = true;
+    if (nH == 0) break;
+    R = nH;
+    E = nextE;
+    rowPtr = newOff;
+    inRow = newRow;
+    inSlot = newSlot;
+    cur = out;
+  }
+
+  // Final chunk list: light chunks of every level, then the W-wide chunks
+  // of the last level (or the heavy rows themselves with no multisplit).
+  int64_t nfc = 0;
+  for (auto& pc : pieces) nfc += pc.n;
+  if (L == 0) nfc = h;
+  p->nfc = nfc;
+  p->fcOff = alloc_n<int64_t>(p, nfc, s);
+  p->fcCnt = alloc_n<int32_t>(p, nfc, s);
+  p->fcRow = alloc_n<int32_t>(p, nfc, s);
+  p->fcSlot = alloc_n<int32_t>(p, nfc, s);
+  p->fcBuf = alloc_n<int8_t>(p, nfc, s);
+  if (L == 0) {
+    launch_final_from_rows(h, chatRowPtr, p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, s);
+    p->lastFirst = 0;
+  } else {
+    int64_t dst = 0;
+    for (auto& pc : pieces) {
+      launch_final_from_level(pc.first, pc.n, pc.newOff, pc.newCnt, pc.newRow, pc.newSlot, pc.buf,
+                              dst, p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, s);
+      dst += pc.n;
+    }
+    p->lastFirst = completed ? nfc - pieces.back().n : nfc;
+  }
+  uint8_t* key = alloc_n<uint8_t>(p, nfc, s);
+  p->fcOrder = alloc_n<int32_t>(p, nfc, s);
+  int32_t* bc = alloc_n<int32_t>(p, 64, s);
+  int32_t* bf = alloc_n<int32_t>(p, 64, s);
+  int32_t* bs = alloc_n<int32_t>(p, 65, s);
+  launch_chunk_bins(nfc, p->fcCnt, p->lastFirst, p->tau, p->dSymCaps, p->NS, p->NS, key,
+                    p->stats + kStatDenseElems, s);
+  launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, p->fcOrder, s);
+  HIP_CHECK(hipMemcpyAsync(p->hBins + 64, bs, sizeof(int32_t) * (p->NS + 2), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  p->fcBinStart.assign(p->hBins + 64, p->hBins + 64 + p->NS + 2);
+
+  p->slotNnz = alloc_n<int32_t>(p, h * p->nreq, s);
+  p->slotOff = alloc_n<int64_t>(p, h * p->nreq, s);
+  launch_fill_i32(p->slotNnz, 0, h * p->nreq, s);
+  ChunkList cl{p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, p->bufCol[0], p->bufCol[1],
+               p->bufVal[0], p->bufVal[1], W, p->nreq, p->xheavy, p->slotOff, p->slotNnz};
+  for (int b = 0; b < p->NS; ++b) {
+    const int64_t a = p->fcBinStart[b], e = p->fcBinStart[b + 1];
+    launch_sym_chunks(p->symBins[b], p->fcOrder + a, e - a, cl, p->errWord, s);
+  }
+  {
+    const int64_t a = p->fcBinStart[p->NS], e = p->fcBinStart[p->NS + 1];
+    launch_dense_sym(p->fcOrder + a, e - a, cl, p->errWord, s);
+    p->st.dense_chunks = e - a;
+  }
+  launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
+  check_launch("heavy symbolic");
+  p->st.final_chunks = nfc;
+}
+
+void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
+  const double t0 = now_ms();
+  hipStream_t s = p->stream;
+  fork(p);
+  const RowArgs a = row_args(p);
+  for (int b = 0; b < p->NS; ++b) {
+    const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
+    launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
+  }
+  check_launch("light symbolic");
+  if (p->h > 0) heavy_symbolic(p);
+  join(p);
+
+  const int64_t m = p->m;
+  p->cRowOff = alloc_n<int64_t>(p, m + 1, s);
+  p->scanTmp = alloc_n<int64_t>(p, scan_tmp_elems(m) + 1, s);
+  launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
+  std::vector<int32_t> caps(p->NS);
+  p->numKey = alloc_n<uint8_t>(p, m, s);
+  p->numOrder = alloc_n<int32_t>(p, m, s);
+  launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s);
+  launch_bin_sort(p->numKey, m, p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
+  check_launch("row pointer scan");
+  HIP_CHECK(hipMemcpyAsync(p->hStats + 20, p->cRowOff + m, 8, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (p->NS + 1), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hBins + 120, p->errWord, 4, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  check_device_errors(p, p->hBins[120]);
+  p->numBinStart.assign(p->hBins, p->hBins + p->NS + 1);
+  p->nnzC = p->hStats[20];
+  p->st.nnz_c = p->nnzC;
+  p->st.lds_dense_products = p->hStats[kStatDenseElems];
+  p->st.lds_hash_products = p->st.products - p->st.lds_dense_products;
+  p->st.global_products = 0;
+  p->st.batches = p->h > 0 ? 1 : 0;
+  if (!p->opts.rowptr64 && p->nnzC > INT32_MAX)
+    throw Error{SPGEMM_ERR_INDEX_OVERFLOW, "nnz(C) exceeds INT32_MAX; request rowptr64"};
+  launch_write_rowptr(p->cRowOff, m + 1, dRowPtr, p->opts.rowptr64 ? 1 : 0, s);
+  check_launch("row pointer write");
+  *nnzC = p->nnzC;
+  p->st.ms_symbolic = now_ms() - t0;
+}
+
+void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
+  const double t0 = now_ms();
+  fork(p);
+  const RowArgs a = row_args(p);
+  for (int b = 0; b < p->NS; ++b) {
+    const int64_t st = p->numBinStart[b], en = p->numBinStart[b + 1];
+    launch_num_rows(p->numBins[b], p->f64, p->numOrder + st, en - st, a, p->cRowOff, ccol, cval,
+                    p->errWord, p->sl);
+  }
+  check_launch("light numeric");
+  if (p->h > 0) {
+    hipStream_t s = p->sh;
+    ChunkList cl{p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, p->bufCol[0], p->bufCol[1],
+                 p->bufVal[0], p->bufVal[1], p->params.dense_width, p->nreq, p->xheavy,
+                 p->slotOff, p->slotNnz};
+    for (int b = 0; b < p->NS; ++b) {
+      const int64_t st = p->fcBinStart[b], en = p->fcBinStart[b + 1];
+      launch_num_chunks(p->numBins[b], p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol,
+                        cval, p->errWord, s);
+    }
+    const int64_t st = p->fcBinStart[p->NS], en = p->fcBinStart[p->NS + 1];
+    launch_dense_num(p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord, s);
+    check_launch("heavy numeric");
+  }
+  join(p);
+  p->st.ms_numeric = now_ms() - t0;
+}
+
+template <typename F>
+spgemm_status guarded(spgemm_plan_t p, F&& f) {
+  try {
+    f();
+    return SPGEMM_OK;
+  } catch (const Error& e) {
+    if (p) {
+      p->err = e.msg;
+      p->state = -1;
+    }
+    g_thread_error = e.msg;
+    return e.st;
+  } catch (const std::exception& e) {
+    if (p) {
+      p->err = e.what();
+      p->state = -1;
+    }
+    g_thread_error = e.what();
+    return SPGEMM_ERR_INTERNAL;
+  }
+}
+
+void destroy_plan(spgemm_plan_t p) {
+  if (!p) return;
+  if (p->sl && p->sl != p->stream) {
+    (void)hipEventRecord(p->evL, p->sl);
+    (void)hipEventRecord(p->evH, p->sh);
+    (void)hipStreamWaitEvent(p->stream, p->evL, 0);
+    (void)hipStreamWaitEvent(p->stream, p->evH, 0);
+  }
+  release(p);
+  if (p->sl && p->sl != p->stream) {
+    (void)hipStreamSynchronize(p->sl);
+    (void)hipStreamSynchronize(p->sh);
+    (void)hipStreamDestroy(p->sl);
+    (void)hipStreamDestroy(p->sh);
+    (void)hipEventDestroy(p->evFork);
+    (void)hipEventDestroy(p->evL);
+    (void)hipEventDestroy(p->evH);
+  }
+  if (p->hStats || p->hBins) (void)hipStreamSynchronize(p->stream);
+  if (p->hStats) (void)hipHostFree(p->hStats);
+  if (p->hBins) (void)hipHostFree(p->hBins);
+  delete p;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+spgemm_status spgemm_plan(spgemm_plan_t* out, int64_t m, int64_t k, int64_t n,
+                          const int32_t* dA_row_ptr, const int32_t* dA_col, const void* dA_val,
+                          int64_t nnzA, const int32_t* dB_row_ptr, const int32_t* dB_col,
+                          const void* dB_val, int64_t nnzB, spgemm_dtype dtype,
+                          const spgemm_options* opts, void* stream) {
+  if (!out) {
+    g_thread_error = "out is NULL";
+    return SPGEMM_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (m < 0 || k < 0 || n < 0 || nnzA < 0 || nnzB < 0 || (dtype != SPGEMM_F32 && dtype != SPGEMM_F64)) {
+    g_thread_error = "negative size or bad dtype";
+    return SPGEMM_ERR_INVALID_ARG;
+  }
+  if (!dA_row_ptr || !dB_row_ptr || (nnzA > 0 && (!dA_col || !dA_val)) ||
+      (nnzB > 0 && (!dB_col || !dB_val))) {
+    g_thread_error = "null device pointer";
+    return SPGEMM_ERR_INVALID_ARG;
+  }
+  if (m >= INT32_MAX || k >= INT32_MAX || n >= INT32_MAX || nnzA > INT32_MAX || nnzB > INT32_MAX) {
+    g_thread_error = "a size exceeds the int32 index range";
+    return SPGEMM_ERR_INDEX_OVERFLOW;
+  }
+  spgemm_plan_t p = new spgemm_plan_s();
+  p->m = m;
+  p->k = k;
+  p->n = n;
+  p->nnzA = nnzA;
+  p->nnzB = nnzB;
+  p->arp = dA_row_ptr;
+  p->acol = dA_col;
+  p->aval = dA_val;
+  p->brp = dB_row_ptr;
+  p->bcol = dB_col;
+  p->bval = dB_val;
+  p->f64 = dtype == SPGEMM_F64;
+  if (opts) p->opts = *opts;
+  p->stream = (hipStream_t)stream;
+  spgemm_status st = guarded(p, [&] { do_plan(p); });
+  if (st != SPGEMM_OK) {
+    g_thread_error = p->err;
+    destroy_plan(p);
+    return st;
+  }
+  *out = p;
+  return SPGEMM_OK;
+}
+
+spgemm_status spgemm_symbolic(spgemm_plan_t p, void* dC_row_ptr, int64_t* nnzC) {
+  if (!p || !nnzC || !dC_row_ptr) return SPGEMM_ERR_INVALID_ARG;
+  if (p->state != 0) {
+    p->err = "symbolic must follow a successful plan, once";
+    return SPGEMM_ERR_STATE;
+  }
+  spgemm_status st = guarded(p, [&] { do_symbolic(p, dC_row_ptr, nnzC); });
+  if (st == SPGEMM_OK) p->state = 1;
+  return st;
+}
+
+spgemm_status spgemm_numeric(spgemm_plan_t p, int32_t* dC_col, void* dC_val) {
+  if (!p) return SPGEMM_ERR_INVALID_ARG;
+  if (p->state != 1) {
+    p->err = "numeric must follow a successful symbolic, once";
+    return SPGEMM_ERR_STATE;
+  }
+  if (p->nnzC > 0 && (!dC_col || !dC_val)) return SPGEMM_ERR_INVALID_ARG;
+  spgemm_status st = guarded(p, [&] { do_numeric(p, dC_col, dC_val); });
+  if (st == SPGEMM_OK) p->state = 2;
+  return st;
+}
+
+spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats* out) {
+  if (!p || !out) return SPGEMM_ERR_INVALID_ARG;
+  spgemm_status st = guarded(p, [&] {
+    if (p->state >= 1) check_device_errors(p, read_err(p, p->stream));
+  });
+  *out = p->st;
+  return st;
+}
+
+void spgemm_destroy(spgemm_plan_t p) { destroy_plan(p); }
+
+const char* spgemm_status_string(spgemm_status s) {
+  switch (s) {
+    case SPGEMM_OK: return "ok";
+    case SPGEMM_ERR_INVALID_ARG: return "invalid argument";
+    case SPGEMM_ERR_INVALID_CSR: return "input is not canonical CSR";
+    case SPGEMM_ERR_INDEX_OVERFLOW: return "index overflow";
+    case SPGEMM_ERR_OOM: return "out of device memory";
+    case SPGEMM_ERR_HIP: return "HIP runtime error";
+    case SPGEMM_ERR_STATE: return "call order violated";
+    case SPGEMM_ERR_INTERNAL: return "internal capacity check failed";
+  }
+  return "unknown status";
+}
+
+const char* spgemm_last_error(spgemm_plan_t p) {
+  return p ? p->err.c_str() : g_thread_error.c_str();
+}
+
+}  // extern "C"
+
+// ============================================================ prune / renorm
+struct spgemm_prune_s {
+  int64_t m = 0, n = 0;
+  const void* rp = nullptr;
+  int rp64 = 0;
+  const int32_t* col = nullptr;
+  const void* val = nullptr;
+  bool f64 = false;
+  double thr = 0;
+  hipStream_t stream = nullptr;
+  int64_t *keep = nullptr, *off = nullptr, *tmp = nullptr;
+  double* colsum = nullptr;
+  int64_t nnzOut = 0;
+  int state = 0;
+  std::string err;
+  int64_t* hbuf = nullptr;
+};
+
+namespace {
+void prune_free(spgemm_prune_t p) {
+  if (!p) return;
+  for (void* ptr : {(void*)p->keep, (void*)p->off, (void*)p->tmp, (void*)p->colsum})
+    if (ptr) (void)hipFreeAsync(ptr, p->stream);
+  if (p->hbuf) {
+    (void)hipStreamSynchronize(p->stream);
+    (void)hipHostFree(p->hbuf);
+  }
+  delete p;
+}
+}  // namespace
+
+extern "C" spgemm_status spgemm_prune_colnorm_count(
+    spgemm_prune_t* out, int64_t m, int64_t n, const void* dC_row_ptr, int32_t c_rowptr64,
+    const int32_t* dC_col, const void* dC_val, spgemm_dtype dtype, double threshold,
+    void* dOut_row_ptr, int32_t out_rowptr64, int64_t* nnzOut, void* stream) {
+  if (!out || !nnzOut || !dC_row_ptr || !dOut_row_ptr || m < 0 || n < 0 ||
+      (dtype != SPGEMM_F32 && dtype != SPGEMM_F64)) {
+    g_thread_error = "invalid argument";
+    return SPGEMM_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  spgemm_prune_t p = new spgemm_prune_s();
+  p->m = m;
+  p->n = n;
+  p->rp = dC_row_ptr;
+  p->rp64 = c_rowptr64;
+  p->col = dC_col;
+  p->val = dC_val;
+  p->f64 = dtype == SPGEMM_F64;
+  p->thr = threshold;
+  p->stream = (hipStream_t)stream;
+  try {
+    hipStream_t s = p->stream;
+    HIP_CHECK(hipHostMalloc((void**)&p->hbuf, 64, hipHostMallocDefault));
+    HIP_CHECK(hipMallocAsync((void**)&p->keep, sizeof(int64_t) * std::max<int64_t>(m, 1), s));
+    HIP_CHECK(hipMallocAsync((void**)&p->off, sizeof(int64_t) * (m + 1), s));
+    HIP_CHECK(hipMallocAsync((void**)&p->tmp, sizeof(int64_t) * (scan_tmp_elems(m) + 1), s));
+    HIP_CHECK(hipMallocAsync((void**)&p->colsum, sizeof(double) * std::max<int64_t>(n, 1), s));
+    launch_fill_i64((int64_t*)p->colsum, 0, n, s);  // +0.0 has an all-zero bit pattern
+    launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->keep, p->colsum, s);
+    launch_scan_i64(p->keep, m, p->off, p->tmp, s);
+    check_launch("prune count");
+    HIP_CHECK(hipMemcpyAsync(p->hbuf, p->off + m, 8, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    p->nnzOut = p->hbuf[0];
+    if (!out_rowptr64 && p->nnzOut > INT32_MAX)
+      throw Error{SPGEMM_ERR_INDEX_OVERFLOW, "kept entries exceed INT32_MAX"};
+    launch_write_rowptr(p->off, m + 1, dOut_row_ptr, out_rowptr64 ? 1 : 0, s);
+    check_launch("prune row pointers");
+  } catch (const Error& e) {
+    g_thread_error = e.msg;
+    prune_free(p);
+    return e.st;
+  }
+  *nnzOut = p->nnzOut;
+  *out = p;
+  return SPGEMM_OK;
+}
+
+extern "C" spgemm_status spgemm_prune_colnorm_fill(spgemm_prune_t p, int32_t* dOut_col,
+                                                   void* dOut_val) {
+  if (!p) return SPGEMM_ERR_INVALID_ARG;
+  if (p->state != 0) return SPGEMM_ERR_STATE;
+  if (p->nnzOut > 0 && (!dOut_col || !dOut_val)) return SPGEMM_ERR_INVALID_ARG;
+  try {
+    launch_prune_fill(p->m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->off, p->colsum,
+                      dOut_col, dOut_val, p->stream);
+    check_launch("prune fill");
+  } catch (const Error& e) {
+    p->err = e.msg;
+    g_thread_error = e.msg;
+    return e.st;
+  }
+  p->state = 1;
+  return SPGEMM_OK;
+}
+
+extern "C" void spgemm_prune_destroy(spgemm_prune_t p) { prune_free(p); }

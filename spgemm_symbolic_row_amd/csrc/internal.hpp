@@ -1,0 +1,184 @@
+// Declarations shared between the host orchestrator (api.cpp) and the kernel
+// translation units.  Every launcher enqueues on the given stream and
+// returns without synchronising.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sg {
+
+constexpr int32_t kEmptyKey = -1;
+
+// Bits of the plan's device status word.
+enum : int32_t {
+  kErrHashFull = 1,       // an LDS hash table ran out of slots
+  kErrCsr = 2,            // validation found a non-canonical input
+  kErrRowsPerBlock = 4,   // a multisplit work group met more rows than sized for
+  kErrCountMismatch = 8,  // numeric produced a row/chunk size != symbolic
+};
+
+// Indices of the per-plan int64 counters filled by the row-information pass.
+enum : int {
+  kStatProducts = 0,
+  kStatHeavyProducts = 1,
+  kStatHeavyANnz = 2,
+  kStatMaxRowProducts = 3,
+  kStatHeavyRows = 4,
+  kStatLightRows = 5,
+  kStatDenseElems = 6,
+  kNumStats = 8,
+};
+
+// One LDS hash-accumulator bin: items with size <= cap run with `tpr`
+// threads each, `rpb` items per work group, a table of T = tpr*spt slots and
+// (numeric) a sort of N = next_pow2(cap) entries.
+struct BinCfg {
+  int32_t cap;
+  int32_t tpr;
+  int32_t rpb;
+  int32_t spt;
+  int32_t T;
+  int32_t N;
+  size_t lds;  // dynamic LDS bytes per work group
+};
+
+struct RowArgs {
+  const int32_t* arp;
+  const int32_t* acol;
+  const void* aval;
+  const int32_t* brp;
+  const int32_t* bcol;
+  const void* bval;
+  const int32_t* scanA;  // row-local exclusive product offset of each A entry
+  const int64_t* rowP;   // products per row
+};
+
+// Final chunks of the heavy rows, in the order they were listed.  Chunk c
+// holds cnt[c] elements at off[c] of buffer buf[c]; it belongs to heavy row
+// row[c] and covers the W-wide column slots starting at slot[c] (its column
+// base is slot[c] * W).
+struct ChunkList {
+  const int64_t* off;
+  const int32_t* cnt;
+  const int32_t* row;
+  const int32_t* slot;
+  const int8_t* buf;
+  const int32_t* col0;
+  const int32_t* col1;
+  const void* val0;
+  const void* val1;
+  int64_t W;
+  int64_t nreq;           // W-wide slots per heavy row
+  const int32_t* xheavy;  // heavy row index -> row of C
+  const int64_t* slotOff; // exclusive offset of each slot inside its row
+  int32_t* slotNnz;       // nnz of the chunk starting at each slot
+};
+
+// ---- k_util.hip ----
+void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s);
+void launch_copy_i64(int64_t* dst, const int64_t* src, int64_t n, hipStream_t s);
+// out[i] = sum_{j<i} in[j] for i in [0, n]; out has n+1 entries.  tmp needs
+// scan_tmp_elems(n) int64 entries.
+int64_t scan_tmp_elems(int64_t n);
+void launch_scan_i64(const int64_t* in, int64_t n, int64_t* out, int64_t* tmp, hipStream_t s);
+void launch_scan_i32(const int32_t* in, int64_t n, int64_t* out, int64_t* tmp, hipStream_t s);
+// Counting sort of item indices by an 8-bit key (keys >= nbins are dropped).
+// cnt/fill: nbins int32 scratch; start: nbins+1 int32 (bin offsets).
+void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int32_t* fill,
+                     int32_t* start, int32_t* out, hipStream_t s);
+void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
+                     const int32_t* bcol, int64_t tau, const int32_t* caps, int nbins,
+                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* stats,
+                     hipStream_t s);
+void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
+                     const int32_t* col, int32_t* err, hipStream_t s);
+void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hipStream_t s);
+void launch_gather_i64(const int64_t* src, const int32_t* idx, int64_t n, int64_t* dst,
+                       hipStream_t s);
+// key[i] = bin of cnt[rows[i]] among caps[0..nbins) (first cap >= value), for
+// light rows; heavy rows (rowBin == heavyBin) get 255.
+void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,
+                             int heavyBin, const int32_t* caps, int nbins, uint8_t* key,
+                             hipStream_t s);
+
+// ---- k_light.hip ----
+void light_set_attributes();
+void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
+                     int64_t* cnt, int32_t* err, hipStream_t s);
+void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
+                     const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
+                     int32_t* err, hipStream_t s);
+void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const ChunkList& cl,
+                       int32_t* err, hipStream_t s);
+void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
+                       const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
+                       int32_t* err, hipStream_t s);
+
+// ---- k_heavy.hip ----
+void heavy_set_attributes();
+void launch_csc_count(int64_t h, const int32_t* xheavy, const int32_t* arp, const int32_t* acol,
+                      int32_t* colCnt, hipStream_t s);
+void launch_csc_fill(int64_t h, const int32_t* xheavy, const int32_t* arp, const int32_t* acol,
+                     const void* aval, bool f64, int64_t* colFill, int32_t* cscRow,
+                     int32_t* cscCol, void* cscVal, hipStream_t s);
+void launch_entry_products(int64_t nE, const int32_t* cscCol, const int32_t* brp, int64_t* nb,
+                           hipStream_t s);
+void launch_seg_base(int64_t nE, const int32_t* cscRow, const int64_t* nb, int64_t* cursor,
+                     int64_t* segBase, hipStream_t s);
+void launch_outer_product(bool f64, int64_t Ph, const int64_t* entryOff, int64_t nE,
+                          const int32_t* cscCol, const void* cscVal, const int64_t* segBase,
+                          const int32_t* brp, const int32_t* bcol, const void* bval,
+                          int32_t* outCol, void* outVal, hipStream_t s);
+// Multisplit levels.  Input rows r in [0, R) hold elements
+// [rowPtr[r], rowPtr[r+1]) whose chunk is col >> shift (< v).
+// Elements per multisplit work group and the most input rows such a range
+// can meet, for rows of more than tau elements and v chunks per row.
+void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int* maxRows);
+void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
+                      const int32_t* col, int shift, int v, int maxRows, int32_t* counts,
+                      int32_t* err, hipStream_t s);
+void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, int v,
+                      const int32_t* inRow, const int32_t* inSlot, int32_t slotStep,
+                      int32_t* inv, int32_t* newCnt, int32_t* newRow, int32_t* newSlot,
+                      int32_t* ctr, hipStream_t s);
+void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
+                       int64_t R, const int32_t* inCol, const void* inVal, int shift, int v,
+                       int32_t wmask, int maxRows, const int32_t* inv, int64_t* cursor,
+                       int32_t* outCol, void* outVal, int32_t* err, hipStream_t s);
+// Final-chunk descriptors: from a level's light positions [first, first+n)
+// or, when there is no multisplit, from the heavy rows themselves.
+void launch_final_from_level(int64_t first, int64_t n, const int64_t* newOff,
+                             const int32_t* newCnt, const int32_t* newRow,
+                             const int32_t* newSlot, int8_t buf, int64_t dst0, int64_t* fcOff,
+                             int32_t* fcCnt, int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf,
+                             hipStream_t s);
+void launch_final_from_rows(int64_t h, const int64_t* rowPtr, int64_t* fcOff, int32_t* fcCnt,
+                            int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf, hipStream_t s);
+// Bin of each final chunk: dense when it is W wide (list positions
+// >= lastFirst hold the W-wide chunks) and has more than tau elements, else
+// the hash bin of its element count.
+void launch_chunk_bins(int64_t nfc, const int32_t* fcCnt, int64_t lastFirst, int64_t tau,
+                       const int32_t* caps, int nbins, int denseBin, uint8_t* key,
+                       int64_t* denseElems, hipStream_t s);
+void launch_dense_sym(const int32_t* items, int64_t n, const ChunkList& cl, int32_t* err,
+                      hipStream_t s);
+void launch_dense_num(bool f64, const int32_t* items, int64_t n, const ChunkList& cl,
+                      const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
+                      hipStream_t s);
+size_t dense_num_lds(bool f64, int64_t W);
+// Per heavy row: exclusive scan of its nreq slot counts -> slotOff, and the
+// row total -> cnt[xheavy[r]].
+void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,
+                      const int32_t* xheavy, int64_t* cnt, hipStream_t s);
+
+// ---- k_prune.hip ----
+void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                        bool f64, double thr, int64_t* keepCnt, double* colsum,
+                        hipStream_t s);
+void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                       bool f64, double thr, const int64_t* outOff, const double* colsum,
+                       int32_t* ocol, void* oval, hipStream_t s);
+
+}  // namespace sg

@@ -1,0 +1,404 @@
+// LDS hash accumulators (gMAGNUS page §III-E; Ocean page §2): light rows of C
+// computed row by row with Gustavson's method (gMAGNUS §II-B, Eq. 1), and
+// light chunks of the reordered heavy intermediate.  Items are binned by
+// size; each bin runs `tpr` threads per item with a table of T slots.
+//
+//   symbolic: insert column keys into an LDS key set, count the new ones;
+//   numeric:  insert-or-add (key, value) pairs with LDS atomics, compact the
+//             occupied slots, bitonic-sort them by column in LDS and write
+//             the sorted row (or chunk) to its place in C.
+#include <climits>
+
+#include "device_common.hpp"
+
+namespace sg {
+namespace {
+
+constexpr int kMaxSpt = 24;  // slots per thread held in registers by the compaction
+
+// Products [p0, p1) of one row of A*B in Gustavson order (entry-major): the
+// flattened product index q of entry e starts at scanA[e] (row-local
+// exclusive offset).  The wave keeps 64 consecutive A entries in registers,
+// finds for each of 64 consecutive products the entry that owns it with a
+// 6-step binary search across lanes, and hands f(act, b, a) the index b of
+// the B element and the A value.  Every lane runs the same iterations.
+template <bool VAL, typename V, typename F>
+__device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
+                                           const int32_t* __restrict__ acol,
+                                           const V* __restrict__ aval,
+                                           const int32_t* __restrict__ brp, int64_t rs,
+                                           int64_t re, int32_t P, int32_t p0, int32_t p1,
+                                           F&& f) {
+  if (p0 >= p1) return;
+  int64_t j = wave_last_le(scanA, rs, re, p0);
+  int32_t p = p0;
+  while (p < p1) {
+    const int64_t e = j + lane_id();
+    const bool ev = e < re;
+    const int32_t off = ev ? scanA[e] : P;
+    int32_t bs = 0;
+    V a = V(0);
+    if (ev) {
+      bs = brp[acol[e]];
+      if (VAL) a = aval[e];
+    }
+    int32_t bend = (j + kWave < re) ? scanA[j + kWave] : P;
+    if (bend > p1) bend = p1;
+    for (; p < bend; p += kWave) {
+      const int32_t q = p + lane_id();
+      const bool act = q < bend;
+      int s = 0;
+#pragma unroll
+      for (int step = 32; step >= 1; step >>= 1) {
+        const int32_t o = __shfl(off, s + step);
+        if (o <= q) s += step;
+      }
+      const int32_t so = __shfl(off, s);
+      const int32_t sb = __shfl(bs, s);
+      V sa = V(0);
+      if (VAL) sa = __shfl(a, s);
+      f(act, sb + (q - so), sa);
+    }
+    p = bend;
+    j += kWave;
+  }
+}
+
+// ---------------------------------------------------------------- symbolic
+template <int TPR, int RPB>
+__global__ __launch_bounds__(TPR* RPB) void k_sym_rows(const int32_t* __restrict__ rows,
+                                                       int64_t nrows, int32_t T, RowArgs a,
+                                                       int64_t* __restrict__ cnt,
+                                                       int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* keysAll = (int32_t*)smem;
+  int32_t* gcount = keysAll + RPB * T;
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
+  int32_t* keys = keysAll + g * T;
+  for (int s = t; s < T; s += TPR) keys[s] = kEmptyKey;
+  if (t == 0) gcount[g] = 0;
+  __syncthreads();
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t mine = 0;
+  int32_t row = 0;
+  if (ri < nrows) {
+    row = rows[ri];
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t P = (int32_t)a.rowP[row];
+    constexpr int WPR = TPR / kWave;
+    const int w = t / kWave;
+    const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
+    const int32_t* __restrict__ bcol = a.bcol;
+    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, rs, re, P, p0, p1,
+                             [&](bool act, int32_t b, float) {
+                               if (act && hset_insert(keys, (uint32_t)T, bcol[b], err)) ++mine;
+                             });
+  }
+  const int32_t ws = wave_sum(mine);
+  if (lane_id() == 0 && ri < nrows) atomicAdd(&gcount[g], ws);
+  __syncthreads();
+  if (t == 0 && ri < nrows) cnt[row] = gcount[g];
+}
+
+template <int TPR, int RPB>
+__global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const int32_t* __restrict__ items,
+                                                         int64_t n, int32_t T, ChunkList cl,
+                                                         int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* keysAll = (int32_t*)smem;
+  int32_t* gcount = keysAll + RPB * T;
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
+  int32_t* keys = keysAll + g * T;
+  for (int s = t; s < T; s += TPR) keys[s] = kEmptyKey;
+  if (t == 0) gcount[g] = 0;
+  __syncthreads();
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t mine = 0;
+  int32_t item = 0;
+  if (ri < n) {
+    item = items[ri];
+    const int64_t off = cl.off[item];
+    const int64_t end = off + cl.cnt[item];
+    const int32_t* __restrict__ col = cl.buf[item] ? cl.col1 : cl.col0;
+    for (int64_t e = off + t; e < end; e += TPR)
+      if (hset_insert(keys, (uint32_t)T, col[e], err)) ++mine;
+  }
+  const int32_t ws = wave_sum(mine);
+  if (lane_id() == 0 && ri < n) atomicAdd(&gcount[g], ws);
+  __syncthreads();
+  if (t == 0 && ri < n) cl.slotNnz[(int64_t)cl.row[item] * cl.nreq + cl.slot[item]] = gcount[g];
+}
+
+// ----------------------------------------------------------------- numeric
+// Shared tail of the numeric kernels: compact the occupied slots of this
+// group's table into [0, total), sort them by key, return total.  Called by
+// every thread of the work group.
+template <int TPR, int RPB, typename V>
+__device__ __forceinline__ int32_t compact_and_sort(int32_t* keys, V* vals, int32_t spt,
+                                                    int32_t N, int32_t* wtot) {
+  constexpr int WPR = TPR / kWave;
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR, w = t / kWave;
+  int32_t kk[kMaxSpt];
+  V vv[kMaxSpt];
+  int32_t mine = 0;
+#pragma unroll
+  for (int s = 0; s < kMaxSpt; ++s) {
+    kk[s] = kEmptyKey;
+    vv[s] = V(0);
+    if (s < spt) {
+      const int slot = t + s * TPR;
+      kk[s] = keys[slot];
+      vv[s] = vals[slot];
+      mine += (kk[s] != kEmptyKey);
+    }
+  }
+  const int32_t inc = wave_incl_scan(mine);
+  if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < WPR; ++i) {
+    const int32_t tv = wtot[g * WPR + i];
+    if (i < w) before += tv;
+    total += tv;
+  }
+  int32_t pos = before + inc - mine;
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kMaxSpt; ++s) {
+    if (s < spt && kk[s] != kEmptyKey) {
+      keys[pos] = kk[s];
+      vals[pos] = vv[s];
+      ++pos;
+    }
+  }
+  for (int i = total + t; i < N; i += TPR) keys[i] = INT_MAX;
+  __syncthreads();
+  // Bitonic sort of keys[0, N) carrying vals; N is a power of two.
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < (N >> 1); i += TPR) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int hi = lo + j;
+        const bool up = (lo & k) == 0;
+        const int32_t ka = keys[lo], kb = keys[hi];
+        if ((ka > kb) == up) {
+          keys[lo] = kb;
+          keys[hi] = ka;
+          const V va = vals[lo];
+          vals[lo] = vals[hi];
+          vals[hi] = va;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  return total;
+}
+
+template <int TPR, int RPB, typename V>
+__global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict__ rows,
+                                                       int64_t nrows, int32_t T, int32_t spt,
+                                                       int32_t N, RowArgs a,
+                                                       const int64_t* __restrict__ cRowOff,
+                                                       int32_t* __restrict__ ccol,
+                                                       V* __restrict__ cval,
+                                                       int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  V* valsAll = (V*)smem;
+  int32_t* keysAll = (int32_t*)(valsAll + RPB * T);
+  int32_t* wtot = keysAll + RPB * T;
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
+  int32_t* keys = keysAll + g * T;
+  V* vals = valsAll + g * T;
+  for (int s = t; s < T; s += TPR) {
+    keys[s] = kEmptyKey;
+    vals[s] = V(0);
+  }
+  __syncthreads();
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t row = 0;
+  if (ri < nrows) {
+    row = rows[ri];
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t P = (int32_t)a.rowP[row];
+    constexpr int WPR = TPR / kWave;
+    const int w = t / kWave;
+    const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
+    const int32_t* __restrict__ bcol = a.bcol;
+    const V* __restrict__ bval = (const V*)a.bval;
+    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, rs, re, P, p0, p1,
+                        [&](bool act, int32_t b, V av) {
+                          if (act) hmap_add(keys, vals, (uint32_t)T, bcol[b], av * bval[b], err);
+                        });
+  }
+  __syncthreads();
+  const int32_t total = compact_and_sort<TPR, RPB, V>(keys, vals, spt, N, wtot);
+  if (ri < nrows) {
+    const int64_t base = cRowOff[row];
+    const int64_t want = cRowOff[row + 1] - base;
+    if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
+    const int32_t lim = (int32_t)(want < total ? want : total);
+    for (int e = t; e < lim; e += TPR) {
+      ccol[base + e] = keys[e];
+      cval[base + e] = vals[e];
+    }
+  }
+}
+
+template <int TPR, int RPB, typename V>
+__global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restrict__ items,
+                                                         int64_t n, int32_t T, int32_t spt,
+                                                         int32_t N, ChunkList cl,
+                                                         const int64_t* __restrict__ cRowOff,
+                                                         int32_t* __restrict__ ccol,
+                                                         V* __restrict__ cval,
+                                                         int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  V* valsAll = (V*)smem;
+  int32_t* keysAll = (int32_t*)(valsAll + RPB * T);
+  int32_t* wtot = keysAll + RPB * T;
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
+  int32_t* keys = keysAll + g * T;
+  V* vals = valsAll + g * T;
+  for (int s = t; s < T; s += TPR) {
+    keys[s] = kEmptyKey;
+    vals[s] = V(0);
+  }
+  __syncthreads();
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t item = 0;
+  if (ri < n) {
+    item = items[ri];
+    const int64_t off = cl.off[item];
+    const int64_t end = off + cl.cnt[item];
+    const bool b1 = cl.buf[item] != 0;
+    const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
+    const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
+    for (int64_t e = off + t; e < end; e += TPR) hmap_add(keys, vals, (uint32_t)T, col[e], val[e], err);
+  }
+  __syncthreads();
+  const int32_t total = compact_and_sort<TPR, RPB, V>(keys, vals, spt, N, wtot);
+  if (ri < n) {
+    const int64_t hr = cl.row[item];
+    const int64_t sidx = hr * cl.nreq + cl.slot[item];
+    const int64_t base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
+    const int32_t want = cl.slotNnz[sidx];
+    if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
+    const int32_t lim = want < total ? want : total;
+    const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+    for (int e = t; e < lim; e += TPR) {
+      ccol[base + e] = colBase + keys[e];
+      cval[base + e] = vals[e];
+    }
+  }
+}
+
+template <typename K>
+void set_lds_attr(K kernel) {
+  (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+}
+
+}  // namespace
+
+void light_set_attributes() {
+  set_lds_attr(k_sym_rows<64, 4>);
+  set_lds_attr(k_sym_rows<128, 2>);
+  set_lds_attr(k_sym_rows<256, 1>);
+  set_lds_attr(k_sym_rows<512, 1>);
+  set_lds_attr(k_sym_rows<1024, 1>);
+  set_lds_attr(k_sym_chunks<64, 4>);
+  set_lds_attr(k_sym_chunks<128, 2>);
+  set_lds_attr(k_sym_chunks<256, 1>);
+  set_lds_attr(k_sym_chunks<512, 1>);
+  set_lds_attr(k_sym_chunks<1024, 1>);
+#define SG_NUM_ATTR(V)                     \
+  set_lds_attr(k_num_rows<64, 4, V>);      \
+  set_lds_attr(k_num_rows<128, 2, V>);     \
+  set_lds_attr(k_num_rows<256, 1, V>);     \
+  set_lds_attr(k_num_rows<512, 1, V>);     \
+  set_lds_attr(k_num_rows<1024, 1, V>);    \
+  set_lds_attr(k_num_chunks<64, 4, V>);    \
+  set_lds_attr(k_num_chunks<128, 2, V>);   \
+  set_lds_attr(k_num_chunks<256, 1, V>);   \
+  set_lds_attr(k_num_chunks<512, 1, V>);   \
+  set_lds_attr(k_num_chunks<1024, 1, V>);
+  SG_NUM_ATTR(float)
+  SG_NUM_ATTR(double)
+#undef SG_NUM_ATTR
+}
+
+#define SG_DISPATCH_TPR(b, MACRO)                      \
+  switch ((b).tpr) {                                   \
+    case 64: MACRO(64, 4); break;                      \
+    case 128: MACRO(128, 2); break;                    \
+    case 256: MACRO(256, 1); break;                    \
+    case 512: MACRO(512, 1); break;                    \
+    default: MACRO(1024, 1); break;                    \
+  }
+
+void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
+                     int64_t* cnt, int32_t* err, hipStream_t s) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
+#define L(TPR, RPB)                                                                         \
+  hipLaunchKernelGGL((k_sym_rows<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, nrows, \
+                     b.T, a, cnt, err)
+  SG_DISPATCH_TPR(b, L)
+#undef L
+}
+
+void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const ChunkList& cl,
+                       int32_t* err, hipStream_t s) {
+  if (n <= 0) return;
+  const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
+#define L(TPR, RPB)                                                                          \
+  hipLaunchKernelGGL((k_sym_chunks<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, items, n, \
+                     b.T, cl, err)
+  SG_DISPATCH_TPR(b, L)
+#undef L
+}
+
+void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
+                     const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
+                     int32_t* err, hipStream_t s) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
+  if (f64) {
+#define L(TPR, RPB)                                                                            \
+  hipLaunchKernelGGL((k_num_rows<TPR, RPB, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, \
+                     nrows, b.T, b.spt, b.N, a, cRowOff, ccol, (double*)cval, err)
+    SG_DISPATCH_TPR(b, L)
+#undef L
+  } else {
+#define L(TPR, RPB)                                                                           \
+  hipLaunchKernelGGL((k_num_rows<TPR, RPB, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, \
+                     nrows, b.T, b.spt, b.N, a, cRowOff, ccol, (float*)cval, err)
+    SG_DISPATCH_TPR(b, L)
+#undef L
+  }
+}
+
+void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
+                       const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
+                       int32_t* err, hipStream_t s) {
+  if (n <= 0) return;
+  const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
+  if (f64) {
+#define L(TPR, RPB)                                                                            \
+  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, double>), dim3(grid), dim3(TPR * RPB), b.lds, s,     \
+                     items, n, b.T, b.spt, b.N, cl, cRowOff, ccol, (double*)cval, err)
+    SG_DISPATCH_TPR(b, L)
+#undef L
+  } else {
+#define L(TPR, RPB)                                                                           \
+  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, float>), dim3(grid), dim3(TPR * RPB), b.lds, s,     \
+                     items, n, b.T, b.spt, b.N, cl, cRowOff, ccol, (float*)cval, err)
+    SG_DISPATCH_TPR(b, L)
+#undef L
+  }
+}
+
+}  // namespace sg

@@ -1,0 +1,123 @@
+// One Markov-clustering prune and column renormalisation (Trident page,
+// "Communication-Avoiding SpGEMM via Trident Partitioning", §5.7): entries
+// below the threshold are dropped, then every column is divided by the sum
+// of its kept entries.  The comparison is made in the value type; column
+// sums are accumulated in fp64 and each kept value is rounded once.
+#include "device_common.hpp"
+
+namespace sg {
+namespace {
+
+constexpr int kNT = 256;
+
+template <typename RP>
+__device__ __forceinline__ int64_t rp_at(const void* rp, int64_t i) {
+  return (int64_t)((const RP*)rp)[i];
+}
+
+// One wave per row: count kept entries, add kept values into column sums.
+template <typename V, typename RP>
+__global__ __launch_bounds__(kNT) void k_prune_count(int64_t m, const void* __restrict__ rp,
+                                                     const int32_t* __restrict__ col,
+                                                     const V* __restrict__ val, V thr,
+                                                     int64_t* __restrict__ keep,
+                                                     double* __restrict__ colsum) {
+  const int64_t r = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
+  if (r >= m) return;
+  const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
+  int64_t kept = 0;
+  for (int64_t base = a; base < b; base += kWave) {
+    const int64_t e = base + lane_id();
+    bool k = false;
+    if (e < b) {
+      const V x = val[e];
+      k = x >= thr;
+      if (k) unsafeAtomicAdd(&colsum[col[e]], (double)x);
+    }
+    kept += __popcll(__ballot(k));
+  }
+  if (lane_id() == 0) keep[r] = kept;
+}
+
+// One wave per row: order-preserving compaction of the kept entries.
+template <typename V, typename RP>
+__global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __restrict__ rp,
+                                                    const int32_t* __restrict__ col,
+                                                    const V* __restrict__ val, V thr,
+                                                    const int64_t* __restrict__ outOff,
+                                                    const double* __restrict__ colsum,
+                                                    int32_t* __restrict__ ocol,
+                                                    V* __restrict__ oval) {
+  const int64_t r = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
+  if (r >= m) return;
+  const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
+  int64_t w = outOff[r];
+  for (int64_t base = a; base < b; base += kWave) {
+    const int64_t e = base + lane_id();
+    bool k = false;
+    V x = V(0);
+    int32_t c = 0;
+    if (e < b) {
+      x = val[e];
+      c = col[e];
+      k = x >= thr;
+    }
+    const uint64_t mk = __ballot(k);
+    if (k) {
+      const int64_t pos = w + __popcll(mk & lanemask_lt());
+      ocol[pos] = c;
+      oval[pos] = (V)((double)x / colsum[c]);
+    }
+    w += __popcll(mk);
+  }
+}
+
+inline unsigned grid_rows(int64_t m) { return (unsigned)((m * kWave + kNT - 1) / kNT); }
+
+}  // namespace
+
+void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                        bool f64, double thr, int64_t* keepCnt, double* colsum,
+                        hipStream_t s) {
+  if (m <= 0) return;
+  const dim3 g(grid_rows(m)), b(kNT);
+  if (f64) {
+    if (rp64)
+      hipLaunchKernelGGL((k_prune_count<double, int64_t>), g, b, 0, s, m, rp, col,
+                         (const double*)val, thr, keepCnt, colsum);
+    else
+      hipLaunchKernelGGL((k_prune_count<double, int32_t>), g, b, 0, s, m, rp, col,
+                         (const double*)val, thr, keepCnt, colsum);
+  } else {
+    if (rp64)
+      hipLaunchKernelGGL((k_prune_count<float, int64_t>), g, b, 0, s, m, rp, col,
+                         (const float*)val, (float)thr, keepCnt, colsum);
+    else
+      hipLaunchKernelGGL((k_prune_count<float, int32_t>), g, b, 0, s, m, rp, col,
+                         (const float*)val, (float)thr, keepCnt, colsum);
+  }
+}
+
+void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                       bool f64, double thr, const int64_t* outOff, const double* colsum,
+                       int32_t* ocol, void* oval, hipStream_t s) {
+  if (m <= 0) return;
+  const dim3 g(grid_rows(m)), b(kNT);
+  if (f64) {
+    if (rp64)
+      hipLaunchKernelGGL((k_prune_fill<double, int64_t>), g, b, 0, s, m, rp, col,
+                         (const double*)val, thr, outOff, colsum, ocol, (double*)oval);
+    else
+      hipLaunchKernelGGL((k_prune_fill<double, int32_t>), g, b, 0, s, m, rp, col,
+                         (const double*)val, thr, outOff, colsum, ocol, (double*)oval);
+  } else {
+    if (rp64)
+      hipLaunchKernelGGL((k_prune_fill<float, int64_t>), g, b, 0, s, m, rp, col,
+                         (const float*)val, (float)thr, outOff, colsum, ocol, (float*)oval);
+    else
+      hipLaunchKernelGGL((k_prune_fill<float, int32_t>), g, b, 0, s, m, rp, col,
+                         (const float*)val, (float)thr, outOff, colsum, ocol, (float*)oval);
+  }
+}
+
+}  // namespace sg

@@ -1,0 +1,384 @@
+// Utility kernels: fills, device-wide exclusive scan, counting sort by bin,
+// the per-row intermediate-product pass (InterOffsets of gMAGNUS Algorithm 3,
+// §III-A), CSR validation and row-pointer output.
+#include "device_common.hpp"
+
+namespace sg {
+
+namespace {
+
+constexpr int kNT = 256;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline unsigned grid_for(int64_t n, int per_block) {
+  int64_t g = cdiv(n, per_block);
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kNT) void k_fill(T* __restrict__ p, T v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n; i += (int64_t)gridDim.x * kNT)
+    p[i] = v;
+}
+
+__global__ __launch_bounds__(kNT) void k_copy_i64(int64_t* __restrict__ d, const int64_t* __restrict__ s,
+                                                  int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n; i += (int64_t)gridDim.x * kNT)
+    d[i] = s[i];
+}
+
+__global__ __launch_bounds__(kNT) void k_gather_i64(const int64_t* __restrict__ src,
+                                                    const int32_t* __restrict__ idx, int64_t n,
+                                                    int64_t* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n; i += (int64_t)gridDim.x * kNT)
+    dst[i] = src[idx[i]];
+}
+
+// ---- exclusive scan: tile sums, one-block scan of tile sums, down-sweep ----
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kNT * kScanItems;
+
+template <typename TIn>
+__global__ __launch_bounds__(kNT) void k_scan_reduce(const TIn* __restrict__ in, int64_t n,
+                                                     int64_t* __restrict__ tileSum) {
+  __shared__ int64_t wt[kNT / kWave];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile;
+  int64_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k * kNT + threadIdx.x;
+    if (i < n) s += (int64_t)in[i];
+  }
+  int64_t tot;
+  block_excl_scan<kNT>(s, wt, &tot);
+  if (threadIdx.x == 0) tileSum[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kNT) void k_scan_tiles(int64_t* __restrict__ t, int64_t nt) {
+  __shared__ int64_t wt[kNT / kWave];
+  int64_t carry = 0;
+  for (int64_t base = 0; base < nt; base += kNT) {
+    const int64_t i = base + threadIdx.x;
+    const int64_t x = i < nt ? t[i] : 0;
+    int64_t tot;
+    const int64_t ex = block_excl_scan<kNT>(x, wt, &tot);
+    if (i < nt) t[i] = carry + ex;
+    carry += tot;
+  }
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kNT) void k_scan_down(const TIn* __restrict__ in, int64_t n,
+                                                   const int64_t* __restrict__ tileOff,
+                                                   int64_t* __restrict__ out) {
+  __shared__ int64_t wt[kNT / kWave];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+  int64_t v[kScanItems];
+  int64_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    v[k] = i < n ? (int64_t)in[i] : 0;
+    s += v[k];
+  }
+  int64_t tot;
+  int64_t run = block_excl_scan<kNT>(s, wt, &tot) + tileOff[blockIdx.x];
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    const int64_t i = base + k;
+    if (i < n) out[i] = run;
+    run += v[k];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) out[n] = tileOff[blockIdx.x] + tot;
+}
+
+template <typename TIn>
+void scan_impl(const TIn* in, int64_t n, int64_t* out, int64_t* tmp, hipStream_t s) {
+  if (n <= 0) {
+    hipLaunchKernelGGL(k_fill<int64_t>, dim3(1), dim3(kNT), 0, s, out, (int64_t)0, (int64_t)1);
+    return;
+  }
+  const int64_t nt = cdiv(n, kScanTile);
+  hipLaunchKernelGGL(k_scan_reduce<TIn>, dim3((unsigned)nt), dim3(kNT), 0, s, in, n, tmp);
+  hipLaunchKernelGGL(k_scan_tiles, dim3(1), dim3(kNT), 0, s, tmp, nt);
+  hipLaunchKernelGGL(k_scan_down<TIn>, dim3((unsigned)nt), dim3(kNT), 0, s, in, n,
+                     (const int64_t*)tmp, out);
+}
+
+// ---- counting sort of item indices by an 8-bit bin key ----
+constexpr int kMaxBins = 64;
+
+__global__ __launch_bounds__(kNT) void k_bin_count(const uint8_t* __restrict__ key, int64_t n,
+                                                   int nbins, int32_t* __restrict__ cnt) {
+  __shared__ int32_t h[kMaxBins];
+  if (threadIdx.x < kMaxBins) h[threadIdx.x] = 0;
+  __syncthreads();
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n; i += (int64_t)gridDim.x * kNT) {
+    const int b = key[i];
+    if (b < nbins) atomicAdd(&h[b], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < nbins && h[threadIdx.x]) atomicAdd(&cnt[threadIdx.x], h[threadIdx.x]);
+}
+
+__global__ void k_bin_offsets(const int32_t* __restrict__ cnt, int nbins, int32_t* __restrict__ start,
+                              int32_t* __restrict__ fill) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    int32_t r = 0;
+    for (int b = 0; b < nbins; ++b) {
+      start[b] = r;
+      fill[b] = r;
+      r += cnt[b];
+    }
+    start[nbins] = r;
+  }
+}
+
+// One block per 4096 items: LDS histogram, one global atomic per bin for the
+// block's base, then per-item positions from LDS atomics.  Order inside a
+// bin is not preserved (the consumers do not depend on it).
+constexpr int kBinItems = 16;
+__global__ __launch_bounds__(kNT) void k_bin_scatter(const uint8_t* __restrict__ key, int64_t n,
+                                                     int nbins, int32_t* __restrict__ fill,
+                                                     int32_t* __restrict__ out) {
+  __shared__ int32_t h[kMaxBins];
+  __shared__ int32_t base[kMaxBins];
+  if (threadIdx.x < kMaxBins) h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t b0 = (int64_t)blockIdx.x * kNT * kBinItems;
+  uint8_t kk[kBinItems];
+#pragma unroll
+  for (int k = 0; k < kBinItems; ++k) {
+    const int64_t i = b0 + k * kNT + threadIdx.x;
+    kk[k] = i < n ? key[i] : (uint8_t)255;
+    if (kk[k] < nbins) atomicAdd(&h[kk[k]], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < nbins) {
+    const int32_t c = h[threadIdx.x];
+    base[threadIdx.x] = c ? atomicAdd(&fill[threadIdx.x], c) : 0;
+    h[threadIdx.x] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kBinItems; ++k) {
+    const int64_t i = b0 + k * kNT + threadIdx.x;
+    if (kk[k] < nbins) {
+      const int32_t r = atomicAdd(&h[kk[k]], 1);
+      out[base[kk[k]] + r] = (int32_t)i;
+    }
+  }
+}
+
+// ---- per-row intermediate products (InterOffsets) ----
+// A group of G lanes walks one row of A: for each entry k it reads
+// nnz(B[k,:]) from B.row_ptr, scans those counts across the group and
+// stores the row-local exclusive offset of every entry (the flattened
+// product index where that entry's scaled B row starts).  The row total is
+// P_i; its bin is 0 when P_i == 0, 1 + (first cap >= P_i) when P_i <= tau,
+// and nbins + 1 (heavy) otherwise.
+template <int G>
+__global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __restrict__ arp,
+                                                  const int32_t* __restrict__ acol,
+                                                  const int32_t* __restrict__ brp, int64_t tau,
+                                                  const int32_t* __restrict__ caps, int nbins,
+                                                  int64_t* __restrict__ rowP,
+                                                  int32_t* __restrict__ scanA,
+                                                  uint8_t* __restrict__ rowBin,
+                                                  int64_t* __restrict__ stats) {
+  __shared__ unsigned long long sP, sPh, sAh, sMax, sH, sL;
+  if (threadIdx.x == 0) sP = sPh = sAh = sMax = sH = sL = 0;
+  __syncthreads();
+  const int gl = threadIdx.x % G;
+  const int64_t row = ((int64_t)blockIdx.x * kNT + threadIdx.x) / G;
+  if (row < m) {
+    const int64_t rs = arp[row], re = arp[row + 1];
+    int64_t p = 0;
+    for (int64_t b = rs; b < re; b += G) {
+      const int64_t j = b + gl;
+      int64_t nb = 0;
+      if (j < re) {
+        const int32_t k = acol[j];
+        nb = (int64_t)brp[k + 1] - brp[k];
+      }
+      int64_t inc = nb;
+#pragma unroll
+      for (int d = 1; d < G; d <<= 1) {
+        const int64_t t = __shfl_up(inc, d, G);
+        if (gl >= d) inc += t;
+      }
+      if (j < re) scanA[j] = (int32_t)(p + inc - nb);
+      p += __shfl(inc, G - 1, G);
+    }
+    if (gl == 0) {
+      rowP[row] = p;
+      uint8_t bin;
+      if (p == 0) {
+        bin = 0;
+      } else if (p > tau) {
+        bin = (uint8_t)(nbins + 1);
+        atomicAdd(&sPh, (unsigned long long)p);
+        atomicAdd(&sAh, (unsigned long long)(re - rs));
+        atomicAdd(&sH, 1ull);
+      } else {
+        int b = 0;
+        while (b < nbins - 1 && p > caps[b]) ++b;
+        bin = (uint8_t)(1 + b);
+        atomicAdd(&sL, 1ull);
+      }
+      rowBin[row] = bin;
+      atomicAdd(&sP, (unsigned long long)p);
+      atomicMax(&sMax, (unsigned long long)p);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd((unsigned long long*)&stats[kStatProducts], sP);
+    atomicAdd((unsigned long long*)&stats[kStatHeavyProducts], sPh);
+    atomicAdd((unsigned long long*)&stats[kStatHeavyANnz], sAh);
+    atomicMax((unsigned long long*)&stats[kStatMaxRowProducts], sMax);
+    atomicAdd((unsigned long long*)&stats[kStatHeavyRows], sH);
+    atomicAdd((unsigned long long*)&stats[kStatLightRows], sL);
+  }
+}
+
+// ---- CSR validation: one thread per row ----
+__global__ __launch_bounds__(kNT) void k_validate(int64_t rows, int64_t cols, int64_t nnz,
+                                                  const int32_t* __restrict__ rp,
+                                                  const int32_t* __restrict__ col,
+                                                  int32_t* __restrict__ err) {
+  const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (i >= rows) return;
+  const int64_t a = rp[i], b = rp[i + 1];
+  bool ok = (a >= 0) && (b >= a) && (b <= nnz);
+  if (i == 0 && a != 0) ok = false;
+  if (i == rows - 1 && b != nnz) ok = false;
+  if (ok) {
+    int64_t prev = -1;
+    for (int64_t e = a; e < b; ++e) {
+      const int64_t c = col[e];
+      if (c < 0 || c >= cols || c <= prev) {
+        ok = false;
+        break;
+      }
+      prev = c;
+    }
+  }
+  if (!ok) flag_error(err, kErrCsr);
+}
+
+__global__ __launch_bounds__(kNT) void k_write_rowptr(const int64_t* __restrict__ off, int64_t n,
+                                                      void* __restrict__ out, int is64) {
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n; i += (int64_t)gridDim.x * kNT) {
+    if (is64)
+      ((int64_t*)out)[i] = off[i];
+    else
+      ((int32_t*)out)[i] = (int32_t)off[i];
+  }
+}
+
+__global__ __launch_bounds__(kNT) void k_numeric_row_bins(int64_t m, const int64_t* __restrict__ cnt,
+                                                          const uint8_t* __restrict__ rowBin,
+                                                          int heavyBin,
+                                                          const int32_t* __restrict__ caps,
+                                                          int nbins, uint8_t* __restrict__ key) {
+  const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (i >= m) return;
+  const int rb = rowBin[i];
+  if (rb == 0 || rb == heavyBin) {
+    key[i] = 255;
+    return;
+  }
+  const int64_t c = cnt[i];
+  int b = 0;
+  while (b < nbins - 1 && c > caps[b]) ++b;
+  key[i] = (uint8_t)b;
+}
+
+}  // namespace
+
+void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_fill<int32_t>, dim3(g), dim3(kNT), 0, s, p, v, n);
+}
+void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_fill<int64_t>, dim3(g), dim3(kNT), 0, s, p, v, n);
+}
+void launch_copy_i64(int64_t* dst, const int64_t* src, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_copy_i64, dim3(g), dim3(kNT), 0, s, dst, src, n);
+}
+void launch_gather_i64(const int64_t* src, const int32_t* idx, int64_t n, int64_t* dst,
+                       hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_gather_i64, dim3(g), dim3(kNT), 0, s, src, idx, n, dst);
+}
+
+int64_t scan_tmp_elems(int64_t n) { return cdiv(n > 0 ? n : 1, kScanTile); }
+
+void launch_scan_i64(const int64_t* in, int64_t n, int64_t* out, int64_t* tmp, hipStream_t s) {
+  scan_impl<int64_t>(in, n, out, tmp, s);
+}
+void launch_scan_i32(const int32_t* in, int64_t n, int64_t* out, int64_t* tmp, hipStream_t s) {
+  scan_impl<int32_t>(in, n, out, tmp, s);
+}
+
+void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int32_t* fill,
+                     int32_t* start, int32_t* out, hipStream_t s) {
+  launch_fill_i32(cnt, 0, nbins, s);
+  if (n > 0) {
+    unsigned g = grid_for(n, kNT * 4);
+    if (g > 65536) g = 65536;
+    hipLaunchKernelGGL(k_bin_count, dim3(g), dim3(kNT), 0, s, key, n, nbins, cnt);
+  }
+  hipLaunchKernelGGL(k_bin_offsets, dim3(1), dim3(64), 0, s, (const int32_t*)cnt, nbins, start,
+                     fill);
+  if (n > 0) {
+    hipLaunchKernelGGL(k_bin_scatter, dim3(grid_for(n, kNT * kBinItems)), dim3(kNT), 0, s, key,
+                       n, nbins, fill, out);
+  }
+}
+
+void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
+                     const int32_t* /*bcol*/, int64_t tau, const int32_t* caps, int nbins,
+                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* stats,
+                     hipStream_t s) {
+  if (m <= 0) return;
+  constexpr int G = 16;
+  hipLaunchKernelGGL(k_row_info<G>, dim3(grid_for(m * G, kNT)), dim3(kNT), 0, s, m, arp, acol,
+                     brp, tau, caps, nbins, rowP, scanA, rowBin, stats);
+}
+
+void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
+                     const int32_t* col, int32_t* err, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_validate, dim3(grid_for(rows, kNT)), dim3(kNT), 0, s, rows, cols, nnz, rp,
+                     col, err);
+}
+
+void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_write_rowptr, dim3(g), dim3(kNT), 0, s, off, n, out, is64);
+}
+
+void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,
+                             int heavyBin, const int32_t* caps, int nbins, uint8_t* key,
+                             hipStream_t s) {
+  if (m <= 0) return;
+  hipLaunchKernelGGL(k_numeric_row_bins, dim3(grid_for(m, kNT)), dim3(kNT), 0, s, m, cnt, rowBin,
+                     heavyBin, caps, nbins, key);
+}
+
+}  // namespace sg

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Structure (row_ptr and sorted col) must match exactly.  Values: integer-valued
+inputs must match exactly; otherwise |c - c_ref| <= rtol * sum_k |a_ik b_kj|
+per entry with rtol = 1e-12 (fp64) or 1e-5 (fp32).  The sum of |terms| is the
+scale that bounds the error of any summation order (for same-sign terms it
+equals |c_ref|).  Full-size configurations are checked on sampled rows, which
+the oracle computes one by one, and through properties that hold at any size.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import assert_csr_equal_structure, assert_values_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+sg = pytest.importorskip("spgemm_symbolic_row_amd")
+
+RTOL = {np.float64: 1e-12, np.float32: 1e-5}
+
+
+def _rtol(A, ref):
+    if A.val.dtype == np.float32:
+        # fp32 accumulation over t terms: at most about t * 2^-24 of the term
+        # magnitudes; the stated 1e-5 holds up to ~160 terms per entry.
+        return np.maximum(1e-5, ref.terms * 2.0 ** -24)
+    return 1e-12
+
+
+def _to_np(t, dtype=None):
+    a = t.detach().cpu().numpy()
+    return a.astype(dtype) if dtype is not None else a
+
+
+def gpu_product(A, B, **opts):
+    dA = sg.to_device(A)
+    dB = dA if B is A else sg.to_device(B)
+    with sg.Plan(dA, dB, **opts) as p:
+        rp, nnz = p.symbolic()
+        col, val = p.numeric()
+        st = p.stats()
+    torch.cuda.synchronize()
+    return _to_np(rp, np.int64), _to_np(col), _to_np(val), st
+
+
+def check_full(A, B, exact=False, **opts):
+    rp, col, val, st = gpu_product(A, B, **opts)
+    ref = oracle.spgemm(A, B)
+    assert_csr_equal_structure(rp, col, ref.row_ptr, ref.col, "C")
+    if exact:
+        np.testing.assert_array_equal(val, ref.val)
+    else:
+        assert_values_close(val, ref.val, ref.mag, _rtol(A, ref), "C")
+    assert st["global_products"] == 0
+    assert st["lds_hash_products"] + st["lds_dense_products"] == st["products"]
+    assert st["nnz_c"] == int(ref.row_ptr[-1])
+    return st
+
+
+# ------------------------------------------------------------ small shapes
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("m,k,n,per_row,seed", [
+    (1, 1, 1, 1.0, 0), (7, 5, 3, 2.0, 1), (64, 64, 64, 4.0, 3), (300, 200, 500, 6.0, 4),
+    (1000, 1, 1000, 0.7, 5), (50, 120, 7, 10.0, 6), (2000, 3000, 1500, 12.0, 7),
+])
+def test_small_random_exact(m, k, n, per_row, seed, dtype):
+    A = synth.random_csr(m, k, per_row, seed, values="int", empty_row_frac=0.2, dtype=dtype)
+    B = synth.random_csr(k, n, per_row, seed + 100, values="int", empty_row_frac=0.2, dtype=dtype)
+    check_full(A, B, exact=True)
+
+
+@pytest.mark.parametrize("case", ["m0", "k0", "nnz0", "single", "empty_b"])
+def test_degenerate(case):
+    if case == "m0":
+        A = synth.CSR(np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0), 0, 5)
+        B = synth.random_csr(5, 6, 2.0, 1)
+    elif case == "k0":
+        A = synth.CSR(np.zeros(4, np.int32), np.zeros(0, np.int32), np.zeros(0), 3, 0)
+        B = synth.CSR(np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0), 0, 6)
+    elif case == "nnz0":
+        A = synth.CSR(np.zeros(11, np.int32), np.zeros(0, np.int32), np.zeros(0), 10, 10)
+        B = synth.random_csr(10, 10, 3.0, 2)
+    elif case == "single":
+        A = synth.CSR(np.array([0, 1], np.int32), np.array([0], np.int32), np.array([2.0]), 1, 1)
+        B = synth.CSR(np.array([0, 1], np.int32), np.array([0], np.int32), np.array([3.0]), 1, 1)
+    else:
+        A = synth.random_csr(20, 30, 4.0, 3)
+        B = synth.CSR(np.zeros(31, np.int32), np.zeros(0, np.int32), np.zeros(0), 30, 9)
+    check_full(A, B, exact=True)
+
+
+def test_er4096_config():
+    A = synth.workload("er4096")
+    st = check_full(A, A)
+    assert st["heavy_rows"] == 0
+
+
+def test_uniform_values_fp64_and_fp32():
+    for dt in (np.float64, np.float32):
+        A = synth.random_csr(3000, 2500, 20.0, 11, values="uniform", dtype=dt)
+        B = synth.random_csr(2500, 4000, 30.0, 12, values="uniform", dtype=dt)
+        check_full(A, B)
+
+
+def test_wide_light_rows_all_bins():
+    # rows of 1..~6000 products exercise every light-row bin, with both hash
+    # sizes and sorts near their capacity
+    rng = np.random.default_rng(5)
+    m, k, n = 4000, 3000, 200000
+    A = synth.random_csr(m, k, 1.0, 13, values="int")
+    lens = np.minimum((2.0 ** rng.uniform(0, 12.5, size=m)).astype(int), k)
+    cols = [np.sort(rng.choice(k, size=int(c), replace=False)) for c in lens]
+    rp = np.zeros(m + 1, np.int64)
+    np.cumsum(lens, out=rp[1:])
+    A = synth.CSR(rp.astype(np.int32), np.concatenate(cols).astype(np.int32),
+                  rng.integers(-3, 4, size=int(rp[-1])).astype(np.float64), m, k)
+    B = synth.random_csr(k, n, 1.5, 14, values="int")
+    st = check_full(A, B, exact=True)
+    assert st["heavy_rows"] == 0 or st["heavy_products"] > 0
+
+
+# -------------------------------------------------- heavy path, forced sizes
+@pytest.mark.parametrize("scale,tau,W,nmax", [
+    (10, 64, 256, 32),     # one level, 4 chunks
+    (11, 64, 256, 4),      # two levels [4, 2]
+    (12, 32, 128, 2),      # five levels of 2
+    (12, 200, 1024, 64),   # one level, light and dense chunks
+    (11, 64, 2048, 32),    # one W-wide chunk: no multisplit
+])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_heavy_path_forced(scale, tau, W, nmax, dtype):
+    A = synth.rmat(scale, 16, seed=scale)
+    A.val = A.val.astype(dtype)
+    st = check_full(A, A, heavy_threshold=tau, dense_width=W, max_chunks_per_level=nmax)
+    assert st["heavy_rows"] > 0
+    nreq = max(1, 1 << int(np.ceil(np.log2(max(A.n / W, 1)))))
+    assert st["params"]["chunks_required"] == nreq
+    if nreq > 1:
+        assert st["level_elems"][0] == st["heavy_products"]
+
+
+def test_heavy_integer_exact_multilevel():
+    A = synth.rmat(12, 16, seed=21)
+    A.val = np.round(A.val * 6 - 3)   # small integers: any summation order is exact
+    check_full(A, A, exact=True, heavy_threshold=48, dense_width=256, max_chunks_per_level=4)
+
+
+def test_rectangular_heavy():
+    A = synth.random_csr(600, 400, 60.0, 31, values="int")
+    B = synth.random_csr(400, 5000, 80.0, 32, values="int")
+    check_full(A, B, exact=True, heavy_threshold=256, dense_width=512, max_chunks_per_level=4)
+
+
+def test_rmat14_default_parameters():
+    A = synth.rmat(14, 16, seed=0)
+    st = check_full(A, A)
+    assert st["params"]["tau"] == 6826
+
+
+def test_options_do_not_change_the_result():
+    A = synth.rmat(11, 16, seed=3)
+    A.val = np.round(A.val * 4 - 2)
+    ref = gpu_product(A, A, heavy_threshold=64, dense_width=256, max_chunks_per_level=4)
+    for opts in (dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, single_stream=1),
+                 dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, rowptr64=1),
+                 dict(heavy_threshold=100, dense_width=512, max_chunks_per_level=2),
+                 dict()):
+        rp, col, val, _ = gpu_product(A, A, **opts)
+        np.testing.assert_array_equal(rp, ref[0])
+        np.testing.assert_array_equal(col, ref[1])
+        np.testing.assert_array_equal(val, ref[2])
+
+
+def test_validate_rejects_non_canonical():
+    A = synth.random_csr(50, 50, 4.0, 1)
+    bad = synth.CSR(A.row_ptr.copy(), A.col.copy(), A.val.copy(), 50, 50)
+    r = int(np.nonzero(np.diff(bad.row_ptr) >= 2)[0][0])
+    a = bad.row_ptr[r]
+    bad.col[a], bad.col[a + 1] = bad.col[a + 1], bad.col[a]   # unsorted row, in range
+    with pytest.raises(sg.SpgemmError) as e:
+        gpu_product(bad, A, validate=1)
+    assert e.value.status == -2
+    check_full(A, A, exact=True, validate=1)
+
+
+# ------------------------------------------------------------ full configs
+def test_laplacian_config_exact():
+    A = synth.workload("lap27_64")
+    st = check_full(A, A, exact=True)
+    assert st["products"] == 566 ** 3 and st["nnz_c"] == 314 ** 3 and st["heavy_rows"] == 0
+
+
+def _sampled_check(A, rows, **opts):
+    dA = sg.to_device(A)
+    with sg.Plan(dA, dA, **opts) as p:
+        rp, nnz = p.symbolic()
+        col, val = p.numeric()
+        st = p.stats()
+    torch.cuda.synchronize()
+    rp_h = _to_np(rp, np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    lens = rp_h[rows + 1] - rp_h[rows]
+    idx = np.repeat(rp_h[rows] - np.concatenate([[0], np.cumsum(lens)[:-1]]), lens) + \
+        np.arange(int(lens.sum()))
+    it = torch.from_numpy(idx).to(col.device)
+    gcol, gval = _to_np(col[it]), _to_np(val[it])
+    ref = oracle.spgemm(A, A, rows=rows)
+    grp = np.zeros(rows.size + 1, np.int64)
+    np.cumsum(lens, out=grp[1:])
+    assert_csr_equal_structure(grp, gcol, ref.row_ptr, ref.col, "sampled rows")
+    assert_values_close(gval, ref.val, ref.mag, _rtol(A, ref), "sampled rows")
+    assert np.all(np.diff(rp_h) >= 0) and rp_h[0] == 0 and rp_h[-1] == nnz
+    return rp_h, st, (rp, col, val)
+
+
+def test_rmat18_config_sampled():
+    A = synth.workload("rmat18")
+    P = oracle.row_products(A, A)
+    rng = np.random.default_rng(1)
+    heavy = np.nonzero(P > 6826)[0]
+    light = np.nonzero((P > 0) & (P <= 6826))[0]
+    rows = np.unique(np.concatenate([np.arange(40), rng.choice(heavy, 300, replace=False),
+                                     rng.choice(light, 1500, replace=False),
+                                     np.nonzero(P == 0)[0][:20], [A.m - 1]]))
+    rp_h, st, _ = _sampled_check(A, rows)
+    assert st["heavy_rows"] == heavy.size and st["params"]["v_chunks"] == [16]
+    assert st["global_products"] == 0 and st["lds_dense_products"] > 0
+    # the whole row-pointer array against the oracle's symbolic counts
+    cnt = oracle.symbolic(A, A)
+    np.testing.assert_array_equal(np.diff(rp_h), cnt)
+
+
+def test_planted_partition_small_with_prune():
+    A = synth.planted_partition(100, 500, 28, 4, seed=3)
+    check_full(A, A)
+    dA = sg.to_device(A)
+    rp, col, val = sg.matmul(dA, dA)
+    orp, ocol, oval = sg.prune_colnorm(rp, col, val, A.m, A.n, 1e-4)
+    ref = oracle.spgemm(A, A)
+    # keep decisions in fp32 (the value type); entries within 1e-5 relative of
+    # the threshold may go either way, so adopt the GPU's decision there.
+    ref32 = ref.val.astype(np.float32)
+    band = np.abs(ref.val - 1e-4) <= 1e-5 * 1e-4
+    gval = _to_np(val).astype(np.float64)
+    keep = np.where(band, gval >= np.float32(1e-4), -1).astype(np.int8)
+    erp, ecol, evals = oracle.prune_colnorm(A.m, A.n, ref.row_ptr, ref.col, ref.val, 1e-4, keep=keep)
+    assert_csr_equal_structure(_to_np(orp, np.int64), _to_np(ocol), erp, ecol, "pruned")
+    np.testing.assert_allclose(_to_np(oval).astype(np.float64), evals, rtol=1e-5, atol=0)
+    # outside the band the keep decision is the oracle's fp32 comparison
+    assert np.array_equal(keep[~band] == -1, np.ones((~band).sum(), bool))
+    assert ecol.size == int(((ref32 >= np.float32(1e-4)) & ~band).sum() + (keep[band] == 1).sum())
+
+
+def test_mcl_config_sampled_and_prune_properties():
+    A = synth.workload("mcl1m")
+    rng = np.random.default_rng(2)
+    rows = np.unique(rng.choice(A.m, 1500, replace=False))
+    rp_h, st, (rp, col, val) = _sampled_check(A, rows)
+    assert st["heavy_rows"] == 0
+    # column sums of C = A^2 are 1 (A is column-stochastic)
+    cs = torch.zeros(A.n, dtype=torch.float64, device=col.device)
+    cs.index_add_(0, col.long(), val.double())
+    assert float((cs - 1).abs().max()) < 1e-5
+    orp, ocol, oval = sg.prune_colnorm(rp, col, val, A.m, A.n, 1e-4)
+    # every kept entry passed the threshold and every dropped one did not
+    kept_mask = val >= 1e-4
+    assert int(kept_mask.sum()) == ocol.numel()
+    np.testing.assert_array_equal(_to_np(ocol), _to_np(col[kept_mask]))
+    cs2 = torch.zeros(A.n, dtype=torch.float64, device=col.device)
+    cs2.index_add_(0, ocol.long(), oval.double())
+    nz = torch.bincount(ocol.long(), minlength=A.n) > 0
+    assert float((cs2[nz] - 1).abs().max()) < 1e-5
+    del rp, col, val, orp, ocol, oval
