@@ -1,0 +1,232 @@
+"""Throughput of C = A*A on one MI355X, with the roofline of the dominant
+kernel and the CPU oracle timed beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config rmat18]
+
+A step is one whole product: plan + symbolic + allocation of C + numeric
+(+ prune/renormalise for the Markov-clustering workload), inputs resident in
+HBM.  The metric is GFLOP/s with flops = 2 x intermediate products.  Prints
+one JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = {
+    "rmat18": "R-MAT scale 18 (262,144 rows), edge factor 16, (a,b,c,d)=(0.57,0.19,0.19,0.05), "
+              "duplicates merged, fp64 U[0,1], seed 0; C = A*A",
+    "rmat20": "R-MAT scale 20 (1,048,576 rows), edge factor 16, same (a,b,c,d), fp64; C = A*A",
+    "lap27_64": "27-point Laplacian on a 64^3 grid, fp64; C = A*A",
+    "er4096": "Erdos-Renyi 4096x4096, Poisson(8) per row, fp64 U[-1,1], seed 0; C = A*A",
+    "mcl1m": "planted partition 1000x1000, 28 intra + 4 inter + self per column, fp32 "
+             "column-stochastic; C = A*A, prune < 1e-4, renormalise columns",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(st, phase, sv, si=4):
+    """Algorithmic bytes moved by one launch of the given phase, and the
+    per-unit figure it is built from."""
+    L = st["params"]["levels"]
+    E = st["level_elems"]
+    if phase == "outer_product":
+        return st["heavy_products"] * (si + sv), f"{si + sv} B written per heavy product"
+    if phase == "multisplit":
+        return (sum(E) / max(L, 1)) * 2 * (si + sv), f"{2 * (si + sv)} B (read + write) per element per level"
+    if phase == "histogram":
+        return (sum(E) / max(L, 1)) * si, f"{si} B read per element per level"
+    if phase == "num_chunk_dense":
+        return st["lds_dense_products"] * (si + sv), f"{si + sv} B read per dense-chunk element"
+    if phase == "sym_chunk_dense":
+        return st["lds_dense_products"] * si, f"{si} B read per dense-chunk element"
+    return None, None
+
+
+def effective_bytes(A, st, sv, si=4):
+    """Frozen effective-byte denominator: compulsory traffic plus the heavy
+    intermediate that the method materialises (expand once, with values)."""
+    m, n, nnzA, nnzC = A.m, A.n, A.nnz, st["nnz_c"]
+    rp = 4
+    sym = 2 * ((m + 1) * rp + nnzA * si) + (m + 1) * rp
+    num = 2 * ((m + 1) * rp + nnzA * (si + sv)) + (m + 1) * rp + nnzC * (si + sv)
+    Ph = st["heavy_products"]
+    E = sum(st["level_elems"])
+    heavy = Ph * (si + sv) + E * (3 * si + 2 * sv) + Ph * (2 * si + sv)
+    return sym + num + heavy
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if digest != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(A, target_s=15.0):
+    """The oracle (as it stands) on a uniform random sample of rows."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(0)
+
+    def sub(frac):
+        rows = np.sort(rng.choice(A.m, max(1, int(A.m * frac)), replace=False))
+        rp = A.row_ptr.astype(np.int64)
+        lens = rp[rows + 1] - rp[rows]
+        nrp = np.zeros(rows.size + 1, np.int64)
+        np.cumsum(lens, out=nrp[1:])
+        idx = np.repeat(rp[rows] - nrp[:-1], lens) + np.arange(int(nrp[-1]))
+        import synth
+        return synth.CSR(nrp.astype(np.int32), A.col[idx], A.val[idx], rows.size, A.n), rows.size
+
+    def timed(S):
+        P = int(oracle.row_products(S, A).sum())
+        t0 = time.perf_counter()
+        oracle.spgemm(S, A)
+        return P, time.perf_counter() - t0
+
+    S, _ = sub(0.002)
+    P0, t0 = timed(S)
+    rate = P0 / max(t0, 1e-6)
+    P_all = int(oracle.row_products(A, A).sum())
+    frac = min(1.0, target_s * rate / max(P_all, 1))
+    S, nrows = sub(frac)
+    P, t = timed(S)
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
+    return {"value": round(2 * P / t / 1e9, 4), "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nrows} of {A.m} rows chosen uniformly at random (seed 0), "
+                      f"{P} intermediate products, {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="rmat18", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="do not time kernel phases with HIP events")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build is a single-GPU SpGEMM; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import spgemm_symbolic_row_amd as sg
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    t = time.time()
+    A = synth.workload(args.config)
+    log(f"generated {args.config}: {A.m} rows, nnz {A.nnz} in {time.time() - t:.1f} s")
+    dA = sg.to_device(A)
+    f64 = A.val.dtype == np.float64
+    sv = 8 if f64 else 4
+    opts = {} if args.no_profile else {"profile": 1}
+    mcl = args.config == "mcl1m"
+
+    def step():
+        with sg.Plan(dA, dA, **opts) as p:
+            rp, _ = p.symbolic()
+            col, val = p.numeric()
+            out = (rp, col, val)
+            if mcl:
+                out = sg.prune_colnorm(rp, col, val, A.m, A.n, 1e-4)
+            st = p.stats()
+        return out, st
+
+    for _ in range(args.warmup):
+        _, st = step()
+    torch.cuda.synchronize()
+    phase_tot = {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        _, st = step()
+        for k, v in st["phase_ms"].items():
+            phase_tot[k] = phase_tot.get(k, 0.0) + v
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    K = args.steps
+    P = st["products"]
+    value = 2.0 * P * K / dt / 1e9
+    ms = dt / K * 1e3
+    eff = effective_bytes(A, st, sv)
+    log(f"{ms:.3f} ms/step, {value:.2f} GFLOP/s, effective {eff / (dt / K) / 1e9:.1f} GB/s")
+    for k, v in sorted(phase_tot.items(), key=lambda kv: -kv[1]):
+        if v > 0:
+            log(f"  {k:18s} {v / K:9.3f} ms/step  windows/step {st['phase_windows'][k]}")
+
+    roof = None
+    if not args.no_profile:
+        cands = [k for k in ("multisplit", "outer_product", "num_chunk_dense", "histogram",
+                             "sym_chunk_dense") if phase_tot.get(k, 0) > 0]
+        if cands:
+            kern = max(cands, key=lambda k: phase_tot[k])
+            launches = st["phase_windows"][kern] * K
+            avg_ms = phase_tot[kern] / launches
+            byt, unit_desc = algorithmic_bytes(st, kern, sv)
+            achieved = byt / (avg_ms / 1e3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": traffic_for(kern, args.config), "kernel": kern,
+                    "avg_launch_ms": round(avg_ms, 4), "bytes_per_launch": int(byt),
+                    "per_unit": unit_desc}
+
+    line = {
+        "metric": "SpGEMM GFLOP/s (2x intermediate products) + % HBM roofline, 1 MI355X",
+        "value": round(value, 3), "unit": "GFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64" if f64 else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "rows": A.m, "nnz_a": A.nnz,
+                   "products": P, "nnz_c": st["nnz_c"], "heavy_rows": st["heavy_rows"],
+                   "heavy_products": st["heavy_products"],
+                   "v_chunks": st["params"]["v_chunks"], "tau": st["params"]["tau"],
+                   "effective_bytes": int(eff),
+                   "effective_gbps": round(eff / (dt / K) / 1e9, 1),
+                   "effective_frac": round(eff / (dt / K) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "lds_accumulated_frac": round((st["lds_hash_products"] + st["lds_dense_products"])
+                                                 / max(P, 1), 6),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    del dA
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(A)
+        log(f"cpu baseline: {line['cpu_baseline']}")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -72,6 +72,10 @@ typedef struct spgemm_options {
   int32_t rowptr64;             /* 1: C.row_ptr is int64, else int32            */
   int32_t validate;             /* 1: check A and B are canonical CSR           */
   int32_t single_stream;        /* 1: light and heavy work on the caller's stream */
+  int32_t profile;              /* 1: time each kernel phase with HIP events
+                                   recorded on the stream it runs on; read the
+                                   result from spgemm_stats.phase_ms           */
+  int32_t reserved32;
   spgemm_alloc_fn alloc;        /* optional allocator (see above)               */
   spgemm_free_fn free;
   void *alloc_ctx;
@@ -91,6 +95,23 @@ typedef struct spgemm_params {
   int64_t level_width[8];   /* column width of a chunk after each level       */
 } spgemm_params;
 
+/* Kernel phases timed when spgemm_options.profile is set. */
+typedef enum spgemm_phase {
+  SPGEMM_PH_ROW_INFO = 0,        /* products per row, light/heavy bins (plan)   */
+  SPGEMM_PH_SYM_LIGHT = 1,       /* light-row LDS hash symbolic                 */
+  SPGEMM_PH_CSC = 2,             /* masked CSR->CSC and segment reservations   */
+  SPGEMM_PH_OUTER_PRODUCT = 3,   /* C-hat expansion                             */
+  SPGEMM_PH_HISTOGRAM = 4,       /* per-level (row, chunk) counts               */
+  SPGEMM_PH_MULTISPLIT = 5,      /* per-level reorder into chunks              */
+  SPGEMM_PH_SYM_CHUNK_HASH = 6,  /* light-chunk hash symbolic                   */
+  SPGEMM_PH_SYM_CHUNK_DENSE = 7, /* heavy-chunk bitmap symbolic                 */
+  SPGEMM_PH_ROWPTR = 8,          /* C.row_ptr scan and numeric binning          */
+  SPGEMM_PH_NUM_LIGHT = 9,       /* light-row LDS hash numeric + sort           */
+  SPGEMM_PH_NUM_CHUNK_HASH = 10, /* light-chunk hash numeric + sort             */
+  SPGEMM_PH_NUM_CHUNK_DENSE = 11,/* heavy-chunk dense LDS numeric               */
+  SPGEMM_PH_COUNT = 12
+} spgemm_phase;
+
 typedef struct spgemm_stats {
   int64_t products;           /* P = sum_i sum_{k in A_i} nnz(B_k); flops = 2P */
   int64_t max_row_products;
@@ -108,6 +129,12 @@ typedef struct spgemm_stats {
   int64_t global_products;    /* products summed in global memory (always 0)   */
   int64_t batches;            /* heavy-row batches                             */
   double ms_plan, ms_symbolic, ms_numeric; /* host wall time of each call      */
+  double phase_ms[16];        /* GPU time of each spgemm_phase (with profile)  */
+  int32_t phase_windows[16];  /* event-bracketed windows summed in phase_ms;
+                                 a window holds one launch for the outer
+                                 product, histogram, multisplit and dense
+                                 phases (one per level for the per-level ones) */
+  int64_t device_errors;      /* device status bits seen (0 when all is well)  */
 } spgemm_stats;
 
 typedef struct spgemm_plan_s *spgemm_plan_t;

@@ -32,7 +32,8 @@ class Options(ctypes.Structure):
     _fields_ = [
         ("lds_budget", c_i64), ("heavy_threshold", c_i64), ("dense_width", c_i64),
         ("mem_budget", c_i64), ("max_chunks_per_level", c_i32), ("rowptr64", c_i32),
-        ("validate", c_i32), ("single_stream", c_i32), ("alloc", c_vp), ("free", c_vp),
+        ("validate", c_i32), ("single_stream", c_i32), ("profile", c_i32),
+        ("reserved32", c_i32), ("alloc", c_vp), ("free", c_vp),
         ("alloc_ctx", c_vp), ("reserved", c_i64 * 8),
     ]
 
@@ -60,15 +61,23 @@ class Stats(ctypes.Structure):
         ("final_chunks", c_i64), ("dense_chunks", c_i64), ("lds_hash_products", c_i64),
         ("lds_dense_products", c_i64), ("global_products", c_i64), ("batches", c_i64),
         ("ms_plan", ctypes.c_double), ("ms_symbolic", ctypes.c_double),
-        ("ms_numeric", ctypes.c_double),
+        ("ms_numeric", ctypes.c_double), ("phase_ms", ctypes.c_double * 16),
+        ("phase_windows", c_i32 * 16), ("device_errors", c_i64),
     ]
 
     def as_dict(self):
         d = {name: getattr(self, name) for name, _ in self._fields_
-             if name not in ("params", "level_elems")}
+             if name not in ("params", "level_elems", "phase_ms", "phase_windows")}
         d["params"] = self.params.as_dict()
         d["level_elems"] = list(self.level_elems[:self.params.levels])
+        d["phase_ms"] = {PHASES[i]: self.phase_ms[i] for i in range(len(PHASES))}
+        d["phase_windows"] = {PHASES[i]: self.phase_windows[i] for i in range(len(PHASES))}
         return d
+
+
+PHASES = ["row_info", "sym_light", "csc", "outer_product", "histogram", "multisplit",
+          "sym_chunk_hash", "sym_chunk_dense", "rowptr", "num_light", "num_chunk_hash",
+          "num_chunk_dense"]
 
 
 SPGEMM_F32, SPGEMM_F64 = 0, 1

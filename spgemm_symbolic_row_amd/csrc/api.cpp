@@ -18,6 +18,7 @@
 #include <chrono>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -112,6 +113,72 @@ void make_bins(int64_t tau, int64_t lds, int val_bytes, std::vector<BinCfg>* sym
   }
 }
 
+// Light-chunk numeric bins for the bitmap-rank accumulator: the same caps
+// as make_bins, tables sized to leave room for the chunk-width bitmap and
+// its word prefix.
+void make_rank_bins(int64_t lds, bool f64, int32_t words, const std::vector<BinCfg>& sym,
+                    std::vector<BinCfg>* out) {
+  for (const BinCfg& s : sym) {
+    BinCfg b = s;
+    int64_t T = std::max<int64_t>(next_pow2(2 * (int64_t)s.cap), s.tpr);
+    while (T > s.cap + 1 && (int64_t)rank_chunk_lds(f64, (int32_t)T, words, s.rpb) > lds)
+      T = T * 15 / 16;
+    if ((int64_t)rank_chunk_lds(f64, (int32_t)T, words, s.rpb) > lds || T <= s.cap)
+      throw Error{SPGEMM_ERR_INVALID_ARG, "chunk hash table does not fit the LDS budget"};
+    b.T = (int32_t)T;
+    b.lds = rank_chunk_lds(f64, b.T, words, s.rpb);
+    out->push_back(b);
+  }
+}
+
+// Side streams for the light and heavy work, one pair per device, created on
+// first use and kept for the life of the process: workspace freed on a side
+// stream is then reused by the next product's allocations on it.
+struct SideStreams {
+  hipStream_t sl = nullptr, sh = nullptr;
+};
+SideStreams side_streams(int device) {
+  static SideStreams pool[64];
+  SideStreams& ss = pool[device & 63];
+  if (!ss.sl) {
+    HIP_CHECK(hipStreamCreateWithFlags(&ss.sl, hipStreamNonBlocking));
+    HIP_CHECK(hipStreamCreateWithFlags(&ss.sh, hipStreamNonBlocking));
+  }
+  return ss;
+}
+
+// Per-device workspace arena.  One plan at a time bump-allocates from a
+// single device block that persists across products, so repeated products
+// of similar size allocate nothing.  The block grows (between plans) to the
+// largest workspace demand seen.  A plan that finds the arena busy, or runs
+// out of it, falls back to stream-ordered allocation.  `done` is recorded on
+// the last user's stream after all its streams joined; the next user's
+// stream waits for it before touching the memory.
+struct Arena {
+  std::mutex mu;
+  char* base = nullptr;
+  size_t cap = 0;
+  size_t highWater = 0;
+  bool busy = false;
+  hipEvent_t done = nullptr;
+  bool doneValid = false;
+};
+Arena g_arena[64];
+
+// Small pinned host buffers for readbacks, one set per host thread.
+struct Pinned {
+  int64_t* stats = nullptr;  // 32 entries
+  int32_t* bins = nullptr;   // 128 entries
+};
+Pinned& pinned() {
+  thread_local Pinned pb;
+  if (!pb.stats) {
+    HIP_CHECK(hipHostMalloc((void**)&pb.stats, sizeof(int64_t) * 32, hipHostMallocDefault));
+    HIP_CHECK(hipHostMalloc((void**)&pb.bins, sizeof(int32_t) * 128, hipHostMallocDefault));
+  }
+  return pb;
+}
+
 }  // namespace
 
 struct spgemm_plan_s {
@@ -128,8 +195,13 @@ struct spgemm_plan_s {
   spgemm_params params{};
   int state = 0;  // 0 planned, 1 symbolic done, 2 numeric done, -1 failed
   std::string err;
-  std::vector<void*> allocs;
-  std::vector<BinCfg> symBins, numBins;
+  std::vector<std::pair<void*, hipStream_t>> allocs;
+  Arena* arena = nullptr;   // held from plan to destroy, or null
+  size_t arenaUsed = 0, demand = 0;
+  std::vector<BinCfg> symBins, numBins, rankBins;
+  int32_t chunkWords = 0;  // bitmap words of the widest final chunk (0: hash fallback)
+  int32_t* fcOrderSym = nullptr;
+  std::vector<int32_t> fcSymStart;
   int NS = 0;  // number of hash bins
   // device arrays
   int32_t *dSymCaps = nullptr;
@@ -155,6 +227,11 @@ struct spgemm_plan_s {
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
   spgemm_stats st{};
+  struct PhaseRec {
+    int id;
+    hipEvent_t a, b;
+  };
+  std::vector<PhaseRec> phases;
 };
 
 namespace {
@@ -162,6 +239,12 @@ namespace {
 void* plan_alloc(spgemm_plan_t p, size_t bytes, hipStream_t s) {
   if (bytes == 0) bytes = 16;
   bytes = (bytes + 255) & ~size_t(255);
+  p->demand += bytes;
+  if (p->arena && p->arenaUsed + bytes <= p->arena->cap) {
+    void* ptr = p->arena->base + p->arenaUsed;
+    p->arenaUsed += bytes;
+    return ptr;
+  }
   void* ptr = nullptr;
   if (p->opts.alloc) {
     ptr = p->opts.alloc(bytes, (void*)s, p->opts.alloc_ctx);
@@ -171,7 +254,7 @@ void* plan_alloc(spgemm_plan_t p, size_t bytes, hipStream_t s) {
   }
   if (!ptr)
     throw Error{SPGEMM_ERR_OOM, "device allocation of " + std::to_string(bytes) + " bytes failed"};
-  p->allocs.push_back(ptr);
+  p->allocs.push_back({ptr, s});
   return ptr;
 }
 template <typename T>
@@ -179,15 +262,83 @@ T* alloc_n(spgemm_plan_t p, int64_t n, hipStream_t s) {
   return (T*)plan_alloc(p, (size_t)std::max<int64_t>(n, 1) * sizeof(T), s);
 }
 
+// Frees every workspace buffer on the stream that allocated it.  Callers
+// first make the caller's stream and both side streams wait for each other.
 void release(spgemm_plan_t p) {
-  for (void* ptr : p->allocs) {
+  for (auto& a : p->allocs) {
     if (p->opts.alloc) {
-      if (p->opts.free) p->opts.free(ptr, (void*)p->stream, p->opts.alloc_ctx);
+      if (p->opts.free) p->opts.free(a.first, (void*)a.second, p->opts.alloc_ctx);
     } else {
-      (void)hipFreeAsync(ptr, p->stream);
+      (void)hipFreeAsync(a.first, a.second);
     }
   }
   p->allocs.clear();
+}
+
+// Optional GPU timing of kernel phases: an event pair recorded on the
+// stream the phase's kernels are launched on.
+int ph_begin(spgemm_plan_t p, int id, hipStream_t s) {
+  if (!p->opts.profile) return -1;
+  spgemm_plan_s::PhaseRec r{id, nullptr, nullptr};
+  HIP_CHECK(hipEventCreate(&r.a));
+  HIP_CHECK(hipEventCreate(&r.b));
+  p->phases.push_back(r);
+  HIP_CHECK(hipEventRecord(r.a, s));
+  return (int)p->phases.size() - 1;
+}
+void ph_end(spgemm_plan_t p, int idx, hipStream_t s) {
+  if (idx < 0) return;
+  HIP_CHECK(hipEventRecord(p->phases[idx].b, s));
+}
+void ph_collect(spgemm_plan_t p) {
+  for (int i = 0; i < 16; ++i) {
+    p->st.phase_ms[i] = 0;
+    p->st.phase_windows[i] = 0;
+  }
+  for (auto& r : p->phases) {
+    HIP_CHECK(hipEventSynchronize(r.b));
+    float ms = 0;
+    HIP_CHECK(hipEventElapsedTime(&ms, r.a, r.b));
+    p->st.phase_ms[r.id] += ms;
+    p->st.phase_windows[r.id] += 1;
+  }
+}
+
+// Take the device's arena if it is free, growing it to the largest demand
+// seen so far.  The plan's stream waits for the previous user to finish.
+void arena_acquire(spgemm_plan_t p) {
+  if (p->opts.alloc) return;
+  Arena& a = g_arena[p->device & 63];
+  std::lock_guard<std::mutex> lk(a.mu);
+  if (a.busy) return;
+  if (a.cap < a.highWater) {
+    if (a.doneValid) HIP_CHECK(hipEventSynchronize(a.done));
+    if (a.base) HIP_CHECK(hipFree(a.base));
+    a.base = nullptr;
+    a.cap = 0;
+    if (hipMalloc((void**)&a.base, a.highWater) == hipSuccess) {
+      a.cap = a.highWater;
+    } else {
+      (void)hipGetLastError();
+      a.base = nullptr;
+    }
+  }
+  if (!a.done) HIP_CHECK(hipEventCreateWithFlags(&a.done, hipEventDisableTiming));
+  if (a.doneValid) HIP_CHECK(hipStreamWaitEvent(p->stream, a.done, 0));
+  a.busy = true;
+  p->arena = &a;
+}
+
+// Give the arena back: called after the plan's streams have joined into
+// the caller's stream, so `done` covers all of the plan's work.
+void arena_release(spgemm_plan_t p) {
+  if (!p->arena) return;
+  Arena& a = *p->arena;
+  std::lock_guard<std::mutex> lk(a.mu);
+  a.highWater = std::max(a.highWater, p->demand);
+  if (hipEventRecord(a.done, p->stream) == hipSuccess) a.doneValid = true;
+  a.busy = false;
+  p->arena = nullptr;
 }
 
 void fork(spgemm_plan_t p) {
@@ -254,6 +405,7 @@ void do_plan(spgemm_plan_t p) {
   if (!attrs) {
     light_set_attributes();
     heavy_set_attributes();
+    chunks_set_attributes();
     attrs = true;
   }
   if (!p->opts.alloc) {
@@ -274,14 +426,16 @@ void do_plan(spgemm_plan_t p) {
   if (p->opts.single_stream) {
     p->sl = p->sh = p->stream;
   } else {
-    HIP_CHECK(hipStreamCreateWithFlags(&p->sl, hipStreamNonBlocking));
-    HIP_CHECK(hipStreamCreateWithFlags(&p->sh, hipStreamNonBlocking));
+    const SideStreams ss = side_streams(p->device);
+    p->sl = ss.sl;
+    p->sh = ss.sh;
     HIP_CHECK(hipEventCreateWithFlags(&p->evFork, hipEventDisableTiming));
     HIP_CHECK(hipEventCreateWithFlags(&p->evL, hipEventDisableTiming));
     HIP_CHECK(hipEventCreateWithFlags(&p->evH, hipEventDisableTiming));
   }
-  HIP_CHECK(hipHostMalloc((void**)&p->hStats, sizeof(int64_t) * 32, hipHostMallocDefault));
-  HIP_CHECK(hipHostMalloc((void**)&p->hBins, sizeof(int32_t) * 128, hipHostMallocDefault));
+  p->hStats = pinned().stats;
+  p->hBins = pinned().bins;
+  arena_acquire(p);
 
   hipStream_t s = p->stream;
   const int64_t m = p->m;
@@ -314,10 +468,12 @@ void do_plan(spgemm_plan_t p) {
   p->binFill = alloc_n<int32_t>(p, 64, s);
   p->binStart = alloc_n<int32_t>(p, 65, s);
   launch_fill_i64(p->cnt, 0, m, s);
+  const int ph = ph_begin(p, SPGEMM_PH_ROW_INFO, s);
   launch_row_info(m, p->arp, p->acol, p->brp, p->bcol, p->tau, p->dSymCaps, p->NS, p->rowP,
                   p->scanA, p->rowBin, p->stats, s);
   const int nkeys = p->NS + 2;  // 0 empty, 1..NS hash bins, NS+1 heavy
   launch_bin_sort(p->rowBin, m, nkeys, p->binCnt, p->binFill, p->binStart, p->rowOrder, s);
+  ph_end(p, ph, s);
   check_launch("plan kernels");
   HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (nkeys + 1), hipMemcpyDeviceToHost, s));
@@ -344,6 +500,7 @@ void heavy_symbolic(spgemm_plan_t p) {
   const size_t vb = f64 ? 8 : 4;
   const int64_t W = p->params.dense_width;
   int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(std::max<int64_t>({h, nE, p->k, 1}) + 1), s);
+  const int phCsc = ph_begin(p, SPGEMM_PH_CSC, s);
 
   // C-hat row pointers: scan of the heavy rows' product counts.
   int64_t* hP = alloc_n<int64_t>(p, h, s);
@@ -373,6 +530,7 @@ void heavy_symbolic(spgemm_plan_t p) {
   launch_scan_i64(nb, nE, entryOff, tmp, s);
   launch_copy_i64(cursor, chatRowPtr, h, s);
   launch_seg_base(nE, cscRow, nb, cursor, segBase, s);
+  ph_end(p, phCsc, s);
 
   // Outer product into buffer 0.
   const int L = p->params.levels;
@@ -382,8 +540,10 @@ void heavy_symbolic(spgemm_plan_t p) {
     p->bufCol[1] = alloc_n<int32_t>(p, Ph, s);
     p->bufVal[1] = plan_alloc(p, std::max<int64_t>(Ph, 1) * vb, s);
   }
+  const int phOp = ph_begin(p, SPGEMM_PH_OUTER_PRODUCT, s);
   launch_outer_product(f64, Ph, entryOff, nE, cscCol, cscVal, segBase, p->brp, p->bcol, p->bval,
                        p->bufCol[0], p->bufVal[0], s);
+  ph_end(p, phOp, s);
   check_launch("outer product");
 
   struct Piece {
@@ -421,16 +581,20 @@ void heavy_symbolic(spgemm_plan_t p) {
     int32_t blockElems;
     int maxRows;
     multisplit_geometry(f64, p->tau, v, &blockElems, &maxRows);
+    const int phH = ph_begin(p, SPGEMM_PH_HISTOGRAM, s);
     launch_histogram(E, blockElems, rowPtr, R, p->bufCol[cur], shift, v, maxRows, counts,
                      p->errWord, s);
+    ph_end(p, phH, s);
     launch_partition(Q, counts, p->tau, last, v, inRow, inSlot, (int32_t)(w / W), inv, newCnt,
                      newRow, newSlot, ctr, s);
     launch_scan_i32(newCnt, Q, newOff, ltmp, s);
     launch_copy_i64(cur64, newOff, Q, s);
     const int out = 1 - cur;
+    const int phM = ph_begin(p, SPGEMM_PH_MULTISPLIT, s);
     launch_multisplit(f64, E, blockElems, rowPtr, R, p->bufCol[cur], p->bufVal[cur], shift, v,
                       (int32_t)(w - 1), maxRows, inv, cur64, p->bufCol[out], p->bufVal[out],
                       p->errWord, s);
+    ph_end(p, phM, s);
     check_launch("multisplit level");
     HIP_CHECK(hipMemcpyAsync(p->hBins + 100, ctr, 8, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
@@ -492,14 +656,44 @@ void heavy_symbolic(spgemm_plan_t p) {
   launch_fill_i32(p->slotNnz, 0, h * p->nreq, s);
   ChunkList cl{p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, p->bufCol[0], p->bufCol[1],
                p->bufVal[0], p->bufVal[1], W, p->nreq, p->xheavy, p->slotOff, p->slotNnz};
-  for (int b = 0; b < p->NS; ++b) {
-    const int64_t a = p->fcBinStart[b], e = p->fcBinStart[b + 1];
-    launch_sym_chunks(p->symBins[b], p->fcOrder + a, e - a, cl, p->errWord, s);
-  }
-  {
+  p->st.dense_chunks = p->fcBinStart[p->NS + 1] - p->fcBinStart[p->NS];
+  // Widest final chunk: the first level's width (or W with no multisplit).
+  const int64_t maxWidth = L == 0 ? W : p->params.level_width[0];
+  if (maxWidth <= 65536) {
+    // Bitmap symbolic for every chunk, in three size classes.
+    p->chunkWords = (int32_t)((maxWidth + 31) / 32);
+    make_rank_bins(p->lds, f64, p->chunkWords, p->symBins, &p->rankBins);
+    uint8_t* skey = alloc_n<uint8_t>(p, nfc, s);
+    p->fcOrderSym = alloc_n<int32_t>(p, nfc, s);
+    int32_t* sc = alloc_n<int32_t>(p, 64, s);
+    int32_t* sf = alloc_n<int32_t>(p, 64, s);
+    int32_t* ss = alloc_n<int32_t>(p, 65, s);
+    int32_t* dcc = alloc_n<int32_t>(p, 4, s);
+    const int32_t classCaps[3] = {256, 4096, INT32_MAX};
+    std::memcpy(p->hBins + 110, classCaps, sizeof(classCaps));
+    HIP_CHECK(hipMemcpyAsync(dcc, p->hBins + 110, sizeof(classCaps), hipMemcpyHostToDevice, s));
+    launch_chunk_bins(nfc, p->fcCnt, nfc, INT32_MAX, dcc, 3, 3, skey, nullptr, s);
+    launch_bin_sort(skey, nfc, 3, sc, sf, ss, p->fcOrderSym, s);
+    HIP_CHECK(hipMemcpyAsync(p->hBins + 104, ss, sizeof(int32_t) * 4, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    p->fcSymStart.assign(p->hBins + 104, p->hBins + 108);
+    const int phSc = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
+    for (int c = 0; c < 3; ++c) {
+      const int64_t a = p->fcSymStart[c], e = p->fcSymStart[c + 1];
+      launch_sym_chunks_bitmap(c, p->fcOrderSym + a, e - a, p->chunkWords, cl, s);
+    }
+    ph_end(p, phSc, s);
+  } else {
+    const int phSc = ph_begin(p, SPGEMM_PH_SYM_CHUNK_HASH, s);
+    for (int b = 0; b < p->NS; ++b) {
+      const int64_t a = p->fcBinStart[b], e = p->fcBinStart[b + 1];
+      launch_sym_chunks(p->symBins[b], p->fcOrder + a, e - a, cl, p->errWord, s);
+    }
+    ph_end(p, phSc, s);
     const int64_t a = p->fcBinStart[p->NS], e = p->fcBinStart[p->NS + 1];
+    const int phSd = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
     launch_dense_sym(p->fcOrder + a, e - a, cl, p->errWord, s);
-    p->st.dense_chunks = e - a;
+    ph_end(p, phSd, s);
   }
   launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
   check_launch("heavy symbolic");
@@ -511,10 +705,12 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   hipStream_t s = p->stream;
   fork(p);
   const RowArgs a = row_args(p);
+  const int phL = ph_begin(p, SPGEMM_PH_SYM_LIGHT, p->sl);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
     launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
   }
+  ph_end(p, phL, p->sl);
   check_launch("light symbolic");
   if (p->h > 0) heavy_symbolic(p);
   join(p);
@@ -522,12 +718,13 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   const int64_t m = p->m;
   p->cRowOff = alloc_n<int64_t>(p, m + 1, s);
   p->scanTmp = alloc_n<int64_t>(p, scan_tmp_elems(m) + 1, s);
-  launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
-  std::vector<int32_t> caps(p->NS);
   p->numKey = alloc_n<uint8_t>(p, m, s);
   p->numOrder = alloc_n<int32_t>(p, m, s);
+  const int phR = ph_begin(p, SPGEMM_PH_ROWPTR, s);
+  launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
   launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s);
   launch_bin_sort(p->numKey, m, p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
+  ph_end(p, phR, s);
   check_launch("row pointer scan");
   HIP_CHECK(hipMemcpyAsync(p->hStats + 20, p->cRowOff + m, 8, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (p->NS + 1), hipMemcpyDeviceToHost, s));
@@ -554,24 +751,34 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   const double t0 = now_ms();
   fork(p);
   const RowArgs a = row_args(p);
+  const int phL = ph_begin(p, SPGEMM_PH_NUM_LIGHT, p->sl);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = p->numBinStart[b], en = p->numBinStart[b + 1];
     launch_num_rows(p->numBins[b], p->f64, p->numOrder + st, en - st, a, p->cRowOff, ccol, cval,
                     p->errWord, p->sl);
   }
+  ph_end(p, phL, p->sl);
   check_launch("light numeric");
   if (p->h > 0) {
     hipStream_t s = p->sh;
     ChunkList cl{p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, p->bufCol[0], p->bufCol[1],
                  p->bufVal[0], p->bufVal[1], p->params.dense_width, p->nreq, p->xheavy,
                  p->slotOff, p->slotNnz};
+    const int phH = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
     for (int b = 0; b < p->NS; ++b) {
       const int64_t st = p->fcBinStart[b], en = p->fcBinStart[b + 1];
-      launch_num_chunks(p->numBins[b], p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol,
-                        cval, p->errWord, s);
+      if (p->chunkWords)
+        launch_num_chunks_rank(p->rankBins[b], p->f64, p->fcOrder + st, en - st, p->chunkWords,
+                               cl, p->cRowOff, ccol, cval, p->errWord, s);
+      else
+        launch_num_chunks(p->numBins[b], p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol,
+                          cval, p->errWord, s);
     }
+    ph_end(p, phH, s);
     const int64_t st = p->fcBinStart[p->NS], en = p->fcBinStart[p->NS + 1];
+    const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
     launch_dense_num(p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord, s);
+    ph_end(p, phD, s);
     check_launch("heavy numeric");
   }
   join(p);
@@ -602,25 +809,29 @@ spgemm_status guarded(spgemm_plan_t p, F&& f) {
 
 void destroy_plan(spgemm_plan_t p) {
   if (!p) return;
-  if (p->sl && p->sl != p->stream) {
+  if (p->sl && p->sl != p->stream && p->evL) {
+    // Every stream waits for every other before any buffer is freed, so a
+    // free on one stream never overtakes a use on another.
     (void)hipEventRecord(p->evL, p->sl);
     (void)hipEventRecord(p->evH, p->sh);
+    (void)hipEventRecord(p->evFork, p->stream);
     (void)hipStreamWaitEvent(p->stream, p->evL, 0);
     (void)hipStreamWaitEvent(p->stream, p->evH, 0);
+    (void)hipStreamWaitEvent(p->sl, p->evH, 0);
+    (void)hipStreamWaitEvent(p->sl, p->evFork, 0);
+    (void)hipStreamWaitEvent(p->sh, p->evL, 0);
+    (void)hipStreamWaitEvent(p->sh, p->evFork, 0);
   }
+  arena_release(p);
   release(p);
-  if (p->sl && p->sl != p->stream) {
-    (void)hipStreamSynchronize(p->sl);
-    (void)hipStreamSynchronize(p->sh);
-    (void)hipStreamDestroy(p->sl);
-    (void)hipStreamDestroy(p->sh);
-    (void)hipEventDestroy(p->evFork);
-    (void)hipEventDestroy(p->evL);
-    (void)hipEventDestroy(p->evH);
+  if (!p->phases.empty()) (void)hipStreamSynchronize(p->stream);
+  for (auto& r : p->phases) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
-  if (p->hStats || p->hBins) (void)hipStreamSynchronize(p->stream);
-  if (p->hStats) (void)hipHostFree(p->hStats);
-  if (p->hBins) (void)hipHostFree(p->hBins);
+  if (p->evFork) (void)hipEventDestroy(p->evFork);
+  if (p->evL) (void)hipEventDestroy(p->evL);
+  if (p->evH) (void)hipEventDestroy(p->evH);
   delete p;
 }
 
@@ -703,7 +914,12 @@ spgemm_status spgemm_numeric(spgemm_plan_t p, int32_t* dC_col, void* dC_val) {
 spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats* out) {
   if (!p || !out) return SPGEMM_ERR_INVALID_ARG;
   spgemm_status st = guarded(p, [&] {
-    if (p->state >= 1) check_device_errors(p, read_err(p, p->stream));
+    if (p->state >= 1) {
+      const int32_t word = read_err(p, p->stream);
+      p->st.device_errors = word;
+      if (p->opts.profile) ph_collect(p);
+      check_device_errors(p, word);
+    }
   });
   *out = p->st;
   return st;

@@ -173,6 +173,16 @@ size_t dense_num_lds(bool f64, int64_t W);
 void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,
                       const int32_t* xheavy, int64_t* cnt, hipStream_t s);
 
+// ---- k_chunks.hip ----
+void chunks_set_attributes();
+size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb);
+// sizeClass 0: chunks of <= 256 elements (4 per work group), 1: <= 4096, 2: larger.
+void launch_sym_chunks_bitmap(int sizeClass, const int32_t* items, int64_t n, int32_t words,
+                              const ChunkList& cl, hipStream_t s);
+void launch_num_chunks_rank(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
+                            int32_t words, const ChunkList& cl, const int64_t* cRowOff,
+                            int32_t* ccol, void* cval, int32_t* err, hipStream_t s);
+
 // ---- k_prune.hip ----
 void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
                         bool f64, double thr, int64_t* keepCnt, double* colsum,

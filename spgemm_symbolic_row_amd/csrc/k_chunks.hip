@@ -1,0 +1,227 @@
+// Accumulation of the final chunks of the heavy rows (gMAGNUS page, §III-E),
+// exploiting that a chunk's local columns lie in [0, width) with width a
+// power of two no larger than a few tens of thousands:
+//
+//   symbolic: an LDS bitmap of `width` bits per chunk; each element sets its
+//             column's bit (reading first, so repeats cost a read only); the
+//             chunk's nnz is the bitmap's popcount.
+//   numeric (light chunks): an LDS hash of (column, value) with LDS atomic
+//             adds; a new key also sets its column's bit.  A prefix popcount
+//             over the bitmap words then gives every occupied slot its rank
+//             among the chunk's columns, i.e. its position in the sorted
+//             output, so no sort is needed.
+// Heavy W-wide chunks use the dense accumulator in k_heavy.hip.
+#include "device_common.hpp"
+
+namespace sg {
+namespace {
+
+template <int TPC, int CPB>
+__global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const int32_t* __restrict__ items,
+                                                                int64_t n, int32_t words,
+                                                                ChunkList cl) {
+  extern __shared__ __align__(16) uint32_t bmAll[];
+  __shared__ int32_t gsum[CPB * (TPC / kWave)];
+  const int g = threadIdx.x / TPC, t = threadIdx.x % TPC;
+  uint32_t* bm = bmAll + g * words;
+  for (int i = t; i < words; i += TPC) bm[i] = 0;
+  __syncthreads();
+  const int64_t ci = (int64_t)blockIdx.x * CPB + g;
+  int32_t item = 0;
+  if (ci < n) {
+    item = items[ci];
+    const int64_t off = cl.off[item], end = off + cl.cnt[item];
+    const int32_t* __restrict__ col = cl.buf[item] ? cl.col1 : cl.col0;
+    for (int64_t e = off + t; e < end; e += TPC) {
+      const int32_t c = col[e];
+      const uint32_t bit = 1u << (c & 31);
+      if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+    }
+  }
+  __syncthreads();
+  int32_t mine = 0;
+  for (int i = t; i < words; i += TPC) mine += __popc(bm[i]);
+  mine = wave_sum(mine);
+  if (lane_id() == 0) gsum[threadIdx.x / kWave] = mine;
+  __syncthreads();
+  if (t == 0 && ci < n) {
+    int32_t tot = 0;
+    for (int i = 0; i < TPC / kWave; ++i) tot += gsum[g * (TPC / kWave) + i];
+    cl.slotNnz[(int64_t)cl.row[item] * cl.nreq + cl.slot[item]] = tot;
+  }
+}
+
+template <typename V>
+__device__ __forceinline__ void hmap_add_mark(int32_t* keys, V* vals, uint32_t* bm, uint32_t T,
+                                              int32_t key, V v, int32_t* err) {
+  uint32_t s = hash_slot(key, T);
+  for (uint32_t probe = 0; probe < T; ++probe) {
+    const int32_t cur = lds_load_relaxed(&keys[s]);
+    if (cur == key) {
+      atomicAdd(&vals[s], v);
+      return;
+    }
+    if (cur == kEmptyKey) {
+      const int32_t old = atomicCAS(&keys[s], kEmptyKey, key);
+      if (old == kEmptyKey) atomicOr(&bm[key >> 5], 1u << (key & 31));
+      if (old == kEmptyKey || old == key) {
+        atomicAdd(&vals[s], v);
+        return;
+      }
+    }
+    s = (s + 1 == T) ? 0 : s + 1;
+  }
+  flag_error(err, kErrHashFull);
+}
+
+// LDS per chunk group: vals[T], keys[T], bitmap[words], word prefix[words].
+template <typename V>
+__host__ __device__ constexpr size_t rank_group_bytes(int32_t T, int32_t words) {
+  return (size_t)T * sizeof(V) + (size_t)T * 4 + (size_t)words * 8;
+}
+
+template <int TPC, int CPB, typename V>
+__global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const int32_t* __restrict__ items,
+                                                              int64_t n, int32_t T, int32_t words,
+                                                              ChunkList cl,
+                                                              const int64_t* __restrict__ cRowOff,
+                                                              int32_t* __restrict__ ccol,
+                                                              V* __restrict__ cval,
+                                                              int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int WPG = TPC / kWave;
+  __shared__ int32_t wtot[CPB * WPG];
+  const int g = threadIdx.x / TPC, t = threadIdx.x % TPC, w = t / kWave;
+  unsigned char* base = smem + (size_t)g * rank_group_bytes<V>(T, words);
+  V* vals = (V*)base;
+  int32_t* keys = (int32_t*)(vals + T);
+  uint32_t* bm = (uint32_t*)(keys + T);
+  int32_t* wpre = (int32_t*)(bm + words);
+  for (int s = t; s < T; s += TPC) {
+    keys[s] = kEmptyKey;
+    vals[s] = V(0);
+  }
+  for (int i = t; i < words; i += TPC) bm[i] = 0;
+  __syncthreads();
+  const int64_t ci = (int64_t)blockIdx.x * CPB + g;
+  int32_t item = 0;
+  if (ci < n) {
+    item = items[ci];
+    const int64_t off = cl.off[item], end = off + cl.cnt[item];
+    const bool b1 = cl.buf[item] != 0;
+    const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
+    const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
+    for (int64_t e = off + t; e < end; e += TPC)
+      hmap_add_mark(keys, vals, bm, (uint32_t)T, col[e], val[e], err);
+  }
+  __syncthreads();
+  // Exclusive prefix of the word popcounts: each thread owns a contiguous
+  // run of words.
+  const int wpt = (words + TPC - 1) / TPC;
+  const int w0 = t * wpt;
+  int32_t mine = 0;
+  for (int i = 0; i < wpt; ++i)
+    if (w0 + i < words) mine += __popc(bm[w0 + i]);
+  const int32_t inc = wave_incl_scan(mine);
+  if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < WPG; ++i) {
+    const int32_t tv = wtot[g * WPG + i];
+    if (i < w) before += tv;
+    total += tv;
+  }
+  int32_t run = before + inc - mine;
+  for (int i = 0; i < wpt; ++i) {
+    if (w0 + i < words) {
+      wpre[w0 + i] = run;
+      run += __popc(bm[w0 + i]);
+    }
+  }
+  __syncthreads();
+  if (ci < n) {
+    const int64_t hr = cl.row[item];
+    const int64_t sidx = hr * cl.nreq + cl.slot[item];
+    const int64_t obase = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
+    const int32_t want = cl.slotNnz[sidx];
+    if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
+    const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+    for (int s = t; s < T; s += TPC) {
+      const int32_t k = keys[s];
+      if (k != kEmptyKey) {
+        const int32_t r = wpre[k >> 5] + __popc(bm[k >> 5] & ((1u << (k & 31)) - 1u));
+        if (r < want) {
+          ccol[obase + r] = colBase + k;
+          cval[obase + r] = vals[s];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+void chunks_set_attributes() {
+#define SG_ATTR(K) (void)hipFuncSetAttribute((const void*)(K), hipFuncAttributeMaxDynamicSharedMemorySize, 163840)
+  SG_ATTR((k_sym_chunks_bitmap<64, 4>));
+  SG_ATTR((k_sym_chunks_bitmap<256, 1>));
+  SG_ATTR((k_sym_chunks_bitmap<1024, 1>));
+  SG_ATTR((k_num_chunks_rank<64, 4, float>));
+  SG_ATTR((k_num_chunks_rank<128, 2, float>));
+  SG_ATTR((k_num_chunks_rank<256, 1, float>));
+  SG_ATTR((k_num_chunks_rank<512, 1, float>));
+  SG_ATTR((k_num_chunks_rank<1024, 1, float>));
+  SG_ATTR((k_num_chunks_rank<64, 4, double>));
+  SG_ATTR((k_num_chunks_rank<128, 2, double>));
+  SG_ATTR((k_num_chunks_rank<256, 1, double>));
+  SG_ATTR((k_num_chunks_rank<512, 1, double>));
+  SG_ATTR((k_num_chunks_rank<1024, 1, double>));
+#undef SG_ATTR
+}
+
+size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb) {
+  return (size_t)rpb * (f64 ? rank_group_bytes<double>(T, words) : rank_group_bytes<float>(T, words));
+}
+
+void launch_sym_chunks_bitmap(int sizeClass, const int32_t* items, int64_t n, int32_t words,
+                              const ChunkList& cl, hipStream_t s) {
+  if (n <= 0) return;
+  if (sizeClass == 0) {
+    hipLaunchKernelGGL((k_sym_chunks_bitmap<64, 4>), dim3((unsigned)((n + 3) / 4)), dim3(256),
+                       (size_t)4 * words * 4, s, items, n, words, cl);
+  } else if (sizeClass == 1) {
+    hipLaunchKernelGGL((k_sym_chunks_bitmap<256, 1>), dim3((unsigned)n), dim3(256),
+                       (size_t)words * 4, s, items, n, words, cl);
+  } else {
+    hipLaunchKernelGGL((k_sym_chunks_bitmap<1024, 1>), dim3((unsigned)n), dim3(1024),
+                       (size_t)words * 4, s, items, n, words, cl);
+  }
+}
+
+void launch_num_chunks_rank(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
+                            int32_t words, const ChunkList& cl, const int64_t* cRowOff,
+                            int32_t* ccol, void* cval, int32_t* err, hipStream_t s) {
+  if (n <= 0) return;
+  const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
+  const size_t lds = rank_chunk_lds(f64, b.T, words, b.rpb);
+#define L(TPC, CPB)                                                                            \
+  do {                                                                                         \
+    if (f64)                                                                                   \
+      hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, double>), dim3(grid), dim3(TPC * CPB),   \
+                         lds, s, items, n, b.T, words, cl, cRowOff, ccol, (double*)cval, err); \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, float>), dim3(grid), dim3(TPC * CPB),    \
+                         lds, s, items, n, b.T, words, cl, cRowOff, ccol, (float*)cval, err);  \
+  } while (0)
+  switch (b.tpr) {
+    case 64: L(64, 4); break;
+    case 128: L(128, 2); break;
+    case 256: L(256, 1); break;
+    case 512: L(512, 1); break;
+    default: L(1024, 1); break;
+  }
+#undef L
+}
+
+}  // namespace sg

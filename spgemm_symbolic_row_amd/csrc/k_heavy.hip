@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kNT) void k_chunk_bins(int64_t nfc, const int32_t* 
   const int32_t c = fcCnt[i];
   if (i >= lastFirst && c > tau) {
     key[i] = (uint8_t)denseBin;
-    atomicAdd((unsigned long long*)denseElems, (unsigned long long)c);
+    if (denseElems) atomicAdd((unsigned long long*)denseElems, (unsigned long long)c);
     return;
   }
   int b = 0;
