@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not time kernel phases with HIP events")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="run light and heavy work on one stream (diagnostics)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -152,6 +154,8 @@ def main():
     f64 = A.val.dtype == np.float64
     sv = 8 if f64 else 4
     opts = {} if args.no_profile else {"profile": 1}
+    if args.single_stream:
+        opts["single_stream"] = 1
     mcl = args.config == "mcl1m"
 
     def step():

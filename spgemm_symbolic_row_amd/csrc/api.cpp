@@ -644,7 +644,11 @@ void heavy_symbolic(spgemm_plan_t p) {
   int32_t* bc = alloc_n<int32_t>(p, 64, s);
   int32_t* bf = alloc_n<int32_t>(p, 64, s);
   int32_t* bs = alloc_n<int32_t>(p, 65, s);
-  launch_chunk_bins(nfc, p->fcCnt, p->lastFirst, p->tau, p->dSymCaps, p->NS, p->NS, key,
+  // W-wide chunks with more than W/8 elements (or tau, if smaller) go to the
+  // dense accumulator: at that density zeroing and scanning W columns is
+  // cheaper than hashing.
+  const int64_t denseMin = std::min<int64_t>(p->tau, W / 8);
+  launch_chunk_bins(nfc, p->fcCnt, p->lastFirst, denseMin, p->dSymCaps, p->NS, p->NS, key,
                     p->stats + kStatDenseElems, s);
   launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, p->fcOrder, s);
   HIP_CHECK(hipMemcpyAsync(p->hBins + 64, bs, sizeof(int32_t) * (p->NS + 2), hipMemcpyDeviceToHost, s));

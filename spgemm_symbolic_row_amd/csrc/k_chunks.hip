@@ -32,10 +32,22 @@ __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const int32_t* _
     item = items[ci];
     const int64_t off = cl.off[item], end = off + cl.cnt[item];
     const int32_t* __restrict__ col = cl.buf[item] ? cl.col1 : cl.col0;
-    for (int64_t e = off + t; e < end; e += TPC) {
-      const int32_t c = col[e];
-      const uint32_t bit = 1u << (c & 31);
-      if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+    constexpr int kB = 8;  // loads in flight per thread
+    for (int64_t e0 = off + t; e0 < end; e0 += (int64_t)TPC * kB) {
+      int32_t cc[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int64_t e = e0 + (int64_t)k * TPC;
+        cc[k] = e < end ? col[e] : -1;
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int32_t c = cc[k];
+        if (c >= 0) {
+          const uint32_t bit = 1u << (c & 31);
+          if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+        }
+      }
     }
   }
   __syncthreads();
@@ -111,8 +123,20 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const int32_t* __r
     const bool b1 = cl.buf[item] != 0;
     const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
     const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
-    for (int64_t e = off + t; e < end; e += TPC)
-      hmap_add_mark(keys, vals, bm, (uint32_t)T, col[e], val[e], err);
+    constexpr int kB = 4;  // loads in flight per thread
+    for (int64_t e0 = off + t; e0 < end; e0 += (int64_t)TPC * kB) {
+      int32_t cc[kB];
+      V vv[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int64_t e = e0 + (int64_t)k * TPC;
+        cc[k] = e < end ? col[e] : -1;
+        vv[k] = e < end ? val[e] : V(0);
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k)
+        if (cc[k] >= 0) hmap_add_mark(keys, vals, bm, (uint32_t)T, cc[k], vv[k], err);
+    }
   }
   __syncthreads();
   // Exclusive prefix of the word popcounts: each thread owns a contiguous

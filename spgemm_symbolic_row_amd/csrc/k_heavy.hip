@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kNT) void k_seg_base(int64_t nE, const int32_t* __r
 // binary search across lanes, and writes col_B and val_A*val_B to
 // segBase[entry] + (position inside the segment).  Consecutive elements of
 // a segment read consecutive B entries and write consecutive C-hat slots.
-constexpr int kOpBlock = 8192;
+constexpr int kOpBlock = 32768;
+constexpr int kXcds = 8;
 
 template <typename V>
 __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t* __restrict__ entryOff,
@@ -100,7 +101,12 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
   constexpr int kNW = kNT / kWave;
   constexpr int kPerWave = kOpBlock / kNW;
   const int w = threadIdx.x / kWave;
-  const int64_t g0 = (int64_t)blockIdx.x * kOpBlock;
+  // Work groups are dealt round-robin to the 8 XCDs; give each XCD a
+  // contiguous run of tiles so that the B rows shared by neighbouring tiles
+  // stay in that XCD's L2.
+  const int64_t perXcd = (int64_t)gridDim.x / kXcds;
+  const int64_t tile = (int64_t)(blockIdx.x % kXcds) * perXcd + blockIdx.x / kXcds;
+  const int64_t g0 = tile * kOpBlock;
   int64_t p = g0 + (int64_t)w * kPerWave;
   int64_t p1 = p + kPerWave;
   if (p1 > Ph) p1 = Ph;
@@ -120,23 +126,43 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
     }
     int64_t bend = entryOff[(j + kWave < nE) ? j + kWave : nE];
     if (bend > p1) bend = p1;
-    for (; p < bend; p += kWave) {
-      const int64_t q = p + lane_id();
-      int s = 0;
+    // Four windows of 64 elements per iteration: all their B loads are in
+    // flight before the first store.
+    constexpr int kU = 4;
+    for (; p < bend; p += kWave * kU) {
+      int64_t dpos[kU];
+      int32_t bidx[kU];
+      V av[kU];
 #pragma unroll
-      for (int step = 32; step >= 1; step >>= 1) {
-        const int64_t o = __shfl(off, s + step);
-        if (o <= q) s += step;
-      }
-      const int64_t so = __shfl(off, s);
-      const int32_t sb = __shfl(bs, s);
-      const V sa = __shfl(a, s);
-      const int64_t sd = __shfl(dst, s);
-      if (q < bend) {
+      for (int u = 0; u < kU; ++u) {
+        const int64_t q = p + u * kWave + lane_id();
+        int s = 0;
+#pragma unroll
+        for (int step = 32; step >= 1; step >>= 1) {
+          const int64_t o = __shfl(off, s + step);
+          if (o <= q) s += step;
+        }
+        const int64_t so = __shfl(off, s);
+        const int32_t sb = __shfl(bs, s);
+        av[u] = __shfl(a, s);
+        const int64_t sd = __shfl(dst, s);
         const int64_t r = q - so;
-        const int32_t b = sb + (int32_t)r;
-        outCol[sd + r] = bcol[b];
-        outVal[sd + r] = sa * bval[b];
+        dpos[u] = q < bend ? sd + r : -1;
+        bidx[u] = sb + (int32_t)r;
+      }
+      int32_t cv[kU];
+      V bv[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        cv[u] = dpos[u] >= 0 ? bcol[bidx[u]] : 0;
+        bv[u] = dpos[u] >= 0 ? bval[bidx[u]] : V(0);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (dpos[u] >= 0) {
+          outCol[dpos[u]] = cv[u];
+          outVal[dpos[u]] = av[u] * bv[u];
+        }
       }
     }
     p = bend;
@@ -152,6 +178,8 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
 // ballot per bit so a single lane per bucket updates the LDS counters.
 constexpr int kMsNBMax = 1024;  // LDS buckets per work group
 constexpr int kMsRowsMax = 512;
+constexpr int kMsItemsF64 = 8;   // elements per thread held in registers
+constexpr int kMsItemsF32 = 16;
 
 __device__ __forceinline__ int bits_for(int n) {
   int b = 0;
@@ -214,16 +242,24 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
   const int nbits = bits_for(NB);
   for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
   __syncthreads();
-  for (int base = 0; base < n; base += kNT) {
-    const int idx = base + threadIdx.x;
-    const bool act = idx < n;
-    uint32_t b = 0;
-    if (act) {
-      const int64_t e = e0 + idx;
-      b = (uint32_t)(local_row(bnd, nrows, e) * v + (col[e] >> shift));
+  // All loads of a batch are issued before any is used.
+  constexpr int kBatch = 8;
+  for (int base = 0; base < n; base += kNT * kBatch) {
+    int32_t cc[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int idx = base + k * kNT + threadIdx.x;
+      cc[k] = idx < n ? col[e0 + idx] : 0;
     }
-    const uint64_t m = match_key(b, nbits, act);
-    if (act && lane_id() == ffs64(m)) atomicAdd(&hist[b], __popcll(m));
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int idx = base + k * kNT + threadIdx.x;
+      const bool act = idx < n;
+      uint32_t b = 0;
+      if (act) b = (uint32_t)(local_row(bnd, nrows, e0 + idx) * v + (cc[k] >> shift));
+      const uint64_t m = match_key(b, nbits, act);
+      if (act && lane_id() == ffs64(m)) atomicAdd(&hist[b], __popcll(m));
+    }
   }
   __syncthreads();
   const int64_t r0 = s_r0;
@@ -250,14 +286,18 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
                                                     int32_t* __restrict__ outCol,
                                                     V* __restrict__ outVal,
                                                     int32_t* __restrict__ err) {
-  constexpr int G = kNT * ITEMS;
-  __shared__ int32_t colBuf[G];
-  __shared__ V valBuf[G];
-  __shared__ uint16_t bktBuf[G];
-  __shared__ int32_t hist[kMsNBMax];
-  __shared__ int32_t loff[kMsNBMax];
-  __shared__ int64_t gbase[kMsNBMax];
-  __shared__ int64_t bnd[kMsRowsMax];
+  // LDS (sized by the host for blockElems elements and maxRows rows):
+  // gbase[NB] i64 | bnd[maxRows] i64 | valBuf[blockElems] V |
+  // colBuf[blockElems] i32 | hist[NB] i32 | loff[NB] i32 | bktBuf u16
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NBcap = maxRows * v;
+  int64_t* gbase = (int64_t*)smem;
+  int64_t* bnd = gbase + NBcap;
+  V* valBuf = (V*)(bnd + maxRows);
+  int32_t* colBuf = (int32_t*)(valBuf + blockElems);
+  int32_t* hist = colBuf + blockElems;
+  int32_t* loff = hist + NBcap;
+  uint16_t* bktBuf = (uint16_t*)(loff + NBcap);
   __shared__ int32_t wtot[kNT / kWave];
   __shared__ int64_t s_r0;
   __shared__ int32_t s_nrows;
@@ -507,11 +547,25 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
   const bool b1 = cl.buf[item] != 0;
   const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
   const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
-  for (int64_t e = off + threadIdx.x; e < end; e += kDenseNT) {
-    const int32_t c = col[e];
-    atomicAdd(&vals[c], val[e]);
-    const uint32_t bit = 1u << (c & 31);
-    if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+  constexpr int kB = 8;  // loads in flight per thread
+  for (int64_t e0 = off + threadIdx.x; e0 < end; e0 += (int64_t)kDenseNT * kB) {
+    int32_t cc[kB];
+    V vv[kB];
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int64_t e = e0 + (int64_t)k * kDenseNT;
+      cc[k] = e < end ? col[e] : -1;
+      vv[k] = e < end ? val[e] : V(0);
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      const int32_t c = cc[k];
+      if (c >= 0) {
+        atomicAdd(&vals[c], vv[k]);
+        const uint32_t bit = 1u << (c & 31);
+        if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+      }
+    }
   }
   __syncthreads();
   const int cpt = W >= kDenseNT ? W / kDenseNT : 1;  // columns per thread, <= 32
@@ -562,6 +616,10 @@ __global__ __launch_bounds__(kNT) void k_slot_scan(int64_t h, int64_t nreq,
 }  // namespace
 
 void heavy_set_attributes() {
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF64, double>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
   (void)hipFuncSetAttribute((const void*)k_dense_num<float>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
   (void)hipFuncSetAttribute((const void*)k_dense_num<double>,
@@ -610,7 +668,8 @@ void launch_outer_product(bool f64, int64_t Ph, const int64_t* entryOff, int64_t
                           const int32_t* brp, const int32_t* bcol, const void* bval,
                           int32_t* outCol, void* outVal, hipStream_t s) {
   if (Ph <= 0) return;
-  const unsigned g = grid_for(Ph, kOpBlock);
+  // A multiple of the XCD count; tiles past the end exit at once.
+  const unsigned g = (grid_for(Ph, kOpBlock) + kXcds - 1) / kXcds * kXcds;
   if (f64)
     hipLaunchKernelGGL(k_outer_product<double>, dim3(g), dim3(kNT), 0, s, Ph, entryOff, nE, cscCol,
                        (const double*)cscVal, segBase, brp, bcol, (const double*)bval, outCol,
@@ -620,9 +679,6 @@ void launch_outer_product(bool f64, int64_t Ph, const int64_t* entryOff, int64_t
                        (const float*)cscVal, segBase, brp, bcol, (const float*)bval, outCol,
                        (float*)outVal);
 }
-
-constexpr int kMsItemsF64 = 8;
-constexpr int kMsItemsF32 = 16;
 
 void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int* maxRows) {
   int64_t G = (int64_t)kNT * (f64 ? kMsItemsF64 : kMsItemsF32);
@@ -657,12 +713,15 @@ void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* r
                        int32_t* outCol, void* outVal, int32_t* err, hipStream_t s) {
   if (E <= 0) return;
   const unsigned g = grid_for(E, blockElems);
+  const size_t NB = (size_t)maxRows * v;
+  const size_t lds = NB * 8 + (size_t)maxRows * 8 + (size_t)blockElems * ((f64 ? 8 : 4) + 4 + 2) +
+                     NB * 8 + 16;
   if (f64)
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF64, double>), dim3(g), dim3(kNT), 0, s, E,
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF64, double>), dim3(g), dim3(kNT), lds, s, E,
                        blockElems, rowPtr, R, inCol, (const double*)inVal, shift, v, wmask,
                        maxRows, inv, cursor, outCol, (double*)outVal, err);
   else
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float>), dim3(g), dim3(kNT), 0, s, E,
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float>), dim3(g), dim3(kNT), lds, s, E,
                        blockElems, rowPtr, R, inCol, (const float*)inVal, shift, v, wmask,
                        maxRows, inv, cursor, outCol, (float*)outVal, err);
 }

@@ -178,6 +178,8 @@ __global__ __launch_bounds__(kNT) void k_bin_scatter(const uint8_t* __restrict__
 // product index where that entry's scaled B row starts).  The row total is
 // P_i; its bin is 0 when P_i == 0, 1 + (first cap >= P_i) when P_i <= tau,
 // and nbins + 1 (heavy) otherwise.
+// A grid-stride loop over rows keeps the number of work groups (and so of
+// same-address global atomics for the totals, one set per work group) small.
 template <int G>
 __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __restrict__ arp,
                                                   const int32_t* __restrict__ acol,
@@ -191,8 +193,8 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
   if (threadIdx.x == 0) sP = sPh = sAh = sMax = sH = sL = 0;
   __syncthreads();
   const int gl = threadIdx.x % G;
-  const int64_t row = ((int64_t)blockIdx.x * kNT + threadIdx.x) / G;
-  if (row < m) {
+  const int64_t rowsPerPass = (int64_t)gridDim.x * (kNT / G);
+  for (int64_t row = ((int64_t)blockIdx.x * kNT + threadIdx.x) / G; row < m; row += rowsPerPass) {
     const int64_t rs = arp[row], re = arp[row + 1];
     int64_t p = 0;
     for (int64_t b = rs; b < re; b += G) {
@@ -355,8 +357,10 @@ void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const i
                      hipStream_t s) {
   if (m <= 0) return;
   constexpr int G = 16;
-  hipLaunchKernelGGL(k_row_info<G>, dim3(grid_for(m * G, kNT)), dim3(kNT), 0, s, m, arp, acol,
-                     brp, tau, caps, nbins, rowP, scanA, rowBin, stats);
+  unsigned g = grid_for(m * G, kNT);
+  if (g > 65535) g = 65535;
+  hipLaunchKernelGGL(k_row_info<G>, dim3(g), dim3(kNT), 0, s, m, arp, acol, brp, tau, caps, nbins,
+                     rowP, scanA, rowBin, stats);
 }
 
 void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
