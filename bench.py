@@ -131,6 +131,11 @@ def main():
                     help="do not time kernel phases with HIP events")
     ap.add_argument("--single-stream", action="store_true",
                     help="run light and heavy work on one stream (diagnostics)")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="first run one device-to-device copy of this many GiB, so "
+                         "hardware byte counters can be scaled against a known size")
+    ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
+    ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -147,6 +152,15 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    if args.copy_calibration_gib > 0:
+        nbytes = int(args.copy_calibration_gib * 2 ** 30)
+        src = torch.ones(nbytes // 8, dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {nbytes} bytes read and {nbytes} bytes written")
+        del src, dst
     t = time.time()
     A = synth.workload(args.config)
     log(f"generated {args.config}: {A.m} rows, nnz {A.nnz} in {time.time() - t:.1f} s")
@@ -156,6 +170,10 @@ def main():
     opts = {} if args.no_profile else {"profile": 1}
     if args.single_stream:
         opts["single_stream"] = 1
+    if args.dense_width:
+        opts["dense_width"] = args.dense_width
+    if args.lds_budget:
+        opts["lds_budget"] = args.lds_budget
     mcl = args.config == "mcl1m"
 
     def step():

@@ -27,8 +27,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["k_util.hip", "k_light.hip", "k_heavy.hip", "k_chunks.hip", "k_prune.hip", "api.cpp",
-           "params.cpp"]
+SOURCES = ["k_util.hip", "k_light.hip", "k_outer.hip", "k_multisplit.hip", "k_heavy.hip",
+           "k_chunks.hip", "k_prune.hip", "api.cpp", "params.cpp"]
 
 
 def _compile(src: str) -> str:

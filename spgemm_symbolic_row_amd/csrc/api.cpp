@@ -405,6 +405,7 @@ void do_plan(spgemm_plan_t p) {
   if (!attrs) {
     light_set_attributes();
     heavy_set_attributes();
+    multisplit_set_attributes();
     chunks_set_attributes();
     attrs = true;
   }

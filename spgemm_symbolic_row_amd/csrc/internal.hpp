@@ -116,8 +116,9 @@ void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t 
                        const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
                        int32_t* err, hipStream_t s);
 
-// ---- k_heavy.hip ----
+// ---- k_outer.hip, k_multisplit.hip, k_heavy.hip ----
 void heavy_set_attributes();
+void multisplit_set_attributes();
 void launch_csc_count(int64_t h, const int32_t* xheavy, const int32_t* arp, const int32_t* acol,
                       int32_t* colCnt, hipStream_t s);
 void launch_csc_fill(int64_t h, const int32_t* xheavy, const int32_t* arp, const int32_t* acol,

@@ -1,0 +1,302 @@
+// One level of the hierarchical multisplit (gMAGNUS page, §III-C): the
+// per-(row, chunk) histogram and the multisplit kernel that reorders each
+// input row into column-range chunks through LDS.
+#include "device_common.hpp"
+
+namespace sg {
+namespace {
+
+constexpr int kNT = 256;
+inline unsigned grid_for(int64_t n, int per_block) {
+  int64_t g = (n + per_block - 1) / per_block;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+// ------------------------------------------------------------ multisplit
+// A work group owns a static range of `blockElems` elements of the level's
+// input (heavy rows, or heavy chunks of the previous level, each longer than
+// tau).  Local bucket of an element = (row inside the range) * v + chunk,
+// chunk = col >> shift.  Bucket ids are matched across the wave with one
+// ballot per bit so a single lane per bucket updates the LDS counters.
+constexpr int kMsNBMax = 1024;  // LDS buckets per work group
+constexpr int kMsRowsMax = 512;
+constexpr int kMsItemsF64 = 8;   // elements per thread held in registers
+constexpr int kMsItemsF32 = 16;
+
+__device__ __forceinline__ int bits_for(int n) {
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+// Rows of the range [e0, e1): first row r0 and the row boundaries inside the
+// range (rowPtr[r0+1 .. r0+nrows-1]) into bnd.  Returns nrows, or -1 when
+// more than maxRows rows meet the range.
+__device__ __forceinline__ int range_rows(const int64_t* __restrict__ rowPtr, int64_t R, int64_t e0,
+                                          int64_t e1, int maxRows, int64_t* bnd, int64_t* s_r0,
+                                          int32_t* s_nrows) {
+  if (threadIdx.x < kWave) {
+    const int64_t r0 = wave_last_le(rowPtr, (int64_t)0, R, e0);
+    const int64_t r1 = wave_last_le(rowPtr, (int64_t)0, R, e1 - 1);
+    if (lane_id() == 0) {
+      *s_r0 = r0;
+      *s_nrows = (int32_t)(r1 - r0 + 1);
+    }
+  }
+  __syncthreads();
+  const int nrows = *s_nrows;
+  if (nrows > maxRows) return -1;
+  for (int i = threadIdx.x; i < nrows - 1; i += kNT) bnd[i] = rowPtr[*s_r0 + 1 + i];
+  return nrows;
+}
+
+__device__ __forceinline__ int local_row(const int64_t* bnd, int nrows, int64_t e) {
+  int lo = 0, hi = nrows - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (bnd[mid] <= e)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// Histogram: per (input row, chunk) element counts into counts[r*v + c].
+__global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems,
+                                                   const int64_t* __restrict__ rowPtr, int64_t R,
+                                                   const int32_t* __restrict__ col, int shift, int v,
+                                                   int maxRows, int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ err) {
+  __shared__ int32_t hist[kMsNBMax];
+  __shared__ int64_t bnd[kMsRowsMax];
+  __shared__ int64_t s_r0;
+  __shared__ int32_t s_nrows;
+  const int64_t e0 = (int64_t)blockIdx.x * blockElems;
+  const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
+  const int n = (int)(e1 - e0);
+  const int nrows = range_rows(rowPtr, R, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
+  if (nrows < 0) {
+    if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
+    return;
+  }
+  const int NB = nrows * v;
+  const int nbits = bits_for(NB);
+  for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
+  __syncthreads();
+  // All loads of a batch are issued before any is used.
+  constexpr int kBatch = 8;
+  for (int base = 0; base < n; base += kNT * kBatch) {
+    int32_t cc[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int idx = base + k * kNT + threadIdx.x;
+      cc[k] = idx < n ? col[e0 + idx] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int idx = base + k * kNT + threadIdx.x;
+      const bool act = idx < n;
+      uint32_t b = 0;
+      if (act) b = (uint32_t)(local_row(bnd, nrows, e0 + idx) * v + (cc[k] >> shift));
+      const uint64_t m = match_key(b, nbits, act);
+      if (act && lane_id() == ffs64(m)) atomicAdd(&hist[b], __popcll(m));
+    }
+  }
+  __syncthreads();
+  const int64_t r0 = s_r0;
+  for (int i = threadIdx.x; i < NB; i += kNT) {
+    const int32_t c = hist[i];
+    if (c) {
+      const int lr = i / v;
+      atomicAdd(&counts[(r0 + lr) * v + (i - lr * v)], c);
+    }
+  }
+}
+
+// Multisplit (§III-C): local histogram, one global reservation per
+// (row, chunk) bucket, LDS permute into bucket order, then coalesced writes
+// of whole bucket runs with the column shifted into the chunk's range.
+template <int ITEMS, typename V>
+__global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElems,
+                                                    const int64_t* __restrict__ rowPtr, int64_t R,
+                                                    const int32_t* __restrict__ inCol,
+                                                    const V* __restrict__ inVal, int shift, int v,
+                                                    int32_t wmask, int maxRows,
+                                                    const int32_t* __restrict__ inv,
+                                                    int64_t* __restrict__ cursor,
+                                                    int32_t* __restrict__ outCol,
+                                                    V* __restrict__ outVal,
+                                                    int32_t* __restrict__ err) {
+  // LDS (sized by the host for blockElems elements and maxRows rows):
+  // gbase[NB] i64 | bnd[maxRows] i64 | valBuf[blockElems] V |
+  // colBuf[blockElems] i32 | hist[NB] i32 | loff[NB] i32 | bktBuf u16
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NBcap = maxRows * v;
+  int64_t* gbase = (int64_t*)smem;
+  int64_t* bnd = gbase + NBcap;
+  V* valBuf = (V*)(bnd + maxRows);
+  int32_t* colBuf = (int32_t*)(valBuf + blockElems);
+  int32_t* hist = colBuf + blockElems;
+  int32_t* loff = hist + NBcap;
+  uint16_t* bktBuf = (uint16_t*)(loff + NBcap);
+  __shared__ int32_t wtot[kNT / kWave];
+  __shared__ int64_t s_r0;
+  __shared__ int32_t s_nrows;
+  const int64_t e0 = (int64_t)blockIdx.x * blockElems;
+  const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
+  const int n = (int)(e1 - e0);
+  const int nrows = range_rows(rowPtr, R, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
+  if (nrows < 0) {
+    if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
+    return;
+  }
+  const int NB = nrows * v;
+  const int nbits = bits_for(NB);
+  for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
+  __syncthreads();
+
+  int32_t cc[ITEMS];
+  V xv[ITEMS];
+  uint32_t bb[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int idx = it * kNT + threadIdx.x;
+    const bool act = idx < n;
+    cc[it] = 0;
+    xv[it] = V(0);
+    bb[it] = 0;
+    if (act) {
+      const int64_t e = e0 + idx;
+      cc[it] = inCol[e];
+      xv[it] = inVal[e];
+      bb[it] = (uint32_t)(local_row(bnd, nrows, e) * v + (cc[it] >> shift));
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const bool act = it * kNT + (int)threadIdx.x < n;
+    const uint64_t m = match_key(bb[it], nbits, act);
+    if (act && lane_id() == ffs64(m)) atomicAdd(&hist[bb[it]], __popcll(m));
+  }
+  __syncthreads();
+
+  // Exclusive scan of the bucket counts (4 buckets per thread).
+  {
+    int32_t h4[4];
+    int32_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = threadIdx.x * 4 + k;
+      h4[k] = b < NB ? hist[b] : 0;
+      sum += h4[k];
+    }
+    int32_t tot;
+    int32_t ex = block_excl_scan<kNT>(sum, wtot, &tot);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = threadIdx.x * 4 + k;
+      if (b < NB) loff[b] = ex;
+      ex += h4[k];
+    }
+  }
+  __syncthreads();
+  // Reserve each bucket's run in its chunk.  The atomics' results are only
+  // needed by the final write, so they stay in registers while the LDS
+  // permute runs and their latency overlaps it.
+  const int64_t r0 = s_r0;
+  constexpr int kBPT = kMsNBMax / kNT;  // buckets per thread
+  unsigned long long gres[kBPT];
+#pragma unroll
+  for (int k = 0; k < kBPT; ++k) {
+    const int b = threadIdx.x + k * kNT;
+    gres[k] = 0;
+    if (b < NB) {
+      const int32_t c = hist[b];
+      if (c) {
+        const int lr = b / v;
+        const int32_t q = inv[(r0 + lr) * v + (b - lr * v)];
+        gres[k] = atomicAdd((unsigned long long*)&cursor[q], (unsigned long long)c);
+      }
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < NB; b += kNT) hist[b] = loff[b];
+  __syncthreads();
+
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const bool act = it * kNT + (int)threadIdx.x < n;
+    const uint64_t m = match_key(bb[it], nbits, act);
+    const int leader = act ? ffs64(m) : lane_id();
+    int32_t base = 0;
+    if (act && lane_id() == leader) base = atomicAdd(&hist[bb[it]], __popcll(m));
+    base = __shfl(base, leader);
+    if (act) {
+      const int pos = base + __popcll(m & lanemask_lt());
+      colBuf[pos] = cc[it] & wmask;
+      valBuf[pos] = xv[it];
+      bktBuf[pos] = (uint16_t)bb[it];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kBPT; ++k) {
+    const int b = threadIdx.x + k * kNT;
+    if (b < NB) gbase[b] = (int64_t)gres[k];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < n; idx += kNT) {
+    const int b = bktBuf[idx];
+    const int64_t dest = gbase[b] + (idx - loff[b]);
+    outCol[dest] = colBuf[idx];
+    outVal[dest] = valBuf[idx];
+  }
+}
+
+}  // namespace
+
+void multisplit_set_attributes() {
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF64, double>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+}
+
+void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int* maxRows) {
+  int64_t G = (int64_t)kNT * (f64 ? kMsItemsF64 : kMsItemsF32);
+  // A range of G elements meets at most floor((G-1)/(tau+1)) + 2 rows when
+  // every row holds more than tau elements; shrink G until the buckets fit.
+  auto rows_for = [&](int64_t g) { return (g - 1) / (tau + 1) + 2; };
+  while (G > 64 && (rows_for(G) * v > kMsNBMax || rows_for(G) > kMsRowsMax)) G /= 2;
+  *blockElems = (int32_t)G;
+  *maxRows = (int)rows_for(G);
+}
+
+void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
+                      const int32_t* col, int shift, int v, int maxRows, int32_t* counts,
+                      int32_t* err, hipStream_t s) {
+  if (E <= 0) return;
+  hipLaunchKernelGGL(k_histogram, dim3(grid_for(E, blockElems)), dim3(kNT), 0, s, E, blockElems,
+                     rowPtr, R, col, shift, v, maxRows, counts, err);
+}
+
+void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
+                       int64_t R, const int32_t* inCol, const void* inVal, int shift, int v,
+                       int32_t wmask, int maxRows, const int32_t* inv, int64_t* cursor,
+                       int32_t* outCol, void* outVal, int32_t* err, hipStream_t s) {
+  if (E <= 0) return;
+  const unsigned g = grid_for(E, blockElems);
+  const size_t NB = (size_t)maxRows * v;
+  const size_t lds = NB * 8 + (size_t)maxRows * 8 + (size_t)blockElems * ((f64 ? 8 : 4) + 4 + 2) +
+                     NB * 8 + 16;
+  if (f64)
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF64, double>), dim3(g), dim3(kNT), lds, s, E,
+                       blockElems, rowPtr, R, inCol, (const double*)inVal, shift, v, wmask,
+                       maxRows, inv, cursor, outCol, (double*)outVal, err);
+  else
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float>), dim3(g), dim3(kNT), lds, s, E,
+                       blockElems, rowPtr, R, inCol, (const float*)inVal, shift, v, wmask,
+                       maxRows, inv, cursor, outCol, (float*)outVal, err);
+}
+
+}  // namespace sg
