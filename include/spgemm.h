@@ -67,7 +67,16 @@ typedef struct spgemm_options {
                                    work group of the device (160 KiB on gfx950) */
   int64_t heavy_threshold;      /* tau; 0 = derived from s_LM (Eq. 4 reading)   */
   int64_t dense_width;          /* final chunk width W (power of two); 0 = derived */
-  int64_t mem_budget;           /* bytes for the heavy intermediate; 0 = all free */
+  int64_t mem_budget;           /* bytes for the heavy intermediate (the outer
+                                   product and multisplit buffers, 8 (fp32) or
+                                   12 (fp64) bytes per element, two buffers when
+                                   there are levels); heavy rows are processed
+                                   in batches of consecutive rows that fit it
+                                   (at least one row a batch).  One batch keeps
+                                   its expansion from symbolic to numeric;
+                                   several batches expand again in numeric.
+                                   0 = 45% of the device memory free at
+                                   spgemm_symbolic, at least 1 GiB            */
   int32_t max_chunks_per_level; /* n_chunksMax (power of two >= 2); 0 = 32       */
   int32_t rowptr64;             /* 1: C.row_ptr is int64, else int32            */
   int32_t validate;             /* 1: check A and B are canonical CSR           */
@@ -127,13 +136,14 @@ typedef struct spgemm_stats {
   int64_t lds_hash_products;  /* products summed in LDS hash tables            */
   int64_t lds_dense_products; /* products summed in LDS dense accumulators     */
   int64_t global_products;    /* products summed in global memory (always 0)   */
-  int64_t batches;            /* heavy-row batches                             */
+  int64_t batches;            /* heavy-row batches (0 with no heavy rows)      */
   double ms_plan, ms_symbolic, ms_numeric; /* host wall time of each call      */
   double phase_ms[16];        /* GPU time of each spgemm_phase (with profile)  */
   int32_t phase_windows[16];  /* event-bracketed windows summed in phase_ms;
                                  a window holds one launch for the outer
                                  product, histogram, multisplit and dense
-                                 phases (one per level for the per-level ones) */
+                                 phases (one per level for the per-level ones,
+                                 and one per batch and expansion)           */
   int64_t device_errors;      /* device status bits seen (0 when all is well)  */
 } spgemm_stats;
 

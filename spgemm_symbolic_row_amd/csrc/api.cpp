@@ -165,6 +165,33 @@ struct Arena {
 };
 Arena g_arena[64];
 
+// Per-device region for the heavy intermediate (the outer-product and
+// multisplit buffers): one block, sized to the largest batch seen and reused
+// by every batch of every product, with the same one-user-at-a-time and
+// `done` protocol as the arena.  Kept apart from the arena so that the
+// intermediate, the largest allocation by far, is never split or cached in
+// pieces that a later, larger batch cannot use.
+struct Region {
+  std::mutex mu;
+  char* base = nullptr;
+  size_t cap = 0;
+  bool busy = false;
+  hipEvent_t done = nullptr;
+  bool doneValid = false;
+};
+Region g_region[64];
+
+// Return the stream-ordered pool's cached memory to the device (after all
+// queued work), so that a large block can be allocated in its place.
+void trim_pool(int device) {
+  hipMemPool_t pool;
+  if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
+    HIP_CHECK(hipDeviceSynchronize());
+    (void)hipMemPoolTrimTo(pool, 0);
+  }
+  (void)hipGetLastError();
+}
+
 // Small pinned host buffers for readbacks, one set per host thread.
 struct Pinned {
   int64_t* stats = nullptr;  // 32 entries
@@ -178,6 +205,20 @@ Pinned& pinned() {
   }
   return pb;
 }
+
+// One batch of heavy rows after expansion: its intermediate buffers and
+// final chunk list, ordered by numeric bin.
+struct Batch {
+  int64_t hb0 = 0, hb1 = 0, Pb = 0;
+  int32_t* bufCol[2] = {nullptr, nullptr};
+  void* bufVal[2] = {nullptr, nullptr};
+  int64_t nfc = 0, lastFirst = 0, denseChunks = 0;
+  int64_t* fcOff = nullptr;
+  int32_t *fcCnt = nullptr, *fcRow = nullptr, *fcSlot = nullptr, *fcOrder = nullptr;
+  int8_t* fcBuf = nullptr;
+  std::vector<int32_t> fcBinStart;
+  int64_t levelElems[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+};
 
 }  // namespace
 
@@ -197,11 +238,12 @@ struct spgemm_plan_s {
   std::string err;
   std::vector<std::pair<void*, hipStream_t>> allocs;
   Arena* arena = nullptr;   // held from plan to destroy, or null
+  Region* region = nullptr; // held from the first heavy batch to destroy, or null
+  char* heavyBuf = nullptr; // the heavy intermediate buffers of the current batch
   size_t arenaUsed = 0, demand = 0;
   std::vector<BinCfg> symBins, numBins, rankBins;
   int32_t chunkWords = 0;  // bitmap words of the widest final chunk (0: hash fallback)
-  int32_t* fcOrderSym = nullptr;
-  std::vector<int32_t> fcSymStart;
+  int32_t* dClassCaps = nullptr;  // size classes of the bitmap chunk symbolic
   int NS = 0;  // number of hash bins
   // device arrays
   int32_t *dSymCaps = nullptr;
@@ -213,16 +255,15 @@ struct spgemm_plan_s {
   int64_t* hStats = nullptr;   // kNumStats + 8
   int32_t* hBins = nullptr;    // 128
   // host copies
-  std::vector<int32_t> rowBinStart, numBinStart, fcBinStart;
+  std::vector<int32_t> rowBinStart, numBinStart;
   // heavy path
-  int64_t h = 0, Ph = 0, nAh = 0;
+  int64_t h = 0, Ph = 0, nAh = 0, nreq = 1;
   const int32_t* xheavy = nullptr;
-  int32_t *bufCol[2] = {nullptr, nullptr};
-  void* bufVal[2] = {nullptr, nullptr};
-  int64_t nfc = 0, lastFirst = 0, nreq = 1;
-  int64_t* fcOff = nullptr;
-  int32_t *fcCnt = nullptr, *fcRow = nullptr, *fcSlot = nullptr, *fcOrder = nullptr;
-  int8_t* fcBuf = nullptr;
+  std::vector<int64_t> hChat, hAnnz;                   // scans over heavy rows
+  std::vector<std::pair<int64_t, int64_t>> batches;   // heavy-row ranges
+  Batch kept{};          // the expansion symbolic leaves for numeric (one batch)
+  bool haveKept = false;
+  size_t wsCur = 0;      // workspace bytes currently held
   int32_t* slotNnz = nullptr;
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
@@ -239,7 +280,8 @@ namespace {
 void* plan_alloc(spgemm_plan_t p, size_t bytes, hipStream_t s) {
   if (bytes == 0) bytes = 16;
   bytes = (bytes + 255) & ~size_t(255);
-  p->demand += bytes;
+  p->wsCur += bytes;
+  p->demand = std::max(p->demand, p->wsCur);
   if (p->arena && p->arenaUsed + bytes <= p->arena->cap) {
     void* ptr = p->arena->base + p->arenaUsed;
     p->arenaUsed += bytes;
@@ -273,6 +315,27 @@ void release(spgemm_plan_t p) {
     }
   }
   p->allocs.clear();
+}
+
+// Workspace marks: everything allocated after a mark is given back by
+// ws_reset, in stream order on `s` (the only stream that used it), so the
+// next batch reuses the same memory.
+struct WsMark {
+  size_t arenaUsed, wsCur, nAllocs;
+};
+WsMark ws_mark(spgemm_plan_t p) { return WsMark{p->arenaUsed, p->wsCur, p->allocs.size()}; }
+void ws_reset(spgemm_plan_t p, const WsMark& mk, hipStream_t s) {
+  for (size_t i = mk.nAllocs; i < p->allocs.size(); ++i) {
+    auto& a = p->allocs[i];
+    if (p->opts.alloc) {
+      if (p->opts.free) p->opts.free(a.first, (void*)s, p->opts.alloc_ctx);
+    } else {
+      HIP_CHECK(hipFreeAsync(a.first, s));
+    }
+  }
+  p->allocs.resize(mk.nAllocs);
+  p->arenaUsed = mk.arenaUsed;
+  p->wsCur = mk.wsCur;
 }
 
 // Optional GPU timing of kernel phases: an event pair recorded on the
@@ -316,6 +379,7 @@ void arena_acquire(spgemm_plan_t p) {
     if (a.base) HIP_CHECK(hipFree(a.base));
     a.base = nullptr;
     a.cap = 0;
+    trim_pool(p->device);
     if (hipMalloc((void**)&a.base, a.highWater) == hipSuccess) {
       a.cap = a.highWater;
     } else {
@@ -339,6 +403,55 @@ void arena_release(spgemm_plan_t p) {
   if (hipEventRecord(a.done, p->stream) == hipSuccess) a.doneValid = true;
   a.busy = false;
   p->arena = nullptr;
+}
+
+// The heavy intermediate block of `bytes`: the device region if it is free
+// (grown first if needed), else an ordinary workspace allocation.
+char* heavy_region(spgemm_plan_t p, size_t bytes) {
+  if (!p->opts.alloc) {
+    Region& r = g_region[p->device & 63];
+    std::lock_guard<std::mutex> lk(r.mu);
+    if (!r.busy) {
+      if (!r.done) HIP_CHECK(hipEventCreateWithFlags(&r.done, hipEventDisableTiming));
+      if (r.cap < bytes) {
+        if (r.doneValid) HIP_CHECK(hipEventSynchronize(r.done));
+        if (r.base) HIP_CHECK(hipFree(r.base));
+        r.base = nullptr;
+        r.cap = 0;
+        trim_pool(p->device);
+        if (hipMalloc((void**)&r.base, bytes) == hipSuccess) {
+          r.cap = bytes;
+        } else {
+          (void)hipGetLastError();
+          r.base = nullptr;
+        }
+      }
+      if (r.base) {
+        if (r.doneValid) HIP_CHECK(hipStreamWaitEvent(p->sh, r.done, 0));
+        r.busy = true;
+        p->region = &r;
+        return r.base;
+      }
+    }
+  }
+  return (char*)plan_alloc(p, bytes, p->sh);
+}
+
+// Bytes of the region the device would give this plan without growing.
+size_t region_free(spgemm_plan_t p) {
+  if (p->opts.alloc) return 0;
+  Region& r = g_region[p->device & 63];
+  std::lock_guard<std::mutex> lk(r.mu);
+  return r.busy ? 0 : r.cap;
+}
+
+void region_release(spgemm_plan_t p) {
+  if (!p->region) return;
+  Region& r = *p->region;
+  std::lock_guard<std::mutex> lk(r.mu);
+  if (hipEventRecord(r.done, p->stream) == hipSuccess) r.doneValid = true;
+  r.busy = false;
+  p->region = nullptr;
 }
 
 void fork(spgemm_plan_t p) {
@@ -397,6 +510,7 @@ void do_plan(spgemm_plan_t p) {
   if ((int64_t)dense_num_lds(p->f64, p->params.dense_width) > ldsDev ||
       p->params.dense_width > 32768)
     throw Error{SPGEMM_ERR_INVALID_ARG, "dense width does not fit the LDS"};
+  if (p->opts.mem_budget < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "mem_budget must be >= 0"};
   make_bins(p->tau, p->lds, vb, &p->symBins, &p->numBins);
   p->NS = (int)p->symBins.size();
   if (p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
@@ -494,22 +608,89 @@ void do_plan(spgemm_plan_t p) {
 }
 
 // -------------------------------------------------------------- symbolic
-void heavy_symbolic(spgemm_plan_t p) {
+// ---------------------------------------------------------------- heavy
+// Heavy rows are processed in batches of consecutive heavy rows whose
+// intermediate fits the memory budget.  With one batch the expansion made by
+// symbolic is kept for numeric (gMAGNUS Alg. 3); with several, symbolic
+// keeps only the chunk counts and numeric expands every batch again.
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Column and value buffers for `Pb` elements: one pair, or two with levels.
+size_t heavy_buf_bytes(spgemm_plan_t p, int64_t Pb) {
+  const size_t n = (size_t)std::max<int64_t>(Pb, 1);
+  const size_t pair = align256(n * 4) + align256(n * (p->f64 ? 8 : 4));
+  return (p->params.levels > 0 ? 2 : 1) * pair;
+}
+
+// Per heavy row: products (C-hat row length) and nnz of its A row, both
+// scanned, copied to the host; then the batch boundaries.
+void heavy_prepare(spgemm_plan_t p) {
   hipStream_t s = p->sh;
-  const int64_t h = p->h, Ph = p->Ph, nE = p->nAh;
+  const int64_t h = p->h;
+  int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, s);
+  int64_t* hv = alloc_n<int64_t>(p, h, s);
+  int64_t* pref = alloc_n<int64_t>(p, h + 1, s);
+  p->hChat.assign(h + 1, 0);
+  p->hAnnz.assign(h + 1, 0);
+  launch_gather_i64(p->rowP, p->xheavy, h, hv, s);
+  launch_scan_i64(hv, h, pref, tmp, s);
+  HIP_CHECK(hipMemcpyAsync(p->hChat.data(), pref, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
+  launch_row_lengths(h, p->xheavy, p->arp, hv, s);
+  launch_scan_i64(hv, h, pref, tmp, s);
+  HIP_CHECK(hipMemcpyAsync(p->hAnnz.data(), pref, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
+  check_launch("heavy prepare");
+  HIP_CHECK(hipStreamSynchronize(s));
+  // Bytes of intermediate per heavy element: one or two (col, val) buffers.
+  const int64_t vb = p->f64 ? 8 : 4;
+  const int64_t perElem = (p->params.levels > 0 ? 2 : 1) * (4 + vb);
+  int64_t budget = p->opts.mem_budget;
+  if (!budget) {
+    size_t freeB = 0, totalB = 0;
+    HIP_CHECK(hipMemGetInfo(&freeB, &totalB));
+    int64_t avail = (int64_t)freeB + (int64_t)region_free(p);
+    if (p->arena) avail += (int64_t)(p->arena->cap - p->arenaUsed);
+    budget = std::max<int64_t>(avail * 45 / 100, (int64_t)1 << 30);
+  }
+  const int64_t cap = std::max<int64_t>(budget / perElem, 1);
+  p->batches.clear();
+  int64_t r0 = 0, maxPb = 0;
+  while (r0 < h) {
+    int64_t r1 = r0 + 1;  // at least one row per batch
+    while (r1 < h && p->hChat[r1 + 1] - p->hChat[r0] <= cap) ++r1;
+    p->batches.push_back({r0, r1});
+    maxPb = std::max(maxPb, p->hChat[r1] - p->hChat[r0]);
+    r0 = r1;
+  }
+  p->st.batches = (int64_t)p->batches.size();
+  p->heavyBuf = heavy_region(p, heavy_buf_bytes(p, maxPb));
+}
+
+// Expand heavy rows [hb0, hb1): CSC, outer product, multisplit levels, the
+// final chunk list and its numeric bins.
+void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, Batch* B) {
+  hipStream_t s = p->sh;
+  const int64_t hb = hb1 - hb0;
+  const int64_t Pb = p->hChat[hb1] - p->hChat[hb0];
+  const int64_t nE = p->hAnnz[hb1] - p->hAnnz[hb0];
+  const int32_t* xb = p->xheavy + hb0;
   const bool f64 = p->f64;
   const size_t vb = f64 ? 8 : 4;
   const int64_t W = p->params.dense_width;
-  int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(std::max<int64_t>({h, nE, p->k, 1}) + 1), s);
+  *B = Batch{};
+  B->hb0 = hb0;
+  B->hb1 = hb1;
+  B->Pb = Pb;
+  int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(std::max<int64_t>({hb, nE, p->k, 1}) + 1), s);
   const int phCsc = ph_begin(p, SPGEMM_PH_CSC, s);
 
-  // C-hat row pointers: scan of the heavy rows' product counts.
-  int64_t* hP = alloc_n<int64_t>(p, h, s);
-  int64_t* chatRowPtr = alloc_n<int64_t>(p, h + 1, s);
-  launch_gather_i64(p->rowP, p->xheavy, h, hP, s);
-  launch_scan_i64(hP, h, chatRowPtr, tmp, s);
+  // C-hat row pointers of the batch: scan of its rows' product counts.
+  int64_t* hP = alloc_n<int64_t>(p, hb, s);
+  int64_t* chatRowPtr = alloc_n<int64_t>(p, hb + 1, s);
+  launch_gather_i64(p->rowP, xb, hb, hP, s);
+  launch_scan_i64(hP, hb, chatRowPtr, tmp, s);
 
-  // Masked CSR -> CSC of A restricted to the heavy rows.
+  // Masked CSR -> CSC of A restricted to the batch's heavy rows.
   int32_t* colCnt = alloc_n<int32_t>(p, p->k, s);
   int64_t* colPtr = alloc_n<int64_t>(p, p->k + 1, s);
   int64_t* colFill = alloc_n<int64_t>(p, p->k, s);
@@ -517,33 +698,37 @@ void heavy_symbolic(spgemm_plan_t p) {
   int32_t* cscCol = alloc_n<int32_t>(p, nE, s);
   void* cscVal = plan_alloc(p, std::max<int64_t>(nE, 1) * vb, s);
   launch_fill_i32(colCnt, 0, p->k, s);
-  launch_csc_count(h, p->xheavy, p->arp, p->acol, colCnt, s);
+  launch_csc_count(hb, xb, p->arp, p->acol, colCnt, s);
   launch_scan_i32(colCnt, p->k, colPtr, tmp, s);
   launch_copy_i64(colFill, colPtr, p->k, s);
-  launch_csc_fill(h, p->xheavy, p->arp, p->acol, p->aval, f64, colFill, cscRow, cscCol, cscVal, s);
+  launch_csc_fill(hb, xb, p->arp, p->acol, p->aval, f64, colFill, cscRow, cscCol, cscVal, s);
 
   // Flattened element offsets of the CSC entries and their C-hat segments.
   int64_t* nb = alloc_n<int64_t>(p, nE, s);
   int64_t* entryOff = alloc_n<int64_t>(p, nE + 1, s);
-  int64_t* cursor = alloc_n<int64_t>(p, h, s);
+  int64_t* cursor = alloc_n<int64_t>(p, hb, s);
   int64_t* segBase = alloc_n<int64_t>(p, nE, s);
   launch_entry_products(nE, cscCol, p->brp, nb, s);
   launch_scan_i64(nb, nE, entryOff, tmp, s);
-  launch_copy_i64(cursor, chatRowPtr, h, s);
+  launch_copy_i64(cursor, chatRowPtr, hb, s);
   launch_seg_base(nE, cscRow, nb, cursor, segBase, s);
   ph_end(p, phCsc, s);
 
   // Outer product into buffer 0.
   const int L = p->params.levels;
-  p->bufCol[0] = alloc_n<int32_t>(p, Ph, s);
-  p->bufVal[0] = plan_alloc(p, std::max<int64_t>(Ph, 1) * vb, s);
-  if (L > 0) {
-    p->bufCol[1] = alloc_n<int32_t>(p, Ph, s);
-    p->bufVal[1] = plan_alloc(p, std::max<int64_t>(Ph, 1) * vb, s);
+  {
+    char* q = p->heavyBuf;
+    const size_t n = (size_t)std::max<int64_t>(Pb, 1);
+    for (int b = 0; b < (L > 0 ? 2 : 1); ++b) {
+      B->bufCol[b] = (int32_t*)q;
+      q += align256(n * 4);
+      B->bufVal[b] = q;
+      q += align256(n * vb);
+    }
   }
   const int phOp = ph_begin(p, SPGEMM_PH_OUTER_PRODUCT, s);
-  launch_outer_product(f64, Ph, entryOff, nE, cscCol, cscVal, segBase, p->brp, p->bcol, p->bval,
-                       p->bufCol[0], p->bufVal[0], s);
+  launch_outer_product(f64, Pb, entryOff, nE, cscCol, cscVal, segBase, p->brp, p->bcol, p->bval,
+                       B->bufCol[0], B->bufVal[0], s);
   ph_end(p, phOp, s);
   check_launch("outer product");
 
@@ -555,12 +740,12 @@ void heavy_symbolic(spgemm_plan_t p) {
   };
   std::vector<Piece> pieces;
   bool completed = (L == 0);
-  int64_t R = h, E = Ph;
+  int64_t R = hb, E = Pb;
   const int64_t* rowPtr = chatRowPtr;
   const int32_t *inRow = nullptr, *inSlot = nullptr;
   int cur = 0;
   for (int l = 0; l < L; ++l) {
-    p->st.level_elems[l] = E;
+    B->levelElems[l] = E;
     const int v = p->params.v_chunks[l];
     const int64_t w = p->params.level_width[l];
     const int shift = log2_exact(w);
@@ -583,7 +768,7 @@ void heavy_symbolic(spgemm_plan_t p) {
     int maxRows;
     multisplit_geometry(f64, p->tau, v, &blockElems, &maxRows);
     const int phH = ph_begin(p, SPGEMM_PH_HISTOGRAM, s);
-    launch_histogram(E, blockElems, rowPtr, R, p->bufCol[cur], shift, v, maxRows, counts,
+    launch_histogram(E, blockElems, rowPtr, R, B->bufCol[cur], shift, v, maxRows, counts,
                      p->errWord, s);
     ph_end(p, phH, s);
     launch_partition(Q, counts, p->tau, last, v, inRow, inSlot, (int32_t)(w / W), inv, newCnt,
@@ -592,8 +777,8 @@ void heavy_symbolic(spgemm_plan_t p) {
     launch_copy_i64(cur64, newOff, Q, s);
     const int out = 1 - cur;
     const int phM = ph_begin(p, SPGEMM_PH_MULTISPLIT, s);
-    launch_multisplit(f64, E, blockElems, rowPtr, R, p->bufCol[cur], p->bufVal[cur], shift, v,
-                      (int32_t)(w - 1), maxRows, inv, cur64, p->bufCol[out], p->bufVal[out],
+    launch_multisplit(f64, E, blockElems, rowPtr, R, B->bufCol[cur], B->bufVal[cur], shift, v,
+                      (int32_t)(w - 1), maxRows, inv, cur64, B->bufCol[out], B->bufVal[out],
                       p->errWord, s);
     ph_end(p, phM, s);
     check_launch("multisplit level");
@@ -621,88 +806,160 @@ void heavy_symbolic(spgemm_plan_t p) {
   // of the last level (or the heavy rows themselves with no multisplit).
   int64_t nfc = 0;
   for (auto& pc : pieces) nfc += pc.n;
-  if (L == 0) nfc = h;
-  p->nfc = nfc;
-  p->fcOff = alloc_n<int64_t>(p, nfc, s);
-  p->fcCnt = alloc_n<int32_t>(p, nfc, s);
-  p->fcRow = alloc_n<int32_t>(p, nfc, s);
-  p->fcSlot = alloc_n<int32_t>(p, nfc, s);
-  p->fcBuf = alloc_n<int8_t>(p, nfc, s);
+  if (L == 0) nfc = hb;
+  B->nfc = nfc;
+  B->fcOff = alloc_n<int64_t>(p, nfc, s);
+  B->fcCnt = alloc_n<int32_t>(p, nfc, s);
+  B->fcRow = alloc_n<int32_t>(p, nfc, s);
+  B->fcSlot = alloc_n<int32_t>(p, nfc, s);
+  B->fcBuf = alloc_n<int8_t>(p, nfc, s);
   if (L == 0) {
-    launch_final_from_rows(h, chatRowPtr, p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, s);
-    p->lastFirst = 0;
+    launch_final_from_rows(hb, chatRowPtr, B->fcOff, B->fcCnt, B->fcRow, B->fcSlot, B->fcBuf, s);
+    B->lastFirst = 0;
   } else {
     int64_t dst = 0;
     for (auto& pc : pieces) {
       launch_final_from_level(pc.first, pc.n, pc.newOff, pc.newCnt, pc.newRow, pc.newSlot, pc.buf,
-                              dst, p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, s);
+                              dst, B->fcOff, B->fcCnt, B->fcRow, B->fcSlot, B->fcBuf, s);
       dst += pc.n;
     }
-    p->lastFirst = completed ? nfc - pieces.back().n : nfc;
+    B->lastFirst = completed ? nfc - pieces.back().n : nfc;
   }
+  // Numeric bins: W-wide chunks with more than W/8 elements (or tau, if
+  // smaller) go to the dense accumulator, at that density zeroing and
+  // scanning W columns is cheaper than hashing; the rest by element count.
   uint8_t* key = alloc_n<uint8_t>(p, nfc, s);
-  p->fcOrder = alloc_n<int32_t>(p, nfc, s);
+  B->fcOrder = alloc_n<int32_t>(p, nfc, s);
   int32_t* bc = alloc_n<int32_t>(p, 64, s);
   int32_t* bf = alloc_n<int32_t>(p, 64, s);
   int32_t* bs = alloc_n<int32_t>(p, 65, s);
-  // W-wide chunks with more than W/8 elements (or tau, if smaller) go to the
-  // dense accumulator: at that density zeroing and scanning W columns is
-  // cheaper than hashing.
   const int64_t denseMin = std::min<int64_t>(p->tau, W / 8);
-  launch_chunk_bins(nfc, p->fcCnt, p->lastFirst, denseMin, p->dSymCaps, p->NS, p->NS, key,
-                    p->stats + kStatDenseElems, s);
-  launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, p->fcOrder, s);
+  launch_chunk_bins(nfc, B->fcCnt, B->lastFirst, denseMin, p->dSymCaps, p->NS, p->NS, key,
+                    countStats ? p->stats + kStatDenseElems : nullptr, s);
+  launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, B->fcOrder, s);
   HIP_CHECK(hipMemcpyAsync(p->hBins + 64, bs, sizeof(int32_t) * (p->NS + 2), hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
-  p->fcBinStart.assign(p->hBins + 64, p->hBins + 64 + p->NS + 2);
+  B->fcBinStart.assign(p->hBins + 64, p->hBins + 64 + p->NS + 2);
+  B->denseChunks = B->fcBinStart[p->NS + 1] - B->fcBinStart[p->NS];
+}
 
-  p->slotNnz = alloc_n<int32_t>(p, h * p->nreq, s);
-  p->slotOff = alloc_n<int64_t>(p, h * p->nreq, s);
-  launch_fill_i32(p->slotNnz, 0, h * p->nreq, s);
-  ChunkList cl{p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, p->bufCol[0], p->bufCol[1],
-               p->bufVal[0], p->bufVal[1], W, p->nreq, p->xheavy, p->slotOff, p->slotNnz};
-  p->st.dense_chunks = p->fcBinStart[p->NS + 1] - p->fcBinStart[p->NS];
-  // Widest final chunk: the first level's width (or W with no multisplit).
-  const int64_t maxWidth = L == 0 ? W : p->params.level_width[0];
-  if (maxWidth <= 65536) {
-    // Bitmap symbolic for every chunk, in three size classes.
-    p->chunkWords = (int32_t)((maxWidth + 31) / 32);
-    make_rank_bins(p->lds, f64, p->chunkWords, p->symBins, &p->rankBins);
+ChunkList chunk_list(spgemm_plan_t p, const Batch& B) {
+  return ChunkList{B.fcOff, B.fcCnt, B.fcRow, B.fcSlot, B.fcBuf, B.bufCol[0], B.bufCol[1],
+                   B.bufVal[0], B.bufVal[1], p->params.dense_width, p->nreq,
+                   p->xheavy + B.hb0, p->slotOff + B.hb0 * p->nreq,
+                   p->slotNnz + B.hb0 * p->nreq};
+}
+
+// Chunk symbolic: per-chunk nnz into the batch's slots.
+void symbolic_batch(spgemm_plan_t p, const Batch& B) {
+  hipStream_t s = p->sh;
+  const int64_t nfc = B.nfc;
+  const ChunkList cl = chunk_list(p, B);
+  if (p->chunkWords) {
     uint8_t* skey = alloc_n<uint8_t>(p, nfc, s);
-    p->fcOrderSym = alloc_n<int32_t>(p, nfc, s);
+    int32_t* order = alloc_n<int32_t>(p, nfc, s);
     int32_t* sc = alloc_n<int32_t>(p, 64, s);
     int32_t* sf = alloc_n<int32_t>(p, 64, s);
     int32_t* ss = alloc_n<int32_t>(p, 65, s);
-    int32_t* dcc = alloc_n<int32_t>(p, 4, s);
-    const int32_t classCaps[3] = {256, 4096, INT32_MAX};
-    std::memcpy(p->hBins + 110, classCaps, sizeof(classCaps));
-    HIP_CHECK(hipMemcpyAsync(dcc, p->hBins + 110, sizeof(classCaps), hipMemcpyHostToDevice, s));
-    launch_chunk_bins(nfc, p->fcCnt, nfc, INT32_MAX, dcc, 3, 3, skey, nullptr, s);
-    launch_bin_sort(skey, nfc, 3, sc, sf, ss, p->fcOrderSym, s);
+    launch_chunk_bins(nfc, B.fcCnt, nfc, INT32_MAX, p->dClassCaps, 3, 3, skey, nullptr, s);
+    launch_bin_sort(skey, nfc, 3, sc, sf, ss, order, s);
     HIP_CHECK(hipMemcpyAsync(p->hBins + 104, ss, sizeof(int32_t) * 4, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
-    p->fcSymStart.assign(p->hBins + 104, p->hBins + 108);
-    const int phSc = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
-    for (int c = 0; c < 3; ++c) {
-      const int64_t a = p->fcSymStart[c], e = p->fcSymStart[c + 1];
-      launch_sym_chunks_bitmap(c, p->fcOrderSym + a, e - a, p->chunkWords, cl, s);
-    }
-    ph_end(p, phSc, s);
+    const std::vector<int32_t> st(p->hBins + 104, p->hBins + 108);
+    const int ph = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
+    for (int c = 0; c < 3; ++c)
+      launch_sym_chunks_bitmap(c, order + st[c], st[c + 1] - st[c], p->chunkWords, cl, s);
+    ph_end(p, ph, s);
   } else {
-    const int phSc = ph_begin(p, SPGEMM_PH_SYM_CHUNK_HASH, s);
+    const int ph = ph_begin(p, SPGEMM_PH_SYM_CHUNK_HASH, s);
     for (int b = 0; b < p->NS; ++b) {
-      const int64_t a = p->fcBinStart[b], e = p->fcBinStart[b + 1];
-      launch_sym_chunks(p->symBins[b], p->fcOrder + a, e - a, cl, p->errWord, s);
+      const int64_t a = B.fcBinStart[b], e = B.fcBinStart[b + 1];
+      launch_sym_chunks(p->symBins[b], B.fcOrder + a, e - a, cl, p->errWord, s);
     }
-    ph_end(p, phSc, s);
-    const int64_t a = p->fcBinStart[p->NS], e = p->fcBinStart[p->NS + 1];
-    const int phSd = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
-    launch_dense_sym(p->fcOrder + a, e - a, cl, p->errWord, s);
-    ph_end(p, phSd, s);
+    ph_end(p, ph, s);
+    const int64_t a = B.fcBinStart[p->NS], e = B.fcBinStart[p->NS + 1];
+    const int phD = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
+    launch_dense_sym(B.fcOrder + a, e - a, cl, p->errWord, s);
+    ph_end(p, phD, s);
+  }
+  check_launch("chunk symbolic");
+}
+
+void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval) {
+  hipStream_t s = p->sh;
+  const ChunkList cl = chunk_list(p, B);
+  const int ph = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
+  for (int b = 0; b < p->NS; ++b) {
+    const int64_t st = B.fcBinStart[b], en = B.fcBinStart[b + 1];
+    if (p->chunkWords)
+      launch_num_chunks_rank(p->rankBins[b], p->f64, B.fcOrder + st, en - st, p->chunkWords, cl,
+                             p->cRowOff, ccol, cval, p->errWord, s);
+    else
+      launch_num_chunks(p->numBins[b], p->f64, B.fcOrder + st, en - st, cl, p->cRowOff, ccol,
+                        cval, p->errWord, s);
+  }
+  ph_end(p, ph, s);
+  const int64_t st = B.fcBinStart[p->NS], en = B.fcBinStart[p->NS + 1];
+  const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
+  launch_dense_num(p->f64, B.fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord, s);
+  ph_end(p, phD, s);
+  check_launch("chunk numeric");
+}
+
+void heavy_symbolic(spgemm_plan_t p) {
+  hipStream_t s = p->sh;
+  const int64_t h = p->h, W = p->params.dense_width;
+  const int L = p->params.levels;
+  heavy_prepare(p);
+  p->slotNnz = alloc_n<int32_t>(p, h * p->nreq, s);
+  p->slotOff = alloc_n<int64_t>(p, h * p->nreq, s);
+  launch_fill_i32(p->slotNnz, 0, h * p->nreq, s);
+  // Bitmap chunk symbolic and rank numeric when the widest final chunk (the
+  // first level's width, or W with no multisplit) is at most 64 Kbit.
+  const int64_t maxWidth = L == 0 ? W : p->params.level_width[0];
+  if (maxWidth <= 65536) {
+    p->chunkWords = (int32_t)((maxWidth + 31) / 32);
+    make_rank_bins(p->lds, p->f64, p->chunkWords, p->symBins, &p->rankBins);
+    p->dClassCaps = alloc_n<int32_t>(p, 4, s);
+    const int32_t classCaps[3] = {256, 4096, INT32_MAX};
+    std::memcpy(p->hBins + 110, classCaps, sizeof(classCaps));
+    HIP_CHECK(hipMemcpyAsync(p->dClassCaps, p->hBins + 110, sizeof(classCaps), hipMemcpyHostToDevice, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+  }
+  p->st.final_chunks = 0;
+  p->st.dense_chunks = 0;
+  const bool single = p->batches.size() == 1;
+  for (const auto& bt : p->batches) {
+    const WsMark mk = ws_mark(p);
+    Batch B;
+    expand_batch(p, bt.first, bt.second, true, &B);
+    symbolic_batch(p, B);
+    p->st.final_chunks += B.nfc;
+    p->st.dense_chunks += B.denseChunks;
+    for (int l = 0; l < 8; ++l) p->st.level_elems[l] += B.levelElems[l];
+    if (single) {
+      p->kept = B;
+      p->haveKept = true;
+    } else {
+      ws_reset(p, mk, s);
+    }
   }
   launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
   check_launch("heavy symbolic");
-  p->st.final_chunks = nfc;
+}
+
+void heavy_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
+  if (p->haveKept) {
+    numeric_batch(p, p->kept, ccol, cval);
+    return;
+  }
+  for (const auto& bt : p->batches) {
+    const WsMark mk = ws_mark(p);
+    Batch B;
+    expand_batch(p, bt.first, bt.second, false, &B);
+    numeric_batch(p, B, ccol, cval);
+    ws_reset(p, mk, p->sh);
+  }
 }
 
 void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
@@ -743,7 +1000,6 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   p->st.lds_dense_products = p->hStats[kStatDenseElems];
   p->st.lds_hash_products = p->st.products - p->st.lds_dense_products;
   p->st.global_products = 0;
-  p->st.batches = p->h > 0 ? 1 : 0;
   if (!p->opts.rowptr64 && p->nnzC > INT32_MAX)
     throw Error{SPGEMM_ERR_INDEX_OVERFLOW, "nnz(C) exceeds INT32_MAX; request rowptr64"};
   launch_write_rowptr(p->cRowOff, m + 1, dRowPtr, p->opts.rowptr64 ? 1 : 0, s);
@@ -764,28 +1020,7 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   }
   ph_end(p, phL, p->sl);
   check_launch("light numeric");
-  if (p->h > 0) {
-    hipStream_t s = p->sh;
-    ChunkList cl{p->fcOff, p->fcCnt, p->fcRow, p->fcSlot, p->fcBuf, p->bufCol[0], p->bufCol[1],
-                 p->bufVal[0], p->bufVal[1], p->params.dense_width, p->nreq, p->xheavy,
-                 p->slotOff, p->slotNnz};
-    const int phH = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
-    for (int b = 0; b < p->NS; ++b) {
-      const int64_t st = p->fcBinStart[b], en = p->fcBinStart[b + 1];
-      if (p->chunkWords)
-        launch_num_chunks_rank(p->rankBins[b], p->f64, p->fcOrder + st, en - st, p->chunkWords,
-                               cl, p->cRowOff, ccol, cval, p->errWord, s);
-      else
-        launch_num_chunks(p->numBins[b], p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol,
-                          cval, p->errWord, s);
-    }
-    ph_end(p, phH, s);
-    const int64_t st = p->fcBinStart[p->NS], en = p->fcBinStart[p->NS + 1];
-    const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
-    launch_dense_num(p->f64, p->fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord, s);
-    ph_end(p, phD, s);
-    check_launch("heavy numeric");
-  }
+  if (p->h > 0) heavy_numeric(p, ccol, cval);
   join(p);
   p->st.ms_numeric = now_ms() - t0;
 }
@@ -828,6 +1063,7 @@ void destroy_plan(spgemm_plan_t p) {
     (void)hipStreamWaitEvent(p->sh, p->evFork, 0);
   }
   arena_release(p);
+  region_release(p);
   release(p);
   if (!p->phases.empty()) (void)hipStreamSynchronize(p->stream);
   for (auto& r : p->phases) {

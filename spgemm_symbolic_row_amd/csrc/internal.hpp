@@ -97,6 +97,9 @@ void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
 void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hipStream_t s);
 void launch_gather_i64(const int64_t* src, const int32_t* idx, int64_t n, int64_t* dst,
                        hipStream_t s);
+// dst[i] = rp[rows[i] + 1] - rp[rows[i]]
+void launch_row_lengths(int64_t n, const int32_t* rows, const int32_t* rp, int64_t* dst,
+                        hipStream_t s);
 // key[i] = bin of cnt[rows[i]] among caps[0..nbins) (first cap >= value), for
 // light rows; heavy rows (rowBin == heavyBin) get 255.
 void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,

@@ -35,6 +35,15 @@ __global__ __launch_bounds__(kNT) void k_gather_i64(const int64_t* __restrict__ 
     dst[i] = src[idx[i]];
 }
 
+__global__ __launch_bounds__(kNT) void k_row_lengths(const int32_t* __restrict__ rows, int64_t n,
+                                                     const int32_t* __restrict__ rp,
+                                                     int64_t* __restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x; i < n; i += (int64_t)gridDim.x * kNT) {
+    const int32_t r = rows[i];
+    dst[i] = rp[r + 1] - rp[r];
+  }
+}
+
 // ---- exclusive scan: tile sums, one-block scan of tile sums, down-sweep ----
 constexpr int kScanItems = 16;
 constexpr int kScanTile = kNT * kScanItems;
@@ -324,6 +333,14 @@ void launch_gather_i64(const int64_t* src, const int32_t* idx, int64_t n, int64_
   unsigned g = grid_for(n, kNT * 4);
   if (g > 65536) g = 65536;
   hipLaunchKernelGGL(k_gather_i64, dim3(g), dim3(kNT), 0, s, src, idx, n, dst);
+}
+
+void launch_row_lengths(int64_t n, const int32_t* rows, const int32_t* rp, int64_t* dst,
+                        hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_row_lengths, dim3(g), dim3(kNT), 0, s, rows, n, rp, dst);
 }
 
 int64_t scan_tmp_elems(int64_t n) { return cdiv(n > 0 ? n : 1, kScanTile); }

@@ -174,6 +174,33 @@ def test_options_do_not_change_the_result():
         np.testing.assert_array_equal(val, ref[2])
 
 
+@pytest.mark.parametrize("budget", [1, 200_000])
+def test_heavy_rows_in_batches(budget):
+    # A memory budget far below the intermediate's size splits the heavy rows
+    # into batches (one row each at budget 1); symbolic keeps only chunk
+    # counts and numeric expands every batch again.
+    A = synth.rmat(11 if budget == 1 else 12, 16, seed=5)
+    A.val = np.round(A.val * 6 - 3)
+    opts = dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4)
+    st = check_full(A, A, exact=True, mem_budget=budget, **opts)
+    assert st["batches"] > 1
+    if budget == 1:
+        assert st["batches"] == st["heavy_rows"]
+    one = gpu_product(A, A, **opts)
+    assert one[3]["batches"] == 1
+    for a, b in zip(gpu_product(A, A, mem_budget=budget, **opts)[:3], one[:3]):
+        np.testing.assert_array_equal(a, b)
+    assert st["level_elems"] == one[3]["level_elems"]
+    assert st["final_chunks"] == one[3]["final_chunks"]
+
+
+def test_batches_fp32_multilevel():
+    A = synth.rmat(12, 16, seed=8, dtype=np.float32)
+    st = check_full(A, A, mem_budget=300_000, heavy_threshold=48, dense_width=256,
+                    max_chunks_per_level=2)
+    assert st["batches"] > 1 and st["params"]["levels"] == 4   # 4096 / 256 = 2^4
+
+
 def test_validate_rejects_non_canonical():
     A = synth.random_csr(50, 50, 4.0, 1)
     bad = synth.CSR(A.row_ptr.copy(), A.col.copy(), A.val.copy(), 50, 50)
@@ -274,3 +301,22 @@ def test_mcl_config_sampled_and_prune_properties():
     nz = torch.bincount(ocol.long(), minlength=A.n) > 0
     assert float((cs2[nz] - 1).abs().max()) < 1e-5
     del rp, col, val, orp, ocol, oval
+
+
+def test_rmat20_config_sampled_batched_rowptr64():
+    A = synth.workload("rmat20")
+    P = oracle.row_products(A, A)
+    rng = np.random.default_rng(3)
+    heavy = np.nonzero(P > 6826)[0]
+    light = np.nonzero((P > 0) & (P <= 6826))[0]
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(heavy, 200, replace=False),
+                                     rng.choice(light, 1000, replace=False), [A.m - 1]]))
+    torch.cuda.empty_cache()
+    rp_h, st, out = _sampled_check(A, rows, rowptr64=1)
+    del out
+    torch.cuda.empty_cache()
+    assert st["params"]["v_chunks"] == [32, 2] and st["params"]["levels"] == 2
+    assert st["heavy_rows"] == heavy.size and st["heavy_products"] == int(P[heavy].sum())
+    assert st["batches"] > 1
+    cnt = oracle.symbolic(A, A)
+    np.testing.assert_array_equal(np.diff(rp_h), cnt)
