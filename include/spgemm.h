@@ -84,7 +84,12 @@ typedef struct spgemm_options {
   int32_t profile;              /* 1: time each kernel phase with HIP events
                                    recorded on the stream it runs on; read the
                                    result from spgemm_stats.phase_ms           */
-  int32_t reserved32;
+  int32_t histogram_from_data;  /* 1: count each level's (row, chunk) elements
+                                   by reading the expanded columns (K6 as the
+                                   gMAGNUS page prints it); 0: derive the same
+                                   counts from the structure of A and of B's
+                                   rows (default; the read pass is also used
+                                   when n_req exceeds 8192)                    */
   spgemm_alloc_fn alloc;        /* optional allocator (see above)               */
   spgemm_free_fn free;
   void *alloc_ctx;
@@ -118,7 +123,8 @@ typedef enum spgemm_phase {
   SPGEMM_PH_NUM_LIGHT = 9,       /* light-row LDS hash numeric + sort           */
   SPGEMM_PH_NUM_CHUNK_HASH = 10, /* light-chunk hash numeric + sort             */
   SPGEMM_PH_NUM_CHUNK_DENSE = 11,/* heavy-chunk dense LDS numeric               */
-  SPGEMM_PH_COUNT = 12
+  SPGEMM_PH_CHUNK_HIST = 12,     /* per-row W-wide chunk counts from structure  */
+  SPGEMM_PH_COUNT = 13
 } spgemm_phase;
 
 typedef struct spgemm_stats {

@@ -33,7 +33,7 @@ class Options(ctypes.Structure):
         ("lds_budget", c_i64), ("heavy_threshold", c_i64), ("dense_width", c_i64),
         ("mem_budget", c_i64), ("max_chunks_per_level", c_i32), ("rowptr64", c_i32),
         ("validate", c_i32), ("single_stream", c_i32), ("profile", c_i32),
-        ("reserved32", c_i32), ("alloc", c_vp), ("free", c_vp),
+        ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
         ("alloc_ctx", c_vp), ("reserved", c_i64 * 8),
     ]
 
@@ -77,7 +77,7 @@ class Stats(ctypes.Structure):
 
 PHASES = ["row_info", "sym_light", "csc", "outer_product", "histogram", "multisplit",
           "sym_chunk_hash", "sym_chunk_dense", "rowptr", "num_light", "num_chunk_hash",
-          "num_chunk_dense"]
+          "num_chunk_dense", "chunk_hist"]
 
 
 SPGEMM_F32, SPGEMM_F64 = 0, 1

@@ -264,6 +264,7 @@ struct spgemm_plan_s {
   Batch kept{};          // the expansion symbolic leaves for numeric (one batch)
   bool haveKept = false;
   size_t wsCur = 0;      // workspace bytes currently held
+  int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
   int32_t* slotNnz = nullptr;
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
@@ -664,6 +665,28 @@ void heavy_prepare(spgemm_plan_t p) {
   }
   p->st.batches = (int64_t)p->batches.size();
   p->heavyBuf = heavy_region(p, heavy_buf_bytes(p, maxPb));
+
+  // Chunk counts of every heavy row from the structure, for all levels.
+  const int64_t nreq = p->nreq;
+  if (p->params.levels > 0 && !p->opts.histogram_from_data && nreq <= 8192) {
+    const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, s);
+    p->CH = alloc_n<int32_t>(p, h * nreq, s);
+    const WsMark mk = ws_mark(p);
+    const int64_t nnzB = p->nnzB;
+    int32_t* flags = alloc_n<int32_t>(p, nnzB, s);
+    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, s);
+    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
+    int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, s);
+    int32_t* runChunk = alloc_n<int32_t>(p, nnzB, s);
+    int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, s);
+    launch_b_runs(p->k, nnzB, p->brp, p->bcol, log2_exact(p->params.dense_width), flags, runIdx,
+                  stmp, runPtr, runChunk, runStart, s);
+    launch_chunk_hist_rows(h, p->xheavy, p->arp, p->acol, runPtr, runChunk, runStart,
+                           (int32_t)nreq, p->CH, s);
+    check_launch("chunk histogram");
+    ws_reset(p, mk, s);
+    ph_end(p, ph, s);
+  }
 }
 
 // Expand heavy rows [hb0, hb1): CSC, outer product, multisplit levels, the
@@ -761,15 +784,19 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, Ba
     int64_t* cur64 = alloc_n<int64_t>(p, Q, s);
     int32_t* ctr = alloc_n<int32_t>(p, 2, s);
     int64_t* ltmp = alloc_n<int64_t>(p, scan_tmp_elems(Q) + 1, s);
-    launch_fill_i32(counts, 0, Q, s);
+    if (!p->CH) launch_fill_i32(counts, 0, Q, s);
     launch_fill_i32(newCnt, 0, Q, s);
     launch_fill_i32(ctr, 0, 2, s);
     int32_t blockElems;
     int maxRows;
     multisplit_geometry(f64, p->tau, v, &blockElems, &maxRows);
     const int phH = ph_begin(p, SPGEMM_PH_HISTOGRAM, s);
-    launch_histogram(E, blockElems, rowPtr, R, B->bufCol[cur], shift, v, maxRows, counts,
-                     p->errWord, s);
+    if (p->CH)
+      launch_level_counts(Q, v, (int32_t)(w / W), (int32_t)p->nreq, inRow, inSlot,
+                          p->CH + hb0 * p->nreq, counts, s);
+    else
+      launch_histogram(E, blockElems, rowPtr, R, B->bufCol[cur], shift, v, maxRows, counts,
+                       p->errWord, s);
     ph_end(p, phH, s);
     launch_partition(Q, counts, p->tau, last, v, inRow, inSlot, (int32_t)(w / W), inv, newCnt,
                      newRow, newSlot, ctr, s);

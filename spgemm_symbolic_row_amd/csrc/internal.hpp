@@ -143,6 +143,19 @@ void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int*
 void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
                       const int32_t* col, int shift, int v, int maxRows, int32_t* counts,
                       int32_t* err, hipStream_t s);
+// Runs of equal W-wide chunk in B's rows (chunk = col >> shift): runPtr[K+1],
+// runChunk/runStart[runs + 1]; flags[nnzB] and runIdx[nnzB + 1] are scratch.
+void launch_b_runs(int64_t K, int64_t nnzB, const int32_t* brp, const int32_t* bcol, int shift,
+                   int32_t* flags, int64_t* runIdx, int64_t* scanTmp, int32_t* runPtr,
+                   int32_t* runChunk, int32_t* runStart, hipStream_t s);
+// CH[i][f] = products of row rows[i] in W-wide chunk f (nreq <= 16384).
+void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,
+                            const int32_t* acol, const int32_t* runPtr, const int32_t* runChunk,
+                            const int32_t* runStart, int32_t nreq, int32_t* CH, hipStream_t s);
+// One level's (row, chunk) counts as sums of `span` W-wide counts.
+void launch_level_counts(int64_t Q, int v, int32_t span, int32_t nreq, const int32_t* inRow,
+                         const int32_t* inSlot, const int32_t* CH, int32_t* counts,
+                         hipStream_t s);
 void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, int v,
                       const int32_t* inRow, const int32_t* inSlot, int32_t slotStep,
                       int32_t* inv, int32_t* newCnt, int32_t* newRow, int32_t* newSlot,

@@ -194,6 +194,27 @@ def test_heavy_rows_in_batches(budget):
     assert st["final_chunks"] == one[3]["final_chunks"]
 
 
+@pytest.mark.parametrize("W,nmax,budget", [(256, 4, 0), (128, 2, 0), (256, 32, 0), (256, 4, 150_000)])
+def test_chunk_counts_from_structure_match_data_pass(W, nmax, budget):
+    # The level histograms derived from A's structure and B's chunk runs must
+    # be the integers the pass over the expanded columns counts: same chunk
+    # tree (level sizes, final chunks) and the same product.
+    A = synth.rmat(12, 16, seed=13)
+    A.val = np.round(A.val * 6 - 3)
+    opts = dict(heavy_threshold=40, dense_width=W, max_chunks_per_level=nmax, mem_budget=budget)
+    a = gpu_product(A, A, histogram_from_data=1, **opts)
+    b = gpu_product(A, A, **opts)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+    for key in ("level_elems", "final_chunks", "dense_chunks"):
+        assert a[3][key] == b[3][key], key
+    # batch cuts follow the (unordered) heavy-row list, so only their presence
+    assert (a[3]["batches"] > 1) == (b[3]["batches"] > 1) == (budget > 0)
+    ref = oracle.spgemm(A, A)
+    assert_csr_equal_structure(b[0], b[1], ref.row_ptr, ref.col, "C")
+    np.testing.assert_array_equal(b[2], ref.val)
+
+
 def test_batches_fp32_multilevel():
     A = synth.rmat(12, 16, seed=8, dtype=np.float32)
     st = check_full(A, A, mem_budget=300_000, heavy_threshold=48, dense_width=256,
