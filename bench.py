@@ -38,21 +38,20 @@ def log(*a):
 
 def algorithmic_bytes(st, phase, sv, si=4):
     """Algorithmic bytes one step moves in the given phase, and the per-unit
-    figure it is built from.  With several heavy-row batches numeric expands
-    every batch again, so the expansion phases run twice per step."""
+    figure it is built from.  With several heavy-row batches, symbolic
+    expands columns only and numeric expands every batch again with values,
+    so the expansion phases run twice per step."""
     E = sum(st["level_elems"])
-    x = 2 if st["batches"] > 1 else 1
+    batched = st["batches"] > 1
+    cv = (si + (si + sv)) if batched else (si + sv)   # bytes per element over both expansions
     if phase == "outer_product":
-        return x * st["heavy_products"] * (si + sv), f"{si + sv} B written per heavy product"
+        return st["heavy_products"] * cv, f"{cv} B written per heavy product"
     if phase == "multisplit":
-        return x * E * 2 * (si + sv), f"{2 * (si + sv)} B (read + write) per element per level"
+        return E * 2 * cv, f"{2 * cv} B (read + write) per element per level"
     if phase == "histogram":
-        return x * E * si, f"{si} B read per element per level"
+        return E * si * (2 if batched else 1), f"{si} B read per element per level"
     if phase == "num_chunk_dense":
         return st["lds_dense_products"] * (si + sv), f"{si + sv} B read per dense-chunk element"
-    if phase == "sym_chunk_dense":
-        # the bitmap chunk symbolic reads the column of every final-chunk element
-        return st["heavy_products"] * si, f"{si} B read per heavy element"
     return None, None
 
 
@@ -213,8 +212,8 @@ def main():
 
     roof = None
     if not args.no_profile:
-        cands = [k for k in ("multisplit", "outer_product", "num_chunk_dense", "histogram",
-                             "sym_chunk_dense") if phase_tot.get(k, 0) > 0]
+        cands = [k for k in ("multisplit", "outer_product", "num_chunk_dense", "histogram")
+                 if phase_tot.get(k, 0) > 0]
         if cands:
             kern = max(cands, key=lambda k: phase_tot[k])
             windows = st["phase_windows"][kern]

@@ -243,7 +243,6 @@ struct spgemm_plan_s {
   size_t arenaUsed = 0, demand = 0;
   std::vector<BinCfg> symBins, numBins, rankBins;
   int32_t chunkWords = 0;  // bitmap words of the widest final chunk (0: hash fallback)
-  int32_t* dClassCaps = nullptr;  // size classes of the bitmap chunk symbolic
   int NS = 0;  // number of hash bins
   // device arrays
   int32_t *dSymCaps = nullptr;
@@ -260,7 +259,9 @@ struct spgemm_plan_s {
   int64_t h = 0, Ph = 0, nAh = 0, nreq = 1;
   const int32_t* xheavy = nullptr;
   std::vector<int64_t> hChat, hAnnz;                   // scans over heavy rows
-  std::vector<std::pair<int64_t, int64_t>> batches;   // heavy-row ranges
+  std::vector<std::pair<int64_t, int64_t>> batches;   // heavy-row ranges of numeric
+  std::vector<std::pair<int64_t, int64_t>> batchesSym; // and of symbolic
+  bool symVals = true;   // symbolic expands values too (one batch, kept)
   Batch kept{};          // the expansion symbolic leaves for numeric (one batch)
   bool haveKept = false;
   size_t wsCur = 0;      // workspace bytes currently held
@@ -617,11 +618,26 @@ void do_plan(spgemm_plan_t p) {
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// Column and value buffers for `Pb` elements: one pair, or two with levels.
-size_t heavy_buf_bytes(spgemm_plan_t p, int64_t Pb) {
+// Column (and value) buffers for `Pb` elements: one set, or two with levels.
+size_t heavy_buf_bytes(spgemm_plan_t p, int64_t Pb, bool vals) {
   const size_t n = (size_t)std::max<int64_t>(Pb, 1);
-  const size_t pair = align256(n * 4) + align256(n * (p->f64 ? 8 : 4));
+  const size_t pair = align256(n * 4) + (vals ? align256(n * (p->f64 ? 8 : 4)) : 0);
   return (p->params.levels > 0 ? 2 : 1) * pair;
+}
+
+// Consecutive heavy rows whose C-hat rows together hold at most `cap`
+// elements (at least one row each); returns the largest batch's elements.
+int64_t cut_batches(spgemm_plan_t p, int64_t cap, std::vector<std::pair<int64_t, int64_t>>* out) {
+  out->clear();
+  int64_t r0 = 0, maxPb = 0;
+  while (r0 < p->h) {
+    int64_t r1 = r0 + 1;
+    while (r1 < p->h && p->hChat[r1 + 1] - p->hChat[r0] <= cap) ++r1;
+    out->push_back({r0, r1});
+    maxPb = std::max(maxPb, p->hChat[r1] - p->hChat[r0]);
+    r0 = r1;
+  }
+  return maxPb;
 }
 
 // Per heavy row: products (C-hat row length) and nnz of its A row, both
@@ -643,8 +659,7 @@ void heavy_prepare(spgemm_plan_t p) {
   check_launch("heavy prepare");
   HIP_CHECK(hipStreamSynchronize(s));
   // Bytes of intermediate per heavy element: one or two (col, val) buffers.
-  const int64_t vb = p->f64 ? 8 : 4;
-  const int64_t perElem = (p->params.levels > 0 ? 2 : 1) * (4 + vb);
+  const int64_t vb = p->f64 ? 8 : 4, nbuf = p->params.levels > 0 ? 2 : 1;
   int64_t budget = p->opts.mem_budget;
   if (!budget) {
     size_t freeB = 0, totalB = 0;
@@ -653,18 +668,20 @@ void heavy_prepare(spgemm_plan_t p) {
     if (p->arena) avail += (int64_t)(p->arena->cap - p->arenaUsed);
     budget = std::max<int64_t>(avail * 45 / 100, (int64_t)1 << 30);
   }
-  const int64_t cap = std::max<int64_t>(budget / perElem, 1);
-  p->batches.clear();
-  int64_t r0 = 0, maxPb = 0;
-  while (r0 < h) {
-    int64_t r1 = r0 + 1;  // at least one row per batch
-    while (r1 < h && p->hChat[r1 + 1] - p->hChat[r0] <= cap) ++r1;
-    p->batches.push_back({r0, r1});
-    maxPb = std::max(maxPb, p->hChat[r1] - p->hChat[r0]);
-    r0 = r1;
+  // Numeric needs columns and values.  If that takes one batch, symbolic
+  // expands with values and numeric reuses the result; otherwise symbolic
+  // expands columns only, in batches a third (fp64) or half (fp32) the size.
+  const int64_t maxNum = cut_batches(p, std::max<int64_t>(budget / (nbuf * (4 + vb)), 1), &p->batches);
+  int64_t bytes = (int64_t)heavy_buf_bytes(p, maxNum, true);
+  p->symVals = p->batches.size() == 1;
+  if (p->symVals) {
+    p->batchesSym = p->batches;
+  } else {
+    const int64_t maxSym = cut_batches(p, std::max<int64_t>(budget / (nbuf * 4), 1), &p->batchesSym);
+    bytes = std::max<int64_t>(bytes, (int64_t)heavy_buf_bytes(p, maxSym, false));
   }
   p->st.batches = (int64_t)p->batches.size();
-  p->heavyBuf = heavy_region(p, heavy_buf_bytes(p, maxPb));
+  p->heavyBuf = heavy_region(p, (size_t)bytes);
 
   // Chunk counts of every heavy row from the structure, for all levels.
   const int64_t nreq = p->nreq;
@@ -691,7 +708,7 @@ void heavy_prepare(spgemm_plan_t p) {
 
 // Expand heavy rows [hb0, hb1): CSC, outer product, multisplit levels, the
 // final chunk list and its numeric bins.
-void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, Batch* B) {
+void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bool vals, Batch* B) {
   hipStream_t s = p->sh;
   const int64_t hb = hb1 - hb0;
   const int64_t Pb = p->hChat[hb1] - p->hChat[hb0];
@@ -745,8 +762,10 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, Ba
     for (int b = 0; b < (L > 0 ? 2 : 1); ++b) {
       B->bufCol[b] = (int32_t*)q;
       q += align256(n * 4);
-      B->bufVal[b] = q;
-      q += align256(n * vb);
+      if (vals) {
+        B->bufVal[b] = q;
+        q += align256(n * vb);
+      }
     }
   }
   const int phOp = ph_begin(p, SPGEMM_PH_OUTER_PRODUCT, s);
@@ -789,7 +808,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, Ba
     launch_fill_i32(ctr, 0, 2, s);
     int32_t blockElems;
     int maxRows;
-    multisplit_geometry(f64, p->tau, v, &blockElems, &maxRows);
+    multisplit_geometry(f64 && vals, p->tau, v, &blockElems, &maxRows);
     const int phH = ph_begin(p, SPGEMM_PH_HISTOGRAM, s);
     if (p->CH)
       launch_level_counts(Q, v, (int32_t)(w / W), (int32_t)p->nreq, inRow, inSlot,
@@ -878,37 +897,41 @@ ChunkList chunk_list(spgemm_plan_t p, const Batch& B) {
 }
 
 // Chunk symbolic: per-chunk nnz into the batch's slots.
+// Light chunks take the bitmap kernels (no sort: a chunk's columns are
+// ranked by prefix popcounts over its width) when the bitmap is small next
+// to the hash table of the chunk's bin; small chunks of wide levels take the
+// hash kernels, whose cost follows the element count, not the width.
+bool sym_bitmap(spgemm_plan_t p, int b) {
+  return p->chunkWords && p->chunkWords <= 2 * (int64_t)p->symBins[b].cap;
+}
+bool num_bitmap(spgemm_plan_t p, int b) {
+  return p->chunkWords && p->chunkWords <= 4 * (int64_t)p->symBins[b].cap;
+}
+
+// Chunk symbolic: per-chunk nnz into the batch's slots.
 void symbolic_batch(spgemm_plan_t p, const Batch& B) {
   hipStream_t s = p->sh;
-  const int64_t nfc = B.nfc;
   const ChunkList cl = chunk_list(p, B);
-  if (p->chunkWords) {
-    uint8_t* skey = alloc_n<uint8_t>(p, nfc, s);
-    int32_t* order = alloc_n<int32_t>(p, nfc, s);
-    int32_t* sc = alloc_n<int32_t>(p, 64, s);
-    int32_t* sf = alloc_n<int32_t>(p, 64, s);
-    int32_t* ss = alloc_n<int32_t>(p, 65, s);
-    launch_chunk_bins(nfc, B.fcCnt, nfc, INT32_MAX, p->dClassCaps, 3, 3, skey, nullptr, s);
-    launch_bin_sort(skey, nfc, 3, sc, sf, ss, order, s);
-    HIP_CHECK(hipMemcpyAsync(p->hBins + 104, ss, sizeof(int32_t) * 4, hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipStreamSynchronize(s));
-    const std::vector<int32_t> st(p->hBins + 104, p->hBins + 108);
-    const int ph = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
-    for (int c = 0; c < 3; ++c)
-      launch_sym_chunks_bitmap(c, order + st[c], st[c + 1] - st[c], p->chunkWords, cl, s);
-    ph_end(p, ph, s);
-  } else {
-    const int ph = ph_begin(p, SPGEMM_PH_SYM_CHUNK_HASH, s);
-    for (int b = 0; b < p->NS; ++b) {
-      const int64_t a = B.fcBinStart[b], e = B.fcBinStart[b + 1];
-      launch_sym_chunks(p->symBins[b], B.fcOrder + a, e - a, cl, p->errWord, s);
-    }
-    ph_end(p, ph, s);
-    const int64_t a = B.fcBinStart[p->NS], e = B.fcBinStart[p->NS + 1];
-    const int phD = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
-    launch_dense_sym(B.fcOrder + a, e - a, cl, p->errWord, s);
-    ph_end(p, phD, s);
+  const int ph = ph_begin(p, SPGEMM_PH_SYM_CHUNK_HASH, s);
+  for (int b = 0; b < p->NS; ++b) {
+    const int64_t a = B.fcBinStart[b], e = B.fcBinStart[b + 1];
+    if (!sym_bitmap(p, b)) launch_sym_chunks(p->symBins[b], B.fcOrder + a, e - a, cl, p->errWord, s);
   }
+  ph_end(p, ph, s);
+  const int phD = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
+  for (int b = 0; b < p->NS; ++b) {
+    const int64_t a = B.fcBinStart[b], e = B.fcBinStart[b + 1];
+    const int64_t cap = p->symBins[b].cap;
+    if (sym_bitmap(p, b))
+      launch_sym_chunks_bitmap(cap <= 256 ? 0 : cap <= 4096 ? 1 : 2, B.fcOrder + a, e - a,
+                               p->chunkWords, cl, s);
+  }
+  const int64_t a = B.fcBinStart[p->NS], e = B.fcBinStart[p->NS + 1];
+  if (p->chunkWords)
+    launch_sym_chunks_bitmap(2, B.fcOrder + a, e - a, p->chunkWords, cl, s);
+  else
+    launch_dense_sym(B.fcOrder + a, e - a, cl, p->errWord, s);
+  ph_end(p, phD, s);
   check_launch("chunk symbolic");
 }
 
@@ -918,7 +941,7 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval) {
   const int ph = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = B.fcBinStart[b], en = B.fcBinStart[b + 1];
-    if (p->chunkWords)
+    if (num_bitmap(p, b))
       launch_num_chunks_rank(p->rankBins[b], p->f64, B.fcOrder + st, en - st, p->chunkWords, cl,
                              p->cRowOff, ccol, cval, p->errWord, s);
     else
@@ -947,19 +970,14 @@ void heavy_symbolic(spgemm_plan_t p) {
   if (maxWidth <= 65536) {
     p->chunkWords = (int32_t)((maxWidth + 31) / 32);
     make_rank_bins(p->lds, p->f64, p->chunkWords, p->symBins, &p->rankBins);
-    p->dClassCaps = alloc_n<int32_t>(p, 4, s);
-    const int32_t classCaps[3] = {256, 4096, INT32_MAX};
-    std::memcpy(p->hBins + 110, classCaps, sizeof(classCaps));
-    HIP_CHECK(hipMemcpyAsync(p->dClassCaps, p->hBins + 110, sizeof(classCaps), hipMemcpyHostToDevice, s));
-    HIP_CHECK(hipStreamSynchronize(s));
   }
   p->st.final_chunks = 0;
   p->st.dense_chunks = 0;
-  const bool single = p->batches.size() == 1;
-  for (const auto& bt : p->batches) {
+  const bool single = p->symVals;
+  for (const auto& bt : p->batchesSym) {
     const WsMark mk = ws_mark(p);
     Batch B;
-    expand_batch(p, bt.first, bt.second, true, &B);
+    expand_batch(p, bt.first, bt.second, true, p->symVals, &B);
     symbolic_batch(p, B);
     p->st.final_chunks += B.nfc;
     p->st.dense_chunks += B.denseChunks;
@@ -983,7 +1001,7 @@ void heavy_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   for (const auto& bt : p->batches) {
     const WsMark mk = ws_mark(p);
     Batch B;
-    expand_batch(p, bt.first, bt.second, false, &B);
+    expand_batch(p, bt.first, bt.second, false, true, &B);
     numeric_batch(p, B, ccol, cval);
     ws_reset(p, mk, p->sh);
   }

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
 // Multisplit (§III-C): local histogram, one global reservation per
 // (row, chunk) bucket, LDS permute into bucket order, then coalesced writes
 // of whole bucket runs with the column shifted into the chunk's range.
-template <int ITEMS, typename V>
+template <int ITEMS, typename V, bool kVals>
 __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElems,
                                                     const int64_t* __restrict__ rowPtr, int64_t R,
                                                     const int32_t* __restrict__ inCol,
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   int64_t* gbase = (int64_t*)smem;
   int64_t* bnd = gbase + NBcap;
   V* valBuf = (V*)(bnd + maxRows);
-  int32_t* colBuf = (int32_t*)(valBuf + blockElems);
+  int32_t* colBuf = (int32_t*)(valBuf + (kVals ? blockElems : 0));
   int32_t* hist = colBuf + blockElems;
   int32_t* loff = hist + NBcap;
   uint16_t* bktBuf = (uint16_t*)(loff + NBcap);
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     if (act) {
       const int64_t e = e0 + idx;
       cc[it] = inCol[e];
-      xv[it] = inVal[e];
+      if constexpr (kVals) xv[it] = inVal[e];
       bb[it] = (uint32_t)(local_row(bnd, nrows, e) * v + (cc[it] >> shift));
     }
   }
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     if (act) {
       const int pos = base + __popcll(m & lanemask_lt());
       colBuf[pos] = cc[it] & wmask;
-      valBuf[pos] = xv[it];
+      if constexpr (kVals) valBuf[pos] = xv[it];
       bktBuf[pos] = (uint16_t)bb[it];
     }
   }
@@ -249,16 +249,18 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     const int b = bktBuf[idx];
     const int64_t dest = gbase[b] + (idx - loff[b]);
     outCol[dest] = colBuf[idx];
-    outVal[dest] = valBuf[idx];
+    if constexpr (kVals) outVal[dest] = valBuf[idx];
   }
 }
 
 }  // namespace
 
 void multisplit_set_attributes() {
-  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF64, double>,
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF64, double, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float>,
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float, false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
 }
 
@@ -287,14 +289,18 @@ void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* r
   if (E <= 0) return;
   const unsigned g = grid_for(E, blockElems);
   const size_t NB = (size_t)maxRows * v;
-  const size_t lds = NB * 8 + (size_t)maxRows * 8 + (size_t)blockElems * ((f64 ? 8 : 4) + 4 + 2) +
-                     NB * 8 + 16;
-  if (f64)
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF64, double>), dim3(g), dim3(kNT), lds, s, E,
+  const size_t vb = !outVal ? 0 : f64 ? 8 : 4;
+  const size_t lds = NB * 8 + (size_t)maxRows * 8 + (size_t)blockElems * (vb + 4 + 2) + NB * 8 + 16;
+  if (!outVal)  // columns only: the geometry of the fp32 instance
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float, false>), dim3(g), dim3(kNT), lds, s, E,
+                       blockElems, rowPtr, R, inCol, (const float*)nullptr, shift, v, wmask,
+                       maxRows, inv, cursor, outCol, (float*)nullptr, err);
+  else if (f64)
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF64, double, true>), dim3(g), dim3(kNT), lds, s, E,
                        blockElems, rowPtr, R, inCol, (const double*)inVal, shift, v, wmask,
                        maxRows, inv, cursor, outCol, (double*)outVal, err);
   else
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float>), dim3(g), dim3(kNT), lds, s, E,
+    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float, true>), dim3(g), dim3(kNT), lds, s, E,
                        blockElems, rowPtr, R, inCol, (const float*)inVal, shift, v, wmask,
                        maxRows, inv, cursor, outCol, (float*)outVal, err);
 }

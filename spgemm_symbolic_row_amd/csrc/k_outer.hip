@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kNT) void k_seg_base(int64_t nE, const int32_t* __r
 constexpr int kOpBlock = 32768;
 constexpr int kXcds = 8;
 
-template <typename V>
+template <typename V, bool kVals>
 __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t* __restrict__ entryOff,
                                                        int64_t nE, const int32_t* __restrict__ cscCol,
                                                        const V* __restrict__ cscVal,
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
     int64_t dst = 0;
     if (ev) {
       bs = brp[cscCol[e]];
-      a = cscVal[e];
+      if constexpr (kVals) a = cscVal[e];
       dst = segBase[e];
     }
     int64_t bend = entryOff[(j + kWave < nE) ? j + kWave : nE];
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
         }
         const int64_t so = __shfl(off, s);
         const int32_t sb = __shfl(bs, s);
-        av[u] = __shfl(a, s);
+        if constexpr (kVals) av[u] = __shfl(a, s);
         const int64_t sd = __shfl(dst, s);
         const int64_t r = q - so;
         dpos[u] = q < bend ? sd + r : -1;
@@ -153,13 +153,13 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         cv[u] = dpos[u] >= 0 ? bcol[bidx[u]] : 0;
-        bv[u] = dpos[u] >= 0 ? bval[bidx[u]] : V(0);
+        if constexpr (kVals) bv[u] = dpos[u] >= 0 ? bval[bidx[u]] : V(0);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         if (dpos[u] >= 0) {
           outCol[dpos[u]] = cv[u];
-          outVal[dpos[u]] = av[u] * bv[u];
+          if constexpr (kVals) outVal[dpos[u]] = av[u] * bv[u];
         }
       }
     }
@@ -212,13 +212,17 @@ void launch_outer_product(bool f64, int64_t Ph, const int64_t* entryOff, int64_t
   if (Ph <= 0) return;
   // A multiple of the XCD count; tiles past the end exit at once.
   const unsigned g = (grid_for(Ph, kOpBlock) + kXcds - 1) / kXcds * kXcds;
-  if (f64)
-    hipLaunchKernelGGL(k_outer_product<double>, dim3(g), dim3(kNT), 0, s, Ph, entryOff, nE, cscCol,
-                       (const double*)cscVal, segBase, brp, bcol, (const double*)bval, outCol,
-                       (double*)outVal);
+  if (!outVal)  // columns only
+    hipLaunchKernelGGL((k_outer_product<float, false>), dim3(g), dim3(kNT), 0, s, Ph, entryOff, nE,
+                       cscCol, (const float*)nullptr, segBase, brp, bcol, (const float*)nullptr,
+                       outCol, (float*)nullptr);
+  else if (f64)
+    hipLaunchKernelGGL((k_outer_product<double, true>), dim3(g), dim3(kNT), 0, s, Ph, entryOff, nE,
+                       cscCol, (const double*)cscVal, segBase, brp, bcol, (const double*)bval,
+                       outCol, (double*)outVal);
   else
-    hipLaunchKernelGGL(k_outer_product<float>, dim3(g), dim3(kNT), 0, s, Ph, entryOff, nE, cscCol,
-                       (const float*)cscVal, segBase, brp, bcol, (const float*)bval, outCol,
+    hipLaunchKernelGGL((k_outer_product<float, true>), dim3(g), dim3(kNT), 0, s, Ph, entryOff, nE,
+                       cscCol, (const float*)cscVal, segBase, brp, bcol, (const float*)bval, outCol,
                        (float*)outVal);
 }
 

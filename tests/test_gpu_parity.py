@@ -129,6 +129,7 @@ def test_wide_light_rows_all_bins():
     (12, 32, 128, 2),      # five levels of 2
     (12, 200, 1024, 64),   # one level, light and dense chunks
     (11, 64, 2048, 32),    # one W-wide chunk: no multisplit
+    (13, 64, 4096, 2),     # wide chunks: small ones take the hash kernels
 ])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_heavy_path_forced(scale, tau, W, nmax, dtype):
