@@ -41,9 +41,12 @@ def algorithmic_bytes(st, phase, sv, si=4):
     figure it is built from.  With several heavy-row batches, symbolic
     expands columns only and numeric expands every batch again with values,
     so the expansion phases run twice per step."""
-    E = sum(st["level_elems"])
+    fused = st["phase_windows"]["expand_split"] > 0
+    E = sum(st["level_elems"][1:] if fused else st["level_elems"])
     batched = st["batches"] > 1
     cv = (si + (si + sv)) if batched else (si + sv)   # bytes per element over both expansions
+    if phase == "expand_split":
+        return st["level_elems"][0] * cv, f"{cv} B written per heavy product (first-level chunks)"
     if phase == "outer_product":
         return st["heavy_products"] * cv, f"{cv} B written per heavy product"
     if phase == "multisplit":
@@ -212,7 +215,8 @@ def main():
 
     roof = None
     if not args.no_profile:
-        cands = [k for k in ("multisplit", "outer_product", "num_chunk_dense", "histogram")
+        cands = [k for k in ("multisplit", "expand_split", "outer_product", "num_chunk_dense",
+                             "histogram")
                  if phase_tot.get(k, 0) > 0]
         if cands:
             kern = max(cands, key=lambda k: phase_tot[k])

@@ -93,7 +93,15 @@ typedef struct spgemm_options {
   spgemm_alloc_fn alloc;        /* optional allocator (see above)               */
   spgemm_free_fn free;
   void *alloc_ctx;
-  int64_t reserved[8];
+  int32_t outer_product_expansion; /* 1: expand the heavy rows as the gMAGNUS
+                                   page prints it (masked CSC, outer product
+                                   into C-hat, then every multisplit level);
+                                   0: feed the first multisplit level straight
+                                   from A and B, row by row, so C-hat in row
+                                   order is never written (default, when the
+                                   counts come from the structure)            */
+  int32_t reserved32;
+  int64_t reserved[7];
 } spgemm_options;
 
 /* Parameters chosen by GetMagnusParams (gMAGNUS §III-D, Eq. 4-7). */
@@ -124,7 +132,8 @@ typedef enum spgemm_phase {
   SPGEMM_PH_NUM_CHUNK_HASH = 10, /* light-chunk hash numeric + sort             */
   SPGEMM_PH_NUM_CHUNK_DENSE = 11,/* heavy-chunk dense LDS numeric               */
   SPGEMM_PH_CHUNK_HIST = 12,     /* per-row W-wide chunk counts from structure  */
-  SPGEMM_PH_COUNT = 13
+  SPGEMM_PH_EXPAND_SPLIT = 13,   /* first multisplit level fed from A and B     */
+  SPGEMM_PH_COUNT = 14
 } spgemm_phase;
 
 typedef struct spgemm_stats {

@@ -266,6 +266,8 @@ struct spgemm_plan_s {
   bool haveKept = false;
   size_t wsCur = 0;      // workspace bytes currently held
   int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
+  int64_t* dAnnz = nullptr; // scan of the heavy rows' A lengths (h + 1)
+  bool fused = false;    // the first level is fed straight from A and B
   int32_t* slotNnz = nullptr;
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
@@ -618,11 +620,18 @@ void do_plan(spgemm_plan_t p) {
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// Column (and value) buffers for `Pb` elements: one set, or two with levels.
+// Intermediate buffers that hold `Pb` elements at once: one, or two for
+// ping-pong between levels.  The outer product fills one that the first
+// level reads; fed straight from A and B, one level needs only its output.
+int heavy_nbuf(spgemm_plan_t p) {
+  const int L = p->params.levels;
+  if (L == 0) return 1;
+  return (p->fused && L == 1) ? 1 : 2;
+}
 size_t heavy_buf_bytes(spgemm_plan_t p, int64_t Pb, bool vals) {
   const size_t n = (size_t)std::max<int64_t>(Pb, 1);
   const size_t pair = align256(n * 4) + (vals ? align256(n * (p->f64 ? 8 : 4)) : 0);
-  return (p->params.levels > 0 ? 2 : 1) * pair;
+  return heavy_nbuf(p) * pair;
 }
 
 // Consecutive heavy rows whose C-hat rows together hold at most `cap`
@@ -648,18 +657,19 @@ void heavy_prepare(spgemm_plan_t p) {
   int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, s);
   int64_t* hv = alloc_n<int64_t>(p, h, s);
   int64_t* pref = alloc_n<int64_t>(p, h + 1, s);
+  p->dAnnz = alloc_n<int64_t>(p, h + 1, s);
   p->hChat.assign(h + 1, 0);
   p->hAnnz.assign(h + 1, 0);
   launch_gather_i64(p->rowP, p->xheavy, h, hv, s);
   launch_scan_i64(hv, h, pref, tmp, s);
   HIP_CHECK(hipMemcpyAsync(p->hChat.data(), pref, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
   launch_row_lengths(h, p->xheavy, p->arp, hv, s);
-  launch_scan_i64(hv, h, pref, tmp, s);
-  HIP_CHECK(hipMemcpyAsync(p->hAnnz.data(), pref, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
+  launch_scan_i64(hv, h, p->dAnnz, tmp, s);
+  HIP_CHECK(hipMemcpyAsync(p->hAnnz.data(), p->dAnnz, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
   check_launch("heavy prepare");
   HIP_CHECK(hipStreamSynchronize(s));
   // Bytes of intermediate per heavy element: one or two (col, val) buffers.
-  const int64_t vb = p->f64 ? 8 : 4, nbuf = p->params.levels > 0 ? 2 : 1;
+  const int64_t vb = p->f64 ? 8 : 4;
   int64_t budget = p->opts.mem_budget;
   if (!budget) {
     size_t freeB = 0, totalB = 0;
@@ -668,6 +678,12 @@ void heavy_prepare(spgemm_plan_t p) {
     if (p->arena) avail += (int64_t)(p->arena->cap - p->arenaUsed);
     budget = std::max<int64_t>(avail * 45 / 100, (int64_t)1 << 30);
   }
+  // Chunk counts come from the structure unless asked otherwise or too wide
+  // for LDS; with them the first level can be fed straight from A and B.
+  const bool structCounts =
+      p->params.levels > 0 && !p->opts.histogram_from_data && p->nreq <= 8192;
+  p->fused = structCounts && !p->opts.outer_product_expansion;
+  const int64_t nbuf = heavy_nbuf(p);
   // Numeric needs columns and values.  If that takes one batch, symbolic
   // expands with values and numeric reuses the result; otherwise symbolic
   // expands columns only, in batches a third (fp64) or half (fp32) the size.
@@ -685,7 +701,7 @@ void heavy_prepare(spgemm_plan_t p) {
 
   // Chunk counts of every heavy row from the structure, for all levels.
   const int64_t nreq = p->nreq;
-  if (p->params.levels > 0 && !p->opts.histogram_from_data && nreq <= 8192) {
+  if (structCounts) {
     const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, s);
     p->CH = alloc_n<int32_t>(p, h * nreq, s);
     const WsMark mk = ws_mark(p);
@@ -730,6 +746,33 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
   launch_gather_i64(p->rowP, xb, hb, hP, s);
   launch_scan_i64(hP, hb, chatRowPtr, tmp, s);
 
+  const int L = p->params.levels;
+  {
+    char* q = p->heavyBuf;
+    const size_t n = (size_t)std::max<int64_t>(Pb, 1);
+    for (int b = 0; b < heavy_nbuf(p); ++b) {
+      B->bufCol[b] = (int32_t*)q;
+      q += align256(n * 4);
+      if (vals) {
+        B->bufVal[b] = q;
+        q += align256(n * vb);
+      }
+    }
+  }
+  ExpandSrc src{};
+  if (p->fused) {
+    // The heavy rows' A entries in row order with their product offsets:
+    // the first multisplit level makes its elements from these.
+    int32_t* eB = alloc_n<int32_t>(p, nE, s);
+    int64_t* nbE = alloc_n<int64_t>(p, nE, s);
+    int64_t* eOff = alloc_n<int64_t>(p, nE + 1, s);
+    void* eVal = vals ? plan_alloc(p, std::max<int64_t>(nE, 1) * vb, s) : nullptr;
+    launch_expand_entries(f64, hb, xb, p->dAnnz + hb0, p->arp, p->acol, p->aval, p->brp, eB, nbE,
+                          eVal, s);
+    launch_scan_i64(nbE, nE, eOff, tmp, s);
+    src = ExpandSrc{eOff, eB, eVal, p->bcol, vals ? p->bval : nullptr, nE};
+    ph_end(p, phCsc, s);
+  } else {
   // Masked CSR -> CSC of A restricted to the batch's heavy rows.
   int32_t* colCnt = alloc_n<int32_t>(p, p->k, s);
   int64_t* colPtr = alloc_n<int64_t>(p, p->k + 1, s);
@@ -755,24 +798,12 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
   ph_end(p, phCsc, s);
 
   // Outer product into buffer 0.
-  const int L = p->params.levels;
-  {
-    char* q = p->heavyBuf;
-    const size_t n = (size_t)std::max<int64_t>(Pb, 1);
-    for (int b = 0; b < (L > 0 ? 2 : 1); ++b) {
-      B->bufCol[b] = (int32_t*)q;
-      q += align256(n * 4);
-      if (vals) {
-        B->bufVal[b] = q;
-        q += align256(n * vb);
-      }
-    }
-  }
   const int phOp = ph_begin(p, SPGEMM_PH_OUTER_PRODUCT, s);
   launch_outer_product(f64, Pb, entryOff, nE, cscCol, cscVal, segBase, p->brp, p->bcol, p->bval,
                        B->bufCol[0], B->bufVal[0], s);
   ph_end(p, phOp, s);
   check_launch("outer product");
+  }
 
   struct Piece {
     int64_t first, n;
@@ -785,7 +816,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
   int64_t R = hb, E = Pb;
   const int64_t* rowPtr = chatRowPtr;
   const int32_t *inRow = nullptr, *inSlot = nullptr;
-  int cur = 0;
+  int cur = p->fused ? 1 : 0;  // buffer the level reads (none when fed from A and B)
   for (int l = 0; l < L; ++l) {
     B->levelElems[l] = E;
     const int v = p->params.v_chunks[l];
@@ -822,8 +853,10 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     launch_scan_i32(newCnt, Q, newOff, ltmp, s);
     launch_copy_i64(cur64, newOff, Q, s);
     const int out = 1 - cur;
-    const int phM = ph_begin(p, SPGEMM_PH_MULTISPLIT, s);
-    launch_multisplit(f64, E, blockElems, rowPtr, R, B->bufCol[cur], B->bufVal[cur], shift, v,
+    const bool direct = p->fused && l == 0;
+    const int phM = ph_begin(p, direct ? SPGEMM_PH_EXPAND_SPLIT : SPGEMM_PH_MULTISPLIT, s);
+    launch_multisplit(f64, E, blockElems, rowPtr, R, direct ? nullptr : B->bufCol[cur],
+                      direct ? nullptr : B->bufVal[cur], direct ? &src : nullptr, shift, v,
                       (int32_t)(w - 1), maxRows, inv, cur64, B->bufCol[out], B->bufVal[out],
                       p->errWord, s);
     ph_end(p, phM, s);

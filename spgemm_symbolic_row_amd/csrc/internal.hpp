@@ -160,10 +160,31 @@ void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, 
                       const int32_t* inRow, const int32_t* inSlot, int32_t slotStep,
                       int32_t* inv, int32_t* newCnt, int32_t* newRow, int32_t* newSlot,
                       int32_t* ctr, hipStream_t s);
+// Source of a multisplit fed straight from the expansion: the heavy rows'
+// A entries in row order, with the first product of each (eOff, nE + 1
+// entries), its B row start and its A value.
+struct ExpandSrc {
+  const int64_t* eOff;
+  const int32_t* eB;
+  const void* eVal;
+  const int32_t* bcol;
+  const void* bval;
+  int64_t nE;
+};
+// One multisplit level.  inCol/inVal: the level's input, or src (not null)
+// to make the elements from A and B.  outVal null: columns only.
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
-                       int64_t R, const int32_t* inCol, const void* inVal, int shift, int v,
-                       int32_t wmask, int maxRows, const int32_t* inv, int64_t* cursor,
-                       int32_t* outCol, void* outVal, int32_t* err, hipStream_t s);
+                       int64_t R, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
+                       int shift, int v, int32_t wmask, int maxRows, const int32_t* inv,
+                       int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
+                       hipStream_t s);
+// Heavy-row entries of rows[0..hb) in row order: entry t of local row q sits
+// at rowEntry[q] - rowEntry[0] + (j - arp[rows[q]]); eB = B row start, nb =
+// products, eVal = A value.
+void launch_expand_entries(bool f64, int64_t hb, const int32_t* rows, const int64_t* rowEntry,
+                           const int32_t* arp, const int32_t* acol, const void* aval,
+                           const int32_t* brp, int32_t* eB, int64_t* nb, void* eVal,
+                           hipStream_t s);
 // Final-chunk descriptors: from a level's light positions [first, first+n)
 // or, when there is no multisplit, from the heavy rows themselves.
 void launch_final_from_level(int64_t first, int64_t n, const int64_t* newOff,

@@ -117,11 +117,18 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
 // Multisplit (§III-C): local histogram, one global reservation per
 // (row, chunk) bucket, LDS permute into bucket order, then coalesced writes
 // of whole bucket runs with the column shifted into the chunk's range.
-template <int ITEMS, typename V, bool kVals>
+//
+// With kExpand the input elements are not read from a C-hat array but made
+// on the fly from A and B: element e of the heavy rows' row-major product
+// sequence belongs to the heavy-row entry t with src.eOff[t] <= e <
+// src.eOff[t+1], and is (B.col[p], a_t * B.val[p]) with p = src.eB[t] + e -
+// src.eOff[t].  This is the first level fed straight from the expansion.
+template <int ITEMS, typename V, bool kVals, bool kExpand>
 __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElems,
                                                     const int64_t* __restrict__ rowPtr, int64_t R,
                                                     const int32_t* __restrict__ inCol,
-                                                    const V* __restrict__ inVal, int shift, int v,
+                                                    const V* __restrict__ inVal, ExpandSrc src,
+                                                    int shift, int v,
                                                     int32_t wmask, int maxRows,
                                                     const int32_t* __restrict__ inv,
                                                     int64_t* __restrict__ cursor,
@@ -141,11 +148,23 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   int32_t* loff = hist + NBcap;
   uint16_t* bktBuf = (uint16_t*)(loff + NBcap);
   __shared__ int32_t wtot[kNT / kWave];
-  __shared__ int64_t s_r0;
+  __shared__ int64_t s_r0, s_t0, s_t1;
   __shared__ int32_t s_nrows;
   const int64_t e0 = (int64_t)blockIdx.x * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
+  if constexpr (kExpand) {
+    // Entries that hold the block's first and last element (range_rows
+    // below synchronises before they are read).
+    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) {
+      const int64_t t0 = wave_last_le(src.eOff, (int64_t)0, src.nE, e0);
+      const int64_t t1 = wave_last_le(src.eOff, t0, src.nE, e1 - 1);
+      if (lane_id() == 0) {
+        s_t0 = t0;
+        s_t1 = t1;
+      }
+    }
+  }
   const int nrows = range_rows(rowPtr, R, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
@@ -168,8 +187,22 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     bb[it] = 0;
     if (act) {
       const int64_t e = e0 + idx;
-      cc[it] = inCol[e];
-      if constexpr (kVals) xv[it] = inVal[e];
+      if constexpr (kExpand) {
+        int64_t lo = s_t0, hi = s_t1;
+        while (lo < hi) {
+          const int64_t mid = (lo + hi + 1) >> 1;
+          if (src.eOff[mid] <= e)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        const int64_t bp = (int64_t)src.eB[lo] + (e - src.eOff[lo]);
+        cc[it] = src.bcol[bp];
+        if constexpr (kVals) xv[it] = ((const V*)src.eVal)[lo] * ((const V*)src.bval)[bp];
+      } else {
+        cc[it] = inCol[e];
+        if constexpr (kVals) xv[it] = inVal[e];
+      }
       bb[it] = (uint32_t)(local_row(bnd, nrows, e) * v + (cc[it] >> shift));
     }
   }
@@ -256,12 +289,16 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
 }  // namespace
 
 void multisplit_set_attributes() {
-  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF64, double, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-  (void)hipFuncSetAttribute((const void*)k_multisplit<kMsItemsF32, float, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+#define SG_ATTR(...)                                                                      \
+  (void)hipFuncSetAttribute((const void*)__VA_ARGS__, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                            163840)
+  SG_ATTR(k_multisplit<kMsItemsF64, double, true, false>);
+  SG_ATTR(k_multisplit<kMsItemsF32, float, true, false>);
+  SG_ATTR(k_multisplit<kMsItemsF32, float, false, false>);
+  SG_ATTR(k_multisplit<kMsItemsF64, double, true, true>);
+  SG_ATTR(k_multisplit<kMsItemsF32, float, true, true>);
+  SG_ATTR(k_multisplit<kMsItemsF32, float, false, true>);
+#undef SG_ATTR
 }
 
 void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int* maxRows) {
@@ -283,26 +320,32 @@ void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int6
 }
 
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
-                       int64_t R, const int32_t* inCol, const void* inVal, int shift, int v,
-                       int32_t wmask, int maxRows, const int32_t* inv, int64_t* cursor,
-                       int32_t* outCol, void* outVal, int32_t* err, hipStream_t s) {
+                       int64_t R, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
+                       int shift, int v, int32_t wmask, int maxRows, const int32_t* inv,
+                       int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
+                       hipStream_t s) {
   if (E <= 0) return;
   const unsigned g = grid_for(E, blockElems);
   const size_t NB = (size_t)maxRows * v;
   const size_t vb = !outVal ? 0 : f64 ? 8 : 4;
   const size_t lds = NB * 8 + (size_t)maxRows * 8 + (size_t)blockElems * (vb + 4 + 2) + NB * 8 + 16;
-  if (!outVal)  // columns only: the geometry of the fp32 instance
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float, false>), dim3(g), dim3(kNT), lds, s, E,
-                       blockElems, rowPtr, R, inCol, (const float*)nullptr, shift, v, wmask,
-                       maxRows, inv, cursor, outCol, (float*)nullptr, err);
-  else if (f64)
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF64, double, true>), dim3(g), dim3(kNT), lds, s, E,
-                       blockElems, rowPtr, R, inCol, (const double*)inVal, shift, v, wmask,
-                       maxRows, inv, cursor, outCol, (double*)outVal, err);
-  else
-    hipLaunchKernelGGL((k_multisplit<kMsItemsF32, float, true>), dim3(g), dim3(kNT), lds, s, E,
-                       blockElems, rowPtr, R, inCol, (const float*)inVal, shift, v, wmask,
-                       maxRows, inv, cursor, outCol, (float*)outVal, err);
+  const ExpandSrc none{};
+  const ExpandSrc& x = src ? *src : none;
+#define SG_MS(ITEMS, V, VALS, EXP)                                                              \
+  hipLaunchKernelGGL((k_multisplit<ITEMS, V, VALS, EXP>), dim3(g), dim3(kNT), lds, s, E,        \
+                     blockElems, rowPtr, R, inCol, (const V*)inVal, x, shift, v, wmask, maxRows, \
+                     inv, cursor, outCol, (V*)outVal, err)
+  // Columns only: the geometry of the fp32 instance.
+  if (src) {
+    if (!outVal) SG_MS(kMsItemsF32, float, false, true);
+    else if (f64) SG_MS(kMsItemsF64, double, true, true);
+    else SG_MS(kMsItemsF32, float, true, true);
+  } else {
+    if (!outVal) SG_MS(kMsItemsF32, float, false, false);
+    else if (f64) SG_MS(kMsItemsF64, double, true, false);
+    else SG_MS(kMsItemsF32, float, true, false);
+  }
+#undef SG_MS
 }
 
 }  // namespace sg

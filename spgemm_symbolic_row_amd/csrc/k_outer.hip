@@ -168,7 +168,48 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
   }
 }
 
+// Heavy-row entries in row order (one wave per heavy row): B row start,
+// product count and A value of each.
+template <typename V>
+__global__ __launch_bounds__(kNT) void k_expand_entries(int64_t hb, const int32_t* __restrict__ rows,
+                                                        const int64_t* __restrict__ rowEntry,
+                                                        const int32_t* __restrict__ arp,
+                                                        const int32_t* __restrict__ acol,
+                                                        const V* __restrict__ aval,
+                                                        const int32_t* __restrict__ brp,
+                                                        int32_t* __restrict__ eB,
+                                                        int64_t* __restrict__ nb,
+                                                        V* __restrict__ eVal) {
+  const int64_t q = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
+  if (q >= hb) return;
+  const int32_t row = rows[q];
+  const int64_t base = rowEntry[q] - rowEntry[0];
+  const int32_t j0 = arp[row], j1 = arp[row + 1];
+  for (int32_t j = j0 + lane_id(); j < j1; j += kWave) {
+    const int32_t k = acol[j];
+    const int64_t t = base + (j - j0);
+    const int32_t b0 = brp[k];
+    eB[t] = b0;
+    nb[t] = brp[k + 1] - b0;
+    if (eVal) eVal[t] = aval[j];
+  }
+}
+
 }  // namespace
+
+void launch_expand_entries(bool f64, int64_t hb, const int32_t* rows, const int64_t* rowEntry,
+                           const int32_t* arp, const int32_t* acol, const void* aval,
+                           const int32_t* brp, int32_t* eB, int64_t* nb, void* eVal,
+                           hipStream_t s) {
+  if (hb <= 0) return;
+  const unsigned g = grid_for(hb * kWave, kNT);
+  if (f64)
+    hipLaunchKernelGGL(k_expand_entries<double>, dim3(g), dim3(kNT), 0, s, hb, rows, rowEntry, arp,
+                       acol, (const double*)aval, brp, eB, nb, (double*)eVal);
+  else
+    hipLaunchKernelGGL(k_expand_entries<float>, dim3(g), dim3(kNT), 0, s, hb, rows, rowEntry, arp,
+                       acol, (const float*)aval, brp, eB, nb, (float*)eVal);
+}
 
 void launch_csc_count(int64_t h, const int32_t* xheavy, const int32_t* arp, const int32_t* acol,
                       int32_t* colCnt, hipStream_t s) {

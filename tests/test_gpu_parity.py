@@ -216,6 +216,28 @@ def test_chunk_counts_from_structure_match_data_pass(W, nmax, budget):
     np.testing.assert_array_equal(b[2], ref.val)
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("W,nmax,budget", [(256, 4, 0), (256, 32, 0), (128, 2, 0), (256, 4, 150_000)])
+def test_direct_first_level_matches_outer_product(W, nmax, budget, dtype):
+    # Feeding the first multisplit level straight from A and B (default) and
+    # expanding through the outer product into C-hat first must give the
+    # same chunk tree and the same C.
+    A = synth.rmat(12, 16, seed=17)
+    A.val = np.round(A.val * 6 - 3).astype(dtype)
+    opts = dict(heavy_threshold=40, dense_width=W, max_chunks_per_level=nmax, mem_budget=budget)
+    a = gpu_product(A, A, outer_product_expansion=1, profile=1, **opts)
+    b = gpu_product(A, A, profile=1, **opts)
+    assert a[3]["phase_windows"]["expand_split"] == 0 and a[3]["phase_windows"]["outer_product"] > 0
+    assert b[3]["phase_windows"]["expand_split"] > 0 and b[3]["phase_windows"]["outer_product"] == 0
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+    for key in ("level_elems", "final_chunks", "dense_chunks"):
+        assert a[3][key] == b[3][key], key
+    ref = oracle.spgemm(A, A)
+    assert_csr_equal_structure(b[0], b[1], ref.row_ptr, ref.col, "C")
+    np.testing.assert_array_equal(b[2], ref.val.astype(dtype))
+
+
 def test_batches_fp32_multilevel():
     A = synth.rmat(12, 16, seed=8, dtype=np.float32)
     st = check_full(A, A, mem_budget=300_000, heavy_threshold=48, dense_width=256,
