@@ -140,9 +140,13 @@ void launch_outer_product(bool f64, int64_t Ph, const int64_t* entryOff, int64_t
 // Elements per multisplit work group and the most input rows such a range
 // can meet, for rows of more than tau elements and v chunks per row.
 void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int* maxRows);
+// out[b] = the item t with off[t] <= b * G < off[t+1], for b < nBlocks: the
+// first row (or entry) of each multisplit work group.
+void launch_block_starts(int64_t nItems, const int64_t* off, int64_t G, int64_t nBlocks,
+                         int32_t* out, hipStream_t s);
 void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
-                      const int32_t* col, int shift, int v, int maxRows, int32_t* counts,
-                      int32_t* err, hipStream_t s);
+                      const int32_t* blkRow, const int32_t* col, int shift, int v, int maxRows,
+                      int32_t* counts, int32_t* err, hipStream_t s);
 // Runs of equal W-wide chunk in B's rows (chunk = col >> shift): runPtr[K+1],
 // runChunk/runStart[runs + 1]; flags[nnzB] and runIdx[nnzB + 1] are scratch.
 void launch_b_runs(int64_t K, int64_t nnzB, const int32_t* brp, const int32_t* bcol, int shift,
@@ -164,6 +168,7 @@ void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, 
 // A entries in row order, with the first product of each (eOff, nE + 1
 // entries), its B row start and its A value.
 struct ExpandSrc {
+  const int32_t* blkEnt;  // entry of each work group's first element
   const int64_t* eOff;
   const int32_t* eB;
   const void* eVal;
@@ -174,7 +179,7 @@ struct ExpandSrc {
 // One multisplit level.  inCol/inVal: the level's input, or src (not null)
 // to make the elements from A and B.  outVal null: columns only.
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
-                       int64_t R, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
+                       int64_t R, const int32_t* blkRow, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
                        int shift, int v, int32_t wmask, int maxRows, const int32_t* inv,
                        int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
                        hipStream_t s);

@@ -29,25 +29,43 @@ __device__ __forceinline__ int bits_for(int n) {
   return b;
 }
 
-// Rows of the range [e0, e1): first row r0 and the row boundaries inside the
-// range (rowPtr[r0+1 .. r0+nrows-1]) into bnd.  Returns nrows, or -1 when
-// more than maxRows rows meet the range.
-__device__ __forceinline__ int range_rows(const int64_t* __restrict__ rowPtr, int64_t R, int64_t e0,
+// Rows of the range [e0, e1) of block b: its first row r0 = blkRow[b] and
+// the row boundaries inside the range (rowPtr[r0+1 .. r0+nrows-1]) into bnd.
+// Rows are never empty (each holds more than tau elements), so the row of
+// the last element is the next block's first row, or the one before it when
+// that row starts exactly at e1.  Returns nrows, or -1 when more than
+// maxRows rows meet the range.
+__device__ __forceinline__ int range_rows(const int64_t* __restrict__ rowPtr, int64_t R,
+                                          const int32_t* __restrict__ blkRow, int64_t e0,
                                           int64_t e1, int maxRows, int64_t* bnd, int64_t* s_r0,
                                           int32_t* s_nrows) {
-  if (threadIdx.x < kWave) {
-    const int64_t r0 = wave_last_le(rowPtr, (int64_t)0, R, e0);
-    const int64_t r1 = wave_last_le(rowPtr, (int64_t)0, R, e1 - 1);
-    if (lane_id() == 0) {
-      *s_r0 = r0;
-      *s_nrows = (int32_t)(r1 - r0 + 1);
-    }
+  if (threadIdx.x == 0) {
+    const int64_t r0 = blkRow[blockIdx.x];
+    int64_t r1 = (blockIdx.x + 1 < gridDim.x) ? blkRow[blockIdx.x + 1] : R - 1;
+    if (r1 > r0 && rowPtr[r1] >= e1) r1 -= 1;
+    *s_r0 = r0;
+    *s_nrows = (int32_t)(r1 - r0 + 1);
   }
   __syncthreads();
   const int nrows = *s_nrows;
   if (nrows > maxRows) return -1;
   for (int i = threadIdx.x; i < nrows - 1; i += kNT) bnd[i] = rowPtr[*s_r0 + 1 + i];
   return nrows;
+}
+
+// out[b] = the item whose range [off[t], off[t+1]) holds element b * G, for
+// every block b < nBlocks (items without elements hold no block start).
+__global__ __launch_bounds__(kNT) void k_block_starts(int64_t nItems, const int64_t* __restrict__ off,
+                                                      int64_t G, int64_t nBlocks,
+                                                      int32_t* __restrict__ out) {
+  for (int64_t t = (int64_t)blockIdx.x * kNT + threadIdx.x; t < nItems;
+       t += (int64_t)gridDim.x * kNT) {
+    const int64_t lo = off[t], hi = off[t + 1];
+    if (hi <= lo) continue;
+    int64_t b = (lo + G - 1) / G;
+    const int64_t bl = (hi - 1) / G;
+    for (; b <= bl && b < nBlocks; ++b) out[b] = (int32_t)t;
+  }
 }
 
 __device__ __forceinline__ int local_row(const int64_t* bnd, int nrows, int64_t e) {
@@ -65,6 +83,7 @@ __device__ __forceinline__ int local_row(const int64_t* bnd, int nrows, int64_t 
 // Histogram: per (input row, chunk) element counts into counts[r*v + c].
 __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems,
                                                    const int64_t* __restrict__ rowPtr, int64_t R,
+                                                   const int32_t* __restrict__ blkRow,
                                                    const int32_t* __restrict__ col, int shift, int v,
                                                    int maxRows, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ err) {
@@ -75,7 +94,7 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
   const int64_t e0 = (int64_t)blockIdx.x * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
-  const int nrows = range_rows(rowPtr, R, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
+  const int nrows = range_rows(rowPtr, R, blkRow, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
@@ -126,6 +145,7 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
 template <int ITEMS, typename V, bool kVals, bool kExpand>
 __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElems,
                                                     const int64_t* __restrict__ rowPtr, int64_t R,
+                                                    const int32_t* __restrict__ blkRow,
                                                     const int32_t* __restrict__ inCol,
                                                     const V* __restrict__ inVal, ExpandSrc src,
                                                     int shift, int v,
@@ -154,18 +174,14 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
   if constexpr (kExpand) {
-    // Entries that hold the block's first and last element (range_rows
-    // below synchronises before they are read).
-    if (threadIdx.x >= kWave && threadIdx.x < 2 * kWave) {
-      const int64_t t0 = wave_last_le(src.eOff, (int64_t)0, src.nE, e0);
-      const int64_t t1 = wave_last_le(src.eOff, t0, src.nE, e1 - 1);
-      if (lane_id() == 0) {
-        s_t0 = t0;
-        s_t1 = t1;
-      }
+    // The entry of the block's first element, and a bound on the entry of
+    // its last (range_rows below synchronises before they are read).
+    if (threadIdx.x == kWave) {
+      s_t0 = src.blkEnt[blockIdx.x];
+      s_t1 = (blockIdx.x + 1 < gridDim.x) ? src.blkEnt[blockIdx.x + 1] : src.nE - 1;
     }
   }
-  const int nrows = range_rows(rowPtr, R, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
+  const int nrows = range_rows(rowPtr, R, blkRow, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
@@ -173,6 +189,42 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   const int NB = nrows * v;
   const int nbits = bits_for(NB);
   for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
+  if constexpr (kExpand) {
+    // Entry of every element of the range, as in a merge of the elements
+    // with the entries' first products: each entry that starts inside the
+    // range marks its start (the largest index wins, which skips entries
+    // without products), then a prefix maximum carries it forward.  colBuf
+    // holds these until the permute.
+    int32_t* ent = colBuf;
+    const int32_t t0 = (int32_t)s_t0, t1 = (int32_t)s_t1;
+    for (int i = threadIdx.x; i < n; i += kNT) ent[i] = (i == 0) ? t0 : -1;
+    __syncthreads();
+    for (int32_t t = t0 + 1 + (int32_t)threadIdx.x; t <= t1; t += kNT) {
+      const int64_t pos = src.eOff[t] - e0;
+      if (pos < n) atomicMax(&ent[(int)pos], t);
+    }
+    __syncthreads();
+    const int cpt = (n + kNT - 1) / kNT;
+    const int i0 = threadIdx.x * cpt, i1 = (i0 + cpt < n) ? i0 + cpt : n;
+    int32_t run = -1;
+    for (int i = i0; i < i1; ++i) {
+      run = ent[i] > run ? ent[i] : run;
+      ent[i] = run;
+    }
+    int32_t x = run;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t y = __shfl_up(x, d);
+      if (lane_id() >= d && y > x) x = y;
+    }
+    int32_t carry = __shfl_up(x, 1);
+    if (lane_id() == 0) carry = -1;
+    if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = x;
+    __syncthreads();
+    for (int w = 0; w < (int)threadIdx.x / kWave; ++w) carry = wtot[w] > carry ? wtot[w] : carry;
+    for (int i = i0; i < i1; ++i)
+      if (ent[i] < carry) ent[i] = carry;
+  }
   __syncthreads();
 
   int32_t cc[ITEMS];
@@ -188,17 +240,10 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     if (act) {
       const int64_t e = e0 + idx;
       if constexpr (kExpand) {
-        int64_t lo = s_t0, hi = s_t1;
-        while (lo < hi) {
-          const int64_t mid = (lo + hi + 1) >> 1;
-          if (src.eOff[mid] <= e)
-            lo = mid;
-          else
-            hi = mid - 1;
-        }
-        const int64_t bp = (int64_t)src.eB[lo] + (e - src.eOff[lo]);
+        const int32_t t = colBuf[idx];
+        const int64_t bp = (int64_t)src.eB[t] + (e - src.eOff[t]);
         cc[it] = src.bcol[bp];
-        if constexpr (kVals) xv[it] = ((const V*)src.eVal)[lo] * ((const V*)src.bval)[bp];
+        if constexpr (kVals) xv[it] = ((const V*)src.eVal)[t] * ((const V*)src.bval)[bp];
       } else {
         cc[it] = inCol[e];
         if constexpr (kVals) xv[it] = inVal[e];
@@ -311,16 +356,24 @@ void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int*
   *maxRows = (int)rows_for(G);
 }
 
+void launch_block_starts(int64_t nItems, const int64_t* off, int64_t G, int64_t nBlocks,
+                         int32_t* out, hipStream_t s) {
+  if (nItems <= 0 || nBlocks <= 0) return;
+  unsigned g = grid_for(nItems, kNT);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_block_starts, dim3(g), dim3(kNT), 0, s, nItems, off, G, nBlocks, out);
+}
+
 void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
-                      const int32_t* col, int shift, int v, int maxRows, int32_t* counts,
-                      int32_t* err, hipStream_t s) {
+                      const int32_t* blkRow, const int32_t* col, int shift, int v, int maxRows,
+                      int32_t* counts, int32_t* err, hipStream_t s) {
   if (E <= 0) return;
   hipLaunchKernelGGL(k_histogram, dim3(grid_for(E, blockElems)), dim3(kNT), 0, s, E, blockElems,
-                     rowPtr, R, col, shift, v, maxRows, counts, err);
+                     rowPtr, R, blkRow, col, shift, v, maxRows, counts, err);
 }
 
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
-                       int64_t R, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
+                       int64_t R, const int32_t* blkRow, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
                        int shift, int v, int32_t wmask, int maxRows, const int32_t* inv,
                        int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
                        hipStream_t s) {
@@ -333,7 +386,8 @@ void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* r
   const ExpandSrc& x = src ? *src : none;
 #define SG_MS(ITEMS, V, VALS, EXP)                                                              \
   hipLaunchKernelGGL((k_multisplit<ITEMS, V, VALS, EXP>), dim3(g), dim3(kNT), lds, s, E,        \
-                     blockElems, rowPtr, R, inCol, (const V*)inVal, x, shift, v, wmask, maxRows, \
+                     blockElems, rowPtr, R, blkRow, inCol, (const V*)inVal, x, shift, v, wmask, \
+                     maxRows,                                                                    \
                      inv, cursor, outCol, (V*)outVal, err)
   // Columns only: the geometry of the fp32 instance.
   if (src) {
