@@ -140,10 +140,8 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const int32_t* __restrict__ i
   (void)err;
 }
 
-// Numeric: val[W] + W-bit bitmap in LDS; LDS atomic adds; then every thread
-// owns W/1024 consecutive columns, a work-group scan of their popcounts
-// gives each thread its output position, and set bits are written in column
-// order: the chunk comes out sorted and compacted.
+// Numeric: val[W] + W-bit bitmap in LDS, filled by LDS atomics; the set
+// bits, taken in column order, give the chunk sorted and compacted.
 constexpr int kDenseNT = 1024;
 template <typename V>
 __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restrict__ items, ChunkList cl,
@@ -186,29 +184,44 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
     }
   }
   __syncthreads();
-  const int cpt = W >= kDenseNT ? W / kDenseNT : 1;  // columns per thread, <= 32
-  const int c0 = threadIdx.x * cpt;
-  uint32_t bits = 0;
-  if (c0 < W) {
-    const uint32_t word = bm[c0 >> 5];
-    bits = (cpt >= 32) ? word : ((word >> (c0 & 31)) & ((1u << cpt) - 1u));
+  // Output in column order with coalesced stores: each wave owns a
+  // contiguous range of 64-column groups; a group's set columns are ranked
+  // by a ballot, so consecutive lanes write consecutive entries.
+  constexpr int kWaves = kDenseNT / kWave;
+  const int ngroups = (W + kWave - 1) / kWave;
+  const int gpw = (ngroups + kWaves - 1) / kWaves;  // groups per wave
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int g0 = w * gpw, g1 = (g0 + gpw < ngroups) ? g0 + gpw : ngroups;
+  int32_t mine = 0;
+  for (int g = g0 + lane; g < g1; g += kWave) {
+    const int c = g * kWave;
+    mine += __popc(bm[c >> 5]) + (c + 32 < W ? __popc(bm[(c >> 5) + 1]) : 0);
   }
-  int32_t total;
-  int32_t pos = block_excl_scan<kDenseNT>((int32_t)__popc(bits), wtot, &total);
+  mine = wave_sum(mine);
+  if (lane == 0) wtot[w] = mine;
+  __syncthreads();
+  int32_t pos = 0, total = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    const int32_t t = wtot[i];
+    if (i < w) pos += t;
+    total += t;
+  }
   const int64_t hr = cl.row[item];
   const int64_t sidx = hr * cl.nreq + cl.slot[item];
   const int64_t base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
   const int32_t want = cl.slotNnz[sidx];
   if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
   const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
-  while (bits) {
-    const int b = __ffs(bits) - 1;
-    bits &= bits - 1;
-    if (pos < want) {
-      ccol[base + pos] = colBase + c0 + b;
-      cval[base + pos] = vals[c0 + b];
+  for (int g = g0; g < g1; ++g) {
+    const int c = g * kWave + lane;
+    const bool set = c < W && ((bm[c >> 5] >> (c & 31)) & 1u);
+    const uint64_t m = __ballot(set);
+    const int32_t p = pos + __popcll(m & lanemask_lt());
+    if (set && p < want) {
+      ccol[base + p] = colBase + c;
+      cval[base + p] = vals[c];
     }
-    ++pos;
+    pos += __popcll(m);
   }
 }
 
