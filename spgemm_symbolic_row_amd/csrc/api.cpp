@@ -233,6 +233,7 @@ struct spgemm_plan_s {
   hipEvent_t evFork = nullptr, evL = nullptr, evH = nullptr;
   int device = 0;
   int64_t lds = 0, tau = 0;
+  int numCUs = 0;
   spgemm_params params{};
   int state = 0;  // 0 planned, 1 symbolic done, 2 numeric done, -1 failed
   std::string err;
@@ -498,6 +499,7 @@ void do_plan(spgemm_plan_t p) {
   HIP_CHECK(hipGetDevice(&p->device));
   int ldsDev = 0;
   HIP_CHECK(hipDeviceGetAttribute(&ldsDev, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device));
+  HIP_CHECK(hipDeviceGetAttribute(&p->numCUs, hipDeviceAttributeMultiprocessorCount, p->device));
   p->lds = p->opts.lds_budget ? p->opts.lds_budget : ldsDev;
   if (p->lds > ldsDev || p->lds < 4096)
     throw Error{SPGEMM_ERR_INVALID_ARG, "lds_budget must lie in [4096, LDS per work group]"};
@@ -993,7 +995,8 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval) {
   ph_end(p, ph, s);
   const int64_t st = B.fcBinStart[p->NS], en = B.fcBinStart[p->NS + 1];
   const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
-  launch_dense_num(p->f64, B.fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord, s);
+  launch_dense_num(p->f64, B.fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord,
+                   p->numCUs, s);
   ph_end(p, phD, s);
   check_launch("chunk numeric");
 }

@@ -209,7 +209,7 @@ void launch_dense_sym(const int32_t* items, int64_t n, const ChunkList& cl, int3
                       hipStream_t s);
 void launch_dense_num(bool f64, const int32_t* items, int64_t n, const ChunkList& cl,
                       const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
-                      hipStream_t s);
+                      int numCUs, hipStream_t s);
 size_t dense_num_lds(bool f64, int64_t W);
 // Per heavy row: exclusive scan of its nreq slot counts -> slotOff, and the
 // row total -> cnt[xheavy[r]].

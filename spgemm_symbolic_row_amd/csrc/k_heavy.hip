@@ -2,6 +2,8 @@
 // page, §III-C and §III-E): heavy-first placement of each level's chunks,
 // the list of final chunks, their bins, the dense LDS accumulator of W-wide
 // heavy chunks, and the per-row assembly of chunk offsets.
+#include <algorithm>
+
 #include "device_common.hpp"
 
 namespace sg {
@@ -142,86 +144,142 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const int32_t* __restrict__ i
 
 // Numeric: val[W] + W-bit bitmap in LDS, filled by LDS atomics; the set
 // bits, taken in column order, give the chunk sorted and compacted.
+//
+// One work group per CU holds the 128 KiB accumulator, so the kernel is
+// persistent: a work group takes chunks blockIdx.x, blockIdx.x + gridDim.x,
+// ..., loads the first batch of its next chunk while it writes out the
+// current one, and clears only the slots the current chunk touched (the
+// whole accumulator is cleared once, at the start).
 constexpr int kDenseNT = 1024;
+constexpr int kDenseB = 8;  // elements per thread per batch
 template <typename V>
-__global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restrict__ items, ChunkList cl,
+__device__ __forceinline__ void dense_load_batch(const int32_t* __restrict__ col,
+                                                 const V* __restrict__ val, int64_t e0, int64_t end,
+                                                 int32_t (&cc)[kDenseB], V (&vv)[kDenseB]) {
+#pragma unroll
+  for (int k = 0; k < kDenseB; ++k) {
+    const int64_t e = e0 + (int64_t)k * kDenseNT;
+    cc[k] = e < end ? col[e] : -1;
+    vv[k] = e < end ? val[e] : V(0);
+  }
+}
+template <typename V>
+__device__ __forceinline__ void dense_add_batch(V* vals, uint32_t* bm, const int32_t (&cc)[kDenseB],
+                                                const V (&vv)[kDenseB]) {
+#pragma unroll
+  for (int k = 0; k < kDenseB; ++k) {
+    const int32_t c = cc[k];
+    if (c >= 0) {
+      atomicAdd(&vals[c], vv[k]);
+      const uint32_t bit = 1u << (c & 31);
+      if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+    }
+  }
+}
+
+template <typename V>
+__global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restrict__ items, int64_t n,
+                                                        ChunkList cl,
                                                         const int64_t* __restrict__ cRowOff,
                                                         int32_t* __restrict__ ccol,
                                                         V* __restrict__ cval,
                                                         int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kWaves = kDenseNT / kWave;
   const int W = (int)cl.W;
   const int nwords = (W + 31) / 32;
   V* vals = (V*)smem;
   uint32_t* bm = (uint32_t*)(vals + W);
   int32_t* wtot = (int32_t*)(bm + nwords);
-  const int32_t item = items[blockIdx.x];
   for (int i = threadIdx.x; i < W; i += kDenseNT) vals[i] = V(0);
   for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
-  __syncthreads();
-  const int64_t off = cl.off[item], end = off + cl.cnt[item];
-  const bool b1 = cl.buf[item] != 0;
-  const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
-  const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
-  constexpr int kB = 8;  // loads in flight per thread
-  for (int64_t e0 = off + threadIdx.x; e0 < end; e0 += (int64_t)kDenseNT * kB) {
-    int32_t cc[kB];
-    V vv[kB];
-#pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      const int64_t e = e0 + (int64_t)k * kDenseNT;
-      cc[k] = e < end ? col[e] : -1;
-      vv[k] = e < end ? val[e] : V(0);
-    }
-#pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      const int32_t c = cc[k];
-      if (c >= 0) {
-        atomicAdd(&vals[c], vv[k]);
-        const uint32_t bit = 1u << (c & 31);
-        if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
-      }
-    }
-  }
-  __syncthreads();
-  // Output in column order with coalesced stores: each wave owns a
-  // contiguous range of 64-column groups; a group's set columns are ranked
-  // by a ballot, so consecutive lanes write consecutive entries.
-  constexpr int kWaves = kDenseNT / kWave;
-  const int ngroups = (W + kWave - 1) / kWave;
-  const int gpw = (ngroups + kWaves - 1) / kWaves;  // groups per wave
+  const int ngroups = (W + kWave - 1) / kWave;  // 64-column groups
+  const int gpw = (ngroups + kWaves - 1) / kWaves;
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int g0 = w * gpw, g1 = (g0 + gpw < ngroups) ? g0 + gpw : ngroups;
-  int32_t mine = 0;
-  for (int g = g0 + lane; g < g1; g += kWave) {
-    const int c = g * kWave;
-    mine += __popc(bm[c >> 5]) + (c + 32 < W ? __popc(bm[(c >> 5) + 1]) : 0);
+
+  int64_t ci = blockIdx.x;
+  int32_t cc[kDenseB];
+  V vv[kDenseB];
+  int32_t item = 0;
+  int64_t off = 0, end = 0;
+  const int32_t* col = cl.col0;
+  const V* val = (const V*)cl.val0;
+  if (ci < n) {
+    item = items[ci];
+    off = cl.off[item];
+    end = off + cl.cnt[item];
+    const bool b1 = cl.buf[item] != 0;
+    col = b1 ? cl.col1 : cl.col0;
+    val = (const V*)(b1 ? cl.val1 : cl.val0);
+    dense_load_batch(col, val, off + threadIdx.x, end, cc, vv);
   }
-  mine = wave_sum(mine);
-  if (lane == 0) wtot[w] = mine;
   __syncthreads();
-  int32_t pos = 0, total = 0;
-  for (int i = 0; i < kWaves; ++i) {
-    const int32_t t = wtot[i];
-    if (i < w) pos += t;
-    total += t;
-  }
-  const int64_t hr = cl.row[item];
-  const int64_t sidx = hr * cl.nreq + cl.slot[item];
-  const int64_t base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
-  const int32_t want = cl.slotNnz[sidx];
-  if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
-  const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
-  for (int g = g0; g < g1; ++g) {
-    const int c = g * kWave + lane;
-    const bool set = c < W && ((bm[c >> 5] >> (c & 31)) & 1u);
-    const uint64_t m = __ballot(set);
-    const int32_t p = pos + __popcll(m & lanemask_lt());
-    if (set && p < want) {
-      ccol[base + p] = colBase + c;
-      cval[base + p] = vals[c];
+  while (ci < n) {
+    // Where the chunk goes, read before any later load is issued.
+    const int64_t hr = cl.row[item];
+    const int64_t sidx = hr * cl.nreq + cl.slot[item];
+    const int64_t base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
+    const int32_t want = cl.slotNnz[sidx];
+    const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+    dense_add_batch(vals, bm, cc, vv);
+    for (int64_t e0 = off + threadIdx.x + (int64_t)kDenseNT * kDenseB; e0 < end;
+         e0 += (int64_t)kDenseNT * kDenseB) {
+      dense_load_batch(col, val, e0, end, cc, vv);
+      dense_add_batch(vals, bm, cc, vv);
     }
-    pos += __popcll(m);
+    __syncthreads();
+    // First batch of the next chunk, in flight during the write-out.
+    const int64_t cn = ci + gridDim.x;
+    if (cn < n) {
+      item = items[cn];
+      off = cl.off[item];
+      end = off + cl.cnt[item];
+      const bool b1 = cl.buf[item] != 0;
+      col = b1 ? cl.col1 : cl.col0;
+      val = (const V*)(b1 ? cl.val1 : cl.val0);
+      dense_load_batch(col, val, off + threadIdx.x, end, cc, vv);
+    }
+    // Write-out in column order with coalesced stores: each wave owns a
+    // contiguous range of 64-column groups; a group's set columns are
+    // ranked by a ballot, so consecutive lanes write consecutive entries.
+    int32_t mine = 0;
+    for (int g = g0 + lane; g < g1; g += kWave) {
+      const int c = g * kWave;
+      mine += __popc(bm[c >> 5]) + (c + 32 < W ? __popc(bm[(c >> 5) + 1]) : 0);
+    }
+    mine = wave_sum(mine);
+    if (lane == 0) wtot[w] = mine;
+    __syncthreads();
+    int32_t pos = 0, total = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      const int32_t t = wtot[i];
+      if (i < w) pos += t;
+      total += t;
+    }
+    if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
+    for (int g = g0; g < g1; ++g) {
+      const int c = g * kWave + lane;
+      const bool set = c < W && ((bm[c >> 5] >> (c & 31)) & 1u);
+      const uint64_t m = __ballot(set);
+      const int32_t p = pos + __popcll(m & lanemask_lt());
+      if (set) {
+        if (p < want) {
+          ccol[base + p] = colBase + c;
+          cval[base + p] = vals[c];
+        }
+        vals[c] = V(0);
+      }
+      pos += __popcll(m);
+    }
+    // This wave alone reads its groups' words: clear them for the next chunk.
+    for (int g = g0 + lane; g < g1; g += kWave) {
+      const int c = g * kWave;
+      bm[c >> 5] = 0;
+      if (c + 32 < W) bm[(c >> 5) + 1] = 0;
+    }
+    __syncthreads();
+    ci = cn;
   }
 }
 
@@ -302,15 +360,16 @@ size_t dense_num_lds(bool f64, int64_t W) {
 
 void launch_dense_num(bool f64, const int32_t* items, int64_t n, const ChunkList& cl,
                       const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
-                      hipStream_t s) {
+                      int numCUs, hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = dense_num_lds(f64, cl.W);
+  const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1));
   if (f64)
-    hipLaunchKernelGGL(k_dense_num<double>, dim3((unsigned)n), dim3(kDenseNT), lds, s, items, cl,
-                       cRowOff, ccol, (double*)cval, err);
+    hipLaunchKernelGGL(k_dense_num<double>, dim3(g), dim3(kDenseNT), lds, s, items, n, cl, cRowOff,
+                       ccol, (double*)cval, err);
   else
-    hipLaunchKernelGGL(k_dense_num<float>, dim3((unsigned)n), dim3(kDenseNT), lds, s, items, cl,
-                       cRowOff, ccol, (float*)cval, err);
+    hipLaunchKernelGGL(k_dense_num<float>, dim3(g), dim3(kDenseNT), lds, s, items, n, cl, cRowOff,
+                       ccol, (float*)cval, err);
 }
 
 void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,
