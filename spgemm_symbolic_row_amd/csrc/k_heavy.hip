@@ -363,7 +363,9 @@ void launch_dense_num(bool f64, const int32_t* items, int64_t n, const ChunkList
                       int numCUs, hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = dense_num_lds(f64, cl.W);
-  const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1));
+  // As many work groups as fit on the device at once (LDS of a CU: 160 KiB).
+  const int64_t perCU = std::max<int64_t>(1, (int64_t)163840 / (int64_t)lds);
+  const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1) * perCU);
   if (f64)
     hipLaunchKernelGGL(k_dense_num<double>, dim3(g), dim3(kDenseNT), lds, s, items, n, cl, cRowOff,
                        ccol, (double*)cval, err);
