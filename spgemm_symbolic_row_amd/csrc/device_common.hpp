@@ -9,6 +9,9 @@
 
 namespace sg {
 
+// XCDs of an MI355X; work groups are dealt to them round-robin.
+constexpr int kXcds = 8;
+
 constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -36,12 +36,12 @@ __device__ __forceinline__ int bits_for(int n) {
 // that row starts exactly at e1.  Returns nrows, or -1 when more than
 // maxRows rows meet the range.
 __device__ __forceinline__ int range_rows(const int64_t* __restrict__ rowPtr, int64_t R,
-                                          const int32_t* __restrict__ blkRow, int64_t e0,
-                                          int64_t e1, int maxRows, int64_t* bnd, int64_t* s_r0,
-                                          int32_t* s_nrows) {
+                                          const int32_t* __restrict__ blkRow, int64_t tile,
+                                          int64_t nTiles, int64_t e0, int64_t e1, int maxRows,
+                                          int64_t* bnd, int64_t* s_r0, int32_t* s_nrows) {
   if (threadIdx.x == 0) {
-    const int64_t r0 = blkRow[blockIdx.x];
-    int64_t r1 = (blockIdx.x + 1 < gridDim.x) ? blkRow[blockIdx.x + 1] : R - 1;
+    const int64_t r0 = blkRow[tile];
+    int64_t r1 = (tile + 1 < nTiles) ? blkRow[tile + 1] : R - 1;
     if (r1 > r0 && rowPtr[r1] >= e1) r1 -= 1;
     *s_r0 = r0;
     *s_nrows = (int32_t)(r1 - r0 + 1);
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
   const int64_t e0 = (int64_t)blockIdx.x * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
-  const int nrows = range_rows(rowPtr, R, blkRow, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
+  const int nrows = range_rows(rowPtr, R, blkRow, blockIdx.x, gridDim.x, e0, e1, maxRows, bnd,
+                               &s_r0, &s_nrows);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
@@ -170,18 +171,26 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   __shared__ int32_t wtot[kNT / kWave];
   __shared__ int64_t s_r0, s_t0, s_t1;
   __shared__ int32_t s_nrows;
-  const int64_t e0 = (int64_t)blockIdx.x * blockElems;
+  // Work groups are dealt round-robin to the XCDs; each XCD gets a
+  // contiguous run of tiles instead, so that neighbouring heavy rows, which
+  // share B rows, are expanded under the same L2.  The grid is padded to a
+  // multiple of the XCD count; padding tiles exit at once.
+  const int64_t nTiles = (E + blockElems - 1) / blockElems;
+  const int64_t tile = (int64_t)(blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+  if (tile >= nTiles) return;
+  const int64_t e0 = tile * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
   if constexpr (kExpand) {
-    // The entry of the block's first element, and a bound on the entry of
+    // The entry of the tile's first element, and a bound on the entry of
     // its last (range_rows below synchronises before they are read).
     if (threadIdx.x == kWave) {
-      s_t0 = src.blkEnt[blockIdx.x];
-      s_t1 = (blockIdx.x + 1 < gridDim.x) ? src.blkEnt[blockIdx.x + 1] : src.nE - 1;
+      s_t0 = src.blkEnt[tile];
+      s_t1 = (tile + 1 < nTiles) ? src.blkEnt[tile + 1] : src.nE - 1;
     }
   }
-  const int nrows = range_rows(rowPtr, R, blkRow, e0, e1, maxRows, bnd, &s_r0, &s_nrows);
+  const int nrows = range_rows(rowPtr, R, blkRow, tile, nTiles, e0, e1, maxRows, bnd, &s_r0,
+                               &s_nrows);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
@@ -378,7 +387,7 @@ void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* r
                        int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
                        hipStream_t s) {
   if (E <= 0) return;
-  const unsigned g = grid_for(E, blockElems);
+  const unsigned g = (grid_for(E, blockElems) + kXcds - 1) / kXcds * kXcds;
   const size_t NB = (size_t)maxRows * v;
   const size_t vb = !outVal ? 0 : f64 ? 8 : 4;
   const size_t lds = NB * 8 + (size_t)maxRows * 8 + (size_t)blockElems * (vb + 4 + 2) + NB * 8 + 16;

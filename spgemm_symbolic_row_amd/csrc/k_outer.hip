@@ -84,7 +84,6 @@ __global__ __launch_bounds__(kNT) void k_seg_base(int64_t nE, const int32_t* __r
 // segBase[entry] + (position inside the segment).  Consecutive elements of
 // a segment read consecutive B entries and write consecutive C-hat slots.
 constexpr int kOpBlock = 32768;
-constexpr int kXcds = 8;
 
 template <typename V, bool kVals>
 __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t* __restrict__ entryOff,
