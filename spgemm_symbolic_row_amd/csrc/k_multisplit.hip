@@ -20,8 +20,8 @@ inline unsigned grid_for(int64_t n, int per_block) {
 // ballot per bit so a single lane per bucket updates the LDS counters.
 constexpr int kMsNBMax = 1024;  // LDS buckets per work group
 constexpr int kMsRowsMax = 512;
-constexpr int kMsItemsF64 = 8;   // elements per thread held in registers
-constexpr int kMsItemsF32 = 16;
+constexpr int kMsItemsF64 = 4;   // elements per thread held in registers
+constexpr int kMsItemsF32 = 8;
 
 __device__ __forceinline__ int bits_for(int n) {
   int b = 0;
