@@ -109,6 +109,8 @@ void make_bins(int64_t tau, int64_t lds, int val_bytes, std::vector<BinCfg>* sym
     n.spt = (int32_t)(T / tpr);
     n.N = (int32_t)N;
     n.lds = (size_t)rpb * T * slot + extra;
+    if (!num_bin_supported(n))
+      throw Error{SPGEMM_ERR_INVALID_ARG, "no numeric kernel for this bin size"};
     num->push_back(n);
   }
 }

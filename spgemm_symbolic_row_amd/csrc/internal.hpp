@@ -115,6 +115,8 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
                      int32_t* err, hipStream_t s);
 void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const ChunkList& cl,
                        int32_t* err, hipStream_t s);
+// Whether a numeric bin's (tpr, sort size) has a kernel instance.
+bool num_bin_supported(const BinCfg& b);
 void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
                        const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
                        int32_t* err, hipStream_t s);

@@ -131,12 +131,12 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const int32_t* __restri
 }
 
 // ----------------------------------------------------------------- numeric
-// Shared tail of the numeric kernels: compact the occupied slots of this
-// group's table into [0, total), sort them by key, return total.  Called by
-// every thread of the work group.
-template <int TPR, int RPB, typename V>
-__device__ __forceinline__ int32_t compact_and_sort(int32_t* keys, V* vals, int32_t spt,
-                                                    int32_t N, int32_t* wtot) {
+// Shared tail of the numeric kernels, part 1: compact the occupied slots of
+// this group's table into [0, total) and pad [total, TPR * E) with INT_MAX.
+// Returns total.  Called by every thread of the work group.
+template <int TPR, int RPB, int E, typename V>
+__device__ __forceinline__ int32_t compact_slots(int32_t* keys, V* vals, int32_t spt,
+                                                 int32_t* wtot) {
   constexpr int WPR = TPR / kWave;
   const int g = threadIdx.x / TPR, t = threadIdx.x % TPR, w = t / kWave;
   int32_t kk[kMaxSpt];
@@ -173,34 +173,102 @@ __device__ __forceinline__ int32_t compact_and_sort(int32_t* keys, V* vals, int3
       ++pos;
     }
   }
-  for (int i = total + t; i < N; i += TPR) keys[i] = INT_MAX;
+  for (int i = total + t; i < TPR * E; i += TPR) keys[i] = INT_MAX;
   __syncthreads();
-  // Bitonic sort of keys[0, N) carrying vals; N is a power of two.
-  for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = t; i < (N >> 1); i += TPR) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo + j;
-        const bool up = (lo & k) == 0;
-        const int32_t ka = keys[lo], kb = keys[hi];
-        if ((ka > kb) == up) {
-          keys[lo] = kb;
-          keys[hi] = ka;
-          const V va = vals[lo];
-          vals[lo] = vals[hi];
-          vals[hi] = va;
-        }
-      }
-      __syncthreads();
-    }
-  }
   return total;
 }
 
-template <int TPR, int RPB, typename V>
+// Part 2: bitonic sort of the padded entries [0, TPR * E) into registers:
+// thread t ends with the entries of rank t*E .. t*E+E-1.  Of the network's
+// compare-exchange distances, those below E are register swaps inside a
+// thread, those below 64*E shuffles between lanes of one wave, and only the
+// longer ones go through LDS with barriers (none when a wave owns the item).
+template <int TPR, int E, typename V>
+__device__ __forceinline__ void sort_to_regs(int32_t* keys, V* vals, int32_t (&kk)[E],
+                                             V (&vv)[E]) {
+  constexpr int NP = TPR * E;
+  constexpr int kLaneSpan = kWave * E;
+  const int t = threadIdx.x % TPR;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    kk[e] = keys[t * E + e];
+    vv[e] = vals[t * E + e];
+  }
+  for (int k = 2; k <= NP; k <<= 1) {
+    int j = k >> 1;
+    if (j >= kLaneSpan) {
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        keys[t * E + e] = kk[e];
+        vals[t * E + e] = vv[e];
+      }
+      __syncthreads();
+      for (; j >= kLaneSpan; j >>= 1) {
+        for (int i = t; i < NP / 2; i += TPR) {
+          const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+          const int hi = lo + j;
+          const bool up = (lo & k) == 0;
+          const int32_t ka = keys[lo], kb = keys[hi];
+          if ((ka > kb) == up) {
+            keys[lo] = kb;
+            keys[hi] = ka;
+            const V va = vals[lo];
+            vals[lo] = vals[hi];
+            vals[hi] = va;
+          }
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        kk[e] = keys[t * E + e];
+        vv[e] = vals[t * E + e];
+      }
+    }
+    for (; j >= E; j >>= 1) {
+      const int ld = j / E;  // lane distance, below 64
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int32_t ok = __shfl_xor(kk[e], ld);
+        const V ov = __shfl_xor(vv[e], ld);
+        const int i = t * E + e;
+        const bool up = (i & k) == 0;
+        const bool lower = (i & j) == 0;
+        // In an ascending pair the lower position keeps the smaller key.
+        const bool take = (lower == up) ? (ok < kk[e]) : (ok > kk[e]);
+        if (take) {
+          kk[e] = ok;
+          vv[e] = ov;
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = E / 2; jj >= 1; jj >>= 1) {
+      if (jj < k) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & jj) == 0) {
+            const bool up = ((t * E + e) & k) == 0;
+            if ((kk[e] > kk[e + jj]) == up) {
+              const int32_t tk = kk[e];
+              kk[e] = kk[e + jj];
+              kk[e + jj] = tk;
+              const V tv = vv[e];
+              vv[e] = vv[e + jj];
+              vv[e + jj] = tv;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int TPR, int RPB, int E, typename V>
 __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict__ rows,
                                                        int64_t nrows, int32_t T, int32_t spt,
-                                                       int32_t N, RowArgs a,
+                                                       RowArgs a,
                                                        const int64_t* __restrict__ cRowOff,
                                                        int32_t* __restrict__ ccol,
                                                        V* __restrict__ cval,
@@ -235,23 +303,30 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
                         });
   }
   __syncthreads();
-  const int32_t total = compact_and_sort<TPR, RPB, V>(keys, vals, spt, N, wtot);
+  const int32_t total = compact_slots<TPR, RPB, E, V>(keys, vals, spt, wtot);
+  int32_t kk[E];
+  V vv[E];
+  sort_to_regs<TPR, E, V>(keys, vals, kk, vv);
   if (ri < nrows) {
     const int64_t base = cRowOff[row];
     const int64_t want = cRowOff[row + 1] - base;
     if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
     const int32_t lim = (int32_t)(want < total ? want : total);
-    for (int e = t; e < lim; e += TPR) {
-      ccol[base + e] = keys[e];
-      cval[base + e] = vals[e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int r = t * E + e;
+      if (r < lim) {
+        ccol[base + r] = kk[e];
+        cval[base + r] = vv[e];
+      }
     }
   }
 }
 
-template <int TPR, int RPB, typename V>
+template <int TPR, int RPB, int E, typename V>
 __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restrict__ items,
                                                          int64_t n, int32_t T, int32_t spt,
-                                                         int32_t N, ChunkList cl,
+                                                         ChunkList cl,
                                                          const int64_t* __restrict__ cRowOff,
                                                          int32_t* __restrict__ ccol,
                                                          V* __restrict__ cval,
@@ -280,7 +355,10 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restri
     for (int64_t e = off + t; e < end; e += TPR) hmap_add(keys, vals, (uint32_t)T, col[e], val[e], err);
   }
   __syncthreads();
-  const int32_t total = compact_and_sort<TPR, RPB, V>(keys, vals, spt, N, wtot);
+  const int32_t total = compact_slots<TPR, RPB, E, V>(keys, vals, spt, wtot);
+  int32_t kk[E];
+  V vv[E];
+  sort_to_regs<TPR, E, V>(keys, vals, kk, vv);
   if (ri < n) {
     const int64_t hr = cl.row[item];
     const int64_t sidx = hr * cl.nreq + cl.slot[item];
@@ -289,9 +367,13 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restri
     if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
     const int32_t lim = want < total ? want : total;
     const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
-    for (int e = t; e < lim; e += TPR) {
-      ccol[base + e] = colBase + keys[e];
-      cval[base + e] = vals[e];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int r = t * E + e;
+      if (r < lim) {
+        ccol[base + r] = colBase + kk[e];
+        cval[base + r] = vv[e];
+      }
     }
   }
 }
@@ -314,17 +396,25 @@ void light_set_attributes() {
   set_lds_attr(k_sym_chunks<256, 1>);
   set_lds_attr(k_sym_chunks<512, 1>);
   set_lds_attr(k_sym_chunks<1024, 1>);
-#define SG_NUM_ATTR(V)                     \
-  set_lds_attr(k_num_rows<64, 4, V>);      \
-  set_lds_attr(k_num_rows<128, 2, V>);     \
-  set_lds_attr(k_num_rows<256, 1, V>);     \
-  set_lds_attr(k_num_rows<512, 1, V>);     \
-  set_lds_attr(k_num_rows<1024, 1, V>);    \
-  set_lds_attr(k_num_chunks<64, 4, V>);    \
-  set_lds_attr(k_num_chunks<128, 2, V>);   \
-  set_lds_attr(k_num_chunks<256, 1, V>);   \
-  set_lds_attr(k_num_chunks<512, 1, V>);   \
-  set_lds_attr(k_num_chunks<1024, 1, V>);
+#define SG_NUM_ATTR(V)                          \
+  set_lds_attr(k_num_rows<64, 4, 1, V>);        \
+  set_lds_attr(k_num_rows<64, 4, 2, V>);        \
+  set_lds_attr(k_num_rows<64, 4, 4, V>);        \
+  set_lds_attr(k_num_rows<128, 2, 4, V>);       \
+  set_lds_attr(k_num_rows<256, 1, 4, V>);       \
+  set_lds_attr(k_num_rows<512, 1, 4, V>);       \
+  set_lds_attr(k_num_rows<1024, 1, 4, V>);      \
+  set_lds_attr(k_num_rows<1024, 1, 8, V>);      \
+  set_lds_attr(k_num_rows<1024, 1, 16, V>);     \
+  set_lds_attr(k_num_chunks<64, 4, 1, V>);      \
+  set_lds_attr(k_num_chunks<64, 4, 2, V>);      \
+  set_lds_attr(k_num_chunks<64, 4, 4, V>);      \
+  set_lds_attr(k_num_chunks<128, 2, 4, V>);     \
+  set_lds_attr(k_num_chunks<256, 1, 4, V>);     \
+  set_lds_attr(k_num_chunks<512, 1, 4, V>);     \
+  set_lds_attr(k_num_chunks<1024, 1, 4, V>);    \
+  set_lds_attr(k_num_chunks<1024, 1, 8, V>);    \
+  set_lds_attr(k_num_chunks<1024, 1, 16, V>);
   SG_NUM_ATTR(float)
   SG_NUM_ATTR(double)
 #undef SG_NUM_ATTR
@@ -361,44 +451,76 @@ void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const C
 #undef L
 }
 
+// Entries per thread of the register sort: max(N, tpr) / tpr.
+int sort_e(const BinCfg& b) { return (b.N > b.tpr ? b.N : b.tpr) / b.tpr; }
+
+// (tpr, E) pairs the bins produce: tpr 64 for N <= 256 (E 1, 2, 4), tpr 128
+// to 512 with N = 4 tpr, tpr 1024 with N = 4096, 8192 or 16384.
+#define SG_DISPATCH_NUM(b, MACRO)                                               \
+  do {                                                                          \
+    const int e_ = sort_e(b);                                                   \
+    if ((b).tpr == 64 && e_ == 1) MACRO(64, 4, 1);                              \
+    else if ((b).tpr == 64 && e_ == 2) MACRO(64, 4, 2);                         \
+    else if ((b).tpr == 64 && e_ == 4) MACRO(64, 4, 4);                         \
+    else if ((b).tpr == 128 && e_ == 4) MACRO(128, 2, 4);                       \
+    else if ((b).tpr == 256 && e_ == 4) MACRO(256, 1, 4);                       \
+    else if ((b).tpr == 512 && e_ == 4) MACRO(512, 1, 4);                       \
+    else if ((b).tpr == 1024 && e_ == 4) MACRO(1024, 1, 4);                     \
+    else if ((b).tpr == 1024 && e_ == 8) MACRO(1024, 1, 8);                     \
+    else if ((b).tpr == 1024 && e_ == 16) MACRO(1024, 1, 16);                   \
+    else flag_unsupported = true;                                               \
+  } while (0)
+
+bool num_bin_supported(const BinCfg& b) {
+  bool flag_unsupported = false;
+#define NOP(TPR, RPB, E) (void)0
+  SG_DISPATCH_NUM(b, NOP);
+#undef NOP
+  return !flag_unsupported;
+}
+
 void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
                      const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
                      int32_t* err, hipStream_t s) {
   if (nrows <= 0) return;
+  bool flag_unsupported = false;
   const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
   if (f64) {
-#define L(TPR, RPB)                                                                            \
-  hipLaunchKernelGGL((k_num_rows<TPR, RPB, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, \
-                     nrows, b.T, b.spt, b.N, a, cRowOff, ccol, (double*)cval, err)
-    SG_DISPATCH_TPR(b, L)
+#define L(TPR, RPB, E)                                                                       \
+  hipLaunchKernelGGL((k_num_rows<TPR, RPB, E, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
+                     rows, nrows, b.T, b.spt, a, cRowOff, ccol, (double*)cval, err)
+    SG_DISPATCH_NUM(b, L);
 #undef L
   } else {
-#define L(TPR, RPB)                                                                           \
-  hipLaunchKernelGGL((k_num_rows<TPR, RPB, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, \
-                     nrows, b.T, b.spt, b.N, a, cRowOff, ccol, (float*)cval, err)
-    SG_DISPATCH_TPR(b, L)
+#define L(TPR, RPB, E)                                                                      \
+  hipLaunchKernelGGL((k_num_rows<TPR, RPB, E, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
+                     rows, nrows, b.T, b.spt, a, cRowOff, ccol, (float*)cval, err)
+    SG_DISPATCH_NUM(b, L);
 #undef L
   }
+  (void)flag_unsupported;  // make_bins rejects bins without an instance
 }
 
 void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
                        const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
                        int32_t* err, hipStream_t s) {
   if (n <= 0) return;
+  bool flag_unsupported = false;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
   if (f64) {
-#define L(TPR, RPB)                                                                            \
-  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, double>), dim3(grid), dim3(TPR * RPB), b.lds, s,     \
-                     items, n, b.T, b.spt, b.N, cl, cRowOff, ccol, (double*)cval, err)
-    SG_DISPATCH_TPR(b, L)
+#define L(TPR, RPB, E)                                                                         \
+  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
+                     items, n, b.T, b.spt, cl, cRowOff, ccol, (double*)cval, err)
+    SG_DISPATCH_NUM(b, L);
 #undef L
   } else {
-#define L(TPR, RPB)                                                                           \
-  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, float>), dim3(grid), dim3(TPR * RPB), b.lds, s,     \
-                     items, n, b.T, b.spt, b.N, cl, cRowOff, ccol, (float*)cval, err)
-    SG_DISPATCH_TPR(b, L)
+#define L(TPR, RPB, E)                                                                        \
+  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
+                     items, n, b.T, b.spt, cl, cRowOff, ccol, (float*)cval, err)
+    SG_DISPATCH_NUM(b, L);
 #undef L
   }
+  (void)flag_unsupported;  // make_bins rejects bins without an instance
 }
 
 }  // namespace sg
