@@ -15,28 +15,76 @@ __device__ __forceinline__ int64_t rp_at(const void* rp, int64_t i) {
   return (int64_t)((const RP*)rp)[i];
 }
 
-// One wave per row: count kept entries, add kept values into column sums.
+// Column sums are aggregated per work group before they reach global memory:
+// a work group takes kPruneRows consecutive rows (one wave per row at a
+// time), adds every kept value into an LDS table keyed by column, and then
+// adds each distinct column's partial sum once with a global atomic.  Rows
+// close to each other usually share most columns (clustered graphs, banded
+// matrices), so far fewer global atomics are issued; a value whose column
+// finds no free slot within kPruneProbes probes goes to global memory
+// directly.  Kept counts per row are exact integers either way.
+constexpr int kPruneRows = 16;
+constexpr int kPruneSlots = 4096;
+constexpr int kPruneProbes = 16;
+
+__device__ __forceinline__ bool colsum_add_lds(int32_t* keys, double* vals, int32_t key, double v) {
+  uint32_t s = hash_slot(key, kPruneSlots);
+  for (int probe = 0; probe < kPruneProbes; ++probe) {
+    const int32_t cur = lds_load_relaxed(&keys[s]);
+    if (cur == key) {
+      atomicAdd(&vals[s], v);
+      return true;
+    }
+    if (cur == kEmptyKey) {
+      const int32_t old = atomicCAS(&keys[s], kEmptyKey, key);
+      if (old == kEmptyKey || old == key) {
+        atomicAdd(&vals[s], v);
+        return true;
+      }
+    }
+    s = (s + 1 == kPruneSlots) ? 0 : s + 1;
+  }
+  return false;
+}
+
 template <typename V, typename RP>
 __global__ __launch_bounds__(kNT) void k_prune_count(int64_t m, const void* __restrict__ rp,
                                                      const int32_t* __restrict__ col,
                                                      const V* __restrict__ val, V thr,
                                                      int64_t* __restrict__ keep,
                                                      double* __restrict__ colsum) {
-  const int64_t r = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
-  if (r >= m) return;
-  const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
-  int64_t kept = 0;
-  for (int64_t base = a; base < b; base += kWave) {
-    const int64_t e = base + lane_id();
-    bool k = false;
-    if (e < b) {
-      const V x = val[e];
-      k = x >= thr;
-      if (k) unsafeAtomicAdd(&colsum[col[e]], (double)x);
-    }
-    kept += __popcll(__ballot(k));
+  __shared__ int32_t keys[kPruneSlots];
+  __shared__ double vals[kPruneSlots];
+  for (int i = threadIdx.x; i < kPruneSlots; i += kNT) {
+    keys[i] = kEmptyKey;
+    vals[i] = 0.0;
   }
-  if (lane_id() == 0) keep[r] = kept;
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * kPruneRows;
+  const int w = threadIdx.x / kWave;
+  for (int64_t r = r0 + w; r < r0 + kPruneRows && r < m; r += kNT / kWave) {
+    const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
+    int64_t kept = 0;
+    for (int64_t base = a; base < b; base += kWave) {
+      const int64_t e = base + lane_id();
+      bool k = false;
+      if (e < b) {
+        const V x = val[e];
+        k = x >= thr;
+        if (k) {
+          const int32_t c = col[e];
+          if (!colsum_add_lds(keys, vals, c, (double)x)) unsafeAtomicAdd(&colsum[c], (double)x);
+        }
+      }
+      kept += __popcll(__ballot(k));
+    }
+    if (lane_id() == 0) keep[r] = kept;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPruneSlots; i += kNT) {
+    const int32_t c = keys[i];
+    if (c != kEmptyKey) unsafeAtomicAdd(&colsum[c], vals[i]);
+  }
 }
 
 // One wave per row: order-preserving compaction of the kept entries.
@@ -80,7 +128,7 @@ void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col,
                         bool f64, double thr, int64_t* keepCnt, double* colsum,
                         hipStream_t s) {
   if (m <= 0) return;
-  const dim3 g(grid_rows(m)), b(kNT);
+  const dim3 g((unsigned)((m + kPruneRows - 1) / kPruneRows)), b(kNT);
   if (f64) {
     if (rp64)
       hipLaunchKernelGGL((k_prune_count<double, int64_t>), g, b, 0, s, m, rp, col,
