@@ -148,6 +148,7 @@ def main():
                          "hardware byte counters can be scaled against a known size")
     ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
+    ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -186,6 +187,8 @@ def main():
         opts["dense_width"] = args.dense_width
     if args.lds_budget:
         opts["lds_budget"] = args.lds_budget
+    if args.heavy_threshold:
+        opts["heavy_threshold"] = args.heavy_threshold
     if args.config == "rmat20":
         opts["rowptr64"] = 1   # nnz(C) is about 9.7e9
     mcl = args.config == "mcl1m"

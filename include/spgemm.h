@@ -100,7 +100,13 @@ typedef struct spgemm_options {
                                    from A and B, row by row, so C-hat in row
                                    order is never written (default, when the
                                    counts come from the structure)            */
-  int32_t reserved32;
+  int32_t heavy_row_threshold;  /* rows with more intermediate products than
+                                   this take the heavy path; 0 = the
+                                   heavy_threshold option if set, else
+                                   floor(tau / 3): the largest light row whose
+                                   numeric LDS table (2 slots per product)
+                                   leaves room for three work groups per CU.
+                                   Chunks keep tau (recursion, bins).        */
   int64_t reserved[7];
 } spgemm_options;
 
@@ -160,6 +166,7 @@ typedef struct spgemm_stats {
                                  phases (one per level for the per-level ones,
                                  and one per batch and expansion)           */
   int64_t device_errors;      /* device status bits seen (0 when all is well)  */
+  int64_t heavy_row_threshold; /* rows above this many products were heavy     */
 } spgemm_stats;
 
 typedef struct spgemm_plan_s *spgemm_plan_t;

@@ -34,7 +34,7 @@ class Options(ctypes.Structure):
         ("mem_budget", c_i64), ("max_chunks_per_level", c_i32), ("rowptr64", c_i32),
         ("validate", c_i32), ("single_stream", c_i32), ("profile", c_i32),
         ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
-        ("alloc_ctx", c_vp), ("outer_product_expansion", c_i32), ("reserved32", c_i32),
+        ("alloc_ctx", c_vp), ("outer_product_expansion", c_i32), ("heavy_row_threshold", c_i32),
         ("reserved", c_i64 * 7),
     ]
 
@@ -64,6 +64,7 @@ class Stats(ctypes.Structure):
         ("ms_plan", ctypes.c_double), ("ms_symbolic", ctypes.c_double),
         ("ms_numeric", ctypes.c_double), ("phase_ms", ctypes.c_double * 16),
         ("phase_windows", c_i32 * 16), ("device_errors", c_i64),
+        ("heavy_row_threshold", c_i64),
     ]
 
     def as_dict(self):

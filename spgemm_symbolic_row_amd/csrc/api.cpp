@@ -234,7 +234,7 @@ struct spgemm_plan_s {
   hipStream_t stream = nullptr, sl = nullptr, sh = nullptr;
   hipEvent_t evFork = nullptr, evL = nullptr, evH = nullptr;
   int device = 0;
-  int64_t lds = 0, tau = 0;
+  int64_t lds = 0, tau = 0, rowTau = 0;  // chunk and row heavy thresholds
   int numCUs = 0;
   spgemm_params params{};
   int state = 0;  // 0 planned, 1 symbolic done, 2 numeric done, -1 failed
@@ -515,6 +515,14 @@ void do_plan(spgemm_plan_t p) {
       throw Error{SPGEMM_ERR_INVALID_ARG, "heavy_threshold must lie in [1, LDS-derived tau]"};
     p->tau = p->opts.heavy_threshold;
   }
+  // Light rows up to tau / 3 products: a numeric table of 2 slots per product
+  // then takes at most a third of the LDS, so three rows share a CU.  Larger
+  // rows run faster through the heavy path (measured on gfx950).
+  p->rowTau = p->opts.heavy_row_threshold ? p->opts.heavy_row_threshold
+              : p->opts.heavy_threshold   ? p->tau
+                                          : std::max<int64_t>(p->tau / 3, 1);
+  if (p->rowTau < 1 || p->rowTau > p->tau)
+    throw Error{SPGEMM_ERR_INVALID_ARG, "heavy_row_threshold must lie in [1, tau]"};
   if ((int64_t)dense_num_lds(p->f64, p->params.dense_width) > ldsDev ||
       p->params.dense_width > 32768)
     throw Error{SPGEMM_ERR_INVALID_ARG, "dense width does not fit the LDS"};
@@ -592,7 +600,7 @@ void do_plan(spgemm_plan_t p) {
   p->binStart = alloc_n<int32_t>(p, 65, s);
   launch_fill_i64(p->cnt, 0, m, s);
   const int ph = ph_begin(p, SPGEMM_PH_ROW_INFO, s);
-  launch_row_info(m, p->arp, p->acol, p->brp, p->bcol, p->tau, p->dSymCaps, p->NS, p->rowP,
+  launch_row_info(m, p->arp, p->acol, p->brp, p->bcol, p->rowTau, p->dSymCaps, p->NS, p->rowP,
                   p->scanA, p->rowBin, p->stats, s);
   const int nkeys = p->NS + 2;  // 0 empty, 1..NS hash bins, NS+1 heavy
   launch_bin_sort(p->rowBin, m, nkeys, p->binCnt, p->binFill, p->binStart, p->rowOrder, s);
@@ -610,6 +618,7 @@ void do_plan(spgemm_plan_t p) {
   p->st.light_rows = p->hStats[kStatLightRows];
   p->st.params = p->params;
   p->st.params.tau = p->tau;
+  p->st.heavy_row_threshold = p->rowTau;
   p->xheavy = p->rowOrder + p->rowBinStart[p->NS + 1];
   p->nreq = p->params.chunks_required;
   p->st.ms_plan = now_ms() - t0;
@@ -843,7 +852,9 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     launch_fill_i32(ctr, 0, 2, s);
     int32_t blockElems;
     int maxRows;
-    multisplit_geometry(f64 && vals, p->tau, v, &blockElems, &maxRows);
+    // Rows of the first level are heavy rows (more than rowTau elements),
+    // of later levels heavy chunks (more than tau).
+    multisplit_geometry(f64 && vals, l == 0 ? p->rowTau : p->tau, v, &blockElems, &maxRows);
     // First row (and, fed from A and B, first entry) of every work group.
     const int64_t nBlk = (E + blockElems - 1) / blockElems;
     int32_t* blkRow = alloc_n<int32_t>(p, nBlk, s);

@@ -168,6 +168,8 @@ def test_options_do_not_change_the_result():
     for opts in (dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, single_stream=1),
                  dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, rowptr64=1),
                  dict(heavy_threshold=100, dense_width=512, max_chunks_per_level=2),
+                 dict(heavy_threshold=100, heavy_row_threshold=20, dense_width=512),
+                 dict(heavy_row_threshold=1),
                  dict()):
         rp, col, val, _ = gpu_product(A, A, **opts)
         np.testing.assert_array_equal(rp, ref[0])
@@ -297,7 +299,8 @@ def test_rmat18_config_sampled():
                                      rng.choice(light, 1500, replace=False),
                                      np.nonzero(P == 0)[0][:20], [A.m - 1]]))
     rp_h, st, _ = _sampled_check(A, rows)
-    assert st["heavy_rows"] == heavy.size and st["params"]["v_chunks"] == [16]
+    assert st["params"]["tau"] == 6826 and st["heavy_row_threshold"] == 6826 // 3
+    assert st["heavy_rows"] == int((P > 6826 // 3).sum()) and st["params"]["v_chunks"] == [16]
     assert st["global_products"] == 0 and st["lds_dense_products"] > 0
     # the whole row-pointer array against the oracle's symbolic counts
     cnt = oracle.symbolic(A, A)
@@ -360,7 +363,8 @@ def test_rmat20_config_sampled_batched_rowptr64():
     del out
     torch.cuda.empty_cache()
     assert st["params"]["v_chunks"] == [32, 2] and st["params"]["levels"] == 2
-    assert st["heavy_rows"] == heavy.size and st["heavy_products"] == int(P[heavy].sum())
+    hv = P > st["heavy_row_threshold"]
+    assert st["heavy_rows"] == int(hv.sum()) and st["heavy_products"] == int(P[hv].sum())
     assert st["batches"] > 1
     cnt = oracle.symbolic(A, A)
     np.testing.assert_array_equal(np.diff(rp_h), cnt)
