@@ -193,10 +193,7 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
   int32_t* wtot = (int32_t*)(bm + nwords);
   for (int i = threadIdx.x; i < W; i += kDenseNT) vals[i] = V(0);
   for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
-  const int ngroups = (W + kWave - 1) / kWave;  // 64-column groups
-  const int gpw = (ngroups + kWaves - 1) / kWaves;
   const int w = threadIdx.x / kWave, lane = lane_id();
-  const int g0 = w * gpw, g1 = (g0 + gpw < ngroups) ? g0 + gpw : ngroups;
 
   int64_t ci = blockIdx.x;
   int32_t cc[kDenseB];
@@ -240,44 +237,67 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
       val = (const V*)(b1 ? cl.val1 : cl.val0);
       dense_load_batch(col, val, off + threadIdx.x, end, cc, vv);
     }
-    // Write-out in column order with coalesced stores: each wave owns a
-    // contiguous range of 64-column groups; a group's set columns are
-    // ranked by a ballot, so consecutive lanes write consecutive entries.
-    int32_t mine = 0;
-    for (int g = g0 + lane; g < g1; g += kWave) {
-      const int c = g * kWave;
-      mine += __popc(bm[c >> 5]) + (c + 32 < W ? __popc(bm[(c >> 5) + 1]) : 0);
+    // Write-out in column order.  Wave w owns columns [w*W/16, (w+1)*W/16),
+    // lane l a run of cpl of them; a wave scan of the lanes' popcounts gives
+    // every lane its output offset, and then output entries j, j+1, ... are
+    // written by consecutive lanes (each finds the lane and bit that hold
+    // entry j), so every store is fully coalesced.  The slot's value is
+    // cleared as it is read.
+    const int cpw = (W + kWaves - 1) / kWaves;        // columns per wave
+    const int cpl = cpw >= kWave ? cpw / kWave : 1;   // columns per lane, <= 32
+    const int lc0 = w * cpw + lane * cpl;             // this lane's first column
+    uint32_t mask = 0;
+    if (lc0 < W && lane * cpl < cpw) {
+      const uint32_t word = bm[lc0 >> 5];
+      mask = cpl >= 32 ? word : (word >> (lc0 & 31)) & ((1u << cpl) - 1u);
     }
-    mine = wave_sum(mine);
-    if (lane == 0) wtot[w] = mine;
+    const int32_t cntL = __popc(mask);
+    const int32_t incL = wave_incl_scan(cntL);
+    const int32_t exclL = incL - cntL;
+    const int32_t nw = __shfl(incL, kWave - 1);
+    if (lane == 0) wtot[w] = nw;
     __syncthreads();
-    int32_t pos = 0, total = 0;
+    int32_t wbase = 0, total = 0;
     for (int i = 0; i < kWaves; ++i) {
       const int32_t t = wtot[i];
-      if (i < w) pos += t;
+      if (i < w) wbase += t;
       total += t;
     }
     if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
-    for (int g = g0; g < g1; ++g) {
-      const int c = g * kWave + lane;
-      const bool set = c < W && ((bm[c >> 5] >> (c & 31)) & 1u);
-      const uint64_t m = __ballot(set);
-      const int32_t p = pos + __popcll(m & lanemask_lt());
-      if (set) {
+    for (int32_t j0 = 0; j0 < nw; j0 += kWave) {
+      const int32_t j = j0 + lane;
+      // Lane holding entry j: the last lane whose exclusive offset is <= j.
+      int src = 0;
+#pragma unroll
+      for (int step = 32; step >= 1; step >>= 1) {
+        const int32_t o = __shfl(exclL, src + step);
+        if (o <= j) src += step;
+      }
+      const uint32_t m = __shfl(mask, src);
+      int32_t k = j - __shfl(exclL, src);
+      // Position of the k-th set bit of m: halve the window each step.
+      int bit = 0;
+#pragma unroll
+      for (int half = 16; half >= 1; half >>= 1) {
+        const int32_t lo = __popc((m >> bit) & ((1u << half) - 1u));
+        if (k >= lo) {
+          k -= lo;
+          bit += half;
+        }
+      }
+      const int c = w * cpw + src * cpl + bit;
+      if (j < nw) {
+        const int32_t p = wbase + j;
+        const V x = vals[c];
+        vals[c] = V(0);
         if (p < want) {
           ccol[base + p] = colBase + c;
-          cval[base + p] = vals[c];
+          cval[base + p] = x;
         }
-        vals[c] = V(0);
       }
-      pos += __popcll(m);
     }
-    // This wave alone reads its groups' words: clear them for the next chunk.
-    for (int g = g0 + lane; g < g1; g += kWave) {
-      const int c = g * kWave;
-      bm[c >> 5] = 0;
-      if (c + 32 < W) bm[(c >> 5) + 1] = 0;
-    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
     __syncthreads();
     ci = cn;
   }
