@@ -995,21 +995,22 @@ void symbolic_batch(spgemm_plan_t p, const Batch& B) {
 void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval) {
   hipStream_t s = p->sh;
   const ChunkList cl = chunk_list(p, B);
+  // Descriptors of the chunks in bin order, gathered once.
+  ChunkDesc* desc = alloc_n<ChunkDesc>(p, B.nfc, s);
+  launch_chunk_desc(B.nfc, B.fcOrder, cl, p->cRowOff, desc, s);
   const int ph = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = B.fcBinStart[b], en = B.fcBinStart[b + 1];
     if (num_bitmap(p, b))
-      launch_num_chunks_rank(p->rankBins[b], p->f64, B.fcOrder + st, en - st, p->chunkWords, cl,
-                             p->cRowOff, ccol, cval, p->errWord, s);
+      launch_num_chunks_rank(p->rankBins[b], p->f64, desc + st, en - st, p->chunkWords, cl, ccol,
+                             cval, p->errWord, s);
     else
-      launch_num_chunks(p->numBins[b], p->f64, B.fcOrder + st, en - st, cl, p->cRowOff, ccol,
-                        cval, p->errWord, s);
+      launch_num_chunks(p->numBins[b], p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, s);
   }
   ph_end(p, ph, s);
   const int64_t st = B.fcBinStart[p->NS], en = B.fcBinStart[p->NS + 1];
   const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
-  launch_dense_num(p->f64, B.fcOrder + st, en - st, cl, p->cRowOff, ccol, cval, p->errWord,
-                   p->numCUs, s);
+  launch_dense_num(p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, p->numCUs, s);
   ph_end(p, phD, s);
   check_launch("chunk numeric");
 }

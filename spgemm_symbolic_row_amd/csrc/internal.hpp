@@ -75,6 +75,18 @@ struct ChunkList {
   int32_t* slotNnz;       // nnz of the chunk starting at each slot
 };
 
+// Everything a numeric chunk kernel needs about one final chunk, gathered
+// once per batch in the order the kernels take the chunks: where its
+// elements are, where its entries go, and how many there are.
+struct ChunkDesc {
+  int64_t off;      // first element in its buffer
+  int64_t base;     // first output position in C
+  int32_t cnt;      // elements
+  int32_t want;     // distinct columns (from symbolic)
+  int32_t colBase;  // global column of local column 0
+  int32_t buf;      // buffer holding the elements (0 or 1)
+};
+
 // ---- k_util.hip ----
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s);
@@ -117,9 +129,9 @@ void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const C
                        int32_t* err, hipStream_t s);
 // Whether a numeric bin's (tpr, sort size) has a kernel instance.
 bool num_bin_supported(const BinCfg& b);
-void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
-                       const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
-                       int32_t* err, hipStream_t s);
+void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
+                       const ChunkList& cl, int32_t* ccol, void* cval, int32_t* err,
+                       hipStream_t s);
 
 // ---- k_outer.hip, k_multisplit.hip, k_heavy.hip ----
 void heavy_set_attributes();
@@ -209,9 +221,11 @@ void launch_chunk_bins(int64_t nfc, const int32_t* fcCnt, int64_t lastFirst, int
                        int64_t* denseElems, hipStream_t s);
 void launch_dense_sym(const int32_t* items, int64_t n, const ChunkList& cl, int32_t* err,
                       hipStream_t s);
-void launch_dense_num(bool f64, const int32_t* items, int64_t n, const ChunkList& cl,
-                      const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
-                      int numCUs, hipStream_t s);
+void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
+                      int32_t* ccol, void* cval, int32_t* err, int numCUs, hipStream_t s);
+// desc[i] for the chunk order[i], i < n.
+void launch_chunk_desc(int64_t n, const int32_t* order, const ChunkList& cl,
+                       const int64_t* cRowOff, ChunkDesc* desc, hipStream_t s);
 size_t dense_num_lds(bool f64, int64_t W);
 // Per heavy row: exclusive scan of its nreq slot counts -> slotOff, and the
 // row total -> cnt[xheavy[r]].
@@ -224,9 +238,9 @@ size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb);
 // sizeClass 0: chunks of <= 256 elements (4 per work group), 1: <= 4096, 2: larger.
 void launch_sym_chunks_bitmap(int sizeClass, const int32_t* items, int64_t n, int32_t words,
                               const ChunkList& cl, hipStream_t s);
-void launch_num_chunks_rank(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
-                            int32_t words, const ChunkList& cl, const int64_t* cRowOff,
-                            int32_t* ccol, void* cval, int32_t* err, hipStream_t s);
+void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
+                            int32_t words, const ChunkList& cl, int32_t* ccol, void* cval,
+                            int32_t* err, hipStream_t s);
 
 // ---- k_prune.hip ----
 void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,

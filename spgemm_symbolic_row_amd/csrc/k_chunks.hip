@@ -93,10 +93,9 @@ __host__ __device__ constexpr size_t rank_group_bytes(int32_t T, int32_t words) 
 }
 
 template <int TPC, int CPB, typename V>
-__global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const int32_t* __restrict__ items,
+__global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const ChunkDesc* __restrict__ desc,
                                                               int64_t n, int32_t T, int32_t words,
                                                               ChunkList cl,
-                                                              const int64_t* __restrict__ cRowOff,
                                                               int32_t* __restrict__ ccol,
                                                               V* __restrict__ cval,
                                                               int32_t* __restrict__ err) {
@@ -116,11 +115,11 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const int32_t* __r
   for (int i = t; i < words; i += TPC) bm[i] = 0;
   __syncthreads();
   const int64_t ci = (int64_t)blockIdx.x * CPB + g;
-  int32_t item = 0;
+  ChunkDesc d{};
   if (ci < n) {
-    item = items[ci];
-    const int64_t off = cl.off[item], end = off + cl.cnt[item];
-    const bool b1 = cl.buf[item] != 0;
+    d = desc[ci];
+    const int64_t off = d.off, end = off + d.cnt;
+    const bool b1 = d.buf != 0;
     const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
     const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
     constexpr int kB = 4;  // loads in flight per thread
@@ -165,12 +164,10 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const int32_t* __r
   }
   __syncthreads();
   if (ci < n) {
-    const int64_t hr = cl.row[item];
-    const int64_t sidx = hr * cl.nreq + cl.slot[item];
-    const int64_t obase = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
-    const int32_t want = cl.slotNnz[sidx];
+    const int64_t obase = d.base;
+    const int32_t want = d.want;
     if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
-    const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+    const int32_t colBase = d.colBase;
     for (int s = t; s < T; s += TPC) {
       const int32_t k = keys[s];
       if (k != kEmptyKey) {
@@ -223,9 +220,9 @@ void launch_sym_chunks_bitmap(int sizeClass, const int32_t* items, int64_t n, in
   }
 }
 
-void launch_num_chunks_rank(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
-                            int32_t words, const ChunkList& cl, const int64_t* cRowOff,
-                            int32_t* ccol, void* cval, int32_t* err, hipStream_t s) {
+void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
+                            int32_t words, const ChunkList& cl, int32_t* ccol, void* cval,
+                            int32_t* err, hipStream_t s) {
   if (n <= 0) return;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
   const size_t lds = rank_chunk_lds(f64, b.T, words, b.rpb);
@@ -233,10 +230,10 @@ void launch_num_chunks_rank(const BinCfg& b, bool f64, const int32_t* items, int
   do {                                                                                         \
     if (f64)                                                                                   \
       hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, double>), dim3(grid), dim3(TPC * CPB),   \
-                         lds, s, items, n, b.T, words, cl, cRowOff, ccol, (double*)cval, err); \
+                         lds, s, desc, n, b.T, words, cl, ccol, (double*)cval, err);           \
     else                                                                                       \
       hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, float>), dim3(grid), dim3(TPC * CPB),    \
-                         lds, s, items, n, b.T, words, cl, cRowOff, ccol, (float*)cval, err);  \
+                         lds, s, desc, n, b.T, words, cl, ccol, (float*)cval, err);            \
   } while (0)
   switch (b.tpr) {
     case 64: L(64, 4); break;

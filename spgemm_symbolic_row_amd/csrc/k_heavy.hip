@@ -178,9 +178,8 @@ __device__ __forceinline__ void dense_add_batch(V* vals, uint32_t* bm, const int
 }
 
 template <typename V>
-__global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restrict__ items, int64_t n,
+__global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restrict__ desc, int64_t n,
                                                         ChunkList cl,
-                                                        const int64_t* __restrict__ cRowOff,
                                                         int32_t* __restrict__ ccol,
                                                         V* __restrict__ cval,
                                                         int32_t* __restrict__ err) {
@@ -198,27 +197,22 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
   int64_t ci = blockIdx.x;
   int32_t cc[kDenseB];
   V vv[kDenseB];
-  int32_t item = 0;
-  int64_t off = 0, end = 0;
+  ChunkDesc d{};
   const int32_t* col = cl.col0;
   const V* val = (const V*)cl.val0;
   if (ci < n) {
-    item = items[ci];
-    off = cl.off[item];
-    end = off + cl.cnt[item];
-    const bool b1 = cl.buf[item] != 0;
-    col = b1 ? cl.col1 : cl.col0;
-    val = (const V*)(b1 ? cl.val1 : cl.val0);
-    dense_load_batch(col, val, off + threadIdx.x, end, cc, vv);
+    d = desc[ci];
+    col = d.buf ? cl.col1 : cl.col0;
+    val = (const V*)(d.buf ? cl.val1 : cl.val0);
+    dense_load_batch(col, val, d.off + threadIdx.x, d.off + d.cnt, cc, vv);
   }
   __syncthreads();
   while (ci < n) {
-    // Where the chunk goes, read before any later load is issued.
-    const int64_t hr = cl.row[item];
-    const int64_t sidx = hr * cl.nreq + cl.slot[item];
-    const int64_t base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
-    const int32_t want = cl.slotNnz[sidx];
-    const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+    const int64_t off = d.off, end = d.off + d.cnt, base = d.base;
+    const int32_t want = d.want, colBase = d.colBase;
+    // The next chunk's descriptor, in flight during this chunk.
+    const int64_t cn = ci + gridDim.x;
+    if (cn < n) d = desc[cn];
     dense_add_batch(vals, bm, cc, vv);
     for (int64_t e0 = off + threadIdx.x + (int64_t)kDenseNT * kDenseB; e0 < end;
          e0 += (int64_t)kDenseNT * kDenseB) {
@@ -227,15 +221,10 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
     }
     __syncthreads();
     // First batch of the next chunk, in flight during the write-out.
-    const int64_t cn = ci + gridDim.x;
     if (cn < n) {
-      item = items[cn];
-      off = cl.off[item];
-      end = off + cl.cnt[item];
-      const bool b1 = cl.buf[item] != 0;
-      col = b1 ? cl.col1 : cl.col0;
-      val = (const V*)(b1 ? cl.val1 : cl.val0);
-      dense_load_batch(col, val, off + threadIdx.x, end, cc, vv);
+      col = d.buf ? cl.col1 : cl.col0;
+      val = (const V*)(d.buf ? cl.val1 : cl.val0);
+      dense_load_batch(col, val, d.off + threadIdx.x, d.off + d.cnt, cc, vv);
     }
     // Write-out in column order.  Wave w owns columns [w*W/16, (w+1)*W/16),
     // lane l a run of cpl of them; a wave scan of the lanes' popcounts gives
@@ -301,6 +290,24 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const int32_t* __restric
     __syncthreads();
     ci = cn;
   }
+}
+
+__global__ __launch_bounds__(kNT) void k_chunk_desc(int64_t n, const int32_t* __restrict__ order,
+                                                    ChunkList cl, const int64_t* __restrict__ cRowOff,
+                                                    ChunkDesc* __restrict__ desc) {
+  const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (i >= n) return;
+  const int32_t item = order[i];
+  const int64_t hr = cl.row[item];
+  const int64_t sidx = hr * cl.nreq + cl.slot[item];
+  ChunkDesc d;
+  d.off = cl.off[item];
+  d.base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
+  d.cnt = cl.cnt[item];
+  d.want = cl.slotNnz[sidx];
+  d.colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+  d.buf = cl.buf[item];
+  desc[i] = d;
 }
 
 // One wave per heavy row: exclusive scan of its slot counts.
@@ -378,20 +385,26 @@ size_t dense_num_lds(bool f64, int64_t W) {
   return (size_t)W * (f64 ? 8 : 4) + (size_t)((W + 31) / 32) * 4 + (kDenseNT / kWave) * 4;
 }
 
-void launch_dense_num(bool f64, const int32_t* items, int64_t n, const ChunkList& cl,
-                      const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
-                      int numCUs, hipStream_t s) {
+void launch_chunk_desc(int64_t n, const int32_t* order, const ChunkList& cl,
+                       const int64_t* cRowOff, ChunkDesc* desc, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_chunk_desc, dim3(grid_for(n, kNT)), dim3(kNT), 0, s, n, order, cl, cRowOff,
+                     desc);
+}
+
+void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
+                      int32_t* ccol, void* cval, int32_t* err, int numCUs, hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = dense_num_lds(f64, cl.W);
   // As many work groups as fit on the device at once (LDS of a CU: 160 KiB).
   const int64_t perCU = std::max<int64_t>(1, (int64_t)163840 / (int64_t)lds);
   const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1) * perCU);
   if (f64)
-    hipLaunchKernelGGL(k_dense_num<double>, dim3(g), dim3(kDenseNT), lds, s, items, n, cl, cRowOff,
-                       ccol, (double*)cval, err);
+    hipLaunchKernelGGL(k_dense_num<double>, dim3(g), dim3(kDenseNT), lds, s, desc, n, cl, ccol,
+                       (double*)cval, err);
   else
-    hipLaunchKernelGGL(k_dense_num<float>, dim3(g), dim3(kDenseNT), lds, s, items, n, cl, cRowOff,
-                       ccol, (float*)cval, err);
+    hipLaunchKernelGGL(k_dense_num<float>, dim3(g), dim3(kDenseNT), lds, s, desc, n, cl, ccol,
+                       (float*)cval, err);
 }
 
 void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,

@@ -324,10 +324,9 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
 }
 
 template <int TPR, int RPB, int E, typename V>
-__global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restrict__ items,
+__global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, int32_t spt,
                                                          ChunkList cl,
-                                                         const int64_t* __restrict__ cRowOff,
                                                          int32_t* __restrict__ ccol,
                                                          V* __restrict__ cval,
                                                          int32_t* __restrict__ err) {
@@ -344,12 +343,12 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restri
   }
   __syncthreads();
   const int64_t ri = (int64_t)blockIdx.x * RPB + g;
-  int32_t item = 0;
+  ChunkDesc d{};
   if (ri < n) {
-    item = items[ri];
-    const int64_t off = cl.off[item];
-    const int64_t end = off + cl.cnt[item];
-    const bool b1 = cl.buf[item] != 0;
+    d = desc[ri];
+    const int64_t off = d.off;
+    const int64_t end = off + d.cnt;
+    const bool b1 = d.buf != 0;
     const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
     const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
     for (int64_t e = off + t; e < end; e += TPR) hmap_add(keys, vals, (uint32_t)T, col[e], val[e], err);
@@ -360,13 +359,11 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const int32_t* __restri
   V vv[E];
   sort_to_regs<TPR, E, V>(keys, vals, kk, vv);
   if (ri < n) {
-    const int64_t hr = cl.row[item];
-    const int64_t sidx = hr * cl.nreq + cl.slot[item];
-    const int64_t base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
-    const int32_t want = cl.slotNnz[sidx];
+    const int64_t base = d.base;
+    const int32_t want = d.want;
     if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
     const int32_t lim = want < total ? want : total;
-    const int32_t colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+    const int32_t colBase = d.colBase;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int r = t * E + e;
@@ -501,22 +498,22 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
   (void)flag_unsupported;  // make_bins rejects bins without an instance
 }
 
-void launch_num_chunks(const BinCfg& b, bool f64, const int32_t* items, int64_t n,
-                       const ChunkList& cl, const int64_t* cRowOff, int32_t* ccol, void* cval,
-                       int32_t* err, hipStream_t s) {
+void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
+                       const ChunkList& cl, int32_t* ccol, void* cval, int32_t* err,
+                       hipStream_t s) {
   if (n <= 0) return;
   bool flag_unsupported = false;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
   if (f64) {
 #define L(TPR, RPB, E)                                                                         \
   hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
-                     items, n, b.T, b.spt, cl, cRowOff, ccol, (double*)cval, err)
+                     desc, n, b.T, b.spt, cl, ccol, (double*)cval, err)
     SG_DISPATCH_NUM(b, L);
 #undef L
   } else {
 #define L(TPR, RPB, E)                                                                        \
   hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
-                     items, n, b.T, b.spt, cl, cRowOff, ccol, (float*)cval, err)
+                     desc, n, b.T, b.spt, cl, ccol, (float*)cval, err)
     SG_DISPATCH_NUM(b, L);
 #undef L
   }
