@@ -783,7 +783,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     launch_expand_entries(f64, hb, xb, p->dAnnz + hb0, p->arp, p->acol, p->aval, p->brp, eB, nbE,
                           eVal, s);
     launch_scan_i64(nbE, nE, eOff, tmp, s);
-    src = ExpandSrc{nullptr, eOff, eB, eVal, p->bcol, vals ? p->bval : nullptr, nE};
+    src = ExpandSrc{eOff, eB, eVal, p->bcol, vals ? p->bval : nullptr, nE};
     ph_end(p, phCsc, s);
   } else {
   // Masked CSR -> CSC of A restricted to the batch's heavy rows.
@@ -858,19 +858,21 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     // First row (and, fed from A and B, first entry) of every work group.
     const int64_t nBlk = (E + blockElems - 1) / blockElems;
     int32_t* blkRow = alloc_n<int32_t>(p, nBlk, s);
+    int32_t* blkEnt = nullptr;
+    TileInfo* info = alloc_n<TileInfo>(p, nBlk, s);
     launch_block_starts(R, rowPtr, blockElems, nBlk, blkRow, s);
     if (p->fused && l == 0) {
-      int32_t* blkEnt = alloc_n<int32_t>(p, nBlk, s);
+      blkEnt = alloc_n<int32_t>(p, nBlk, s);
       launch_block_starts(src.nE, src.eOff, blockElems, nBlk, blkEnt, s);
-      src.blkEnt = blkEnt;
     }
+    launch_tile_info(E, blockElems, rowPtr, R, blkRow, blkEnt, src.nE, info, s);
     const int phH = ph_begin(p, SPGEMM_PH_HISTOGRAM, s);
     if (p->CH)
       launch_level_counts(Q, v, (int32_t)(w / W), (int32_t)p->nreq, inRow, inSlot,
                           p->CH + hb0 * p->nreq, counts, s);
     else
-      launch_histogram(E, blockElems, rowPtr, R, blkRow, B->bufCol[cur], shift, v, maxRows,
-                       counts, p->errWord, s);
+      launch_histogram(E, blockElems, rowPtr, info, B->bufCol[cur], shift, v, maxRows, counts,
+                       p->errWord, s);
     ph_end(p, phH, s);
     launch_partition(Q, counts, p->tau, last, v, inRow, inSlot, (int32_t)(w / W), inv, newCnt,
                      newRow, newSlot, ctr, s);
@@ -879,7 +881,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     const int out = 1 - cur;
     const bool direct = p->fused && l == 0;
     const int phM = ph_begin(p, direct ? SPGEMM_PH_EXPAND_SPLIT : SPGEMM_PH_MULTISPLIT, s);
-    launch_multisplit(f64, E, blockElems, rowPtr, R, blkRow, direct ? nullptr : B->bufCol[cur],
+    launch_multisplit(f64, E, blockElems, rowPtr, info, direct ? nullptr : B->bufCol[cur],
                       direct ? nullptr : B->bufVal[cur], direct ? &src : nullptr, shift, v,
                       (int32_t)(w - 1), maxRows, inv, cur64, B->bufCol[out], B->bufVal[out],
                       p->errWord, s);

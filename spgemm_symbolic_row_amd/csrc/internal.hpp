@@ -87,6 +87,13 @@ struct ChunkDesc {
   int32_t buf;      // buffer holding the elements (0 or 1)
 };
 
+// What a multisplit work group needs to know about its tile of elements.
+struct TileInfo {
+  int32_t r0, nrows;  // first row meeting the tile, rows meeting it
+  int32_t t0, t1;     // first entry, bound on the last (fed from A and B)
+  int64_t bnd0;       // first row boundary inside the tile (nrows > 1)
+};
+
 // ---- k_util.hip ----
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s);
@@ -158,8 +165,13 @@ void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int*
 // first row (or entry) of each multisplit work group.
 void launch_block_starts(int64_t nItems, const int64_t* off, int64_t G, int64_t nBlocks,
                          int32_t* out, hipStream_t s);
-void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
-                      const int32_t* blkRow, const int32_t* col, int shift, int v, int maxRows,
+// info[b] for the tiles of blockElems elements (blkRow/blkEnt from
+// launch_block_starts; blkEnt may be null).
+void launch_tile_info(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
+                      const int32_t* blkRow, const int32_t* blkEnt, int64_t nE, TileInfo* info,
+                      hipStream_t s);
+void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr,
+                      const TileInfo* info, const int32_t* col, int shift, int v, int maxRows,
                       int32_t* counts, int32_t* err, hipStream_t s);
 // Runs of equal W-wide chunk in B's rows (chunk = col >> shift): runPtr[K+1],
 // runChunk/runStart[runs + 1]; flags[nnzB] and runIdx[nnzB + 1] are scratch.
@@ -182,7 +194,6 @@ void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, 
 // A entries in row order, with the first product of each (eOff, nE + 1
 // entries), its B row start and its A value.
 struct ExpandSrc {
-  const int32_t* blkEnt;  // entry of each work group's first element
   const int64_t* eOff;
   const int32_t* eB;
   const void* eVal;
@@ -193,7 +204,7 @@ struct ExpandSrc {
 // One multisplit level.  inCol/inVal: the level's input, or src (not null)
 // to make the elements from A and B.  outVal null: columns only.
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
-                       int64_t R, const int32_t* blkRow, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
+                       const TileInfo* info, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
                        int shift, int v, int32_t wmask, int maxRows, const int32_t* inv,
                        int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
                        hipStream_t s);

@@ -29,28 +29,47 @@ __device__ __forceinline__ int bits_for(int n) {
   return b;
 }
 
-// Rows of the range [e0, e1) of block b: its first row r0 = blkRow[b] and
-// the row boundaries inside the range (rowPtr[r0+1 .. r0+nrows-1]) into bnd.
-// Rows are never empty (each holds more than tau elements), so the row of
-// the last element is the next block's first row, or the one before it when
-// that row starts exactly at e1.  Returns nrows, or -1 when more than
-// maxRows rows meet the range.
-__device__ __forceinline__ int range_rows(const int64_t* __restrict__ rowPtr, int64_t R,
-                                          const int32_t* __restrict__ blkRow, int64_t tile,
-                                          int64_t nTiles, int64_t e0, int64_t e1, int maxRows,
-                                          int64_t* bnd, int64_t* s_r0, int32_t* s_nrows) {
-  if (threadIdx.x == 0) {
-    const int64_t r0 = blkRow[tile];
-    int64_t r1 = (tile + 1 < nTiles) ? blkRow[tile + 1] : R - 1;
-    if (r1 > r0 && rowPtr[r1] >= e1) r1 -= 1;
-    *s_r0 = r0;
-    *s_nrows = (int32_t)(r1 - r0 + 1);
-  }
+// Rows of tile b's range [e0, e1): its first row and row count, and the
+// first row boundary inside the range, precomputed (k_tile_info); further
+// boundaries (only when tau is small next to the tile) are read here.
+// Returns nrows, or -1 when more than maxRows rows meet the range.
+__device__ __forceinline__ int range_rows(const int64_t* __restrict__ rowPtr,
+                                          const TileInfo* __restrict__ info, int64_t tile,
+                                          int maxRows, int64_t* bnd, TileInfo* s_info) {
+  if (threadIdx.x == 0) *s_info = info[tile];
   __syncthreads();
-  const int nrows = *s_nrows;
+  const int nrows = s_info->nrows;
   if (nrows > maxRows) return -1;
-  for (int i = threadIdx.x; i < nrows - 1; i += kNT) bnd[i] = rowPtr[*s_r0 + 1 + i];
+  if (nrows > 1) {
+    if (threadIdx.x == 0) bnd[0] = s_info->bnd0;
+    for (int i = 1 + threadIdx.x; i < nrows - 1; i += kNT) bnd[i] = rowPtr[s_info->r0 + 1 + i];
+  }
   return nrows;
+}
+
+// Per tile of G elements: first row, row count (rows are never empty, each
+// holds more than tau elements, so the row of the tile's last element is
+// the next tile's first row, or the one before it when that row starts
+// exactly at the next tile), the first boundary inside the tile, and with
+// blkEnt the first entry and a bound on the last.
+__global__ __launch_bounds__(kNT) void k_tile_info(int64_t nTiles, int64_t E, int64_t G,
+                                                   const int64_t* __restrict__ rowPtr, int64_t R,
+                                                   const int32_t* __restrict__ blkRow,
+                                                   const int32_t* __restrict__ blkEnt, int64_t nE,
+                                                   TileInfo* __restrict__ out) {
+  const int64_t b = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (b >= nTiles) return;
+  const int64_t e1 = (b + 1) * G < E ? (b + 1) * G : E;
+  const int64_t r0 = blkRow[b];
+  int64_t r1 = (b + 1 < nTiles) ? blkRow[b + 1] : R - 1;
+  if (r1 > r0 && rowPtr[r1] >= e1) r1 -= 1;
+  TileInfo t;
+  t.r0 = (int32_t)r0;
+  t.nrows = (int32_t)(r1 - r0 + 1);
+  t.t0 = blkEnt ? blkEnt[b] : 0;
+  t.t1 = blkEnt ? ((b + 1 < nTiles) ? blkEnt[b + 1] : (int32_t)(nE - 1)) : 0;
+  t.bnd0 = r1 > r0 ? rowPtr[r0 + 1] : 0;
+  out[b] = t;
 }
 
 // out[b] = the item whose range [off[t], off[t+1]) holds element b * G, for
@@ -82,20 +101,18 @@ __device__ __forceinline__ int local_row(const int64_t* bnd, int nrows, int64_t 
 
 // Histogram: per (input row, chunk) element counts into counts[r*v + c].
 __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems,
-                                                   const int64_t* __restrict__ rowPtr, int64_t R,
-                                                   const int32_t* __restrict__ blkRow,
+                                                   const int64_t* __restrict__ rowPtr,
+                                                   const TileInfo* __restrict__ info,
                                                    const int32_t* __restrict__ col, int shift, int v,
                                                    int maxRows, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ err) {
   __shared__ int32_t hist[kMsNBMax];
   __shared__ int64_t bnd[kMsRowsMax];
-  __shared__ int64_t s_r0;
-  __shared__ int32_t s_nrows;
+  __shared__ TileInfo s_info;
   const int64_t e0 = (int64_t)blockIdx.x * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
-  const int nrows = range_rows(rowPtr, R, blkRow, blockIdx.x, gridDim.x, e0, e1, maxRows, bnd,
-                               &s_r0, &s_nrows);
+  const int nrows = range_rows(rowPtr, info, blockIdx.x, maxRows, bnd, &s_info);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
@@ -124,7 +141,7 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
     }
   }
   __syncthreads();
-  const int64_t r0 = s_r0;
+  const int64_t r0 = s_info.r0;
   for (int i = threadIdx.x; i < NB; i += kNT) {
     const int32_t c = hist[i];
     if (c) {
@@ -145,8 +162,8 @@ __global__ __launch_bounds__(kNT) void k_histogram(int64_t E, int32_t blockElems
 // src.eOff[t].  This is the first level fed straight from the expansion.
 template <int ITEMS, typename V, bool kVals, bool kExpand>
 __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElems,
-                                                    const int64_t* __restrict__ rowPtr, int64_t R,
-                                                    const int32_t* __restrict__ blkRow,
+                                                    const int64_t* __restrict__ rowPtr,
+                                                    const TileInfo* __restrict__ info,
                                                     const int32_t* __restrict__ inCol,
                                                     const V* __restrict__ inVal, ExpandSrc src,
                                                     int shift, int v,
@@ -169,8 +186,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   int32_t* loff = hist + NBcap;
   uint16_t* bktBuf = (uint16_t*)(loff + NBcap);
   __shared__ int32_t wtot[kNT / kWave];
-  __shared__ int64_t s_r0, s_t0, s_t1;
-  __shared__ int32_t s_nrows;
+  __shared__ TileInfo s_info;
   // Work groups are dealt round-robin to the XCDs; each XCD gets a
   // contiguous run of tiles instead, so that neighbouring heavy rows, which
   // share B rows, are expanded under the same L2.  The grid is padded to a
@@ -181,16 +197,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   const int64_t e0 = tile * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
-  if constexpr (kExpand) {
-    // The entry of the tile's first element, and a bound on the entry of
-    // its last (range_rows below synchronises before they are read).
-    if (threadIdx.x == kWave) {
-      s_t0 = src.blkEnt[tile];
-      s_t1 = (tile + 1 < nTiles) ? src.blkEnt[tile + 1] : src.nE - 1;
-    }
-  }
-  const int nrows = range_rows(rowPtr, R, blkRow, tile, nTiles, e0, e1, maxRows, bnd, &s_r0,
-                               &s_nrows);
+  const int nrows = range_rows(rowPtr, info, tile, maxRows, bnd, &s_info);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     // without products), then a prefix maximum carries it forward.  colBuf
     // holds these until the permute.
     int32_t* ent = colBuf;
-    const int32_t t0 = (int32_t)s_t0, t1 = (int32_t)s_t1;
+    const int32_t t0 = s_info.t0, t1 = s_info.t1;
     for (int i = threadIdx.x; i < n; i += kNT) ent[i] = (i == 0) ? t0 : -1;
     __syncthreads();
     for (int32_t t = t0 + 1 + (int32_t)threadIdx.x; t <= t1; t += kNT) {
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   // Reserve each bucket's run in its chunk.  The atomics' results are only
   // needed by the final write, so they stay in registers while the LDS
   // permute runs and their latency overlaps it.
-  const int64_t r0 = s_r0;
+  const int64_t r0 = s_info.r0;
   constexpr int kBPT = kMsNBMax / kNT;  // buckets per thread
   unsigned long long gres[kBPT];
 #pragma unroll
@@ -373,16 +380,26 @@ void launch_block_starts(int64_t nItems, const int64_t* off, int64_t G, int64_t 
   hipLaunchKernelGGL(k_block_starts, dim3(g), dim3(kNT), 0, s, nItems, off, G, nBlocks, out);
 }
 
-void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
-                      const int32_t* blkRow, const int32_t* col, int shift, int v, int maxRows,
+void launch_tile_info(int64_t E, int32_t blockElems, const int64_t* rowPtr, int64_t R,
+                      const int32_t* blkRow, const int32_t* blkEnt, int64_t nE, TileInfo* info,
+                      hipStream_t s) {
+  if (E <= 0) return;
+  const int64_t nTiles = (E + blockElems - 1) / blockElems;
+  hipLaunchKernelGGL(k_tile_info, dim3(grid_for(nTiles, kNT)), dim3(kNT), 0, s, nTiles, E,
+                     (int64_t)blockElems, rowPtr, R, blkRow, blkEnt, nE, info);
+}
+
+void launch_histogram(int64_t E, int32_t blockElems, const int64_t* rowPtr,
+                      const TileInfo* info, const int32_t* col, int shift, int v, int maxRows,
                       int32_t* counts, int32_t* err, hipStream_t s) {
   if (E <= 0) return;
   hipLaunchKernelGGL(k_histogram, dim3(grid_for(E, blockElems)), dim3(kNT), 0, s, E, blockElems,
-                     rowPtr, R, blkRow, col, shift, v, maxRows, counts, err);
+                     rowPtr, info, col, shift, v, maxRows, counts, err);
 }
 
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
-                       int64_t R, const int32_t* blkRow, const int32_t* inCol, const void* inVal, const ExpandSrc* src,
+                       const TileInfo* info, const int32_t* inCol, const void* inVal,
+                       const ExpandSrc* src,
                        int shift, int v, int32_t wmask, int maxRows, const int32_t* inv,
                        int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
                        hipStream_t s) {
@@ -395,7 +412,7 @@ void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* r
   const ExpandSrc& x = src ? *src : none;
 #define SG_MS(ITEMS, V, VALS, EXP)                                                              \
   hipLaunchKernelGGL((k_multisplit<ITEMS, V, VALS, EXP>), dim3(g), dim3(kNT), lds, s, E,        \
-                     blockElems, rowPtr, R, blkRow, inCol, (const V*)inVal, x, shift, v, wmask, \
+                     blockElems, rowPtr, info, inCol, (const V*)inVal, x, shift, v, wmask,     \
                      maxRows,                                                                    \
                      inv, cursor, outCol, (V*)outVal, err)
   // Columns only: the geometry of the fp32 instance.
