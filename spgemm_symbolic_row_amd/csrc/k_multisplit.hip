@@ -197,6 +197,11 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   const int64_t e0 = tile * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
+  if constexpr (kExpand) {
+    // Entry marks of the elements (below), cleared before the tile
+    // descriptor is read.
+    for (int i = threadIdx.x; i < n; i += kNT) colBuf[i] = -1;
+  }
   const int nrows = range_rows(rowPtr, info, tile, maxRows, bnd, &s_info);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
@@ -213,8 +218,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
     // holds these until the permute.
     int32_t* ent = colBuf;
     const int32_t t0 = s_info.t0, t1 = s_info.t1;
-    for (int i = threadIdx.x; i < n; i += kNT) ent[i] = (i == 0) ? t0 : -1;
-    __syncthreads();
+    if (threadIdx.x == 0) ent[0] = t0;
     for (int32_t t = t0 + 1 + (int32_t)threadIdx.x; t <= t1; t += kNT) {
       const int64_t pos = src.eOff[t] - e0;
       if (pos < n) atomicMax(&ent[(int)pos], t);
@@ -267,11 +271,17 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
       bb[it] = (uint32_t)(local_row(bnd, nrows, e) * v + (cc[it] >> shift));
     }
   }
+  // Count the buckets and rank every element inside its bucket at once: one
+  // lane per (wave, bucket) adds the group's size and gets its base back.
+  int32_t rank[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const bool act = it * kNT + (int)threadIdx.x < n;
     const uint64_t m = match_key(bb[it], nbits, act);
-    if (act && lane_id() == ffs64(m)) atomicAdd(&hist[bb[it]], __popcll(m));
+    const int leader = act ? ffs64(m) : lane_id();
+    int32_t base = 0;
+    if (act && lane_id() == leader) base = atomicAdd(&hist[bb[it]], __popcll(m));
+    rank[it] = __shfl(base, leader) + __popcll(m & lanemask_lt());
   }
   __syncthreads();
 
@@ -314,20 +324,11 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
       }
     }
   }
-  __syncthreads();
-  for (int b = threadIdx.x; b < NB; b += kNT) hist[b] = loff[b];
-  __syncthreads();
-
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const bool act = it * kNT + (int)threadIdx.x < n;
-    const uint64_t m = match_key(bb[it], nbits, act);
-    const int leader = act ? ffs64(m) : lane_id();
-    int32_t base = 0;
-    if (act && lane_id() == leader) base = atomicAdd(&hist[bb[it]], __popcll(m));
-    base = __shfl(base, leader);
     if (act) {
-      const int pos = base + __popcll(m & lanemask_lt());
+      const int pos = loff[bb[it]] + rank[it];
       colBuf[pos] = cc[it] & wmask;
       if constexpr (kVals) valBuf[pos] = xv[it];
       bktBuf[pos] = (uint16_t)bb[it];
