@@ -971,10 +971,12 @@ bool num_bitmap(spgemm_plan_t p, int b) {
 void symbolic_batch(spgemm_plan_t p, const Batch& B) {
   hipStream_t s = p->sh;
   const ChunkList cl = chunk_list(p, B);
+  ChunkDesc* desc = alloc_n<ChunkDesc>(p, B.nfc, s);
+  launch_chunk_desc(B.nfc, B.fcOrder, cl, nullptr, desc, s);
   const int ph = ph_begin(p, SPGEMM_PH_SYM_CHUNK_HASH, s);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t a = B.fcBinStart[b], e = B.fcBinStart[b + 1];
-    if (!sym_bitmap(p, b)) launch_sym_chunks(p->symBins[b], B.fcOrder + a, e - a, cl, p->errWord, s);
+    if (!sym_bitmap(p, b)) launch_sym_chunks(p->symBins[b], desc + a, e - a, cl, p->errWord, s);
   }
   ph_end(p, ph, s);
   const int phD = ph_begin(p, SPGEMM_PH_SYM_CHUNK_DENSE, s);
@@ -982,14 +984,14 @@ void symbolic_batch(spgemm_plan_t p, const Batch& B) {
     const int64_t a = B.fcBinStart[b], e = B.fcBinStart[b + 1];
     const int64_t cap = p->symBins[b].cap;
     if (sym_bitmap(p, b))
-      launch_sym_chunks_bitmap(cap <= 256 ? 0 : cap <= 4096 ? 1 : 2, B.fcOrder + a, e - a,
+      launch_sym_chunks_bitmap(cap <= 256 ? 0 : cap <= 4096 ? 1 : 2, desc + a, e - a,
                                p->chunkWords, cl, s);
   }
   const int64_t a = B.fcBinStart[p->NS], e = B.fcBinStart[p->NS + 1];
   if (p->chunkWords)
-    launch_sym_chunks_bitmap(2, B.fcOrder + a, e - a, p->chunkWords, cl, s);
+    launch_sym_chunks_bitmap(2, desc + a, e - a, p->chunkWords, cl, s);
   else
-    launch_dense_sym(B.fcOrder + a, e - a, cl, p->errWord, s);
+    launch_dense_sym(desc + a, e - a, cl, p->errWord, s);
   ph_end(p, phD, s);
   check_launch("chunk symbolic");
 }

@@ -132,7 +132,7 @@ void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const 
 void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
                      const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
                      int32_t* err, hipStream_t s);
-void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const ChunkList& cl,
+void launch_sym_chunks(const BinCfg& b, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
                        int32_t* err, hipStream_t s);
 // Whether a numeric bin's (tpr, sort size) has a kernel instance.
 bool num_bin_supported(const BinCfg& b);
@@ -230,11 +230,12 @@ void launch_final_from_rows(int64_t h, const int64_t* rowPtr, int64_t* fcOff, in
 void launch_chunk_bins(int64_t nfc, const int32_t* fcCnt, int64_t lastFirst, int64_t tau,
                        const int32_t* caps, int nbins, int denseBin, uint8_t* key,
                        int64_t* denseElems, hipStream_t s);
-void launch_dense_sym(const int32_t* items, int64_t n, const ChunkList& cl, int32_t* err,
+void launch_dense_sym(const ChunkDesc* desc, int64_t n, const ChunkList& cl, int32_t* err,
                       hipStream_t s);
 void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
                       int32_t* ccol, void* cval, int32_t* err, int numCUs, hipStream_t s);
-// desc[i] for the chunk order[i], i < n.
+// desc[i] for the chunk order[i], i < n; with cRowOff null (symbolic) base
+// is the chunk's slot index and want is 0.
 void launch_chunk_desc(int64_t n, const int32_t* order, const ChunkList& cl,
                        const int64_t* cRowOff, ChunkDesc* desc, hipStream_t s);
 size_t dense_num_lds(bool f64, int64_t W);
@@ -247,7 +248,7 @@ void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* 
 void chunks_set_attributes();
 size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb);
 // sizeClass 0: chunks of <= 256 elements (4 per work group), 1: <= 4096, 2: larger.
-void launch_sym_chunks_bitmap(int sizeClass, const int32_t* items, int64_t n, int32_t words,
+void launch_sym_chunks_bitmap(int sizeClass, const ChunkDesc* desc, int64_t n, int32_t words,
                               const ChunkList& cl, hipStream_t s);
 void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
                             int32_t words, const ChunkList& cl, int32_t* ccol, void* cval,

@@ -17,7 +17,7 @@ namespace sg {
 namespace {
 
 template <int TPC, int CPB>
-__global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const int32_t* __restrict__ items,
+__global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const ChunkDesc* __restrict__ desc,
                                                                 int64_t n, int32_t words,
                                                                 ChunkList cl) {
   extern __shared__ __align__(16) uint32_t bmAll[];
@@ -27,11 +27,11 @@ __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const int32_t* _
   for (int i = t; i < words; i += TPC) bm[i] = 0;
   __syncthreads();
   const int64_t ci = (int64_t)blockIdx.x * CPB + g;
-  int32_t item = 0;
+  ChunkDesc d{};
   if (ci < n) {
-    item = items[ci];
-    const int64_t off = cl.off[item], end = off + cl.cnt[item];
-    const int32_t* __restrict__ col = cl.buf[item] ? cl.col1 : cl.col0;
+    d = desc[ci];
+    const int64_t off = d.off, end = off + d.cnt;
+    const int32_t* __restrict__ col = d.buf ? cl.col1 : cl.col0;
     constexpr int kB = 8;  // loads in flight per thread
     for (int64_t e0 = off + t; e0 < end; e0 += (int64_t)TPC * kB) {
       int32_t cc[kB];
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const int32_t* _
   if (t == 0 && ci < n) {
     int32_t tot = 0;
     for (int i = 0; i < TPC / kWave; ++i) tot += gsum[g * (TPC / kWave) + i];
-    cl.slotNnz[(int64_t)cl.row[item] * cl.nreq + cl.slot[item]] = tot;
+    cl.slotNnz[d.base] = tot;
   }
 }
 
@@ -205,18 +205,18 @@ size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb) {
   return (size_t)rpb * (f64 ? rank_group_bytes<double>(T, words) : rank_group_bytes<float>(T, words));
 }
 
-void launch_sym_chunks_bitmap(int sizeClass, const int32_t* items, int64_t n, int32_t words,
+void launch_sym_chunks_bitmap(int sizeClass, const ChunkDesc* desc, int64_t n, int32_t words,
                               const ChunkList& cl, hipStream_t s) {
   if (n <= 0) return;
   if (sizeClass == 0) {
     hipLaunchKernelGGL((k_sym_chunks_bitmap<64, 4>), dim3((unsigned)((n + 3) / 4)), dim3(256),
-                       (size_t)4 * words * 4, s, items, n, words, cl);
+                       (size_t)4 * words * 4, s, desc, n, words, cl);
   } else if (sizeClass == 1) {
     hipLaunchKernelGGL((k_sym_chunks_bitmap<256, 1>), dim3((unsigned)n), dim3(256),
-                       (size_t)words * 4, s, items, n, words, cl);
+                       (size_t)words * 4, s, desc, n, words, cl);
   } else {
     hipLaunchKernelGGL((k_sym_chunks_bitmap<1024, 1>), dim3((unsigned)n), dim3(1024),
-                       (size_t)words * 4, s, items, n, words, cl);
+                       (size_t)words * 4, s, desc, n, words, cl);
   }
 }
 

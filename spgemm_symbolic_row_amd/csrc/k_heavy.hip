@@ -113,16 +113,16 @@ __global__ __launch_bounds__(kNT) void k_chunk_bins(int64_t nfc, const int32_t* 
 // ------------------------------------------------- dense LDS accumulators
 // Symbolic: a W-bit LDS bitmap per chunk (read before or-ing, so repeated
 // columns cost a read only), then a popcount.
-__global__ __launch_bounds__(kNT) void k_dense_sym(const int32_t* __restrict__ items, ChunkList cl,
+__global__ __launch_bounds__(kNT) void k_dense_sym(const ChunkDesc* __restrict__ desc, ChunkList cl,
                                                    int32_t* __restrict__ err) {
   extern __shared__ __align__(16) uint32_t bm[];
   __shared__ int32_t wsum[kNT / kWave];
   const int nwords = (int)((cl.W + 31) / 32);
-  const int32_t item = items[blockIdx.x];
+  const ChunkDesc d = desc[blockIdx.x];
   for (int i = threadIdx.x; i < nwords; i += kNT) bm[i] = 0;
   __syncthreads();
-  const int64_t off = cl.off[item], end = off + cl.cnt[item];
-  const int32_t* __restrict__ col = cl.buf[item] ? cl.col1 : cl.col0;
+  const int64_t off = d.off, end = off + d.cnt;
+  const int32_t* __restrict__ col = d.buf ? cl.col1 : cl.col0;
   for (int64_t e = off + threadIdx.x; e < end; e += kNT) {
     const int32_t c = col[e];
     const uint32_t bit = 1u << (c & 31);
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const int32_t* __restrict__ i
   if (threadIdx.x == 0) {
     int32_t t = 0;
     for (int i = 0; i < kNT / kWave; ++i) t += wsum[i];
-    cl.slotNnz[(int64_t)cl.row[item] * cl.nreq + cl.slot[item]] = t;
+    cl.slotNnz[d.base] = t;
   }
   (void)err;
 }
@@ -302,9 +302,10 @@ __global__ __launch_bounds__(kNT) void k_chunk_desc(int64_t n, const int32_t* __
   const int64_t sidx = hr * cl.nreq + cl.slot[item];
   ChunkDesc d;
   d.off = cl.off[item];
-  d.base = cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx];
+  // Without C's row offsets (symbolic), base is the chunk's slot index.
+  d.base = cRowOff ? cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx] : sidx;
   d.cnt = cl.cnt[item];
-  d.want = cl.slotNnz[sidx];
+  d.want = cRowOff ? cl.slotNnz[sidx] : 0;
   d.colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
   d.buf = cl.buf[item];
   desc[i] = d;
@@ -374,11 +375,11 @@ void launch_chunk_bins(int64_t nfc, const int32_t* fcCnt, int64_t lastFirst, int
                      lastFirst, tau, caps, nbins, denseBin, key, denseElems);
 }
 
-void launch_dense_sym(const int32_t* items, int64_t n, const ChunkList& cl, int32_t* err,
+void launch_dense_sym(const ChunkDesc* desc, int64_t n, const ChunkList& cl, int32_t* err,
                       hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = (size_t)((cl.W + 31) / 32) * 4;
-  hipLaunchKernelGGL(k_dense_sym, dim3((unsigned)n), dim3(kNT), lds, s, items, cl, err);
+  hipLaunchKernelGGL(k_dense_sym, dim3((unsigned)n), dim3(kNT), lds, s, desc, cl, err);
 }
 
 size_t dense_num_lds(bool f64, int64_t W) {

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows(const int32_t* __restrict
 }
 
 template <int TPR, int RPB>
-__global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const int32_t* __restrict__ items,
+__global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, ChunkList cl,
                                                          int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -115,19 +115,19 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const int32_t* __restri
   __syncthreads();
   const int64_t ri = (int64_t)blockIdx.x * RPB + g;
   int32_t mine = 0;
-  int32_t item = 0;
+  ChunkDesc d{};
   if (ri < n) {
-    item = items[ri];
-    const int64_t off = cl.off[item];
-    const int64_t end = off + cl.cnt[item];
-    const int32_t* __restrict__ col = cl.buf[item] ? cl.col1 : cl.col0;
+    d = desc[ri];
+    const int64_t off = d.off;
+    const int64_t end = off + d.cnt;
+    const int32_t* __restrict__ col = d.buf ? cl.col1 : cl.col0;
     for (int64_t e = off + t; e < end; e += TPR)
       if (hset_insert(keys, (uint32_t)T, col[e], err)) ++mine;
   }
   const int32_t ws = wave_sum(mine);
   if (lane_id() == 0 && ri < n) atomicAdd(&gcount[g], ws);
   __syncthreads();
-  if (t == 0 && ri < n) cl.slotNnz[(int64_t)cl.row[item] * cl.nreq + cl.slot[item]] = gcount[g];
+  if (t == 0 && ri < n) cl.slotNnz[d.base] = gcount[g];
 }
 
 // ----------------------------------------------------------------- numeric
@@ -437,12 +437,12 @@ void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const 
 #undef L
 }
 
-void launch_sym_chunks(const BinCfg& b, const int32_t* items, int64_t n, const ChunkList& cl,
+void launch_sym_chunks(const BinCfg& b, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
                        int32_t* err, hipStream_t s) {
   if (n <= 0) return;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
-#define L(TPR, RPB)                                                                          \
-  hipLaunchKernelGGL((k_sym_chunks<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, items, n, \
+#define L(TPR, RPB)                                                                         \
+  hipLaunchKernelGGL((k_sym_chunks<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, desc, n, \
                      b.T, cl, err)
   SG_DISPATCH_TPR(b, L)
 #undef L
