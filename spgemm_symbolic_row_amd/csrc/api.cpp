@@ -600,8 +600,9 @@ void do_plan(spgemm_plan_t p) {
   p->binStart = alloc_n<int32_t>(p, 65, s);
   launch_fill_i64(p->cnt, 0, m, s);
   const int ph = ph_begin(p, SPGEMM_PH_ROW_INFO, s);
+  int64_t* part = alloc_n<int64_t>(p, row_info_partials(m), s);
   launch_row_info(m, p->arp, p->acol, p->brp, p->bcol, p->rowTau, p->dSymCaps, p->NS, p->rowP,
-                  p->scanA, p->rowBin, p->stats, s);
+                  p->scanA, p->rowBin, part, p->stats, s);
   const int nkeys = p->NS + 2;  // 0 empty, 1..NS hash bins, NS+1 heavy
   launch_bin_sort(p->rowBin, m, nkeys, p->binCnt, p->binFill, p->binStart, p->rowOrder, s);
   ph_end(p, ph, s);

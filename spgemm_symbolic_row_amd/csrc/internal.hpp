@@ -107,10 +107,12 @@ void launch_scan_i32(const int32_t* in, int64_t n, int64_t* out, int64_t* tmp, h
 // cnt/fill: nbins int32 scratch; start: nbins+1 int32 (bin offsets).
 void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int32_t* fill,
                      int32_t* start, int32_t* out, hipStream_t s);
+// Scratch entries (int64) launch_row_info needs for its per-work-group partials.
+int64_t row_info_partials(int64_t m);
 void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
                      const int32_t* bcol, int64_t tau, const int32_t* caps, int nbins,
-                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* stats,
-                     hipStream_t s);
+                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* part,
+                     int64_t* stats, hipStream_t s);
 void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
                      const int32_t* col, int32_t* err, hipStream_t s);
 void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hipStream_t s);

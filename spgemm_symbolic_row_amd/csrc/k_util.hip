@@ -187,8 +187,9 @@ __global__ __launch_bounds__(kNT) void k_bin_scatter(const uint8_t* __restrict__
 // product index where that entry's scaled B row starts).  The row total is
 // P_i; its bin is 0 when P_i == 0, 1 + (first cap >= P_i) when P_i <= tau,
 // and nbins + 1 (heavy) otherwise.
-// A grid-stride loop over rows keeps the number of work groups (and so of
-// same-address global atomics for the totals, one set per work group) small.
+// The totals are reduced per work group in LDS and written as one partial
+// per work group (part[blockIdx.x * 8 + i]); k_row_stats folds them, so no
+// two work groups update the same global address.
 template <int G>
 __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __restrict__ arp,
                                                   const int32_t* __restrict__ acol,
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
                                                   int64_t* __restrict__ rowP,
                                                   int32_t* __restrict__ scanA,
                                                   uint8_t* __restrict__ rowBin,
-                                                  int64_t* __restrict__ stats) {
+                                                  int64_t* __restrict__ part) {
   __shared__ unsigned long long sP, sPh, sAh, sMax, sH, sL;
   if (threadIdx.x == 0) sP = sPh = sAh = sMax = sH = sL = 0;
   __syncthreads();
@@ -245,12 +246,44 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    atomicAdd((unsigned long long*)&stats[kStatProducts], sP);
-    atomicAdd((unsigned long long*)&stats[kStatHeavyProducts], sPh);
-    atomicAdd((unsigned long long*)&stats[kStatHeavyANnz], sAh);
-    atomicMax((unsigned long long*)&stats[kStatMaxRowProducts], sMax);
-    atomicAdd((unsigned long long*)&stats[kStatHeavyRows], sH);
-    atomicAdd((unsigned long long*)&stats[kStatLightRows], sL);
+    int64_t* q = part + (int64_t)blockIdx.x * 8;
+    q[kStatProducts] = (int64_t)sP;
+    q[kStatHeavyProducts] = (int64_t)sPh;
+    q[kStatHeavyANnz] = (int64_t)sAh;
+    q[kStatMaxRowProducts] = (int64_t)sMax;
+    q[kStatHeavyRows] = (int64_t)sH;
+    q[kStatLightRows] = (int64_t)sL;
+  }
+}
+
+// One work group folds the nb partials of k_row_info into stats (added to
+// what stats holds; the maximum is taken).
+__global__ __launch_bounds__(kNT) void k_row_stats(int64_t nb, const int64_t* __restrict__ part,
+                                                   int64_t* __restrict__ stats) {
+  __shared__ int64_t red[kNT / kWave];
+  const int ids[6] = {kStatProducts, kStatHeavyProducts, kStatHeavyANnz, kStatMaxRowProducts,
+                      kStatHeavyRows, kStatLightRows};
+  for (int q = 0; q < 6; ++q) {
+    const int id = ids[q];
+    const bool isMax = id == kStatMaxRowProducts;
+    int64_t x = 0;
+    for (int64_t b = threadIdx.x; b < nb; b += kNT) {
+      const int64_t y = part[b * 8 + id];
+      x = isMax ? (y > x ? y : x) : x + y;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const int64_t y = __shfl_xor(x, d);
+      x = isMax ? (y > x ? y : x) : x + y;
+    }
+    if (lane_id() == 0) red[threadIdx.x / kWave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int64_t t = stats[id];
+      for (int w = 0; w < kNT / kWave; ++w) t = isMax ? (red[w] > t ? red[w] : t) : t + red[w];
+      stats[id] = t;
+    }
+    __syncthreads();
   }
 }
 
@@ -368,16 +401,22 @@ void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int
   }
 }
 
+int64_t row_info_partials(int64_t m) {
+  const int64_t g = (m * 16 + kNT - 1) / kNT;
+  return (g < 1 ? 1 : (g > 65535 ? 65535 : g)) * 8;
+}
+
 void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
                      const int32_t* /*bcol*/, int64_t tau, const int32_t* caps, int nbins,
-                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* stats,
-                     hipStream_t s) {
+                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* part,
+                     int64_t* stats, hipStream_t s) {
   if (m <= 0) return;
   constexpr int G = 16;
   unsigned g = grid_for(m * G, kNT);
   if (g > 65535) g = 65535;
   hipLaunchKernelGGL(k_row_info<G>, dim3(g), dim3(kNT), 0, s, m, arp, acol, brp, tau, caps, nbins,
-                     rowP, scanA, rowBin, stats);
+                     rowP, scanA, rowBin, part);
+  hipLaunchKernelGGL(k_row_stats, dim3(1), dim3(kNT), 0, s, (int64_t)g, part, stats);
 }
 
 void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
