@@ -49,6 +49,8 @@ def algorithmic_bytes(st, phase, sv, si=4):
         return st["level_elems"][0] * cv, f"{cv} B written per heavy product (first-level chunks)"
     if phase == "outer_product":
         return st["heavy_products"] * cv, f"{cv} B written per heavy product"
+    if phase == "expand_final":
+        return st["heavy_products"] * cv, f"{cv} B written per heavy product (final chunks)"
     if phase == "multisplit":
         return E * 2 * cv, f"{2 * cv} B (read + write) per element per level"
     if phase == "histogram":
@@ -149,6 +151,9 @@ def main():
     ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
+    ap.add_argument("--expansion", type=int, default=-1,
+                    help="heavy-row expansion: 0 one-pass run scatter, 1 outer product + "
+                         "multisplit, 2 first level fed from A and B (default: the library's)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -189,6 +194,8 @@ def main():
         opts["lds_budget"] = args.lds_budget
     if args.heavy_threshold:
         opts["heavy_threshold"] = args.heavy_threshold
+    if args.expansion >= 0:
+        opts["expansion"] = args.expansion
     if args.config == "rmat20":
         opts["rowptr64"] = 1   # nnz(C) is about 9.7e9
     mcl = args.config == "mcl1m"
@@ -226,8 +233,8 @@ def main():
 
     roof = None
     if not args.no_profile:
-        cands = [k for k in ("multisplit", "expand_split", "outer_product", "num_chunk_dense",
-                             "histogram")
+        cands = [k for k in ("multisplit", "expand_split", "outer_product", "expand_final",
+                             "num_chunk_dense", "histogram")
                  if phase_tot.get(k, 0) > 0]
         if cands:
             kern = max(cands, key=lambda k: phase_tot[k])

@@ -93,13 +93,21 @@ typedef struct spgemm_options {
   spgemm_alloc_fn alloc;        /* optional allocator (see above)               */
   spgemm_free_fn free;
   void *alloc_ctx;
-  int32_t outer_product_expansion; /* 1: expand the heavy rows as the gMAGNUS
-                                   page prints it (masked CSC, outer product
-                                   into C-hat, then every multisplit level);
-                                   0: feed the first multisplit level straight
-                                   from A and B, row by row, so C-hat in row
-                                   order is never written (default, when the
-                                   counts come from the structure)            */
+  int32_t expansion;            /* how the heavy rows' products reach their
+                                   final chunks (the chunk tree, C and the
+                                   parameters are the same in every mode):
+                                   0 (default): one pass; every product
+                                     is made from A and B row by row and
+                                     written straight to its final chunk
+                                     (needs the chunk counts from the
+                                     structure and n_req <= 4096, else
+                                     mode 2);
+                                   1: as the gMAGNUS page prints it: masked
+                                     CSC, outer product into C-hat, then one
+                                     multisplit pass per level;
+                                   2: the first multisplit level made from A
+                                     and B row by row (C-hat never written),
+                                     later levels as in mode 1              */
   int32_t heavy_row_threshold;  /* rows with more intermediate products than
                                    this take the heavy path; 0 = the
                                    heavy_threshold option if set, else
@@ -139,7 +147,8 @@ typedef enum spgemm_phase {
   SPGEMM_PH_NUM_CHUNK_DENSE = 11,/* heavy-chunk dense LDS numeric               */
   SPGEMM_PH_CHUNK_HIST = 12,     /* per-row W-wide chunk counts from structure  */
   SPGEMM_PH_EXPAND_SPLIT = 13,   /* first multisplit level fed from A and B     */
-  SPGEMM_PH_COUNT = 14
+  SPGEMM_PH_EXPAND_FINAL = 14,   /* products made and written to final chunks   */
+  SPGEMM_PH_COUNT = 15
 } spgemm_phase;
 
 typedef struct spgemm_stats {

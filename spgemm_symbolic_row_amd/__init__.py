@@ -34,7 +34,7 @@ class Options(ctypes.Structure):
         ("mem_budget", c_i64), ("max_chunks_per_level", c_i32), ("rowptr64", c_i32),
         ("validate", c_i32), ("single_stream", c_i32), ("profile", c_i32),
         ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
-        ("alloc_ctx", c_vp), ("outer_product_expansion", c_i32), ("heavy_row_threshold", c_i32),
+        ("alloc_ctx", c_vp), ("expansion", c_i32), ("heavy_row_threshold", c_i32),
         ("reserved", c_i64 * 7),
     ]
 
@@ -79,7 +79,7 @@ class Stats(ctypes.Structure):
 
 PHASES = ["row_info", "sym_light", "csc", "outer_product", "histogram", "multisplit",
           "sym_chunk_hash", "sym_chunk_dense", "rowptr", "num_light", "num_chunk_hash",
-          "num_chunk_dense", "chunk_hist", "expand_split"]
+          "num_chunk_dense", "chunk_hist", "expand_split", "expand_final"]
 
 
 SPGEMM_F32, SPGEMM_F64 = 0, 1

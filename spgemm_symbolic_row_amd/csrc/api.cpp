@@ -218,6 +218,7 @@ struct Batch {
   int64_t* fcOff = nullptr;
   int32_t *fcCnt = nullptr, *fcRow = nullptr, *fcSlot = nullptr, *fcOrder = nullptr;
   int8_t* fcBuf = nullptr;
+  int8_t* fcSpan = nullptr;  // log2 of the W-wide slots each chunk covers
   std::vector<int32_t> fcBinStart;
   int64_t levelElems[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 };
@@ -271,6 +272,7 @@ struct spgemm_plan_s {
   int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
   int64_t* dAnnz = nullptr; // scan of the heavy rows' A lengths (h + 1)
   bool fused = false;    // the first level is fed straight from A and B
+  bool direct = false;   // one pass straight into the final chunks
   int32_t* slotNnz = nullptr;
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
@@ -639,7 +641,7 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // level reads; fed straight from A and B, one level needs only its output.
 int heavy_nbuf(spgemm_plan_t p) {
   const int L = p->params.levels;
-  if (L == 0) return 1;
+  if (L == 0 || p->direct) return 1;
   return (p->fused && L == 1) ? 1 : 2;
 }
 size_t heavy_buf_bytes(spgemm_plan_t p, int64_t Pb, bool vals) {
@@ -693,10 +695,17 @@ void heavy_prepare(spgemm_plan_t p) {
     budget = std::max<int64_t>(avail * 45 / 100, (int64_t)1 << 30);
   }
   // Chunk counts come from the structure unless asked otherwise or too wide
-  // for LDS; with them the first level can be fed straight from A and B.
+  // for LDS.  With them the whole chunk tree is known before any element
+  // moves: the elements go straight to their final chunks when one work
+  // group's (row, chunk) buckets fit its LDS, else the first level is fed
+  // straight from A and B.
   const bool structCounts =
       p->params.levels > 0 && !p->opts.histogram_from_data && p->nreq <= 8192;
-  p->fused = structCounts && !p->opts.outer_product_expansion;
+  int32_t xfElems = 0;
+  int xfRows = 0;
+  const bool xfFits = expand_final_geometry(p->f64, p->rowTau, p->nreq, &xfElems, &xfRows);
+  p->direct = structCounts && p->opts.expansion == 0 && xfFits;
+  p->fused = structCounts && !p->direct && p->opts.expansion != 1;
   const int64_t nbuf = heavy_nbuf(p);
   // Numeric needs columns and values.  If that takes one batch, symbolic
   // expands with values and numeric reuses the result; otherwise symbolic
@@ -774,7 +783,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     }
   }
   ExpandSrc src{};
-  if (p->fused) {
+  if (p->fused || p->direct) {
     // The heavy rows' A entries in row order with their product offsets:
     // the first multisplit level makes its elements from these.
     int32_t* eB = alloc_n<int32_t>(p, nE, s);
@@ -823,14 +832,16 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     int64_t first, n;
     const int64_t* newOff;
     const int32_t *newCnt, *newRow, *newSlot;
-    int8_t buf;
+    int8_t buf, spanLog2;
   };
   std::vector<Piece> pieces;
   bool completed = (L == 0);
   int64_t R = hb, E = Pb;
   const int64_t* rowPtr = chatRowPtr;
   const int32_t *inRow = nullptr, *inSlot = nullptr;
-  int cur = p->fused ? 1 : 0;  // buffer the level reads (none when fed from A and B)
+  // Buffer the level reads (none when fed from A and B; with the direct
+  // expansion the levels only shape the chunk tree).
+  int cur = p->fused ? 1 : 0;
   for (int l = 0; l < L; ++l) {
     B->levelElems[l] = E;
     const int v = p->params.v_chunks[l];
@@ -851,22 +862,25 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     if (!p->CH) launch_fill_i32(counts, 0, Q, s);
     launch_fill_i32(newCnt, 0, Q, s);
     launch_fill_i32(ctr, 0, 2, s);
-    int32_t blockElems;
-    int maxRows;
-    // Rows of the first level are heavy rows (more than rowTau elements),
-    // of later levels heavy chunks (more than tau).
-    multisplit_geometry(f64 && vals, l == 0 ? p->rowTau : p->tau, v, &blockElems, &maxRows);
-    // First row (and, fed from A and B, first entry) of every work group.
-    const int64_t nBlk = (E + blockElems - 1) / blockElems;
-    int32_t* blkRow = alloc_n<int32_t>(p, nBlk, s);
-    int32_t* blkEnt = nullptr;
-    TileInfo* info = alloc_n<TileInfo>(p, nBlk, s);
-    launch_block_starts(R, rowPtr, blockElems, nBlk, blkRow, s);
-    if (p->fused && l == 0) {
-      blkEnt = alloc_n<int32_t>(p, nBlk, s);
-      launch_block_starts(src.nE, src.eOff, blockElems, nBlk, blkEnt, s);
+    int32_t blockElems = 0;
+    int maxRows = 0;
+    TileInfo* info = nullptr;
+    if (!p->direct) {
+      // Rows of the first level are heavy rows (more than rowTau elements),
+      // of later levels heavy chunks (more than tau).
+      multisplit_geometry(f64 && vals, l == 0 ? p->rowTau : p->tau, v, &blockElems, &maxRows);
+      // First row (and, fed from A and B, first entry) of every work group.
+      const int64_t nBlk = (E + blockElems - 1) / blockElems;
+      int32_t* blkRow = alloc_n<int32_t>(p, nBlk, s);
+      int32_t* blkEnt = nullptr;
+      info = alloc_n<TileInfo>(p, nBlk, s);
+      launch_block_starts(R, rowPtr, blockElems, nBlk, blkRow, s);
+      if (p->fused && l == 0) {
+        blkEnt = alloc_n<int32_t>(p, nBlk, s);
+        launch_block_starts(src.nE, src.eOff, blockElems, nBlk, blkEnt, s);
+      }
+      launch_tile_info(E, blockElems, rowPtr, R, blkRow, blkEnt, src.nE, info, s);
     }
-    launch_tile_info(E, blockElems, rowPtr, R, blkRow, blkEnt, src.nE, info, s);
     const int phH = ph_begin(p, SPGEMM_PH_HISTOGRAM, s);
     if (p->CH)
       launch_level_counts(Q, v, (int32_t)(w / W), (int32_t)p->nreq, inRow, inSlot,
@@ -879,14 +893,16 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
                      newRow, newSlot, ctr, s);
     launch_scan_i32(newCnt, Q, newOff, ltmp, s);
     launch_copy_i64(cur64, newOff, Q, s);
-    const int out = 1 - cur;
-    const bool direct = p->fused && l == 0;
-    const int phM = ph_begin(p, direct ? SPGEMM_PH_EXPAND_SPLIT : SPGEMM_PH_MULTISPLIT, s);
-    launch_multisplit(f64, E, blockElems, rowPtr, info, direct ? nullptr : B->bufCol[cur],
-                      direct ? nullptr : B->bufVal[cur], direct ? &src : nullptr, shift, v,
-                      (int32_t)(w - 1), maxRows, inv, cur64, B->bufCol[out], B->bufVal[out],
-                      p->errWord, s);
-    ph_end(p, phM, s);
+    const int out = p->direct ? 0 : 1 - cur;
+    if (!p->direct) {
+      const bool direct = p->fused && l == 0;
+      const int phM = ph_begin(p, direct ? SPGEMM_PH_EXPAND_SPLIT : SPGEMM_PH_MULTISPLIT, s);
+      launch_multisplit(f64, E, blockElems, rowPtr, info, direct ? nullptr : B->bufCol[cur],
+                        direct ? nullptr : B->bufVal[cur], direct ? &src : nullptr, shift, v,
+                        (int32_t)(w - 1), maxRows, inv, cur64, B->bufCol[out], B->bufVal[out],
+                        p->errWord, s);
+      ph_end(p, phM, s);
+    }
     check_launch("multisplit level");
     HIP_CHECK(hipMemcpyAsync(p->hBins + 100, ctr, 8, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
@@ -897,7 +913,8 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
       HIP_CHECK(hipStreamSynchronize(s));
       nextE = p->hStats[16];
     }
-    pieces.push_back(Piece{Q - nL, nL, newOff, newCnt, newRow, newSlot, (int8_t)out});
+    pieces.push_back(Piece{Q - nL, nL, newOff, newCnt, newRow, newSlot, (int8_t)out,
+                           (int8_t)log2_exact(w / W)});
     if (last) completed = true;
     if (nH == 0) break;
     R = nH;
@@ -919,17 +936,54 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
   B->fcRow = alloc_n<int32_t>(p, nfc, s);
   B->fcSlot = alloc_n<int32_t>(p, nfc, s);
   B->fcBuf = alloc_n<int8_t>(p, nfc, s);
+  B->fcSpan = alloc_n<int8_t>(p, nfc, s);
   if (L == 0) {
-    launch_final_from_rows(hb, chatRowPtr, B->fcOff, B->fcCnt, B->fcRow, B->fcSlot, B->fcBuf, s);
+    launch_final_from_rows(hb, chatRowPtr, B->fcOff, B->fcCnt, B->fcRow, B->fcSlot, B->fcBuf,
+                           B->fcSpan, s);
     B->lastFirst = 0;
   } else {
     int64_t dst = 0;
     for (auto& pc : pieces) {
       launch_final_from_level(pc.first, pc.n, pc.newOff, pc.newCnt, pc.newRow, pc.newSlot, pc.buf,
-                              dst, B->fcOff, B->fcCnt, B->fcRow, B->fcSlot, B->fcBuf, s);
+                              pc.spanLog2, dst, B->fcOff, B->fcCnt, B->fcRow, B->fcSlot,
+                              B->fcBuf, B->fcSpan, s);
       dst += pc.n;
     }
     B->lastFirst = completed ? nfc - pieces.back().n : nfc;
+  }
+  if (p->direct) {
+    // Final chunks back to back in buffer 0, in list order; every product
+    // goes straight to the final chunk covering its column.
+    const int phX = ph_begin(p, SPGEMM_PH_EXPAND_FINAL, s);
+    int64_t* fcOff = alloc_n<int64_t>(p, nfc + 1, s);
+    int64_t* ftmp = alloc_n<int64_t>(p, scan_tmp_elems(nfc) + 1, s);
+    launch_scan_i32(B->fcCnt, nfc, fcOff, ftmp, s);
+    B->fcOff = fcOff;
+    launch_fill_i8(B->fcBuf, 0, nfc, s);
+    const int64_t nslot = hb * p->nreq;
+    int32_t* finalOf = alloc_n<int32_t>(p, nslot, s);
+    int8_t* spanOf = alloc_n<int8_t>(p, nslot, s);
+    launch_fill_i32(finalOf, -1, nslot, s);
+    launch_fill_i8(spanOf, 0, nslot, s);
+    launch_final_map(nfc, B->fcRow, B->fcSlot, B->fcSpan, p->nreq, finalOf, spanOf, s);
+    int64_t* fcCursor = alloc_n<int64_t>(p, nfc, s);
+    launch_copy_i64(fcCursor, fcOff, nfc, s);
+    int32_t blockElems = 0;
+    int maxRows = 0;
+    if (!expand_final_geometry(f64 && vals, p->rowTau, p->nreq, &blockElems, &maxRows))
+      throw Error{SPGEMM_ERR_INTERNAL, "direct expansion geometry"};
+    const int64_t nBlk = (Pb + blockElems - 1) / blockElems;
+    int32_t* blkRow = alloc_n<int32_t>(p, nBlk, s);
+    int32_t* blkEnt = alloc_n<int32_t>(p, nBlk, s);
+    TileInfo* info = alloc_n<TileInfo>(p, nBlk, s);
+    launch_block_starts(hb, chatRowPtr, blockElems, nBlk, blkRow, s);
+    launch_block_starts(src.nE, src.eOff, blockElems, nBlk, blkEnt, s);
+    launch_tile_info(Pb, blockElems, chatRowPtr, hb, blkRow, blkEnt, src.nE, info, s);
+    launch_expand_final(f64, Pb, blockElems, chatRowPtr, info, src, finalOf, spanOf,
+                        (int32_t)p->nreq, log2_exact(W), maxRows, fcCursor, B->bufCol[0],
+                        vals ? B->bufVal[0] : nullptr, p->errWord, s);
+    ph_end(p, phX, s);
+    check_launch("direct expansion");
   }
   // Numeric bins: W-wide chunks with more than W/8 elements (or tau, if
   // smaller) go to the dense accumulator, at that density zeroing and

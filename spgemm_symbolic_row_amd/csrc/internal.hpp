@@ -97,6 +97,7 @@ struct TileInfo {
 // ---- k_util.hip ----
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s);
+void launch_fill_i8(int8_t* p, int8_t v, int64_t n, hipStream_t s);
 void launch_copy_i64(int64_t* dst, const int64_t* src, int64_t n, hipStream_t s);
 // out[i] = sum_{j<i} in[j] for i in [0, n]; out has n+1 entries.  tmp needs
 // scan_tmp_elems(n) int64 entries.
@@ -184,6 +185,12 @@ void launch_b_runs(int64_t K, int64_t nnzB, const int32_t* brp, const int32_t* b
 void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,
                             const int32_t* acol, const int32_t* runPtr, const int32_t* runChunk,
                             const int32_t* runStart, int32_t nreq, int32_t* CH, hipStream_t s);
+// finalOf[row * nreq + slot] = the final chunk covering W-wide slot `slot`
+// of batch row `row`, spanOf[...] = that chunk's width as log2 of W-wide
+// slots (slots of no chunk are left as they are).
+void launch_final_map(int64_t nfc, const int32_t* fcRow, const int32_t* fcSlot,
+                      const int8_t* fcSpan, int64_t nreq, int32_t* finalOf, int8_t* spanOf,
+                      hipStream_t s);
 // One level's (row, chunk) counts as sums of `span` W-wide counts.
 void launch_level_counts(int64_t Q, int v, int32_t span, int32_t nreq, const int32_t* inRow,
                          const int32_t* inSlot, const int32_t* CH, int32_t* counts,
@@ -203,6 +210,16 @@ struct ExpandSrc {
   const void* bval;
   int64_t nE;
 };
+// Heavy-row expansion straight into the final chunks (chunk tree known from
+// the structure): tile geometry, false when (rows per tile) x nreq buckets
+// cannot fit.
+bool expand_final_geometry(bool f64, int64_t rowTau, int64_t nreq, int32_t* blockElems,
+                           int* maxRows);
+void launch_expand_final(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
+                         const TileInfo* info, const ExpandSrc& src, const int32_t* finalOf,
+                         const int8_t* spanOf, int32_t nreq, int log2W, int maxRows,
+                         int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
+                         hipStream_t s);
 // One multisplit level.  inCol/inVal: the level's input, or src (not null)
 // to make the elements from A and B.  outVal null: columns only.
 void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
@@ -221,11 +238,12 @@ void launch_expand_entries(bool f64, int64_t hb, const int32_t* rows, const int6
 // or, when there is no multisplit, from the heavy rows themselves.
 void launch_final_from_level(int64_t first, int64_t n, const int64_t* newOff,
                              const int32_t* newCnt, const int32_t* newRow,
-                             const int32_t* newSlot, int8_t buf, int64_t dst0, int64_t* fcOff,
-                             int32_t* fcCnt, int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf,
-                             hipStream_t s);
+                             const int32_t* newSlot, int8_t buf, int8_t spanLog2, int64_t dst0,
+                             int64_t* fcOff, int32_t* fcCnt, int32_t* fcRow, int32_t* fcSlot,
+                             int8_t* fcBuf, int8_t* fcSpan, hipStream_t s);
 void launch_final_from_rows(int64_t h, const int64_t* rowPtr, int64_t* fcOff, int32_t* fcCnt,
-                            int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf, hipStream_t s);
+                            int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf, int8_t* fcSpan,
+                            hipStream_t s);
 // Bin of each final chunk: dense when it is W wide (list positions
 // >= lastFirst hold the W-wide chunks) and has more than tau elements, else
 // the hash bin of its element count.

@@ -61,12 +61,14 @@ __global__ __launch_bounds__(kNT) void k_final_from_level(int64_t first, int64_t
                                                           const int32_t* __restrict__ newCnt,
                                                           const int32_t* __restrict__ newRow,
                                                           const int32_t* __restrict__ newSlot,
-                                                          int8_t buf, int64_t dst0,
+                                                          int8_t buf, int8_t spanLog2,
+                                                          int64_t dst0,
                                                           int64_t* __restrict__ fcOff,
                                                           int32_t* __restrict__ fcCnt,
                                                           int32_t* __restrict__ fcRow,
                                                           int32_t* __restrict__ fcSlot,
-                                                          int8_t* __restrict__ fcBuf) {
+                                                          int8_t* __restrict__ fcBuf,
+                                                          int8_t* __restrict__ fcSpan) {
   const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
   if (i >= n) return;
   const int64_t pos = first + i, d = dst0 + i;
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(kNT) void k_final_from_level(int64_t first, int64_t
   fcRow[d] = newRow[pos];
   fcSlot[d] = newSlot[pos];
   fcBuf[d] = buf;
+  fcSpan[d] = spanLog2;
 }
 
 __global__ __launch_bounds__(kNT) void k_final_from_rows(int64_t h, const int64_t* __restrict__ rowPtr,
@@ -82,7 +85,8 @@ __global__ __launch_bounds__(kNT) void k_final_from_rows(int64_t h, const int64_
                                                          int32_t* __restrict__ fcCnt,
                                                          int32_t* __restrict__ fcRow,
                                                          int32_t* __restrict__ fcSlot,
-                                                         int8_t* __restrict__ fcBuf) {
+                                                         int8_t* __restrict__ fcBuf,
+                                                         int8_t* __restrict__ fcSpan) {
   const int64_t r = (int64_t)blockIdx.x * kNT + threadIdx.x;
   if (r >= h) return;
   fcOff[r] = rowPtr[r];
@@ -90,6 +94,7 @@ __global__ __launch_bounds__(kNT) void k_final_from_rows(int64_t h, const int64_
   fcRow[r] = (int32_t)r;
   fcSlot[r] = 0;
   fcBuf[r] = 0;
+  fcSpan[r] = 0;
 }
 
 __global__ __launch_bounds__(kNT) void k_chunk_bins(int64_t nfc, const int32_t* __restrict__ fcCnt,
@@ -330,6 +335,22 @@ __global__ __launch_bounds__(kNT) void k_slot_scan(int64_t h, int64_t nreq,
   if (lane_id() == 0) cnt[xheavy[r]] = carry;
 }
 
+// finalOf / spanOf over the W-wide slots of every final chunk.
+__global__ __launch_bounds__(kNT) void k_final_map(int64_t nfc, const int32_t* __restrict__ fcRow,
+                                                   const int32_t* __restrict__ fcSlot,
+                                                   const int8_t* __restrict__ fcSpan, int64_t nreq,
+                                                   int32_t* __restrict__ finalOf,
+                                                   int8_t* __restrict__ spanOf) {
+  const int64_t c = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (c >= nfc) return;
+  const int64_t q = (int64_t)fcRow[c] * nreq + fcSlot[c];
+  const int8_t sp = fcSpan[c];
+  for (int s = 0; s < (1 << sp); ++s) {
+    finalOf[q + s] = (int32_t)c;
+    spanOf[q + s] = sp;
+  }
+}
+
 }  // namespace
 
 void heavy_set_attributes() {
@@ -350,21 +371,31 @@ void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, 
                      last ? 1 : 0, v, inRow, inSlot, slotStep, inv, newCnt, newRow, newSlot, ctr);
 }
 
+void launch_final_map(int64_t nfc, const int32_t* fcRow, const int32_t* fcSlot,
+                      const int8_t* fcSpan, int64_t nreq, int32_t* finalOf, int8_t* spanOf,
+                      hipStream_t s) {
+  if (nfc <= 0) return;
+  hipLaunchKernelGGL(k_final_map, dim3(grid_for(nfc, kNT)), dim3(kNT), 0, s, nfc, fcRow, fcSlot,
+                     fcSpan, nreq, finalOf, spanOf);
+}
+
 void launch_final_from_level(int64_t first, int64_t n, const int64_t* newOff,
                              const int32_t* newCnt, const int32_t* newRow,
-                             const int32_t* newSlot, int8_t buf, int64_t dst0, int64_t* fcOff,
-                             int32_t* fcCnt, int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf,
-                             hipStream_t s) {
+                             const int32_t* newSlot, int8_t buf, int8_t spanLog2, int64_t dst0,
+                             int64_t* fcOff, int32_t* fcCnt, int32_t* fcRow, int32_t* fcSlot,
+                             int8_t* fcBuf, int8_t* fcSpan, hipStream_t s) {
   if (n <= 0) return;
   hipLaunchKernelGGL(k_final_from_level, dim3(grid_for(n, kNT)), dim3(kNT), 0, s, first, n, newOff,
-                     newCnt, newRow, newSlot, buf, dst0, fcOff, fcCnt, fcRow, fcSlot, fcBuf);
+                     newCnt, newRow, newSlot, buf, spanLog2, dst0, fcOff, fcCnt, fcRow, fcSlot,
+                     fcBuf, fcSpan);
 }
 
 void launch_final_from_rows(int64_t h, const int64_t* rowPtr, int64_t* fcOff, int32_t* fcCnt,
-                            int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf, hipStream_t s) {
+                            int32_t* fcRow, int32_t* fcSlot, int8_t* fcBuf, int8_t* fcSpan,
+                            hipStream_t s) {
   if (h <= 0) return;
   hipLaunchKernelGGL(k_final_from_rows, dim3(grid_for(h, kNT)), dim3(kNT), 0, s, h, rowPtr, fcOff,
-                     fcCnt, fcRow, fcSlot, fcBuf);
+                     fcCnt, fcRow, fcSlot, fcBuf, fcSpan);
 }
 
 void launch_chunk_bins(int64_t nfc, const int32_t* fcCnt, int64_t lastFirst, int64_t tau,

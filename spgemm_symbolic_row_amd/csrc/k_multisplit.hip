@@ -22,6 +22,10 @@ constexpr int kMsNBMax = 1024;  // LDS buckets per work group
 constexpr int kMsRowsMax = 512;
 constexpr int kMsItemsF64 = 4;   // elements per thread held in registers
 constexpr int kMsItemsF32 = 8;
+// Straight into final chunks: no LDS staging, so larger tiles.
+constexpr int kXfItemsF64 = 8;
+constexpr int kXfItemsF32 = 16;
+constexpr int kXfNBMax = 8192;   // (row, chunk) buckets per work group
 
 __device__ __forceinline__ int bits_for(int n) {
   int b = 0;
@@ -97,6 +101,42 @@ __device__ __forceinline__ int local_row(const int64_t* bnd, int nrows, int64_t 
       hi = mid;
   }
   return lo;
+}
+
+// Entry of every element of the range [e0, e0 + n), as in a merge of the
+// elements with the entries' first products: each entry in [t0, t1] that
+// starts inside the range marks its start (the largest index wins, which
+// skips entries without products), then a prefix maximum carries it
+// forward.  ent[] must hold -1 on entry; t0 is the entry of element e0.
+__device__ __forceinline__ void entries_of_range(int32_t* ent, int n, int64_t e0, int32_t t0,
+                                                 int32_t t1, const int64_t* __restrict__ eOff,
+                                                 int32_t* wtot) {
+  if (threadIdx.x == 0) ent[0] = t0;
+  for (int32_t t = t0 + 1 + (int32_t)threadIdx.x; t <= t1; t += kNT) {
+    const int64_t pos = eOff[t] - e0;
+    if (pos < n) atomicMax(&ent[(int)pos], t);
+  }
+  __syncthreads();
+  const int cpt = (n + kNT - 1) / kNT;
+  const int i0 = threadIdx.x * cpt, i1 = (i0 + cpt < n) ? i0 + cpt : n;
+  int32_t run = -1;
+  for (int i = i0; i < i1; ++i) {
+    run = ent[i] > run ? ent[i] : run;
+    ent[i] = run;
+  }
+  int32_t x = run;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int32_t y = __shfl_up(x, d);
+    if (lane_id() >= d && y > x) x = y;
+  }
+  int32_t carry = __shfl_up(x, 1);
+  if (lane_id() == 0) carry = -1;
+  if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = x;
+  __syncthreads();
+  for (int w = 0; w < (int)threadIdx.x / kWave; ++w) carry = wtot[w] > carry ? wtot[w] : carry;
+  for (int i = i0; i < i1; ++i)
+    if (ent[i] < carry) ent[i] = carry;
 }
 
 // Histogram: per (input row, chunk) element counts into counts[r*v + c].
@@ -210,41 +250,7 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   const int NB = nrows * v;
   const int nbits = bits_for(NB);
   for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
-  if constexpr (kExpand) {
-    // Entry of every element of the range, as in a merge of the elements
-    // with the entries' first products: each entry that starts inside the
-    // range marks its start (the largest index wins, which skips entries
-    // without products), then a prefix maximum carries it forward.  colBuf
-    // holds these until the permute.
-    int32_t* ent = colBuf;
-    const int32_t t0 = s_info.t0, t1 = s_info.t1;
-    if (threadIdx.x == 0) ent[0] = t0;
-    for (int32_t t = t0 + 1 + (int32_t)threadIdx.x; t <= t1; t += kNT) {
-      const int64_t pos = src.eOff[t] - e0;
-      if (pos < n) atomicMax(&ent[(int)pos], t);
-    }
-    __syncthreads();
-    const int cpt = (n + kNT - 1) / kNT;
-    const int i0 = threadIdx.x * cpt, i1 = (i0 + cpt < n) ? i0 + cpt : n;
-    int32_t run = -1;
-    for (int i = i0; i < i1; ++i) {
-      run = ent[i] > run ? ent[i] : run;
-      ent[i] = run;
-    }
-    int32_t x = run;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int32_t y = __shfl_up(x, d);
-      if (lane_id() >= d && y > x) x = y;
-    }
-    int32_t carry = __shfl_up(x, 1);
-    if (lane_id() == 0) carry = -1;
-    if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = x;
-    __syncthreads();
-    for (int w = 0; w < (int)threadIdx.x / kWave; ++w) carry = wtot[w] > carry ? wtot[w] : carry;
-    for (int i = i0; i < i1; ++i)
-      if (ent[i] < carry) ent[i] = carry;
-  }
+  if constexpr (kExpand) entries_of_range(colBuf, n, e0, s_info.t0, s_info.t1, src.eOff, wtot);
   __syncthreads();
 
   int32_t cc[ITEMS];
@@ -348,6 +354,127 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
   }
 }
 
+
+// Expansion straight into the final chunks.  With every chunk count known
+// from the structure, the chunk tree of each heavy row is fixed before any
+// element moves, so the levels of the multisplit (§III-C) collapse into one
+// pass over the row-major product sequence: element e (made from A and B as
+// above) goes to the final chunk covering its column, finalOf[row * nreq +
+// slot] with slot = col >> log2W; spanOf holds that chunk's width as log2 of
+// W-wide slots.  A work group's buckets are (row inside the range, first
+// slot of the final chunk).  Consecutive elements that share a bucket (most
+// of a scaled B row's run inside one W-wide slot) are ranked together: the
+// first lane of each such group adds the group's size to the bucket's LDS
+// counter.  One global reservation per bucket, then every element is
+// written in place with its column made local to the chunk.
+template <int ITEMS, typename V, bool kVals>
+__global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockElems,
+                                                      const int64_t* __restrict__ rowPtr,
+                                                      const TileInfo* __restrict__ info,
+                                                      ExpandSrc src,
+                                                      const int32_t* __restrict__ finalOf,
+                                                      const int8_t* __restrict__ spanOf,
+                                                      int32_t nreq, int log2W, int maxRows,
+                                                      int64_t* __restrict__ cursor,
+                                                      int32_t* __restrict__ outCol,
+                                                      V* __restrict__ outVal,
+                                                      int32_t* __restrict__ err) {
+  // LDS (sized by the host): gbase[NB] i64 | bnd[maxRows] i64 |
+  // ent[blockElems] i32 | hist[NB] i32, NB = maxRows * nreq.
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int NBcap = maxRows * nreq;
+  int64_t* gbase = (int64_t*)smem;
+  int64_t* bnd = gbase + NBcap;
+  int32_t* ent = (int32_t*)(bnd + maxRows);
+  int32_t* hist = ent + blockElems;
+  __shared__ int32_t wtot[kNT / kWave];
+  __shared__ TileInfo s_info;
+  const int64_t nTiles = (E + blockElems - 1) / blockElems;
+  const int64_t tile = (int64_t)(blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+  if (tile >= nTiles) return;
+  const int64_t e0 = tile * blockElems;
+  const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
+  const int n = (int)(e1 - e0);
+  for (int i = threadIdx.x; i < n; i += kNT) ent[i] = -1;
+  const int nrows = range_rows(rowPtr, info, tile, maxRows, bnd, &s_info);
+  if (nrows < 0) {
+    if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
+    return;
+  }
+  const int NB = nrows * nreq;
+  for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
+  entries_of_range(ent, n, e0, s_info.t0, s_info.t1, src.eOff, wtot);
+  __syncthreads();
+
+  const int64_t r0 = s_info.r0;
+  const int32_t W = 1 << log2W;
+  int32_t cc[ITEMS];
+  V xv[ITEMS];
+  int32_t bb[ITEMS];
+  int32_t rank[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int idx = it * kNT + threadIdx.x;
+    const bool act = idx < n;
+    cc[it] = 0;
+    xv[it] = V(0);
+    bb[it] = -1;
+    if (act) {
+      const int64_t e = e0 + idx;
+      const int32_t t = ent[idx];
+      const int64_t bp = (int64_t)src.eB[t] + (e - src.eOff[t]);
+      const int32_t col = src.bcol[bp];
+      if constexpr (kVals) xv[it] = ((const V*)src.eVal)[t] * ((const V*)src.bval)[bp];
+      const int lr = local_row(bnd, nrows, e);
+      const int32_t slot = col >> log2W;
+      const int sp = spanOf[(r0 + lr) * nreq + slot];
+      cc[it] = col & ((W << sp) - 1);
+      bb[it] = lr * nreq + (slot & ~((1 << sp) - 1));
+    }
+  }
+  // Rank: groups of consecutive lanes with one bucket share one LDS atomic.
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const bool act = bb[it] >= 0;
+    const int32_t prev = __shfl_up(bb[it], 1);
+    const bool head = act && (lane_id() == 0 || prev != bb[it]);
+    const uint64_t heads = __ballot(head);
+    const uint64_t actm = __ballot(act);
+    const uint64_t le = lanemask_lt() | (1ull << lane_id());
+    const int h = last_set64(heads & le);
+    const uint64_t above = heads & ~le;
+    const int nxt = above ? ffs64(above) : 64 - __clzll((long long)actm);
+    int32_t base = 0;
+    if (head) base = atomicAdd(&hist[bb[it]], nxt - lane_id());
+    rank[it] = __shfl(base, act ? h : lane_id()) + (lane_id() - h);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < NB; b += kNT) {
+    const int32_t c = hist[b];
+    int64_t g = 0;
+    if (c) {
+      const int32_t q = finalOf[r0 * nreq + b];
+      if (q < 0) {
+        flag_error(err, kErrCountMismatch);
+      } else {
+        g = (int64_t)atomicAdd((unsigned long long*)&cursor[q], (unsigned long long)c);
+      }
+    }
+    gbase[b] = g;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    if (bb[it] >= 0) {
+      const int64_t dest = gbase[bb[it]] + rank[it];
+      if (dest < E) {
+        outCol[dest] = cc[it];
+        if constexpr (kVals) outVal[dest] = xv[it];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 void multisplit_set_attributes() {
@@ -360,6 +487,9 @@ void multisplit_set_attributes() {
   SG_ATTR(k_multisplit<kMsItemsF64, double, true, true>);
   SG_ATTR(k_multisplit<kMsItemsF32, float, true, true>);
   SG_ATTR(k_multisplit<kMsItemsF32, float, false, true>);
+  SG_ATTR(k_expand_final<kXfItemsF64, double, true>);
+  SG_ATTR(k_expand_final<kXfItemsF32, float, true>);
+  SG_ATTR(k_expand_final<kXfItemsF32, float, false>);
 #undef SG_ATTR
 }
 
@@ -371,6 +501,35 @@ void multisplit_geometry(bool f64, int64_t tau, int v, int32_t* blockElems, int*
   while (G > 64 && (rows_for(G) * v > kMsNBMax || rows_for(G) > kMsRowsMax)) G /= 2;
   *blockElems = (int32_t)G;
   *maxRows = (int)rows_for(G);
+}
+
+bool expand_final_geometry(bool f64, int64_t rowTau, int64_t nreq, int32_t* blockElems,
+                           int* maxRows) {
+  int64_t G = (int64_t)kNT * (f64 ? kXfItemsF64 : kXfItemsF32);
+  auto rows_for = [&](int64_t g) { return (g - 1) / (rowTau + 1) + 2; };
+  while (G > 64 && (rows_for(G) * nreq > kXfNBMax || rows_for(G) > kMsRowsMax)) G /= 2;
+  *blockElems = (int32_t)G;
+  *maxRows = (int)rows_for(G);
+  return rows_for(G) * nreq <= kXfNBMax && rows_for(G) <= kMsRowsMax;
+}
+
+void launch_expand_final(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
+                         const TileInfo* info, const ExpandSrc& src, const int32_t* finalOf,
+                         const int8_t* spanOf, int32_t nreq, int log2W, int maxRows,
+                         int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
+                         hipStream_t s) {
+  if (E <= 0) return;
+  const unsigned g = (grid_for(E, blockElems) + kXcds - 1) / kXcds * kXcds;
+  const size_t NB = (size_t)maxRows * nreq;
+  const size_t lds = NB * 12 + (size_t)maxRows * 8 + (size_t)blockElems * 4 + 16;
+#define SG_XF(ITEMS, V, VALS)                                                                  \
+  hipLaunchKernelGGL((k_expand_final<ITEMS, V, VALS>), dim3(g), dim3(kNT), lds, s, E, blockElems, \
+                     rowPtr, info, src, finalOf, spanOf, nreq, log2W, maxRows, cursor, outCol,  \
+                     (V*)outVal, err)
+  if (!outVal) SG_XF(kXfItemsF32, float, false);
+  else if (f64) SG_XF(kXfItemsF64, double, true);
+  else SG_XF(kXfItemsF32, float, true);
+#undef SG_XF
 }
 
 void launch_block_starts(int64_t nItems, const int64_t* off, int64_t G, int64_t nBlocks,

@@ -354,6 +354,12 @@ void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s) {
   if (g > 65536) g = 65536;
   hipLaunchKernelGGL(k_fill<int64_t>, dim3(g), dim3(kNT), 0, s, p, v, n);
 }
+void launch_fill_i8(int8_t* p, int8_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  unsigned g = grid_for(n, kNT * 4);
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(k_fill<int8_t>, dim3(g), dim3(kNT), 0, s, p, v, n);
+}
 void launch_copy_i64(int64_t* dst, const int64_t* src, int64_t n, hipStream_t s) {
   if (n <= 0) return;
   unsigned g = grid_for(n, kNT * 4);

@@ -220,24 +220,26 @@ def test_chunk_counts_from_structure_match_data_pass(W, nmax, budget):
 
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 @pytest.mark.parametrize("W,nmax,budget", [(256, 4, 0), (256, 32, 0), (128, 2, 0), (256, 4, 150_000)])
-def test_direct_first_level_matches_outer_product(W, nmax, budget, dtype):
-    # Feeding the first multisplit level straight from A and B (default) and
-    # expanding through the outer product into C-hat first must give the
-    # same chunk tree and the same C.
+def test_expansion_modes_agree(W, nmax, budget, dtype):
+    # The one-pass run scatter (default), the page's outer product followed by
+    # one multisplit pass per level, and the first level fed from A and B
+    # must give the same chunk tree and the same C.
     A = synth.rmat(12, 16, seed=17)
     A.val = np.round(A.val * 6 - 3).astype(dtype)
     opts = dict(heavy_threshold=40, dense_width=W, max_chunks_per_level=nmax, mem_budget=budget)
-    a = gpu_product(A, A, outer_product_expansion=1, profile=1, **opts)
-    b = gpu_product(A, A, profile=1, **opts)
-    assert a[3]["phase_windows"]["expand_split"] == 0 and a[3]["phase_windows"]["outer_product"] > 0
-    assert b[3]["phase_windows"]["expand_split"] > 0 and b[3]["phase_windows"]["outer_product"] == 0
-    for x, y in zip(a[:3], b[:3]):
-        np.testing.assert_array_equal(x, y)
-    for key in ("level_elems", "final_chunks", "dense_chunks"):
-        assert a[3][key] == b[3][key], key
+    runs = {m: gpu_product(A, A, expansion=m, profile=1, **opts) for m in (0, 1, 2)}
+    win = {m: r[3]["phase_windows"] for m, r in runs.items()}
+    assert win[0]["expand_final"] > 0 and win[0]["outer_product"] == 0 and win[0]["multisplit"] == 0
+    assert win[1]["outer_product"] > 0 and win[1]["expand_final"] == 0 and win[1]["expand_split"] == 0
+    assert win[2]["expand_split"] > 0 and win[2]["outer_product"] == 0 and win[2]["expand_final"] == 0
+    for m in (1, 2):
+        for x, y in zip(runs[m][:3], runs[0][:3]):
+            np.testing.assert_array_equal(x, y)
+        for key in ("level_elems", "final_chunks", "dense_chunks"):
+            assert runs[m][3][key] == runs[0][3][key], key
     ref = oracle.spgemm(A, A)
-    assert_csr_equal_structure(b[0], b[1], ref.row_ptr, ref.col, "C")
-    np.testing.assert_array_equal(b[2], ref.val.astype(dtype))
+    assert_csr_equal_structure(runs[0][0], runs[0][1], ref.row_ptr, ref.col, "C")
+    np.testing.assert_array_equal(runs[0][2], ref.val.astype(dtype))
 
 
 def test_batches_fp32_multilevel():
