@@ -23,8 +23,8 @@ constexpr int kMsRowsMax = 512;
 constexpr int kMsItemsF64 = 4;   // elements per thread held in registers
 constexpr int kMsItemsF32 = 8;
 // Straight into final chunks: no LDS staging, so larger tiles.
-constexpr int kXfItemsF64 = 8;
-constexpr int kXfItemsF32 = 16;
+constexpr int kXfItemsF64 = 4;
+constexpr int kXfItemsF32 = 8;
 constexpr int kXfNBMax = 8192;   // (row, chunk) buckets per work group
 
 __device__ __forceinline__ int bits_for(int n) {
@@ -362,11 +362,17 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
 // above) goes to the final chunk covering its column, finalOf[row * nreq +
 // slot] with slot = col >> log2W; spanOf holds that chunk's width as log2 of
 // W-wide slots.  A work group's buckets are (row inside the range, first
-// slot of the final chunk).  Consecutive elements that share a bucket (most
-// of a scaled B row's run inside one W-wide slot) are ranked together: the
-// first lane of each such group adds the group's size to the bucket's LDS
-// counter.  One global reservation per bucket, then every element is
-// written in place with its column made local to the chunk.
+// slot of the final chunk).
+//
+// The entries that start inside the range are staged in LDS at their first
+// element (B offset, a_ik, row), so an element reads only B from memory: a
+// wave finds each lane's entry as the last start at or before it, from one
+// ballot of the start flags (and, for entries begun in an earlier 64-element
+// segment, that segment's last start).  Consecutive elements that share a
+// bucket (most of a scaled B row's run inside one W-wide slot) are ranked
+// together: the first lane of each such group adds the group's size to the
+// bucket's LDS counter.  One global reservation per bucket, then every
+// element is written in place with its column made local to the chunk.
 template <int ITEMS, typename V, bool kVals>
 __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockElems,
                                                       const int64_t* __restrict__ rowPtr,
@@ -380,14 +386,19 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
                                                       V* __restrict__ outVal,
                                                       int32_t* __restrict__ err) {
   // LDS (sized by the host): gbase[NB] i64 | bnd[maxRows] i64 |
-  // ent[blockElems] i32 | hist[NB] i32, NB = maxRows * nreq.
+  // eA[blockElems] V | eBase[blockElems] i32 | eRow[blockElems] i32 |
+  // hist[NB] i32 | spanS[NB] i8, NB = maxRows * nreq.
   extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kSegs = ITEMS * (kNT / kWave);
   const int NBcap = maxRows * nreq;
   int64_t* gbase = (int64_t*)smem;
   int64_t* bnd = gbase + NBcap;
-  int32_t* ent = (int32_t*)(bnd + maxRows);
-  int32_t* hist = ent + blockElems;
-  __shared__ int32_t wtot[kNT / kWave];
+  V* eA = (V*)(bnd + maxRows);
+  int32_t* eBase = (int32_t*)(eA + (kVals ? blockElems : 0));
+  int32_t* eRow = eBase + blockElems;
+  int32_t* hist = eRow + blockElems;
+  int8_t* spanS = (int8_t*)(hist + NBcap);
+  __shared__ int32_t segLast[kSegs];
   __shared__ TileInfo s_info;
   const int64_t nTiles = (E + blockElems - 1) / blockElems;
   const int64_t tile = (int64_t)(blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
@@ -395,44 +406,88 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   const int64_t e0 = tile * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
-  for (int i = threadIdx.x; i < n; i += kNT) ent[i] = -1;
+  for (int i = threadIdx.x; i < n; i += kNT) eRow[i] = -1;
   const int nrows = range_rows(rowPtr, info, tile, maxRows, bnd, &s_info);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
   }
+  const int64_t r0 = s_info.r0;
   const int NB = nrows * nreq;
-  for (int i = threadIdx.x; i < NB; i += kNT) hist[i] = 0;
-  entries_of_range(ent, n, e0, s_info.t0, s_info.t1, src.eOff, wtot);
+  for (int i = threadIdx.x; i < NB; i += kNT) {
+    hist[i] = 0;
+    spanS[i] = spanOf[r0 * nreq + i];
+  }
+  __syncthreads();
+  // Entries with products that start inside the range (and t0, which holds
+  // the range's first element): B offset relative to the element index,
+  // a_ik and local row, stored at the entry's first element.
+  for (int32_t t = s_info.t0 + (int32_t)threadIdx.x; t <= s_info.t1; t += kNT) {
+    const int64_t o = src.eOff[t];
+    if (src.eOff[t + 1] == o) continue;
+    const int64_t from = o > e0 ? o : e0;
+    const int64_t pos = from - e0;
+    if (pos >= n) continue;
+    eRow[pos] = local_row(bnd, nrows, from);
+    eBase[pos] = (int32_t)((int64_t)src.eB[t] + e0 - o);
+    if constexpr (kVals) eA[pos] = ((const V*)src.eVal)[t];
+  }
   __syncthreads();
 
-  const int64_t r0 = s_info.r0;
-  const int32_t W = 1 << log2W;
-  int32_t cc[ITEMS];
-  V xv[ITEMS];
-  int32_t bb[ITEMS];
-  int32_t rank[ITEMS];
+  // Entry start of every element: the last start flag at or before it in
+  // its 64-element segment, else the last one of an earlier segment.
+  const int w = threadIdx.x / kWave;
+  const uint64_t le = lanemask_lt() | (1ull << lane_id());
+  int32_t hp[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int idx = it * kNT + threadIdx.x;
-    const bool act = idx < n;
+    const bool head = idx < n && eRow[idx] >= 0;
+    const uint64_t hm = __ballot(head);
+    const int segBase = it * kNT + w * kWave;
+    hp[it] = (hm & le) ? segBase + last_set64(hm & le) : -1;
+    if (lane_id() == 0) segLast[it * (kNT / kWave) + w] = hm ? segBase + last_set64(hm) : -1;
+  }
+  __syncthreads();
+  // segLast becomes its own inclusive prefix maximum: the last start at or
+  // before the end of each segment.
+  static_assert(kSegs <= kWave, "one wave scans the segments");
+  if (w == 0) {
+    int32_t x = lane_id() < kSegs ? segLast[lane_id()] : -1;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int32_t y = __shfl_up(x, d);
+      if (lane_id() >= d && y > x) x = y;
+    }
+    if (lane_id() < kSegs) segLast[lane_id()] = x;
+  }
+  __syncthreads();
+  const int W = 1 << log2W;
+  int32_t cc[ITEMS];
+  V xv[ITEMS];
+  int32_t bb[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int idx = it * kNT + threadIdx.x;
     cc[it] = 0;
     xv[it] = V(0);
     bb[it] = -1;
-    if (act) {
-      const int64_t e = e0 + idx;
-      const int32_t t = ent[idx];
-      const int64_t bp = (int64_t)src.eB[t] + (e - src.eOff[t]);
+    if (idx < n) {
+      // Segment 0 starts with the range's first entry, so every element of
+      // a later segment without a start of its own finds one before it.
+      const int h = hp[it] >= 0 ? hp[it] : segLast[it * (kNT / kWave) + w - 1];
+      const int32_t bp = idx + eBase[h];
       const int32_t col = src.bcol[bp];
-      if constexpr (kVals) xv[it] = ((const V*)src.eVal)[t] * ((const V*)src.bval)[bp];
-      const int lr = local_row(bnd, nrows, e);
+      if constexpr (kVals) xv[it] = eA[h] * ((const V*)src.bval)[bp];
+      const int lr = eRow[h];
       const int32_t slot = col >> log2W;
-      const int sp = spanOf[(r0 + lr) * nreq + slot];
+      const int sp = spanS[lr * nreq + slot];
       cc[it] = col & ((W << sp) - 1);
       bb[it] = lr * nreq + (slot & ~((1 << sp) - 1));
     }
   }
   // Rank: groups of consecutive lanes with one bucket share one LDS atomic.
+  int32_t rank[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const bool act = bb[it] >= 0;
@@ -440,7 +495,6 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
     const bool head = act && (lane_id() == 0 || prev != bb[it]);
     const uint64_t heads = __ballot(head);
     const uint64_t actm = __ballot(act);
-    const uint64_t le = lanemask_lt() | (1ull << lane_id());
     const int h = last_set64(heads & le);
     const uint64_t above = heads & ~le;
     const int nxt = above ? ffs64(above) : 64 - __clzll((long long)actm);
@@ -521,7 +575,8 @@ void launch_expand_final(bool f64, int64_t E, int32_t blockElems, const int64_t*
   if (E <= 0) return;
   const unsigned g = (grid_for(E, blockElems) + kXcds - 1) / kXcds * kXcds;
   const size_t NB = (size_t)maxRows * nreq;
-  const size_t lds = NB * 12 + (size_t)maxRows * 8 + (size_t)blockElems * 4 + 16;
+  const size_t vb = !outVal ? 0 : f64 ? 8 : 4;
+  const size_t lds = NB * 13 + (size_t)maxRows * 8 + (size_t)blockElems * (vb + 8) + 16;
 #define SG_XF(ITEMS, V, VALS)                                                                  \
   hipLaunchKernelGGL((k_expand_final<ITEMS, V, VALS>), dim3(g), dim3(kNT), lds, s, E, blockElems, \
                      rowPtr, info, src, finalOf, spanOf, nreq, log2W, maxRows, cursor, outCol,  \
