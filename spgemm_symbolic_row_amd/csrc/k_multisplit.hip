@@ -463,28 +463,37 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   }
   __syncthreads();
   const int W = 1 << log2W;
+  // Every lane loads (lanes past the range repeat element 0), so the loads
+  // of all items are in flight together.
+  int32_t hh[ITEMS];
+  uint32_t bp[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    const int idx = it * kNT + threadIdx.x;
+    // Segment 0 starts with the range's first entry, so every element of a
+    // later segment without a start of its own finds one before it.
+    const int sg = it * (kNT / kWave) + w - 1;
+    const int h = hp[it] >= 0 ? hp[it] : segLast[sg > 0 ? sg : 0];
+    hh[it] = idx < n ? h : 0;
+    bp[it] = (uint32_t)((idx < n ? idx : 0) + eBase[hh[it]]);
+  }
   int32_t cc[ITEMS];
   V xv[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+    cc[it] = src.bcol[bp[it]];
+    if constexpr (kVals) xv[it] = ((const V*)src.bval)[bp[it]];
+  }
   int32_t bb[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int idx = it * kNT + threadIdx.x;
-    cc[it] = 0;
-    xv[it] = V(0);
-    bb[it] = -1;
-    if (idx < n) {
-      // Segment 0 starts with the range's first entry, so every element of
-      // a later segment without a start of its own finds one before it.
-      const int h = hp[it] >= 0 ? hp[it] : segLast[it * (kNT / kWave) + w - 1];
-      const int32_t bp = idx + eBase[h];
-      const int32_t col = src.bcol[bp];
-      if constexpr (kVals) xv[it] = eA[h] * ((const V*)src.bval)[bp];
-      const int lr = eRow[h];
-      const int32_t slot = col >> log2W;
-      const int sp = spanS[lr * nreq + slot];
-      cc[it] = col & ((W << sp) - 1);
-      bb[it] = lr * nreq + (slot & ~((1 << sp) - 1));
-    }
+    const int lr = eRow[hh[it]];
+    if constexpr (kVals) xv[it] *= eA[hh[it]];
+    const int32_t slot = cc[it] >> log2W;
+    const int sp = spanS[lr * nreq + slot];
+    cc[it] &= (W << sp) - 1;
+    bb[it] = idx < n ? lr * nreq + (slot & ~((1 << sp) - 1)) : -1;
   }
   // Rank: groups of consecutive lanes with one bucket share one LDS atomic.
   int32_t rank[ITEMS];
