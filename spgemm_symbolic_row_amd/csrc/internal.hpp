@@ -267,6 +267,13 @@ void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* 
 // ---- k_chunks.hip ----
 void chunks_set_attributes();
 size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb);
+// Light-chunk numeric with elements in registers and a dense LDS array of
+// the chunk's output size indexed by bitmap rank.  Returns false (nothing
+// launched) when the bin does not fit this kernel.
+size_t direct_chunk_lds(bool f64, int32_t cap, int32_t words, int rpb);
+bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
+                              int32_t words, size_t ldsMax, const ChunkList& cl, int32_t* ccol,
+                              void* cval, int32_t* err, hipStream_t s);
 // sizeClass 0: chunks of <= 256 elements (4 per work group), 1: <= 4096, 2: larger.
 void launch_sym_chunks_bitmap(int sizeClass, const ChunkDesc* desc, int64_t n, int32_t words,
                               const ChunkList& cl, hipStream_t s);

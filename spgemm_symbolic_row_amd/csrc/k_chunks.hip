@@ -181,6 +181,107 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const ChunkDesc* _
   }
 }
 
+// Light chunks with their elements held in registers (at most TPC * KB per
+// chunk): the columns set bits of a chunk-width bitmap, the word prefix of
+// its popcounts gives every column its rank among the chunk's distinct
+// columns, and each element adds its value straight into slot rank of a
+// dense LDS array of the chunk's exact output size.  Ranks follow column
+// order, so the output is written sorted and coalesced, with no hash table
+// and no probing.
+__host__ __device__ constexpr size_t direct_group_bytes(int32_t cap, int32_t words, int vb) {
+  return ((size_t)cap * vb + (size_t)words * 8 + (size_t)cap * 2 + 15) / 16 * 16;
+}
+
+template <int TPC, int CPB, int KB, typename V>
+__global__ __launch_bounds__(TPC* CPB) void k_num_chunks_direct(const ChunkDesc* __restrict__ desc,
+                                                                int64_t n, int32_t cap,
+                                                                int32_t words, ChunkList cl,
+                                                                int32_t* __restrict__ ccol,
+                                                                V* __restrict__ cval,
+                                                                int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int WPG = TPC / kWave;
+  __shared__ int32_t wtot[CPB * WPG];
+  const int g = threadIdx.x / TPC, t = threadIdx.x % TPC, w = t / kWave;
+  unsigned char* base = smem + (size_t)g * direct_group_bytes(cap, words, (int)sizeof(V));
+  V* vals = (V*)base;
+  uint32_t* bm = (uint32_t*)(vals + cap);
+  int32_t* wpre = (int32_t*)(bm + words);
+  uint16_t* cols = (uint16_t*)(wpre + words);
+  const int64_t ci = (int64_t)blockIdx.x * CPB + g;
+  ChunkDesc d{};
+  int32_t cc[KB];
+  V vv[KB];
+  if (ci < n) d = desc[ci];
+  {
+    const int64_t end = d.off + d.cnt;
+    const bool b1 = d.buf != 0;
+    const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
+    const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int64_t e = d.off + t + (int64_t)k * TPC;
+      cc[k] = e < end ? col[e] : -1;
+      vv[k] = e < end ? val[e] : V(0);
+    }
+  }
+  if (t == 0 && d.cnt > (int64_t)TPC * KB) flag_error(err, kErrHashFull);
+  const int32_t want = d.want < cap ? d.want : cap;
+  for (int i = t; i < words; i += TPC) bm[i] = 0;
+  for (int i = t; i < want; i += TPC) vals[i] = V(0);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < KB; ++k)
+    if (cc[k] >= 0) atomicOr(&bm[cc[k] >> 5], 1u << (cc[k] & 31));
+  __syncthreads();
+  // Exclusive prefix of the word popcounts: each thread owns a contiguous
+  // run of words.
+  const int wpt = (words + TPC - 1) / TPC;
+  const int w0 = t * wpt;
+  int32_t mine = 0;
+  for (int i = 0; i < wpt; ++i)
+    if (w0 + i < words) mine += __popc(bm[w0 + i]);
+  const int32_t inc = wave_incl_scan(mine);
+  if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < WPG; ++i) {
+    const int32_t tv = wtot[g * WPG + i];
+    if (i < w) before += tv;
+    total += tv;
+  }
+  int32_t run = before + inc - mine;
+  for (int i = 0; i < wpt; ++i) {
+    if (w0 + i < words) {
+      wpre[w0 + i] = run;
+      run += __popc(bm[w0 + i]);
+    }
+  }
+  __syncthreads();
+  if (ci < n && t == 0 && total != d.want) flag_error(err, kErrCountMismatch);
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    const int32_t c = cc[k];
+    if (c >= 0) {
+      const int32_t r = wpre[c >> 5] + __popc(bm[c >> 5] & ((1u << (c & 31)) - 1u));
+      if (r < want) {
+        atomicAdd(&vals[r], vv[k]);
+        cols[r] = (uint16_t)c;
+      }
+    }
+  }
+  __syncthreads();
+  if (ci < n) {
+    const int64_t obase = d.base;
+    const int32_t colBase = d.colBase;
+    for (int r = t; r < want; r += TPC) {
+      ccol[obase + r] = colBase + cols[r];
+      cval[obase + r] = vals[r];
+    }
+  }
+}
+
 }  // namespace
 
 void chunks_set_attributes() {
@@ -198,7 +299,62 @@ void chunks_set_attributes() {
   SG_ATTR((k_num_chunks_rank<256, 1, double>));
   SG_ATTR((k_num_chunks_rank<512, 1, double>));
   SG_ATTR((k_num_chunks_rank<1024, 1, double>));
+#define SG_DIR(V) \
+  SG_ATTR((k_num_chunks_direct<64, 4, 1, V>));  \
+  SG_ATTR((k_num_chunks_direct<64, 4, 2, V>));  \
+  SG_ATTR((k_num_chunks_direct<64, 4, 4, V>));  \
+  SG_ATTR((k_num_chunks_direct<128, 2, 4, V>)); \
+  SG_ATTR((k_num_chunks_direct<256, 1, 4, V>)); \
+  SG_ATTR((k_num_chunks_direct<512, 1, 4, V>)); \
+  SG_ATTR((k_num_chunks_direct<1024, 1, 4, V>)); \
+  SG_ATTR((k_num_chunks_direct<1024, 1, 8, V>)); \
+  SG_ATTR((k_num_chunks_direct<1024, 1, 16, V>))
+  SG_DIR(float);
+  SG_DIR(double);
+#undef SG_DIR
 #undef SG_ATTR
+}
+
+size_t direct_chunk_lds(bool f64, int32_t cap, int32_t words, int rpb) {
+  return (size_t)rpb * direct_group_bytes(cap, words, f64 ? 8 : 4);
+}
+
+bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
+                              int32_t words, size_t ldsMax, const ChunkList& cl, int32_t* ccol,
+                              void* cval, int32_t* err, hipStream_t s) {
+  const int kb = (int)((b.cap + b.tpr - 1) / b.tpr);
+  const size_t lds = direct_chunk_lds(f64, b.cap, words, b.rpb);
+  if (kb > 16 || (b.tpr < 1024 && b.tpr * 4 < b.cap) || lds > ldsMax) return false;
+  if (n <= 0) return true;
+  const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
+#define L(TPC, CPB, KB)                                                                        \
+  do {                                                                                         \
+    if (f64)                                                                                   \
+      hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, double>), dim3(grid),              \
+                         dim3(TPC * CPB), lds, s, desc, n, b.cap, words, cl, ccol,             \
+                         (double*)cval, err);                                                  \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, float>), dim3(grid),               \
+                         dim3(TPC * CPB), lds, s, desc, n, b.cap, words, cl, ccol,             \
+                         (float*)cval, err);                                                   \
+  } while (0)
+  switch (b.tpr) {
+    case 64:
+      if (kb <= 1) L(64, 4, 1);
+      else if (kb <= 2) L(64, 4, 2);
+      else L(64, 4, 4);
+      break;
+    case 128: L(128, 2, 4); break;
+    case 256: L(256, 1, 4); break;
+    case 512: L(512, 1, 4); break;
+    default:
+      if (kb <= 4) L(1024, 1, 4);
+      else if (kb <= 8) L(1024, 1, 8);
+      else L(1024, 1, 16);
+      break;
+  }
+#undef L
+  return true;
 }
 
 size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb) {
