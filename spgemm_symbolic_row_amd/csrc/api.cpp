@@ -273,6 +273,7 @@ struct spgemm_plan_s {
   int64_t* dAnnz = nullptr; // scan of the heavy rows' A lengths (h + 1)
   bool fused = false;    // the first level is fed straight from A and B
   bool direct = false;   // one pass straight into the final chunks
+  bool col16 = false;    // final chunk columns stored as uint16_t
   int32_t* slotNnz = nullptr;
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
@@ -646,7 +647,7 @@ int heavy_nbuf(spgemm_plan_t p) {
 }
 size_t heavy_buf_bytes(spgemm_plan_t p, int64_t Pb, bool vals) {
   const size_t n = (size_t)std::max<int64_t>(Pb, 1);
-  const size_t pair = align256(n * 4) + (vals ? align256(n * (p->f64 ? 8 : 4)) : 0);
+  const size_t pair = align256(n * (p->col16 ? 2 : 4)) + (vals ? align256(n * (p->f64 ? 8 : 4)) : 0);
   return heavy_nbuf(p) * pair;
 }
 
@@ -706,6 +707,9 @@ void heavy_prepare(spgemm_plan_t p) {
   const bool xfFits = expand_final_geometry(p->f64, p->rowTau, p->nreq, &xfElems, &xfRows);
   p->direct = structCounts && p->opts.expansion == 0 && xfFits;
   p->fused = structCounts && !p->direct && p->opts.expansion != 1;
+  // Straight into final chunks at most 65536 columns wide, a local column
+  // takes two bytes.
+  p->col16 = p->direct && p->params.level_width[0] <= 65536;
   const int64_t nbuf = heavy_nbuf(p);
   // Numeric needs columns and values.  If that takes one batch, symbolic
   // expands with values and numeric reuses the result; otherwise symbolic
@@ -775,7 +779,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     const size_t n = (size_t)std::max<int64_t>(Pb, 1);
     for (int b = 0; b < heavy_nbuf(p); ++b) {
       B->bufCol[b] = (int32_t*)q;
-      q += align256(n * 4);
+      q += align256(n * (p->col16 ? 2 : 4));
       if (vals) {
         B->bufVal[b] = q;
         q += align256(n * vb);
@@ -981,7 +985,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     launch_tile_info(Pb, blockElems, chatRowPtr, hb, blkRow, blkEnt, src.nE, info, s);
     launch_expand_final(f64, Pb, blockElems, chatRowPtr, info, src, finalOf, spanOf,
                         (int32_t)p->nreq, log2_exact(W), maxRows, fcCursor, B->bufCol[0],
-                        vals ? B->bufVal[0] : nullptr, p->errWord, s);
+                        p->col16, vals ? B->bufVal[0] : nullptr, p->errWord, s);
     ph_end(p, phX, s);
     check_launch("direct expansion");
   }
@@ -1007,7 +1011,7 @@ ChunkList chunk_list(spgemm_plan_t p, const Batch& B) {
   return ChunkList{B.fcOff, B.fcCnt, B.fcRow, B.fcSlot, B.fcBuf, B.bufCol[0], B.bufCol[1],
                    B.bufVal[0], B.bufVal[1], p->params.dense_width, p->nreq,
                    p->xheavy + B.hb0, p->slotOff + B.hb0 * p->nreq,
-                   p->slotNnz + B.hb0 * p->nreq};
+                   p->slotNnz + B.hb0 * p->nreq, p->col16 ? 1 : 0};
 }
 
 // Chunk symbolic: per-chunk nnz into the batch's slots.

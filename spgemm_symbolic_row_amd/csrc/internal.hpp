@@ -64,8 +64,8 @@ struct ChunkList {
   const int32_t* row;
   const int32_t* slot;
   const int8_t* buf;
-  const int32_t* col0;
-  const int32_t* col1;
+  const void* col0;       // final columns: int32_t, or uint16_t with col16
+  const void* col1;
   const void* val0;
   const void* val1;
   int64_t W;
@@ -73,6 +73,7 @@ struct ChunkList {
   const int32_t* xheavy;  // heavy row index -> row of C
   const int64_t* slotOff; // exclusive offset of each slot inside its row
   int32_t* slotNnz;       // nnz of the chunk starting at each slot
+  int32_t col16;          // chunk columns stored as uint16_t
 };
 
 // Everything a numeric chunk kernel needs about one final chunk, gathered
@@ -218,7 +219,7 @@ bool expand_final_geometry(bool f64, int64_t rowTau, int64_t nreq, int32_t* bloc
 void launch_expand_final(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
                          const TileInfo* info, const ExpandSrc& src, const int32_t* finalOf,
                          const int8_t* spanOf, int32_t nreq, int log2W, int maxRows,
-                         int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
+                         int64_t* cursor, void* outCol, bool col16, void* outVal, int32_t* err,
                          hipStream_t s);
 // One multisplit level.  inCol/inVal: the level's input, or src (not null)
 // to make the elements from A and B.  outVal null: columns only.

@@ -16,7 +16,7 @@
 namespace sg {
 namespace {
 
-template <int TPC, int CPB>
+template <int TPC, int CPB, typename C = int32_t>
 __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const ChunkDesc* __restrict__ desc,
                                                                 int64_t n, int32_t words,
                                                                 ChunkList cl) {
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const ChunkDesc*
   if (ci < n) {
     d = desc[ci];
     const int64_t off = d.off, end = off + d.cnt;
-    const int32_t* __restrict__ col = d.buf ? cl.col1 : cl.col0;
+    const C* __restrict__ col = (const C*)(d.buf ? cl.col1 : cl.col0);
     constexpr int kB = 8;  // loads in flight per thread
     for (int64_t e0 = off + t; e0 < end; e0 += (int64_t)TPC * kB) {
       int32_t cc[kB];
@@ -92,7 +92,7 @@ __host__ __device__ constexpr size_t rank_group_bytes(int32_t T, int32_t words) 
   return (size_t)T * sizeof(V) + (size_t)T * 4 + (size_t)words * 8;
 }
 
-template <int TPC, int CPB, typename V>
+template <int TPC, int CPB, typename V, typename C = int32_t>
 __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const ChunkDesc* __restrict__ desc,
                                                               int64_t n, int32_t T, int32_t words,
                                                               ChunkList cl,
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_rank(const ChunkDesc* _
     d = desc[ci];
     const int64_t off = d.off, end = off + d.cnt;
     const bool b1 = d.buf != 0;
-    const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
+    const C* __restrict__ col = (const C*)(b1 ? cl.col1 : cl.col0);
     const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
     constexpr int kB = 4;  // loads in flight per thread
     for (int64_t e0 = off + t; e0 < end; e0 += (int64_t)TPC * kB) {
@@ -192,7 +192,7 @@ __host__ __device__ constexpr size_t direct_group_bytes(int32_t cap, int32_t wor
   return ((size_t)cap * vb + (size_t)words * 8 + (size_t)cap * 2 + 15) / 16 * 16;
 }
 
-template <int TPC, int CPB, int KB, typename V>
+template <int TPC, int CPB, int KB, typename V, typename C = int32_t>
 __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_direct(const ChunkDesc* __restrict__ desc,
                                                                 int64_t n, int32_t cap,
                                                                 int32_t words, ChunkList cl,
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_direct(const ChunkDesc*
   {
     const int64_t end = d.off + d.cnt;
     const bool b1 = d.buf != 0;
-    const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
+    const C* __restrict__ col = (const C*)(b1 ? cl.col1 : cl.col0);
     const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
@@ -289,16 +289,29 @@ void chunks_set_attributes() {
   SG_ATTR((k_sym_chunks_bitmap<64, 4>));
   SG_ATTR((k_sym_chunks_bitmap<256, 1>));
   SG_ATTR((k_sym_chunks_bitmap<1024, 1>));
+  SG_ATTR((k_sym_chunks_bitmap<64, 4, uint16_t>));
+  SG_ATTR((k_sym_chunks_bitmap<256, 1, uint16_t>));
+  SG_ATTR((k_sym_chunks_bitmap<1024, 1, uint16_t>));
   SG_ATTR((k_num_chunks_rank<64, 4, float>));
+  SG_ATTR((k_num_chunks_rank<64, 4, float, uint16_t>));
   SG_ATTR((k_num_chunks_rank<128, 2, float>));
+  SG_ATTR((k_num_chunks_rank<128, 2, float, uint16_t>));
   SG_ATTR((k_num_chunks_rank<256, 1, float>));
+  SG_ATTR((k_num_chunks_rank<256, 1, float, uint16_t>));
   SG_ATTR((k_num_chunks_rank<512, 1, float>));
+  SG_ATTR((k_num_chunks_rank<512, 1, float, uint16_t>));
   SG_ATTR((k_num_chunks_rank<1024, 1, float>));
+  SG_ATTR((k_num_chunks_rank<1024, 1, float, uint16_t>));
   SG_ATTR((k_num_chunks_rank<64, 4, double>));
+  SG_ATTR((k_num_chunks_rank<64, 4, double, uint16_t>));
   SG_ATTR((k_num_chunks_rank<128, 2, double>));
+  SG_ATTR((k_num_chunks_rank<128, 2, double, uint16_t>));
   SG_ATTR((k_num_chunks_rank<256, 1, double>));
+  SG_ATTR((k_num_chunks_rank<256, 1, double, uint16_t>));
   SG_ATTR((k_num_chunks_rank<512, 1, double>));
+  SG_ATTR((k_num_chunks_rank<512, 1, double, uint16_t>));
   SG_ATTR((k_num_chunks_rank<1024, 1, double>));
+  SG_ATTR((k_num_chunks_rank<1024, 1, double, uint16_t>));
 #define SG_DIR(V) \
   SG_ATTR((k_num_chunks_direct<64, 4, 1, V>));  \
   SG_ATTR((k_num_chunks_direct<64, 4, 2, V>));  \
@@ -309,6 +322,19 @@ void chunks_set_attributes() {
   SG_ATTR((k_num_chunks_direct<1024, 1, 4, V>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 8, V>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 16, V>))
+  SG_DIR(float);
+  SG_DIR(double);
+#undef SG_DIR
+#define SG_DIR(V) \
+  SG_ATTR((k_num_chunks_direct<64, 4, 1, V, uint16_t>));  \
+  SG_ATTR((k_num_chunks_direct<64, 4, 2, V, uint16_t>));  \
+  SG_ATTR((k_num_chunks_direct<64, 4, 4, V, uint16_t>));  \
+  SG_ATTR((k_num_chunks_direct<128, 2, 4, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<256, 1, 4, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<512, 1, 4, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<1024, 1, 4, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<1024, 1, 8, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<1024, 1, 16, V, uint16_t>))
   SG_DIR(float);
   SG_DIR(double);
 #undef SG_DIR
@@ -327,16 +353,15 @@ bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, 
   if (kb > 16 || (b.tpr < 1024 && b.tpr * 4 < b.cap) || lds > ldsMax) return false;
   if (n <= 0) return true;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
+#define L1(TPC, CPB, KB, V, C)                                                                 \
+  hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, V, C>), dim3(grid), dim3(TPC * CPB),    \
+                     lds, s, desc, n, b.cap, words, cl, ccol, (V*)cval, err)
 #define L(TPC, CPB, KB)                                                                        \
   do {                                                                                         \
-    if (f64)                                                                                   \
-      hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, double>), dim3(grid),              \
-                         dim3(TPC * CPB), lds, s, desc, n, b.cap, words, cl, ccol,             \
-                         (double*)cval, err);                                                  \
-    else                                                                                       \
-      hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, float>), dim3(grid),               \
-                         dim3(TPC * CPB), lds, s, desc, n, b.cap, words, cl, ccol,             \
-                         (float*)cval, err);                                                   \
+    if (f64 && cl.col16) L1(TPC, CPB, KB, double, uint16_t);                                   \
+    else if (f64) L1(TPC, CPB, KB, double, int32_t);                                           \
+    else if (cl.col16) L1(TPC, CPB, KB, float, uint16_t);                                      \
+    else L1(TPC, CPB, KB, float, int32_t);                                                     \
   } while (0)
   switch (b.tpr) {
     case 64:
@@ -354,6 +379,7 @@ bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, 
       break;
   }
 #undef L
+#undef L1
   return true;
 }
 
@@ -364,16 +390,22 @@ size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb) {
 void launch_sym_chunks_bitmap(int sizeClass, const ChunkDesc* desc, int64_t n, int32_t words,
                               const ChunkList& cl, hipStream_t s) {
   if (n <= 0) return;
-  if (sizeClass == 0) {
-    hipLaunchKernelGGL((k_sym_chunks_bitmap<64, 4>), dim3((unsigned)((n + 3) / 4)), dim3(256),
-                       (size_t)4 * words * 4, s, desc, n, words, cl);
-  } else if (sizeClass == 1) {
-    hipLaunchKernelGGL((k_sym_chunks_bitmap<256, 1>), dim3((unsigned)n), dim3(256),
-                       (size_t)words * 4, s, desc, n, words, cl);
-  } else {
-    hipLaunchKernelGGL((k_sym_chunks_bitmap<1024, 1>), dim3((unsigned)n), dim3(1024),
-                       (size_t)words * 4, s, desc, n, words, cl);
-  }
+#define L(TPC, CPB, G, LDS)                                                                     \
+  do {                                                                                          \
+    if (cl.col16)                                                                               \
+      hipLaunchKernelGGL((k_sym_chunks_bitmap<TPC, CPB, uint16_t>), dim3(G), dim3(TPC * CPB),   \
+                         LDS, s, desc, n, words, cl);                                           \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_sym_chunks_bitmap<TPC, CPB, int32_t>), dim3(G), dim3(TPC * CPB),    \
+                         LDS, s, desc, n, words, cl);                                           \
+  } while (0)
+  if (sizeClass == 0)
+    L(64, 4, (unsigned)((n + 3) / 4), (size_t)4 * words * 4);
+  else if (sizeClass == 1)
+    L(256, 1, (unsigned)n, (size_t)words * 4);
+  else
+    L(1024, 1, (unsigned)n, (size_t)words * 4);
+#undef L
 }
 
 void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
@@ -382,14 +414,15 @@ void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, in
   if (n <= 0) return;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
   const size_t lds = rank_chunk_lds(f64, b.T, words, b.rpb);
+#define L1(TPC, CPB, V, C)                                                                     \
+  hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, V, C>), dim3(grid), dim3(TPC * CPB), lds, s,  \
+                     desc, n, b.T, words, cl, ccol, (V*)cval, err)
 #define L(TPC, CPB)                                                                            \
   do {                                                                                         \
-    if (f64)                                                                                   \
-      hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, double>), dim3(grid), dim3(TPC * CPB),   \
-                         lds, s, desc, n, b.T, words, cl, ccol, (double*)cval, err);           \
-    else                                                                                       \
-      hipLaunchKernelGGL((k_num_chunks_rank<TPC, CPB, float>), dim3(grid), dim3(TPC * CPB),    \
-                         lds, s, desc, n, b.T, words, cl, ccol, (float*)cval, err);            \
+    if (f64 && cl.col16) L1(TPC, CPB, double, uint16_t);                                       \
+    else if (f64) L1(TPC, CPB, double, int32_t);                                               \
+    else if (cl.col16) L1(TPC, CPB, float, uint16_t);                                          \
+    else L1(TPC, CPB, float, int32_t);                                                         \
   } while (0)
   switch (b.tpr) {
     case 64: L(64, 4); break;
@@ -399,6 +432,7 @@ void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, in
     default: L(1024, 1); break;
   }
 #undef L
+#undef L1
 }
 
 }  // namespace sg

@@ -118,6 +118,7 @@ __global__ __launch_bounds__(kNT) void k_chunk_bins(int64_t nfc, const int32_t* 
 // ------------------------------------------------- dense LDS accumulators
 // Symbolic: a W-bit LDS bitmap per chunk (read before or-ing, so repeated
 // columns cost a read only), then a popcount.
+template <typename C>
 __global__ __launch_bounds__(kNT) void k_dense_sym(const ChunkDesc* __restrict__ desc, ChunkList cl,
                                                    int32_t* __restrict__ err) {
   extern __shared__ __align__(16) uint32_t bm[];
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const ChunkDesc* __restrict__
   for (int i = threadIdx.x; i < nwords; i += kNT) bm[i] = 0;
   __syncthreads();
   const int64_t off = d.off, end = off + d.cnt;
-  const int32_t* __restrict__ col = d.buf ? cl.col1 : cl.col0;
+  const C* __restrict__ col = (const C*)(d.buf ? cl.col1 : cl.col0);
   for (int64_t e = off + threadIdx.x; e < end; e += kNT) {
     const int32_t c = col[e];
     const uint32_t bit = 1u << (c & 31);
@@ -157,8 +158,8 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const ChunkDesc* __restrict__
 // whole accumulator is cleared once, at the start).
 constexpr int kDenseNT = 1024;
 constexpr int kDenseB = 8;  // elements per thread per batch
-template <typename V>
-__device__ __forceinline__ void dense_load_batch(const int32_t* __restrict__ col,
+template <typename V, typename C>
+__device__ __forceinline__ void dense_load_batch(const C* __restrict__ col,
                                                  const V* __restrict__ val, int64_t e0, int64_t end,
                                                  int32_t (&cc)[kDenseB], V (&vv)[kDenseB]) {
 #pragma unroll
@@ -182,7 +183,7 @@ __device__ __forceinline__ void dense_add_batch(V* vals, uint32_t* bm, const int
   }
 }
 
-template <typename V>
+template <typename V, typename C>
 __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restrict__ desc, int64_t n,
                                                         ChunkList cl,
                                                         int32_t* __restrict__ ccol,
@@ -203,11 +204,11 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
   int32_t cc[kDenseB];
   V vv[kDenseB];
   ChunkDesc d{};
-  const int32_t* col = cl.col0;
+  const C* col = (const C*)cl.col0;
   const V* val = (const V*)cl.val0;
   if (ci < n) {
     d = desc[ci];
-    col = d.buf ? cl.col1 : cl.col0;
+    col = (const C*)(d.buf ? cl.col1 : cl.col0);
     val = (const V*)(d.buf ? cl.val1 : cl.val0);
     dense_load_batch(col, val, d.off + threadIdx.x, d.off + d.cnt, cc, vv);
   }
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
     __syncthreads();
     // First batch of the next chunk, in flight during the write-out.
     if (cn < n) {
-      col = d.buf ? cl.col1 : cl.col0;
+      col = (const C*)(d.buf ? cl.col1 : cl.col0);
       val = (const V*)(d.buf ? cl.val1 : cl.val0);
       dense_load_batch(col, val, d.off + threadIdx.x, d.off + d.cnt, cc, vv);
     }
@@ -354,12 +355,15 @@ __global__ __launch_bounds__(kNT) void k_final_map(int64_t nfc, const int32_t* _
 }  // namespace
 
 void heavy_set_attributes() {
-  (void)hipFuncSetAttribute((const void*)k_dense_num<float>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-  (void)hipFuncSetAttribute((const void*)k_dense_num<double>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-  (void)hipFuncSetAttribute((const void*)k_dense_sym, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            163840);
+#define SG_ATTR(K) \
+  (void)hipFuncSetAttribute((const void*)(K), hipFuncAttributeMaxDynamicSharedMemorySize, 163840)
+  SG_ATTR((k_dense_num<float, int32_t>));
+  SG_ATTR((k_dense_num<double, int32_t>));
+  SG_ATTR((k_dense_num<float, uint16_t>));
+  SG_ATTR((k_dense_num<double, uint16_t>));
+  SG_ATTR(k_dense_sym<int32_t>);
+  SG_ATTR(k_dense_sym<uint16_t>);
+#undef SG_ATTR
 }
 
 void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, int v,
@@ -410,7 +414,10 @@ void launch_dense_sym(const ChunkDesc* desc, int64_t n, const ChunkList& cl, int
                       hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = (size_t)((cl.W + 31) / 32) * 4;
-  hipLaunchKernelGGL(k_dense_sym, dim3((unsigned)n), dim3(kNT), lds, s, desc, cl, err);
+  if (cl.col16)
+    hipLaunchKernelGGL(k_dense_sym<uint16_t>, dim3((unsigned)n), dim3(kNT), lds, s, desc, cl, err);
+  else
+    hipLaunchKernelGGL(k_dense_sym<int32_t>, dim3((unsigned)n), dim3(kNT), lds, s, desc, cl, err);
 }
 
 size_t dense_num_lds(bool f64, int64_t W) {
@@ -431,12 +438,14 @@ void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkLis
   // As many work groups as fit on the device at once (LDS of a CU: 160 KiB).
   const int64_t perCU = std::max<int64_t>(1, (int64_t)163840 / (int64_t)lds);
   const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1) * perCU);
-  if (f64)
-    hipLaunchKernelGGL(k_dense_num<double>, dim3(g), dim3(kDenseNT), lds, s, desc, n, cl, ccol,
-                       (double*)cval, err);
-  else
-    hipLaunchKernelGGL(k_dense_num<float>, dim3(g), dim3(kDenseNT), lds, s, desc, n, cl, ccol,
-                       (float*)cval, err);
+#define L(V, C)                                                                              \
+  hipLaunchKernelGGL((k_dense_num<V, C>), dim3(g), dim3(kDenseNT), lds, s, desc, n, cl, ccol,   \
+                     (V*)cval, err)
+  if (f64 && cl.col16) L(double, uint16_t);
+  else if (f64) L(double, int32_t);
+  else if (cl.col16) L(float, uint16_t);
+  else L(float, int32_t);
+#undef L
 }
 
 void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows(const int32_t* __restrict
   if (t == 0 && ri < nrows) cnt[row] = gcount[g];
 }
 
-template <int TPR, int RPB>
+template <int TPR, int RPB, typename C = int32_t>
 __global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, ChunkList cl,
                                                          int32_t* __restrict__ err) {
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const ChunkDesc* __rest
     d = desc[ri];
     const int64_t off = d.off;
     const int64_t end = off + d.cnt;
-    const int32_t* __restrict__ col = d.buf ? cl.col1 : cl.col0;
+    const C* __restrict__ col = (const C*)(d.buf ? cl.col1 : cl.col0);
     for (int64_t e = off + t; e < end; e += TPR)
       if (hset_insert(keys, (uint32_t)T, col[e], err)) ++mine;
   }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
   }
 }
 
-template <int TPR, int RPB, int E, typename V>
+template <int TPR, int RPB, int E, typename V, typename C = int32_t>
 __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, int32_t spt,
                                                          ChunkList cl,
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __rest
     const int64_t off = d.off;
     const int64_t end = off + d.cnt;
     const bool b1 = d.buf != 0;
-    const int32_t* __restrict__ col = b1 ? cl.col1 : cl.col0;
+    const C* __restrict__ col = (const C*)(b1 ? cl.col1 : cl.col0);
     const V* __restrict__ val = (const V*)(b1 ? cl.val1 : cl.val0);
     for (int64_t e = off + t; e < end; e += TPR) hmap_add(keys, vals, (uint32_t)T, col[e], val[e], err);
   }
@@ -393,6 +393,11 @@ void light_set_attributes() {
   set_lds_attr(k_sym_chunks<256, 1>);
   set_lds_attr(k_sym_chunks<512, 1>);
   set_lds_attr(k_sym_chunks<1024, 1>);
+  set_lds_attr(k_sym_chunks<64, 4, uint16_t>);
+  set_lds_attr(k_sym_chunks<128, 2, uint16_t>);
+  set_lds_attr(k_sym_chunks<256, 1, uint16_t>);
+  set_lds_attr(k_sym_chunks<512, 1, uint16_t>);
+  set_lds_attr(k_sym_chunks<1024, 1, uint16_t>);
 #define SG_NUM_ATTR(V)                          \
   set_lds_attr(k_num_rows<64, 4, 1, V>);        \
   set_lds_attr(k_num_rows<64, 4, 2, V>);        \
@@ -411,7 +416,16 @@ void light_set_attributes() {
   set_lds_attr(k_num_chunks<512, 1, 4, V>);     \
   set_lds_attr(k_num_chunks<1024, 1, 4, V>);    \
   set_lds_attr(k_num_chunks<1024, 1, 8, V>);    \
-  set_lds_attr(k_num_chunks<1024, 1, 16, V>);
+  set_lds_attr(k_num_chunks<1024, 1, 16, V>);   \
+  set_lds_attr(k_num_chunks<64, 4, 1, V, uint16_t>);      \
+  set_lds_attr(k_num_chunks<64, 4, 2, V, uint16_t>);      \
+  set_lds_attr(k_num_chunks<64, 4, 4, V, uint16_t>);      \
+  set_lds_attr(k_num_chunks<128, 2, 4, V, uint16_t>);     \
+  set_lds_attr(k_num_chunks<256, 1, 4, V, uint16_t>);     \
+  set_lds_attr(k_num_chunks<512, 1, 4, V, uint16_t>);     \
+  set_lds_attr(k_num_chunks<1024, 1, 4, V, uint16_t>);    \
+  set_lds_attr(k_num_chunks<1024, 1, 8, V, uint16_t>);    \
+  set_lds_attr(k_num_chunks<1024, 1, 16, V, uint16_t>);
   SG_NUM_ATTR(float)
   SG_NUM_ATTR(double)
 #undef SG_NUM_ATTR
@@ -441,9 +455,15 @@ void launch_sym_chunks(const BinCfg& b, const ChunkDesc* desc, int64_t n, const 
                        int32_t* err, hipStream_t s) {
   if (n <= 0) return;
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
-#define L(TPR, RPB)                                                                         \
-  hipLaunchKernelGGL((k_sym_chunks<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, desc, n, \
-                     b.T, cl, err)
+#define L(TPR, RPB)                                                                          \
+  do {                                                                                       \
+    if (cl.col16)                                                                            \
+      hipLaunchKernelGGL((k_sym_chunks<TPR, RPB, uint16_t>), dim3(grid), dim3(TPR * RPB),      \
+                         b.lds, s, desc, n, b.T, cl, err);                                   \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_sym_chunks<TPR, RPB, int32_t>), dim3(grid), dim3(TPR * RPB),       \
+                         b.lds, s, desc, n, b.T, cl, err);                                   \
+  } while (0);
   SG_DISPATCH_TPR(b, L)
 #undef L
 }
@@ -506,14 +526,26 @@ void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t
   const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
   if (f64) {
 #define L(TPR, RPB, E)                                                                         \
-  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
-                     desc, n, b.T, b.spt, cl, ccol, (double*)cval, err)
+  do { \
+  if (cl.col16)                                                                                 \
+    hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, double, uint16_t>), dim3(grid),                 \
+                       dim3(TPR * RPB), b.lds, s, desc, n, b.T, b.spt, cl, ccol, (double*)cval, err);  \
+  else                                                                                          \
+    hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, double>), dim3(grid), dim3(TPR * RPB), b.lds, s,  \
+                       desc, n, b.T, b.spt, cl, ccol, (double*)cval, err); \
+  } while (0)
     SG_DISPATCH_NUM(b, L);
 #undef L
   } else {
 #define L(TPR, RPB, E)                                                                        \
-  hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
-                     desc, n, b.T, b.spt, cl, ccol, (float*)cval, err)
+  do { \
+  if (cl.col16)                                                                                \
+    hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, float, uint16_t>), dim3(grid),                 \
+                       dim3(TPR * RPB), b.lds, s, desc, n, b.T, b.spt, cl, ccol, (float*)cval, err);  \
+  else                                                                                         \
+    hipLaunchKernelGGL((k_num_chunks<TPR, RPB, E, float>), dim3(grid), dim3(TPR * RPB), b.lds, s,  \
+                       desc, n, b.T, b.spt, cl, ccol, (float*)cval, err); \
+  } while (0)
     SG_DISPATCH_NUM(b, L);
 #undef L
   }

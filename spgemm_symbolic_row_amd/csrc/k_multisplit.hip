@@ -26,6 +26,7 @@ constexpr int kMsItemsF32 = 8;
 constexpr int kXfItemsF64 = 4;
 constexpr int kXfItemsF32 = 8;
 constexpr int kXfNBMax = 8192;   // (row, chunk) buckets per work group
+constexpr int kXfEnt = 256;      // entries per tile staged in LDS
 
 __device__ __forceinline__ int bits_for(int n) {
   int b = 0;
@@ -372,8 +373,9 @@ __global__ __launch_bounds__(kNT) void k_multisplit(int64_t E, int32_t blockElem
 // bucket (most of a scaled B row's run inside one W-wide slot) are ranked
 // together: the first lane of each such group adds the group's size to the
 // bucket's LDS counter.  One global reservation per bucket, then every
-// element is written in place with its column made local to the chunk.
-template <int ITEMS, typename V, bool kVals>
+// element is written in place with its column made local to the chunk
+// (as uint16_t when every chunk is at most 65536 columns wide).
+template <int ITEMS, typename V, bool kVals, typename OC>
 __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockElems,
                                                       const int64_t* __restrict__ rowPtr,
                                                       const TileInfo* __restrict__ info,
@@ -382,21 +384,22 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
                                                       const int8_t* __restrict__ spanOf,
                                                       int32_t nreq, int log2W, int maxRows,
                                                       int64_t* __restrict__ cursor,
-                                                      int32_t* __restrict__ outCol,
+                                                      OC* __restrict__ outCol,
                                                       V* __restrict__ outVal,
                                                       int32_t* __restrict__ err) {
   // LDS (sized by the host): gbase[NB] i64 | bnd[maxRows] i64 |
-  // eA[blockElems] V | eBase[blockElems] i32 | eRow[blockElems] i32 |
-  // hist[NB] i32 | spanS[NB] i8, NB = maxRows * nreq.
+  // eA[kXfEnt] V | eBase[kXfEnt] i32 | eRow[kXfEnt] i32 |
+  // slotAt[blockElems] i32 | hist[NB] i32 | spanS[NB] i8, NB = maxRows * nreq.
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kSegs = ITEMS * (kNT / kWave);
   const int NBcap = maxRows * nreq;
   int64_t* gbase = (int64_t*)smem;
   int64_t* bnd = gbase + NBcap;
   V* eA = (V*)(bnd + maxRows);
-  int32_t* eBase = (int32_t*)(eA + (kVals ? blockElems : 0));
-  int32_t* eRow = eBase + blockElems;
-  int32_t* hist = eRow + blockElems;
+  int32_t* eBase = (int32_t*)(eA + (kVals ? kXfEnt : 0));
+  int32_t* eRow = eBase + kXfEnt;
+  int32_t* slotAt = eRow + kXfEnt;
+  int32_t* hist = slotAt + blockElems;
   int8_t* spanS = (int8_t*)(hist + NBcap);
   __shared__ int32_t segLast[kSegs];
   __shared__ TileInfo s_info;
@@ -406,13 +409,14 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   const int64_t e0 = tile * blockElems;
   const int64_t e1 = (e0 + blockElems < E) ? e0 + blockElems : E;
   const int n = (int)(e1 - e0);
-  for (int i = threadIdx.x; i < n; i += kNT) eRow[i] = -1;
+  for (int i = threadIdx.x; i < n; i += kNT) slotAt[i] = -1;
   const int nrows = range_rows(rowPtr, info, tile, maxRows, bnd, &s_info);
   if (nrows < 0) {
     if (threadIdx.x == 0) flag_error(err, kErrRowsPerBlock);
     return;
   }
   const int64_t r0 = s_info.r0;
+  const int32_t t0 = s_info.t0;
   const int NB = nrows * nreq;
   for (int i = threadIdx.x; i < NB; i += kNT) {
     hist[i] = 0;
@@ -420,17 +424,24 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   }
   __syncthreads();
   // Entries with products that start inside the range (and t0, which holds
-  // the range's first element): B offset relative to the element index,
-  // a_ik and local row, stored at the entry's first element.
-  for (int32_t t = s_info.t0 + (int32_t)threadIdx.x; t <= s_info.t1; t += kNT) {
+  // the range's first element) mark their first element with their index
+  // j = t - t0; the first kXfEnt of them also leave their B offset relative
+  // to the element index, a_ik and local row in LDS (later ones are read
+  // from memory by their elements, which long tiles of very short entries
+  // only need).
+  for (int32_t t = t0 + (int32_t)threadIdx.x; t <= s_info.t1; t += kNT) {
     const int64_t o = src.eOff[t];
     if (src.eOff[t + 1] == o) continue;
     const int64_t from = o > e0 ? o : e0;
     const int64_t pos = from - e0;
     if (pos >= n) continue;
-    eRow[pos] = local_row(bnd, nrows, from);
-    eBase[pos] = (int32_t)((int64_t)src.eB[t] + e0 - o);
-    if constexpr (kVals) eA[pos] = ((const V*)src.eVal)[t];
+    const int j = t - t0;
+    slotAt[pos] = j;
+    if (j < kXfEnt) {
+      eRow[j] = local_row(bnd, nrows, from);
+      eBase[j] = (int32_t)((int64_t)src.eB[t] + e0 - o);
+      if constexpr (kVals) eA[j] = ((const V*)src.eVal)[t];
+    }
   }
   __syncthreads();
 
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int idx = it * kNT + threadIdx.x;
-    const bool head = idx < n && eRow[idx] >= 0;
+    const bool head = idx < n && slotAt[idx] >= 0;
     const uint64_t hm = __ballot(head);
     const int segBase = it * kNT + w * kWave;
     hp[it] = (hm & le) ? segBase + last_set64(hm & le) : -1;
@@ -465,17 +476,30 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   const int W = 1 << log2W;
   // Every lane loads (lanes past the range repeat element 0), so the loads
   // of all items are in flight together.
-  int32_t hh[ITEMS];
+  int32_t lrow[ITEMS];
   uint32_t bp[ITEMS];
+  V av[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int idx = it * kNT + threadIdx.x;
     // Segment 0 starts with the range's first entry, so every element of a
     // later segment without a start of its own finds one before it.
     const int sg = it * (kNT / kWave) + w - 1;
-    const int h = hp[it] >= 0 ? hp[it] : segLast[sg > 0 ? sg : 0];
-    hh[it] = idx < n ? h : 0;
-    bp[it] = (uint32_t)((idx < n ? idx : 0) + eBase[hh[it]]);
+    const int h = idx < n ? (hp[it] >= 0 ? hp[it] : segLast[sg > 0 ? sg : 0]) : 0;
+    const int j = slotAt[h];
+    int32_t eb;
+    if (j < kXfEnt) {
+      eb = eBase[j];
+      lrow[it] = eRow[j];
+      if constexpr (kVals) av[it] = eA[j];
+    } else {
+      const int32_t t = t0 + j;
+      const int64_t o = src.eOff[t];
+      eb = (int32_t)((int64_t)src.eB[t] + e0 - o);
+      lrow[it] = local_row(bnd, nrows, o > e0 ? o : e0);
+      if constexpr (kVals) av[it] = ((const V*)src.eVal)[t];
+    }
+    bp[it] = (uint32_t)((idx < n ? idx : 0) + eb);
   }
   int32_t cc[ITEMS];
   V xv[ITEMS];
@@ -488,8 +512,8 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     const int idx = it * kNT + threadIdx.x;
-    const int lr = eRow[hh[it]];
-    if constexpr (kVals) xv[it] *= eA[hh[it]];
+    const int lr = lrow[it];
+    if constexpr (kVals) xv[it] *= av[it];
     const int32_t slot = cc[it] >> log2W;
     const int sp = spanS[lr * nreq + slot];
     cc[it] &= (W << sp) - 1;
@@ -531,7 +555,7 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
     if (bb[it] >= 0) {
       const int64_t dest = gbase[bb[it]] + rank[it];
       if (dest < E) {
-        outCol[dest] = cc[it];
+        outCol[dest] = (OC)cc[it];
         if constexpr (kVals) outVal[dest] = xv[it];
       }
     }
@@ -550,9 +574,12 @@ void multisplit_set_attributes() {
   SG_ATTR(k_multisplit<kMsItemsF64, double, true, true>);
   SG_ATTR(k_multisplit<kMsItemsF32, float, true, true>);
   SG_ATTR(k_multisplit<kMsItemsF32, float, false, true>);
-  SG_ATTR(k_expand_final<kXfItemsF64, double, true>);
-  SG_ATTR(k_expand_final<kXfItemsF32, float, true>);
-  SG_ATTR(k_expand_final<kXfItemsF32, float, false>);
+  SG_ATTR((k_expand_final<kXfItemsF64, double, true, int32_t>));
+  SG_ATTR((k_expand_final<kXfItemsF32, float, true, int32_t>));
+  SG_ATTR((k_expand_final<kXfItemsF32, float, false, int32_t>));
+  SG_ATTR((k_expand_final<kXfItemsF64, double, true, uint16_t>));
+  SG_ATTR((k_expand_final<kXfItemsF32, float, true, uint16_t>));
+  SG_ATTR((k_expand_final<kXfItemsF32, float, false, uint16_t>));
 #undef SG_ATTR
 }
 
@@ -579,21 +606,28 @@ bool expand_final_geometry(bool f64, int64_t rowTau, int64_t nreq, int32_t* bloc
 void launch_expand_final(bool f64, int64_t E, int32_t blockElems, const int64_t* rowPtr,
                          const TileInfo* info, const ExpandSrc& src, const int32_t* finalOf,
                          const int8_t* spanOf, int32_t nreq, int log2W, int maxRows,
-                         int64_t* cursor, int32_t* outCol, void* outVal, int32_t* err,
+                         int64_t* cursor, void* outCol, bool col16, void* outVal, int32_t* err,
                          hipStream_t s) {
   if (E <= 0) return;
   const unsigned g = (grid_for(E, blockElems) + kXcds - 1) / kXcds * kXcds;
   const size_t NB = (size_t)maxRows * nreq;
   const size_t vb = !outVal ? 0 : f64 ? 8 : 4;
-  const size_t lds = NB * 13 + (size_t)maxRows * 8 + (size_t)blockElems * (vb + 8) + 16;
+  const size_t lds = NB * 13 + (size_t)maxRows * 8 + (size_t)kXfEnt * (vb + 8) +
+                     (size_t)blockElems * 4 + 16;
+#define SG_XF1(ITEMS, V, VALS, OC)                                                             \
+  hipLaunchKernelGGL((k_expand_final<ITEMS, V, VALS, OC>), dim3(g), dim3(kNT), lds, s, E,        \
+                     blockElems, rowPtr, info, src, finalOf, spanOf, nreq, log2W, maxRows,       \
+                     cursor, (OC*)outCol, (V*)outVal, err)
 #define SG_XF(ITEMS, V, VALS)                                                                  \
-  hipLaunchKernelGGL((k_expand_final<ITEMS, V, VALS>), dim3(g), dim3(kNT), lds, s, E, blockElems, \
-                     rowPtr, info, src, finalOf, spanOf, nreq, log2W, maxRows, cursor, outCol,  \
-                     (V*)outVal, err)
+  do {                                                                                         \
+    if (col16) SG_XF1(ITEMS, V, VALS, uint16_t);                                               \
+    else SG_XF1(ITEMS, V, VALS, int32_t);                                                      \
+  } while (0)
   if (!outVal) SG_XF(kXfItemsF32, float, false);
   else if (f64) SG_XF(kXfItemsF64, double, true);
   else SG_XF(kXfItemsF32, float, true);
 #undef SG_XF
+#undef SG_XF1
 }
 
 void launch_block_starts(int64_t nItems, const int64_t* off, int64_t G, int64_t nBlocks,
