@@ -63,6 +63,78 @@ __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const ChunkDesc*
   }
 }
 
+// Symbolic of the dense chunks: one persistent 1024-thread work group per
+// half CU walks its chunks, and the first batch of the next chunk's columns
+// (and its descriptor) is in flight while the current bitmap is counted and
+// cleared.
+constexpr int kSymPT = 1024;
+constexpr int kSymB = 8;  // columns per thread per batch
+template <typename C>
+__global__ __launch_bounds__(kSymPT) void k_sym_chunks_persist(const ChunkDesc* __restrict__ desc,
+                                                               int64_t n, int32_t words,
+                                                               ChunkList cl) {
+  extern __shared__ __align__(16) uint32_t bm[];
+  __shared__ int32_t gsum[kSymPT / kWave];
+  for (int i = threadIdx.x; i < words; i += kSymPT) bm[i] = 0;
+  int64_t ci = blockIdx.x;
+  ChunkDesc d{};
+  int32_t cc[kSymB];
+  const C* col = (const C*)cl.col0;
+  auto load = [&](int64_t e0, int64_t end) {
+#pragma unroll
+    for (int k = 0; k < kSymB; ++k) {
+      const int64_t e = e0 + (int64_t)k * kSymPT;
+      cc[k] = e < end ? (int32_t)col[e] : -1;
+    }
+  };
+  auto mark = [&]() {
+#pragma unroll
+    for (int k = 0; k < kSymB; ++k) {
+      const int32_t c = cc[k];
+      if (c >= 0) {
+        const uint32_t bit = 1u << (c & 31);
+        if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+      }
+    }
+  };
+  if (ci < n) {
+    d = desc[ci];
+    col = (const C*)(d.buf ? cl.col1 : cl.col0);
+    load(d.off + threadIdx.x, d.off + d.cnt);
+  }
+  __syncthreads();
+  while (ci < n) {
+    const int64_t off = d.off, end = off + d.cnt, slot = d.base;
+    const int64_t cn = ci + gridDim.x;
+    if (cn < n) d = desc[cn];
+    mark();
+    for (int64_t e0 = off + threadIdx.x + (int64_t)kSymPT * kSymB; e0 < end;
+         e0 += (int64_t)kSymPT * kSymB) {
+      load(e0, end);
+      mark();
+    }
+    __syncthreads();
+    if (cn < n) {
+      col = (const C*)(d.buf ? cl.col1 : cl.col0);
+      load(d.off + threadIdx.x, d.off + d.cnt);
+    }
+    int32_t mine = 0;
+    for (int i = threadIdx.x; i < words; i += kSymPT) {
+      mine += __popc(bm[i]);
+      bm[i] = 0;
+    }
+    mine = wave_sum(mine);
+    if (lane_id() == 0) gsum[threadIdx.x / kWave] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int32_t tot = 0;
+      for (int i = 0; i < kSymPT / kWave; ++i) tot += gsum[i];
+      cl.slotNnz[slot] = tot;
+    }
+    ci = cn;
+  }
+}
+
 template <typename V>
 __device__ __forceinline__ void hmap_add_mark(int32_t* keys, V* vals, uint32_t* bm, uint32_t T,
                                               int32_t key, V v, int32_t* err) {
@@ -292,6 +364,8 @@ void chunks_set_attributes() {
   SG_ATTR((k_sym_chunks_bitmap<64, 4, uint16_t>));
   SG_ATTR((k_sym_chunks_bitmap<256, 1, uint16_t>));
   SG_ATTR((k_sym_chunks_bitmap<1024, 1, uint16_t>));
+  SG_ATTR(k_sym_chunks_persist<int32_t>);
+  SG_ATTR(k_sym_chunks_persist<uint16_t>);
   SG_ATTR((k_num_chunks_rank<64, 4, float>));
   SG_ATTR((k_num_chunks_rank<64, 4, float, uint16_t>));
   SG_ATTR((k_num_chunks_rank<128, 2, float>));
@@ -406,6 +480,20 @@ void launch_sym_chunks_bitmap(int sizeClass, const ChunkDesc* desc, int64_t n, i
   else
     L(1024, 1, (unsigned)n, (size_t)words * 4);
 #undef L
+}
+
+void launch_sym_chunks_persist(const ChunkDesc* desc, int64_t n, int32_t words,
+                               const ChunkList& cl, int numCUs, hipStream_t s) {
+  if (n <= 0) return;
+  // Two 1024-thread work groups fill a CU's waves.
+  const unsigned g = (unsigned)std::min<int64_t>(n, (int64_t)std::max(numCUs, 1) * 2);
+  const size_t lds = (size_t)words * 4;
+  if (cl.col16)
+    hipLaunchKernelGGL(k_sym_chunks_persist<uint16_t>, dim3(g), dim3(kSymPT), lds, s, desc, n,
+                       words, cl);
+  else
+    hipLaunchKernelGGL(k_sym_chunks_persist<int32_t>, dim3(g), dim3(kSymPT), lds, s, desc, n,
+                       words, cl);
 }
 
 void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,

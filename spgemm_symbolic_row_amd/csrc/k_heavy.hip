@@ -234,10 +234,10 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
     }
     // Write-out in column order.  Wave w owns columns [w*W/16, (w+1)*W/16),
     // lane l a run of cpl of them; a wave scan of the lanes' popcounts gives
-    // every lane its output offset, and then output entries j, j+1, ... are
-    // written by consecutive lanes (each finds the lane and bit that hold
-    // entry j), so every store is fully coalesced.  The slot's value is
-    // cleared as it is read.
+    // every lane its output offset, and each lane then writes its own
+    // entries in column order, one per step (the wave's stores of a step
+    // fall in a short stretch of the output).  The slot's value is cleared
+    // as it is read.
     const int cpw = (W + kWaves - 1) / kWaves;        // columns per wave
     const int cpl = cpw >= kWave ? cpw / kWave : 1;   // columns per lane, <= 32
     const int lc0 = w * cpw + lane * cpl;             // this lane's first column
@@ -259,36 +259,19 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
       total += t;
     }
     if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
-    for (int32_t j0 = 0; j0 < nw; j0 += kWave) {
-      const int32_t j = j0 + lane;
-      // Lane holding entry j: the last lane whose exclusive offset is <= j.
-      int src = 0;
-#pragma unroll
-      for (int step = 32; step >= 1; step >>= 1) {
-        const int32_t o = __shfl(exclL, src + step);
-        if (o <= j) src += step;
-      }
-      const uint32_t m = __shfl(mask, src);
-      int32_t k = j - __shfl(exclL, src);
-      // Position of the k-th set bit of m: halve the window each step.
-      int bit = 0;
-#pragma unroll
-      for (int half = 16; half >= 1; half >>= 1) {
-        const int32_t lo = __popc((m >> bit) & ((1u << half) - 1u));
-        if (k >= lo) {
-          k -= lo;
-          bit += half;
-        }
-      }
-      const int c = w * cpw + src * cpl + bit;
-      if (j < nw) {
-        const int32_t p = wbase + j;
+    uint32_t m = mask;
+    int32_t p = wbase + exclL;
+    while (__ballot(m != 0)) {
+      if (m) {
+        const int c = lc0 + __ffs(m) - 1;
+        m &= m - 1;
         const V x = vals[c];
         vals[c] = V(0);
         if (p < want) {
           ccol[base + p] = colBase + c;
           cval[base + p] = x;
         }
+        ++p;
       }
     }
     __syncthreads();
