@@ -44,6 +44,8 @@ def algorithmic_bytes(st, phase, sv, si=4):
     fused = st["phase_windows"]["expand_split"] > 0
     E = sum(st["level_elems"][1:] if fused else st["level_elems"])
     batched = st["batches"] > 1
+    if phase in ("expand_final", "num_chunk_dense"):
+        si = st["chunk_col_bytes"] or si   # chunk-local 16-bit columns
     cv = (si + (si + sv)) if batched else (si + sv)   # bytes per element over both expansions
     if phase == "expand_split":
         return st["level_elems"][0] * cv, f"{cv} B written per heavy product (first-level chunks)"

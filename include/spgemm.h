@@ -176,6 +176,8 @@ typedef struct spgemm_stats {
                                  and one per batch and expansion)           */
   int64_t device_errors;      /* device status bits seen (0 when all is well)  */
   int64_t heavy_row_threshold; /* rows above this many products were heavy     */
+  int64_t chunk_col_bytes;    /* bytes of a column in the heavy intermediate:
+                                 2 when it holds chunk-local 16-bit columns */
 } spgemm_stats;
 
 typedef struct spgemm_plan_s *spgemm_plan_t;

@@ -64,7 +64,7 @@ class Stats(ctypes.Structure):
         ("ms_plan", ctypes.c_double), ("ms_symbolic", ctypes.c_double),
         ("ms_numeric", ctypes.c_double), ("phase_ms", ctypes.c_double * 16),
         ("phase_windows", c_i32 * 16), ("device_errors", c_i64),
-        ("heavy_row_threshold", c_i64),
+        ("heavy_row_threshold", c_i64), ("chunk_col_bytes", c_i64),
     ]
 
     def as_dict(self):

@@ -623,6 +623,7 @@ void do_plan(spgemm_plan_t p) {
   p->st.params = p->params;
   p->st.params.tau = p->tau;
   p->st.heavy_row_threshold = p->rowTau;
+  p->st.chunk_col_bytes = 4;
   p->xheavy = p->rowOrder + p->rowBinStart[p->NS + 1];
   p->nreq = p->params.chunks_required;
   p->st.ms_plan = now_ms() - t0;
@@ -710,6 +711,7 @@ void heavy_prepare(spgemm_plan_t p) {
   // Straight into final chunks at most 65536 columns wide, a local column
   // takes two bytes.
   p->col16 = p->direct && p->params.level_width[0] <= 65536;
+  p->st.chunk_col_bytes = p->col16 ? 2 : 4;
   const int64_t nbuf = heavy_nbuf(p);
   // Numeric needs columns and values.  If that takes one batch, symbolic
   // expands with values and numeric reuses the result; otherwise symbolic
