@@ -115,7 +115,15 @@ typedef struct spgemm_options {
                                    numeric LDS table (2 slots per product)
                                    leaves room for three work groups per CU.
                                    Chunks keep tau (recursion, bins).        */
-  int64_t reserved[7];
+  int32_t light_hash_only;      /* 1: every light row takes the LDS hash
+                                   accumulator; 0 (default): a light row whose
+                                   products span at most 128 x its bin's
+                                   product bound columns (at most 65536) takes
+                                   the dense window: an LDS bitmap over the
+                                   span, ranks by prefix popcount, values
+                                   added at their rank (no hash, no sort)    */
+  int32_t reserved32;
+  int64_t reserved[6];
 } spgemm_options;
 
 /* Parameters chosen by GetMagnusParams (gMAGNUS §III-D, Eq. 4-7). */

@@ -35,7 +35,7 @@ class Options(ctypes.Structure):
         ("validate", c_i32), ("single_stream", c_i32), ("profile", c_i32),
         ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
         ("alloc_ctx", c_vp), ("expansion", c_i32), ("heavy_row_threshold", c_i32),
-        ("reserved", c_i64 * 7),
+        ("light_hash_only", c_i32), ("reserved32", c_i32), ("reserved", c_i64 * 6),
     ]
 
 

@@ -248,10 +248,14 @@ struct spgemm_plan_s {
   std::vector<BinCfg> symBins, numBins, rankBins;
   int32_t chunkWords = 0;  // bitmap words of the widest final chunk (0: hash fallback)
   int NS = 0;  // number of hash bins
+  int winBins = 0;  // leading light bins whose rows may take the dense window
   // device arrays
   int32_t *dSymCaps = nullptr;
   int64_t *rowP = nullptr, *cnt = nullptr, *stats = nullptr, *cRowOff = nullptr, *scanTmp = nullptr;
   int32_t *scanA = nullptr, *rowOrder = nullptr, *numOrder = nullptr, *errWord = nullptr;
+  int64_t* rowWin = nullptr;  // dense-window rows: first column and span words
+  int32_t* winMax = nullptr;  // widest window of each light bin, in words
+  std::vector<int32_t> winWords;
   int32_t *binCnt = nullptr, *binFill = nullptr, *binStart = nullptr;
   uint8_t *rowBin = nullptr, *numKey = nullptr;
   // pinned host mirrors
@@ -495,7 +499,7 @@ int32_t read_err(spgemm_plan_t p, hipStream_t s) {
 }
 
 RowArgs row_args(spgemm_plan_t p) {
-  return RowArgs{p->arp, p->acol, p->aval, p->brp, p->bcol, p->bval, p->scanA, p->rowP};
+  return RowArgs{p->arp, p->acol, p->aval, p->brp, p->bcol, p->bval, p->scanA, p->rowP, p->rowWin};
 }
 
 // ------------------------------------------------------------------ plan
@@ -532,7 +536,15 @@ void do_plan(spgemm_plan_t p) {
   if (p->opts.mem_budget < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "mem_budget must be >= 0"};
   make_bins(p->tau, p->lds, vb, &p->symBins, &p->numBins);
   p->NS = (int)p->symBins.size();
-  if (p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
+  if (2 * p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
+  // Dense windows for light rows unless turned off or a bin's window does
+  // not fit the LDS budget.
+  p->winBins = 0;
+  if (!p->opts.light_hash_only)
+    while (p->winBins < p->NS &&
+           (int64_t)window_row_lds(true, p->f64, p->symBins[p->winBins],
+                                   window_words(p->symBins[p->winBins].cap)) <= p->lds)
+      ++p->winBins;
 
   static bool attrs = false;
   if (!attrs) {
@@ -597,6 +609,11 @@ void do_plan(spgemm_plan_t p) {
   p->cnt = alloc_n<int64_t>(p, m, s);
   p->scanA = alloc_n<int32_t>(p, p->nnzA, s);
   p->rowBin = alloc_n<uint8_t>(p, m, s);
+  if (p->winBins) {
+    p->rowWin = alloc_n<int64_t>(p, m, s);
+    p->winMax = alloc_n<int32_t>(p, 64, s);
+    launch_fill_i32(p->winMax, 0, 64, s);
+  }
   p->rowOrder = alloc_n<int32_t>(p, m, s);
   p->binCnt = alloc_n<int32_t>(p, 64, s);
   p->binFill = alloc_n<int32_t>(p, 64, s);
@@ -604,16 +621,27 @@ void do_plan(spgemm_plan_t p) {
   launch_fill_i64(p->cnt, 0, m, s);
   const int ph = ph_begin(p, SPGEMM_PH_ROW_INFO, s);
   int64_t* part = alloc_n<int64_t>(p, row_info_partials(m), s);
-  launch_row_info(m, p->arp, p->acol, p->brp, p->bcol, p->rowTau, p->dSymCaps, p->NS, p->rowP,
-                  p->scanA, p->rowBin, part, p->stats, s);
-  const int nkeys = p->NS + 2;  // 0 empty, 1..NS hash bins, NS+1 heavy
+  int2* bSpan = nullptr;
+  if (p->winBins) {
+    bSpan = alloc_n<int2>(p, std::max<int64_t>(p->k, 1), s);
+    launch_b_span(p->k, p->brp, p->bcol, bSpan, s);
+  }
+  launch_row_info(m, p->arp, p->acol, p->brp, bSpan, p->rowTau, p->dSymCaps, p->NS, p->rowP,
+                  p->scanA, p->rowBin, p->rowWin, p->winBins, p->winMax, part, p->stats, s);
+  // 0 empty, 1..NS hash bins, NS+1 heavy, NS+2..2NS+1 dense-window bins
+  const int nkeys = 2 * p->NS + 2;
   launch_bin_sort(p->rowBin, m, nkeys, p->binCnt, p->binFill, p->binStart, p->rowOrder, s);
   ph_end(p, ph, s);
   check_launch("plan kernels");
   HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (nkeys + 1), hipMemcpyDeviceToHost, s));
+  if (p->winBins)
+    HIP_CHECK(hipMemcpyAsync(p->hBins + 64, p->winMax, sizeof(int32_t) * p->NS,
+                             hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
   p->rowBinStart.assign(p->hBins, p->hBins + nkeys + 1);
+  p->winWords.assign(p->NS, 0);
+  if (p->winBins) std::copy(p->hBins + 64, p->hBins + 64 + p->NS, p->winWords.begin());
   p->st.products = p->hStats[kStatProducts];
   p->st.heavy_products = p->Ph = p->hStats[kStatHeavyProducts];
   p->st.heavy_a_nnz = p->nAh = p->hStats[kStatHeavyANnz];
@@ -1143,6 +1171,10 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
     launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
+    const int64_t ws = p->rowBinStart[p->NS + 2 + b], we = p->rowBinStart[p->NS + 3 + b];
+    if (we > ws)
+      launch_sym_rows_win(p->symBins[b], p->winWords[b], p->rowOrder + ws, we - ws, a, p->cnt,
+                          p->sl);
   }
   ph_end(p, phL, p->sl);
   check_launch("light symbolic");
@@ -1157,16 +1189,16 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   const int phR = ph_begin(p, SPGEMM_PH_ROWPTR, s);
   launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
   launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s);
-  launch_bin_sort(p->numKey, m, p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
+  launch_bin_sort(p->numKey, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
   ph_end(p, phR, s);
   check_launch("row pointer scan");
   HIP_CHECK(hipMemcpyAsync(p->hStats + 20, p->cRowOff + m, 8, hipMemcpyDeviceToHost, s));
-  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (p->NS + 1), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (2 * p->NS + 1), hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hBins + 120, p->errWord, 4, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
   check_device_errors(p, p->hBins[120]);
-  p->numBinStart.assign(p->hBins, p->hBins + p->NS + 1);
+  p->numBinStart.assign(p->hBins, p->hBins + 2 * p->NS + 1);
   p->nnzC = p->hStats[20];
   p->st.nnz_c = p->nnzC;
   p->st.lds_dense_products = p->hStats[kStatDenseElems];
@@ -1189,6 +1221,10 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
     const int64_t st = p->numBinStart[b], en = p->numBinStart[b + 1];
     launch_num_rows(p->numBins[b], p->f64, p->numOrder + st, en - st, a, p->cRowOff, ccol, cval,
                     p->errWord, p->sl);
+    const int64_t ws = p->numBinStart[p->NS + b], we = p->numBinStart[p->NS + b + 1];
+    if (we > ws)
+      launch_num_rows_win(p->symBins[b], p->winWords[b], p->f64, p->numOrder + ws, we - ws, a,
+                          p->cRowOff, ccol, cval, p->errWord, p->sl);
   }
   ph_end(p, phL, p->sl);
   check_launch("light numeric");

@@ -52,7 +52,21 @@ struct RowArgs {
   const void* bval;
   const int32_t* scanA;  // row-local exclusive product offset of each A entry
   const int64_t* rowP;   // products per row
+  const int64_t* rowWin; // dense-window rows: first product column (low 32
+                         // bits) and span in 32-bit words (high bits)
 };
+
+// Dense window of a light row (gMAGNUS page §III-E: any local-memory
+// accumulator; Ocean page §2: hash-based and dense accumulators chosen per
+// row): a row whose products span at most 32 * window_words(cap) columns,
+// cap being its bin's product bound, is accumulated in an LDS bitmap over
+// [lo, lo + 32 * words) and a dense array indexed by bitmap rank instead of a
+// hash table.  The bitmap (16 bytes per product of the bin's bound) stays
+// within a small multiple of the hash table it replaces, and at most 65536
+// columns wide.
+__host__ __device__ inline int32_t window_words(int64_t cap) {
+  return (int32_t)(4 * cap < 2048 ? 4 * cap : 2048);
+}
 
 // Final chunks of the heavy rows, in the order they were listed.  Chunk c
 // holds cnt[c] elements at off[c] of buffer buf[c]; it belongs to heavy row
@@ -111,10 +125,19 @@ void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int
                      int32_t* start, int32_t* out, hipStream_t s);
 // Scratch entries (int64) launch_row_info needs for its per-work-group partials.
 int64_t row_info_partials(int64_t m);
+// rowWin (null: no window bins) receives, for light rows of the first
+// winBins bins whose products fit their bin's window, the span's first
+// column and its length in 32-bit words (see RowArgs); those rows get bin
+// nbins + 2 + b instead of 1 + b; winMax[b] (zeroed by the caller) receives
+// the widest window of bin b in words.
+// bSpan: first and last column of every B row (launch_b_span), needed with
+// rowWin.
+void launch_b_span(int64_t K, const int32_t* brp, const int32_t* bcol, int2* span, hipStream_t s);
 void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
-                     const int32_t* bcol, int64_t tau, const int32_t* caps, int nbins,
-                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* part,
-                     int64_t* stats, hipStream_t s);
+                     const int2* bSpan, int64_t tau, const int32_t* caps, int nbins,
+                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* rowWin,
+                     int winBins, int32_t* winMax, int64_t* part, int64_t* stats,
+                     hipStream_t s);
 void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,
                      const int32_t* col, int32_t* err, hipStream_t s);
 void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hipStream_t s);
@@ -131,6 +154,15 @@ void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBi
 
 // ---- k_light.hip ----
 void light_set_attributes();
+// Dense-window light rows (window_words(b.cap) bitmap words per row); LDS
+// bytes per work group of the symbolic or numeric kernel.
+// `words`: the widest window among the rows (at most window_words(b.cap)).
+size_t window_row_lds(bool numeric, bool f64, const BinCfg& b, int32_t words);
+void launch_sym_rows_win(const BinCfg& b, int32_t words, const int32_t* rows, int64_t nrows,
+                         const RowArgs& a, int64_t* cnt, hipStream_t s);
+void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t* rows,
+                         int64_t nrows, const RowArgs& a, const int64_t* cRowOff, int32_t* ccol,
+                         void* cval, int32_t* err, hipStream_t s);
 void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
                      int64_t* cnt, int32_t* err, hipStream_t s);
 void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,

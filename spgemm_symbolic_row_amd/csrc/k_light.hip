@@ -20,8 +20,9 @@ constexpr int kMaxSpt = 24;  // slots per thread held in registers by the compac
 // flattened product index q of entry e starts at scanA[e] (row-local
 // exclusive offset).  The wave keeps 64 consecutive A entries in registers,
 // finds for each of 64 consecutive products the entry that owns it with a
-// 6-step binary search across lanes, and hands f(act, b, a) the index b of
-// the B element and the A value.  Every lane runs the same iterations.
+// 6-step binary search across lanes, and hands f(act, b, a, q) the index b of
+// the B element, the A value and the product index q.  Every lane runs the
+// same iterations.
 template <bool VAL, typename V, typename F>
 __device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
                                            const int32_t* __restrict__ acol,
@@ -57,7 +58,7 @@ __device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
       const int32_t sb = __shfl(bs, s);
       V sa = V(0);
       if (VAL) sa = __shfl(a, s);
-      f(act, sb + (q - so), sa);
+      f(act, sb + (q - so), sa, q);
     }
     p = bend;
     j += kWave;
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows(const int32_t* __restrict
     const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
     const int32_t* __restrict__ bcol = a.bcol;
     stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, rs, re, P, p0, p1,
-                             [&](bool act, int32_t b, float) {
+                             [&](bool act, int32_t b, float, int32_t) {
                                if (act && hset_insert(keys, (uint32_t)T, bcol[b], err)) ++mine;
                              });
   }
@@ -128,6 +129,167 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_chunks(const ChunkDesc* __rest
   if (lane_id() == 0 && ri < n) atomicAdd(&gcount[g], ws);
   __syncthreads();
   if (t == 0 && ri < n) cl.slotNnz[d.base] = gcount[g];
+}
+
+// ------------------------------------------------------- dense window rows
+// Light rows whose products span at most 32 * window_words(cap) columns:
+// rowWin[row] holds the span's first column (low 32 bits) and its length in
+// 32-bit words (high bits), and an LDS bitmap over the span replaces the
+// hash table.  Symbolic counts its set bits.  Numeric stages every product's
+// (column, value) in LDS by product index while setting the bits, takes the
+// word prefix of the popcounts (the rank of a column among the row's columns
+// is its output position), then adds each staged product straight into an
+// LDS array of the row's exact output size: no probing and no sort, and the
+// row is written in column order.
+__device__ __forceinline__ int32_t win_lo(int64_t w) { return (int32_t)(uint32_t)(w & 0xffffffff); }
+__device__ __forceinline__ int32_t win_words(int64_t w) { return (int32_t)(w >> 32); }
+
+template <int TPR, int RPB>
+__global__ __launch_bounds__(TPR* RPB) void k_sym_rows_win(const int32_t* __restrict__ rows,
+                                                           int64_t nrows, int32_t words, RowArgs a,
+                                                           int64_t* __restrict__ cnt) {
+  extern __shared__ __align__(16) uint32_t bmAll[];
+  constexpr int WPR = TPR / kWave;
+  __shared__ int32_t gsum[RPB * WPR];
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR, w = t / kWave;
+  uint32_t* bm = bmAll + g * words;
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t row = 0, lo = 0, nw = 0;
+  if (ri < nrows) {
+    row = rows[ri];
+    const int64_t win = a.rowWin[row];
+    lo = win_lo(win);
+    nw = win_words(win);
+  }
+  for (int i = t; i < nw; i += TPR) bm[i] = 0;
+  __syncthreads();
+  if (ri < nrows) {
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t P = (int32_t)a.rowP[row];
+    const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
+    const int32_t* __restrict__ bcol = a.bcol;
+    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, rs, re, P, p0, p1,
+                             [&](bool act, int32_t b, float, int32_t) {
+                               if (act) {
+                                 const int32_t c = bcol[b] - lo;
+                                 const uint32_t bit = 1u << (c & 31);
+                                 if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+                               }
+                             });
+  }
+  __syncthreads();
+  int32_t mine = 0;
+  for (int i = t; i < nw; i += TPR) mine += __popc(bm[i]);
+  mine = wave_sum(mine);
+  if (lane_id() == 0) gsum[threadIdx.x / kWave] = mine;
+  __syncthreads();
+  if (t == 0 && ri < nrows) {
+    int32_t tot = 0;
+    for (int i = 0; i < WPR; ++i) tot += gsum[g * WPR + i];
+    cnt[row] = tot;
+  }
+}
+
+// LDS per row: vals[cap] V | pv[cap] V | bm[words] | wpre[words] |
+// cols[cap] u16 | pc[cap] u16.
+__host__ __device__ constexpr size_t window_group_bytes(int32_t cap, int32_t words, int vb) {
+  return ((size_t)cap * (2 * vb + 4) + (size_t)words * 8 + 15) / 16 * 16;
+}
+
+template <int TPR, int RPB, typename V>
+__global__ __launch_bounds__(TPR* RPB) void k_num_rows_win(const int32_t* __restrict__ rows,
+                                                           int64_t nrows, int32_t words,
+                                                           int32_t cap, RowArgs a,
+                                                           const int64_t* __restrict__ cRowOff,
+                                                           int32_t* __restrict__ ccol,
+                                                           V* __restrict__ cval,
+                                                           int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int WPR = TPR / kWave;
+  __shared__ int32_t wtot[RPB * WPR];
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR, w = t / kWave;
+  unsigned char* base = smem + (size_t)g * window_group_bytes(cap, words, (int)sizeof(V));
+  V* vals = (V*)base;
+  V* pv = vals + cap;
+  uint32_t* bm = (uint32_t*)(pv + cap);
+  int32_t* wpre = (int32_t*)(bm + words);
+  uint16_t* cols = (uint16_t*)(wpre + words);
+  uint16_t* pc = cols + cap;
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t row = 0, lo = 0, nw = 0, P = 0, want = 0;
+  int64_t obase = 0;
+  if (ri < nrows) {
+    row = rows[ri];
+    const int64_t win = a.rowWin[row];
+    lo = win_lo(win);
+    nw = win_words(win);
+    P = (int32_t)a.rowP[row];
+    if (P > cap) P = cap;
+    obase = cRowOff[row];
+    const int64_t wn = cRowOff[row + 1] - obase;
+    want = (int32_t)(wn < cap ? wn : cap);
+  }
+  for (int i = t; i < nw; i += TPR) bm[i] = 0;
+  for (int i = t; i < want; i += TPR) vals[i] = V(0);
+  __syncthreads();
+  if (ri < nrows) {
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
+    const int32_t* __restrict__ bcol = a.bcol;
+    const V* __restrict__ bval = (const V*)a.bval;
+    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, rs, re, P, p0, p1,
+                        [&](bool act, int32_t b, V av, int32_t q) {
+                          if (act) {
+                            const int32_t c = bcol[b] - lo;
+                            pc[q] = (uint16_t)c;
+                            pv[q] = av * bval[b];
+                            const uint32_t bit = 1u << (c & 31);
+                            if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+                          }
+                        });
+  }
+  __syncthreads();
+  // Exclusive prefix of the word popcounts: each thread owns a contiguous
+  // run of words.
+  const int wpt = (nw + TPR - 1) / TPR;
+  const int w0 = t * wpt;
+  int32_t mine = 0;
+  for (int i = 0; i < wpt; ++i)
+    if (w0 + i < nw) mine += __popc(bm[w0 + i]);
+  const int32_t inc = wave_incl_scan(mine);
+  if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = inc;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < WPR; ++i) {
+    const int32_t tv = wtot[g * WPR + i];
+    if (i < w) before += tv;
+    total += tv;
+  }
+  int32_t run = before + inc - mine;
+  for (int i = 0; i < wpt; ++i) {
+    if (w0 + i < nw) {
+      wpre[w0 + i] = run;
+      run += __popc(bm[w0 + i]);
+    }
+  }
+  __syncthreads();
+  if (ri < nrows && t == 0 && total != want) flag_error(err, kErrCountMismatch);
+  for (int q = t; q < P; q += TPR) {
+    const int32_t c = pc[q];
+    const int32_t r = wpre[c >> 5] + __popc(bm[c >> 5] & ((1u << (c & 31)) - 1u));
+    if (r < want) {
+      atomicAdd(&vals[r], pv[q]);
+      cols[r] = (uint16_t)c;
+    }
+  }
+  __syncthreads();
+  for (int r = t; r < want; r += TPR) {
+    ccol[obase + r] = lo + cols[r];
+    cval[obase + r] = vals[r];
+  }
 }
 
 // ----------------------------------------------------------------- numeric
@@ -298,7 +460,7 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
     const int32_t* __restrict__ bcol = a.bcol;
     const V* __restrict__ bval = (const V*)a.bval;
     stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, rs, re, P, p0, p1,
-                        [&](bool act, int32_t b, V av) {
+                        [&](bool act, int32_t b, V av, int32_t) {
                           if (act) hmap_add(keys, vals, (uint32_t)T, bcol[b], av * bval[b], err);
                         });
   }
@@ -393,6 +555,21 @@ void light_set_attributes() {
   set_lds_attr(k_sym_chunks<256, 1>);
   set_lds_attr(k_sym_chunks<512, 1>);
   set_lds_attr(k_sym_chunks<1024, 1>);
+  set_lds_attr(k_sym_rows_win<64, 4>);
+  set_lds_attr(k_sym_rows_win<128, 2>);
+  set_lds_attr(k_sym_rows_win<256, 1>);
+  set_lds_attr(k_sym_rows_win<512, 1>);
+  set_lds_attr(k_sym_rows_win<1024, 1>);
+  set_lds_attr(k_num_rows_win<64, 4, float>);
+  set_lds_attr(k_num_rows_win<128, 2, float>);
+  set_lds_attr(k_num_rows_win<256, 1, float>);
+  set_lds_attr(k_num_rows_win<512, 1, float>);
+  set_lds_attr(k_num_rows_win<1024, 1, float>);
+  set_lds_attr(k_num_rows_win<64, 4, double>);
+  set_lds_attr(k_num_rows_win<128, 2, double>);
+  set_lds_attr(k_num_rows_win<256, 1, double>);
+  set_lds_attr(k_num_rows_win<512, 1, double>);
+  set_lds_attr(k_num_rows_win<1024, 1, double>);
   set_lds_attr(k_sym_chunks<64, 4, uint16_t>);
   set_lds_attr(k_sym_chunks<128, 2, uint16_t>);
   set_lds_attr(k_sym_chunks<256, 1, uint16_t>);
@@ -447,6 +624,42 @@ void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const 
 #define L(TPR, RPB)                                                                         \
   hipLaunchKernelGGL((k_sym_rows<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, nrows, \
                      b.T, a, cnt, err)
+  SG_DISPATCH_TPR(b, L)
+#undef L
+}
+
+size_t window_row_lds(bool numeric, bool f64, const BinCfg& b, int32_t words) {
+  if (!numeric) return (size_t)b.rpb * words * 4;
+  return (size_t)b.rpb * window_group_bytes(b.cap, words, f64 ? 8 : 4);
+}
+
+void launch_sym_rows_win(const BinCfg& b, int32_t words, const int32_t* rows, int64_t nrows,
+                         const RowArgs& a, int64_t* cnt, hipStream_t s) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
+  const size_t lds = window_row_lds(false, false, b, words);
+#define L(TPR, RPB)                                                                         \
+  hipLaunchKernelGGL((k_sym_rows_win<TPR, RPB>), dim3(grid), dim3(TPR * RPB), lds, s, rows,  \
+                     nrows, words, a, cnt)
+  SG_DISPATCH_TPR(b, L)
+#undef L
+}
+
+void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t* rows,
+                         int64_t nrows, const RowArgs& a, const int64_t* cRowOff, int32_t* ccol,
+                         void* cval, int32_t* err, hipStream_t s) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
+  const size_t lds = window_row_lds(true, f64, b, words);
+#define L(TPR, RPB)                                                                           \
+  do {                                                                                       \
+    if (f64)                                                                                 \
+      hipLaunchKernelGGL((k_num_rows_win<TPR, RPB, double>), dim3(grid), dim3(TPR * RPB), lds, \
+                         s, rows, nrows, words, b.cap, a, cRowOff, ccol, (double*)cval, err);  \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_num_rows_win<TPR, RPB, float>), dim3(grid), dim3(TPR * RPB), lds,  \
+                         s, rows, nrows, words, b.cap, a, cRowOff, ccol, (float*)cval, err);   \
+  } while (0);
   SG_DISPATCH_TPR(b, L)
 #undef L
 }

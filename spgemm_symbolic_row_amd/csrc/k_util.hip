@@ -1,6 +1,8 @@
 // Utility kernels: fills, device-wide exclusive scan, counting sort by bin,
 // the per-row intermediate-product pass (InterOffsets of gMAGNUS Algorithm 3,
 // §III-A), CSR validation and row-pointer output.
+#include <climits>
+
 #include "device_common.hpp"
 
 namespace sg {
@@ -193,26 +195,40 @@ __global__ __launch_bounds__(kNT) void k_bin_scatter(const uint8_t* __restrict__
 template <int G>
 __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __restrict__ arp,
                                                   const int32_t* __restrict__ acol,
-                                                  const int32_t* __restrict__ brp, int64_t tau,
+                                                  const int32_t* __restrict__ brp,
+                                                  const int2* __restrict__ bSpan, int64_t tau,
                                                   const int32_t* __restrict__ caps, int nbins,
                                                   int64_t* __restrict__ rowP,
                                                   int32_t* __restrict__ scanA,
                                                   uint8_t* __restrict__ rowBin,
+                                                  int64_t* __restrict__ rowWin, int winBins,
+                                                  int32_t* __restrict__ winMax,
                                                   int64_t* __restrict__ part) {
-  __shared__ unsigned long long sP, sPh, sAh, sMax, sH, sL;
-  if (threadIdx.x == 0) sP = sPh = sAh = sMax = sH = sL = 0;
+  __shared__ unsigned long long sP, sPh, sAh, sMax, sH, sL, sW;
+  __shared__ int32_t sWm[64];
+  if (threadIdx.x == 0) sP = sPh = sAh = sMax = sH = sL = sW = 0;
+  if (threadIdx.x < 64) sWm[threadIdx.x] = 0;
   __syncthreads();
   const int gl = threadIdx.x % G;
   const int64_t rowsPerPass = (int64_t)gridDim.x * (kNT / G);
   for (int64_t row = ((int64_t)blockIdx.x * kNT + threadIdx.x) / G; row < m; row += rowsPerPass) {
     const int64_t rs = arp[row], re = arp[row + 1];
     int64_t p = 0;
+    // Span of the row's products: first column of its first-starting B row
+    // to last column of its last-ending one (B rows are sorted).
+    int32_t lo = INT_MAX, hi = -1;
     for (int64_t b = rs; b < re; b += G) {
       const int64_t j = b + gl;
       int64_t nb = 0;
       if (j < re) {
         const int32_t k = acol[j];
-        nb = (int64_t)brp[k + 1] - brp[k];
+        const int32_t b0 = brp[k], b1 = brp[k + 1];
+        nb = (int64_t)b1 - b0;
+        if (rowWin && nb > 0) {
+          const int2 sp = bSpan[k];
+          lo = sp.x < lo ? sp.x : lo;
+          hi = sp.y > hi ? sp.y : hi;
+        }
       }
       int64_t inc = nb;
 #pragma unroll
@@ -222,6 +238,14 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
       }
       if (j < re) scanA[j] = (int32_t)(p + inc - nb);
       p += __shfl(inc, G - 1, G);
+    }
+    if (rowWin) {
+#pragma unroll
+      for (int d = 1; d < G; d <<= 1) {
+        const int32_t l2 = __shfl_xor(lo, d, G), h2 = __shfl_xor(hi, d, G);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+      }
     }
     if (gl == 0) {
       rowP[row] = p;
@@ -237,6 +261,13 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
         int b = 0;
         while (b < nbins - 1 && p > caps[b]) ++b;
         bin = (uint8_t)(1 + b);
+        const int64_t span = (int64_t)hi - lo + 1;
+        if (b < winBins && span <= 32 * (int64_t)window_words(caps[b])) {
+          bin = (uint8_t)(nbins + 2 + b);
+          rowWin[row] = ((span + 31) / 32) << 32 | (int64_t)(uint32_t)lo;
+          atomicMax(&sWm[b], (int32_t)((span + 31) / 32));
+          atomicAdd(&sW, (unsigned long long)p);
+        }
         atomicAdd(&sL, 1ull);
       }
       rowBin[row] = bin;
@@ -253,7 +284,21 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
     q[kStatMaxRowProducts] = (int64_t)sMax;
     q[kStatHeavyRows] = (int64_t)sH;
     q[kStatLightRows] = (int64_t)sL;
+    q[kStatDenseElems] = (int64_t)sW;
   }
+  // Widest window of each bin, for the LDS the window kernels reserve.
+  if (threadIdx.x < winBins && sWm[threadIdx.x] > 0)
+    atomicMax(&winMax[threadIdx.x], sWm[threadIdx.x]);
+}
+
+// First and last column of every B row (rows are sorted).
+__global__ __launch_bounds__(kNT) void k_b_span(int64_t K, const int32_t* __restrict__ brp,
+                                                const int32_t* __restrict__ bcol,
+                                                int2* __restrict__ span) {
+  const int64_t k = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (k >= K) return;
+  const int32_t b0 = brp[k], b1 = brp[k + 1];
+  span[k] = b1 > b0 ? make_int2(bcol[b0], bcol[b1 - 1]) : make_int2(INT_MAX, -1);
 }
 
 // One work group folds the nb partials of k_row_info into stats (added to
@@ -261,9 +306,9 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
 __global__ __launch_bounds__(kNT) void k_row_stats(int64_t nb, const int64_t* __restrict__ part,
                                                    int64_t* __restrict__ stats) {
   __shared__ int64_t red[kNT / kWave];
-  const int ids[6] = {kStatProducts, kStatHeavyProducts, kStatHeavyANnz, kStatMaxRowProducts,
-                      kStatHeavyRows, kStatLightRows};
-  for (int q = 0; q < 6; ++q) {
+  const int ids[7] = {kStatProducts, kStatHeavyProducts, kStatHeavyANnz, kStatMaxRowProducts,
+                      kStatHeavyRows, kStatLightRows, kStatDenseElems};
+  for (int q = 0; q < 7; ++q) {
     const int id = ids[q];
     const bool isMax = id == kStatMaxRowProducts;
     int64_t x = 0;
@@ -332,6 +377,10 @@ __global__ __launch_bounds__(kNT) void k_numeric_row_bins(int64_t m, const int64
   const int rb = rowBin[i];
   if (rb == 0 || rb == heavyBin) {
     key[i] = 255;
+    return;
+  }
+  if (rb > heavyBin) {  // dense window rows: bin by products, after the hash bins
+    key[i] = (uint8_t)(nbins + rb - heavyBin - 1);
     return;
   }
   const int64_t c = cnt[i];
@@ -413,16 +462,22 @@ int64_t row_info_partials(int64_t m) {
 }
 
 void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
-                     const int32_t* /*bcol*/, int64_t tau, const int32_t* caps, int nbins,
-                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* part,
-                     int64_t* stats, hipStream_t s) {
+                     const int2* bSpan, int64_t tau, const int32_t* caps, int nbins,
+                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* rowWin,
+                     int winBins, int32_t* winMax, int64_t* part, int64_t* stats,
+                     hipStream_t s) {
   if (m <= 0) return;
   constexpr int G = 16;
   unsigned g = grid_for(m * G, kNT);
   if (g > 65535) g = 65535;
-  hipLaunchKernelGGL(k_row_info<G>, dim3(g), dim3(kNT), 0, s, m, arp, acol, brp, tau, caps, nbins,
-                     rowP, scanA, rowBin, part);
+  hipLaunchKernelGGL(k_row_info<G>, dim3(g), dim3(kNT), 0, s, m, arp, acol, brp, bSpan, tau, caps,
+                     nbins, rowP, scanA, rowBin, rowWin, rowWin ? winBins : 0, winMax, part);
   hipLaunchKernelGGL(k_row_stats, dim3(1), dim3(kNT), 0, s, (int64_t)g, part, stats);
+}
+
+void launch_b_span(int64_t K, const int32_t* brp, const int32_t* bcol, int2* span, hipStream_t s) {
+  if (K <= 0) return;
+  hipLaunchKernelGGL(k_b_span, dim3(grid_for(K, kNT)), dim3(kNT), 0, s, K, brp, bcol, span);
 }
 
 void launch_validate(int64_t rows, int64_t cols, int64_t nnz, const int32_t* rp,

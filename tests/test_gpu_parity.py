@@ -122,6 +122,35 @@ def test_wide_light_rows_all_bins():
     assert st["heavy_rows"] == 0 or st["heavy_products"] > 0
 
 
+# ------------------------------------------------ dense-window light rows
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("m,n,per_row,band,seed", [
+    (3000, 3000, 3.0, 40, 21),      # small bins, narrow spans
+    (2000, 2500, 14.0, 300, 22),    # middle bins
+    (1500, 60000, 40.0, 1000, 23),  # large bins, spans up to a few thousand columns
+    (2500, 200000, 10.0, None, 24), # unbanded: spans too wide, the hash path
+])
+def test_dense_window_rows_match_hash(m, n, per_row, band, seed, dtype):
+    # Light rows whose products span a narrow window take the LDS bitmap +
+    # rank accumulator; turning it off must give the same C, and both the
+    # oracle's.
+    A = synth.random_csr(m, m, per_row, seed, values="int", empty_row_frac=0.1, dtype=dtype,
+                         banded=band)
+    B = synth.random_csr(m, n, per_row, seed + 50, values="int", empty_row_frac=0.1,
+                         dtype=dtype, banded=None if band is None else band * n // m)
+    st = check_full(A, B, exact=True)
+    rp, col, val, st_h = gpu_product(A, B, light_hash_only=1)
+    rp_w, col_w, val_w, _ = gpu_product(A, B)
+    np.testing.assert_array_equal(rp, rp_w)
+    np.testing.assert_array_equal(col, col_w)
+    np.testing.assert_array_equal(val, val_w)
+    assert st_h["lds_dense_products"] == 0
+    if band is not None:
+        assert st["lds_dense_products"] > 0
+    else:
+        assert st["lds_dense_products"] == 0
+
+
 # -------------------------------------------------- heavy path, forced sizes
 @pytest.mark.parametrize("scale,tau,W,nmax", [
     (10, 64, 256, 32),     # one level, 4 chunks
@@ -266,6 +295,9 @@ def test_laplacian_config_exact():
     A = synth.workload("lap27_64")
     st = check_full(A, A, exact=True)
     assert st["products"] == 566 ** 3 and st["nnz_c"] == 314 ** 3 and st["heavy_rows"] == 0
+    # every row's products span at most 2 * (2 + 2*64 + 2*4096) + 1 columns:
+    # all of them take the dense window
+    assert st["lds_dense_products"] == st["products"]
 
 
 def _sampled_check(A, rows, **opts):
