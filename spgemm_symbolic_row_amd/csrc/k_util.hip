@@ -214,21 +214,12 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
   for (int64_t row = ((int64_t)blockIdx.x * kNT + threadIdx.x) / G; row < m; row += rowsPerPass) {
     const int64_t rs = arp[row], re = arp[row + 1];
     int64_t p = 0;
-    // Span of the row's products: first column of its first-starting B row
-    // to last column of its last-ending one (B rows are sorted).
-    int32_t lo = INT_MAX, hi = -1;
     for (int64_t b = rs; b < re; b += G) {
       const int64_t j = b + gl;
       int64_t nb = 0;
       if (j < re) {
         const int32_t k = acol[j];
-        const int32_t b0 = brp[k], b1 = brp[k + 1];
-        nb = (int64_t)b1 - b0;
-        if (rowWin && nb > 0) {
-          const int2 sp = bSpan[k];
-          lo = sp.x < lo ? sp.x : lo;
-          hi = sp.y > hi ? sp.y : hi;
-        }
+        nb = (int64_t)brp[k + 1] - brp[k];
       }
       int64_t inc = nb;
 #pragma unroll
@@ -239,7 +230,20 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
       if (j < re) scanA[j] = (int32_t)(p + inc - nb);
       p += __shfl(inc, G - 1, G);
     }
-    if (rowWin) {
+    // Light rows of a bin with dense windows: span of the row's products,
+    // from the first column of its first-starting B row to the last column
+    // of its last-ending one (B rows are sorted; empty ones hold an empty
+    // span).
+    int lb = 0;
+    if (p > 0 && p <= tau)
+      while (lb < nbins - 1 && p > caps[lb]) ++lb;
+    int32_t lo = INT_MAX, hi = -1;
+    if (p > 0 && p <= tau && lb < winBins) {
+      for (int64_t j = rs + gl; j < re; j += G) {
+        const int2 sp = bSpan[acol[j]];
+        lo = sp.x < lo ? sp.x : lo;
+        hi = sp.y > hi ? sp.y : hi;
+      }
 #pragma unroll
       for (int d = 1; d < G; d <<= 1) {
         const int32_t l2 = __shfl_xor(lo, d, G), h2 = __shfl_xor(hi, d, G);
@@ -258,8 +262,7 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
         atomicAdd(&sAh, (unsigned long long)(re - rs));
         atomicAdd(&sH, 1ull);
       } else {
-        int b = 0;
-        while (b < nbins - 1 && p > caps[b]) ++b;
+        const int b = lb;
         bin = (uint8_t)(1 + b);
         const int64_t span = (int64_t)hi - lo + 1;
         if (b < winBins && span <= 32 * (int64_t)window_words(caps[b])) {
