@@ -345,6 +345,62 @@ __device__ __forceinline__ int32_t compact_slots(int32_t* keys, V* vals, int32_t
 // compare-exchange distances, those below E are register swaps inside a
 // thread, those below 64*E shuffles between lanes of one wave, and only the
 // longer ones go through LDS with barriers (none when a wave owns the item).
+// Value of lane (lane xor LD) of the wave, for the bitonic network's lane
+// exchanges: within a row of 16 lanes by DPP (quad permutes for 1 and 2, row
+// rotations for 4 and 8), across 16 by a swizzle inside each half wave, and
+// across 32 by a permute through the LDS crossbar.
+template <int LD>
+__device__ __forceinline__ int32_t lane_xor(int32_t x) {
+  if constexpr (LD == 1) {
+    return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (LD == 2) {
+    return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (LD == 4) {
+    const int32_t up = __builtin_amdgcn_update_dpp(x, x, 0x12C, 0xF, 0xF, false);  // row_ror:12
+    const int32_t dn = __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false);  // row_ror:4
+    return (lane_id() & 4) ? dn : up;
+  } else if constexpr (LD == 8) {
+    return __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (LD == 16) {
+    return __builtin_amdgcn_ds_swizzle(x, (16 << 10) | 0x1F);  // xor 16 within 32 lanes
+  } else {
+    return __shfl_xor(x, LD);
+  }
+}
+template <int LD>
+__device__ __forceinline__ float lane_xor_v(float x) {
+  return __int_as_float(lane_xor<LD>(__float_as_int(x)));
+}
+template <int LD>
+__device__ __forceinline__ double lane_xor_v(double x) {
+  const int64_t b = __double_as_longlong(x);
+  const int32_t lo = lane_xor<LD>((int32_t)(uint32_t)(b & 0xffffffff));
+  const int32_t hi = lane_xor<LD>((int32_t)(b >> 32));
+  return __longlong_as_double(((int64_t)hi << 32) | (int64_t)(uint32_t)lo);
+}
+
+// One compare-exchange step of the bitonic network between lanes LD apart
+// (element distance j = LD * E, phase k).
+template <int LD, int TPR, int E, typename V>
+__device__ __forceinline__ void bitonic_lane_step(int k, int32_t (&kk)[E], V (&vv)[E]) {
+  const int t = threadIdx.x % TPR;
+  constexpr int j = LD * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int32_t ok = lane_xor<LD>(kk[e]);
+    const V ov = lane_xor_v<LD>(vv[e]);
+    const int i = t * E + e;
+    const bool up = (i & k) == 0;
+    const bool lower = (i & j) == 0;
+    // In an ascending pair the lower position keeps the smaller key.
+    const bool take = (lower == up) ? (ok < kk[e]) : (ok > kk[e]);
+    if (take) {
+      kk[e] = ok;
+      vv[e] = ov;
+    }
+  }
+}
+
 template <int TPR, int E, typename V>
 __device__ __forceinline__ void sort_to_regs(int32_t* keys, V* vals, int32_t (&kk)[E],
                                              V (&vv)[E]) {
@@ -389,20 +445,13 @@ __device__ __forceinline__ void sort_to_regs(int32_t* keys, V* vals, int32_t (&k
       }
     }
     for (; j >= E; j >>= 1) {
-      const int ld = j / E;  // lane distance, below 64
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int32_t ok = __shfl_xor(kk[e], ld);
-        const V ov = __shfl_xor(vv[e], ld);
-        const int i = t * E + e;
-        const bool up = (i & k) == 0;
-        const bool lower = (i & j) == 0;
-        // In an ascending pair the lower position keeps the smaller key.
-        const bool take = (lower == up) ? (ok < kk[e]) : (ok > kk[e]);
-        if (take) {
-          kk[e] = ok;
-          vv[e] = ov;
-        }
+      switch (j / E) {  // lane distance, below 64
+        case 1: bitonic_lane_step<1, TPR, E, V>(k, kk, vv); break;
+        case 2: bitonic_lane_step<2, TPR, E, V>(k, kk, vv); break;
+        case 4: bitonic_lane_step<4, TPR, E, V>(k, kk, vv); break;
+        case 8: bitonic_lane_step<8, TPR, E, V>(k, kk, vv); break;
+        case 16: bitonic_lane_step<16, TPR, E, V>(k, kk, vv); break;
+        default: bitonic_lane_step<32, TPR, E, V>(k, kk, vv); break;
       }
     }
 #pragma unroll
