@@ -256,6 +256,23 @@ spgemm_status spgemm_prune_colnorm_count(
     int32_t out_rowptr64, int64_t *nnzOut, void *stream);
 spgemm_status spgemm_prune_colnorm_fill(spgemm_prune_t p, int32_t *dOut_col,
                                         void *dOut_val);
+
+/* The rest of one Markov-clustering iteration after the expansion C = A*A
+ * (Trident page, §5.7: normalise the columns, prune entries below a
+ * threshold, square the remaining entries).  With s_j the fp64 sum of all
+ * entries of column j, y = C[i,j] / s_j is formed in fp64 and rounded once
+ * to the value type (y = 0 when s_j = 0); entries with y >= threshold
+ * (compared in the value type) are kept, with value y * y computed in the
+ * value type.  Same two-call pattern, arguments, ownership and errors as
+ * spgemm_prune_colnorm_count / _fill; the handle is released with
+ * spgemm_prune_destroy. */
+spgemm_status spgemm_mcl_inflate_count(
+    spgemm_prune_t *out, int64_t m, int64_t n, const void *dC_row_ptr,
+    int32_t c_rowptr64, const int32_t *dC_col, const void *dC_val,
+    spgemm_dtype dtype, double threshold, void *dOut_row_ptr,
+    int32_t out_rowptr64, int64_t *nnzOut, void *stream);
+spgemm_status spgemm_mcl_inflate_fill(spgemm_prune_t p, int32_t *dOut_col,
+                                      void *dOut_val);
 void spgemm_prune_destroy(spgemm_prune_t p);
 
 #ifdef __cplusplus

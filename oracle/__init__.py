@@ -53,6 +53,9 @@ def _load():
         lib.oracle_prune_colnorm.restype = i64
         lib.oracle_prune_colnorm.argtypes = [i64, i64, vp, vp, vp, ctypes.c_float, vp,
                                              vp, vp, vp]
+        lib.oracle_mcl_inflate.restype = i64
+        lib.oracle_mcl_inflate.argtypes = [i64, i64, vp, vp, vp, ctypes.c_double, ctypes.c_int,
+                                           vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -157,4 +160,25 @@ def prune_colnorm(m: int, n: int, row_ptr, col, val, threshold: float = 1e-4,
                                  _p(kk), _p(orp), _p(oc), _p(ov))
     if w < 0:
         raise MemoryError("oracle_prune_colnorm failed")
+    return orp, oc[:w].copy(), ov[:w].copy()
+
+
+def mcl_inflate(m: int, n: int, row_ptr, col, val, threshold: float = 0.002,
+                single: bool = True, keep: np.ndarray | None = None):
+    """The rest of one Markov-clustering iteration after the expansion:
+    column normalisation (fp64 sums of every entry; each value divided in
+    fp64 and rounded to fp32 when `single`), prune below `threshold`
+    (compared in fp32 when `single`), square (in fp32 when `single`).
+    Returns (row_ptr int64, col int32, val float64)."""
+    lib = _load()
+    rp, cc, vv = _c(row_ptr, np.int64), _c(col, np.int32), _c(val, np.float64)
+    kk = None if keep is None else _c(keep, np.int8)
+    nnz = cc.shape[0]
+    orp = np.zeros(m + 1, dtype=np.int64)
+    oc = np.empty(max(nnz, 1), dtype=np.int32)
+    ov = np.empty(max(nnz, 1), dtype=np.float64)
+    w = lib.oracle_mcl_inflate(m, n, _p(rp), _p(cc), _p(vv), float(threshold),
+                               1 if single else 0, _p(kk), _p(orp), _p(oc), _p(ov))
+    if w < 0:
+        raise MemoryError("oracle_mcl_inflate failed")
     return orp, oc[:w].copy(), ov[:w].copy()

@@ -191,3 +191,42 @@ int64_t oracle_prune_colnorm(int64_t m, int64_t n, const int64_t *c_rp,
   free(colsum);
   return w;
 }
+
+/* MCL iteration tail (Trident page, §5.7): normalise the columns, prune the
+ * normalised entries below the threshold, square the rest. */
+int64_t oracle_mcl_inflate(int64_t m, int64_t n, const int64_t *c_rp,
+                           const int32_t *c_col, const double *c_val,
+                           double threshold, int single, const int8_t *keep,
+                           int64_t *out_rp, int32_t *out_col, double *out_val) {
+  double *colsum = (double *)calloc((size_t)(n > 0 ? n : 1), sizeof(double));
+  if (!colsum) return -1;
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t e = c_rp[i]; e < c_rp[i + 1]; ++e) colsum[c_col[e]] += c_val[e];
+  int64_t w = 0;
+  out_rp[0] = 0;
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t e = c_rp[i]; e < c_rp[i + 1]; ++e) {
+      const double s = colsum[c_col[e]];
+      const double y64 = s != 0.0 ? c_val[e] / s : 0.0;
+      int k;
+      double z;
+      if (single) {
+        const float y = (float)y64;
+        k = y >= (float)threshold;
+        z = (double)(y * y);
+      } else {
+        k = y64 >= threshold;
+        z = y64 * y64;
+      }
+      if (keep && keep[e] >= 0) k = keep[e];
+      if (k) {
+        out_col[w] = c_col[e];
+        out_val[w] = z;
+        ++w;
+      }
+    }
+    out_rp[i + 1] = w;
+  }
+  free(colsum);
+  return w;
+}

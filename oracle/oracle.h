@@ -65,6 +65,18 @@ int64_t oracle_prune_colnorm(int64_t m, int64_t n, const int64_t *c_rp,
                              int64_t *out_rp, int32_t *out_col,
                              double *out_val);
 
+/* The rest of one Markov-clustering iteration after the expansion (Trident
+ * page, §5.7): s_j = sum of every entry of column j (fp64, in row order);
+ * y = C[i,j] / s_j in fp64, rounded to fp32 when single != 0 (0 when s_j is
+ * 0); keep y >= threshold (compared in fp32 when single, else in fp64);
+ * output y * y (computed in fp32 when single).  keep (may be NULL) overrides
+ * the decision of entry e when keep[e] >= 0.  out arrays as for
+ * oracle_prune_colnorm.  Returns the kept count, or -1 if out of memory. */
+int64_t oracle_mcl_inflate(int64_t m, int64_t n, const int64_t *c_rp,
+                           const int32_t *c_col, const double *c_val,
+                           double threshold, int single, const int8_t *keep,
+                           int64_t *out_rp, int32_t *out_col, double *out_val);
+
 #ifdef __cplusplus
 }
 #endif

@@ -125,6 +125,10 @@ def lib():
                                                  c_i32, ctypes.POINTER(c_i64), c_vp]
         L.spgemm_prune_colnorm_fill.restype = st
         L.spgemm_prune_colnorm_fill.argtypes = [c_vp, c_vp, c_vp]
+        L.spgemm_mcl_inflate_count.restype = st
+        L.spgemm_mcl_inflate_count.argtypes = L.spgemm_prune_colnorm_count.argtypes
+        L.spgemm_mcl_inflate_fill.restype = st
+        L.spgemm_mcl_inflate_fill.argtypes = [c_vp, c_vp, c_vp]
         L.spgemm_prune_destroy.restype = None
         L.spgemm_prune_destroy.argtypes = [c_vp]
         _lib = L
@@ -281,6 +285,55 @@ def matmul(A, B, with_stats: bool = False, **options):
         st = p.stats() if with_stats else None
     _last_stats = st
     return (rp, col, val, st) if with_stats else (rp, col, val)
+
+
+def _two_call(count_fn, fill_fn, row_ptr, col, val, m, n, threshold, out_rowptr64):
+    import torch
+    L = lib()
+    rp64 = 1 if row_ptr.dtype == torch.int64 else 0
+    dt = SPGEMM_F64 if val.dtype == torch.float64 else SPGEMM_F32
+    orp = torch.empty(m + 1, dtype=torch.int64 if out_rowptr64 else torch.int32,
+                      device=col.device)
+    h = c_vp()
+    nnz = c_i64()
+    stream = torch.cuda.current_stream().cuda_stream
+    _check(count_fn(ctypes.byref(h), m, n, row_ptr.data_ptr(), rp64, col.data_ptr(),
+                    val.data_ptr(), dt, float(threshold), orp.data_ptr(),
+                    1 if out_rowptr64 else 0, ctypes.byref(nnz), c_vp(stream)))
+    try:
+        ocol = torch.empty(max(nnz.value, 1), dtype=torch.int32, device=col.device)[:nnz.value]
+        oval = torch.empty(max(nnz.value, 1), dtype=val.dtype, device=col.device)[:nnz.value]
+        _check(fill_fn(h, ocol.data_ptr(), oval.data_ptr()))
+    finally:
+        L.spgemm_prune_destroy(h)
+    return orp, ocol, oval
+
+
+def mcl_inflate(row_ptr, col, val, m, n, threshold=0.002, out_rowptr64=False):
+    """The rest of one Markov-clustering iteration after the expansion:
+    normalise the columns, drop entries below the threshold, square the rest."""
+    L = lib()
+    return _two_call(L.spgemm_mcl_inflate_count, L.spgemm_mcl_inflate_fill, row_ptr, col, val,
+                     m, n, threshold, out_rowptr64)
+
+
+def mcl(A, iterations=10, threshold=0.002, **options):
+    """Markov clustering: `iterations` times, C = A*A (expansion), then
+    normalise, prune and square (mcl_inflate); C becomes the next A.
+    Returns the final CsrDevice and the products of every expansion."""
+    X = _as_csr(A)
+    options = dict(options)
+    options.setdefault("rowptr64", 1)   # C may hold more than 2^31 entries
+    products = []
+    for _ in range(iterations):
+        with Plan(X, X, **options) as p:
+            rp, _ = p.symbolic()
+            col, val = p.numeric()
+            products.append(p.stats()["products"])
+        # The kept matrix is the next input, whose indices are int32.
+        rp, col, val = mcl_inflate(rp, col, val, X.m, X.n, threshold, out_rowptr64=False)
+        X = CsrDevice(rp, col, val, X.m, X.n)
+    return X, products
 
 
 def prune_colnorm(row_ptr, col, val, m, n, threshold=1e-4, out_rowptr64=False):

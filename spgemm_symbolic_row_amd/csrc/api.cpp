@@ -16,6 +16,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -1405,6 +1406,7 @@ struct spgemm_prune_s {
   const void* val = nullptr;
   bool f64 = false;
   double thr = 0;
+  bool mcl = false;  // normalise, prune, square (else prune, normalise)
   hipStream_t stream = nullptr;
   int64_t *keep = nullptr, *off = nullptr, *tmp = nullptr;
   double* colsum = nullptr;
@@ -1427,10 +1429,12 @@ void prune_free(spgemm_prune_t p) {
 }
 }  // namespace
 
-extern "C" spgemm_status spgemm_prune_colnorm_count(
-    spgemm_prune_t* out, int64_t m, int64_t n, const void* dC_row_ptr, int32_t c_rowptr64,
-    const int32_t* dC_col, const void* dC_val, spgemm_dtype dtype, double threshold,
-    void* dOut_row_ptr, int32_t out_rowptr64, int64_t* nnzOut, void* stream) {
+namespace {
+spgemm_status prune_count(bool mcl, spgemm_prune_t* out, int64_t m, int64_t n,
+                          const void* dC_row_ptr, int32_t c_rowptr64, const int32_t* dC_col,
+                          const void* dC_val, spgemm_dtype dtype, double threshold,
+                          void* dOut_row_ptr, int32_t out_rowptr64, int64_t* nnzOut,
+                          void* stream) {
   if (!out || !nnzOut || !dC_row_ptr || !dOut_row_ptr || m < 0 || n < 0 ||
       (dtype != SPGEMM_F32 && dtype != SPGEMM_F64)) {
     g_thread_error = "invalid argument";
@@ -1446,6 +1450,7 @@ extern "C" spgemm_status spgemm_prune_colnorm_count(
   p->val = dC_val;
   p->f64 = dtype == SPGEMM_F64;
   p->thr = threshold;
+  p->mcl = mcl;
   p->stream = (hipStream_t)stream;
   try {
     hipStream_t s = p->stream;
@@ -1455,7 +1460,15 @@ extern "C" spgemm_status spgemm_prune_colnorm_count(
     HIP_CHECK(hipMallocAsync((void**)&p->tmp, sizeof(int64_t) * (scan_tmp_elems(m) + 1), s));
     HIP_CHECK(hipMallocAsync((void**)&p->colsum, sizeof(double) * std::max<int64_t>(n, 1), s));
     launch_fill_i64((int64_t*)p->colsum, 0, n, s);  // +0.0 has an all-zero bit pattern
-    launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->keep, p->colsum, s);
+    if (mcl) {
+      // Column sums of every entry, then the kept count of every row.
+      launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, -INFINITY, p->keep,
+                         p->colsum, s);
+      launch_mcl_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->colsum, p->keep, s);
+    } else {
+      launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->keep, p->colsum,
+                         s);
+    }
     launch_scan_i64(p->keep, m, p->off, p->tmp, s);
     check_launch("prune count");
     HIP_CHECK(hipMemcpyAsync(p->hbuf, p->off + m, 8, hipMemcpyDeviceToHost, s));
@@ -1475,14 +1488,37 @@ extern "C" spgemm_status spgemm_prune_colnorm_count(
   return SPGEMM_OK;
 }
 
-extern "C" spgemm_status spgemm_prune_colnorm_fill(spgemm_prune_t p, int32_t* dOut_col,
-                                                   void* dOut_val) {
+}  // namespace
+
+extern "C" spgemm_status spgemm_prune_colnorm_count(
+    spgemm_prune_t* out, int64_t m, int64_t n, const void* dC_row_ptr, int32_t c_rowptr64,
+    const int32_t* dC_col, const void* dC_val, spgemm_dtype dtype, double threshold,
+    void* dOut_row_ptr, int32_t out_rowptr64, int64_t* nnzOut, void* stream) {
+  return prune_count(false, out, m, n, dC_row_ptr, c_rowptr64, dC_col, dC_val, dtype, threshold,
+                     dOut_row_ptr, out_rowptr64, nnzOut, stream);
+}
+
+extern "C" spgemm_status spgemm_mcl_inflate_count(
+    spgemm_prune_t* out, int64_t m, int64_t n, const void* dC_row_ptr, int32_t c_rowptr64,
+    const int32_t* dC_col, const void* dC_val, spgemm_dtype dtype, double threshold,
+    void* dOut_row_ptr, int32_t out_rowptr64, int64_t* nnzOut, void* stream) {
+  return prune_count(true, out, m, n, dC_row_ptr, c_rowptr64, dC_col, dC_val, dtype, threshold,
+                     dOut_row_ptr, out_rowptr64, nnzOut, stream);
+}
+
+namespace {
+spgemm_status prune_fill(bool mcl, spgemm_prune_t p, int32_t* dOut_col, void* dOut_val) {
   if (!p) return SPGEMM_ERR_INVALID_ARG;
+  if (p->mcl != mcl) return SPGEMM_ERR_STATE;
   if (p->state != 0) return SPGEMM_ERR_STATE;
   if (p->nnzOut > 0 && (!dOut_col || !dOut_val)) return SPGEMM_ERR_INVALID_ARG;
   try {
-    launch_prune_fill(p->m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->off, p->colsum,
+    if (mcl)
+      launch_mcl_fill(p->m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->off, p->colsum,
                       dOut_col, dOut_val, p->stream);
+    else
+      launch_prune_fill(p->m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->off,
+                        p->colsum, dOut_col, dOut_val, p->stream);
     check_launch("prune fill");
   } catch (const Error& e) {
     p->err = e.msg;
@@ -1491,6 +1527,17 @@ extern "C" spgemm_status spgemm_prune_colnorm_fill(spgemm_prune_t p, int32_t* dO
   }
   p->state = 1;
   return SPGEMM_OK;
+}
+}  // namespace
+
+extern "C" spgemm_status spgemm_prune_colnorm_fill(spgemm_prune_t p, int32_t* dOut_col,
+                                                   void* dOut_val) {
+  return prune_fill(false, p, dOut_col, dOut_val);
+}
+
+extern "C" spgemm_status spgemm_mcl_inflate_fill(spgemm_prune_t p, int32_t* dOut_col,
+                                                 void* dOut_val) {
+  return prune_fill(true, p, dOut_col, dOut_val);
 }
 
 extern "C" void spgemm_prune_destroy(spgemm_prune_t p) { prune_free(p); }

@@ -324,5 +324,12 @@ void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col,
 void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
                        bool f64, double thr, const int64_t* outOff, const double* colsum,
                        int32_t* ocol, void* oval, hipStream_t s);
+// MCL inflation (normalise, drop below the threshold, square); column sums
+// of all entries from launch_prune_count with threshold -inf.
+void launch_mcl_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                      bool f64, double thr, const double* colsum, int64_t* keep, hipStream_t s);
+void launch_mcl_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                     bool f64, double thr, const int64_t* outOff, const double* colsum,
+                     int32_t* ocol, void* oval, hipStream_t s);
 
 }  // namespace sg

@@ -120,6 +120,71 @@ __global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __res
   }
 }
 
+// ------------------------------------------------------------ MCL inflation
+// One Markov-clustering iteration after the expansion (Trident page, §5.7):
+// columns normalised to sum 1, entries below the threshold dropped, the rest
+// squared.  The column sums s_j of all entries come from k_prune_count with
+// no threshold; y = x / s_j is formed in fp64 and rounded once to the value
+// type (0 for a zero column sum), kept when y >= threshold in the value type,
+// and written as y * y in the value type (one more rounding).
+template <typename V>
+__device__ __forceinline__ V mcl_normalised(V x, double s) {
+  return s != 0.0 ? (V)((double)x / s) : V(0);
+}
+
+// One wave per row: kept entries per row.
+template <typename V, typename RP>
+__global__ __launch_bounds__(kNT) void k_mcl_count(int64_t m, const void* __restrict__ rp,
+                                                   const int32_t* __restrict__ col,
+                                                   const V* __restrict__ val, V thr,
+                                                   const double* __restrict__ colsum,
+                                                   int64_t* __restrict__ keep) {
+  const int64_t r = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
+  if (r >= m) return;
+  const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
+  int64_t kept = 0;
+  for (int64_t base = a; base < b; base += kWave) {
+    const int64_t e = base + lane_id();
+    bool k = false;
+    if (e < b) k = mcl_normalised(val[e], colsum[col[e]]) >= thr;
+    kept += __popcll(__ballot(k));
+  }
+  if (lane_id() == 0) keep[r] = kept;
+}
+
+// One wave per row: order-preserving compaction of the kept entries, squared.
+template <typename V, typename RP>
+__global__ __launch_bounds__(kNT) void k_mcl_fill(int64_t m, const void* __restrict__ rp,
+                                                  const int32_t* __restrict__ col,
+                                                  const V* __restrict__ val, V thr,
+                                                  const int64_t* __restrict__ outOff,
+                                                  const double* __restrict__ colsum,
+                                                  int32_t* __restrict__ ocol,
+                                                  V* __restrict__ oval) {
+  const int64_t r = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
+  if (r >= m) return;
+  const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
+  int64_t w = outOff[r];
+  for (int64_t base = a; base < b; base += kWave) {
+    const int64_t e = base + lane_id();
+    bool k = false;
+    V y = V(0);
+    int32_t c = 0;
+    if (e < b) {
+      c = col[e];
+      y = mcl_normalised(val[e], colsum[c]);
+      k = y >= thr;
+    }
+    const uint64_t mk = __ballot(k);
+    if (k) {
+      const int64_t pos = w + __popcll(mk & lanemask_lt());
+      ocol[pos] = c;
+      oval[pos] = y * y;
+    }
+    w += __popcll(mk);
+  }
+}
+
 inline unsigned grid_rows(int64_t m) { return (unsigned)((m * kWave + kNT - 1) / kNT); }
 
 }  // namespace
@@ -166,6 +231,35 @@ void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, 
       hipLaunchKernelGGL((k_prune_fill<float, int32_t>), g, b, 0, s, m, rp, col,
                          (const float*)val, (float)thr, outOff, colsum, ocol, (float*)oval);
   }
+}
+
+void launch_mcl_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                      bool f64, double thr, const double* colsum, int64_t* keep, hipStream_t s) {
+  if (m <= 0) return;
+  const dim3 g(grid_rows(m)), b(kNT);
+#define L(V, RP)                                                                              \
+  hipLaunchKernelGGL((k_mcl_count<V, RP>), g, b, 0, s, m, rp, col, (const V*)val, (V)thr,   \
+                     colsum, keep)
+  if (f64 && rp64) L(double, int64_t);
+  else if (f64) L(double, int32_t);
+  else if (rp64) L(float, int64_t);
+  else L(float, int32_t);
+#undef L
+}
+
+void launch_mcl_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
+                     bool f64, double thr, const int64_t* outOff, const double* colsum,
+                     int32_t* ocol, void* oval, hipStream_t s) {
+  if (m <= 0) return;
+  const dim3 g(grid_rows(m)), b(kNT);
+#define L(V, RP)                                                                              \
+  hipLaunchKernelGGL((k_mcl_fill<V, RP>), g, b, 0, s, m, rp, col, (const V*)val, (V)thr,    \
+                     outOff, colsum, ocol, (V*)oval)
+  if (f64 && rp64) L(double, int64_t);
+  else if (f64) L(double, int32_t);
+  else if (rp64) L(float, int64_t);
+  else L(float, int32_t);
+#undef L
 }
 
 }  // namespace sg

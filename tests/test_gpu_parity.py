@@ -362,6 +362,71 @@ def test_planted_partition_small_with_prune():
     assert ecol.size == int(((ref32 >= np.float32(1e-4)) & ~band).sum() + (keep[band] == 1).sum())
 
 
+def _check_mcl_inflate(rp, col, val, m, n, thr, dtype):
+    """GPU MCL inflation of C (device CSR) against the oracle on the same C;
+    normalised values within 1e-6 relative of the threshold may go either
+    way, so the GPU's decision is adopted there.  Returns the GPU result."""
+    orp, ocol, oval = sg.mcl_inflate(rp, col, val, m, n, thr)
+    crp, ccol = _to_np(rp, np.int64), _to_np(col)
+    cval = _to_np(val).astype(np.float64)
+    s = np.zeros(n)
+    np.add.at(s, ccol, cval)
+    y = np.where(s[ccol] != 0, cval / np.where(s[ccol] != 0, s[ccol], 1), 0.0)
+    band = np.abs(y - thr) <= 1e-6 * thr
+    grows = np.repeat(np.arange(m), np.diff(_to_np(orp, np.int64)))
+    gkept = set(zip(grows.tolist(), _to_np(ocol).tolist()))
+    crows = np.repeat(np.arange(m), np.diff(crp))
+    keep = np.full(ccol.size, -1, np.int8)
+    for e in np.nonzero(band)[0]:
+        keep[e] = 1 if (int(crows[e]), int(ccol[e])) in gkept else 0
+    erp, ecol, evals = oracle.mcl_inflate(m, n, crp, ccol, cval, thr,
+                                          single=dtype == np.float32, keep=keep)
+    assert_csr_equal_structure(_to_np(orp, np.int64), _to_np(ocol), erp, ecol, "mcl inflation")
+    np.testing.assert_allclose(_to_np(oval).astype(np.float64), evals,
+                               rtol=1e-5 if dtype == np.float32 else 1e-12, atol=0)
+    return orp, ocol, oval
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_mcl_inflate_matches_oracle(dtype):
+    A = synth.planted_partition(40, 200, 28, 4, seed=5, dtype=dtype)
+    dA = sg.to_device(A)
+    rp, col, val = sg.matmul(dA, dA)
+    _check_mcl_inflate(rp, col, val, A.m, A.n, 0.002, dtype)
+    # a threshold below every value keeps the whole structure
+    orp, ocol, _ = sg.mcl_inflate(rp, col, val, A.m, A.n, 0.0)
+    np.testing.assert_array_equal(_to_np(orp, np.int64), _to_np(rp, np.int64))
+    np.testing.assert_array_equal(_to_np(ocol), _to_np(col))
+
+
+def test_mcl_iterations_step_by_step():
+    # Markov clustering as on the Trident page (10 iterations, threshold
+    # 0.002), each step checked against the oracle on the GPU's own input:
+    # the expansion against the oracle's product, the inflation against the
+    # oracle's inflation of the GPU's C.
+    A = synth.planted_partition(30, 150, 28, 4, seed=7)
+    X = sg.to_device(A)
+    Xh = A
+    for it in range(10):
+        st = check_full(Xh, Xh, rowptr64=1)
+        rp, col, val = sg.matmul(X, X, rowptr64=1)
+        orp, ocol, oval = _check_mcl_inflate(rp, col, val, A.m, A.n, 0.002, np.float32)
+        orp = orp.to(torch.int32)
+        X = sg.CsrDevice(orp, ocol, oval, A.m, A.n)
+        Xh = synth.CSR(_to_np(orp, np.int32), _to_np(ocol), _to_np(oval), A.m, A.n)
+    # the loop in the binding gives the same clustering (LDS atomics may add
+    # in another order, so a value that lands on the threshold could flip)
+    Y, products = sg.mcl(sg.to_device(A), iterations=10, threshold=0.002)
+    assert len(products) == 10
+    def entries(Z):
+        r = np.repeat(np.arange(A.m), np.diff(_to_np(Z.row_ptr, np.int64)))
+        return dict(zip(zip(r.tolist(), _to_np(Z.col).tolist()), _to_np(Z.val).tolist()))
+    ey, ex = entries(Y), entries(X)
+    assert len(set(ey) ^ set(ex)) <= max(1, len(ex) // 1000)
+    common = sorted(set(ey) & set(ex))
+    np.testing.assert_allclose([ey[k] for k in common], [ex[k] for k in common], rtol=1e-4)
+
+
 def test_mcl_config_sampled_and_prune_properties():
     A = synth.workload("mcl1m")
     rng = np.random.default_rng(2)

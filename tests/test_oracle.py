@@ -278,6 +278,73 @@ def test_fp32_inputs_accumulate_in_fp64():
     assert Ad.dtype == np.float64
 
 
+def _read_golden(name):
+    out = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        k, *v = line.split()
+        out[k] = np.array([float(x) for x in v])
+    return out
+
+
+def test_mcl_inflate_hand_example():
+    # tests/golden/mcl_inflate_hand.txt: worked by hand from the step the
+    # Trident page describes (normalise columns, prune, square).
+    g = _read_golden("mcl_inflate_hand.txt")
+    rp, col, val = g["row_ptr"].astype(np.int64), g["col"].astype(np.int32), g["val"]
+    for single in (True, False):
+        for thr, key in ((0.3, "t0.3"), (0.0, "t0")):
+            orp, oc, ov = oracle.mcl_inflate(3, 3, rp, col, val, thr, single=single)
+            np.testing.assert_array_equal(orp, g[key + "_row_ptr"].astype(np.int64))
+            np.testing.assert_array_equal(oc, g[key + "_col"].astype(np.int32))
+            np.testing.assert_array_equal(ov, g[key + "_val"])
+
+
+def test_mcl_inflate_fixpoints():
+    # The identity is a fixed point of the whole iteration (I*I = I, columns
+    # already sum to 1, 1 >= any threshold below 1, 1^2 = 1).
+    I = synth.identity(7, np.float32)
+    C = oracle.spgemm(I, I)
+    orp, oc, ov = oracle.mcl_inflate(7, 7, C.row_ptr, C.col, C.val, 0.5)
+    np.testing.assert_array_equal(orp, I.row_ptr.astype(np.int64))
+    np.testing.assert_array_equal(oc, I.col)
+    np.testing.assert_array_equal(ov, np.ones(7))
+    # The uniform 4x4 matrix J/4: (J/4)^2 = J/4, normalised 1/4 everywhere,
+    # squared 1/16; pruned away entirely above 1/4.
+    n = 4
+    J = synth.CSR(np.arange(0, n * n + 1, n, dtype=np.int32),
+                  np.tile(np.arange(n, dtype=np.int32), n), np.full(n * n, 0.25, np.float32), n, n)
+    C = oracle.spgemm(J, J)
+    np.testing.assert_array_equal(C.val, np.full(n * n, 0.25))
+    orp, oc, ov = oracle.mcl_inflate(n, n, C.row_ptr, C.col, C.val, 0.25)
+    np.testing.assert_array_equal(ov, np.full(n * n, 0.0625))
+    orp, oc, ov = oracle.mcl_inflate(n, n, C.row_ptr, C.col, C.val, 0.26)
+    assert orp[-1] == 0
+
+
+def test_mcl_iterations_separate_clusters():
+    # Markov clustering of two 30-node cliques joined by one edge: after a
+    # few iterations no mass flows between the cliques, and every column
+    # keeps at least one entry inside its own clique.
+    n, h = 60, 30
+    dense = np.zeros((n, n))
+    dense[:h, :h] = 1.0
+    dense[h:, h:] = 1.0
+    dense[h - 1, h] = dense[h, h - 1] = 1.0
+    dense /= dense.sum(axis=0, keepdims=True)
+    X = sp.csr_matrix(dense.astype(np.float32))
+    A = synth.CSR(X.indptr.astype(np.int32), X.indices.astype(np.int32), X.data, n, n)
+    for _ in range(6):
+        C = oracle.spgemm(A, A)
+        rp, col, val = oracle.mcl_inflate(n, n, C.row_ptr, C.col, C.val, 0.002)
+        A = synth.CSR(rp.astype(np.int32), col, val.astype(np.float32), n, n)
+    rows = np.repeat(np.arange(n), np.diff(A.row_ptr))
+    assert np.all((rows < h) == (A.col < h))
+    assert set(A.col.tolist()) == set(range(n))
+
+
 def test_prune_colnorm_small():
     # C (3x3) with entries straddling the threshold 1e-4
     rp = np.array([0, 2, 4, 5], np.int64)
@@ -306,6 +373,10 @@ _MUTANTS = {
     "unsorted": ("qsort(touched, (size_t)nt, sizeof(int32_t), cmp_i32);", "(void)cmp_i32;"),
     "a_value_index": ("double a = val_is_f32 ? (double)af[j] : ad[j];",
                       "double a = val_is_f32 ? (double)af[a_rp[i]] : ad[a_rp[i]];"),
+    "mcl_no_square": ("z = (double)(y * y);", "z = (double)y;"),
+    "mcl_prune_raw": ("k = y >= (float)threshold;", "k = (float)c_val[e] >= (float)threshold;"),
+    "mcl_count_not_sum": ("e < c_rp[i + 1]; ++e) colsum[c_col[e]] += c_val[e];",
+                          "e < c_rp[i + 1]; ++e) colsum[c_col[e]] += 1.0;"),
 }
 
 
@@ -323,6 +394,8 @@ def _pins_pass(lib_path):
             _laplacian_closed_form_check(4)
             test_transpose_identity("rect")
             test_compensated_sum_exact()
+            test_mcl_inflate_hand_example()
+            test_mcl_inflate_fixpoints()
         except (AssertionError, RuntimeError):
             return False
         return True
