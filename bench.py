@@ -29,6 +29,9 @@ WORKLOADS = {
     "er4096": "Erdos-Renyi 4096x4096, Poisson(8) per row, fp64 U[-1,1], seed 0; C = A*A",
     "mcl1m": "planted partition 1000x1000, 28 intra + 4 inter + self per column, fp32 "
              "column-stochastic; C = A*A, prune < 1e-4, renormalise columns",
+    "mcl_iter": "planted partition 100x1000, 28 intra + 4 inter + self per column, fp32 "
+                "column-stochastic; 10 Markov-clustering iterations (C = A*A, normalise "
+                "columns, prune < 0.002, square; C is the next A)",
 }
 
 
@@ -88,6 +91,76 @@ def traffic_for(kernel, workload):
     if digest != rec["source_sha256"]:
         return None
     return rec["bytes_per_launch"]
+
+
+MCL_ITERS, MCL_THRESHOLD = 10, 0.002
+
+
+def run_mcl_iter(args, A, opts):
+    """Markov clustering: a step is the whole run of MCL_ITERS iterations;
+    GFLOP/s counts 2 x the products of every expansion."""
+    import numpy as np
+    import torch
+
+    import spgemm_symbolic_row_amd as sg
+
+    dA = sg.to_device(A)
+    opts = {k: v for k, v in opts.items() if k != "profile"}
+
+    def step():
+        return sg.mcl(dA, iterations=MCL_ITERS, threshold=MCL_THRESHOLD, **opts)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        X, prods = step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    K = args.steps
+    P = int(sum(prods))
+    value = 2.0 * P * K / dt / 1e9
+    log(f"{dt / K * 1e3:.3f} ms/step, {value:.2f} GFLOP/s; products per iteration {prods}; "
+        f"final nnz {int(X.col.numel())}")
+    line = {
+        "metric": "SpGEMM GFLOP/s (2x intermediate products) + % HBM roofline, 1 MI355X",
+        "value": round(value, 3), "unit": "GFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(dt / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "rows": A.m, "nnz_a": A.nnz,
+                   "iterations": MCL_ITERS, "threshold": MCL_THRESHOLD,
+                   "products_per_iteration": [int(x) for x in prods], "products": P,
+                   "final_nnz": int(X.col.numel()), "parallelism": "single GPU"},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    del dA, X
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
+        B = A
+        t0 = time.perf_counter()
+        Pc = 0
+        for _ in range(MCL_ITERS):
+            Pc += int(oracle.row_products(B, B).sum())
+            C = oracle.spgemm(B, B)
+            rp, col, val = oracle.mcl_inflate(B.m, B.n, C.row_ptr, C.col, C.val, MCL_THRESHOLD)
+            B = synth_csr(rp, col, val.astype(np.float32), A.m, A.n)
+        t = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(2 * Pc / t / 1e9, 4), "unit": "GFLOP/s",
+                                "cores": threads, "kind": "oracle",
+                                "sample": f"the whole {MCL_ITERS}-iteration run once, {t:.2f} s"}
+        log(f"cpu baseline: {line['cpu_baseline']}")
+    print(json.dumps(line), flush=True)
+
+
+def synth_csr(rp, col, val, m, n):
+    import numpy as np
+
+    import synth
+    return synth.CSR(rp.astype(np.int32), col.astype(np.int32), val, m, n)
 
 
 def cpu_baseline(A, target_s=15.0):
@@ -154,7 +227,7 @@ def main():
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
     ap.add_argument("--expansion", type=int, default=-1,
-                    help="heavy-row expansion: 0 one-pass run scatter, 1 outer product + "
+                    help="heavy-row expansion: 0 straight into final chunks, 1 outer product + "
                          "multisplit, 2 first level fed from A and B (default: the library's)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -200,6 +273,8 @@ def main():
         opts["expansion"] = args.expansion
     if args.config == "rmat20":
         opts["rowptr64"] = 1   # nnz(C) is about 9.7e9
+    if args.config == "mcl_iter":
+        return run_mcl_iter(args, A, opts)
     mcl = args.config == "mcl1m"
 
     def step():

@@ -267,6 +267,8 @@ def workload(name: str) -> CSR:
         return rmat(20, 16, seed=0)
     if name == "mcl1m":
         return planted_partition(1000, 1000, 28, 4, seed=0)
+    if name == "mcl_iter":
+        return planted_partition(100, 1000, 28, 4, seed=0)
     m = name.split("_")
     if m[0] == "rmat" and len(m) == 2:          # e.g. "rmat_12"
         return rmat(int(m[1]), 16, seed=0)
