@@ -56,6 +56,8 @@ def _load():
         lib.oracle_mcl_inflate.restype = i64
         lib.oracle_mcl_inflate.argtypes = [i64, i64, vp, vp, vp, ctypes.c_double, ctypes.c_int,
                                            vp, vp, vp, vp]
+        lib.oracle_transpose.restype = ctypes.c_int
+        lib.oracle_transpose.argtypes = [i64, i64, vp, vp, vp, ctypes.c_int, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -182,3 +184,35 @@ def mcl_inflate(m: int, n: int, row_ptr, col, val, threshold: float = 0.002,
     if w < 0:
         raise MemoryError("oracle_mcl_inflate failed")
     return orp, oc[:w].copy(), ov[:w].copy()
+
+
+@dataclass
+class CSRMatrix:
+    """An m x n CSR matrix in host arrays (the attribute names spgemm reads)."""
+    row_ptr: np.ndarray   # int64, m+1
+    col: np.ndarray       # int32
+    val: np.ndarray | None
+    m: int
+    n: int
+
+
+def transpose(A) -> CSRMatrix:
+    """A^T by the definition T[j, i] = A[i, j]; rows of T list their column
+    indices in rising order, values are copied unchanged (A's dtype)."""
+    lib = _load()
+    rp, cc = _c(A.row_ptr, np.int64), _c(A.col, np.int32)
+    vv = None
+    if A.val is not None:
+        vv = _c(A.val, np.float32 if A.val.dtype == np.float32 else np.float64)
+    nnz = int(rp[A.m])
+    trp = np.zeros(A.n + 1, dtype=np.int64)
+    tc = np.empty(max(nnz, 1), dtype=np.int32)
+    tv = None if vv is None else np.empty(max(nnz, 1), dtype=vv.dtype)
+    rc = lib.oracle_transpose(A.m, A.n, _p(rp), _p(cc), _p(vv),
+                              1 if (vv is not None and vv.dtype == np.float32) else 0,
+                              _p(trp), _p(tc), _p(tv))
+    if rc == -2:
+        raise ValueError("column index out of range")
+    if rc != 0:
+        raise MemoryError("oracle_transpose failed")
+    return CSRMatrix(trp, tc[:nnz].copy(), None if tv is None else tv[:nnz].copy(), A.n, A.m)

@@ -230,3 +230,40 @@ int64_t oracle_mcl_inflate(int64_t m, int64_t n, const int64_t *c_rp,
   free(colsum);
   return w;
 }
+
+/* T = A^T by the definition T[j, i] = A[i, j]: count the entries of every
+ * column, turn the counts into row starts of T, then place the entries of A
+ * row by row (rising i), each at the next free position of its column. */
+int oracle_transpose(int64_t m, int64_t n, const int64_t *a_rp,
+                     const int32_t *a_col, const void *a_val, int val_is_f32,
+                     int64_t *t_rp, int32_t *t_col, void *t_val) {
+  int64_t *next = (int64_t *)calloc((size_t)(n > 0 ? n : 1), sizeof(int64_t));
+  if (!next) return -1;
+  const int64_t nnz = a_rp[m];
+  for (int64_t e = 0; e < nnz; ++e) {
+    if (a_col[e] < 0 || a_col[e] >= n) {
+      free(next);
+      return -2;
+    }
+    next[a_col[e]] += 1;
+  }
+  t_rp[0] = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    t_rp[j + 1] = t_rp[j] + next[j];
+    next[j] = t_rp[j];
+  }
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t e = a_rp[i]; e < a_rp[i + 1]; ++e) {
+      const int64_t q = next[a_col[e]]++;
+      t_col[q] = (int32_t)i;
+      if (a_val && t_val) {
+        if (val_is_f32)
+          ((float *)t_val)[q] = ((const float *)a_val)[e];
+        else
+          ((double *)t_val)[q] = ((const double *)a_val)[e];
+      }
+    }
+  }
+  free(next);
+  return 0;
+}

@@ -77,6 +77,19 @@ int64_t oracle_mcl_inflate(int64_t m, int64_t n, const int64_t *c_rp,
                            double threshold, int single, const int8_t *keep,
                            int64_t *out_rp, int32_t *out_col, double *out_val);
 
+/* Transpose of an m x n CSR matrix: T[j, i] = A[i, j] for every stored
+ * entry (the operand of the rectangular product A * A^T that the Ocean page,
+ * "Ocean: Fast Estimation-Based Sparse General Matrix-Matrix Multiplication
+ * on GPU", evaluates on its rectangular matrix set).  Stored entries are
+ * visited row by row with rising i, so every row of T lists its column
+ * indices in rising order.  a_val / t_val may be NULL (pattern only);
+ * val_is_f32 selects float or double for both.  t_rp has n+1 entries; t_col
+ * and t_val are sized by the caller at nnz(A).  Returns 0, -1 when out of
+ * memory, -2 when a column index lies outside [0, n). */
+int oracle_transpose(int64_t m, int64_t n, const int64_t *a_rp,
+                     const int32_t *a_col, const void *a_val, int val_is_f32,
+                     int64_t *t_rp, int32_t *t_col, void *t_val);
+
 #ifdef __cplusplus
 }
 #endif

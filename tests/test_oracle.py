@@ -362,6 +362,76 @@ def test_prune_colnorm_small():
     np.testing.assert_allclose(ov, [1.0, 5e-5 / (5e-5 + 0.75), 1.0, 0.75 / (5e-5 + 0.75)], rtol=1e-15)
 
 
+def _golden_csr(g, p, m, n, dtype=np.float64):
+    return CSR(g[p + "_row_ptr"].astype(np.int32), g[p + "_col"].astype(np.int32),
+               g[p + "_val"].astype(dtype), m, n)
+
+
+def test_transpose_hand_example():
+    # tests/golden/transpose_hand.txt: transpose and A*A^T worked by hand.
+    g = _read_golden("transpose_hand.txt")
+    for dt in (np.float64, np.float32):
+        A = _golden_csr(g, "a", 3, 4, dt)
+        T = oracle.transpose(A)
+        assert (T.m, T.n) == (4, 3) and T.val.dtype == dt
+        np.testing.assert_array_equal(T.row_ptr, g["t_row_ptr"].astype(np.int64))
+        np.testing.assert_array_equal(T.col, g["t_col"].astype(np.int32))
+        np.testing.assert_array_equal(T.val, g["t_val"].astype(dt))
+        C = oracle.spgemm(A, T)
+        np.testing.assert_array_equal(C.row_ptr, g["aat_row_ptr"].astype(np.int64))
+        np.testing.assert_array_equal(C.col, g["aat_col"].astype(np.int32))
+        np.testing.assert_array_equal(C.val, g["aat_val"])
+    P = oracle.transpose(CSR(A.row_ptr, A.col, None, 3, 4))
+    assert P.val is None and P.col.tolist() == g["t_col"].astype(int).tolist()
+
+
+@pytest.mark.parametrize("m,n,per_row,seed", [
+    (0, 5, 1.0, 0), (5, 0, 0.0, 0), (1, 1, 1.0, 1), (40, 7, 3.0, 2), (7, 300, 20.0, 3),
+    (500, 800, 6.0, 4), (300, 2000, 1.5, 5)])
+def test_transpose_against_scipy_and_sort(m, n, per_row, seed):
+    # Two independent transposes: scipy's, and a stable sort of the entries
+    # by (column, row) in the test itself.
+    for values in ("uniform", "int"):
+        A = synth.random_csr(m, n, per_row, seed, values=values, empty_row_frac=0.2)
+        for dt in (np.float64, np.float32):
+            A = CSR(A.row_ptr, A.col, A.val.astype(dt), m, n)
+            T = oracle.transpose(A)
+            S = sp.csr_matrix((A.val, A.col, A.row_ptr), shape=(m, n)).T.tocsr()
+            S.sort_indices()
+            np.testing.assert_array_equal(T.row_ptr, S.indptr.astype(np.int64))
+            np.testing.assert_array_equal(T.col, S.indices.astype(np.int32))
+            np.testing.assert_array_equal(T.val, S.data)
+            R = _transpose(A)
+            np.testing.assert_array_equal(T.col, R.col)
+            np.testing.assert_array_equal(T.val, R.val)
+            # involution: (A^T)^T == A, bit for bit
+            TT = oracle.transpose(T)
+            np.testing.assert_array_equal(TT.row_ptr, A.row_ptr.astype(np.int64))
+            np.testing.assert_array_equal(TT.col, A.col)
+            np.testing.assert_array_equal(TT.val, A.val)
+
+
+def test_transpose_rejects_bad_column():
+    A = CSR(np.array([0, 2], np.int32), np.array([0, 3], np.int32), np.ones(2), 1, 3)
+    with pytest.raises(ValueError):
+        oracle.transpose(A)
+
+
+@pytest.mark.parametrize("m,k,per_row,seed", [(30, 50, 3.0, 11), (64, 200, 8.0, 12),
+                                              (100, 20, 2.0, 13)])
+def test_aat_bruteforce(m, k, per_row, seed):
+    # A*A^T from the oracle's transpose and product against dense brute force;
+    # the result is symmetric, structure and values alike.
+    A = synth.random_csr(m, k, per_row, seed, values="int", empty_row_frac=0.2)
+    T = oracle.transpose(A)
+    Tc = CSR(T.row_ptr.astype(np.int32), T.col, T.val, T.m, T.n)
+    r = _check_vs_bruteforce(A, Tc)
+    D = np.zeros((m, m))
+    rows = np.repeat(np.arange(m), np.diff(r.row_ptr))
+    D[rows, r.col] = r.val + 0.5   # stored zeros stay visible
+    np.testing.assert_array_equal(D, D.T)
+
+
 # --- planted mistakes -------------------------------------------------------
 
 _MUTANTS = {
@@ -377,6 +447,11 @@ _MUTANTS = {
     "mcl_prune_raw": ("k = y >= (float)threshold;", "k = (float)c_val[e] >= (float)threshold;"),
     "mcl_count_not_sum": ("e < c_rp[i + 1]; ++e) colsum[c_col[e]] += c_val[e];",
                           "e < c_rp[i + 1]; ++e) colsum[c_col[e]] += 1.0;"),
+    "transpose_rows_reversed": ("for (int64_t i = 0; i < m; ++i) {\n    for (int64_t e = a_rp[i]; e < a_rp[i + 1]; ++e) {\n      const int64_t q",
+                                "for (int64_t i = m - 1; i >= 0; --i) {\n    for (int64_t e = a_rp[i]; e < a_rp[i + 1]; ++e) {\n      const int64_t q"),
+    "transpose_value_index": ("((double *)t_val)[q] = ((const double *)a_val)[e];",
+                              "((double *)t_val)[q] = ((const double *)a_val)[q];"),
+    "transpose_row_index": ("t_col[q] = (int32_t)i;", "t_col[q] = a_col[e];"),
 }
 
 
@@ -396,6 +471,8 @@ def _pins_pass(lib_path):
             test_compensated_sum_exact()
             test_mcl_inflate_hand_example()
             test_mcl_inflate_fixpoints()
+            test_transpose_hand_example()
+            test_transpose_against_scipy_and_sort(500, 800, 6.0, 4)
         except (AssertionError, RuntimeError):
             return False
         return True
