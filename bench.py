@@ -32,7 +32,14 @@ WORKLOADS = {
     "mcl_iter": "planted partition 100x1000, 28 intra + 4 inter + self per column, fp32 "
                 "column-stochastic; 10 Markov-clustering iterations (C = A*A, normalise "
                 "columns, prune < 0.002, square; C is the next A)",
+    "aat": "rectangular R-MAT 2^17 x 2^20, 16 edges per row, same (a,b,c,d), fp64 U[0,1], "
+           "seed 0; C = A*A^T with A^T formed on the GPU inside the step",
+    "restrict": "R-MAT scale 18 as rmat18 times an aggregation operator R (2^18 x 2^15, "
+                "random aggregates of 8, ones, seed 1); C = A*R",
 }
+
+# matrices of each configuration: A, and B when it is not A (or A^T)
+CONFIG_MATRICES = {"aat": ("rmat_rect", "transpose"), "restrict": ("rmat18", "agg_rmat18")}
 
 
 def log(*a):
@@ -62,16 +69,25 @@ def algorithmic_bytes(st, phase, sv, si=4):
         return E * si * (2 if batched else 1), f"{si} B read per element per level"
     if phase == "num_chunk_dense":
         return st["lds_dense_products"] * (si + sv), f"{si + sv} B read per dense-chunk element"
+    if phase == "num_light":
+        return ((st["products"] - st["heavy_products"]) * (si + sv),
+                f"{si + sv} B of B read per light-row product")
     return None, None
 
 
-def effective_bytes(A, st, sv, si=4):
+def effective_bytes(A, st, sv, si=4, B=None, transposed=False):
     """Frozen effective-byte denominator: compulsory traffic plus the heavy
-    intermediate that the method materialises (expand once, with values)."""
-    m, n, nnzA, nnzC = A.m, A.n, A.nnz, st["nnz_c"]
+    intermediate that the method materialises (expand once, with values).
+    B defaults to A; with `transposed`, B = A^T is formed inside the step
+    (read A once, write A^T once)."""
+    m, nnzA, nnzC = A.m, A.nnz, st["nnz_c"]
     rp = 4
-    sym = 2 * ((m + 1) * rp + nnzA * si) + (m + 1) * rp
-    num = 2 * ((m + 1) * rp + nnzA * (si + sv)) + (m + 1) * rp + nnzC * (si + sv)
+    kB, nnzB = (A.n, A.nnz) if transposed else ((A.m, A.nnz) if B is None else (B.m, B.nnz))
+    sym = (m + 1) * rp + nnzA * si + (kB + 1) * rp + nnzB * si + (m + 1) * rp
+    num = ((m + 1) * rp + nnzA * (si + sv) + (kB + 1) * rp + nnzB * (si + sv) + (m + 1) * rp
+           + nnzC * (si + sv))
+    if transposed:
+        num += (m + 1) * rp + (A.n + 1) * rp + 2 * nnzA * (si + sv)
     Ph = st["heavy_products"]
     E = sum(st["level_elems"])
     heavy = Ph * (si + sv) + E * (3 * si + 2 * sv) + Ph * (2 * si + sv)
@@ -163,10 +179,10 @@ def synth_csr(rp, col, val, m, n):
     return synth.CSR(rp.astype(np.int32), col.astype(np.int32), val, m, n)
 
 
-def cpu_baseline(A, target_s=15.0):
-    """The oracle (as it stands) on the same matrix: a uniform random sample
-    of rows sized to about target_s seconds, or, when the whole product takes
-    less than that, the whole product repeated."""
+def cpu_baseline(A, target_s=15.0, B=None, note=""):
+    """The oracle (as it stands) on the same matrices (B defaults to A): a
+    uniform random sample of rows of A sized to about target_s seconds, or,
+    when the whole product takes less than that, the whole product repeated."""
     import numpy as np
 
     import oracle
@@ -183,20 +199,22 @@ def cpu_baseline(A, target_s=15.0):
         idx = np.repeat(rp[rows] - nrp[:-1], lens) + np.arange(int(nrp[-1]))
         return synth.CSR(nrp.astype(np.int32), A.col[idx], A.val[idx], rows.size, A.n), rows.size
 
+    B = A if B is None else B
+
     def timed(S):
         t0 = time.perf_counter()
-        oracle.spgemm(S, A)
+        oracle.spgemm(S, B)
         return time.perf_counter() - t0
 
-    P_all = int(oracle.row_products(A, A).sum())
+    P_all = int(oracle.row_products(A, B).sum())
     S, _ = sub(0.02)
-    P0 = int(oracle.row_products(S, A).sum())
+    P0 = int(oracle.row_products(S, B).sum())
     rate = P0 / max(timed(S), 1e-6)
     est_full = P_all / max(rate, 1.0)
     threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
     if est_full >= target_s:
         S, nrows = sub(target_s / est_full)
-        P = int(oracle.row_products(S, A).sum())
+        P = int(oracle.row_products(S, B).sum())
         t = timed(S)
         sample = (f"{nrows} of {A.m} rows chosen uniformly at random (seed 0), "
                   f"{P} intermediate products, {t:.2f} s")
@@ -206,7 +224,7 @@ def cpu_baseline(A, target_s=15.0):
         P = P_all * runs
         sample = f"the whole product (all {A.m} rows, {P_all} products) run {runs} times, {t:.2f} s"
     return {"value": round(2 * P / t / 1e9, 4), "unit": "GFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": sample}
+            "kind": "oracle", "sample": sample + note}
 
 
 def main():
@@ -255,9 +273,15 @@ def main():
         log(f"calibration copy: {nbytes} bytes read and {nbytes} bytes written")
         del src, dst
     t = time.time()
-    A = synth.workload(args.config)
-    log(f"generated {args.config}: {A.m} rows, nnz {A.nnz} in {time.time() - t:.1f} s")
+    a_name, b_name = CONFIG_MATRICES.get(args.config, (args.config, None))
+    A = synth.workload(a_name)
+    transposed = b_name == "transpose"
+    B = synth.workload(b_name) if b_name and not transposed else None
+    log(f"generated {args.config}: {A.m} x {A.n}, nnz {A.nnz}"
+        + (f"; B {B.m} x {B.n}, nnz {B.nnz}" if B is not None else "")
+        + f" in {time.time() - t:.1f} s")
     dA = sg.to_device(A)
+    dB = sg.to_device(B) if B is not None else None
     f64 = A.val.dtype == np.float64
     sv = 8 if f64 else 4
     opts = {} if args.no_profile else {"profile": 1}
@@ -278,7 +302,8 @@ def main():
     mcl = args.config == "mcl1m"
 
     def step():
-        with sg.Plan(dA, dA, **opts) as p:
+        dR = dB if dB is not None else (sg.transpose(dA) if transposed else dA)
+        with sg.Plan(dA, dR, **opts) as p:
             rp, _ = p.symbolic()
             col, val = p.numeric()
             out = (rp, col, val)
@@ -302,7 +327,7 @@ def main():
     P = st["products"]
     value = 2.0 * P * K / dt / 1e9
     ms = dt / K * 1e3
-    eff = effective_bytes(A, st, sv)
+    eff = effective_bytes(A, st, sv, B=B, transposed=transposed)
     log(f"{ms:.3f} ms/step, {value:.2f} GFLOP/s, effective {eff / (dt / K) / 1e9:.1f} GB/s")
     for k, v in sorted(phase_tot.items(), key=lambda kv: -kv[1]):
         if v > 0:
@@ -313,6 +338,8 @@ def main():
         cands = [k for k in ("multisplit", "expand_split", "outer_product", "expand_final",
                              "num_chunk_dense", "histogram")
                  if phase_tot.get(k, 0) > 0]
+        if not cands and phase_tot.get("num_light", 0) > 0:
+            cands = ["num_light"]
         if cands:
             kern = max(cands, key=lambda k: phase_tot[k])
             windows = st["phase_windows"][kern]
@@ -332,7 +359,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f64" if f64 else "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "rows": A.m, "nnz_a": A.nnz,
+        "config": {"workload": WORKLOADS[args.config], "rows": A.m, "cols": A.n, "nnz_a": A.nnz,
                    "products": P, "nnz_c": st["nnz_c"], "heavy_rows": st["heavy_rows"],
                    "heavy_products": st["heavy_products"],
                    "v_chunks": st["params"]["v_chunks"], "tau": st["params"]["tau"],
@@ -345,10 +372,27 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
-    del dA
+    if transposed:
+        # the transpose inside the step, timed on its own
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            sg.transpose(dA)
+        torch.cuda.synchronize()
+        line["config"]["transpose_ms"] = round((time.perf_counter() - t0) / 5 * 1e3, 4)
+        log(f"transpose alone: {line['config']['transpose_ms']} ms")
+    del dA, dB
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(A)
+        note = ""
+        if transposed:
+            import oracle
+            t0 = time.perf_counter()
+            T = oracle.transpose(A)
+            tt = time.perf_counter() - t0
+            B = synth.CSR(T.row_ptr.astype(np.int32), T.col, T.val, T.m, T.n)
+            note = f"; A^T formed by the oracle beforehand in {tt:.2f} s, not counted"
+        line["cpu_baseline"] = cpu_baseline(A, B=B, note=note)
         log(f"cpu baseline: {line['cpu_baseline']}")
     print(json.dumps(line), flush=True)
 

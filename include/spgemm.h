@@ -275,6 +275,33 @@ spgemm_status spgemm_mcl_inflate_fill(spgemm_prune_t p, int32_t *dOut_col,
                                       void *dOut_val);
 void spgemm_prune_destroy(spgemm_prune_t p);
 
+/* Transpose T = A^T of an m x n CSR matrix A into an n x m CSR matrix T, for
+ * the rectangular products A * A^T that the Ocean page ("Ocean: Fast
+ * Estimation-Based Sparse General Matrix-Matrix Multiplication on GPU",
+ * evaluation on rectangular matrices) measures, and for restriction-type
+ * operands (Trident page, §5.4).  T[j, i] = A[i, j] for every stored entry;
+ * rows of T list their column indices in rising order (A's entries stored
+ * row by row with rising rows; duplicates, if any, keep their storage
+ * order), values are copied unchanged.
+ * Inputs: dA_row_ptr (m+1; int64 if a_rowptr64 else int32), dA_col (nnz),
+ * dA_val (nnz, float or double per dtype; NULL for the pattern only, then
+ * dT_val is ignored).  Outputs, allocated by the caller: dT_row_ptr (n+1;
+ * int64 if t_rowptr64 else int32), dT_col (nnz, int32), dT_val (nnz).
+ * Temporaries (about 16 + 2*sizeof(value) bytes per entry) are allocated
+ * with hipMallocAsync on `stream` and freed in stream order.  The call
+ * blocks once, to read the device's column check.
+ * Errors: INVALID_ARG (null pointer, negative size, bad dtype),
+ * INDEX_OVERFLOW (m or n above INT32_MAX, or nnz above INT32_MAX with an
+ * int32 dT_row_ptr), INVALID_CSR (a column index outside [0, n); T is then
+ * undefined), OOM, HIP.  A's row pointers are trusted (row_ptr[0] == 0,
+ * non-decreasing, row_ptr[m] == nnz). */
+spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
+                               const void *dA_row_ptr, int32_t a_rowptr64,
+                               const int32_t *dA_col, const void *dA_val,
+                               spgemm_dtype dtype, void *dT_row_ptr,
+                               int32_t t_rowptr64, int32_t *dT_col,
+                               void *dT_val, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

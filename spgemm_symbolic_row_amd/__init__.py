@@ -131,6 +131,9 @@ def lib():
         L.spgemm_mcl_inflate_fill.argtypes = [c_vp, c_vp, c_vp]
         L.spgemm_prune_destroy.restype = None
         L.spgemm_prune_destroy.argtypes = [c_vp]
+        L.spgemm_transpose.restype = st
+        L.spgemm_transpose.argtypes = [c_i64, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, ctypes.c_int,
+                                       c_vp, c_i32, c_vp, c_vp, c_vp]
         _lib = L
     return _lib
 
@@ -358,3 +361,25 @@ def prune_colnorm(row_ptr, col, val, m, n, threshold=1e-4, out_rowptr64=False):
     finally:
         L.spgemm_prune_destroy(h)
     return orp, ocol, oval
+
+
+def transpose(A, out_rowptr64=False, pattern_only=False):
+    """A^T as a CsrDevice (n x m): rows list their columns in rising order,
+    values copied unchanged (spgemm_transpose)."""
+    import torch
+    X = _as_csr(A)
+    dev = X.col.device
+    nnz = X.nnz
+    rp64 = 1 if X.row_ptr.dtype == torch.int64 else 0
+    vals = None if (pattern_only or X.val is None) else X.val
+    vdt = torch.float64 if (vals is None or vals.dtype == torch.float64) else torch.float32
+    dt = SPGEMM_F64 if vdt == torch.float64 else SPGEMM_F32
+    trp = torch.empty(X.n + 1, dtype=torch.int64 if out_rowptr64 else torch.int32, device=dev)
+    tcol = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)[:nnz]
+    tval = None if vals is None else torch.empty(max(nnz, 1), dtype=vdt, device=dev)[:nnz]
+    stream = torch.cuda.current_stream().cuda_stream
+    _check(lib().spgemm_transpose(X.m, X.n, nnz, X.row_ptr.data_ptr(), rp64, X.col.data_ptr(),
+                                  None if vals is None else vals.data_ptr(), dt, trp.data_ptr(),
+                                  1 if out_rowptr64 else 0, tcol.data_ptr(),
+                                  None if tval is None else tval.data_ptr(), c_vp(stream)))
+    return CsrDevice(trp, tcol, tval, X.n, X.m)

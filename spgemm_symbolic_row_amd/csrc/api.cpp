@@ -621,13 +621,13 @@ void do_plan(spgemm_plan_t p) {
   p->binStart = alloc_n<int32_t>(p, 65, s);
   launch_fill_i64(p->cnt, 0, m, s);
   const int ph = ph_begin(p, SPGEMM_PH_ROW_INFO, s);
-  int64_t* part = alloc_n<int64_t>(p, row_info_partials(m), s);
+  int64_t* part = alloc_n<int64_t>(p, row_info_partials(m, p->nnzA), s);
   int2* bSpan = nullptr;
   if (p->winBins) {
     bSpan = alloc_n<int2>(p, std::max<int64_t>(p->k, 1), s);
     launch_b_span(p->k, p->brp, p->bcol, bSpan, s);
   }
-  launch_row_info(m, p->arp, p->acol, p->brp, bSpan, p->rowTau, p->dSymCaps, p->NS, p->rowP,
+  launch_row_info(m, p->nnzA, p->arp, p->acol, p->brp, bSpan, p->rowTau, p->dSymCaps, p->NS, p->rowP,
                   p->scanA, p->rowBin, p->rowWin, p->winBins, p->winMax, part, p->stats, s);
   // 0 empty, 1..NS hash bins, NS+1 heavy, NS+2..2NS+1 dense-window bins
   const int nkeys = 2 * p->NS + 2;
@@ -822,12 +822,10 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     // The heavy rows' A entries in row order with their product offsets:
     // the first multisplit level makes its elements from these.
     int32_t* eB = alloc_n<int32_t>(p, nE, s);
-    int64_t* nbE = alloc_n<int64_t>(p, nE, s);
     int64_t* eOff = alloc_n<int64_t>(p, nE + 1, s);
     void* eVal = vals ? plan_alloc(p, std::max<int64_t>(nE, 1) * vb, s) : nullptr;
-    launch_expand_entries(f64, hb, xb, p->dAnnz + hb0, p->arp, p->acol, p->aval, p->brp, eB, nbE,
-                          eVal, s);
-    launch_scan_i64(nbE, nE, eOff, tmp, s);
+    launch_expand_entries(f64, nE, hb, xb, p->dAnnz + hb0, chatRowPtr, p->arp, p->acol, p->aval,
+                          p->brp, p->scanA, eB, eOff, eVal, s);
     src = ExpandSrc{eOff, eB, eVal, p->bcol, vals ? p->bval : nullptr, nE};
     ph_end(p, phCsc, s);
   } else {
@@ -1541,3 +1539,76 @@ extern "C" spgemm_status spgemm_mcl_inflate_fill(spgemm_prune_t p, int32_t* dOut
 }
 
 extern "C" void spgemm_prune_destroy(spgemm_prune_t p) { prune_free(p); }
+
+// ================================================================ transpose
+extern "C" spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
+                                          const void* dA_row_ptr, int32_t a_rowptr64,
+                                          const int32_t* dA_col, const void* dA_val,
+                                          spgemm_dtype dtype, void* dT_row_ptr,
+                                          int32_t t_rowptr64, int32_t* dT_col, void* dT_val,
+                                          void* stream) {
+  if (m < 0 || n < 0 || nnz < 0 || !dT_row_ptr || (m > 0 && !dA_row_ptr) ||
+      (nnz > 0 && (!dA_col || !dT_col || (dA_val && !dT_val))) ||
+      (dtype != SPGEMM_F32 && dtype != SPGEMM_F64)) {
+    g_thread_error = "invalid argument";
+    return SPGEMM_ERR_INVALID_ARG;
+  }
+  if (m > INT32_MAX || n > INT32_MAX || (!t_rowptr64 && nnz > INT32_MAX)) {
+    g_thread_error = "size exceeds the int32 index range";
+    return SPGEMM_ERR_INDEX_OVERFLOW;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int vb = dtype == SPGEMM_F64 ? 8 : 4;
+  const TransposePlan tp = transpose_plan(n, nnz);
+  // One allocation, carved into 256-byte aligned pieces.
+  auto al = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
+  const int64_t ent = std::max<int64_t>(nnz, 1);
+  const bool multi = tp.passes > 1;
+  const int64_t szRows = al(4 * ent), szKeys = al(4 * ent), szVals = al((int64_t)vb * ent);
+  const int nVals = dA_val ? (tp.passes > 2 ? 2 : (multi ? 1 : 0)) : 0;
+  const int64_t szHist = al(4 * std::max<int64_t>(tp.histElems, 1));
+  const int64_t szOff = al(8 * (tp.histElems + 1));
+  const int64_t szTmp = al(8 * (scan_tmp_elems(tp.histElems) + 1));
+  const int64_t total = szRows * (multi ? 2 : 1) + szKeys * (multi ? 2 : 1) + szVals * nVals +
+                        szHist + szOff + szTmp + 256;
+  char* buf = nullptr;
+  if (hipMallocAsync((void**)&buf, (size_t)total, s) != hipSuccess) {
+    (void)hipGetLastError();
+    g_thread_error = "device allocation failed";
+    return SPGEMM_ERR_OOM;
+  }
+  spgemm_status st = SPGEMM_OK;
+  try {
+    char* q = buf;
+    auto take = [&](int64_t b) {
+      char* r = q;
+      q += b;
+      return r;
+    };
+    int32_t* rows[2] = {nullptr, nullptr};
+    uint32_t* keys[2] = {nullptr, nullptr};
+    void* vals[2] = {nullptr, nullptr};
+    rows[1] = (int32_t*)take(szRows);
+    if (multi) rows[0] = (int32_t*)take(szRows);
+    keys[0] = (uint32_t*)take(szKeys);
+    if (multi) keys[1] = (uint32_t*)take(szKeys);
+    for (int i = 0; i < nVals; ++i) vals[i] = take(szVals);
+    int32_t* hist = (int32_t*)take(szHist);
+    int64_t* off = (int64_t*)take(szOff);
+    int64_t* tmp = (int64_t*)take(szTmp);
+    int32_t* err = (int32_t*)take(256);
+    launch_fill_i32(err, 0, 1, s);
+    launch_transpose(tp, m, n, nnz, dA_row_ptr, a_rowptr64, dA_col, dA_val, vb, dT_row_ptr,
+                     t_rowptr64, dT_col, dT_val, rows, keys, vals, hist, off, tmp, err, s);
+    check_launch("transpose");
+    int32_t herr = 0;
+    HIP_CHECK(hipMemcpyAsync(&herr, err, sizeof(herr), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    if (herr & kErrCsr) throw Error{SPGEMM_ERR_INVALID_CSR, "column index outside [0, n)"};
+  } catch (const Error& e) {
+    g_thread_error = e.msg;
+    st = e.st;
+  }
+  (void)hipFreeAsync(buf, s);
+  return st;
+}

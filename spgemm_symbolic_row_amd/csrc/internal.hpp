@@ -123,8 +123,9 @@ void launch_scan_i32(const int32_t* in, int64_t n, int64_t* out, int64_t* tmp, h
 // cnt/fill: nbins int32 scratch; start: nbins+1 int32 (bin offsets).
 void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int32_t* fill,
                      int32_t* start, int32_t* out, hipStream_t s);
-// Scratch entries (int64) launch_row_info needs for its per-work-group partials.
-int64_t row_info_partials(int64_t m);
+// Scratch entries (int64) launch_row_info needs for its per-work-group
+// partials and its list of long rows.
+int64_t row_info_partials(int64_t m, int64_t nnzA);
 // rowWin (null: no window bins) receives, for light rows of the first
 // winBins bins whose products fit their bin's window, the span's first
 // column and its length in 32-bit words (see RowArgs); those rows get bin
@@ -133,8 +134,9 @@ int64_t row_info_partials(int64_t m);
 // bSpan: first and last column of every B row (launch_b_span), needed with
 // rowWin.
 void launch_b_span(int64_t K, const int32_t* brp, const int32_t* bcol, int2* span, hipStream_t s);
-void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
-                     const int2* bSpan, int64_t tau, const int32_t* caps, int nbins,
+void launch_row_info(int64_t m, int64_t nnzA, const int32_t* arp, const int32_t* acol,
+                     const int32_t* brp, const int2* bSpan, int64_t tau, const int32_t* caps,
+                     int nbins,
                      int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* rowWin,
                      int winBins, int32_t* winMax, int64_t* part, int64_t* stats,
                      hipStream_t s);
@@ -263,10 +265,12 @@ void launch_multisplit(bool f64, int64_t E, int32_t blockElems, const int64_t* r
 // Heavy-row entries of rows[0..hb) in row order: entry t of local row q sits
 // at rowEntry[q] - rowEntry[0] + (j - arp[rows[q]]); eB = B row start, nb =
 // products, eVal = A value.
-void launch_expand_entries(bool f64, int64_t hb, const int32_t* rows, const int64_t* rowEntry,
+// eOff receives nE + 1 flattened product offsets (eOff[nE] = chatRowPtr[hb]).
+void launch_expand_entries(bool f64, int64_t nE, int64_t hb, const int32_t* rows,
+                           const int64_t* rowEntry, const int64_t* chatRowPtr,
                            const int32_t* arp, const int32_t* acol, const void* aval,
-                           const int32_t* brp, int32_t* eB, int64_t* nb, void* eVal,
-                           hipStream_t s);
+                           const int32_t* brp, const int32_t* scanA, int32_t* eB, int64_t* eOff,
+                           void* eVal, hipStream_t s);
 // Final-chunk descriptors: from a level's light positions [first, first+n)
 // or, when there is no multisplit, from the heavy rows themselves.
 void launch_final_from_level(int64_t first, int64_t n, const int64_t* newOff,
@@ -331,5 +335,25 @@ void launch_mcl_count(int64_t m, const void* rp, int rp64, const int32_t* col, c
 void launch_mcl_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
                      bool f64, double thr, const int64_t* outOff, const double* colsum,
                      int32_t* ocol, void* oval, hipStream_t s);
+
+// ---- k_transpose.hip ----
+// Stable radix sort of A's entries on their column: `passes` digits of
+// digitBits bits cover totalBits bits (2^totalBits >= n); every pass works on
+// `tiles` tiles and histElems = 2^digitBits * tiles counters.
+struct TransposePlan {
+  int passes, digitBits, totalBits;
+  int64_t tiles, histElems;
+};
+TransposePlan transpose_plan(int64_t n, int64_t nnz);
+// rows[1] receives A's row indices; rows[0], keys[1] are needed when
+// passes > 1, vals[0] when passes > 1 and values are given, vals[1] when
+// passes > 2; keys[0] always (nnz > 0).  hist: histElems int32, off:
+// histElems + 1 int64, scanTmp: scan_tmp_elems(histElems) int64.  aval null:
+// pattern only.  err receives kErrCsr for a column outside [0, n).
+void launch_transpose(const TransposePlan& tp, int64_t m, int64_t n, int64_t nnz, const void* arp,
+                      int arp64, const int32_t* acol, const void* aval, int valBytes,
+                      void* trp, int trp64, int32_t* tcol, void* tval, int32_t* rows[2],
+                      uint32_t* keys[2], void* vals[2], int32_t* hist, int64_t* off,
+                      int64_t* scanTmp, int32_t* err, hipStream_t s);
 
 }  // namespace sg

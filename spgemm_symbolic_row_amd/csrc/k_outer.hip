@@ -167,47 +167,53 @@ __global__ __launch_bounds__(kNT) void k_outer_product(int64_t Ph, const int64_t
   }
 }
 
-// Heavy-row entries in row order (one wave per heavy row): B row start,
-// product count and A value of each.
+// Heavy-row entries in row order: B row start, A value and flattened product
+// offset of each (entry t of the batch; rowEntry: entry prefix over the
+// batch's rows, absolute; chatRowPtr: product prefix over them, from 0).
+// One thread per entry, so rows of 10^4 entries spread over the grid: a wave
+// finds the row of its first entry by a search over rowEntry, each lane walks
+// forward from there.  offset = product start of the row + the row-local
+// offset the row pass stored in scanA.
 template <typename V>
-__global__ __launch_bounds__(kNT) void k_expand_entries(int64_t hb, const int32_t* __restrict__ rows,
-                                                        const int64_t* __restrict__ rowEntry,
-                                                        const int32_t* __restrict__ arp,
-                                                        const int32_t* __restrict__ acol,
-                                                        const V* __restrict__ aval,
-                                                        const int32_t* __restrict__ brp,
-                                                        int32_t* __restrict__ eB,
-                                                        int64_t* __restrict__ nb,
-                                                        V* __restrict__ eVal) {
-  const int64_t q = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
-  if (q >= hb) return;
+__global__ __launch_bounds__(kNT) void k_expand_entries(
+    int64_t nE, int64_t hb, const int32_t* __restrict__ rows,
+    const int64_t* __restrict__ rowEntry, const int64_t* __restrict__ chatRowPtr,
+    const int32_t* __restrict__ arp, const int32_t* __restrict__ acol,
+    const V* __restrict__ aval, const int32_t* __restrict__ brp,
+    const int32_t* __restrict__ scanA, int32_t* __restrict__ eB, int64_t* __restrict__ eOff,
+    V* __restrict__ eVal) {
+  const int64_t t0 = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave * kWave;
+  if (t0 >= nE) return;
+  const int64_t base = rowEntry[0];
+  int64_t q = wave_last_le(rowEntry, 0, hb, t0 + base);
+  const int64_t t = t0 + lane_id();
+  if (t >= nE) return;
+  while (q + 1 < hb && rowEntry[q + 1] <= t + base) ++q;
   const int32_t row = rows[q];
-  const int64_t base = rowEntry[q] - rowEntry[0];
-  const int32_t j0 = arp[row], j1 = arp[row + 1];
-  for (int32_t j = j0 + lane_id(); j < j1; j += kWave) {
-    const int32_t k = acol[j];
-    const int64_t t = base + (j - j0);
-    const int32_t b0 = brp[k];
-    eB[t] = b0;
-    nb[t] = brp[k + 1] - b0;
-    if (eVal) eVal[t] = aval[j];
-  }
+  const int64_t j = arp[row] + (t + base - rowEntry[q]);
+  eB[t] = brp[acol[j]];
+  eOff[t] = chatRowPtr[q] + scanA[j];
+  if (eVal) eVal[t] = aval[j];
+  if (t == nE - 1) eOff[nE] = chatRowPtr[hb];
 }
 
 }  // namespace
 
-void launch_expand_entries(bool f64, int64_t hb, const int32_t* rows, const int64_t* rowEntry,
+void launch_expand_entries(bool f64, int64_t nE, int64_t hb, const int32_t* rows,
+                           const int64_t* rowEntry, const int64_t* chatRowPtr,
                            const int32_t* arp, const int32_t* acol, const void* aval,
-                           const int32_t* brp, int32_t* eB, int64_t* nb, void* eVal,
-                           hipStream_t s) {
-  if (hb <= 0) return;
-  const unsigned g = grid_for(hb * kWave, kNT);
+                           const int32_t* brp, const int32_t* scanA, int32_t* eB, int64_t* eOff,
+                           void* eVal, hipStream_t s) {
+  if (hb <= 0 || nE <= 0) return;
+  const unsigned g = grid_for(nE, kNT);
   if (f64)
-    hipLaunchKernelGGL(k_expand_entries<double>, dim3(g), dim3(kNT), 0, s, hb, rows, rowEntry, arp,
-                       acol, (const double*)aval, brp, eB, nb, (double*)eVal);
+    hipLaunchKernelGGL(k_expand_entries<double>, dim3(g), dim3(kNT), 0, s, nE, hb, rows, rowEntry,
+                       chatRowPtr, arp, acol, (const double*)aval, brp, scanA, eB, eOff,
+                       (double*)eVal);
   else
-    hipLaunchKernelGGL(k_expand_entries<float>, dim3(g), dim3(kNT), 0, s, hb, rows, rowEntry, arp,
-                       acol, (const float*)aval, brp, eB, nb, (float*)eVal);
+    hipLaunchKernelGGL(k_expand_entries<float>, dim3(g), dim3(kNT), 0, s, nE, hb, rows, rowEntry,
+                       chatRowPtr, arp, acol, (const float*)aval, brp, scanA, eB, eOff,
+                       (float*)eVal);
 }
 
 void launch_csc_count(int64_t h, const int32_t* xheavy, const int32_t* arp, const int32_t* acol,

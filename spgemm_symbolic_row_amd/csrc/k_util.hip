@@ -188,10 +188,91 @@ __global__ __launch_bounds__(kNT) void k_bin_scatter(const uint8_t* __restrict__
 // stores the row-local exclusive offset of every entry (the flattened
 // product index where that entry's scaled B row starts).  The row total is
 // P_i; its bin is 0 when P_i == 0, 1 + (first cap >= P_i) when P_i <= tau,
-// and nbins + 1 (heavy) otherwise.
+// and nbins + 1 (heavy) otherwise.  Each lane takes kRowItems consecutive
+// entries per round, so the dependent A.col -> B.row_ptr loads of several
+// entries are in flight together.
+// Rows of more than kLongRow entries are listed for k_row_info_long, where a
+// whole work group scans one row at a time: walked by G lanes, such a row
+// would take hundreds of rounds of dependent loads (power-law matrices hold
+// rows of 10^4 entries).
 // The totals are reduced per work group in LDS and written as one partial
 // per work group (part[blockIdx.x * 8 + i]); k_row_stats folds them, so no
 // two work groups update the same global address.
+constexpr int kRowItems = 4;
+constexpr int kLongRow = 1024;
+constexpr int kLongNT = 1024;
+constexpr int kLongItems = 4;
+constexpr int kRowInfoBlocks = 2048;
+constexpr int kLongBlocks = 256;
+
+struct RowTotals {
+  unsigned long long P, Ph, Ah, Max, H, L, W;
+  int32_t Wm[64];  // widest window of each bin, in 32-bit words
+  int32_t caps[64];
+};
+
+__device__ __forceinline__ void totals_init(RowTotals& t, const int32_t* caps, int nbins) {
+  if (threadIdx.x == 0) t.P = t.Ph = t.Ah = t.Max = t.H = t.L = t.W = 0;
+  if (threadIdx.x < 64) {
+    t.Wm[threadIdx.x] = 0;
+    t.caps[threadIdx.x] = threadIdx.x < nbins ? caps[threadIdx.x] : INT_MAX;
+  }
+}
+
+__device__ __forceinline__ int light_bin(const RowTotals& t, int64_t p, int64_t tau, int nbins) {
+  int lb = 0;
+  if (p > 0 && p <= tau)
+    while (lb < nbins - 1 && p > t.caps[lb]) ++lb;
+  return lb;
+}
+
+// Bin, window and totals of one row (called by one lane per row).
+__device__ __forceinline__ void finish_row(RowTotals& t, int64_t row, int64_t p, int64_t alen,
+                                           int lb, int32_t lo, int32_t hi, int64_t tau,
+                                           int nbins, int winBins, int64_t* __restrict__ rowP,
+                                           uint8_t* __restrict__ rowBin,
+                                           int64_t* __restrict__ rowWin) {
+  rowP[row] = p;
+  uint8_t bin;
+  if (p == 0) {
+    bin = 0;
+  } else if (p > tau) {
+    bin = (uint8_t)(nbins + 1);
+    atomicAdd(&t.Ph, (unsigned long long)p);
+    atomicAdd(&t.Ah, (unsigned long long)alen);
+    atomicAdd(&t.H, 1ull);
+  } else {
+    bin = (uint8_t)(1 + lb);
+    const int64_t span = (int64_t)hi - lo + 1;
+    if (lb < winBins && span <= 32 * (int64_t)window_words(t.caps[lb])) {
+      bin = (uint8_t)(nbins + 2 + lb);
+      rowWin[row] = ((span + 31) / 32) << 32 | (int64_t)(uint32_t)lo;
+      atomicMax(&t.Wm[lb], (int32_t)((span + 31) / 32));
+      atomicAdd(&t.W, (unsigned long long)p);
+    }
+    atomicAdd(&t.L, 1ull);
+  }
+  rowBin[row] = bin;
+  atomicAdd(&t.P, (unsigned long long)p);
+  atomicMax(&t.Max, (unsigned long long)p);
+}
+
+__device__ __forceinline__ void totals_write(const RowTotals& t, int64_t* __restrict__ q,
+                                             int winBins, int32_t* __restrict__ winMax) {
+  if (threadIdx.x == 0) {
+    q[kStatProducts] = (int64_t)t.P;
+    q[kStatHeavyProducts] = (int64_t)t.Ph;
+    q[kStatHeavyANnz] = (int64_t)t.Ah;
+    q[kStatMaxRowProducts] = (int64_t)t.Max;
+    q[kStatHeavyRows] = (int64_t)t.H;
+    q[kStatLightRows] = (int64_t)t.L;
+    q[kStatDenseElems] = (int64_t)t.W;
+  }
+  // Widest window of each bin, for the LDS the window kernels reserve.
+  if (threadIdx.x < winBins && t.Wm[threadIdx.x] > 0)
+    atomicMax(&winMax[threadIdx.x], t.Wm[threadIdx.x]);
+}
+
 template <int G>
 __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __restrict__ arp,
                                                   const int32_t* __restrict__ acol,
@@ -203,46 +284,69 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
                                                   uint8_t* __restrict__ rowBin,
                                                   int64_t* __restrict__ rowWin, int winBins,
                                                   int32_t* __restrict__ winMax,
-                                                  int64_t* __restrict__ part) {
-  __shared__ unsigned long long sP, sPh, sAh, sMax, sH, sL, sW;
-  __shared__ int32_t sWm[64];
-  if (threadIdx.x == 0) sP = sPh = sAh = sMax = sH = sL = sW = 0;
-  if (threadIdx.x < 64) sWm[threadIdx.x] = 0;
+                                                  int64_t* __restrict__ part,
+                                                  int32_t* __restrict__ longCount,
+                                                  int32_t* __restrict__ longRows) {
+  __shared__ RowTotals tot;
+  totals_init(tot, caps, nbins);
   __syncthreads();
   const int gl = threadIdx.x % G;
   const int64_t rowsPerPass = (int64_t)gridDim.x * (kNT / G);
   for (int64_t row = ((int64_t)blockIdx.x * kNT + threadIdx.x) / G; row < m; row += rowsPerPass) {
     const int64_t rs = arp[row], re = arp[row + 1];
+    if (re - rs > kLongRow) {
+      if (gl == 0) longRows[atomicAdd(longCount, 1)] = (int32_t)row;
+      continue;
+    }
     int64_t p = 0;
-    for (int64_t b = rs; b < re; b += G) {
-      const int64_t j = b + gl;
-      int64_t nb = 0;
-      if (j < re) {
-        const int32_t k = acol[j];
-        nb = (int64_t)brp[k + 1] - brp[k];
+    for (int64_t b = rs; b < re; b += G * kRowItems) {
+      const int64_t j0 = b + (int64_t)gl * kRowItems;
+      int32_t k[kRowItems];
+      int64_t nb[kRowItems];
+#pragma unroll
+      for (int u = 0; u < kRowItems; ++u) k[u] = j0 + u < re ? acol[j0 + u] : -1;
+      int64_t sum = 0;
+#pragma unroll
+      for (int u = 0; u < kRowItems; ++u) {
+        nb[u] = k[u] >= 0 ? (int64_t)brp[k[u] + 1] - brp[k[u]] : 0;
+        sum += nb[u];
       }
-      int64_t inc = nb;
+      int64_t inc = sum;
 #pragma unroll
       for (int d = 1; d < G; d <<= 1) {
         const int64_t t = __shfl_up(inc, d, G);
         if (gl >= d) inc += t;
       }
-      if (j < re) scanA[j] = (int32_t)(p + inc - nb);
+      int64_t ex = p + inc - sum;
+#pragma unroll
+      for (int u = 0; u < kRowItems; ++u) {
+        if (j0 + u < re) scanA[j0 + u] = (int32_t)ex;
+        ex += nb[u];
+      }
       p += __shfl(inc, G - 1, G);
     }
     // Light rows of a bin with dense windows: span of the row's products,
     // from the first column of its first-starting B row to the last column
     // of its last-ending one (B rows are sorted; empty ones hold an empty
     // span).
-    int lb = 0;
-    if (p > 0 && p <= tau)
-      while (lb < nbins - 1 && p > caps[lb]) ++lb;
+    const int lb = light_bin(tot, p, tau, nbins);
     int32_t lo = INT_MAX, hi = -1;
     if (p > 0 && p <= tau && lb < winBins) {
-      for (int64_t j = rs + gl; j < re; j += G) {
-        const int2 sp = bSpan[acol[j]];
-        lo = sp.x < lo ? sp.x : lo;
-        hi = sp.y > hi ? sp.y : hi;
+      for (int64_t b = rs; b < re; b += G * kRowItems) {
+        int32_t k[kRowItems];
+#pragma unroll
+        for (int u = 0; u < kRowItems; ++u) {
+          const int64_t j = b + gl + (int64_t)u * G;
+          k[u] = j < re ? acol[j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kRowItems; ++u) {
+          if (k[u] >= 0) {
+            const int2 sp = bSpan[k[u]];
+            lo = sp.x < lo ? sp.x : lo;
+            hi = sp.y > hi ? sp.y : hi;
+          }
+        }
       }
 #pragma unroll
       for (int d = 1; d < G; d <<= 1) {
@@ -251,47 +355,84 @@ __global__ __launch_bounds__(kNT) void k_row_info(int64_t m, const int32_t* __re
         hi = h2 > hi ? h2 : hi;
       }
     }
-    if (gl == 0) {
-      rowP[row] = p;
-      uint8_t bin;
-      if (p == 0) {
-        bin = 0;
-      } else if (p > tau) {
-        bin = (uint8_t)(nbins + 1);
-        atomicAdd(&sPh, (unsigned long long)p);
-        atomicAdd(&sAh, (unsigned long long)(re - rs));
-        atomicAdd(&sH, 1ull);
-      } else {
-        const int b = lb;
-        bin = (uint8_t)(1 + b);
-        const int64_t span = (int64_t)hi - lo + 1;
-        if (b < winBins && span <= 32 * (int64_t)window_words(caps[b])) {
-          bin = (uint8_t)(nbins + 2 + b);
-          rowWin[row] = ((span + 31) / 32) << 32 | (int64_t)(uint32_t)lo;
-          atomicMax(&sWm[b], (int32_t)((span + 31) / 32));
-          atomicAdd(&sW, (unsigned long long)p);
-        }
-        atomicAdd(&sL, 1ull);
-      }
-      rowBin[row] = bin;
-      atomicAdd(&sP, (unsigned long long)p);
-      atomicMax(&sMax, (unsigned long long)p);
-    }
+    if (gl == 0)
+      finish_row(tot, row, p, re - rs, lb, lo, hi, tau, nbins, winBins, rowP, rowBin, rowWin);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t* q = part + (int64_t)blockIdx.x * 8;
-    q[kStatProducts] = (int64_t)sP;
-    q[kStatHeavyProducts] = (int64_t)sPh;
-    q[kStatHeavyANnz] = (int64_t)sAh;
-    q[kStatMaxRowProducts] = (int64_t)sMax;
-    q[kStatHeavyRows] = (int64_t)sH;
-    q[kStatLightRows] = (int64_t)sL;
-    q[kStatDenseElems] = (int64_t)sW;
+  totals_write(tot, part + (int64_t)blockIdx.x * 8, winBins, winMax);
+}
+
+// The rows k_row_info listed: one work group per row, kLongItems
+// consecutive entries per thread per round, a work-group scan per round.
+// Writes its partials after the short-row grid's.
+__global__ __launch_bounds__(kLongNT) void k_row_info_long(
+    const int32_t* __restrict__ longCount, const int32_t* __restrict__ longRows,
+    const int32_t* __restrict__ arp, const int32_t* __restrict__ acol,
+    const int32_t* __restrict__ brp, const int2* __restrict__ bSpan, int64_t tau,
+    const int32_t* __restrict__ caps, int nbins, int64_t* __restrict__ rowP,
+    int32_t* __restrict__ scanA, uint8_t* __restrict__ rowBin, int64_t* __restrict__ rowWin,
+    int winBins, int32_t* __restrict__ winMax, int64_t* __restrict__ part) {
+  __shared__ RowTotals tot;
+  __shared__ int64_t wtot[kLongNT / kWave];
+  __shared__ int32_t wlo[kLongNT / kWave], whi[kLongNT / kWave];
+  totals_init(tot, caps, nbins);
+  __syncthreads();
+  const int32_t cnt = *longCount;
+  for (int32_t i = blockIdx.x; i < cnt; i += gridDim.x) {
+    const int64_t row = longRows[i];
+    const int64_t rs = arp[row], re = arp[row + 1];
+    int64_t p = 0;
+    for (int64_t b = rs; b < re; b += (int64_t)kLongNT * kLongItems) {
+      const int64_t j0 = b + (int64_t)threadIdx.x * kLongItems;
+      int32_t k[kLongItems];
+      int64_t nb[kLongItems];
+#pragma unroll
+      for (int u = 0; u < kLongItems; ++u) k[u] = j0 + u < re ? acol[j0 + u] : -1;
+      int64_t sum = 0;
+#pragma unroll
+      for (int u = 0; u < kLongItems; ++u) {
+        nb[u] = k[u] >= 0 ? (int64_t)brp[k[u] + 1] - brp[k[u]] : 0;
+        sum += nb[u];
+      }
+      int64_t total;
+      int64_t ex = p + block_excl_scan<kLongNT>(sum, wtot, &total);
+#pragma unroll
+      for (int u = 0; u < kLongItems; ++u) {
+        if (j0 + u < re) scanA[j0 + u] = (int32_t)ex;
+        ex += nb[u];
+      }
+      p += total;
+    }
+    const int lb = light_bin(tot, p, tau, nbins);
+    int32_t lo = INT_MAX, hi = -1;
+    if (p > 0 && p <= tau && lb < winBins) {
+      for (int64_t j = rs + threadIdx.x; j < re; j += kLongNT) {
+        const int2 sp = bSpan[acol[j]];
+        lo = sp.x < lo ? sp.x : lo;
+        hi = sp.y > hi ? sp.y : hi;
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        const int32_t l2 = __shfl_xor(lo, d), h2 = __shfl_xor(hi, d);
+        lo = l2 < lo ? l2 : lo;
+        hi = h2 > hi ? h2 : hi;
+      }
+      if (lane_id() == 0) {
+        wlo[threadIdx.x / kWave] = lo;
+        whi[threadIdx.x / kWave] = hi;
+      }
+      __syncthreads();
+      for (int w = 0; w < kLongNT / kWave; ++w) {
+        lo = wlo[w] < lo ? wlo[w] : lo;
+        hi = whi[w] > hi ? whi[w] : hi;
+      }
+    }
+    if (threadIdx.x == 0)
+      finish_row(tot, row, p, re - rs, lb, lo, hi, tau, nbins, winBins, rowP, rowBin, rowWin);
+    __syncthreads();
   }
-  // Widest window of each bin, for the LDS the window kernels reserve.
-  if (threadIdx.x < winBins && sWm[threadIdx.x] > 0)
-    atomicMax(&winMax[threadIdx.x], sWm[threadIdx.x]);
+  __syncthreads();
+  totals_write(tot, part + (int64_t)blockIdx.x * 8, winBins, winMax);
 }
 
 // First and last column of every B row (rows are sorted).
@@ -459,23 +600,38 @@ void launch_bin_sort(const uint8_t* key, int64_t n, int nbins, int32_t* cnt, int
   }
 }
 
-int64_t row_info_partials(int64_t m) {
-  const int64_t g = (m * 16 + kNT - 1) / kNT;
-  return (g < 1 ? 1 : (g > 65535 ? 65535 : g)) * 8;
+namespace {
+unsigned row_info_grid(int64_t m) {
+  unsigned g = grid_for(m * 16, kNT);
+  return g > (unsigned)kRowInfoBlocks ? (unsigned)kRowInfoBlocks : g;
+}
+}  // namespace
+
+int64_t row_info_partials(int64_t m, int64_t nnzA) {
+  // partials of both grids, the long-row count, the long-row list
+  return ((int64_t)row_info_grid(m) + kLongBlocks) * 8 + 1 + (nnzA / kLongRow + 2) / 2;
 }
 
-void launch_row_info(int64_t m, const int32_t* arp, const int32_t* acol, const int32_t* brp,
-                     const int2* bSpan, int64_t tau, const int32_t* caps, int nbins,
-                     int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* rowWin,
+void launch_row_info(int64_t m, int64_t nnzA, const int32_t* arp, const int32_t* acol,
+                     const int32_t* brp, const int2* bSpan, int64_t tau, const int32_t* caps,
+                     int nbins, int64_t* rowP, int32_t* scanA, uint8_t* rowBin, int64_t* rowWin,
                      int winBins, int32_t* winMax, int64_t* part, int64_t* stats,
                      hipStream_t s) {
   if (m <= 0) return;
   constexpr int G = 16;
-  unsigned g = grid_for(m * G, kNT);
-  if (g > 65535) g = 65535;
+  const unsigned g = row_info_grid(m);
+  int64_t* partLong = part + (int64_t)g * 8;
+  int32_t* longCount = (int32_t*)(part + ((int64_t)g + kLongBlocks) * 8);
+  int32_t* longRows = longCount + 2;
+  (void)nnzA;
+  launch_fill_i32(longCount, 0, 1, s);
   hipLaunchKernelGGL(k_row_info<G>, dim3(g), dim3(kNT), 0, s, m, arp, acol, brp, bSpan, tau, caps,
-                     nbins, rowP, scanA, rowBin, rowWin, rowWin ? winBins : 0, winMax, part);
-  hipLaunchKernelGGL(k_row_stats, dim3(1), dim3(kNT), 0, s, (int64_t)g, part, stats);
+                     nbins, rowP, scanA, rowBin, rowWin, rowWin ? winBins : 0, winMax, part,
+                     longCount, longRows);
+  hipLaunchKernelGGL(k_row_info_long, dim3(kLongBlocks), dim3(kLongNT), 0, s, longCount, longRows,
+                     arp, acol, brp, bSpan, tau, caps, nbins, rowP, scanA, rowBin, rowWin,
+                     rowWin ? winBins : 0, winMax, partLong);
+  hipLaunchKernelGGL(k_row_stats, dim3(1), dim3(kNT), 0, s, (int64_t)g + kLongBlocks, part, stats);
 }
 
 void launch_b_span(int64_t K, const int32_t* brp, const int32_t* bcol, int2* span, hipStream_t s) {

@@ -27,7 +27,8 @@ import numpy as np
 
 __all__ = [
     "CSR", "erdos_renyi", "laplacian27", "rmat", "planted_partition",
-    "random_csr", "identity", "workload",
+    "random_csr", "identity", "workload", "rmat_rect", "sparse_uniform", "aggregation",
+    "grid_aggregation",
 ]
 
 
@@ -246,6 +247,71 @@ def identity(n: int, dtype=np.float64) -> CSR:
                np.ones(n, dtype=dtype), n, n)
 
 
+def rmat_rect(row_scale: int, col_scale: int, edges_per_row: int = 16,
+              abcd=(0.57, 0.19, 0.19, 0.05), seed: int = 0, dtype=np.float64) -> CSR:
+    """Rectangular R-MAT: 2^row_scale x 2^col_scale, edges_per_row * 2^row_scale
+    edges.  The first min(row_scale, col_scale) bits of both indices come from
+    quadrant choices as in rmat(); the remaining bits of the longer index use
+    that index's marginal (c + d for a row bit, b + d for a column bit).
+    Duplicates merged, one uniform [0,1) value per entry."""
+    a, b, c, d = abcd
+    m, n = 1 << row_scale, 1 << col_scale
+    E = edges_per_row * m
+    rng = np.random.default_rng(seed)
+    r = np.zeros(E, dtype=np.int64)
+    q = np.zeros(E, dtype=np.int64)
+    for lvl in range(max(row_scale, col_scale)):
+        u = rng.random(E)
+        if lvl < min(row_scale, col_scale):
+            r = (r << 1) | (u >= a + b)
+            q = (q << 1) | (((u >= a) & (u < a + b)) | (u >= a + b + c))
+        elif row_scale > col_scale:
+            r = (r << 1) | (u < c + d)
+        else:
+            q = (q << 1) | (u < b + d)
+    keys = np.unique(r * n + q)
+    val = rng.random(keys.shape[0]).astype(dtype)
+    return _from_sorted_keys(keys, m, n, val)
+
+
+def sparse_uniform(m: int, n: int, per_row: float, seed: int, dtype=np.float64,
+                   values: str = "uniform") -> CSR:
+    """About per_row * m entries at uniform random positions of an m x n
+    matrix (duplicates merged); values U[-1,1) or small integers ("int")."""
+    rng = np.random.default_rng(seed)
+    E = int(per_row * m)
+    keys = np.unique(rng.integers(0, m * n, size=E, dtype=np.int64)) if m * n else \
+        np.zeros(0, np.int64)
+    if values == "int":
+        val = rng.integers(-3, 4, size=keys.shape[0]).astype(dtype)
+    else:
+        val = rng.uniform(-1.0, 1.0, size=keys.shape[0]).astype(dtype)
+    return _from_sorted_keys(keys, m, n, val)
+
+
+def aggregation(n_fine: int, agg_size: int, seed: int = 0, dtype=np.float64) -> CSR:
+    """Piecewise-constant aggregation operator, n_fine x ceil(n_fine/agg_size):
+    the fine points, in a random order, are cut into aggregates of agg_size
+    (the last may be smaller); R[i, agg(i)] = 1, one entry per row."""
+    rng = np.random.default_rng(seed)
+    nc = (n_fine + agg_size - 1) // agg_size
+    agg = np.empty(n_fine, dtype=np.int64)
+    agg[rng.permutation(n_fine)] = np.arange(n_fine, dtype=np.int64) // agg_size
+    return CSR(np.arange(n_fine + 1, dtype=np.int32), agg.astype(np.int32),
+               np.ones(n_fine, dtype=dtype), n_fine, nc)
+
+
+def grid_aggregation(nx: int, a: int, dtype=np.float64) -> CSR:
+    """Aggregation of an nx^3 grid (index x + nx*(y + nx*z)) into a x a x a
+    blocks: R[i, block(i)] = 1, nx^3 x ceil(nx/a)^3."""
+    nb = (nx + a - 1) // a
+    i = np.arange(nx ** 3, dtype=np.int64)
+    x, y, z = i % nx, (i // nx) % nx, i // (nx * nx)
+    blk = (x // a) + nb * ((y // a) + nb * (z // a))
+    return CSR(np.arange(nx ** 3 + 1, dtype=np.int32), blk.astype(np.int32),
+               np.ones(nx ** 3, dtype=dtype), nx ** 3, nb ** 3)
+
+
 # Named workloads: C = A.A for each.
 WORKLOADS = {
     "er4096": "Erdos-Renyi 4096x4096, Poisson(8) per row, fp64 U[-1,1], seed 0",
@@ -253,6 +319,8 @@ WORKLOADS = {
     "rmat18": "R-MAT scale 18, edge factor 16, (0.57,0.19,0.19,0.05), fp64 U[0,1], seed 0",
     "rmat20": "R-MAT scale 20, edge factor 16, (0.57,0.19,0.19,0.05), fp64 U[0,1], seed 0",
     "mcl1m": "planted partition 1000x1000 clusters, 28 intra + 4 inter + self per column, fp32 column-stochastic, seed 0",
+    "rmat_rect": "rectangular R-MAT 2^17 x 2^20, 16 edges per row, (0.57,0.19,0.19,0.05), fp64 U[0,1], seed 0 (operand of A*A^T)",
+    "agg_rmat18": "aggregation operator 2^18 x 2^15, random aggregates of 8, fp64 ones, seed 1 (operand R of A*R with A = rmat18)",
 }
 
 
@@ -269,6 +337,10 @@ def workload(name: str) -> CSR:
         return planted_partition(1000, 1000, 28, 4, seed=0)
     if name == "mcl_iter":
         return planted_partition(100, 1000, 28, 4, seed=0)
+    if name == "rmat_rect":
+        return rmat_rect(17, 20, 16, seed=0)
+    if name == "agg_rmat18":
+        return aggregation(1 << 18, 8, seed=1)
     m = name.split("_")
     if m[0] == "rmat" and len(m) == 2:          # e.g. "rmat_12"
         return rmat(int(m[1]), 16, seed=0)

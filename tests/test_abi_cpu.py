@@ -21,7 +21,8 @@ def test_header_declares_the_boundary():
     for must in ("spgemm_plan", "spgemm_symbolic", "spgemm_numeric", "spgemm_destroy",
                  "spgemm_get_stats", "spgemm_compute_params", "spgemm_status_string",
                  "spgemm_last_error", "spgemm_prune_colnorm_count", "spgemm_prune_colnorm_fill",
-                 "spgemm_prune_destroy"):
+                 "spgemm_prune_destroy", "spgemm_mcl_inflate_count", "spgemm_mcl_inflate_fill",
+                 "spgemm_transpose"):
         assert must in names
 
 
@@ -58,6 +59,15 @@ def test_argument_validation_without_device():
     assert L.spgemm_symbolic(None, dummy, ctypes.byref(ctypes.c_int64())) == -1
     assert L.spgemm_numeric(None, dummy, dummy) == -1
     L.spgemm_destroy(None)
+    # transpose: negative sizes, bad dtype, NULL outputs, int32 range
+    t = L.spgemm_transpose
+    assert t(-1, 1, 1, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, dummy, None) == -1
+    assert t(1, 1, 1, dummy, 0, dummy, dummy, 7, dummy, 0, dummy, dummy, None) == -1
+    assert t(1, 1, 1, dummy, 0, dummy, dummy, 1, None, 0, dummy, dummy, None) == -1
+    assert t(1, 1, 1, dummy, 0, dummy, dummy, 1, dummy, 0, None, dummy, None) == -1
+    assert t(1, 1, 1, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, None, None) == -1
+    assert t(1 << 31, 1, 1, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, dummy, None) == -3
+    assert t(1, 1, 1 << 31, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, dummy, None) == -3
     for s, word in ((0, b"ok"), (-2, b"canonical"), (-3, b"overflow"), (-6, b"order")):
         assert word in L.spgemm_status_string(s)
 
