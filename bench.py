@@ -244,6 +244,8 @@ def main():
     ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
+    ap.add_argument("--light-hash-only", action="store_true",
+                    help="no dense windows for light rows (diagnostics)")
     ap.add_argument("--expansion", type=int, default=-1,
                     help="heavy-row expansion: 0 straight into final chunks, 1 outer product + "
                          "multisplit, 2 first level fed from A and B (default: the library's)")
@@ -295,6 +297,8 @@ def main():
         opts["heavy_threshold"] = args.heavy_threshold
     if args.expansion >= 0:
         opts["expansion"] = args.expansion
+    if args.light_hash_only:
+        opts["light_hash_only"] = 1
     if args.config == "rmat20":
         opts["rowptr64"] = 1   # nnz(C) is about 9.7e9
     if args.config == "mcl_iter":

@@ -23,7 +23,7 @@ constexpr int kMsRowsMax = 512;
 constexpr int kMsItemsF64 = 4;   // elements per thread held in registers
 constexpr int kMsItemsF32 = 8;
 // Straight into final chunks: no LDS staging, so larger tiles.
-constexpr int kXfItemsF64 = 4;
+constexpr int kXfItemsF64 = 8;
 constexpr int kXfItemsF32 = 8;
 constexpr int kXfNBMax = 8192;   // (row, chunk) buckets per work group
 constexpr int kXfEnt = 256;      // entries per tile staged in LDS
@@ -389,7 +389,8 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
                                                       int32_t* __restrict__ err) {
   // LDS (sized by the host): gbase[NB] i64 | bnd[maxRows] i64 |
   // eA[kXfEnt] V | eBase[kXfEnt] i32 | eRow[kXfEnt] i32 |
-  // slotAt[blockElems] i32 | hist[NB] i32 | spanS[NB] i8, NB = maxRows * nreq.
+  // slotAt[blockElems] i32 | hist[NB] i32 | finS[NB] i32 | spanS[NB] i8,
+  // NB = maxRows * nreq.
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kSegs = ITEMS * (kNT / kWave);
   const int NBcap = maxRows * nreq;
@@ -400,7 +401,8 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   int32_t* eRow = eBase + kXfEnt;
   int32_t* slotAt = eRow + kXfEnt;
   int32_t* hist = slotAt + blockElems;
-  int8_t* spanS = (int8_t*)(hist + NBcap);
+  int32_t* finS = hist + NBcap;
+  int8_t* spanS = (int8_t*)(finS + NBcap);
   __shared__ int32_t segLast[kSegs];
   __shared__ TileInfo s_info;
   const int64_t nTiles = (E + blockElems - 1) / blockElems;
@@ -421,6 +423,7 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   for (int i = threadIdx.x; i < NB; i += kNT) {
     hist[i] = 0;
     spanS[i] = spanOf[r0 * nreq + i];
+    finS[i] = finalOf[r0 * nreq + i];
   }
   __syncthreads();
   // Entries with products that start inside the range (and t0, which holds
@@ -429,9 +432,15 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
   // to the element index, a_ik and local row in LDS (later ones are read
   // from memory by their elements, which long tiles of very short entries
   // only need).
+  // (The entry's B offset and a_ik are loaded together with its offsets, so
+  // the pass waits on one round of memory latency.)
   for (int32_t t = t0 + (int32_t)threadIdx.x; t <= s_info.t1; t += kNT) {
     const int64_t o = src.eOff[t];
-    if (src.eOff[t + 1] == o) continue;
+    const int64_t o1 = src.eOff[t + 1];
+    const int32_t eb = src.eB[t];
+    V ea = V(0);
+    if constexpr (kVals) ea = ((const V*)src.eVal)[t];
+    if (o1 == o) continue;
     const int64_t from = o > e0 ? o : e0;
     const int64_t pos = from - e0;
     if (pos >= n) continue;
@@ -439,8 +448,8 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
     slotAt[pos] = j;
     if (j < kXfEnt) {
       eRow[j] = local_row(bnd, nrows, from);
-      eBase[j] = (int32_t)((int64_t)src.eB[t] + e0 - o);
-      if constexpr (kVals) eA[j] = ((const V*)src.eVal)[t];
+      eBase[j] = (int32_t)((int64_t)eb + e0 - o);
+      if constexpr (kVals) eA[j] = ea;
     }
   }
   __syncthreads();
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
     const int32_t c = hist[b];
     int64_t g = 0;
     if (c) {
-      const int32_t q = finalOf[r0 * nreq + b];
+      const int32_t q = finS[b];
       if (q < 0) {
         flag_error(err, kErrCountMismatch);
       } else {
@@ -612,7 +621,7 @@ void launch_expand_final(bool f64, int64_t E, int32_t blockElems, const int64_t*
   const unsigned g = (grid_for(E, blockElems) + kXcds - 1) / kXcds * kXcds;
   const size_t NB = (size_t)maxRows * nreq;
   const size_t vb = !outVal ? 0 : f64 ? 8 : 4;
-  const size_t lds = NB * 13 + (size_t)maxRows * 8 + (size_t)kXfEnt * (vb + 8) +
+  const size_t lds = NB * 17 + (size_t)maxRows * 8 + (size_t)kXfEnt * (vb + 8) +
                      (size_t)blockElems * 4 + 16;
 #define SG_XF1(ITEMS, V, VALS, OC)                                                             \
   hipLaunchKernelGGL((k_expand_final<ITEMS, V, VALS, OC>), dim3(g), dim3(kNT), lds, s, E,        \
