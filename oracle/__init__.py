@@ -57,6 +57,10 @@ def _load():
         lib.oracle_mcl_inflate.argtypes = [i64, i64, vp, vp, vp, ctypes.c_double, ctypes.c_int,
                                            vp, vp, vp, vp]
         lib.oracle_transpose.restype = ctypes.c_int
+        lib.oracle_hll_sketch.restype = ctypes.c_int
+        lib.oracle_hll_sketch.argtypes = [i64, vp, vp, ctypes.c_int, vp]
+        lib.oracle_hll_estimate.restype = ctypes.c_int
+        lib.oracle_hll_estimate.argtypes = [i64, i64, vp, vp, vp, vp, ctypes.c_int, vp, vp]
         lib.oracle_transpose.argtypes = [i64, i64, vp, vp, vp, ctypes.c_int, vp, vp, vp]
         _lib = lib
     return _lib
@@ -216,3 +220,73 @@ def transpose(A) -> CSRMatrix:
     if rc != 0:
         raise MemoryError("oracle_transpose failed")
     return CSRMatrix(trp, tc[:nnz].copy(), None if tv is None else tv[:nnz].copy(), A.n, A.m)
+
+
+# --- Ocean's size-prediction workflows (Ocean page, §3 and its Table 1) ---
+
+def hll_sketch(B, M: int) -> np.ndarray:
+    """Per-row HyperLogLog registers of B: uint8 array (B.m, M)."""
+    lib = _load()
+    brp, bcol = _c(B.row_ptr, np.int32), _c(B.col, np.int32)
+    regs = np.zeros((max(B.m, 1), M), dtype=np.uint8)
+    if lib.oracle_hll_sketch(B.m, _p(brp), _p(bcol), M, _p(regs)) != 0:
+        raise ValueError("M must be 32 or 64")
+    return regs[:B.m]
+
+
+def hll_estimate(A, B, M: int, r0: int = 0, r1: int | None = None, with_regs: bool = False):
+    """HyperLogLog estimate of nnz(C_i) for rows [r0, r1) of C = A*B, from a
+    sketch of each row's product columns (float64; registers on request)."""
+    lib = _load()
+    r1 = A.m if r1 is None else r1
+    arp, acol = _c(A.row_ptr, np.int32), _c(A.col, np.int32)
+    brp, bcol = _c(B.row_ptr, np.int32), _c(B.col, np.int32)
+    est = np.zeros(max(r1 - r0, 1), dtype=np.float64)
+    regs = np.zeros((max(r1 - r0, 1), M), dtype=np.uint8) if with_regs else None
+    if lib.oracle_hll_estimate(r0, r1, _p(arp), _p(acol), _p(brp), _p(bcol), M, _p(est),
+                               _p(regs)) != 0:
+        raise ValueError("M must be 32 or 64")
+    est = est[:r1 - r0]
+    return (est, regs[:r1 - r0]) if with_regs else est
+
+
+def hll_registers(products: int, nnz_a: int) -> int:
+    """Sketch size: 32 registers when the input expansion ratio
+    products / nnz(A) is below 48, else 64 (Ocean §4, parameters)."""
+    return 32 if products < 48 * max(nnz_a, 1) else 64
+
+
+def hll_coefficient(M: int) -> float:
+    """Estimates are scaled by 1.5 (2.0 with 32 registers) before sizing
+    (Ocean §5.3)."""
+    return 2.0 if M == 32 else 1.5
+
+
+def capacity(P: np.ndarray, est: np.ndarray | None, coef: float) -> np.ndarray:
+    """Output slots reserved per row: the upper bound P_i, or with an estimate
+    min(P_i, ceil(coef * est_i)) and at least 1 for a row with products."""
+    P = np.asarray(P, dtype=np.int64)
+    if est is None:
+        return P.copy()
+    c = np.ceil(coef * np.asarray(est, dtype=np.float64)).astype(np.int64)
+    c = np.minimum(c, P)
+    return np.where(P > 0, np.maximum(c, 1), 0)
+
+
+def sample_rows(m: int) -> np.ndarray:
+    """Rows sampled for the compression ratio: 3% of the rows, at least 600
+    and at most 10,000 (all rows when fewer), evenly spaced."""
+    s = min(m, min(10000, max(600, int(round(0.03 * m)))))
+    return (np.arange(s, dtype=np.int64) * m) // max(s, 1)
+
+
+def select_workflow(m: int, nnz_a: int, products: int, sampled_cr: float | None) -> int:
+    """Ocean's Table 1: 1 = upper bound when the average products per row is
+    below 64; else 2 = HyperLogLog estimation when the expansion ratio
+    products / nnz(A) and the sampled compression ratio are both >= 8; else
+    0 = symbolic."""
+    if products < 64 * m:
+        return 1
+    if products >= 8 * nnz_a and sampled_cr is not None and sampled_cr >= 8.0:
+        return 2
+    return 0

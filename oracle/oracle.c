@@ -19,6 +19,7 @@
 #include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+#include <string.h>
 
 int64_t oracle_row_products(int64_t r0, int64_t r1, const int32_t *a_rp,
                                  const int32_t *a_col, const int32_t *b_rp,
@@ -265,5 +266,76 @@ int oracle_transpose(int64_t m, int64_t n, const int64_t *a_rp,
     }
   }
   free(next);
+  return 0;
+}
+
+/* MurmurHash3's 32-bit finaliser (fmix32), as published with MurmurHash3. */
+static uint32_t hll_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x85ebca6bu;
+  x ^= x >> 13;
+  x *= 0xc2b2ae35u;
+  x ^= x >> 16;
+  return x;
+}
+
+static int hll_log2(int M) { return M == 32 ? 5 : (M == 64 ? 6 : -1); }
+
+/* Record column c in the registers. */
+static void hll_add(uint8_t *regs, int M, int lg, int32_t c) {
+  const uint32_t h = hll_hash((uint32_t)c);
+  const uint32_t j = h & (uint32_t)(M - 1);
+  const uint32_t w = h >> lg; /* 32 - lg significant bits */
+  int rank = 32 - lg + 1;
+  for (int b = 31 - lg; b >= 0; --b) {
+    if ((w >> b) & 1u) {
+      rank = (31 - lg) - b + 1;
+      break;
+    }
+  }
+  if (regs[j] < rank) regs[j] = (uint8_t)rank;
+}
+
+static double hll_value(const uint8_t *regs, int M) {
+  double z = 0.0;
+  int zeros = 0;
+  for (int j = 0; j < M; ++j) {
+    z += ldexp(1.0, -(int)regs[j]);
+    zeros += regs[j] == 0;
+  }
+  const double alpha = M == 32 ? 0.697 : 0.709;
+  double e = alpha * (double)M * (double)M / z;
+  if (e <= 2.5 * M && zeros > 0) e = (double)M * log((double)M / (double)zeros);
+  return e;
+}
+
+int oracle_hll_sketch(int64_t K, const int32_t *b_rp, const int32_t *b_col,
+                      int M, uint8_t *regs) {
+  const int lg = hll_log2(M);
+  if (lg < 0) return -1;
+  for (int64_t k = 0; k < K; ++k) {
+    uint8_t *r = regs + k * M;
+    memset(r, 0, (size_t)M);
+    for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) hll_add(r, M, lg, b_col[b]);
+  }
+  return 0;
+}
+
+int oracle_hll_estimate(int64_t r0, int64_t r1, const int32_t *a_rp,
+                        const int32_t *a_col, const int32_t *b_rp,
+                        const int32_t *b_col, int M, double *est,
+                        uint8_t *regs_out) {
+  const int lg = hll_log2(M);
+  if (lg < 0) return -1;
+  uint8_t regs[64];
+  for (int64_t i = r0; i < r1; ++i) {
+    memset(regs, 0, sizeof(regs));
+    for (int64_t j = a_rp[i]; j < a_rp[i + 1]; ++j) {
+      const int32_t k = a_col[j];
+      for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) hll_add(regs, M, lg, b_col[b]);
+    }
+    est[i - r0] = hll_value(regs, M);
+    if (regs_out) memcpy(regs_out + (i - r0) * M, regs, (size_t)M);
+  }
   return 0;
 }

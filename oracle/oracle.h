@@ -90,6 +90,28 @@ int oracle_transpose(int64_t m, int64_t n, const int64_t *a_rp,
                      const int32_t *a_col, const void *a_val, int val_is_f32,
                      int64_t *t_rp, int32_t *t_col, void *t_val);
 
+/* HyperLogLog size estimation (Ocean page, "Ocean: Fast Estimation-Based
+ * Sparse General Matrix-Matrix Multiplication on GPU", §3: one sketch of M
+ * one-byte registers per row of B, merged by element-wise maximum over the
+ * B rows an A row references, then the estimate of the merged sketch).
+ * Hash of a column index: the 32-bit finaliser of MurmurHash3 (fmix32).
+ * Register index: the low log2(M) bits of the hash; rank: 1 + the number of
+ * leading zeros of the remaining 32 - log2(M) bits (32 - log2(M) + 1 when
+ * they are all zero).  Estimate (Flajolet et al.): E = alpha_M * M^2 / Z
+ * with Z = sum_j 2^-r_j, alpha_32 = 0.697, alpha_64 = 0.709; when
+ * E <= 2.5 M and V > 0 registers are zero, E = M * ln(M / V).
+ * oracle_hll_sketch: regs[k*M + j] for the rows k of B (K rows).
+ * oracle_hll_estimate: est[i - r0] for rows [r0, r1) of A*B, computed
+ * from the columns of the row's products directly (no per-B-row sketches),
+ * and, when regs_out is not NULL, the row's registers.  M is 32 or 64.
+ * Returns 0, or -1 for an unsupported M. */
+int oracle_hll_sketch(int64_t K, const int32_t *b_rp, const int32_t *b_col,
+                      int M, uint8_t *regs);
+int oracle_hll_estimate(int64_t r0, int64_t r1, const int32_t *a_rp,
+                        const int32_t *a_col, const int32_t *b_rp,
+                        const int32_t *b_col, int M, double *est,
+                        uint8_t *regs_out);
+
 #ifdef __cplusplus
 }
 #endif

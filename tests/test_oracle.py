@@ -432,6 +432,87 @@ def test_aat_bruteforce(m, k, per_row, seed):
     np.testing.assert_array_equal(D, D.T)
 
 
+def _rows_of_sizes(sizes, n, seed):
+    """B whose row r holds sizes[r] distinct uniform columns of [0, n)."""
+    rng = np.random.default_rng(seed)
+    cols = [np.sort(rng.choice(n, size=k, replace=False)) for k in sizes]
+    rp = np.zeros(len(sizes) + 1, np.int64)
+    np.cumsum(sizes, out=rp[1:])
+    col = np.concatenate(cols).astype(np.int32) if len(cols) else np.zeros(0, np.int32)
+    return CSR(rp.astype(np.int32), col, np.ones(col.shape[0]), len(sizes), n)
+
+
+@pytest.mark.parametrize("M", [32, 64])
+def test_hll_accuracy(M):
+    # Ocean §3: relative error about 1.04 / sqrt(M).  With A = I the estimate
+    # of row i is that of B's row i, whose exact distinct count is its length.
+    rng = np.random.default_rng(M)
+    large = rng.integers(300, 5000, size=1500)
+    small = rng.integers(1, M // 2, size=1500)
+    for sizes, kind in ((large, "large"), (small, "small")):
+        B = _rows_of_sizes(sizes, 1 << 20, 3)
+        I = synth.identity(B.m)
+        r = oracle.hll_estimate(I, B, M) / sizes
+        sd = 1.04 / np.sqrt(M)
+        if kind == "large":
+            assert abs(r.mean() - 1.0) < 0.03, r.mean()
+            assert 0.7 * sd < r.std() < 1.3 * sd, (r.std(), sd)
+        else:   # linear counting: small bias (about n / 2M), small spread
+            assert abs(r.mean() - 1.0) < 0.05, r.mean()
+            assert r.std() < 0.7 * sd, r.std()
+
+
+def test_hll_special_cases():
+    # empty row -> 0; one column -> M ln(M / (M - 1)); duplicates do not count;
+    # the merged sketch of A's row equals the sketch of its products' columns.
+    B = CSR(np.array([0, 0, 1, 4], np.int32), np.array([7, 7, 7, 7], np.int32)[:4],
+            np.ones(4), 3, 10)
+    B = CSR(np.array([0, 0, 1, 2], np.int32), np.array([7, 7], np.int32), np.ones(2), 3, 10)
+    A = CSR(np.array([0, 1, 2, 4], np.int32), np.array([0, 1, 1, 2], np.int32), np.ones(4), 3, 3)
+    for M in (32, 64):
+        e = oracle.hll_estimate(A, B, M)
+        assert e[0] == 0.0
+        assert e[1] == M * np.log(M / (M - 1))
+        assert e[2] == e[1]
+    with pytest.raises(ValueError):
+        oracle.hll_estimate(A, B, 16)
+
+
+@pytest.mark.parametrize("M", [32, 64])
+def test_hll_merge_equals_direct(M):
+    A = synth.rmat(11, 8, seed=5)
+    S = oracle.hll_sketch(A, M)
+    est, regs = oracle.hll_estimate(A, A, M, with_regs=True)
+    rp = A.row_ptr.astype(np.int64)
+    for i in range(A.m):
+        ks = A.col[rp[i]:rp[i + 1]]
+        want = S[ks].max(axis=0) if ks.size else np.zeros(M, np.uint8)
+        np.testing.assert_array_equal(regs[i], want)
+
+
+def test_capacity_sample_and_workflow_rule():
+    P = np.array([0, 5, 100, 100, 3])
+    est = np.array([0.0, 9.2, 10.0, 80.0, 0.4])
+    np.testing.assert_array_equal(oracle.capacity(P, None, 2.0), P)
+    np.testing.assert_array_equal(oracle.capacity(P, est, 1.5), [0, 5, 15, 100, 1])
+    np.testing.assert_array_equal(oracle.capacity(P, est, 2.0), [0, 5, 20, 100, 1])
+    assert oracle.hll_registers(47 * 100, 100) == 32 and oracle.hll_registers(48 * 100, 100) == 64
+    assert oracle.hll_coefficient(32) == 2.0 and oracle.hll_coefficient(64) == 1.5
+    assert len(oracle.sample_rows(100)) == 100
+    assert len(oracle.sample_rows(5000)) == 600
+    assert len(oracle.sample_rows(100000)) == 3000
+    assert len(oracle.sample_rows(10 ** 6)) == 10000
+    s = oracle.sample_rows(12345)
+    assert s[0] == 0 and np.all(np.diff(s) > 0) and s[-1] < 12345
+    # Table 1: upper bound below 64 products per row; estimation when the
+    # expansion ratio and the sampled compression ratio are both >= 8
+    assert oracle.select_workflow(1000, 5000, 63999, 100.0) == 1
+    assert oracle.select_workflow(1000, 5000, 64000, 8.0) == 2
+    assert oracle.select_workflow(1000, 8000, 64000, 8.0) == 2
+    assert oracle.select_workflow(1000, 8001, 64000, 8.0) == 0
+    assert oracle.select_workflow(1000, 5000, 64000, 7.99) == 0
+
+
 # --- planted mistakes -------------------------------------------------------
 
 _MUTANTS = {
@@ -452,6 +533,11 @@ _MUTANTS = {
     "transpose_value_index": ("((double *)t_val)[q] = ((const double *)a_val)[e];",
                               "((double *)t_val)[q] = ((const double *)a_val)[q];"),
     "transpose_row_index": ("t_col[q] = (int32_t)i;", "t_col[q] = a_col[e];"),
+    "hll_rank_off_by_one": ("rank = (31 - lg) - b + 1;", "rank = (31 - lg) - b + 2;"),
+    "hll_alpha": ("const double alpha = M == 32 ? 0.697 : 0.709;",
+                  "const double alpha = M == 32 ? 0.797 : 0.809;"),
+    "hll_no_linear_counting": ("if (e <= 2.5 * M && zeros > 0)", "if (e <= 0.0 && zeros > 0)"),
+    "hll_unhashed": ("const uint32_t h = hll_hash((uint32_t)c);", "const uint32_t h = (uint32_t)c;"),
 }
 
 
@@ -473,6 +559,9 @@ def _pins_pass(lib_path):
             test_mcl_inflate_fixpoints()
             test_transpose_hand_example()
             test_transpose_against_scipy_and_sort(500, 800, 6.0, 4)
+            test_hll_accuracy(32)
+            test_hll_accuracy(64)
+            test_hll_special_cases()
         except (AssertionError, RuntimeError):
             return False
         return True
