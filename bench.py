@@ -244,6 +244,9 @@ def main():
     ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
+    ap.add_argument("--workflow", type=int, default=-1,
+                    help="light-row size prediction: 0 symbolic, 1 upper bound, 2 HyperLogLog, "
+                         "3 Table 1 choice (default: the library's)")
     ap.add_argument("--light-hash-only", action="store_true",
                     help="no dense windows for light rows (diagnostics)")
     ap.add_argument("--expansion", type=int, default=-1,
@@ -299,6 +302,8 @@ def main():
         opts["expansion"] = args.expansion
     if args.light_hash_only:
         opts["light_hash_only"] = 1
+    if args.workflow >= 0:
+        opts["workflow"] = args.workflow
     if args.config == "rmat20":
         opts["rowptr64"] = 1   # nnz(C) is about 9.7e9
     if args.config == "mcl_iter":

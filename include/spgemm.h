@@ -122,8 +122,30 @@ typedef struct spgemm_options {
                                    the dense window: an LDS bitmap over the
                                    span, ranks by prefix popcount, values
                                    added at their rank (no hash, no sort)    */
+  int32_t workflow;             /* how light rows get their output size (Ocean
+                                   page, §3 and Table 1; heavy rows always take
+                                   the exact chunk path):
+                                   0 (default): symbolic pass (exact counts);
+                                   1: upper bound: each light row reserves its
+                                     product count P_i of output slots, is
+                                     computed into them during
+                                     spgemm_symbolic, and copied into C by
+                                     spgemm_numeric;
+                                   2: HyperLogLog estimate: per-B-row sketches
+                                     merged per A row, min(P_i, ceil(coef*E))
+                                     slots; rows that do not fit are computed
+                                     again with P_i slots;
+                                   3: choose by Table 1 (1 below 64 products
+                                     per row, 2 when products / nnz(A) >= 8
+                                     and the compression ratio of a 3% row
+                                     sample is >= 8, else 0).
+                                   C is the same in every mode. */
+  int32_t hll_registers;        /* registers per sketch, 32 or 64; 0 = 32 when
+                                   products / nnz(A) < 48, else 64          */
+  int32_t hll_coef_pct;         /* estimate multiplier in percent; 0 = 200 with
+                                   32 registers, 150 with 64               */
   int32_t reserved32;
-  int64_t reserved[6];
+  int64_t reserved[4];
 } spgemm_options;
 
 /* Parameters chosen by GetMagnusParams (gMAGNUS §III-D, Eq. 4-7). */
@@ -186,6 +208,11 @@ typedef struct spgemm_stats {
   int64_t heavy_row_threshold; /* rows above this many products were heavy     */
   int64_t chunk_col_bytes;    /* bytes of a column in the heavy intermediate:
                                  2 when it holds chunk-local 16-bit columns */
+  int32_t workflow;           /* size prediction used (options.workflow 0-2) */
+  int32_t hll_registers;      /* registers per sketch (workflow 2), else 0     */
+  int64_t light_capacity;     /* output slots reserved for light rows (1, 2)   */
+  int64_t overflow_rows;      /* light rows computed again with P_i slots      */
+  double sampled_cr;          /* compression ratio of the row sample (mode 3)  */
 } spgemm_stats;
 
 typedef struct spgemm_plan_s *spgemm_plan_t;
@@ -231,6 +258,15 @@ spgemm_status spgemm_symbolic(spgemm_plan_t p, void *dC_row_ptr,
 spgemm_status spgemm_numeric(spgemm_plan_t p, int32_t *dC_col, void *dC_val);
 
 spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats *out);
+
+/* Size prediction of the light rows (Ocean page, §3): after spgemm_symbolic
+ * with options.workflow 1 or 2 (or 3 when it chose one of them), copies the
+ * output slots reserved for every light row into dCap (m int64, device; 0
+ * for other rows) and, with workflow 2, the HyperLogLog estimate of every
+ * light row into dEst (m double, device).  Either pointer may be NULL.
+ * Asynchronous on the plan's stream.  Errors: INVALID_ARG (NULL plan, dEst
+ * without workflow 2), STATE (no symbolic yet, or workflow 0), HIP. */
+spgemm_status spgemm_row_estimates(spgemm_plan_t p, int64_t *dCap, double *dEst);
 
 /* Frees the plan's workspace (stream-ordered on the plan's stream). */
 void spgemm_destroy(spgemm_plan_t p);

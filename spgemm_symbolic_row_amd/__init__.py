@@ -35,7 +35,8 @@ class Options(ctypes.Structure):
         ("validate", c_i32), ("single_stream", c_i32), ("profile", c_i32),
         ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
         ("alloc_ctx", c_vp), ("expansion", c_i32), ("heavy_row_threshold", c_i32),
-        ("light_hash_only", c_i32), ("reserved32", c_i32), ("reserved", c_i64 * 6),
+        ("light_hash_only", c_i32), ("workflow", c_i32), ("hll_registers", c_i32),
+        ("hll_coef_pct", c_i32), ("reserved32", c_i32), ("reserved", c_i64 * 4),
     ]
 
 
@@ -65,6 +66,8 @@ class Stats(ctypes.Structure):
         ("ms_numeric", ctypes.c_double), ("phase_ms", ctypes.c_double * 16),
         ("phase_windows", c_i32 * 16), ("device_errors", c_i64),
         ("heavy_row_threshold", c_i64), ("chunk_col_bytes", c_i64),
+        ("workflow", c_i32), ("hll_registers", c_i32), ("light_capacity", c_i64),
+        ("overflow_rows", c_i64), ("sampled_cr", ctypes.c_double),
     ]
 
     def as_dict(self):
@@ -131,6 +134,8 @@ def lib():
         L.spgemm_mcl_inflate_fill.argtypes = [c_vp, c_vp, c_vp]
         L.spgemm_prune_destroy.restype = None
         L.spgemm_prune_destroy.argtypes = [c_vp]
+        L.spgemm_row_estimates.restype = st
+        L.spgemm_row_estimates.argtypes = [c_vp, c_vp, c_vp]
         L.spgemm_transpose.restype = st
         L.spgemm_transpose.argtypes = [c_i64, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, ctypes.c_int,
                                        c_vp, c_i32, c_vp, c_vp, c_vp]
@@ -248,6 +253,17 @@ class Plan:
             val = torch.empty(max(self.nnz, 1), dtype=self.dtype, device=dev)[:self.nnz]
         _check(lib().spgemm_numeric(self._h, col.data_ptr(), val.data_ptr()), self._h)
         return col, val
+
+    def row_estimates(self, with_estimates=True):
+        """Light rows' reserved output slots (int64) and, with the HyperLogLog
+        workflow, their estimates (float64); other rows 0.  After symbolic."""
+        import torch
+        cap = torch.zeros(self.m, dtype=torch.int64, device=self.A.col.device)
+        est = torch.zeros(self.m, dtype=torch.float64, device=self.A.col.device) \
+            if with_estimates else None
+        _check(lib().spgemm_row_estimates(self._h, cap.data_ptr(),
+                                          None if est is None else est.data_ptr()), self._h)
+        return cap, est
 
     def stats(self) -> dict:
         s = Stats()

@@ -28,7 +28,8 @@ COMMON = [
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["k_util.hip", "k_light.hip", "k_outer.hip", "k_multisplit.hip", "k_heavy.hip",
-           "k_chunks.hip", "k_chunkhist.hip", "k_prune.hip", "k_transpose.hip", "api.cpp",
+           "k_chunks.hip", "k_chunkhist.hip", "k_prune.hip", "k_transpose.hip", "k_estimate.hip",
+           "api.cpp",
            "params.cpp"]
 
 

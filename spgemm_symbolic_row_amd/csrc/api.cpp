@@ -102,7 +102,7 @@ void make_bins(int64_t tau, int64_t lds, int val_bytes, std::vector<BinCfg>* sym
     const int slot = 4 + val_bytes;
     const int64_t N = next_pow2(cap);
     int64_t T = std::max<int64_t>(next_pow2(2 * cap), tpr);
-    const int64_t extra = (int64_t)(tpr * rpb / 64) * 4;
+    const int64_t extra = (int64_t)(tpr * rpb / 64) * 4 + (int64_t)rpb * 4;
     while (T > tpr && (int64_t)rpb * T * slot + extra > lds) T -= tpr;
     if (T < N || T <= cap || T / tpr > 24)
       throw Error{SPGEMM_ERR_INVALID_ARG, "numeric hash table does not fit the LDS budget"};
@@ -282,6 +282,18 @@ struct spgemm_plan_s {
   int32_t* slotNnz = nullptr;
   int64_t* slotOff = nullptr;
   int64_t nnzC = 0;
+  // Size prediction of the light rows: 0 symbolic pass, 1 upper bound, 2
+  // HyperLogLog estimate (Ocean page, §3, Table 1).  With 1 or 2 the light
+  // rows are computed during spgemm_symbolic into reserved slots (tcol1,
+  // tval1 at tmpOff; rows that did not fit again into tcol2, tval2) and
+  // copied into C by spgemm_numeric.
+  int wf = 0;
+  int hllLg = 0;
+  int64_t *capL = nullptr, *tmpOff = nullptr, *cnt1 = nullptr, *cnt2 = nullptr, *off2 = nullptr;
+  double* estL = nullptr;
+  int32_t *tcol1 = nullptr, *tcol2 = nullptr;
+  void *tval1 = nullptr, *tval2 = nullptr;
+  std::vector<double> hLc;
   spgemm_stats st{};
   struct PhaseRec {
     int id;
@@ -535,6 +547,11 @@ void do_plan(spgemm_plan_t p) {
       p->params.dense_width > 32768)
     throw Error{SPGEMM_ERR_INVALID_ARG, "dense width does not fit the LDS"};
   if (p->opts.mem_budget < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "mem_budget must be >= 0"};
+  if (p->opts.workflow < 0 || p->opts.workflow > 3)
+    throw Error{SPGEMM_ERR_INVALID_ARG, "workflow must lie in [0, 3]"};
+  if (p->opts.hll_registers != 0 && p->opts.hll_registers != 32 && p->opts.hll_registers != 64)
+    throw Error{SPGEMM_ERR_INVALID_ARG, "hll_registers must be 0, 32 or 64"};
+  if (p->opts.hll_coef_pct < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "hll_coef_pct must be >= 0"};
   make_bins(p->tau, p->lds, vb, &p->symBins, &p->numBins);
   p->NS = (int)p->symBins.size();
   if (2 * p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
@@ -1161,23 +1178,177 @@ void heavy_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   }
 }
 
+// ------------------------------------------------- size-estimate workflows
+// Registers per sketch: 32 while the expansion ratio products / nnz(A) is
+// below 48, else 64 (Ocean page, parameter settings), unless set.
+int hll_lg(spgemm_plan_t p) {
+  int M = p->opts.hll_registers;
+  if (M == 0) M = p->st.products < 48 * std::max<int64_t>(p->nnzA, 1) ? 32 : 64;
+  if (M != 32 && M != 64) throw Error{SPGEMM_ERR_INVALID_ARG, "hll_registers must be 0, 32 or 64"};
+  return M == 32 ? 5 : 6;
+}
+
+// M * ln(M / V) for V = 0..M, the small-count estimate, on the device.
+const double* hll_table(spgemm_plan_t p, int lg, hipStream_t s) {
+  const int M = 1 << lg;
+  p->hLc.assign(M + 1, 0.0);
+  for (int v = 1; v <= M; ++v) p->hLc[v] = (double)M * std::log((double)M / (double)v);
+  double* d = alloc_n<double>(p, M + 1, s);
+  HIP_CHECK(hipMemcpyAsync(d, p->hLc.data(), sizeof(double) * (M + 1), hipMemcpyHostToDevice, s));
+  HIP_CHECK(hipStreamSynchronize(s));  // the host table may change with the next call
+  return d;
+}
+
+// Ocean's Table 1 on this plan: upper bound below 64 products per row;
+// HyperLogLog when products / nnz(A) >= 8 and the compression ratio of a row
+// sample (products / estimated nnz over 3% of the rows, 600 to 10,000, evenly
+// spaced) is >= 8; else the symbolic pass.
+int select_workflow(spgemm_plan_t p, hipStream_t s) {
+  const int64_t m = p->m, P = p->st.products;
+  if (P < 64 * m) return 1;
+  if (P < 8 * p->nnzA) return 0;
+  const int lg = hll_lg(p);
+  const int64_t ns = std::min<int64_t>(m, std::min<int64_t>(10000, std::max<int64_t>(
+                                                                     600, std::llround(0.03 * m))));
+  std::vector<int32_t> hrows(ns);
+  for (int64_t j = 0; j < ns; ++j) hrows[j] = (int32_t)((j * m) / ns);
+  int32_t* rows = alloc_n<int32_t>(p, ns, s);
+  double* est = alloc_n<double>(p, ns, s);
+  int64_t* pr = alloc_n<int64_t>(p, ns, s);
+  HIP_CHECK(hipMemcpyAsync(rows, hrows.data(), sizeof(int32_t) * ns, hipMemcpyHostToDevice, s));
+  const double* lc = hll_table(p, lg, s);
+  launch_hll_rows_direct(ns, rows, p->arp, p->acol, p->brp, p->bcol, lg, lc, est, s);
+  launch_gather_i64(p->rowP, rows, ns, pr, s);
+  check_launch("row sample estimate");
+  std::vector<double> he(ns);
+  std::vector<int64_t> hp(ns);
+  HIP_CHECK(hipMemcpyAsync(he.data(), est, sizeof(double) * ns, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(hp.data(), pr, sizeof(int64_t) * ns, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  double sp = 0, se = 0;
+  for (int64_t j = 0; j < ns; ++j) {
+    sp += (double)hp[j];
+    se += he[j];
+  }
+  p->st.sampled_cr = se > 0 ? sp / se : 0.0;
+  return p->st.sampled_cr >= 8.0 ? 2 : 0;
+}
+
+// Light rows without the symbolic pass: reserve slots (upper bound or
+// estimate), compute every light row into them, redo the rows that did not
+// fit with P_i slots, and leave each light row's count in p->cnt.
+void estimate_light(spgemm_plan_t p, const RowArgs& a) {
+  hipStream_t s = p->sl;
+  const int64_t m = p->m;
+  const int heavyBin = p->NS + 1;
+  const int phL = ph_begin(p, SPGEMM_PH_SYM_LIGHT, s);
+  p->capL = alloc_n<int64_t>(p, m, s);
+  p->tmpOff = alloc_n<int64_t>(p, m + 1, s);
+  p->cnt1 = alloc_n<int64_t>(p, m, s);
+  int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(m) + 1, s);
+  uint8_t* key = alloc_n<uint8_t>(p, m, s);
+  int32_t* order = alloc_n<int32_t>(p, m, s);
+  launch_fill_i64(p->capL, 0, m, s);
+  launch_fill_i64(p->cnt1, 0, m, s);
+  if (p->wf == 1) {
+    launch_ub_capacity(m, p->rowP, p->rowBin, heavyBin, p->capL, s);
+  } else {
+    const int lg = p->hllLg = hll_lg(p);
+    const int M = 1 << lg;
+    p->st.hll_registers = M;
+    const double coef = p->opts.hll_coef_pct ? p->opts.hll_coef_pct / 100.0 : (M == 32 ? 2.0 : 1.5);
+    uint8_t* regs = alloc_n<uint8_t>(p, std::max<int64_t>(p->k, 1) * M, s);
+    p->estL = alloc_n<double>(p, m, s);
+    launch_fill_i64((int64_t*)p->estL, 0, m, s);  // +0.0 has an all-zero bit pattern
+    const double* lc = hll_table(p, lg, s);
+    launch_hll_sketch(p->k, p->brp, p->bcol, lg, regs, s);
+    launch_hll_capacity(m, p->arp, p->acol, regs, lg, lc, coef, p->rowP, p->rowBin, heavyBin,
+                        p->capL, p->estL, s);
+  }
+  launch_scan_i64(p->capL, m, p->tmpOff, tmp, s);
+  launch_numeric_row_bins(m, p->capL, p->rowBin, heavyBin, p->dSymCaps, p->NS, key, s);
+  launch_bin_sort(key, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, order, s);
+  check_launch("light capacities");
+  std::vector<int32_t> bins(2 * p->NS + 1);
+  int64_t total = 0;
+  HIP_CHECK(hipMemcpyAsync(&total, p->tmpOff + m, 8, hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(bins.data(), p->binStart, sizeof(int32_t) * bins.size(),
+                           hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  p->st.light_capacity = total;
+  const int vb = p->f64 ? 8 : 4;
+  p->tcol1 = alloc_n<int32_t>(p, std::max<int64_t>(total, 1), s);
+  p->tval1 = plan_alloc(p, (size_t)std::max<int64_t>(total, 1) * vb, s);
+  auto run = [&](const std::vector<int32_t>& bs, const int64_t* off, int32_t* tc, void* tv,
+                 int64_t* cntOut) {
+    for (int b = 0; b < p->NS; ++b) {
+      launch_num_rows(p->numBins[b], p->f64, order + bs[b], bs[b + 1] - bs[b], a, off, tc, tv,
+                      p->errWord, s, cntOut);
+      const int64_t ws = bs[p->NS + b], we = bs[p->NS + b + 1];
+      if (we > ws)
+        launch_num_rows_win(p->symBins[b], p->winWords[b], p->f64, order + ws, we - ws, a, off,
+                            tc, tv, p->errWord, s, cntOut);
+    }
+  };
+  run(bins, p->tmpOff, p->tcol1, p->tval1, p->cnt1);
+  check_launch("light numeric into reserved slots");
+  // Rows that did not fit (estimates only; P_i slots always suffice).
+  int32_t nOver = 0;
+  if (p->wf == 2) {
+    int32_t* dOver = alloc_n<int32_t>(p, 1, s);
+    int64_t* cap2 = alloc_n<int64_t>(p, m, s);
+    launch_fill_i32(dOver, 0, 1, s);
+    launch_overflow_rows(m, p->cnt1, p->rowP, p->rowBin, heavyBin, p->NS, cap2, key, dOver, s);
+    HIP_CHECK(hipMemcpyAsync(&nOver, dOver, 4, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    if (nOver > 0) {
+      p->off2 = alloc_n<int64_t>(p, m + 1, s);
+      p->cnt2 = alloc_n<int64_t>(p, m, s);
+      launch_fill_i64(p->cnt2, 0, m, s);
+      launch_scan_i64(cap2, m, p->off2, tmp, s);
+      launch_bin_sort(key, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, order, s);
+      int64_t total2 = 0;
+      HIP_CHECK(hipMemcpyAsync(&total2, p->off2 + m, 8, hipMemcpyDeviceToHost, s));
+      HIP_CHECK(hipMemcpyAsync(bins.data(), p->binStart, sizeof(int32_t) * bins.size(),
+                               hipMemcpyDeviceToHost, s));
+      HIP_CHECK(hipStreamSynchronize(s));
+      p->tcol2 = alloc_n<int32_t>(p, std::max<int64_t>(total2, 1), s);
+      p->tval2 = plan_alloc(p, (size_t)std::max<int64_t>(total2, 1) * vb, s);
+      run(bins, p->off2, p->tcol2, p->tval2, p->cnt2);
+      check_launch("light numeric of rows that did not fit");
+    }
+  }
+  p->st.overflow_rows = nOver;
+  launch_merge_counts(m, p->rowBin, heavyBin, p->cnt1, nOver ? p->cnt2 : nullptr, p->off2,
+                      p->tmpOff, p->cnt, s);
+  ph_end(p, phL, s);
+  check_launch("light counts");
+}
+
 void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   const double t0 = now_ms();
   hipStream_t s = p->stream;
+  p->wf = p->opts.workflow == 3 ? select_workflow(p, s) : p->opts.workflow;
+  p->st.workflow = p->wf;
   fork(p);
   const RowArgs a = row_args(p);
-  const int phL = ph_begin(p, SPGEMM_PH_SYM_LIGHT, p->sl);
-  for (int b = 0; b < p->NS; ++b) {
-    const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
-    launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
-    const int64_t ws = p->rowBinStart[p->NS + 2 + b], we = p->rowBinStart[p->NS + 3 + b];
-    if (we > ws)
-      launch_sym_rows_win(p->symBins[b], p->winWords[b], p->rowOrder + ws, we - ws, a, p->cnt,
-                          p->sl);
+  if (p->wf == 0) {
+    const int phL = ph_begin(p, SPGEMM_PH_SYM_LIGHT, p->sl);
+    for (int b = 0; b < p->NS; ++b) {
+      const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
+      launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
+      const int64_t ws = p->rowBinStart[p->NS + 2 + b], we = p->rowBinStart[p->NS + 3 + b];
+      if (we > ws)
+        launch_sym_rows_win(p->symBins[b], p->winWords[b], p->rowOrder + ws, we - ws, a, p->cnt,
+                            p->sl);
+    }
+    ph_end(p, phL, p->sl);
+    check_launch("light symbolic");
   }
-  ph_end(p, phL, p->sl);
-  check_launch("light symbolic");
   if (p->h > 0) heavy_symbolic(p);
+  // After the heavy batches (their workspace marks), so the light rows'
+  // reserved slots stay allocated until destroy.
+  if (p->wf != 0) estimate_light(p, a);
   join(p);
 
   const int64_t m = p->m;
@@ -1187,8 +1358,12 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   p->numOrder = alloc_n<int32_t>(p, m, s);
   const int phR = ph_begin(p, SPGEMM_PH_ROWPTR, s);
   launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
-  launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s);
-  launch_bin_sort(p->numKey, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
+  if (p->wf == 0) {
+    launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s);
+    launch_bin_sort(p->numKey, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
+  } else {
+    launch_fill_i32(p->binStart, 0, 2 * p->NS + 1, s);  // light rows are done
+  }
   ph_end(p, phR, s);
   check_launch("row pointer scan");
   HIP_CHECK(hipMemcpyAsync(p->hStats + 20, p->cRowOff + m, 8, hipMemcpyDeviceToHost, s));
@@ -1216,7 +1391,10 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   fork(p);
   const RowArgs a = row_args(p);
   const int phL = ph_begin(p, SPGEMM_PH_NUM_LIGHT, p->sl);
-  for (int b = 0; b < p->NS; ++b) {
+  if (p->wf != 0)
+    launch_compact_rows(p->f64, p->m, p->rowBin, p->NS + 1, p->tmpOff, p->cnt, p->cRowOff,
+                        p->tcol1, p->tval1, p->tcol2, p->tval2, ccol, cval, p->sl);
+  for (int b = 0; p->wf == 0 && b < p->NS; ++b) {
     const int64_t st = p->numBinStart[b], en = p->numBinStart[b + 1];
     launch_num_rows(p->numBins[b], p->f64, p->numOrder + st, en - st, a, p->cRowOff, ccol, cval,
                     p->errWord, p->sl);
@@ -1357,6 +1535,26 @@ spgemm_status spgemm_numeric(spgemm_plan_t p, int32_t* dC_col, void* dC_val) {
   spgemm_status st = guarded(p, [&] { do_numeric(p, dC_col, dC_val); });
   if (st == SPGEMM_OK) p->state = 2;
   return st;
+}
+
+spgemm_status spgemm_row_estimates(spgemm_plan_t p, int64_t* dCap, double* dEst) {
+  if (!p) return SPGEMM_ERR_INVALID_ARG;
+  if (p->state < 1 || p->wf == 0) {
+    p->err = "row estimates exist after spgemm_symbolic with workflow 1 or 2";
+    return SPGEMM_ERR_STATE;
+  }
+  if (dEst && p->wf != 2) {
+    p->err = "estimates exist with workflow 2 only";
+    return SPGEMM_ERR_INVALID_ARG;
+  }
+  return guarded(p, [&] {
+    if (dCap)
+      HIP_CHECK(hipMemcpyAsync(dCap, p->capL, sizeof(int64_t) * p->m, hipMemcpyDeviceToDevice,
+                               p->stream));
+    if (dEst)
+      HIP_CHECK(hipMemcpyAsync(dEst, p->estL, sizeof(double) * p->m, hipMemcpyDeviceToDevice,
+                               p->stream));
+  });
 }
 
 spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats* out) {

@@ -162,14 +162,16 @@ void light_set_attributes();
 size_t window_row_lds(bool numeric, bool f64, const BinCfg& b, int32_t words);
 void launch_sym_rows_win(const BinCfg& b, int32_t words, const int32_t* rows, int64_t nrows,
                          const RowArgs& a, int64_t* cnt, hipStream_t s);
+// cntOut (size-estimate workflows): cRowOff holds capacities; each row's
+// count, or -1 when it did not fit, goes to cntOut (no device error).
 void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t* rows,
                          int64_t nrows, const RowArgs& a, const int64_t* cRowOff, int32_t* ccol,
-                         void* cval, int32_t* err, hipStream_t s);
+                         void* cval, int32_t* err, hipStream_t s, int64_t* cntOut = nullptr);
 void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
                      int64_t* cnt, int32_t* err, hipStream_t s);
 void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
                      const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
-                     int32_t* err, hipStream_t s);
+                     int32_t* err, hipStream_t s, int64_t* cntOut = nullptr);
 void launch_sym_chunks(const BinCfg& b, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
                        int32_t* err, hipStream_t s);
 // Whether a numeric bin's (tpr, sort size) has a kernel instance.
@@ -355,5 +357,31 @@ void launch_transpose(const TransposePlan& tp, int64_t m, int64_t n, int64_t nnz
                       void* trp, int trp64, int32_t* tcol, void* tval, int32_t* rows[2],
                       uint32_t* keys[2], void* vals[2], int32_t* hist, int64_t* off,
                       int64_t* scanTmp, int32_t* err, hipStream_t s);
+
+// ---- k_estimate.hip ----
+// Size prediction of light rows without the symbolic pass (upper bound or
+// HyperLogLog estimate); lg = log2 of the registers per sketch (5 or 6), lc
+// = M * ln(M / V) for V = 0..M (device), cap = reserved slots per light row.
+void launch_hll_sketch(int64_t K, const int32_t* brp, const int32_t* bcol, int lg, uint8_t* regs,
+                       hipStream_t s);
+void launch_hll_capacity(int64_t m, const int32_t* arp, const int32_t* acol, const uint8_t* regs,
+                         int lg, const double* lc, double coef, const int64_t* rowP,
+                         const uint8_t* rowBin, int heavyBin, int64_t* cap, double* est,
+                         hipStream_t s);
+void launch_hll_rows_direct(int64_t ns, const int32_t* rows, const int32_t* arp,
+                            const int32_t* acol, const int32_t* brp, const int32_t* bcol, int lg,
+                            const double* lc, double* est, hipStream_t s);
+void launch_ub_capacity(int64_t m, const int64_t* rowP, const uint8_t* rowBin, int heavyBin,
+                        int64_t* cap, hipStream_t s);
+void launch_overflow_rows(int64_t m, const int64_t* cnt, const int64_t* rowP,
+                          const uint8_t* rowBin, int heavyBin, int nbins, int64_t* cap2,
+                          uint8_t* key, int32_t* nOver, hipStream_t s);
+void launch_merge_counts(int64_t m, const uint8_t* rowBin, int heavyBin, const int64_t* cnt1,
+                         const int64_t* cnt2, const int64_t* off2, int64_t* srcOff, int64_t* cnt,
+                         hipStream_t s);
+void launch_compact_rows(bool f64, int64_t m, const uint8_t* rowBin, int heavyBin,
+                         const int64_t* srcOff, const int64_t* cnt, const int64_t* cRowOff,
+                         const int32_t* col1, const void* val1, const int32_t* col2,
+                         const void* val2, int32_t* ccol, void* cval, hipStream_t s);
 
 }  // namespace sg

@@ -204,7 +204,8 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows_win(const int32_t* __rest
                                                            const int64_t* __restrict__ cRowOff,
                                                            int32_t* __restrict__ ccol,
                                                            V* __restrict__ cval,
-                                                           int32_t* __restrict__ err) {
+                                                           int32_t* __restrict__ err,
+                                                           int64_t* __restrict__ cntOut) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int WPR = TPR / kWave;
   __shared__ int32_t wtot[RPB * WPR];
@@ -276,7 +277,14 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows_win(const int32_t* __rest
     }
   }
   __syncthreads();
-  if (ri < nrows && t == 0 && total != want) flag_error(err, kErrCountMismatch);
+  // Estimate workflows: a row with more entries than its reserved capacity
+  // writes nothing and reports -1.
+  const bool over = cntOut && total > want;
+  if (ri < nrows && t == 0) {
+    if (cntOut) cntOut[row] = over ? -1 : total;
+    else if (total != want) flag_error(err, kErrCountMismatch);
+  }
+  if (cntOut) want = over ? 0 : total;
   for (int q = t; q < P; q += TPR) {
     const int32_t c = pc[q];
     const int32_t r = wpre[c >> 5] + __popc(bm[c >> 5] & ((1u << (c & 31)) - 1u));
@@ -476,6 +484,10 @@ __device__ __forceinline__ void sort_to_regs(int32_t* keys, V* vals, int32_t (&k
   }
 }
 
+// With cntOut (size-estimate workflows), cRowOff holds each row's reserved
+// capacity instead of its exact size: a row whose entries fit is written
+// there and its count stored in cntOut; a row with more entries than its
+// capacity, or whose table filled up, writes nothing and gets -1.
 template <int TPR, int RPB, int E, typename V>
 __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict__ rows,
                                                        int64_t nrows, int32_t T, int32_t spt,
@@ -483,11 +495,13 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
                                                        const int64_t* __restrict__ cRowOff,
                                                        int32_t* __restrict__ ccol,
                                                        V* __restrict__ cval,
-                                                       int32_t* __restrict__ err) {
+                                                       int32_t* __restrict__ err,
+                                                       int64_t* __restrict__ cntOut) {
   extern __shared__ __align__(16) unsigned char smem[];
   V* valsAll = (V*)smem;
   int32_t* keysAll = (int32_t*)(valsAll + RPB * T);
   int32_t* wtot = keysAll + RPB * T;
+  int32_t* full = wtot + RPB * (TPR / kWave);  // per row: its table filled up
   const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
   int32_t* keys = keysAll + g * T;
   V* vals = valsAll + g * T;
@@ -495,6 +509,8 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
     keys[s] = kEmptyKey;
     vals[s] = V(0);
   }
+  if (t == 0) full[g] = 0;
+  int32_t* herr = cntOut ? &full[g] : err;
   __syncthreads();
   const int64_t ri = (int64_t)blockIdx.x * RPB + g;
   int32_t row = 0;
@@ -510,7 +526,8 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
     const V* __restrict__ bval = (const V*)a.bval;
     stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, rs, re, P, p0, p1,
                         [&](bool act, int32_t b, V av, int32_t) {
-                          if (act) hmap_add(keys, vals, (uint32_t)T, bcol[b], av * bval[b], err);
+                          if (act && !(cntOut && full[g]))
+                            hmap_add(keys, vals, (uint32_t)T, bcol[b], av * bval[b], herr);
                         });
   }
   __syncthreads();
@@ -521,8 +538,15 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
   if (ri < nrows) {
     const int64_t base = cRowOff[row];
     const int64_t want = cRowOff[row + 1] - base;
-    if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
-    const int32_t lim = (int32_t)(want < total ? want : total);
+    int32_t lim;
+    if (cntOut) {
+      const bool over = total > want || full[g] != 0;
+      if (t == 0) cntOut[row] = over ? -1 : total;
+      lim = over ? 0 : total;
+    } else {
+      if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
+      lim = (int32_t)(want < total ? want : total);
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int r = t * E + e;
@@ -696,7 +720,7 @@ void launch_sym_rows_win(const BinCfg& b, int32_t words, const int32_t* rows, in
 
 void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t* rows,
                          int64_t nrows, const RowArgs& a, const int64_t* cRowOff, int32_t* ccol,
-                         void* cval, int32_t* err, hipStream_t s) {
+                         void* cval, int32_t* err, hipStream_t s, int64_t* cntOut) {
   if (nrows <= 0) return;
   const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
   const size_t lds = window_row_lds(true, f64, b, words);
@@ -704,10 +728,12 @@ void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t
   do {                                                                                       \
     if (f64)                                                                                 \
       hipLaunchKernelGGL((k_num_rows_win<TPR, RPB, double>), dim3(grid), dim3(TPR * RPB), lds, \
-                         s, rows, nrows, words, b.cap, a, cRowOff, ccol, (double*)cval, err);  \
+                         s, rows, nrows, words, b.cap, a, cRowOff, ccol, (double*)cval, err,   \
+                         cntOut);                                                            \
     else                                                                                     \
       hipLaunchKernelGGL((k_num_rows_win<TPR, RPB, float>), dim3(grid), dim3(TPR * RPB), lds,  \
-                         s, rows, nrows, words, b.cap, a, cRowOff, ccol, (float*)cval, err);   \
+                         s, rows, nrows, words, b.cap, a, cRowOff, ccol, (float*)cval, err,    \
+                         cntOut);                                                            \
   } while (0);
   SG_DISPATCH_TPR(b, L)
 #undef L
@@ -760,20 +786,20 @@ bool num_bin_supported(const BinCfg& b) {
 
 void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
                      const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
-                     int32_t* err, hipStream_t s) {
+                     int32_t* err, hipStream_t s, int64_t* cntOut) {
   if (nrows <= 0) return;
   bool flag_unsupported = false;
   const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
   if (f64) {
 #define L(TPR, RPB, E)                                                                       \
   hipLaunchKernelGGL((k_num_rows<TPR, RPB, E, double>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
-                     rows, nrows, b.T, b.spt, a, cRowOff, ccol, (double*)cval, err)
+                     rows, nrows, b.T, b.spt, a, cRowOff, ccol, (double*)cval, err, cntOut)
     SG_DISPATCH_NUM(b, L);
 #undef L
   } else {
 #define L(TPR, RPB, E)                                                                      \
   hipLaunchKernelGGL((k_num_rows<TPR, RPB, E, float>), dim3(grid), dim3(TPR * RPB), b.lds, s, \
-                     rows, nrows, b.T, b.spt, a, cRowOff, ccol, (float*)cval, err)
+                     rows, nrows, b.T, b.spt, a, cRowOff, ccol, (float*)cval, err, cntOut)
     SG_DISPATCH_NUM(b, L);
 #undef L
   }

@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
                  "spgemm_get_stats", "spgemm_compute_params", "spgemm_status_string",
                  "spgemm_last_error", "spgemm_prune_colnorm_count", "spgemm_prune_colnorm_fill",
                  "spgemm_prune_destroy", "spgemm_mcl_inflate_count", "spgemm_mcl_inflate_fill",
-                 "spgemm_transpose"):
+                 "spgemm_transpose", "spgemm_row_estimates"):
         assert must in names
 
 
@@ -68,6 +68,7 @@ def test_argument_validation_without_device():
     assert t(1, 1, 1, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, None, None) == -1
     assert t(1 << 31, 1, 1, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, dummy, None) == -3
     assert t(1, 1, 1 << 31, dummy, 0, dummy, dummy, 1, dummy, 0, dummy, dummy, None) == -3
+    assert L.spgemm_row_estimates(None, None, None) == -1
     for s, word in ((0, b"ok"), (-2, b"canonical"), (-3, b"overflow"), (-6, b"order")):
         assert word in L.spgemm_status_string(s)
 
