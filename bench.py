@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--workflow", type=int, default=-1,
                     help="light-row size prediction: 0 symbolic, 1 upper bound, 2 HyperLogLog, "
                          "3 Table 1 choice (default: the library's)")
+    ap.add_argument("--light-no-esc", action="store_true",
+                    help="short rows by the LDS hash kernels instead of ESC (diagnostics)")
     ap.add_argument("--light-hash-only", action="store_true",
                     help="no dense windows for light rows (diagnostics)")
     ap.add_argument("--expansion", type=int, default=-1,
@@ -304,6 +306,8 @@ def main():
         opts["light_hash_only"] = 1
     if args.workflow >= 0:
         opts["workflow"] = args.workflow
+    if args.light_no_esc:
+        opts["light_no_esc"] = 1
     if args.config == "rmat20":
         opts["rowptr64"] = 1   # nnz(C) is about 9.7e9
     if args.config == "mcl_iter":

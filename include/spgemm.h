@@ -144,7 +144,11 @@ typedef struct spgemm_options {
                                    products / nnz(A) < 48, else 64          */
   int32_t hll_coef_pct;         /* estimate multiplier in percent; 0 = 200 with
                                    32 registers, 150 with 64               */
-  int32_t reserved32;
+  int32_t light_no_esc;         /* 1: rows of at most 32 products take the LDS
+                                   hash kernels; 0 (default): they take the
+                                   expand-sort-compact kernel (32 lanes per
+                                   row, sort by lane exchanges, no LDS;
+                                   Ocean page, §3)                         */
   int64_t reserved[4];
 } spgemm_options;
 

@@ -36,7 +36,7 @@ class Options(ctypes.Structure):
         ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
         ("alloc_ctx", c_vp), ("expansion", c_i32), ("heavy_row_threshold", c_i32),
         ("light_hash_only", c_i32), ("workflow", c_i32), ("hll_registers", c_i32),
-        ("hll_coef_pct", c_i32), ("reserved32", c_i32), ("reserved", c_i64 * 4),
+        ("hll_coef_pct", c_i32), ("light_no_esc", c_i32), ("reserved", c_i64 * 4),
     ]
 
 

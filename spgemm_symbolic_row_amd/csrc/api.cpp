@@ -1178,6 +1178,11 @@ void heavy_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   }
 }
 
+// Rows of the first product bin (at most 32 products) by expand-sort-compact.
+bool esc_on(spgemm_plan_t p) {
+  return !p->opts.light_no_esc && p->symBins[0].cap <= 32;
+}
+
 // ------------------------------------------------- size-estimate workflows
 // Registers per sketch: 32 while the expansion ratio products / nnz(A) is
 // below 48, else 64 (Ocean page, parameter settings), unless set.
@@ -1266,10 +1271,11 @@ void estimate_light(spgemm_plan_t p, const RowArgs& a) {
                         p->capL, p->estL, s);
   }
   launch_scan_i64(p->capL, m, p->tmpOff, tmp, s);
-  launch_numeric_row_bins(m, p->capL, p->rowBin, heavyBin, p->dSymCaps, p->NS, key, s);
-  launch_bin_sort(key, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, order, s);
+  launch_numeric_row_bins(m, p->capL, p->rowBin, heavyBin, p->dSymCaps, p->NS, key, s,
+                          esc_on(p) ? 2 * p->NS : -1);
+  launch_bin_sort(key, m, 2 * p->NS + 1, p->binCnt, p->binFill, p->binStart, order, s);
   check_launch("light capacities");
-  std::vector<int32_t> bins(2 * p->NS + 1);
+  std::vector<int32_t> bins(2 * p->NS + 2);
   int64_t total = 0;
   HIP_CHECK(hipMemcpyAsync(&total, p->tmpOff + m, 8, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(bins.data(), p->binStart, sizeof(int32_t) * bins.size(),
@@ -1281,6 +1287,8 @@ void estimate_light(spgemm_plan_t p, const RowArgs& a) {
   p->tval1 = plan_alloc(p, (size_t)std::max<int64_t>(total, 1) * vb, s);
   auto run = [&](const std::vector<int32_t>& bs, const int64_t* off, int32_t* tc, void* tv,
                  int64_t* cntOut) {
+    launch_num_rows_esc(p->f64, order + bs[2 * p->NS], bs[2 * p->NS + 1] - bs[2 * p->NS], a, off,
+                        tc, tv, p->errWord, s, cntOut);
     for (int b = 0; b < p->NS; ++b) {
       launch_num_rows(p->numBins[b], p->f64, order + bs[b], bs[b + 1] - bs[b], a, off, tc, tv,
                       p->errWord, s, cntOut);
@@ -1306,7 +1314,7 @@ void estimate_light(spgemm_plan_t p, const RowArgs& a) {
       p->cnt2 = alloc_n<int64_t>(p, m, s);
       launch_fill_i64(p->cnt2, 0, m, s);
       launch_scan_i64(cap2, m, p->off2, tmp, s);
-      launch_bin_sort(key, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, order, s);
+      launch_bin_sort(key, m, 2 * p->NS + 1, p->binCnt, p->binFill, p->binStart, order, s);
       int64_t total2 = 0;
       HIP_CHECK(hipMemcpyAsync(&total2, p->off2 + m, 8, hipMemcpyDeviceToHost, s));
       HIP_CHECK(hipMemcpyAsync(bins.data(), p->binStart, sizeof(int32_t) * bins.size(),
@@ -1336,7 +1344,10 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
     const int phL = ph_begin(p, SPGEMM_PH_SYM_LIGHT, p->sl);
     for (int b = 0; b < p->NS; ++b) {
       const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
-      launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
+      if (b == 0 && esc_on(p))
+        launch_sym_rows_esc(p->rowOrder + st, en - st, a, p->cnt, p->sl);
+      else
+        launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
       const int64_t ws = p->rowBinStart[p->NS + 2 + b], we = p->rowBinStart[p->NS + 3 + b];
       if (we > ws)
         launch_sym_rows_win(p->symBins[b], p->winWords[b], p->rowOrder + ws, we - ws, a, p->cnt,
@@ -1359,20 +1370,22 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   const int phR = ph_begin(p, SPGEMM_PH_ROWPTR, s);
   launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
   if (p->wf == 0) {
-    launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s);
-    launch_bin_sort(p->numKey, m, 2 * p->NS, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
+    launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s,
+                            esc_on(p) ? 2 * p->NS : -1);
+    launch_bin_sort(p->numKey, m, 2 * p->NS + 1, p->binCnt, p->binFill, p->binStart, p->numOrder,
+                    s);
   } else {
-    launch_fill_i32(p->binStart, 0, 2 * p->NS + 1, s);  // light rows are done
+    launch_fill_i32(p->binStart, 0, 2 * p->NS + 2, s);  // light rows are done
   }
   ph_end(p, phR, s);
   check_launch("row pointer scan");
   HIP_CHECK(hipMemcpyAsync(p->hStats + 20, p->cRowOff + m, 8, hipMemcpyDeviceToHost, s));
-  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (2 * p->NS + 1), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (2 * p->NS + 2), hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hBins + 120, p->errWord, 4, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
   check_device_errors(p, p->hBins[120]);
-  p->numBinStart.assign(p->hBins, p->hBins + 2 * p->NS + 1);
+  p->numBinStart.assign(p->hBins, p->hBins + 2 * p->NS + 2);
   p->nnzC = p->hStats[20];
   p->st.nnz_c = p->nnzC;
   p->st.lds_dense_products = p->hStats[kStatDenseElems];
@@ -1394,6 +1407,10 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   if (p->wf != 0)
     launch_compact_rows(p->f64, p->m, p->rowBin, p->NS + 1, p->tmpOff, p->cnt, p->cRowOff,
                         p->tcol1, p->tval1, p->tcol2, p->tval2, ccol, cval, p->sl);
+  if (p->wf == 0)
+    launch_num_rows_esc(p->f64, p->numOrder + p->numBinStart[2 * p->NS],
+                        p->numBinStart[2 * p->NS + 1] - p->numBinStart[2 * p->NS], a, p->cRowOff,
+                        ccol, cval, p->errWord, p->sl);
   for (int b = 0; p->wf == 0 && b < p->NS; ++b) {
     const int64_t st = p->numBinStart[b], en = p->numBinStart[b + 1];
     launch_num_rows(p->numBins[b], p->f64, p->numOrder + st, en - st, a, p->cRowOff, ccol, cval,

@@ -149,10 +149,11 @@ void launch_gather_i64(const int64_t* src, const int32_t* idx, int64_t n, int64_
 void launch_row_lengths(int64_t n, const int32_t* rows, const int32_t* rp, int64_t* dst,
                         hipStream_t s);
 // key[i] = bin of cnt[rows[i]] among caps[0..nbins) (first cap >= value), for
-// light rows; heavy rows (rowBin == heavyBin) get 255.
+// light rows; heavy rows (rowBin == heavyBin) get 255; with escKey >= 0,
+// rows of the first product bin (at most 32 products) get escKey.
 void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,
                              int heavyBin, const int32_t* caps, int nbins, uint8_t* key,
-                             hipStream_t s);
+                             hipStream_t s, int escKey = -1);
 
 // ---- k_light.hip ----
 void light_set_attributes();
@@ -169,6 +170,14 @@ void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t
                          void* cval, int32_t* err, hipStream_t s, int64_t* cntOut = nullptr);
 void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
                      int64_t* cnt, int32_t* err, hipStream_t s);
+// Rows of at most 32 products (the first product bin) by expand-sort-compact
+// in 32 lanes each: count of distinct columns, or the sorted row (cntOut as
+// for launch_num_rows).
+void launch_sym_rows_esc(const int32_t* rows, int64_t nrows, const RowArgs& a, int64_t* cnt,
+                         hipStream_t s);
+void launch_num_rows_esc(bool f64, const int32_t* rows, int64_t nrows, const RowArgs& a,
+                         const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
+                         hipStream_t s, int64_t* cntOut = nullptr);
 void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
                      const RowArgs& a, const int64_t* cRowOff, int32_t* ccol, void* cval,
                      int32_t* err, hipStream_t s, int64_t* cntOut = nullptr);

@@ -558,6 +558,143 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
   }
 }
 
+// ------------------------------------------------ ESC for short rows
+// Rows of at most kEscLanes products (Ocean page, §3: an expand-sort-compact
+// accumulator for short rows, several rows per work group): 32 lanes per row,
+// one product per lane, a bitonic sort of (column, value) by lane exchanges,
+// then equal columns are summed by a segmented scan and the last lane of
+// every run writes it.  No LDS.  Symbolic (kNum false) stores the count of
+// distinct columns; numeric writes the row at cRowOff[row], or, with cntOut,
+// into its reserved slots (count, or -1 when it does not fit).
+constexpr int kEscLanes = 32;
+constexpr int kEscNT = 256;
+
+template <int LD, typename V>
+__device__ __forceinline__ void esc_step(int k, int32_t& key, V& val) {
+  const int i = lane_id() % kEscLanes;
+  const int32_t ok = lane_xor<LD>(key);
+  const V ov = lane_xor_v<LD>(val);
+  const bool up = (i & k) == 0;
+  const bool lower = (i & LD) == 0;
+  const bool take = (lower == up) ? (ok < key) : (ok > key);
+  if (take) {
+    key = ok;
+    val = ov;
+  }
+}
+
+template <bool kNum, typename V>
+__global__ __launch_bounds__(kEscNT) void k_rows_esc(const int32_t* __restrict__ rows,
+                                                     int64_t nrows, RowArgs a,
+                                                     const int64_t* __restrict__ cRowOff,
+                                                     int32_t* __restrict__ ccol,
+                                                     V* __restrict__ cval,
+                                                     int64_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ err,
+                                                     int64_t* __restrict__ cntOut) {
+  const int64_t ri = ((int64_t)blockIdx.x * kEscNT + threadIdx.x) / kEscLanes;
+  const int l = lane_id() % kEscLanes;
+  const bool live = ri < nrows;
+  int32_t row = 0, P = 0;
+  int64_t rs = 0, re = 0;
+  if (live) {
+    row = rows[ri];
+    rs = a.arp[row];
+    re = a.arp[row + 1];
+    P = (int32_t)a.rowP[row];
+  }
+  // Product l belongs to the entry whose first product is the last at or
+  // before l.  Rows of at most 32 entries: entry l of the row sits in lane l
+  // and a search by shuffles finds it; longer rows (entries without products
+  // pad them) search scanA in memory.
+  int32_t so, sb;
+  V sa = V(0);
+  if (re - rs <= kEscLanes) {
+    const int64_t e = rs + l;
+    const bool ev = live && e < re;
+    const int32_t off = ev ? a.scanA[e] : P;
+    const int32_t bs = ev ? a.brp[a.acol[e]] : 0;
+    V av = V(0);
+    if constexpr (kNum) av = ev ? ((const V*)a.aval)[e] : V(0);
+    int s = 0;
+#pragma unroll
+    for (int step = 16; step >= 1; step >>= 1) {
+      const int idx = s + step < kEscLanes ? s + step : kEscLanes - 1;
+      const int32_t o = __shfl(off, idx, kEscLanes);
+      if (s + step < kEscLanes && o <= l) s += step;
+    }
+    so = __shfl(off, s, kEscLanes);
+    sb = __shfl(bs, s, kEscLanes);
+    if constexpr (kNum) sa = __shfl(av, s, kEscLanes);
+  } else {
+    int64_t lo = rs, hi = re - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (a.scanA[mid] <= l) lo = mid;
+      else hi = mid - 1;
+    }
+    so = a.scanA[lo];
+    sb = a.brp[a.acol[lo]];
+    if constexpr (kNum) sa = ((const V*)a.aval)[lo];
+  }
+  const bool act = live && l < P;
+  int32_t key = INT_MAX;
+  V val = V(0);
+  if (act) {
+    const int32_t b = sb + (l - so);
+    key = a.bcol[b];
+    if constexpr (kNum) val = sa * ((const V*)a.bval)[b];
+  }
+  // Bitonic sort of the 32 lanes (absent products sort last as INT_MAX).
+#pragma unroll
+  for (int k = 2; k <= kEscLanes; k <<= 1) {
+    if (k >= 32) esc_step<16, V>(k, key, val);
+    if (k >= 16) esc_step<8, V>(k, key, val);
+    if (k >= 8) esc_step<4, V>(k, key, val);
+    if (k >= 4) esc_step<2, V>(k, key, val);
+    esc_step<1, V>(k, key, val);
+  }
+  const int32_t prev = __shfl_up(key, 1, kEscLanes);
+  const bool valid = key != INT_MAX;
+  const bool head = valid && (l == 0 || prev != key);
+  const uint64_t heads = __ballot(head);
+  const int half = (lane_id() / kEscLanes) * kEscLanes;
+  const uint32_t mine = (uint32_t)(heads >> half);
+  const int32_t nnz = __popc(mine);
+  if constexpr (!kNum) {
+    if (live && l == 0) cnt[row] = nnz;
+  } else {
+    // Segmented inclusive sum: a lane adds its left neighbour's partial
+    // while no run starts between them.
+    bool f = head;
+#pragma unroll
+    for (int d = 1; d < kEscLanes; d <<= 1) {
+      const V y = __shfl_up(val, d, kEscLanes);
+      const bool fy = __shfl_up((int)f, d, kEscLanes) != 0;
+      if (l >= d && !f) val += y;
+      if (l >= d) f = f || fy;
+    }
+    const int32_t next = __shfl_down(key, 1, kEscLanes);
+    const bool tail = valid && (l == kEscLanes - 1 || next != key);
+    const int32_t pos = __popc(mine & ((2u << l) - 1u)) - 1;  // run index
+    if (live) {
+      const int64_t base = cRowOff[row];
+      const int64_t want = cRowOff[row + 1] - base;
+      bool write = true;
+      if (cntOut) {
+        write = nnz <= want;
+        if (l == 0) cntOut[row] = write ? nnz : -1;
+      } else if (l == 0 && want != nnz) {
+        flag_error(err, kErrCountMismatch);
+      }
+      if (write && tail && pos < want) {
+        ccol[base + pos] = key;
+        cval[base + pos] = val;
+      }
+    }
+  }
+}
+
 template <int TPR, int RPB, int E, typename V, typename C = int32_t>
 __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, int32_t spt,
@@ -840,4 +977,26 @@ void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t
   (void)flag_unsupported;  // make_bins rejects bins without an instance
 }
 
+void launch_sym_rows_esc(const int32_t* rows, int64_t nrows, const RowArgs& a, int64_t* cnt,
+                         hipStream_t s) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows * kEscLanes + kEscNT - 1) / kEscNT);
+  hipLaunchKernelGGL((k_rows_esc<false, float>), dim3(grid), dim3(kEscNT), 0, s, rows, nrows, a,
+                     nullptr, nullptr, nullptr, cnt, nullptr, nullptr);
+}
+
+void launch_num_rows_esc(bool f64, const int32_t* rows, int64_t nrows, const RowArgs& a,
+                         const int64_t* cRowOff, int32_t* ccol, void* cval, int32_t* err,
+                         hipStream_t s, int64_t* cntOut) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows * kEscLanes + kEscNT - 1) / kEscNT);
+  if (f64)
+    hipLaunchKernelGGL((k_rows_esc<true, double>), dim3(grid), dim3(kEscNT), 0, s, rows, nrows, a,
+                       cRowOff, ccol, (double*)cval, nullptr, err, cntOut);
+  else
+    hipLaunchKernelGGL((k_rows_esc<true, float>), dim3(grid), dim3(kEscNT), 0, s, rows, nrows, a,
+                       cRowOff, ccol, (float*)cval, nullptr, err, cntOut);
+}
+
 }  // namespace sg
+

@@ -515,12 +515,17 @@ __global__ __launch_bounds__(kNT) void k_numeric_row_bins(int64_t m, const int64
                                                           const uint8_t* __restrict__ rowBin,
                                                           int heavyBin,
                                                           const int32_t* __restrict__ caps,
-                                                          int nbins, uint8_t* __restrict__ key) {
+                                                          int nbins, int escKey,
+                                                          uint8_t* __restrict__ key) {
   const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
   if (i >= m) return;
   const int rb = rowBin[i];
   if (rb == 0 || rb == heavyBin) {
     key[i] = 255;
+    return;
+  }
+  if (rb == 1 && escKey >= 0) {  // at most caps[0] <= 32 products: ESC
+    key[i] = (uint8_t)escKey;
     return;
   }
   if (rb > heavyBin) {  // dense window rows: bin by products, after the hash bins
@@ -655,10 +660,10 @@ void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hip
 
 void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,
                              int heavyBin, const int32_t* caps, int nbins, uint8_t* key,
-                             hipStream_t s) {
+                             hipStream_t s, int escKey) {
   if (m <= 0) return;
   hipLaunchKernelGGL(k_numeric_row_bins, dim3(grid_for(m, kNT)), dim3(kNT), 0, s, m, cnt, rowBin,
-                     heavyBin, caps, nbins, key);
+                     heavyBin, caps, nbins, escKey, key);
 }
 
 }  // namespace sg

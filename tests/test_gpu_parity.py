@@ -105,6 +105,23 @@ def test_uniform_values_fp64_and_fp32():
         check_full(A, B)
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_esc_short_rows_match_hash(dtype):
+    # Rows of at most 32 products take the expand-sort-compact kernel: rows of
+    # up to 60 entries whose B rows are mostly empty (more entries than
+    # lanes), duplicate columns, empty rows; the hash kernels and the oracle
+    # agree with it.
+    B = synth.random_csr(3000, 400, 0.8, 41, values="int", empty_row_frac=0.8, dtype=dtype)
+    A = synth.random_csr(2000, 3000, 25.0, 42, values="int", empty_row_frac=0.1, dtype=dtype)
+    P = oracle.row_products(A, B)
+    assert P.max() <= 32 and (np.diff(A.row_ptr) > 32).any()
+    st = check_full(A, B, exact=True)
+    st2 = check_full(A, B, exact=True, light_no_esc=1)
+    assert st["nnz_c"] == st2["nnz_c"]
+    C = synth.random_csr(4000, 4000, 3.0, 43, values="uniform", dtype=dtype)
+    check_full(C, C)
+
+
 def test_wide_light_rows_all_bins():
     # rows of 1..~6000 products exercise every light-row bin, with both hash
     # sizes and sorts near their capacity
