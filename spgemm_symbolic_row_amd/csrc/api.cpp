@@ -102,7 +102,8 @@ void make_bins(int64_t tau, int64_t lds, int val_bytes, std::vector<BinCfg>* sym
     const int slot = 4 + val_bytes;
     const int64_t N = next_pow2(cap);
     int64_t T = std::max<int64_t>(next_pow2(2 * cap), tpr);
-    const int64_t extra = (int64_t)(tpr * rpb / 64) * 4 + (int64_t)rpb * 4;
+    const int64_t extra = (int64_t)(tpr * rpb / 64) * 4 + (int64_t)rpb * 4 +
+                          (int64_t)num_rows_radix_bytes(tpr, rpb);
     while (T > tpr && (int64_t)rpb * T * slot + extra > lds) T -= tpr;
     if (T < N || T <= cap || T / tpr > 24)
       throw Error{SPGEMM_ERR_INVALID_ARG, "numeric hash table does not fit the LDS budget"};

@@ -64,6 +64,14 @@ struct RowArgs {
 // hash table.  The bitmap (16 bytes per product of the bin's bound) stays
 // within a small multiple of the hash table it replaces, and at most 65536
 // columns wide.
+// LDS the light numeric kernel reserves for the radix sort of a row's
+// entries (one row per work group, at least 256 threads): per wave 256
+// 16-bit digit counters, 256 digit bases, and a min/max per wave.
+__host__ __device__ inline size_t num_rows_radix_bytes(int tpr, int rpb) {
+  return (rpb == 1 && tpr >= 256) ? (size_t)(tpr / 64) * 256 * 2 + 256 * 4 + (size_t)(tpr / 64) * 8
+                                  : 0;
+}
+
 __host__ __device__ inline int32_t window_words(int64_t cap) {
   return (int32_t)(4 * cap < 2048 ? 4 * cap : 2048);
 }

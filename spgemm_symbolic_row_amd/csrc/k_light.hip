@@ -484,6 +484,141 @@ __device__ __forceinline__ void sort_to_regs(int32_t* keys, V* vals, int32_t (&k
   }
 }
 
+// Radix sort of a row's compacted entries (one row per work group, at least
+// 256 threads), in place of the bitonic network: the entries are sorted as
+// 32-bit words (column - row minimum) << ptrBits | slot, ptrBits = bits of
+// the slot index, by a least-significant-digit radix sort on 8-bit digits of
+// the column part; the values stay in their slots and are gathered through
+// the slot index as the sorted row is written (the indirect key-pointer sort
+// the Ocean page describes for its hash accumulators, §3).  A pass ranks the
+// entries of each wave stably (lanes with equal digits found by ballots, a
+// running count per wave and digit), orders the waves by a prefix, and
+// scatters; keys[0, total) and keys[total, 2 total) are the two buffers.
+// Returns false, with nothing changed, when the words need more than 32
+// bits, the row has more entries than TPR * E, or keys has no room for the
+// second buffer; the caller then sorts with the network.
+template <int TPR, int E, typename V>
+__device__ bool radix_sorted_write(int32_t* keys, const V* vals, int32_t total, int32_t T,
+                                   unsigned char* scratch, bool live, int64_t base, int32_t lim,
+                                   int32_t* __restrict__ ccol, V* __restrict__ cval) {
+  constexpr int WPR = TPR / kWave;
+  uint16_t* wcnt = (uint16_t*)scratch;                       // [WPR][256]
+  int32_t* rbase = (int32_t*)(scratch + WPR * 256 * 2);      // [256]
+  int32_t* red = rbase + 256;                                // [2 * WPR]
+  const int t = threadIdx.x, w = t / kWave, l = lane_id();
+  if (total > TPR * E || 2 * total > T) return false;
+  int32_t mn = INT_MAX, mx = -1;
+  for (int i = t; i < total; i += TPR) {
+    const int32_t k = keys[i];
+    mn = k < mn ? k : mn;
+    mx = k > mx ? k : mx;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const int32_t a = __shfl_xor(mn, d), b = __shfl_xor(mx, d);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (l == 0) {
+    red[w] = mn;
+    red[WPR + w] = mx;
+  }
+  __syncthreads();
+  mn = INT_MAX;
+  mx = -1;
+#pragma unroll
+  for (int i = 0; i < WPR; ++i) {
+    mn = red[i] < mn ? red[i] : mn;
+    mx = red[WPR + i] > mx ? red[WPR + i] : mx;
+  }
+  int ptrBits = 1, keyBits = 0;
+  while ((1 << ptrBits) < total) ++ptrBits;
+  while (keyBits < 32 && ((int64_t)1 << keyBits) <= (int64_t)mx - mn) ++keyBits;
+  if (total > 0 && keyBits + ptrBits > 32) return false;  // uniform: all threads read red
+  __syncthreads();  // red is read before anyone goes on
+  uint32_t* src = (uint32_t*)keys;
+  uint32_t* dst = src + total;
+  for (int i = t; i < total; i += TPR) src[i] = ((uint32_t)(keys[i] - mn) << ptrBits) | (uint32_t)i;
+  __syncthreads();
+  const int passes = (keyBits + 7) / 8;
+  const int64_t e0 = (int64_t)w * kWave * E + l;  // entry of item i: e0 + i * 64
+  for (int p = 0; p < passes; ++p) {
+    const int shift = ptrBits + 8 * p;
+    const int db = keyBits - 8 * p < 8 ? keyBits - 8 * p : 8;
+    const uint32_t mask = (1u << db) - 1u;
+    uint16_t* my = wcnt + w * 256;
+    for (int d = l; d < 256; d += kWave) my[d] = 0;
+    uint32_t v[E], rank[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int64_t e = e0 + (int64_t)i * kWave;
+      v[i] = e < total ? src[e] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const bool act = e0 + (int64_t)i * kWave < total;
+      const uint32_t d = (v[i] >> shift) & mask;
+      const uint64_t peers = match_key(d, db, act);
+      uint32_t r = 0;
+      if (act) {
+        // The store depends on the load, and one wave's LDS accesses are
+        // performed in order.
+        const uint32_t before = my[d];
+        r = before + (uint32_t)__popcll(peers & lanemask_lt());
+        if (l == last_set64(peers)) my[d] = (uint16_t)(before + __popcll(peers));
+      }
+      rank[i] = r;
+    }
+    __syncthreads();
+    // Per digit: prefix over the waves, then the digit totals' prefix.
+    if (t < 256) {
+      uint32_t run = 0;
+      for (int u = 0; u < WPR; ++u) {
+        const uint32_t c = wcnt[u * 256 + t];
+        wcnt[u * 256 + t] = (uint16_t)run;
+        run += c;
+      }
+      rbase[t] = (int32_t)run;
+    }
+    __syncthreads();
+    if (w == 0) {
+      int32_t c4[4], s4 = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c4[j] = rbase[l * 4 + j];
+        s4 += c4[j];
+      }
+      int32_t run = wave_incl_scan(s4) - s4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rbase[l * 4 + j] = run;
+        run += c4[j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (e0 + (int64_t)i * kWave < total) {
+        const uint32_t d = (v[i] >> shift) & mask;
+        dst[rbase[d] + my[d] + rank[i]] = v[i];
+      }
+    }
+    __syncthreads();
+    uint32_t* tmp = src;
+    src = dst;
+    dst = tmp;
+  }
+  if (live) {
+    const uint32_t pm = (1u << ptrBits) - 1u;
+    for (int r = t; r < lim; r += TPR) {
+      const uint32_t q = src[r];
+      ccol[base + r] = mn + (int32_t)(q >> ptrBits);
+      cval[base + r] = vals[q & pm];
+    }
+  }
+  return true;
+}
+
 // With cntOut (size-estimate workflows), cRowOff holds each row's reserved
 // capacity instead of its exact size: a row whose entries fit is written
 // there and its count stored in cntOut; a row with more entries than its
@@ -532,13 +667,11 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
   }
   __syncthreads();
   const int32_t total = compact_slots<TPR, RPB, E, V>(keys, vals, spt, wtot);
-  int32_t kk[E];
-  V vv[E];
-  sort_to_regs<TPR, E, V>(keys, vals, kk, vv);
+  int64_t base = 0;
+  int32_t lim = 0;
   if (ri < nrows) {
-    const int64_t base = cRowOff[row];
+    base = cRowOff[row];
     const int64_t want = cRowOff[row + 1] - base;
-    int32_t lim;
     if (cntOut) {
       const bool over = total > want || full[g] != 0;
       if (t == 0) cntOut[row] = over ? -1 : total;
@@ -547,6 +680,16 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
       if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
       lim = (int32_t)(want < total ? want : total);
     }
+  }
+  if constexpr (RPB == 1 && TPR >= 256) {
+    if (radix_sorted_write<TPR, E, V>(keys, vals, total, T, (unsigned char*)(full + RPB),
+                                      ri < nrows, base, lim, ccol, cval))
+      return;
+  }
+  int32_t kk[E];
+  V vv[E];
+  sort_to_regs<TPR, E, V>(keys, vals, kk, vv);
+  if (ri < nrows) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int r = t * E + e;
