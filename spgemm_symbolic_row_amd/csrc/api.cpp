@@ -1208,7 +1208,8 @@ const double* hll_table(spgemm_plan_t p, int lg, hipStream_t s) {
 // Ocean's Table 1 on this plan: upper bound below 64 products per row;
 // HyperLogLog when products / nnz(A) >= 8 and the compression ratio of a row
 // sample (products / estimated nnz over 3% of the rows, 600 to 10,000, evenly
-// spaced) is >= 8; else the symbolic pass.
+// spaced; heavy rows, which keep the exact chunk path, left out) is >= 8;
+// else the symbolic pass.
 int select_workflow(spgemm_plan_t p, hipStream_t s) {
   const int64_t m = p->m, P = p->st.products;
   if (P < 64 * m) return 1;
@@ -1223,7 +1224,8 @@ int select_workflow(spgemm_plan_t p, hipStream_t s) {
   int64_t* pr = alloc_n<int64_t>(p, ns, s);
   HIP_CHECK(hipMemcpyAsync(rows, hrows.data(), sizeof(int32_t) * ns, hipMemcpyHostToDevice, s));
   const double* lc = hll_table(p, lg, s);
-  launch_hll_rows_direct(ns, rows, p->arp, p->acol, p->brp, p->bcol, lg, lc, est, s);
+  launch_hll_rows_direct(ns, rows, p->arp, p->acol, p->brp, p->bcol, p->rowP, p->rowTau, lg, lc,
+                         est, s);
   launch_gather_i64(p->rowP, rows, ns, pr, s);
   check_launch("row sample estimate");
   std::vector<double> he(ns);
@@ -1233,6 +1235,7 @@ int select_workflow(spgemm_plan_t p, hipStream_t s) {
   HIP_CHECK(hipStreamSynchronize(s));
   double sp = 0, se = 0;
   for (int64_t j = 0; j < ns; ++j) {
+    if (hp[j] > p->rowTau) continue;
     sp += (double)hp[j];
     se += he[j];
   }

@@ -385,9 +385,11 @@ void launch_hll_capacity(int64_t m, const int32_t* arp, const int32_t* acol, con
                          int lg, const double* lc, double coef, const int64_t* rowP,
                          const uint8_t* rowBin, int heavyBin, int64_t* cap, double* est,
                          hipStream_t s);
+// Rows of more than maxP products get 0 (not estimated).
 void launch_hll_rows_direct(int64_t ns, const int32_t* rows, const int32_t* arp,
-                            const int32_t* acol, const int32_t* brp, const int32_t* bcol, int lg,
-                            const double* lc, double* est, hipStream_t s);
+                            const int32_t* acol, const int32_t* brp, const int32_t* bcol,
+                            const int64_t* rowP, int64_t maxP, int lg, const double* lc,
+                            double* est, hipStream_t s);
 void launch_ub_capacity(int64_t m, const int64_t* rowP, const uint8_t* rowBin, int heavyBin,
                         int64_t* cap, hipStream_t s);
 void launch_overflow_rows(int64_t m, const int64_t* cnt, const int64_t* rowP,

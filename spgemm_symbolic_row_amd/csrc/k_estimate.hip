@@ -122,18 +122,23 @@ __global__ __launch_bounds__(kNT) void k_hll_capacity(
 }
 
 // Estimate of listed rows straight from their products' columns (no B
-// sketches): the row sample of the workflow selection.
+// sketches): the row sample of the workflow selection.  Rows of more than
+// maxP products (heavy rows, sized exactly by the chunk path) get 0.
 __global__ __launch_bounds__(kNT) void k_hll_rows_direct(
     int64_t ns, const int32_t* __restrict__ rows, const int32_t* __restrict__ arp,
     const int32_t* __restrict__ acol, const int32_t* __restrict__ brp,
-    const int32_t* __restrict__ bcol, int lg, const double* __restrict__ lc,
-    double* __restrict__ est) {
+    const int32_t* __restrict__ bcol, const int64_t* __restrict__ rowP, int64_t maxP, int lg,
+    const double* __restrict__ lc, double* __restrict__ est) {
   __shared__ uint32_t r[kWPB][kWave];
   const int w = threadIdx.x / kWave, l = lane_id();
   const int M = 1 << lg;
   const int64_t nw = (int64_t)gridDim.x * kWPB;
   for (int64_t s = (int64_t)blockIdx.x * kWPB + w; s < ns; s += nw) {
     const int64_t i = rows[s];
+    if (rowP[i] > maxP) {
+      if (l == 0) est[s] = 0.0;
+      continue;
+    }
     r[w][l] = 0;
     for (int32_t j = arp[i]; j < arp[i + 1]; ++j) {
       const int32_t k = acol[j];
@@ -246,11 +251,12 @@ void launch_hll_capacity(int64_t m, const int32_t* arp, const int32_t* acol, con
 }
 
 void launch_hll_rows_direct(int64_t ns, const int32_t* rows, const int32_t* arp,
-                            const int32_t* acol, const int32_t* brp, const int32_t* bcol, int lg,
-                            const double* lc, double* est, hipStream_t s) {
+                            const int32_t* acol, const int32_t* brp, const int32_t* bcol,
+                            const int64_t* rowP, int64_t maxP, int lg, const double* lc,
+                            double* est, hipStream_t s) {
   if (ns <= 0) return;
   hipLaunchKernelGGL(k_hll_rows_direct, dim3(capped_grid(ns, kWPB)), dim3(kNT), 0, s, ns, rows,
-                     arp, acol, brp, bcol, lg, lc, est);
+                     arp, acol, brp, bcol, rowP, maxP, lg, lc, est);
 }
 
 void launch_ub_capacity(int64_t m, const int64_t* rowP, const uint8_t* rowBin, int heavyBin,

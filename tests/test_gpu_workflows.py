@@ -119,14 +119,16 @@ def test_workflows_with_heavy_rows():
         assert st["heavy_rows"] > 0 and st["workflow"] == wf
 
 
-def _oracle_choice(A, B):
+def _oracle_choice(A, B, heavy_threshold):
+    # Heavy rows (more than heavy_threshold products) keep the exact chunk
+    # path and are left out of the sampled compression ratio.
     P = oracle.row_products(A, B)
     total = int(P.sum())
     cr = None
     if total >= 64 * A.m and total >= 8 * A.col.shape[0]:
         M = oracle.hll_registers(total, A.col.shape[0])
-        rows = oracle.sample_rows(A.m)
-        e = np.concatenate([oracle.hll_estimate(A, B, M, int(r), int(r) + 1) for r in rows])
+        rows = [int(r) for r in oracle.sample_rows(A.m) if P[r] <= heavy_threshold]
+        e = np.concatenate([oracle.hll_estimate(A, B, M, r, r + 1) for r in rows])
         cr = float(P[rows].sum()) / float(e.sum())
     return oracle.select_workflow(A.m, A.col.shape[0], total, cr), cr
 
@@ -140,7 +142,7 @@ def _narrow(m, k, per_row, width, seed):
                      rng.uniform(-1, 1, k * per_row), k, m)
 
 
-@pytest.mark.parametrize("case", ["er", "narrow", "rmat"])
+@pytest.mark.parametrize("case", ["er", "narrow", "rmat", "rmat_heavy"])
 def test_auto_selection_follows_table_1(case):
     if case == "er":          # about 64 products per row or fewer: upper bound
         A = synth.erdos_renyi(2048, 6.0, seed=1)
@@ -151,12 +153,13 @@ def test_auto_selection_follows_table_1(case):
     else:                      # compression below 8: symbolic
         A = synth.rmat(12, 16, seed=8)
         B = A
-    want, cr = _oracle_choice(A, B)
-    st, *_ = _run(A, B, workflow=3)
+    opts = {"heavy_threshold": 256} if case == "rmat_heavy" else {}
+    st, *_ = _run(A, B, workflow=3, **opts)
+    want, cr = _oracle_choice(A, B, st["heavy_row_threshold"])
     assert st["workflow"] == want
     if cr is not None:
         assert abs(st["sampled_cr"] - cr) <= 1e-12 * cr
-    assert want == {"er": 1, "narrow": 2, "rmat": 0}[case]
+    assert want == {"er": 1, "narrow": 2, "rmat": 0, "rmat_heavy": 0}[case]
 
 
 def test_row_estimates_errors():
