@@ -72,8 +72,10 @@ def test_small_random_exact(m, k, n, per_row, seed, dtype):
     check_full(A, B, exact=True)
 
 
+@pytest.mark.parametrize("opts", [{}, {"workflow": 1}, {"workflow": 2}, {"workflow": 3},
+                                  {"light_no_esc": 1}], ids=["wf0", "wf1", "wf2", "wf3", "noesc"])
 @pytest.mark.parametrize("case", ["m0", "k0", "nnz0", "single", "empty_b"])
-def test_degenerate(case):
+def test_degenerate(case, opts):
     if case == "m0":
         A = synth.CSR(np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0), 0, 5)
         B = synth.random_csr(5, 6, 2.0, 1)
@@ -89,7 +91,7 @@ def test_degenerate(case):
     else:
         A = synth.random_csr(20, 30, 4.0, 3)
         B = synth.CSR(np.zeros(31, np.int32), np.zeros(0, np.int32), np.zeros(0), 30, 9)
-    check_full(A, B, exact=True)
+    check_full(A, B, exact=True, **opts)
 
 
 def test_er4096_config():
