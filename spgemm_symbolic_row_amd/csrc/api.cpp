@@ -1095,7 +1095,7 @@ void symbolic_batch(spgemm_plan_t p, const Batch& B) {
   }
   const int64_t a = B.fcBinStart[p->NS], e = B.fcBinStart[p->NS + 1];
   if (p->chunkWords)
-    launch_sym_chunks_persist(desc + a, e - a, p->chunkWords, cl, p->numCUs, s);
+    launch_sym_chunks_persist(desc + a, e - a, cl, p->numCUs, s);
   else
     launch_dense_sym(desc + a, e - a, cl, p->errWord, s);
   ph_end(p, phD, s);

@@ -324,8 +324,8 @@ void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* 
 void chunks_set_attributes();
 size_t rank_chunk_lds(bool f64, int32_t T, int32_t words, int rpb);
 // Chunk symbolic by bitmap with persistent work groups (dense chunks).
-void launch_sym_chunks_persist(const ChunkDesc* desc, int64_t n, int32_t words,
-                               const ChunkList& cl, int numCUs, hipStream_t s);
+void launch_sym_chunks_persist(const ChunkDesc* desc, int64_t n, const ChunkList& cl,
+                               int numCUs, hipStream_t s);
 // Light-chunk numeric with elements in registers and a dense LDS array of
 // the chunk's output size indexed by bitmap rank.  Returns false (nothing
 // launched) when the bin does not fit this kernel.

@@ -65,17 +65,22 @@ __global__ __launch_bounds__(TPC* CPB) void k_sym_chunks_bitmap(const ChunkDesc*
 
 // Symbolic of the dense chunks: one persistent 1024-thread work group per
 // half CU walks its chunks, and the first batch of the next chunk's columns
-// (and its descriptor) is in flight while the current bitmap is counted and
-// cleared.
+// (and its descriptor) is in flight while the current marks are counted and
+// cleared.  A column is marked by a plain LDS byte store (no read, no atomic:
+// every writer stores the same 1), and the chunk's nnz is the number of
+// marked bytes.
 constexpr int kSymPT = 1024;
 constexpr int kSymB = 8;  // columns per thread per batch
 template <typename C>
 __global__ __launch_bounds__(kSymPT) void k_sym_chunks_persist(const ChunkDesc* __restrict__ desc,
-                                                               int64_t n, int32_t words,
+                                                               int64_t n, int32_t width,
                                                                ChunkList cl) {
-  extern __shared__ __align__(16) uint32_t bm[];
+  // width: the dense chunks' width, a multiple of 16; marks[width] bytes.
+  extern __shared__ __align__(16) uint4 mk4[];
+  unsigned char* mk = (unsigned char*)mk4;
   __shared__ int32_t gsum[kSymPT / kWave];
-  for (int i = threadIdx.x; i < words; i += kSymPT) bm[i] = 0;
+  const int nv = width / 16;
+  for (int i = threadIdx.x; i < nv; i += kSymPT) mk4[i] = uint4{0, 0, 0, 0};
   int64_t ci = blockIdx.x;
   ChunkDesc d{};
   int32_t cc[kSymB];
@@ -91,10 +96,7 @@ __global__ __launch_bounds__(kSymPT) void k_sym_chunks_persist(const ChunkDesc* 
 #pragma unroll
     for (int k = 0; k < kSymB; ++k) {
       const int32_t c = cc[k];
-      if (c >= 0) {
-        const uint32_t bit = 1u << (c & 31);
-        if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
-      }
+      if ((uint32_t)c < (uint32_t)width) mk[c] = 1;
     }
   };
   if (ci < n) {
@@ -118,10 +120,12 @@ __global__ __launch_bounds__(kSymPT) void k_sym_chunks_persist(const ChunkDesc* 
       col = (const C*)(d.buf ? cl.col1 : cl.col0);
       load(d.off + threadIdx.x, d.off + d.cnt);
     }
+    // Marks are 0 or 1, so the popcount of the bytes counts them.
     int32_t mine = 0;
-    for (int i = threadIdx.x; i < words; i += kSymPT) {
-      mine += __popc(bm[i]);
-      bm[i] = 0;
+    for (int i = threadIdx.x; i < nv; i += kSymPT) {
+      const uint4 x = mk4[i];
+      mine += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+      mk4[i] = uint4{0, 0, 0, 0};
     }
     mine = wave_sum(mine);
     if (lane_id() == 0) gsum[threadIdx.x / kWave] = mine;
@@ -482,18 +486,19 @@ void launch_sym_chunks_bitmap(int sizeClass, const ChunkDesc* desc, int64_t n, i
 #undef L
 }
 
-void launch_sym_chunks_persist(const ChunkDesc* desc, int64_t n, int32_t words,
-                               const ChunkList& cl, int numCUs, hipStream_t s) {
+void launch_sym_chunks_persist(const ChunkDesc* desc, int64_t n, const ChunkList& cl,
+                               int numCUs, hipStream_t s) {
   if (n <= 0) return;
   // Two 1024-thread work groups fill a CU's waves.
   const unsigned g = (unsigned)std::min<int64_t>(n, (int64_t)std::max(numCUs, 1) * 2);
-  const size_t lds = (size_t)words * 4;
+  const int32_t width = (int32_t)((cl.W + 15) / 16 * 16);
+  const size_t lds = (size_t)width;
   if (cl.col16)
     hipLaunchKernelGGL(k_sym_chunks_persist<uint16_t>, dim3(g), dim3(kSymPT), lds, s, desc, n,
-                       words, cl);
+                       width, cl);
   else
     hipLaunchKernelGGL(k_sym_chunks_persist<int32_t>, dim3(g), dim3(kSymPT), lds, s, desc, n,
-                       words, cl);
+                       width, cl);
 }
 
 void launch_num_chunks_rank(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,

@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const ChunkDesc* __restrict__
   (void)err;
 }
 
-// Numeric: val[W] + W-bit bitmap in LDS, filled by LDS atomics; the set
-// bits, taken in column order, give the chunk sorted and compacted.
+// Numeric: val[W] and one mark per column in LDS, values added by LDS
+// atomics; the marked columns, taken in column order, give the chunk sorted
+// and compacted.
 //
 // One work group per CU holds the 128 KiB accumulator, so the kernel is
 // persistent: a work group takes chunks blockIdx.x, blockIdx.x + gridDim.x,
@@ -169,21 +170,29 @@ __device__ __forceinline__ void dense_load_batch(const C* __restrict__ col,
     vv[k] = e < end ? val[e] : V(0);
   }
 }
-template <typename V>
-__device__ __forceinline__ void dense_add_batch(V* vals, uint32_t* bm, const int32_t (&cc)[kDenseB],
+// Column marks: one byte per column when the accumulator leaves room for
+// them (a plain LDS byte store per element), else one bit per column (a read
+// and, for a new column, an LDS atomic OR).
+template <typename V, bool kBytes>
+__device__ __forceinline__ void dense_add_batch(V* vals, void* marks, const int32_t (&cc)[kDenseB],
                                                 const V (&vv)[kDenseB]) {
 #pragma unroll
   for (int k = 0; k < kDenseB; ++k) {
     const int32_t c = cc[k];
     if (c >= 0) {
       atomicAdd(&vals[c], vv[k]);
-      const uint32_t bit = 1u << (c & 31);
-      if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+      if constexpr (kBytes) {
+        ((unsigned char*)marks)[c] = 1;
+      } else {
+        uint32_t* bm = (uint32_t*)marks;
+        const uint32_t bit = 1u << (c & 31);
+        if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+      }
     }
   }
 }
 
-template <typename V, typename C>
+template <typename V, typename C, bool kBytes>
 __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restrict__ desc, int64_t n,
                                                         ChunkList cl,
                                                         int32_t* __restrict__ ccol,
@@ -193,11 +202,13 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
   constexpr int kWaves = kDenseNT / kWave;
   const int W = (int)cl.W;
   const int nwords = (W + 31) / 32;
+  // kBytes: W is a power of two from 16 on and the marks take W bytes.
+  const int markWords = kBytes ? W / 4 : nwords;
   V* vals = (V*)smem;
   uint32_t* bm = (uint32_t*)(vals + W);
-  int32_t* wtot = (int32_t*)(bm + nwords);
+  int32_t* wtot = (int32_t*)(bm + markWords);
   for (int i = threadIdx.x; i < W; i += kDenseNT) vals[i] = V(0);
-  for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
+  for (int i = threadIdx.x; i < markWords; i += kDenseNT) bm[i] = 0;
   const int w = threadIdx.x / kWave, lane = lane_id();
 
   int64_t ci = blockIdx.x;
@@ -219,11 +230,11 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
     // The next chunk's descriptor, in flight during this chunk.
     const int64_t cn = ci + gridDim.x;
     if (cn < n) d = desc[cn];
-    dense_add_batch(vals, bm, cc, vv);
+    dense_add_batch<V, kBytes>(vals, bm, cc, vv);
     for (int64_t e0 = off + threadIdx.x + (int64_t)kDenseNT * kDenseB; e0 < end;
          e0 += (int64_t)kDenseNT * kDenseB) {
       dense_load_batch(col, val, e0, end, cc, vv);
-      dense_add_batch(vals, bm, cc, vv);
+      dense_add_batch<V, kBytes>(vals, bm, cc, vv);
     }
     __syncthreads();
     // First batch of the next chunk, in flight during the write-out.
@@ -243,8 +254,21 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
     const int lc0 = w * cpw + lane * cpl;             // this lane's first column
     uint32_t mask = 0;
     if (lc0 < W && lane * cpl < cpw) {
-      const uint32_t word = bm[lc0 >> 5];
-      mask = cpl >= 32 ? word : (word >> (lc0 & 31)) & ((1u << cpl) - 1u);
+      if constexpr (kBytes) {
+        // cpl is a power of two; from 4 on, lc0 is a multiple of 4.
+        const unsigned char* mk = (const unsigned char*)bm;
+        if (cpl >= 4) {
+          for (int k = 0; k < cpl; k += 4) {
+            const uint32_t wd = *(const uint32_t*)(mk + lc0 + k);
+            mask |= ((wd & 1u) | ((wd >> 7) & 2u) | ((wd >> 14) & 4u) | ((wd >> 21) & 8u)) << k;
+          }
+        } else {
+          for (int k = 0; k < cpl; ++k) mask |= (uint32_t)mk[lc0 + k] << k;
+        }
+      } else {
+        const uint32_t word = bm[lc0 >> 5];
+        mask = cpl >= 32 ? word : (word >> (lc0 & 31)) & ((1u << cpl) - 1u);
+      }
     }
     const int32_t cntL = __popc(mask);
     const int32_t incL = wave_incl_scan(cntL);
@@ -275,7 +299,11 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
       }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
+    if constexpr (kBytes) {
+      for (int i = threadIdx.x; i < W / 16; i += kDenseNT) ((uint4*)bm)[i] = uint4{0, 0, 0, 0};
+    } else {
+      for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
+    }
     __syncthreads();
     ci = cn;
   }
@@ -340,10 +368,14 @@ __global__ __launch_bounds__(kNT) void k_final_map(int64_t nfc, const int32_t* _
 void heavy_set_attributes() {
 #define SG_ATTR(K) \
   (void)hipFuncSetAttribute((const void*)(K), hipFuncAttributeMaxDynamicSharedMemorySize, 163840)
-  SG_ATTR((k_dense_num<float, int32_t>));
-  SG_ATTR((k_dense_num<double, int32_t>));
-  SG_ATTR((k_dense_num<float, uint16_t>));
-  SG_ATTR((k_dense_num<double, uint16_t>));
+  SG_ATTR((k_dense_num<float, int32_t, false>));
+  SG_ATTR((k_dense_num<double, int32_t, false>));
+  SG_ATTR((k_dense_num<float, uint16_t, false>));
+  SG_ATTR((k_dense_num<double, uint16_t, false>));
+  SG_ATTR((k_dense_num<float, int32_t, true>));
+  SG_ATTR((k_dense_num<double, int32_t, true>));
+  SG_ATTR((k_dense_num<float, uint16_t, true>));
+  SG_ATTR((k_dense_num<double, uint16_t, true>));
   SG_ATTR(k_dense_sym<int32_t>);
   SG_ATTR(k_dense_sym<uint16_t>);
 #undef SG_ATTR
@@ -403,8 +435,17 @@ void launch_dense_sym(const ChunkDesc* desc, int64_t n, const ChunkList& cl, int
     hipLaunchKernelGGL(k_dense_sym<int32_t>, dim3((unsigned)n), dim3(kNT), lds, s, desc, cl, err);
 }
 
+// Byte marks when W is a power of two from 16 on (so every lane's run of
+// columns is a whole number of 4-byte words, or shorter than one) and they
+// fit beside the values.
+static bool dense_byte_marks(bool f64, int64_t W) {
+  return W >= 16 && (W & (W - 1)) == 0 &&
+         W * ((f64 ? 8 : 4) + 1) + (kDenseNT / kWave) * 4 <= 163840;
+}
+
 size_t dense_num_lds(bool f64, int64_t W) {
-  return (size_t)W * (f64 ? 8 : 4) + (size_t)((W + 31) / 32) * 4 + (kDenseNT / kWave) * 4;
+  const size_t marks = dense_byte_marks(f64, W) ? (size_t)W : (size_t)((W + 31) / 32) * 4;
+  return (size_t)W * (f64 ? 8 : 4) + marks + (kDenseNT / kWave) * 4;
 }
 
 void launch_chunk_desc(int64_t n, const int32_t* order, const ChunkList& cl,
@@ -418,12 +459,19 @@ void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkLis
                       int32_t* ccol, void* cval, int32_t* err, int numCUs, hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = dense_num_lds(f64, cl.W);
+  const bool bytes = dense_byte_marks(f64, cl.W);
   // As many work groups as fit on the device at once (LDS of a CU: 160 KiB).
   const int64_t perCU = std::max<int64_t>(1, (int64_t)163840 / (int64_t)lds);
   const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1) * perCU);
 #define L(V, C)                                                                              \
-  hipLaunchKernelGGL((k_dense_num<V, C>), dim3(g), dim3(kDenseNT), lds, s, desc, n, cl, ccol,   \
-                     (V*)cval, err)
+  do {                                                                                       \
+    if (bytes)                                                                               \
+      hipLaunchKernelGGL((k_dense_num<V, C, true>), dim3(g), dim3(kDenseNT), lds, s, desc, n,  \
+                         cl, ccol, (V*)cval, err);                                           \
+    else                                                                                     \
+      hipLaunchKernelGGL((k_dense_num<V, C, false>), dim3(g), dim3(kDenseNT), lds, s, desc, n, \
+                         cl, ccol, (V*)cval, err);                                           \
+  } while (0)
   if (f64 && cl.col16) L(double, uint16_t);
   else if (f64) L(double, int32_t);
   else if (cl.col16) L(float, uint16_t);
