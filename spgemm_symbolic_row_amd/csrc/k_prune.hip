@@ -22,10 +22,17 @@ __device__ __forceinline__ int64_t rp_at(const void* rp, int64_t i) {
 // close to each other usually share most columns (clustered graphs, banded
 // matrices), so far fewer global atomics are issued; a value whose column
 // finds no free slot within kPruneProbes probes goes to global memory
-// directly.  Kept counts per row are exact integers either way.
-constexpr int kPruneRows = 16;
+// directly (once the table is full, the columns met only once, such as the
+// scattered inter-cluster entries of a clustered graph, take this path
+// after a few probes, while the shared columns already sit in the table).
+// A wave loads kPruneU runs of 64 entries (columns and values together)
+// before it uses any of them.  Kept counts per row are exact integers
+// either way.
+constexpr int kPruneNT = 512;
+constexpr int kPruneRows = 64;
 constexpr int kPruneSlots = 4096;
-constexpr int kPruneProbes = 16;
+constexpr int kPruneProbes = 4;
+constexpr int kPruneU = 4;
 
 __device__ __forceinline__ bool colsum_add_lds(int32_t* keys, double* vals, int32_t key, double v) {
   uint32_t s = hash_slot(key, kPruneSlots);
@@ -48,46 +55,54 @@ __device__ __forceinline__ bool colsum_add_lds(int32_t* keys, double* vals, int3
 }
 
 template <typename V, typename RP>
-__global__ __launch_bounds__(kNT) void k_prune_count(int64_t m, const void* __restrict__ rp,
-                                                     const int32_t* __restrict__ col,
-                                                     const V* __restrict__ val, V thr,
-                                                     int64_t* __restrict__ keep,
-                                                     double* __restrict__ colsum) {
+__global__ __launch_bounds__(kPruneNT) void k_prune_count(int64_t m, const void* __restrict__ rp,
+                                                          const int32_t* __restrict__ col,
+                                                          const V* __restrict__ val, V thr,
+                                                          int64_t* __restrict__ keep,
+                                                          double* __restrict__ colsum) {
   __shared__ int32_t keys[kPruneSlots];
   __shared__ double vals[kPruneSlots];
-  for (int i = threadIdx.x; i < kPruneSlots; i += kNT) {
+  for (int i = threadIdx.x; i < kPruneSlots; i += kPruneNT) {
     keys[i] = kEmptyKey;
     vals[i] = 0.0;
   }
   __syncthreads();
   const int64_t r0 = (int64_t)blockIdx.x * kPruneRows;
   const int w = threadIdx.x / kWave;
-  for (int64_t r = r0 + w; r < r0 + kPruneRows && r < m; r += kNT / kWave) {
+  for (int64_t r = r0 + w; r < r0 + kPruneRows && r < m; r += kPruneNT / kWave) {
     const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
     int64_t kept = 0;
-    for (int64_t base = a; base < b; base += kWave) {
-      const int64_t e = base + lane_id();
-      bool k = false;
-      if (e < b) {
-        const V x = val[e];
-        k = x >= thr;
-        if (k) {
-          const int32_t c = col[e];
-          if (!colsum_add_lds(keys, vals, c, (double)x)) unsafeAtomicAdd(&colsum[c], (double)x);
-        }
+    for (int64_t base = a; base < b; base += kWave * kPruneU) {
+      V x[kPruneU];
+      int32_t c[kPruneU];
+      bool act[kPruneU];
+#pragma unroll
+      for (int u = 0; u < kPruneU; ++u) {
+        const int64_t e = base + u * kWave + lane_id();
+        act[u] = e < b;
+        x[u] = act[u] ? val[e] : V(0);
+        c[u] = act[u] ? col[e] : 0;
       }
-      kept += __popcll(__ballot(k));
+#pragma unroll
+      for (int u = 0; u < kPruneU; ++u) {
+        const bool k = act[u] && x[u] >= thr;
+        if (k && !colsum_add_lds(keys, vals, c[u], (double)x[u]))
+          unsafeAtomicAdd(&colsum[c[u]], (double)x[u]);
+        kept += __popcll(__ballot(k));
+      }
     }
     if (lane_id() == 0) keep[r] = kept;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kPruneSlots; i += kNT) {
+  for (int i = threadIdx.x; i < kPruneSlots; i += kPruneNT) {
     const int32_t c = keys[i];
     if (c != kEmptyKey) unsafeAtomicAdd(&colsum[c], vals[i]);
   }
 }
 
-// One wave per row: order-preserving compaction of the kept entries.
+// One wave per row: order-preserving compaction of the kept entries.  As in
+// the count, a wave loads kPruneU runs of 64 entries, then gathers their
+// column sums, then writes.
 template <typename V, typename RP>
 __global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __restrict__ rp,
                                                     const int32_t* __restrict__ col,
@@ -100,23 +115,31 @@ __global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __res
   if (r >= m) return;
   const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
   int64_t w = outOff[r];
-  for (int64_t base = a; base < b; base += kWave) {
-    const int64_t e = base + lane_id();
-    bool k = false;
-    V x = V(0);
-    int32_t c = 0;
-    if (e < b) {
-      x = val[e];
-      c = col[e];
-      k = x >= thr;
+  for (int64_t base = a; base < b; base += kWave * kPruneU) {
+    V x[kPruneU];
+    int32_t c[kPruneU];
+    bool k[kPruneU];
+    double cs[kPruneU];
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) {
+      const int64_t e = base + u * kWave + lane_id();
+      const bool act = e < b;
+      x[u] = act ? val[e] : V(0);
+      c[u] = act ? col[e] : 0;
+      k[u] = act && x[u] >= thr;
     }
-    const uint64_t mk = __ballot(k);
-    if (k) {
-      const int64_t pos = w + __popcll(mk & lanemask_lt());
-      ocol[pos] = c;
-      oval[pos] = (V)((double)x / colsum[c]);
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) cs[u] = k[u] ? colsum[c[u]] : 1.0;
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) {
+      const uint64_t mk = __ballot(k[u]);
+      if (k[u]) {
+        const int64_t pos = w + __popcll(mk & lanemask_lt());
+        ocol[pos] = c[u];
+        oval[pos] = (V)((double)x[u] / cs[u]);
+      }
+      w += __popcll(mk);
     }
-    w += __popcll(mk);
   }
 }
 
@@ -143,11 +166,23 @@ __global__ __launch_bounds__(kNT) void k_mcl_count(int64_t m, const void* __rest
   if (r >= m) return;
   const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
   int64_t kept = 0;
-  for (int64_t base = a; base < b; base += kWave) {
-    const int64_t e = base + lane_id();
-    bool k = false;
-    if (e < b) k = mcl_normalised(val[e], colsum[col[e]]) >= thr;
-    kept += __popcll(__ballot(k));
+  for (int64_t base = a; base < b; base += kWave * kPruneU) {
+    V x[kPruneU];
+    int32_t c[kPruneU];
+    bool act[kPruneU];
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) {
+      const int64_t e = base + u * kWave + lane_id();
+      act[u] = e < b;
+      x[u] = act[u] ? val[e] : V(0);
+      c[u] = act[u] ? col[e] : 0;
+    }
+    double cs[kPruneU];
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) cs[u] = act[u] ? colsum[c[u]] : 0.0;
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u)
+      kept += __popcll(__ballot(act[u] && mcl_normalised(x[u], cs[u]) >= thr));
   }
   if (lane_id() == 0) keep[r] = kept;
 }
@@ -165,23 +200,32 @@ __global__ __launch_bounds__(kNT) void k_mcl_fill(int64_t m, const void* __restr
   if (r >= m) return;
   const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
   int64_t w = outOff[r];
-  for (int64_t base = a; base < b; base += kWave) {
-    const int64_t e = base + lane_id();
-    bool k = false;
-    V y = V(0);
-    int32_t c = 0;
-    if (e < b) {
-      c = col[e];
-      y = mcl_normalised(val[e], colsum[c]);
-      k = y >= thr;
+  for (int64_t base = a; base < b; base += kWave * kPruneU) {
+    V x[kPruneU];
+    int32_t c[kPruneU];
+    bool act[kPruneU];
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) {
+      const int64_t e = base + u * kWave + lane_id();
+      act[u] = e < b;
+      x[u] = act[u] ? val[e] : V(0);
+      c[u] = act[u] ? col[e] : 0;
     }
-    const uint64_t mk = __ballot(k);
-    if (k) {
-      const int64_t pos = w + __popcll(mk & lanemask_lt());
-      ocol[pos] = c;
-      oval[pos] = y * y;
+    double cs[kPruneU];
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) cs[u] = act[u] ? colsum[c[u]] : 0.0;
+#pragma unroll
+    for (int u = 0; u < kPruneU; ++u) {
+      const V y = act[u] ? mcl_normalised(x[u], cs[u]) : V(0);
+      const bool k = act[u] && y >= thr;
+      const uint64_t mk = __ballot(k);
+      if (k) {
+        const int64_t pos = w + __popcll(mk & lanemask_lt());
+        ocol[pos] = c[u];
+        oval[pos] = y * y;
+      }
+      w += __popcll(mk);
     }
-    w += __popcll(mk);
   }
 }
 
@@ -193,7 +237,7 @@ void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col,
                         bool f64, double thr, int64_t* keepCnt, double* colsum,
                         hipStream_t s) {
   if (m <= 0) return;
-  const dim3 g((unsigned)((m + kPruneRows - 1) / kPruneRows)), b(kNT);
+  const dim3 g((unsigned)((m + kPruneRows - 1) / kPruneRows)), b(kPruneNT);
   if (f64) {
     if (rp64)
       hipLaunchKernelGGL((k_prune_count<double, int64_t>), g, b, 0, s, m, rp, col,
