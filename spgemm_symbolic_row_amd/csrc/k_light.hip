@@ -20,14 +20,19 @@ constexpr int kMaxSpt = 24;  // slots per thread held in registers by the compac
 // flattened product index q of entry e starts at scanA[e] (row-local
 // exclusive offset).  The wave keeps 64 consecutive A entries in registers,
 // finds for each of 64 consecutive products the entry that owns it with a
-// 6-step binary search across lanes, and hands f(act, b, a, q) the index b of
-// the B element, the A value and the product index q.  Every lane runs the
-// same iterations.
+// 6-step binary search across lanes, and loads the B element's column (and
+// value).  kStreamU runs of 64 products are located and their loads issued
+// before any is used, so a wave waits on one memory round trip per 256
+// products, not per 64.  f(act, col, a, b, q) gets the column, the A value,
+// the B value and the product index q.  Every lane runs the same iterations.
+constexpr int kStreamU = 4;
 template <bool VAL, typename V, typename F>
 __device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
                                            const int32_t* __restrict__ acol,
                                            const V* __restrict__ aval,
-                                           const int32_t* __restrict__ brp, int64_t rs,
+                                           const int32_t* __restrict__ brp,
+                                           const int32_t* __restrict__ bcol,
+                                           const V* __restrict__ bval, int64_t rs,
                                            int64_t re, int32_t P, int32_t p0, int32_t p1,
                                            F&& f) {
   if (p0 >= p1) return;
@@ -45,20 +50,37 @@ __device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
     }
     int32_t bend = (j + kWave < re) ? scanA[j + kWave] : P;
     if (bend > p1) bend = p1;
-    for (; p < bend; p += kWave) {
-      const int32_t q = p + lane_id();
-      const bool act = q < bend;
-      int s = 0;
+    for (; p < bend; p += kWave * kStreamU) {
+      bool act[kStreamU];
+      int32_t cc[kStreamU], qq[kStreamU];
+      V sa[kStreamU], bv[kStreamU];
 #pragma unroll
-      for (int step = 32; step >= 1; step >>= 1) {
-        const int32_t o = __shfl(off, s + step);
-        if (o <= q) s += step;
+      for (int u = 0; u < kStreamU; ++u) {
+        const int32_t q = p + u * kWave + lane_id();
+        act[u] = q < bend;
+        qq[u] = q;
+        cc[u] = 0;
+        sa[u] = V(0);
+        bv[u] = V(0);
+        if (p + u * kWave < bend) {  // the same for every lane
+          int s = 0;
+#pragma unroll
+          for (int step = 32; step >= 1; step >>= 1) {
+            const int32_t o = __shfl(off, s + step);
+            if (o <= q) s += step;
+          }
+          const int32_t so = __shfl(off, s);
+          const int32_t sb = __shfl(bs, s);
+          if (VAL) sa[u] = __shfl(a, s);
+          if (act[u]) {
+            const int32_t bi = sb + (q - so);
+            cc[u] = bcol[bi];
+            if (VAL) bv[u] = bval[bi];
+          }
+        }
       }
-      const int32_t so = __shfl(off, s);
-      const int32_t sb = __shfl(bs, s);
-      V sa = V(0);
-      if (VAL) sa = __shfl(a, s);
-      f(act, sb + (q - so), sa, q);
+#pragma unroll
+      for (int u = 0; u < kStreamU; ++u) f(act[u], cc[u], sa[u], bv[u], qq[u]);
     }
     p = bend;
     j += kWave;
@@ -90,10 +112,10 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows(const int32_t* __restrict
     const int w = t / kWave;
     const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
     const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
-    const int32_t* __restrict__ bcol = a.bcol;
-    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, rs, re, P, p0, p1,
-                             [&](bool act, int32_t b, float, int32_t) {
-                               if (act && hset_insert(keys, (uint32_t)T, bcol[b], err)) ++mine;
+    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, a.bcol,
+                             (const float*)nullptr, rs, re, P, p0, p1,
+                             [&](bool act, int32_t c, float, float, int32_t) {
+                               if (act && hset_insert(keys, (uint32_t)T, c, err)) ++mine;
                              });
   }
   const int32_t ws = wave_sum(mine);
@@ -168,11 +190,11 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows_win(const int32_t* __rest
     const int32_t P = (int32_t)a.rowP[row];
     const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
     const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
-    const int32_t* __restrict__ bcol = a.bcol;
-    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, rs, re, P, p0, p1,
-                             [&](bool act, int32_t b, float, int32_t) {
+    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, a.bcol,
+                             (const float*)nullptr, rs, re, P, p0, p1,
+                             [&](bool act, int32_t col, float, float, int32_t) {
                                if (act) {
-                                 const int32_t c = bcol[b] - lo;
+                                 const int32_t c = col - lo;
                                  const uint32_t bit = 1u << (c & 31);
                                  if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
                                }
@@ -238,14 +260,12 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows_win(const int32_t* __rest
     const int64_t rs = a.arp[row], re = a.arp[row + 1];
     const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
     const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
-    const int32_t* __restrict__ bcol = a.bcol;
-    const V* __restrict__ bval = (const V*)a.bval;
-    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, rs, re, P, p0, p1,
-                        [&](bool act, int32_t b, V av, int32_t q) {
+    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, a.bcol, (const V*)a.bval, rs,
+                        re, P, p0, p1, [&](bool act, int32_t col, V av, V bv, int32_t q) {
                           if (act) {
-                            const int32_t c = bcol[b] - lo;
+                            const int32_t c = col - lo;
                             pc[q] = (uint16_t)c;
-                            pv[q] = av * bval[b];
+                            pv[q] = av * bv;
                             const uint32_t bit = 1u << (c & 31);
                             if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
                           }
@@ -657,12 +677,10 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
     const int w = t / kWave;
     const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
     const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
-    const int32_t* __restrict__ bcol = a.bcol;
-    const V* __restrict__ bval = (const V*)a.bval;
-    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, rs, re, P, p0, p1,
-                        [&](bool act, int32_t b, V av, int32_t) {
+    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, a.bcol, (const V*)a.bval, rs,
+                        re, P, p0, p1, [&](bool act, int32_t c, V av, V bv, int32_t) {
                           if (act && !(cntOut && full[g]))
-                            hmap_add(keys, vals, (uint32_t)T, bcol[b], av * bval[b], herr);
+                            hmap_add(keys, vals, (uint32_t)T, c, av * bv, herr);
                         });
   }
   __syncthreads();
