@@ -209,6 +209,18 @@ def test_rmat14_default_parameters():
     assert st["params"]["tau"] == 6826
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_default_width_dense_chunks(dtype):
+    # The default chunk width (16384 for fp64, 32768 for fp32) with chunks
+    # above a lowered tau, so the dense chunk kernels run at full width:
+    # fp64 marks columns with bytes, fp32 with bits (bytes would not fit
+    # beside the 128 KiB accumulator).
+    A = synth.rmat(15, 16, seed=12, dtype=dtype)
+    st = check_full(A, A, heavy_threshold=512)
+    assert st["heavy_rows"] > 0
+    assert st["params"]["dense_width"] == (16384 if dtype == np.float64 else 32768)
+
+
 def test_options_do_not_change_the_result():
     A = synth.rmat(11, 16, seed=3)
     A.val = np.round(A.val * 4 - 2)
