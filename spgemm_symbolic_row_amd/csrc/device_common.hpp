@@ -94,13 +94,11 @@ __device__ __forceinline__ bool hset_insert(int32_t* keys, uint32_t T, int32_t k
                                             int32_t* err) {
   uint32_t s = hash_slot(key, T);
   for (uint32_t probe = 0; probe < T; ++probe) {
-    const int32_t cur = lds_load_relaxed(&keys[s]);
-    if (cur == key) return false;
-    if (cur == kEmptyKey) {
-      const int32_t old = atomicCAS(&keys[s], kEmptyKey, key);
-      if (old == kEmptyKey) return true;
-      if (old == key) return false;
-    }
+    // One compare-and-swap per probe: it claims an empty slot and reports
+    // the key already held by a taken one.
+    const int32_t old = atomicCAS(&keys[s], kEmptyKey, key);
+    if (old == kEmptyKey) return true;
+    if (old == key) return false;
     s = (s + 1 == T) ? 0 : s + 1;
   }
   flag_error(err, kErrHashFull);
@@ -114,17 +112,10 @@ __device__ __forceinline__ void hmap_add(int32_t* keys, V* vals, uint32_t T, int
                                          V v, int32_t* err) {
   uint32_t s = hash_slot(key, T);
   for (uint32_t probe = 0; probe < T; ++probe) {
-    const int32_t cur = lds_load_relaxed(&keys[s]);
-    if (cur == key) {
+    const int32_t old = atomicCAS(&keys[s], kEmptyKey, key);
+    if (old == kEmptyKey || old == key) {
       atomicAdd(&vals[s], v);
       return;
-    }
-    if (cur == kEmptyKey) {
-      const int32_t old = atomicCAS(&keys[s], kEmptyKey, key);
-      if (old == kEmptyKey || old == key) {
-        atomicAdd(&vals[s], v);
-        return;
-      }
     }
     s = (s + 1 == T) ? 0 : s + 1;
   }
