@@ -257,7 +257,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build is a single-GPU SpGEMM; run with --gpus 1",
+        print("bench.py measures one GPU only: the library is a single-GPU SpGEMM; run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
