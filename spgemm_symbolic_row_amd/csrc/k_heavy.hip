@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kNT) void k_dense_sym(const ChunkDesc* __restrict__
 // current one, and clears only the slots the current chunk touched (the
 // whole accumulator is cleared once, at the start).
 constexpr int kDenseNT = 1024;
-constexpr int kDenseB = 8;  // elements per thread per batch
+constexpr int kDenseB = 4;  // elements per thread per batch
 template <typename V, typename C>
 __device__ __forceinline__ void dense_load_batch(const C* __restrict__ col,
                                                  const V* __restrict__ val, int64_t e0, int64_t end,
