@@ -1,7 +1,7 @@
 """Throughput of C = A*A on one MI355X, with the roofline of the dominant
 kernel and the CPU oracle timed beside it.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config rmat18]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config rmat20]
 
 A step is one whole product: plan + symbolic + allocation of C + numeric
 (+ prune/renormalise for the Markov-clustering workload), inputs resident in
@@ -48,25 +48,23 @@ def log(*a):
 
 def algorithmic_bytes(st, phase, sv, si=4):
     """Algorithmic bytes one step moves in the given phase, and the per-unit
-    figure it is built from.  With several heavy-row batches, symbolic
-    expands columns only and numeric expands every batch again with values,
-    so the expansion phases run twice per step."""
-    fused = st["phase_windows"]["expand_split"] > 0
-    E = sum(st["level_elems"][1:] if fused else st["level_elems"])
-    batched = st["batches"] > 1
-    if phase in ("expand_final", "num_chunk_dense"):
-        si = st["chunk_col_bytes"] or si   # chunk-local 16-bit columns
-    cv = (si + (si + sv)) if batched else (si + sv)   # bytes per element over both expansions
+    figure they are built from.  The units are the effective-byte model's:
+    s_i + s_v per heavy product written by an expansion (a 4-byte column and
+    the value, whatever width the build stores), s_i + s_v per element read by
+    a chunk accumulator.  Only expansions that write values count; a
+    columns-only pass is extra work of the build's batched schedule."""
+    E = sum(st["level_elems"])
     if phase == "expand_split":
-        return st["level_elems"][0] * cv, f"{cv} B written per heavy product (first-level chunks)"
+        return st["level_elems"][0] * (si + sv), f"{si + sv} B written per heavy product (first-level chunks)"
     if phase == "outer_product":
-        return st["heavy_products"] * cv, f"{cv} B written per heavy product"
+        return st["heavy_products"] * (si + sv), f"{si + sv} B written per heavy product"
     if phase == "expand_final":
-        return st["heavy_products"] * cv, f"{cv} B written per heavy product (final chunks)"
+        return (st["heavy_products"] * (si + sv),
+                f"{si + sv} B (4 B column + {sv} B value) written per heavy product (final chunks)")
     if phase == "multisplit":
-        return E * 2 * cv, f"{2 * cv} B (read + write) per element per level"
+        return E * 2 * (si + sv), f"{2 * (si + sv)} B (read + write) per element per level"
     if phase == "histogram":
-        return E * si * (2 if batched else 1), f"{si} B read per element per level"
+        return E * si, f"{si} B read per element per level"
     if phase == "num_chunk_dense":
         return st["lds_dense_products"] * (si + sv), f"{si + sv} B read per dense-chunk element"
     if phase == "num_light":
@@ -75,23 +73,109 @@ def algorithmic_bytes(st, phase, sv, si=4):
     return None, None
 
 
-def effective_bytes(A, st, sv, si=4, B=None, transposed=False):
-    """Frozen effective-byte denominator: compulsory traffic plus the heavy
-    intermediate that the method materialises (expand once, with values).
-    B defaults to A; with `transposed`, B = A^T is formed inside the step
-    (read A once, write A^T once)."""
-    m, nnzA, nnzC = A.m, A.nnz, st["nnz_c"]
-    rp = 4
+S_LM = 160 * 1024   # LDS per work group on gfx950 (the default s_LM)
+
+
+def frozen_heavy(A, B, sv):
+    """Heavy products P_h and the elements entering each multisplit level
+    E_l at the default parameters (a row is heavy iff P_i > tau; a chunk
+    recurses iff it holds more than tau elements), computed on the host from
+    the structure of A and B alone, so that no option of the run can move
+    the effective-byte denominator.  Counts per (row, chunk) are the rows of
+    A's pattern times per-row chunk histograms of B."""
+    import numpy as np
+    import scipy.sparse as ssp
+
+    import spgemm_symbolic_row_amd as sg
+
+    prm = sg.compute_params(B.n, S_LM, sv)
+    tau = prm["tau"]
+    arp = A.row_ptr.astype(np.int64)
+    lenB = np.diff(B.row_ptr.astype(np.int64))
+    rowA = np.repeat(np.arange(A.m), np.diff(arp))
+    P = np.bincount(rowA, weights=lenB[A.col].astype(np.float64), minlength=A.m)
+    P = np.rint(P).astype(np.int64)
+    heavy = np.nonzero(P > tau)[0]
+    Ph = int(P[heavy].sum())
+    E = []
+    if prm["levels"] > 0 and heavy.size:
+        E.append(Ph)
+        lens = arp[heavy + 1] - arp[heavy]
+        hrp = np.zeros(heavy.size + 1, np.int64)
+        np.cumsum(lens, out=hrp[1:])
+        idx = np.repeat(arp[heavy] - hrp[:-1], lens) + np.arange(int(hrp[-1]))
+        Ah = ssp.csr_matrix((np.ones(idx.size, np.int64), A.col[idx], hrp),
+                            shape=(heavy.size, B.m))
+        rowB = np.repeat(np.arange(B.m), lenB)
+        for w in prm["level_width"][:-1]:
+            nch = (B.n + w - 1) // w
+            H = ssp.csr_matrix((np.ones(B.nnz, np.int64), (rowB, B.col // w)),
+                               shape=(B.m, nch))
+            cnt = (Ah @ H).data
+            E.append(int(cnt[cnt > tau].sum()))
+    return {"tau": tau, "heavy_rows": int(heavy.size), "heavy_products": Ph,
+            "level_elems": E, "v_chunks": prm["v_chunks"]}
+
+
+def effective_bytes(A, fz, nnzC, sv, si=4, B=None, transposed=False, rp64=False,
+                    prune_nnz=None):
+    """Effective-byte denominator of one step: compulsory traffic (symbolic
+    reads the structure of A and B and writes C.row_ptr; numeric reads A, B
+    and C.row_ptr and writes C.col and C.val) plus what the method
+    materialises when it expands once, with values: P_h (s_i + s_v) for the
+    expansion, sum_l E_l (3 s_i + 2 s_v) for the histogram read and the
+    multisplit read and write of every level, P_h (2 s_i + s_v) for the
+    chunk symbolic read and the numeric read.  P_h and E_l come frozen from
+    frozen_heavy().  B defaults to A; with `transposed`, B = A^T is formed
+    inside the step (A read once, A^T written once).  prune_nnz: the Markov
+    clustering step's kept entries; its prune reads C, writes the kept
+    entries, reads them again and writes their renormalised values."""
+    m, nnzA = A.m, A.nnz
+    rp, rpc = 4, (8 if rp64 else 4)
     kB, nnzB = (A.n, A.nnz) if transposed else ((A.m, A.nnz) if B is None else (B.m, B.nnz))
-    sym = (m + 1) * rp + nnzA * si + (kB + 1) * rp + nnzB * si + (m + 1) * rp
-    num = ((m + 1) * rp + nnzA * (si + sv) + (kB + 1) * rp + nnzB * (si + sv) + (m + 1) * rp
+    sym = (m + 1) * rp + nnzA * si + (kB + 1) * rp + nnzB * si + (m + 1) * rpc
+    num = ((m + 1) * rp + nnzA * (si + sv) + (kB + 1) * rp + nnzB * (si + sv) + (m + 1) * rpc
            + nnzC * (si + sv))
     if transposed:
         num += (m + 1) * rp + (A.n + 1) * rp + 2 * nnzA * (si + sv)
-    Ph = st["heavy_products"]
-    E = sum(st["level_elems"])
+    Ph, E = fz["heavy_products"], sum(fz["level_elems"])
     heavy = Ph * (si + sv) + E * (3 * si + 2 * sv) + Ph * (2 * si + sv)
-    return sym + num + heavy
+    prune = 0
+    if prune_nnz is not None:
+        prune = ((m + 1) * rpc + nnzC * (si + sv) + (m + 1) * 4 + prune_nnz * (si + sv)
+                 + prune_nnz * (si + sv) + prune_nnz * sv)
+    return sym + num + heavy + prune
+
+
+def copy_bandwidth(gib=4.0, reps=5):
+    """Device-to-device copy rate on this GPU (bytes read + written per
+    second, GB/s), the measured ceiling beside the nominal HBM peak."""
+    import torch
+    n = int(gib * 2 ** 30) // 8
+    src = torch.ones(n, dtype=torch.float64, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * n * 8 / (ms / 1e3) / 1e9, 1)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def traffic_for(kernel, workload):
@@ -166,7 +250,7 @@ def run_mcl_iter(args, A, opts):
             B = synth_csr(rp, col, val.astype(np.float32), A.m, A.n)
         t = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(2 * Pc / t / 1e9, 4), "unit": "GFLOP/s",
-                                "cores": threads, "kind": "oracle",
+                                "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                                 "sample": f"the whole {MCL_ITERS}-iteration run once, {t:.2f} s"}
         log(f"cpu baseline: {line['cpu_baseline']}")
     print(json.dumps(line), flush=True)
@@ -224,7 +308,8 @@ def cpu_baseline(A, target_s=15.0, B=None, note=""):
         P = P_all * runs
         sample = f"the whole product (all {A.m} rows, {P_all} products) run {runs} times, {t:.2f} s"
     return {"value": round(2 * P / t / 1e9, 4), "unit": "GFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": sample + note}
+            "kind": "oracle", "sample": sample + note, "cpu_model": cpu_model(),
+            "host_threads": os.cpu_count()}
 
 
 def main():
@@ -232,8 +317,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="rmat18", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="rmat20", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-rate", action="store_true",
+                    help="skip the device-copy bandwidth measurement")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not time kernel phases with HIP events")
     ap.add_argument("--single-stream", action="store_true",
@@ -323,6 +410,8 @@ def main():
             if mcl:
                 out = sg.prune_colnorm(rp, col, val, A.m, A.n, 1e-4)
             st = p.stats()
+        if mcl:
+            st["pruned_nnz"] = int(out[1].numel())
         return out, st
 
     for _ in range(args.warmup):
@@ -340,7 +429,18 @@ def main():
     P = st["products"]
     value = 2.0 * P * K / dt / 1e9
     ms = dt / K * 1e3
-    eff = effective_bytes(A, st, sv, B=B, transposed=transposed)
+    t = time.time()
+    if transposed:
+        import scipy.sparse as ssp
+        T = ssp.csr_matrix((A.val, A.col, A.row_ptr), shape=(A.m, A.n)).T.tocsr()
+        T.sort_indices()
+        Bh = synth.CSR(T.indptr.astype(np.int32), T.indices.astype(np.int32), T.data, A.n, A.m)
+    else:
+        Bh = B if B is not None else A
+    fz = frozen_heavy(A, Bh, sv)
+    log(f"frozen heavy figures at the default parameters: {fz} ({time.time() - t:.1f} s)")
+    eff = effective_bytes(A, fz, st["nnz_c"], sv, B=B, transposed=transposed,
+                          rp64=bool(opts.get("rowptr64")), prune_nnz=st.get("pruned_nnz"))
     log(f"{ms:.3f} ms/step, {value:.2f} GFLOP/s, effective {eff / (dt / K) / 1e9:.1f} GB/s")
     for k, v in sorted(phase_tot.items(), key=lambda kv: -kv[1]):
         if v > 0:
@@ -365,6 +465,10 @@ def main():
                     "traffic": traffic_for(kern, args.config), "kernel": kern,
                     "avg_launch_ms": round(avg_ms, 4), "bytes_per_launch": int(byt),
                     "per_unit": unit_desc}
+            if not args.no_copy_rate:
+                roof["copy_gbps"] = copy_bandwidth()
+                roof["frac_of_copy"] = round(achieved / roof["copy_gbps"], 4)
+                log(f"device copy {roof['copy_gbps']} GB/s (read + write)")
 
     line = {
         "metric": "SpGEMM GFLOP/s (2x intermediate products) + % HBM roofline, 1 MI355X",
@@ -376,11 +480,12 @@ def main():
                    "products": P, "nnz_c": st["nnz_c"], "heavy_rows": st["heavy_rows"],
                    "heavy_products": st["heavy_products"],
                    "v_chunks": st["params"]["v_chunks"], "tau": st["params"]["tau"],
+                   "batches": st["batches"],
+                   "frozen_heavy_products": fz["heavy_products"],
+                   "frozen_level_elems": fz["level_elems"],
                    "effective_bytes": int(eff),
                    "effective_gbps": round(eff / (dt / K) / 1e9, 1),
                    "effective_frac": round(eff / (dt / K) / 1e9 / HBM_PEAK_GBPS, 4),
-                   "lds_accumulated_frac": round((st["lds_hash_products"] + st["lds_dense_products"])
-                                                 / max(P, 1), 6),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": None,

@@ -181,8 +181,11 @@ typedef enum spgemm_phase {
   SPGEMM_PH_NUM_CHUNK_DENSE = 11,/* heavy-chunk dense LDS numeric               */
   SPGEMM_PH_CHUNK_HIST = 12,     /* per-row W-wide chunk counts from structure  */
   SPGEMM_PH_EXPAND_SPLIT = 13,   /* first multisplit level fed from A and B     */
-  SPGEMM_PH_EXPAND_FINAL = 14,   /* products made and written to final chunks   */
-  SPGEMM_PH_COUNT = 15
+  SPGEMM_PH_EXPAND_FINAL = 14,   /* products made with values and written to
+                                    their final chunks                          */
+  SPGEMM_PH_SYM_HEAVY = 15,      /* heavy-row symbolic of the batched schedule,
+                                    where values are not expanded in symbolic   */
+  SPGEMM_PH_COUNT = 16
 } spgemm_phase;
 
 typedef struct spgemm_stats {

@@ -50,6 +50,10 @@ def _load():
         lib.oracle_numeric.restype = ctypes.c_int
         lib.oracle_numeric.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                        vp, vp, vp, vp, vp, ctypes.c_int]
+        lib.oracle_check_rows.restype = i64
+        lib.oracle_check_rows.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                          vp, i64, vp, vp, ctypes.c_int, ctypes.c_double,
+                                          ctypes.c_int, vp, vp, ctypes.c_int]
         lib.oracle_prune_colnorm.restype = i64
         lib.oracle_prune_colnorm.argtypes = [i64, i64, vp, vp, vp, ctypes.c_float, vp,
                                              vp, vp, vp]
@@ -148,6 +152,54 @@ def spgemm(A, B, r0: int = 0, r1: int | None = None, nthreads: int = 0,
     if rc != 0:
         raise RuntimeError("oracle_numeric failed (%d)" % rc)
     return OracleResult(crp, col, val, mag, terms, r0, r1)
+
+
+@dataclass
+class CheckReport:
+    bad_rows: int        # rows whose length or columns differ
+    first_bad_row: int   # -1 when none
+    bad_values: int      # entries outside the tolerance
+    first_bad_value: int # offset in C of the first, -1 when none
+    entries: int         # entries compared
+    max_terms: int       # most products summed into one entry
+    max_rel: float       # largest |g - c| / |c| over entries with c != 0
+
+    @property
+    def ok(self) -> bool:
+        return self.bad_rows == 0 and self.bad_values == 0
+
+
+def check_rows(A, B, r0: int, r1: int, g_rp, g_col, g_val, rtol: float, exact: bool = False,
+               g_base: int | None = None, nthreads: int = 0) -> CheckReport:
+    """Compare rows [r0, r1) of another implementation's C = A*B with the
+    oracle, row by row, without forming the oracle's C.  g_rp: the r1-r0+1
+    row offsets of those rows (absolute); g_col, g_val: their entries, the
+    first at absolute offset g_base (default g_rp[0]).  A row must match in
+    length and columns exactly; a value c' must satisfy |c' - c| <= rtol *
+    sum of |terms| (exact: c' == c), c being the compensated oracle value."""
+    lib = _load()
+    assert A.n == B.m
+    f32 = A.val.dtype == np.float32
+    vdt = np.float32 if f32 else np.float64
+    arp, acol, aval = _c(A.row_ptr, np.int32), _c(A.col, np.int32), _c(A.val, vdt)
+    brp, bcol, bval = _c(B.row_ptr, np.int32), _c(B.col, np.int32), _c(B.val, vdt)
+    grp = _c(g_rp, np.int64)
+    assert grp.shape[0] == r1 - r0 + 1
+    gcol = _c(g_col, np.int32)
+    gf32 = np.asarray(g_val).dtype == np.float32
+    gval = _c(g_val, np.float32 if gf32 else np.float64)
+    base = int(grp[0]) if g_base is None else int(g_base)
+    assert gcol.shape[0] >= int(grp[-1]) - base and gval.shape[0] == gcol.shape[0]
+    rep = np.zeros(8, dtype=np.int64)
+    mr = np.zeros(1, dtype=np.float64)
+    rc = lib.oracle_check_rows(r0, r1, B.n, _p(arp), _p(acol), _p(aval), _p(brp), _p(bcol),
+                               _p(bval), 1 if f32 else 0, _p(grp), base, _p(gcol), _p(gval),
+                               1 if gf32 else 0, float(rtol), 1 if exact else 0, _p(rep),
+                               _p(mr), nthreads)
+    if rc < 0:
+        raise MemoryError("oracle_check_rows failed")
+    return CheckReport(int(rep[0]), int(rep[1]), int(rep[2]), int(rep[3]), int(rep[4]),
+                       int(rep[5]), float(mr[0]))
 
 
 def prune_colnorm(m: int, n: int, row_ptr, col, val, threshold: float = 1e-4,

@@ -81,6 +81,82 @@ static int cmp_i32(const void *x, const void *y) {
   return (a > b) - (a < b);
 }
 
+/* Per-thread scratch of the row accumulation: a dense accumulator over all
+ * columns, its Neumaier compensation, the sum of |terms|, the number of
+ * terms, a row stamp and the list of touched columns. */
+typedef struct {
+  double *acc, *cmp, *mag;
+  int32_t *terms;
+  int64_t *mark;
+  int32_t *touched;
+} row_scratch;
+
+static int scratch_init(row_scratch *w, int64_t n) {
+  size_t nn = (size_t)(n > 0 ? n : 1);
+  w->acc = (double *)malloc(sizeof(double) * nn);
+  w->cmp = (double *)malloc(sizeof(double) * nn);
+  w->mag = (double *)malloc(sizeof(double) * nn);
+  w->terms = (int32_t *)malloc(sizeof(int32_t) * nn);
+  w->mark = (int64_t *)malloc(sizeof(int64_t) * nn);
+  w->touched = (int32_t *)malloc(sizeof(int32_t) * nn);
+  if (!(w->acc && w->cmp && w->mag && w->terms && w->mark && w->touched)) return 0;
+  for (int64_t c = 0; c < n; ++c) w->mark[c] = -1;
+  return 1;
+}
+
+static void scratch_free(row_scratch *w) {
+  free(w->acc);
+  free(w->cmp);
+  free(w->mag);
+  free(w->terms);
+  free(w->mark);
+  free(w->touched);
+}
+
+/* Row i of C = A*B into the scratch: every product A[i,k]*B[k,j] in the
+ * stored order of A[i,:] and then of B[k,:], added into column j; the
+ * touched columns are sorted at the end (SortAndWrite).  The value of
+ * column touched[e] is acc + cmp.  Returns the number of columns. */
+static int64_t accumulate_row(int64_t i, const int32_t *a_rp, const int32_t *a_col,
+                              const void *a_val, const int32_t *b_rp,
+                              const int32_t *b_col, const void *b_val, int val_is_f32,
+                              row_scratch *w) {
+  const double *ad = (const double *)a_val, *bd = (const double *)b_val;
+  const float *af = (const float *)a_val, *bf = (const float *)b_val;
+  double *acc = w->acc, *cmp = w->cmp, *mag = w->mag;
+  int32_t *terms = w->terms, *touched = w->touched;
+  int64_t *mark = w->mark;
+  int64_t nt = 0;
+  for (int64_t j = a_rp[i]; j < a_rp[i + 1]; ++j) {
+    int32_t k = a_col[j];
+    double a = val_is_f32 ? (double)af[j] : ad[j];
+    for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) {
+      int32_t c = b_col[b];
+      double p = a * (val_is_f32 ? (double)bf[b] : bd[b]);
+      if (mark[c] != i) {
+        mark[c] = i;
+        acc[c] = 0.0;
+        cmp[c] = 0.0;
+        mag[c] = 0.0;
+        terms[c] = 0;
+        touched[nt++] = c;
+      }
+      /* Neumaier's compensated addition of p into (acc, cmp). */
+      double s = acc[c];
+      double t = s + p;
+      if (fabs(s) >= fabs(p))
+        cmp[c] += (s - t) + p;
+      else
+        cmp[c] += (p - t) + s;
+      acc[c] = t;
+      mag[c] += fabs(p);
+      terms[c] += 1;
+    }
+  }
+  qsort(touched, (size_t)nt, sizeof(int32_t), cmp_i32);
+  return nt;
+}
+
 int oracle_numeric(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
                    const int32_t *a_col, const void *a_val, const int32_t *b_rp,
                    const int32_t *b_col, const void *b_val, int val_is_f32,
@@ -88,79 +164,112 @@ int oracle_numeric(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
                    double *c_mag, int32_t *c_terms, int nthreads) {
   int status = 0;
   if (nthreads <= 0) nthreads = omp_get_max_threads();
-  const double *ad = (const double *)a_val, *bd = (const double *)b_val;
-  const float *af = (const float *)a_val, *bf = (const float *)b_val;
 #pragma omp parallel num_threads(nthreads)
   {
-    size_t nn = (size_t)(n > 0 ? n : 1);
-    double *acc = (double *)malloc(sizeof(double) * nn);  /* running sum    */
-    double *cmp = (double *)malloc(sizeof(double) * nn);  /* compensation   */
-    double *mag = (double *)malloc(sizeof(double) * nn);  /* sum of |terms| */
-    int32_t *terms = (int32_t *)malloc(sizeof(int32_t) * nn);
-    int64_t *mark = (int64_t *)malloc(sizeof(int64_t) * nn);
-    int32_t *touched = (int32_t *)malloc(sizeof(int32_t) * nn);
-    int ok = acc && cmp && mag && terms && mark && touched;
+    row_scratch w;
+    int ok = scratch_init(&w, n);
     if (!ok) {
 #pragma omp critical
       status = -1;
-    } else {
-      for (int64_t c = 0; c < n; ++c) mark[c] = -1;
     }
 #pragma omp for schedule(dynamic, 64)
     for (int64_t i = r0; i < r1; ++i) {
       if (!ok) continue;
       {
-        int64_t nt = 0;
-        for (int64_t j = a_rp[i]; j < a_rp[i + 1]; ++j) {
-          int32_t k = a_col[j];
-          double a = val_is_f32 ? (double)af[j] : ad[j];
-          for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) {
-            int32_t c = b_col[b];
-            double p = a * (val_is_f32 ? (double)bf[b] : bd[b]);
-            if (mark[c] != i) {
-              mark[c] = i;
-              acc[c] = 0.0;
-              cmp[c] = 0.0;
-              mag[c] = 0.0;
-              terms[c] = 0;
-              touched[nt++] = c;
-            }
-            /* Neumaier's compensated addition of p into (acc, cmp). */
-            double s = acc[c];
-            double t = s + p;
-            if (fabs(s) >= fabs(p))
-              cmp[c] += (s - t) + p;
-            else
-              cmp[c] += (p - t) + s;
-            acc[c] = t;
-            mag[c] += fabs(p);
-            terms[c] += 1;
-          }
-        }
+        const int64_t nt = accumulate_row(i, a_rp, a_col, a_val, b_rp, b_col, b_val,
+                                          val_is_f32, &w);
         int64_t base = c_rp[i - r0];
         if (c_rp[i - r0 + 1] - base != nt) {
 #pragma omp critical
           status = -2;
           continue;
         }
-        qsort(touched, (size_t)nt, sizeof(int32_t), cmp_i32);
         for (int64_t e = 0; e < nt; ++e) {
-          int32_t c = touched[e];
+          int32_t c = w.touched[e];
           c_col[base + e] = c;
-          c_val[base + e] = acc[c] + cmp[c];
-          if (c_mag) c_mag[base + e] = mag[c];
-          if (c_terms) c_terms[base + e] = terms[c];
+          c_val[base + e] = w.acc[c] + w.cmp[c];
+          if (c_mag) c_mag[base + e] = w.mag[c];
+          if (c_terms) c_terms[base + e] = w.terms[c];
         }
       }
     }
-    free(acc);
-    free(cmp);
-    free(mag);
-    free(terms);
-    free(mark);
-    free(touched);
+    scratch_free(&w);
   }
   return status;
+}
+
+int64_t oracle_check_rows(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
+                          const int32_t *a_col, const void *a_val, const int32_t *b_rp,
+                          const int32_t *b_col, const void *b_val, int val_is_f32,
+                          const int64_t *g_rp, int64_t g_base, const int32_t *g_col,
+                          const void *g_val, int g_val_is_f32, double rtol, int exact,
+                          int64_t *report, double *max_rel, int nthreads) {
+  int64_t bad_rows = 0, bad_vals = 0, first_row = -1, first_val = -1, entries = 0;
+  int64_t max_terms = 0;
+  double worst = 0.0;
+  int failed = 0;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const double *gd = (const double *)g_val;
+  const float *gf = (const float *)g_val;
+#pragma omp parallel num_threads(nthreads)
+  {
+    row_scratch w;
+    int ok = scratch_init(&w, n);
+    int64_t br = 0, bv = 0, fr = -1, fv = -1, ne = 0, mt = 0;
+    double wr = 0.0;
+    if (!ok) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t i = r0; i < r1; ++i) {
+      if (!ok) continue;
+      const int64_t nt = accumulate_row(i, a_rp, a_col, a_val, b_rp, b_col, b_val,
+                                        val_is_f32, &w);
+      const int64_t g0 = g_rp[i - r0] - g_base, g1 = g_rp[i - r0 + 1] - g_base;
+      int row_ok = (g1 - g0 == nt);
+      for (int64_t e = 0; row_ok && e < nt; ++e) row_ok = (g_col[g0 + e] == w.touched[e]);
+      if (!row_ok) {
+        ++br;
+        if (fr < 0 || i < fr) fr = i;
+        continue;
+      }
+      ne += nt;
+      for (int64_t e = 0; e < nt; ++e) {
+        const int32_t c = w.touched[e];
+        const double ref = w.acc[c] + w.cmp[c];
+        const double g = g_val_is_f32 ? (double)gf[g0 + e] : gd[g0 + e];
+        const double d = fabs(g - ref);
+        const int good = exact ? (g == ref) : (d <= rtol * w.mag[c]);
+        if (w.terms[c] > mt) mt = w.terms[c];
+        if (ref != 0.0 && d / fabs(ref) > wr) wr = d / fabs(ref);
+        if (!good) {
+          ++bv;
+          if (fv < 0 || g_rp[i - r0] + e < fv) fv = g_rp[i - r0] + e;
+        }
+      }
+    }
+#pragma omp critical
+    {
+      bad_rows += br;
+      bad_vals += bv;
+      entries += ne;
+      if (fr >= 0 && (first_row < 0 || fr < first_row)) first_row = fr;
+      if (fv >= 0 && (first_val < 0 || fv < first_val)) first_val = fv;
+      if (mt > max_terms) max_terms = mt;
+      if (wr > worst) worst = wr;
+    }
+    scratch_free(&w);
+  }
+  if (failed) return -1;
+  report[0] = bad_rows;
+  report[1] = first_row;
+  report[2] = bad_vals;
+  report[3] = first_val;
+  report[4] = entries;
+  report[5] = max_terms;
+  if (max_rel) *max_rel = worst;
+  return bad_rows + bad_vals;
 }
 
 int64_t oracle_prune_colnorm(int64_t m, int64_t n, const int64_t *c_rp,

@@ -53,6 +53,25 @@ int oracle_numeric(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
                    const int64_t *c_rp, int32_t *c_col, double *c_val,
                    double *c_mag, int32_t *c_terms, int nthreads);
 
+/* Row-by-row comparison of another implementation's C with this oracle,
+ * for rows [r0, r1) of A*B, without materialising the oracle's C: every row
+ * is computed as oracle_numeric computes it and compared at once.  The other
+ * C is given by g_rp[0..r1-r0] (absolute offsets of rows r0..r1), and g_col,
+ * g_val holding the entries from offset g_base on (g_val_is_f32 selects
+ * float or double).  A row is bad when its length or any column differs; a
+ * value is bad when |g - c| > rtol * sum of |terms| (exact: g != c), c being
+ * the compensated oracle value.  report[0..5]: bad rows, first bad row (-1
+ * if none), bad values, offset of the first bad value (-1 if none), entries
+ * compared, most terms summed into one entry.  *max_rel (may be NULL): the
+ * largest |g - c| / |c| over compared entries with c != 0.  Returns bad
+ * rows + bad values, or -1 when out of memory. */
+int64_t oracle_check_rows(int64_t r0, int64_t r1, int64_t n, const int32_t *a_rp,
+                          const int32_t *a_col, const void *a_val, const int32_t *b_rp,
+                          const int32_t *b_col, const void *b_val, int val_is_f32,
+                          const int64_t *g_rp, int64_t g_base, const int32_t *g_col,
+                          const void *g_val, int g_val_is_f32, double rtol, int exact,
+                          int64_t *report, double *max_rel, int nthreads);
+
 /* One Markov-clustering prune + column renormalisation (Trident page, §5.7):
  * keep entry (i,j) iff (float)c_val >= threshold (compared in fp32; keep[]
  * overrides the decision where keep[e] is 0 or 1, and is ignored where it is

@@ -82,7 +82,7 @@ class Stats(ctypes.Structure):
 
 PHASES = ["row_info", "sym_light", "csc", "outer_product", "histogram", "multisplit",
           "sym_chunk_hash", "sym_chunk_dense", "rowptr", "num_light", "num_chunk_hash",
-          "num_chunk_dense", "chunk_hist", "expand_split", "expand_final"]
+          "num_chunk_dense", "chunk_hist", "expand_split", "expand_final", "sym_heavy"]
 
 
 SPGEMM_F32, SPGEMM_F64 = 0, 1

@@ -1005,7 +1005,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
   if (p->direct) {
     // Final chunks back to back in buffer 0, in list order; every product
     // goes straight to the final chunk covering its column.
-    const int phX = ph_begin(p, SPGEMM_PH_EXPAND_FINAL, s);
+    const int phX = ph_begin(p, vals ? SPGEMM_PH_EXPAND_FINAL : SPGEMM_PH_SYM_HEAVY, s);
     int64_t* fcOff = alloc_n<int64_t>(p, nfc + 1, s);
     int64_t* ftmp = alloc_n<int64_t>(p, scan_tmp_elems(nfc) + 1, s);
     launch_scan_i32(B->fcCnt, nfc, fcOff, ftmp, s);

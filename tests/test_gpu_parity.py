@@ -4,8 +4,8 @@ Structure (row_ptr and sorted col) must match exactly.  Values: integer-valued
 inputs must match exactly; otherwise |c - c_ref| <= rtol * sum_k |a_ik b_kj|
 per entry with rtol = 1e-12 (fp64) or 1e-5 (fp32).  The sum of |terms| is the
 scale that bounds the error of any summation order (for same-sign terms it
-equals |c_ref|).  Full-size configurations are checked on sampled rows, which
-the oracle computes one by one, and through properties that hold at any size.
+equals |c_ref|).  Full-size configurations are checked on every row, streamed
+to the host in row blocks and compared with the oracle row by row.
 """
 import numpy as np
 import pytest
@@ -23,11 +23,7 @@ RTOL = {np.float64: 1e-12, np.float32: 1e-5}
 
 
 def _rtol(A, ref):
-    if A.val.dtype == np.float32:
-        # fp32 accumulation over t terms: at most about t * 2^-24 of the term
-        # magnitudes; the stated 1e-5 holds up to ~160 terms per entry.
-        return np.maximum(1e-5, ref.terms * 2.0 ** -24)
-    return 1e-12
+    return RTOL[A.val.dtype.type]
 
 
 def _to_np(t, dtype=None):
@@ -331,45 +327,56 @@ def test_laplacian_config_exact():
     assert st["lds_dense_products"] == st["products"]
 
 
-def _sampled_check(A, rows, **opts):
+def _full_product(A, **opts):
     dA = sg.to_device(A)
     with sg.Plan(dA, dA, **opts) as p:
         rp, nnz = p.symbolic()
         col, val = p.numeric()
         st = p.stats()
     torch.cuda.synchronize()
+    del dA
+    return rp, col, val, nnz, st
+
+
+def _check_every_row(A, rp, col, val, block_entries=1 << 30):
+    """Every row of the GPU's C = A*A against the oracle, streamed to the
+    host in row blocks of at most `block_entries` entries: row lengths and
+    columns exactly, values to the stated relative tolerance of the sum of
+    |terms|.  Returns the host row pointers."""
     rp_h = _to_np(rp, np.int64)
-    rows = np.asarray(rows, dtype=np.int64)
-    lens = rp_h[rows + 1] - rp_h[rows]
-    idx = np.repeat(rp_h[rows] - np.concatenate([[0], np.cumsum(lens)[:-1]]), lens) + \
-        np.arange(int(lens.sum()))
-    it = torch.from_numpy(idx).to(col.device)
-    gcol, gval = _to_np(col[it]), _to_np(val[it])
-    ref = oracle.spgemm(A, A, rows=rows)
-    grp = np.zeros(rows.size + 1, np.int64)
-    np.cumsum(lens, out=grp[1:])
-    assert_csr_equal_structure(grp, gcol, ref.row_ptr, ref.col, "sampled rows")
-    assert_values_close(gval, ref.val, ref.mag, _rtol(A, ref), "sampled rows")
-    assert np.all(np.diff(rp_h) >= 0) and rp_h[0] == 0 and rp_h[-1] == nnz
-    return rp_h, st, (rp, col, val)
+    assert rp_h[0] == 0 and np.all(np.diff(rp_h) >= 0)
+    rtol = RTOL[A.val.dtype.type]
+    r0, worst, terms, entries = 0, 0.0, 0, 0
+    while r0 < A.m:
+        r1 = int(np.searchsorted(rp_h, rp_h[r0] + block_entries, side="right")) - 1
+        r1 = min(max(r1, r0 + 1), A.m)
+        a, b = int(rp_h[r0]), int(rp_h[r1])
+        gcol, gval = _to_np(col[a:b]), _to_np(val[a:b])
+        rep = oracle.check_rows(A, A, r0, r1, rp_h[r0:r1 + 1], gcol, gval, rtol)
+        print(f"rows [{r0}, {r1}) entries {b - a}: bad rows {rep.bad_rows} "
+              f"(first {rep.first_bad_row}), bad values {rep.bad_values} "
+              f"(first {rep.first_bad_value}), max rel {rep.max_rel:.3g}, "
+              f"max terms {rep.max_terms}", flush=True)
+        assert rep.ok, f"rows [{r0}, {r1}): {rep}"
+        worst, terms, entries = max(worst, rep.max_rel), max(terms, rep.max_terms), entries + rep.entries
+        del gcol, gval
+        r0 = r1
+    assert entries == rp_h[-1]
+    print(f"all {A.m} rows, {entries} entries: max rel {worst:.3g}, max terms {terms}", flush=True)
+    return rp_h
 
 
-def test_rmat18_config_sampled():
+def test_rmat18_config_every_row():
     A = synth.workload("rmat18")
     P = oracle.row_products(A, A)
-    rng = np.random.default_rng(1)
-    heavy = np.nonzero(P > 6826)[0]
-    light = np.nonzero((P > 0) & (P <= 6826))[0]
-    rows = np.unique(np.concatenate([np.arange(40), rng.choice(heavy, 300, replace=False),
-                                     rng.choice(light, 1500, replace=False),
-                                     np.nonzero(P == 0)[0][:20], [A.m - 1]]))
-    rp_h, st, _ = _sampled_check(A, rows)
+    rp, col, val, nnz, st = _full_product(A)
     assert st["params"]["tau"] == 6826 and st["heavy_row_threshold"] == 6826 // 3
     assert st["heavy_rows"] == int((P > 6826 // 3).sum()) and st["params"]["v_chunks"] == [16]
-    assert st["global_products"] == 0 and st["lds_dense_products"] > 0
-    # the whole row-pointer array against the oracle's symbolic counts
-    cnt = oracle.symbolic(A, A)
-    np.testing.assert_array_equal(np.diff(rp_h), cnt)
+    assert st["lds_dense_products"] > 0
+    rp_h = _check_every_row(A, rp, col, val)
+    assert rp_h[-1] == nnz
+    del rp, col, val
+    torch.cuda.empty_cache()
 
 
 def test_planted_partition_small_with_prune():
@@ -458,43 +465,48 @@ def test_mcl_iterations_step_by_step():
     np.testing.assert_allclose([ey[k] for k in common], [ex[k] for k in common], rtol=1e-4)
 
 
-def test_mcl_config_sampled_and_prune_properties():
+def test_mcl_config_every_row_and_prune():
+    # C = A*A for the 10^6-column planted partition, every row against the
+    # oracle; then the prune and column renormalisation of the whole C against
+    # the oracle's, with the GPU's keep decision adopted only for entries
+    # within 1e-5 relative of the threshold.
     A = synth.workload("mcl1m")
-    rng = np.random.default_rng(2)
-    rows = np.unique(rng.choice(A.m, 1500, replace=False))
-    rp_h, st, (rp, col, val) = _sampled_check(A, rows)
+    rp, col, val, nnz, st = _full_product(A)
     assert st["heavy_rows"] == 0
-    # column sums of C = A^2 are 1 (A is column-stochastic)
-    cs = torch.zeros(A.n, dtype=torch.float64, device=col.device)
-    cs.index_add_(0, col.long(), val.double())
-    assert float((cs - 1).abs().max()) < 1e-5
+    _check_every_row(A, rp, col, val)
     orp, ocol, oval = sg.prune_colnorm(rp, col, val, A.m, A.n, 1e-4)
-    # every kept entry passed the threshold and every dropped one did not
-    kept_mask = val >= 1e-4
-    assert int(kept_mask.sum()) == ocol.numel()
-    np.testing.assert_array_equal(_to_np(ocol), _to_np(col[kept_mask]))
-    cs2 = torch.zeros(A.n, dtype=torch.float64, device=col.device)
-    cs2.index_add_(0, ocol.long(), oval.double())
-    nz = torch.bincount(ocol.long(), minlength=A.n) > 0
-    assert float((cs2[nz] - 1).abs().max()) < 1e-5
-    del rp, col, val, orp, ocol, oval
+    torch.cuda.synchronize()
+    gval = _to_np(val).astype(np.float64)
+    del col, val
+    torch.cuda.empty_cache()
+    ref = oracle.spgemm(A, A)
+    np.testing.assert_array_equal(_to_np(rp, np.int64), ref.row_ptr)
+    band = np.abs(ref.val - 1e-4) <= 1e-5 * 1e-4
+    keep = np.full(ref.val.size, -1, np.int8)
+    keep[band] = gval[band] >= np.float32(1e-4)
+    print(f"entries within the tie band: {int(band.sum())}", flush=True)
+    erp, ecol, evals = oracle.prune_colnorm(A.m, A.n, ref.row_ptr, ref.col, ref.val, 1e-4,
+                                            keep=keep)
+    del ref, gval, keep
+    assert_csr_equal_structure(_to_np(orp, np.int64), _to_np(ocol), erp, ecol, "pruned")
+    g = _to_np(oval).astype(np.float64)
+    np.testing.assert_allclose(g, evals, rtol=1e-5, atol=0)
+    print(f"pruned: {ecol.size} of {int(nnz)} entries kept, max rel "
+          f"{float(np.max(np.abs(g - evals) / evals)):.3g}", flush=True)
+    del rp, orp, ocol, oval
+    torch.cuda.empty_cache()
 
 
-def test_rmat20_config_sampled_batched_rowptr64():
+def test_rmat20_config_every_row_batched_rowptr64():
     A = synth.workload("rmat20")
     P = oracle.row_products(A, A)
-    rng = np.random.default_rng(3)
-    heavy = np.nonzero(P > 6826)[0]
-    light = np.nonzero((P > 0) & (P <= 6826))[0]
-    rows = np.unique(np.concatenate([np.arange(8), rng.choice(heavy, 200, replace=False),
-                                     rng.choice(light, 1000, replace=False), [A.m - 1]]))
     torch.cuda.empty_cache()
-    rp_h, st, out = _sampled_check(A, rows, rowptr64=1)
-    del out
-    torch.cuda.empty_cache()
+    rp, col, val, nnz, st = _full_product(A, rowptr64=1)
     assert st["params"]["v_chunks"] == [32, 2] and st["params"]["levels"] == 2
     hv = P > st["heavy_row_threshold"]
     assert st["heavy_rows"] == int(hv.sum()) and st["heavy_products"] == int(P[hv].sum())
-    assert st["batches"] > 1
-    cnt = oracle.symbolic(A, A)
-    np.testing.assert_array_equal(np.diff(rp_h), cnt)
+    assert st["batches"] > 1 and nnz > 2 ** 31
+    rp_h = _check_every_row(A, rp, col, val)
+    assert rp_h[-1] == nnz
+    del rp, col, val
+    torch.cuda.empty_cache()

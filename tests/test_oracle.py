@@ -516,8 +516,8 @@ def test_capacity_sample_and_workflow_rule():
 # --- planted mistakes -------------------------------------------------------
 
 _MUTANTS = {
-    "dropped_term": ("for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) {\n            int32_t c = b_col[b];\n            double p",
-                     "for (int64_t b = b_rp[k]; b < b_rp[k + 1] - 1; ++b) {\n            int32_t c = b_col[b];\n            double p"),
+    "dropped_term": ("for (int64_t b = b_rp[k]; b < b_rp[k + 1]; ++b) {\n      int32_t c = b_col[b];\n      double p",
+                     "for (int64_t b = b_rp[k]; b < b_rp[k + 1] - 1; ++b) {\n      int32_t c = b_col[b];\n      double p"),
     "wrong_sign": ("cmp[c] += (s - t) + p;", "cmp[c] -= (s - t) + p;"),
     "wrong_index": ("double p = a * (val_is_f32 ? (double)bf[b] : bd[b]);",
                     "double p = a * (val_is_f32 ? (double)bf[b_rp[k]] : bd[b_rp[k]]);"),
@@ -589,3 +589,47 @@ def test_mutants_fail(name):
 
 def test_unmutated_passes_pins():
     assert _pins_pass(oracle.build(force=False))
+
+
+# --- the row-by-row checker used by the full-size GPU parity tests ----------
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_check_rows_accepts_oracle_and_flags_planted_errors(dtype):
+    # The checker recomputes each row as oracle_numeric does; it must accept
+    # the oracle's own C (rounded to the value type) over any row block, and
+    # flag a wrong row length, a wrong column and a value outside the bound.
+    A = synth.random_csr(300, 250, 6.0, 71, values="uniform", empty_row_frac=0.2, dtype=dtype)
+    B = synth.random_csr(250, 400, 7.0, 72, values="uniform", empty_row_frac=0.2, dtype=dtype)
+    ref = oracle.spgemm(A, B)
+    rtol = 1e-12 if dtype == np.float64 else 1e-5
+    g = ref.val.astype(dtype)
+    rep = oracle.check_rows(A, B, 0, A.m, ref.row_ptr, ref.col, g, rtol)
+    assert rep.ok and rep.entries == ref.col.size and rep.max_terms == int(ref.terms.max())
+    # a block in the middle, its entries given from their own offset
+    r0, r1 = 40, 170
+    a, b = int(ref.row_ptr[r0]), int(ref.row_ptr[r1])
+    rep = oracle.check_rows(A, B, r0, r1, ref.row_ptr[r0:r1 + 1], ref.col[a:b], g[a:b], rtol)
+    assert rep.ok and rep.entries == b - a
+    # integer inputs must match exactly
+    Ai = synth.random_csr(120, 90, 5.0, 73, values="int", dtype=dtype)
+    Bi = synth.random_csr(90, 110, 5.0, 74, values="int", dtype=dtype)
+    ri = oracle.spgemm(Ai, Bi)
+    assert oracle.check_rows(Ai, Bi, 0, Ai.m, ri.row_ptr, ri.col, ri.val.astype(dtype), 0,
+                             exact=True).ok
+    # a value one tolerance step outside the bound
+    e = int(np.argmax(ref.mag))
+    bad = g.copy()
+    bad[e] = dtype(ref.val[e] + 3 * rtol * ref.mag[e])
+    rep = oracle.check_rows(A, B, 0, A.m, ref.row_ptr, ref.col, bad, rtol)
+    assert rep.bad_values == 1 and rep.first_bad_value == e and rep.bad_rows == 0
+    # a wrong column inside a row
+    row = int(np.nonzero(np.diff(ref.row_ptr) >= 2)[0][3])
+    cc = ref.col.copy()
+    cc[ref.row_ptr[row]] = cc[ref.row_ptr[row] + 1]
+    rep = oracle.check_rows(A, B, 0, A.m, ref.row_ptr, cc, g, rtol)
+    assert rep.bad_rows == 1 and rep.first_bad_row == row
+    # a row one entry short (the next row starts one earlier)
+    rp = ref.row_ptr.copy()
+    rp[row + 1] -= 1
+    rep = oracle.check_rows(A, B, 0, A.m, rp, ref.col, g, rtol)
+    assert rep.bad_rows == 2 and rep.first_bad_row == row
