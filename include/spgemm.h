@@ -149,7 +149,20 @@ typedef struct spgemm_options {
                                    expand-sort-compact kernel (32 lanes per
                                    row, sort by lane exchanges, no LDS;
                                    Ocean page, §3)                         */
-  int64_t reserved[4];
+  int64_t index_limit;          /* largest value accepted where an index is
+                                   held in 32 bits: nnz(C) with an int32
+                                   C.row_ptr, and a row's intermediate product
+                                   count (its row-local product offsets are
+                                   int32).  0 = INT32_MAX; a smaller value
+                                   only serves tests of the overflow checks  */
+  int64_t debug_device_error;   /* test hook, 0 in normal use: when nonzero,
+                                   spgemm_numeric ends by storing this value
+                                   in the plan's device status word on its
+                                   stream, as a tripped device-side capacity
+                                   check does, so that the reporting path
+                                   (spgemm_wait, spgemm_get_stats) can be
+                                   exercised from the host               */
+  int64_t reserved[2];
 } spgemm_options;
 
 /* Parameters chosen by GetMagnusParams (gMAGNUS §III-D, Eq. 4-7). */
@@ -243,7 +256,9 @@ spgemm_status spgemm_compute_params(int64_t ncols, int64_t lds_bytes,
  * setup phase).  Blocks once to read back the heavy count.  A and B are
  * borrowed until spgemm_destroy and must not change meanwhile.
  * Errors: INVALID_ARG, INDEX_OVERFLOW (nnz > INT32_MAX in an input),
- * INVALID_CSR (with validate), OOM, HIP.  On error *out is NULL. */
+ * INVALID_CSR (with validate), OOM, HIP; INDEX_OVERFLOW also when a row's
+ * intermediate product count exceeds opts->index_limit (INT32_MAX).  On
+ * error *out is NULL and nothing the caller owns was written. */
 spgemm_status spgemm_plan(spgemm_plan_t *out, int64_t m, int64_t k, int64_t n,
                           const int32_t *dA_row_ptr, const int32_t *dA_col,
                           const void *dA_val, int64_t nnzA,
@@ -254,15 +269,34 @@ spgemm_status spgemm_plan(spgemm_plan_t *out, int64_t m, int64_t k, int64_t n,
 /* Symbolic phase: writes C.row_ptr (m+1 entries, int32, or int64 with
  * opts->rowptr64) into the caller's device buffer and returns nnz(C) on the
  * host (blocks once).  Heavy rows are expanded, multisplit and counted here;
- * the reordered intermediate is kept for numeric.
- * Errors: STATE (not planned, or already run), INDEX_OVERFLOW, OOM, HIP. */
+ * the reordered intermediate is kept for numeric.  dC_row_ptr is written
+ * last, only when the call succeeds.
+ * Errors: STATE (not planned, or already run), INDEX_OVERFLOW (nnz(C) above
+ * opts->index_limit, INT32_MAX by default, with an int32 C.row_ptr), OOM,
+ * HIP, INVALID_CSR (with validate), INTERNAL (a device capacity check). */
 spgemm_status spgemm_symbolic(spgemm_plan_t p, void *dC_row_ptr,
                               int64_t *nnzC);
 
 /* Numeric phase: fills C.col (nnz(C) int32) and C.val (nnz(C), dtype),
- * columns sorted within each row.  Asynchronous on the plan's stream.
- * Errors: STATE (symbolic not run), HIP. */
+ * columns sorted within each row.  Asynchronous on the plan's stream: the
+ * kernels' own capacity checks (a numeric row or chunk whose size differs
+ * from the symbolic count, a full hash table) are reported by spgemm_wait
+ * or spgemm_get_stats, never by this call.  With a single heavy-row batch
+ * (the symbolic expansion kept for numeric) this call allocates nothing, so
+ * it cannot fail with OOM; with several batches each batch allocates its
+ * chunk lists, and an OOM then leaves C.col/C.val partly written (C.row_ptr
+ * from symbolic stays valid).
+ * Errors: STATE (symbolic not run, or run twice), INVALID_ARG, OOM, HIP. */
 spgemm_status spgemm_numeric(spgemm_plan_t p, int32_t *dC_col, void *dC_val);
+
+/* Blocks until all work the plan has enqueued is done, then reports the
+ * device status word: INTERNAL (with the check that tripped in
+ * spgemm_last_error) when a device-side capacity check failed during
+ * symbolic or numeric, in which case C must not be used; OK otherwise.  The
+ * plan enters the error state on failure.  Call it (or spgemm_get_stats)
+ * after spgemm_numeric before trusting C.
+ * Errors: INVALID_ARG (NULL plan), INTERNAL, INVALID_CSR, HIP. */
+spgemm_status spgemm_wait(spgemm_plan_t p);
 
 spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats *out);
 

@@ -36,7 +36,8 @@ class Options(ctypes.Structure):
         ("histogram_from_data", c_i32), ("alloc", c_vp), ("free", c_vp),
         ("alloc_ctx", c_vp), ("expansion", c_i32), ("heavy_row_threshold", c_i32),
         ("light_hash_only", c_i32), ("workflow", c_i32), ("hll_registers", c_i32),
-        ("hll_coef_pct", c_i32), ("light_no_esc", c_i32), ("reserved", c_i64 * 4),
+        ("hll_coef_pct", c_i32), ("light_no_esc", c_i32), ("index_limit", c_i64),
+        ("debug_device_error", c_i64), ("reserved", c_i64 * 2),
     ]
 
 
@@ -114,6 +115,8 @@ def lib():
         L.spgemm_symbolic.argtypes = [c_vp, c_vp, ctypes.POINTER(c_i64)]
         L.spgemm_numeric.restype = st
         L.spgemm_numeric.argtypes = [c_vp, c_vp, c_vp]
+        L.spgemm_wait.restype = st
+        L.spgemm_wait.argtypes = [c_vp]
         L.spgemm_get_stats.restype = st
         L.spgemm_get_stats.argtypes = [c_vp, ctypes.POINTER(Stats)]
         L.spgemm_destroy.restype = None
@@ -252,7 +255,13 @@ class Plan:
         if val is None:
             val = torch.empty(max(self.nnz, 1), dtype=self.dtype, device=dev)[:self.nnz]
         _check(lib().spgemm_numeric(self._h, col.data_ptr(), val.data_ptr()), self._h)
+        self._numeric_done = True
         return col, val
+
+    def wait(self):
+        """Block until the plan's work is done; raise SpgemmError when a
+        device-side capacity check tripped (C must not be used then)."""
+        _check(lib().spgemm_wait(self._h), self._h)
 
     def row_estimates(self, with_estimates=True):
         """Light rows' reserved output slots (int64) and, with the HyperLogLog
@@ -278,8 +287,14 @@ class Plan:
     def __enter__(self):
         return self
 
-    def __exit__(self, *exc):
-        self.destroy()
+    def __exit__(self, exc_type, exc, tb):
+        # Device-side checks of the asynchronous numeric phase surface here
+        # (unless an exception is already on its way).
+        try:
+            if exc_type is None and getattr(self, "_numeric_done", False) and self._h:
+                self.wait()
+        finally:
+            self.destroy()
 
     def __del__(self):
         try:

@@ -270,10 +270,10 @@ struct spgemm_plan_s {
   const int32_t* xheavy = nullptr;
   std::vector<int64_t> hChat, hAnnz;                   // scans over heavy rows
   std::vector<std::pair<int64_t, int64_t>> batches;   // heavy-row ranges of numeric
-  std::vector<std::pair<int64_t, int64_t>> batchesSym; // and of symbolic
   bool symVals = true;   // symbolic expands values too (one batch, kept)
   Batch kept{};          // the expansion symbolic leaves for numeric (one batch)
   bool haveKept = false;
+  ChunkDesc* keptDesc = nullptr;  // numeric's chunk descriptors for `kept`
   size_t wsCur = 0;      // workspace bytes currently held
   int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
   int64_t* dAnnz = nullptr; // scan of the heavy rows' A lengths (h + 1)
@@ -318,6 +318,10 @@ void* plan_alloc(spgemm_plan_t p, size_t bytes, hipStream_t s) {
   void* ptr = nullptr;
   if (p->opts.alloc) {
     ptr = p->opts.alloc(bytes, (void*)s, p->opts.alloc_ctx);
+    // The callback reports failure by NULL; a HIP error state it may leave
+    // behind in this thread is not the library's and must not be taken for
+    // a failed launch.
+    (void)hipGetLastError();
   } else if (hipMallocAsync(&ptr, bytes, s) != hipSuccess) {
     (void)hipGetLastError();
     ptr = nullptr;
@@ -338,6 +342,7 @@ void release(spgemm_plan_t p) {
   for (auto& a : p->allocs) {
     if (p->opts.alloc) {
       if (p->opts.free) p->opts.free(a.first, (void*)a.second, p->opts.alloc_ctx);
+      (void)hipGetLastError();  // not the library's error state
     } else {
       (void)hipFreeAsync(a.first, a.second);
     }
@@ -357,6 +362,7 @@ void ws_reset(spgemm_plan_t p, const WsMark& mk, hipStream_t s) {
     auto& a = p->allocs[i];
     if (p->opts.alloc) {
       if (p->opts.free) p->opts.free(a.first, (void*)s, p->opts.alloc_ctx);
+      (void)hipGetLastError();  // not the library's error state
     } else {
       HIP_CHECK(hipFreeAsync(a.first, s));
     }
@@ -503,6 +509,7 @@ void check_device_errors(spgemm_plan_t p, int32_t word) {
     throw Error{SPGEMM_ERR_INTERNAL, "multisplit work group met more rows than sized for"};
   if (word & kErrCountMismatch)
     throw Error{SPGEMM_ERR_INTERNAL, "numeric and symbolic sizes disagree"};
+  if (word) throw Error{SPGEMM_ERR_INTERNAL, "device status word " + std::to_string(word)};
   (void)p;
 }
 
@@ -514,6 +521,12 @@ int32_t read_err(spgemm_plan_t p, hipStream_t s) {
 
 RowArgs row_args(spgemm_plan_t p) {
   return RowArgs{p->arp, p->acol, p->aval, p->brp, p->bcol, p->bval, p->scanA, p->rowP, p->rowWin};
+}
+
+// Largest value held in an int32 index (options.index_limit lowers it for
+// tests of the overflow checks).
+int64_t index_limit(spgemm_plan_t p) {
+  return p->opts.index_limit > 0 ? std::min<int64_t>(p->opts.index_limit, INT32_MAX) : INT32_MAX;
 }
 
 // ------------------------------------------------------------------ plan
@@ -548,6 +561,7 @@ void do_plan(spgemm_plan_t p) {
       p->params.dense_width > 32768)
     throw Error{SPGEMM_ERR_INVALID_ARG, "dense width does not fit the LDS"};
   if (p->opts.mem_budget < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "mem_budget must be >= 0"};
+  if (p->opts.index_limit < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "index_limit must be >= 0"};
   if (p->opts.workflow < 0 || p->opts.workflow > 3)
     throw Error{SPGEMM_ERR_INVALID_ARG, "workflow must lie in [0, 3]"};
   if (p->opts.hll_registers != 0 && p->opts.hll_registers != 32 && p->opts.hll_registers != 64)
@@ -573,6 +587,9 @@ void do_plan(spgemm_plan_t p) {
     chunks_set_attributes();
     attrs = true;
   }
+  // Nothing before this point launched work of this plan: an error state
+  // left in this thread by earlier, unrelated calls is not this plan's.
+  (void)hipGetLastError();
   if (!p->opts.alloc) {
     // Keep freed workspace in the stream-ordered pool for the next product
     // instead of returning it to the driver at every synchronisation.
@@ -673,6 +690,11 @@ void do_plan(spgemm_plan_t p) {
   p->st.chunk_col_bytes = 4;
   p->xheavy = p->rowOrder + p->rowBinStart[p->NS + 1];
   p->nreq = p->params.chunks_required;
+  // Row-local product offsets (scanA) and chunk counts are int32.
+  if (p->st.max_row_products > index_limit(p))
+    throw Error{SPGEMM_ERR_INDEX_OVERFLOW,
+                "a row has " + std::to_string(p->st.max_row_products) +
+                    " intermediate products, beyond the 32-bit row-local product offsets"};
   p->st.ms_plan = now_ms() - t0;
 }
 
@@ -761,17 +783,12 @@ void heavy_prepare(spgemm_plan_t p) {
   p->st.chunk_col_bytes = p->col16 ? 2 : 4;
   const int64_t nbuf = heavy_nbuf(p);
   // Numeric needs columns and values.  If that takes one batch, symbolic
-  // expands with values and numeric reuses the result; otherwise symbolic
-  // expands columns only, in batches a third (fp64) or half (fp32) the size.
+  // expands with values and numeric reuses the result (gMAGNUS Algorithm
+  // 3); otherwise symbolic counts every heavy row's W-wide slots straight
+  // from A and B (no expansion) and numeric expands each batch.
   const int64_t maxNum = cut_batches(p, std::max<int64_t>(budget / (nbuf * (4 + vb)), 1), &p->batches);
-  int64_t bytes = (int64_t)heavy_buf_bytes(p, maxNum, true);
+  const int64_t bytes = (int64_t)heavy_buf_bytes(p, maxNum, true);
   p->symVals = p->batches.size() == 1;
-  if (p->symVals) {
-    p->batchesSym = p->batches;
-  } else {
-    const int64_t maxSym = cut_batches(p, std::max<int64_t>(budget / (nbuf * 4), 1), &p->batchesSym);
-    bytes = std::max<int64_t>(bytes, (int64_t)heavy_buf_bytes(p, maxSym, false));
-  }
   p->st.batches = (int64_t)p->batches.size();
   p->heavyBuf = heavy_region(p, (size_t)bytes);
 
@@ -1058,7 +1075,7 @@ ChunkList chunk_list(spgemm_plan_t p, const Batch& B) {
   return ChunkList{B.fcOff, B.fcCnt, B.fcRow, B.fcSlot, B.fcBuf, B.bufCol[0], B.bufCol[1],
                    B.bufVal[0], B.bufVal[1], p->params.dense_width, p->nreq,
                    p->xheavy + B.hb0, p->slotOff + B.hb0 * p->nreq,
-                   p->slotNnz + B.hb0 * p->nreq, p->col16 ? 1 : 0};
+                   p->slotNnz + B.hb0 * p->nreq, p->col16 ? 1 : 0, B.fcSpan};
 }
 
 // Chunk symbolic: per-chunk nnz into the batch's slots.
@@ -1102,11 +1119,13 @@ void symbolic_batch(spgemm_plan_t p, const Batch& B) {
   check_launch("chunk symbolic");
 }
 
-void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval) {
+void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
+                   ChunkDesc* desc = nullptr) {
   hipStream_t s = p->sh;
   const ChunkList cl = chunk_list(p, B);
-  // Descriptors of the chunks in bin order, gathered once.
-  ChunkDesc* desc = alloc_n<ChunkDesc>(p, B.nfc, s);
+  // Descriptors of the chunks in bin order, gathered once (into space
+  // reserved by symbolic for the kept batch).
+  if (!desc) desc = alloc_n<ChunkDesc>(p, B.nfc, s);
   launch_chunk_desc(B.nfc, B.fcOrder, cl, p->cRowOff, desc, s);
   const int ph = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
   for (int b = 0; b < p->NS; ++b) {
@@ -1145,21 +1164,24 @@ void heavy_symbolic(spgemm_plan_t p) {
   }
   p->st.final_chunks = 0;
   p->st.dense_chunks = 0;
-  const bool single = p->symVals;
-  for (const auto& bt : p->batchesSym) {
-    const WsMark mk = ws_mark(p);
+  if (p->symVals) {
     Batch B;
-    expand_batch(p, bt.first, bt.second, true, p->symVals, &B);
+    expand_batch(p, p->batches[0].first, p->batches[0].second, true, true, &B);
     symbolic_batch(p, B);
     p->st.final_chunks += B.nfc;
     p->st.dense_chunks += B.denseChunks;
     for (int l = 0; l < 8; ++l) p->st.level_elems[l] += B.levelElems[l];
-    if (single) {
-      p->kept = B;
-      p->haveKept = true;
-    } else {
-      ws_reset(p, mk, s);
-    }
+    p->kept = B;
+    p->haveKept = true;
+    // numeric's descriptors, reserved now so that numeric allocates nothing
+    p->keptDesc = alloc_n<ChunkDesc>(p, B.nfc, s);
+  } else {
+    const int ph = ph_begin(p, SPGEMM_PH_SYM_HEAVY, s);
+    int32_t* next = alloc_n<int32_t>(p, 1, s);
+    launch_fill_i32(next, 0, 1, s);
+    launch_sym_heavy_rows(h, p->nreq, log2_exact(W), p->xheavy, row_args(p), p->nnzB,
+                          p->slotNnz, next, p->numCUs, (size_t)p->lds, s);
+    ph_end(p, ph, s);
   }
   launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
   check_launch("heavy symbolic");
@@ -1167,14 +1189,17 @@ void heavy_symbolic(spgemm_plan_t p) {
 
 void heavy_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   if (p->haveKept) {
-    numeric_batch(p, p->kept, ccol, cval);
+    numeric_batch(p, p->kept, ccol, cval, p->keptDesc);
     return;
   }
   for (const auto& bt : p->batches) {
     const WsMark mk = ws_mark(p);
     Batch B;
-    expand_batch(p, bt.first, bt.second, false, true, &B);
+    expand_batch(p, bt.first, bt.second, true, true, &B);
     numeric_batch(p, B, ccol, cval);
+    p->st.final_chunks += B.nfc;
+    p->st.dense_chunks += B.denseChunks;
+    for (int l = 0; l < 8; ++l) p->st.level_elems[l] += B.levelElems[l];
     ws_reset(p, mk, p->sh);
   }
 }
@@ -1395,8 +1420,10 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   p->st.lds_dense_products = p->hStats[kStatDenseElems];
   p->st.lds_hash_products = p->st.products - p->st.lds_dense_products;
   p->st.global_products = 0;
-  if (!p->opts.rowptr64 && p->nnzC > INT32_MAX)
-    throw Error{SPGEMM_ERR_INDEX_OVERFLOW, "nnz(C) exceeds INT32_MAX; request rowptr64"};
+  if (!p->opts.rowptr64 && p->nnzC > index_limit(p))
+    throw Error{SPGEMM_ERR_INDEX_OVERFLOW,
+                "nnz(C) = " + std::to_string(p->nnzC) +
+                    " exceeds the int32 row pointers; request rowptr64"};
   launch_write_rowptr(p->cRowOff, m + 1, dRowPtr, p->opts.rowptr64 ? 1 : 0, s);
   check_launch("row pointer write");
   *nnzC = p->nnzC;
@@ -1428,6 +1455,8 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
   check_launch("light numeric");
   if (p->h > 0) heavy_numeric(p, ccol, cval);
   join(p);
+  if (p->opts.debug_device_error)
+    launch_fill_i32(p->errWord, (int32_t)p->opts.debug_device_error, 1, p->stream);
   p->st.ms_numeric = now_ms() - t0;
 }
 
@@ -1578,6 +1607,19 @@ spgemm_status spgemm_row_estimates(spgemm_plan_t p, int64_t* dCap, double* dEst)
   });
 }
 
+spgemm_status spgemm_wait(spgemm_plan_t p) {
+  if (!p) return SPGEMM_ERR_INVALID_ARG;
+  return guarded(p, [&] {
+    if (p->sl && p->sl != p->stream) {
+      HIP_CHECK(hipStreamSynchronize(p->sl));
+      HIP_CHECK(hipStreamSynchronize(p->sh));
+    }
+    const int32_t word = read_err(p, p->stream);
+    p->st.device_errors = word;
+    check_device_errors(p, word);
+  });
+}
+
 spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats* out) {
   if (!p || !out) return SPGEMM_ERR_INVALID_ARG;
   spgemm_status st = guarded(p, [&] {
@@ -1585,6 +1627,15 @@ spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats* out) {
       const int32_t word = read_err(p, p->stream);
       p->st.device_errors = word;
       if (p->opts.profile) ph_collect(p);
+      if (p->state >= 2 && p->h > 0 && !p->haveKept) {
+        // the batched schedule bins the chunks (and counts the dense
+        // accumulators' products) in numeric
+        HIP_CHECK(hipMemcpyAsync(p->hStats + 24, p->stats + kStatDenseElems, 8,
+                                 hipMemcpyDeviceToHost, p->stream));
+        HIP_CHECK(hipStreamSynchronize(p->stream));
+        p->st.lds_dense_products = p->hStats[24];
+        p->st.lds_hash_products = p->st.products - p->st.lds_dense_products;
+      }
       check_device_errors(p, word);
     }
   });
@@ -1760,12 +1811,14 @@ extern "C" spgemm_status spgemm_mcl_inflate_fill(spgemm_prune_t p, int32_t* dOut
 extern "C" void spgemm_prune_destroy(spgemm_prune_t p) { prune_free(p); }
 
 // ================================================================ transpose
-extern "C" spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
-                                          const void* dA_row_ptr, int32_t a_rowptr64,
-                                          const int32_t* dA_col, const void* dA_val,
-                                          spgemm_dtype dtype, void* dT_row_ptr,
-                                          int32_t t_rowptr64, int32_t* dT_col, void* dT_val,
-                                          void* stream) {
+namespace sg {
+
+// Validation shared by both transpose entry points; 0 when the arguments
+// are usable, else the status (message in g_thread_error).
+spgemm_status transpose_check_args(int64_t m, int64_t n, int64_t nnz, const void* dA_row_ptr,
+                                   const int32_t* dA_col, const void* dA_val,
+                                   spgemm_dtype dtype, void* dT_row_ptr, int32_t t_rowptr64,
+                                   int32_t* dT_col, void* dT_val) {
   if (m < 0 || n < 0 || nnz < 0 || !dT_row_ptr || (m > 0 && !dA_row_ptr) ||
       (nnz > 0 && (!dA_col || !dT_col || (dA_val && !dT_val))) ||
       (dtype != SPGEMM_F32 && dtype != SPGEMM_F64)) {
@@ -1776,29 +1829,51 @@ extern "C" spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
     g_thread_error = "size exceeds the int32 index range";
     return SPGEMM_ERR_INDEX_OVERFLOW;
   }
-  hipStream_t s = (hipStream_t)stream;
-  const int vb = dtype == SPGEMM_F64 ? 8 : 4;
-  const TransposePlan tp = transpose_plan(n, nnz);
-  // One allocation, carved into 256-byte aligned pieces.
+  return SPGEMM_OK;
+}
+
+namespace {
+struct TrLayout {
+  TransposePlan tp;
+  int64_t szRows, szKeys, szVals, szHist, szOff, szTmp, total;
+  int nVals;
+  bool multi;
+};
+TrLayout transpose_layout(int64_t n, int64_t nnz, int vb, bool vals) {
+  TrLayout L{};
+  L.tp = transpose_plan(n, nnz);
   auto al = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
   const int64_t ent = std::max<int64_t>(nnz, 1);
-  const bool multi = tp.passes > 1;
-  const int64_t szRows = al(4 * ent), szKeys = al(4 * ent), szVals = al((int64_t)vb * ent);
-  const int nVals = dA_val ? (tp.passes > 2 ? 2 : (multi ? 1 : 0)) : 0;
-  const int64_t szHist = al(4 * std::max<int64_t>(tp.histElems, 1));
-  const int64_t szOff = al(8 * (tp.histElems + 1));
-  const int64_t szTmp = al(8 * (scan_tmp_elems(tp.histElems) + 1));
-  const int64_t total = szRows * (multi ? 2 : 1) + szKeys * (multi ? 2 : 1) + szVals * nVals +
-                        szHist + szOff + szTmp + 256;
-  char* buf = nullptr;
-  if (hipMallocAsync((void**)&buf, (size_t)total, s) != hipSuccess) {
-    (void)hipGetLastError();
-    g_thread_error = "device allocation failed";
-    return SPGEMM_ERR_OOM;
-  }
-  spgemm_status st = SPGEMM_OK;
+  L.multi = L.tp.passes > 1;
+  L.szRows = al(4 * ent);
+  L.szKeys = al(4 * ent);
+  L.szVals = al((int64_t)vb * ent);
+  L.nVals = vals ? (L.tp.passes > 2 ? 2 : (L.multi ? 1 : 0)) : 0;
+  L.szHist = al(4 * std::max<int64_t>(L.tp.histElems, 1));
+  L.szOff = al(8 * (L.tp.histElems + 1));
+  L.szTmp = al(8 * (scan_tmp_elems(L.tp.histElems) + 1));
+  L.total = L.szRows * (L.multi ? 2 : 1) + L.szKeys * (L.multi ? 2 : 1) + L.szVals * L.nVals +
+            L.szHist + L.szOff + L.szTmp + 256;
+  return L;
+}
+}  // namespace
+
+int64_t transpose_workspace_bytes(int64_t n, int64_t nnz, spgemm_dtype dtype, bool vals) {
+  return transpose_layout(n, nnz, dtype == SPGEMM_F64 ? 8 : 4, vals).total;
+}
+
+// The transpose with its temporaries carved from `ws` (at least
+// transpose_workspace_bytes): enqueues everything on `s`, then blocks once
+// to read the column check.  Every piece of `ws` that must start at zero is
+// cleared by a kernel here.
+spgemm_status transpose_run(int64_t m, int64_t n, int64_t nnz, const void* dA_row_ptr,
+                            int32_t a_rowptr64, const int32_t* dA_col, const void* dA_val,
+                            spgemm_dtype dtype, void* dT_row_ptr, int32_t t_rowptr64,
+                            int32_t* dT_col, void* dT_val, char* ws, hipStream_t s) {
+  const int vb = dtype == SPGEMM_F64 ? 8 : 4;
+  const TrLayout L = transpose_layout(n, nnz, vb, dA_val != nullptr);
   try {
-    char* q = buf;
+    char* q = ws;
     auto take = [&](int64_t b) {
       char* r = q;
       q += b;
@@ -1807,17 +1882,17 @@ extern "C" spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
     int32_t* rows[2] = {nullptr, nullptr};
     uint32_t* keys[2] = {nullptr, nullptr};
     void* vals[2] = {nullptr, nullptr};
-    rows[1] = (int32_t*)take(szRows);
-    if (multi) rows[0] = (int32_t*)take(szRows);
-    keys[0] = (uint32_t*)take(szKeys);
-    if (multi) keys[1] = (uint32_t*)take(szKeys);
-    for (int i = 0; i < nVals; ++i) vals[i] = take(szVals);
-    int32_t* hist = (int32_t*)take(szHist);
-    int64_t* off = (int64_t*)take(szOff);
-    int64_t* tmp = (int64_t*)take(szTmp);
+    rows[1] = (int32_t*)take(L.szRows);
+    if (L.multi) rows[0] = (int32_t*)take(L.szRows);
+    keys[0] = (uint32_t*)take(L.szKeys);
+    if (L.multi) keys[1] = (uint32_t*)take(L.szKeys);
+    for (int i = 0; i < L.nVals; ++i) vals[i] = take(L.szVals);
+    int32_t* hist = (int32_t*)take(L.szHist);
+    int64_t* off = (int64_t*)take(L.szOff);
+    int64_t* tmp = (int64_t*)take(L.szTmp);
     int32_t* err = (int32_t*)take(256);
     launch_fill_i32(err, 0, 1, s);
-    launch_transpose(tp, m, n, nnz, dA_row_ptr, a_rowptr64, dA_col, dA_val, vb, dT_row_ptr,
+    launch_transpose(L.tp, m, n, nnz, dA_row_ptr, a_rowptr64, dA_col, dA_val, vb, dT_row_ptr,
                      t_rowptr64, dT_col, dT_val, rows, keys, vals, hist, off, tmp, err, s);
     check_launch("transpose");
     int32_t herr = 0;
@@ -1826,8 +1901,35 @@ extern "C" spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
     if (herr & kErrCsr) throw Error{SPGEMM_ERR_INVALID_CSR, "column index outside [0, n)"};
   } catch (const Error& e) {
     g_thread_error = e.msg;
-    st = e.st;
+    return e.st;
   }
+  return SPGEMM_OK;
+}
+
+void set_thread_error(const char* msg) { g_thread_error = msg; }
+
+}  // namespace sg
+
+extern "C" spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
+                                          const void* dA_row_ptr, int32_t a_rowptr64,
+                                          const int32_t* dA_col, const void* dA_val,
+                                          spgemm_dtype dtype, void* dT_row_ptr,
+                                          int32_t t_rowptr64, int32_t* dT_col, void* dT_val,
+                                          void* stream) {
+  spgemm_status st = transpose_check_args(m, n, nnz, dA_row_ptr, dA_col, dA_val, dtype,
+                                          dT_row_ptr, t_rowptr64, dT_col, dT_val);
+  if (st != SPGEMM_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t total = transpose_workspace_bytes(n, nnz, dtype, dA_val != nullptr);
+  // One allocation, carved into 256-byte aligned pieces.
+  char* buf = nullptr;
+  if (hipMallocAsync((void**)&buf, (size_t)total, s) != hipSuccess) {
+    (void)hipGetLastError();
+    g_thread_error = "device allocation failed";
+    return SPGEMM_ERR_OOM;
+  }
+  st = transpose_run(m, n, nnz, dA_row_ptr, a_rowptr64, dA_col, dA_val, dtype, dT_row_ptr,
+                     t_rowptr64, dT_col, dT_val, buf, s);
   (void)hipFreeAsync(buf, s);
   return st;
 }

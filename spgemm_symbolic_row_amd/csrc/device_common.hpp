@@ -14,6 +14,20 @@ constexpr int kXcds = 8;
 
 constexpr int kWave = 64;
 
+// LDS of one work group on gfx950.
+constexpr int kLdsPerGroup = 163840;
+
+// Lets `kernel` take as much dynamic LDS as a work group's LDS leaves beside
+// the kernel's static LDS, and leaves the thread's HIP error state clear.
+inline void allow_max_dynamic_lds(const void* kernel) {
+  hipFuncAttributes fa{};
+  size_t st = 0;
+  if (hipFuncGetAttributes(&fa, kernel) == hipSuccess) st = fa.sharedSizeBytes;
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(kLdsPerGroup - (int)st));
+  (void)hipGetLastError();
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = lane_id();

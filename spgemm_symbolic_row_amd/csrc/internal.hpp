@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/spgemm.h"
+
 namespace sg {
 
 constexpr int32_t kEmptyKey = -1;
@@ -94,8 +96,11 @@ struct ChunkList {
   int64_t nreq;           // W-wide slots per heavy row
   const int32_t* xheavy;  // heavy row index -> row of C
   const int64_t* slotOff; // exclusive offset of each slot inside its row
-  int32_t* slotNnz;       // nnz of the chunk starting at each slot
+  int32_t* slotNnz;       // nnz per slot: of the chunk starting there (the
+                          // chunk symbolic kernels; 0 in its other slots),
+                          // or of the slot alone (heavy-row symbolic)
   int32_t col16;          // chunk columns stored as uint16_t
+  const int8_t* span;     // log2 of the W-wide slots each chunk covers
 };
 
 // Everything a numeric chunk kernel needs about one final chunk, gathered
@@ -191,6 +196,15 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
                      int32_t* err, hipStream_t s, int64_t* cntOut = nullptr);
 void launch_sym_chunks(const BinCfg& b, const ChunkDesc* desc, int64_t n, const ChunkList& cl,
                        int32_t* err, hipStream_t s);
+// Heavy-row symbolic straight from A and B (batched schedule): per heavy
+// row r and W-wide slot s, slotNnz[r * nreq + s] = distinct columns of the
+// row's products inside the slot.  `next` is one int32, zeroed by the caller.
+// Windows of 2^winBits columns (a power of two from W up to what ldsMax
+// bytes of bitmap hold, at most nreq * W).
+int32_t sym_heavy_window_bits(int64_t nreq, int32_t log2W, size_t ldsMax);
+void launch_sym_heavy_rows(int64_t h, int64_t nreq, int32_t log2W, const int32_t* xheavy,
+                           const RowArgs& a, int64_t nnzB, int32_t* slotNnz, int32_t* next,
+                           int numCUs, size_t ldsMax, hipStream_t s);
 // Whether a numeric bin's (tpr, sort size) has a kernel instance.
 bool num_bin_supported(const BinCfg& b);
 void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
@@ -374,6 +388,18 @@ void launch_transpose(const TransposePlan& tp, int64_t m, int64_t n, int64_t nnz
                       void* trp, int trp64, int32_t* tcol, void* tval, int32_t* rows[2],
                       uint32_t* keys[2], void* vals[2], int32_t* hist, int64_t* off,
                       int64_t* scanTmp, int32_t* err, hipStream_t s);
+
+// ---- api.cpp: the transpose's host side, shared by both entry points ----
+spgemm_status transpose_check_args(int64_t m, int64_t n, int64_t nnz, const void* dA_row_ptr,
+                                   const int32_t* dA_col, const void* dA_val,
+                                   spgemm_dtype dtype, void* dT_row_ptr, int32_t t_rowptr64,
+                                   int32_t* dT_col, void* dT_val);
+int64_t transpose_workspace_bytes(int64_t n, int64_t nnz, spgemm_dtype dtype, bool vals);
+spgemm_status transpose_run(int64_t m, int64_t n, int64_t nnz, const void* dA_row_ptr,
+                            int32_t a_rowptr64, const int32_t* dA_col, const void* dA_val,
+                            spgemm_dtype dtype, void* dT_row_ptr, int32_t t_rowptr64,
+                            int32_t* dT_col, void* dT_val, char* ws, hipStream_t s);
+void set_thread_error(const char* msg);
 
 // ---- k_estimate.hip ----
 // Size prediction of light rows without the symbolic pass (upper bound or

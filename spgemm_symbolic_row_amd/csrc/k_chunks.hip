@@ -361,7 +361,7 @@ __global__ __launch_bounds__(TPC* CPB) void k_num_chunks_direct(const ChunkDesc*
 }  // namespace
 
 void chunks_set_attributes() {
-#define SG_ATTR(K) (void)hipFuncSetAttribute((const void*)(K), hipFuncAttributeMaxDynamicSharedMemorySize, 163840)
+#define SG_ATTR(K) allow_max_dynamic_lds((const void*)(K))
   SG_ATTR((k_sym_chunks_bitmap<64, 4>));
   SG_ATTR((k_sym_chunks_bitmap<256, 1>));
   SG_ATTR((k_sym_chunks_bitmap<1024, 1>));

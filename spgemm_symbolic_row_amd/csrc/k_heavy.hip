@@ -322,7 +322,13 @@ __global__ __launch_bounds__(kNT) void k_chunk_desc(int64_t n, const int32_t* __
   // Without C's row offsets (symbolic), base is the chunk's slot index.
   d.base = cRowOff ? cRowOff[cl.xheavy[hr]] + cl.slotOff[sidx] : sidx;
   d.cnt = cl.cnt[item];
-  d.want = cRowOff ? cl.slotNnz[sidx] : 0;
+  // The chunk's size: the counts of the W-wide slots it covers.
+  int32_t want = 0;
+  if (cRowOff) {
+    const int nsl = 1 << cl.span[item];
+    for (int j = 0; j < nsl; ++j) want += cl.slotNnz[sidx + j];
+  }
+  d.want = want;
   d.colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
   d.buf = cl.buf[item];
   desc[i] = d;
@@ -366,8 +372,7 @@ __global__ __launch_bounds__(kNT) void k_final_map(int64_t nfc, const int32_t* _
 }  // namespace
 
 void heavy_set_attributes() {
-#define SG_ATTR(K) \
-  (void)hipFuncSetAttribute((const void*)(K), hipFuncAttributeMaxDynamicSharedMemorySize, 163840)
+#define SG_ATTR(K) allow_max_dynamic_lds((const void*)(K))
   SG_ATTR((k_dense_num<float, int32_t, false>));
   SG_ATTR((k_dense_num<double, int32_t, false>));
   SG_ATTR((k_dense_num<float, uint16_t, false>));

@@ -7,6 +7,7 @@
 //   numeric:  insert-or-add (key, value) pairs with LDS atomics, compact the
 //             occupied slots, bitonic-sort them by column in LDS and write
 //             the sorted row (or chunk) to its place in C.
+#include <algorithm>
 #include <climits>
 
 #include "device_common.hpp"
@@ -908,14 +909,138 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __rest
   }
 }
 
+// ------------------------------------------- heavy-row symbolic from A and B
+// Symbolic of the heavy rows when their intermediate is too large to keep
+// until numeric (the batched schedule): nnz of every W-wide column slot of a
+// heavy row, taken straight from A and B with no expansion.  A work item is
+// (heavy row, column window of 2^winBits columns, a multiple of W); a work
+// group clears an LDS bitmap of the window, marks the columns of the row's
+// products, then counts the bits of each W-wide slot, clearing the words it
+// reads for the next item.  Work groups take items from a counter until
+// none is left.  The per-slot counts give the chunk sizes of any chunk
+// tree: a final chunk covering slots [s, s + 2^k) holds the sum of their
+// counts.
+//
+// The products of a heavy row come almost entirely from long B rows (on
+// R-MAT, 99.6% of them from B rows of 64 or more entries), so each wave
+// takes an even share of the row's products and walks the A entries of that
+// share in order, reading every B row's run with the whole wave, four
+// columns per lane per 16-byte load; the offsets, B row starts and lengths
+// of 64 entries at a time are loaded once, lane-parallel, and read back with
+// lane broadcasts.
+constexpr int kSymHeavyNT = 1024;
+constexpr int kSymHeavyU = 2;  // 16-byte loads per lane in flight per step
+
+__device__ __forceinline__ void mark_col(uint32_t* bm, int32_t col, int32_t w0, uint32_t wlen) {
+  const uint32_t c = (uint32_t)(col - w0);
+  if (c < wlen) atomicOr(&bm[c >> 5], 1u << (c & 31));
+}
+
+__global__ __launch_bounds__(kSymHeavyNT) void k_sym_heavy_rows(
+    int64_t h, int32_t nwin, int32_t winBits, int32_t log2W, int64_t nreq,
+    const int32_t* __restrict__ xheavy, RowArgs a, int64_t nnzB, int32_t* __restrict__ slotNnz,
+    int32_t* __restrict__ next) {
+  extern __shared__ uint32_t bm[];
+  __shared__ int64_t item;
+  constexpr int NW = kSymHeavyNT / kWave;
+  const int t = threadIdx.x, w = t / kWave, lane = lane_id();
+  const int32_t words = 1 << (winBits - 5);
+  for (int i = t; i < words; i += kSymHeavyNT) bm[i] = 0;
+  const int64_t nitems = h * nwin;
+  const int32_t wps = 1 << (log2W - 5);           // bitmap words per W-wide slot
+  const int32_t slots = 1 << (winBits - log2W);   // slots per window
+  const int32_t* __restrict__ bcol = a.bcol;
+  // elements by which bcol lies past a 16-byte boundary
+  const int64_t mis = (int64_t)(((uintptr_t)bcol >> 2) & 3);
+  for (;;) {
+    if (t == 0) item = atomicAdd(next, 1);
+    __syncthreads();
+    const int64_t it = item;
+    if (it >= nitems) break;  // the same for every thread
+    const int64_t r = it / nwin;
+    const int32_t win = (int32_t)(it - r * nwin);
+    const int32_t row = xheavy[r];
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t P = (int32_t)a.rowP[row];
+    const int32_t w0 = win << winBits;
+    const uint32_t wlen = 1u << winBits;
+    const int32_t p0 = (int32_t)((int64_t)P * w / NW);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / NW);
+    if (p0 < p1) {
+      int64_t j = wave_last_le(a.scanA, rs, re, p0);  // the entry holding product p0
+      int32_t p = p0;
+      while (p < p1) {
+        // offsets, B row starts and ends of entries j .. j+63
+        const int64_t e = j + lane;
+        const bool ev = e < re;
+        const int32_t o = ev ? a.scanA[e] : P;
+        const int32_t bs = ev ? a.brp[a.acol[e]] : 0;
+        int32_t on = __shfl_down(o, 1);
+        if (lane == kWave - 1) on = (j + kWave < re) ? a.scanA[j + kWave] : P;
+        for (int q = 0; q < kWave && p < p1; ++q) {
+          const int32_t oe = __shfl(o, q), one = __shfl(on, q), be = __shfl(bs, q);
+          if (one <= p) continue;  // no products, or before this wave's share
+          const int64_t x0 = (int64_t)be + (p - oe);
+          const int64_t x1 = (int64_t)be + ((one < p1 ? one : p1) - oe);
+          // 16-byte loads at 16-byte aligned addresses; elements outside
+          // [x0, x1) are loaded only where the whole vector lies in B.
+          for (int64_t base = ((x0 + mis) & ~(int64_t)3) - mis; base < x1;
+               base += 4 * kWave * kSymHeavyU) {
+            int4 v[kSymHeavyU];
+#pragma unroll
+            for (int u = 0; u < kSymHeavyU; ++u) {
+              const int64_t idx = base + 4 * (u * kWave + lane);
+              v[u] = make_int4(-1, -1, -1, -1);
+              if (idx < x1) {
+                if (idx >= 0 && idx + 4 <= nnzB) {
+                  v[u] = *(const int4*)(bcol + idx);
+                } else {
+                  if (idx >= x0) v[u].x = bcol[idx];
+                  if (idx + 1 >= x0 && idx + 1 < x1) v[u].y = bcol[idx + 1];
+                  if (idx + 2 >= x0 && idx + 2 < x1) v[u].z = bcol[idx + 2];
+                  if (idx + 3 >= x0 && idx + 3 < x1) v[u].w = bcol[idx + 3];
+                }
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < kSymHeavyU; ++u) {
+              const int64_t idx = base + 4 * (u * kWave + lane);
+              if (idx >= x0 && idx < x1) mark_col(bm, v[u].x, w0, wlen);
+              if (idx + 1 >= x0 && idx + 1 < x1) mark_col(bm, v[u].y, w0, wlen);
+              if (idx + 2 >= x0 && idx + 2 < x1) mark_col(bm, v[u].z, w0, wlen);
+              if (idx + 3 >= x0 && idx + 3 < x1) mark_col(bm, v[u].w, w0, wlen);
+            }
+          }
+          p = one < p1 ? one : p1;
+        }
+        j += kWave;
+      }
+    }
+    __syncthreads();
+    for (int s = w; s < slots; s += NW) {
+      int32_t cnt = 0;
+      for (int i = lane; i < wps; i += kWave) {
+        uint32_t* q = &bm[s * wps + i];
+        cnt += __popc(*q);
+        *q = 0;
+      }
+      cnt = wave_sum(cnt);
+      const int64_t gs = (int64_t)win * slots + s;
+      if (lane == 0 && gs < nreq) slotNnz[r * nreq + gs] = cnt;
+    }
+    __syncthreads();
+  }
+}
+
 template <typename K>
 void set_lds_attr(K kernel) {
-  (void)hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+  allow_max_dynamic_lds((const void*)kernel);
 }
 
 }  // namespace
 
 void light_set_attributes() {
+  set_lds_attr(k_sym_heavy_rows);
   set_lds_attr(k_sym_rows<64, 4>);
   set_lds_attr(k_sym_rows<128, 2>);
   set_lds_attr(k_sym_rows<256, 1>);
@@ -1161,3 +1286,31 @@ void launch_num_rows_esc(bool f64, const int32_t* rows, int64_t nrows, const Row
 
 }  // namespace sg
 
+
+namespace sg {
+
+int32_t sym_heavy_window_bits(int64_t nreq, int32_t log2W, size_t ldsMax) {
+  int32_t bits = log2W;
+  while ((int64_t(1) << (bits + 1)) <= nreq * (int64_t(1) << log2W) &&
+         (size_t(1) << (bits + 1 - 3)) <= ldsMax && bits < 30)
+    ++bits;
+  return bits;
+}
+
+void launch_sym_heavy_rows(int64_t h, int64_t nreq, int32_t log2W, const int32_t* xheavy,
+                           const RowArgs& a, int64_t nnzB, int32_t* slotNnz, int32_t* next,
+                           int numCUs, size_t ldsMax, hipStream_t s) {
+  if (h <= 0) return;
+  const int32_t winBits = sym_heavy_window_bits(nreq, log2W, ldsMax);
+  const int64_t cols = nreq << log2W;
+  const int32_t nwin = (int32_t)((cols + (int64_t(1) << winBits) - 1) >> winBits);
+  const size_t lds = size_t(1) << (winBits - 3);
+  // Work groups per CU that the bitmap leaves room for (at most two: 32 waves).
+  const int perCU = lds * 2 + 4096 <= ldsMax ? 2 : 1;
+  const int64_t items = h * nwin;
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(items, (int64_t)numCUs * perCU));
+  hipLaunchKernelGGL(k_sym_heavy_rows, dim3(grid), dim3(kSymHeavyNT), lds, s, h, nwin, winBits,
+                     log2W, nreq, xheavy, a, nnzB, slotNnz, next);
+}
+
+}  // namespace sg

@@ -574,9 +574,7 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
 }  // namespace
 
 void multisplit_set_attributes() {
-#define SG_ATTR(...)                                                                      \
-  (void)hipFuncSetAttribute((const void*)__VA_ARGS__, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                            163840)
+#define SG_ATTR(...) allow_max_dynamic_lds((const void*)__VA_ARGS__)
   SG_ATTR(k_multisplit<kMsItemsF64, double, true, false>);
   SG_ATTR(k_multisplit<kMsItemsF32, float, true, false>);
   SG_ATTR(k_multisplit<kMsItemsF32, float, false, false>);

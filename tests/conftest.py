@@ -36,3 +36,8 @@ def assert_values_close(val, ref_val, ref_mag, rtol, what=""):
     bad = np.nonzero(~(err <= lim))[0]
     assert bad.size == 0, (f"{what}: {bad.size} values outside tolerance; first at {bad[0]}: "
                            f"{val[bad[0]]!r} vs {ref_val[bad[0]]!r} (mag {ref_mag[bad[0]]!r})")
+    if val.size:
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.where(lim > 0, err / lim, 0.0)
+        print(f"{what}: {val.size} values, largest error {float(r.max()):.3g} of the bound",
+              flush=True)
