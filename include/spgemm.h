@@ -379,6 +379,27 @@ spgemm_status spgemm_transpose(int64_t m, int64_t n, int64_t nnz,
                                int32_t t_rowptr64, int32_t *dT_col,
                                void *dT_val, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * transpose, arguments, outputs and errors as spgemm_transpose, with the
+ * temporaries taken from a fixed 64 MiB device array inside the library
+ * instead of hipMallocAsync (each GPU the library runs on holds its own
+ * array until the process ends).  The call makes no device allocation.
+ * The caller still allocates T.  About 16 + 2 * sizeof(value) bytes per
+ * entry are needed (fewer for narrow column ranges); a call whose
+ * temporaries exceed 64 MiB returns INVALID_ARG (message in
+ * spgemm_last_error(NULL)) without touching T.  Calls on one GPU share the
+ * array: calls in stream order are safe (every piece that must start at
+ * zero is cleared by a kernel on `stream`), calls that overlap on one GPU
+ * (other streams or host threads) race.  Blocks once, as spgemm_transpose
+ * does. */
+spgemm_status spgemm_transpose_noalloc(int64_t m, int64_t n, int64_t nnz,
+                                       const void *dA_row_ptr, int32_t a_rowptr64,
+                                       const int32_t *dA_col, const void *dA_val,
+                                       spgemm_dtype dtype, void *dT_row_ptr,
+                                       int32_t t_rowptr64, int32_t *dT_col,
+                                       void *dT_val, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

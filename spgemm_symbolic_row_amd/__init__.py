@@ -142,6 +142,8 @@ def lib():
         L.spgemm_transpose.restype = st
         L.spgemm_transpose.argtypes = [c_i64, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, ctypes.c_int,
                                        c_vp, c_i32, c_vp, c_vp, c_vp]
+        L.spgemm_transpose_noalloc.restype = st
+        L.spgemm_transpose_noalloc.argtypes = L.spgemm_transpose.argtypes
         _lib = L
     return _lib
 
@@ -394,9 +396,11 @@ def prune_colnorm(row_ptr, col, val, m, n, threshold=1e-4, out_rowptr64=False):
     return orp, ocol, oval
 
 
-def transpose(A, out_rowptr64=False, pattern_only=False):
+def transpose(A, out_rowptr64=False, pattern_only=False, no_alloc=False):
     """A^T as a CsrDevice (n x m): rows list their columns in rising order,
-    values copied unchanged (spgemm_transpose)."""
+    values copied unchanged (spgemm_transpose; with no_alloc, the entry point
+    whose temporaries live in the library's fixed scratch array,
+    spgemm_transpose_noalloc)."""
     import torch
     X = _as_csr(A)
     dev = X.col.device
@@ -409,7 +413,8 @@ def transpose(A, out_rowptr64=False, pattern_only=False):
     tcol = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)[:nnz]
     tval = None if vals is None else torch.empty(max(nnz, 1), dtype=vdt, device=dev)[:nnz]
     stream = torch.cuda.current_stream().cuda_stream
-    _check(lib().spgemm_transpose(X.m, X.n, nnz, X.row_ptr.data_ptr(), rp64, X.col.data_ptr(),
+    fn = lib().spgemm_transpose_noalloc if no_alloc else lib().spgemm_transpose
+    _check(fn(X.m, X.n, nnz, X.row_ptr.data_ptr(), rp64, X.col.data_ptr(),
                                   None if vals is None else vals.data_ptr(), dt, trp.data_ptr(),
                                   1 if out_rowptr64 else 0, tcol.data_ptr(),
                                   None if tval is None else tval.data_ptr(), c_vp(stream)))

@@ -29,6 +29,7 @@ COMMON = [
 ]
 SOURCES = ["k_util.hip", "k_light.hip", "k_outer.hip", "k_multisplit.hip", "k_heavy.hip",
            "k_chunks.hip", "k_chunkhist.hip", "k_prune.hip", "k_transpose.hip", "k_estimate.hip",
+           "noalloc.hip",
            "api.cpp",
            "params.cpp"]
 
