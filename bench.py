@@ -336,6 +336,8 @@ def main():
                          "3 Table 1 choice (default: the library's)")
     ap.add_argument("--light-no-esc", action="store_true",
                     help="short rows by the LDS hash kernels instead of ESC (diagnostics)")
+    ap.add_argument("--dense-direct", action="store_true",
+                    help="dense chunks accumulated straight from A and B (diagnostics)")
     ap.add_argument("--light-hash-only", action="store_true",
                     help="no dense windows for light rows (diagnostics)")
     ap.add_argument("--expansion", type=int, default=-1,
@@ -391,6 +393,8 @@ def main():
         opts["expansion"] = args.expansion
     if args.light_hash_only:
         opts["light_hash_only"] = 1
+    if args.dense_direct:
+        opts["dense_direct"] = 1
     if args.workflow >= 0:
         opts["workflow"] = args.workflow
     if args.light_no_esc:

@@ -162,7 +162,16 @@ typedef struct spgemm_options {
                                    check does, so that the reporting path
                                    (spgemm_wait, spgemm_get_stats) can be
                                    exercised from the host               */
-  int64_t reserved[2];
+  int64_t dense_direct;         /* 1: with expansion 0, dense chunks (W-wide
+                                   slots of a heavy row holding more than
+                                   min(tau, W/8) products) are accumulated
+                                   straight from A and B (each entry's run of
+                                   its B row inside the slot, found among B's
+                                   per-slot runs) instead of from the expanded
+                                   intermediate, which then holds only the
+                                   light chunks' products; 0 (default): every
+                                   product is expanded.  Same C either way.  */
+  int64_t reserved[1];
 } spgemm_options;
 
 /* Parameters chosen by GetMagnusParams (gMAGNUS §III-D, Eq. 4-7). */

@@ -37,7 +37,7 @@ class Options(ctypes.Structure):
         ("alloc_ctx", c_vp), ("expansion", c_i32), ("heavy_row_threshold", c_i32),
         ("light_hash_only", c_i32), ("workflow", c_i32), ("hll_registers", c_i32),
         ("hll_coef_pct", c_i32), ("light_no_esc", c_i32), ("index_limit", c_i64),
-        ("debug_device_error", c_i64), ("reserved", c_i64 * 2),
+        ("debug_device_error", c_i64), ("dense_direct", c_i64), ("reserved", c_i64 * 1),
     ]
 
 

@@ -223,6 +223,7 @@ struct Batch {
   int8_t* fcSpan = nullptr;  // log2 of the W-wide slots each chunk covers
   std::vector<int32_t> fcBinStart;
   int64_t levelElems[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  bool denseDirect = false;  // dense chunks taken straight from A and B
 };
 
 }  // namespace
@@ -276,6 +277,7 @@ struct spgemm_plan_s {
   ChunkDesc* keptDesc = nullptr;  // numeric's chunk descriptors for `kept`
   size_t wsCur = 0;      // workspace bytes currently held
   int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
+  const int32_t *runPtr = nullptr, *runChunk = nullptr, *runStart = nullptr;  // B's slot runs
   int64_t* dAnnz = nullptr; // scan of the heavy rows' A lengths (h + 1)
   bool fused = false;    // the first level is fed straight from A and B
   bool direct = false;   // one pass straight into the final chunks
@@ -633,13 +635,11 @@ void do_plan(spgemm_plan_t p) {
     check_device_errors(p, read_err(p, s));
   }
 
+  // Bin caps reach the device as kernel arguments (no copy to wait for).
   std::vector<int32_t> caps(p->NS);
   for (int b = 0; b < p->NS; ++b) caps[b] = p->symBins[b].cap;
   p->dSymCaps = alloc_n<int32_t>(p, 64, s);
-  std::memcpy(p->hBins, caps.data(), sizeof(int32_t) * p->NS);
-  HIP_CHECK(hipMemcpyAsync(p->dSymCaps, p->hBins, sizeof(int32_t) * p->NS, hipMemcpyHostToDevice, s));
-  // The copy reads pinned memory that is rewritten below; wait for it.
-  HIP_CHECK(hipStreamSynchronize(s));
+  launch_set_small_i32(p->dSymCaps, caps.data(), p->NS, s);
 
   p->rowP = alloc_n<int64_t>(p, m, s);
   p->cnt = alloc_n<int64_t>(p, m, s);
@@ -743,18 +743,10 @@ void heavy_prepare(spgemm_plan_t p) {
   const int64_t h = p->h;
   int64_t* tmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, s);
   int64_t* hv = alloc_n<int64_t>(p, h, s);
-  int64_t* pref = alloc_n<int64_t>(p, h + 1, s);
   p->dAnnz = alloc_n<int64_t>(p, h + 1, s);
-  p->hChat.assign(h + 1, 0);
-  p->hAnnz.assign(h + 1, 0);
-  launch_gather_i64(p->rowP, p->xheavy, h, hv, s);
-  launch_scan_i64(hv, h, pref, tmp, s);
-  HIP_CHECK(hipMemcpyAsync(p->hChat.data(), pref, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
   launch_row_lengths(h, p->xheavy, p->arp, hv, s);
   launch_scan_i64(hv, h, p->dAnnz, tmp, s);
-  HIP_CHECK(hipMemcpyAsync(p->hAnnz.data(), p->dAnnz, sizeof(int64_t) * (h + 1), hipMemcpyDeviceToHost, s));
   check_launch("heavy prepare");
-  HIP_CHECK(hipStreamSynchronize(s));
   // Bytes of intermediate per heavy element: one or two (col, val) buffers.
   const int64_t vb = p->f64 ? 8 : 4;
   int64_t budget = p->opts.mem_budget;
@@ -786,7 +778,30 @@ void heavy_prepare(spgemm_plan_t p) {
   // expands with values and numeric reuses the result (gMAGNUS Algorithm
   // 3); otherwise symbolic counts every heavy row's W-wide slots straight
   // from A and B (no expansion) and numeric expands each batch.
-  const int64_t maxNum = cut_batches(p, std::max<int64_t>(budget / (nbuf * (4 + vb)), 1), &p->batches);
+  const int64_t cap = std::max<int64_t>(budget / (nbuf * (4 + vb)), 1);
+  int64_t maxNum = p->Ph;
+  if (p->Ph <= cap) {
+    // One batch: only the totals (known since plan) are needed on the host.
+    p->hChat.assign(h + 1, 0);
+    p->hAnnz.assign(h + 1, 0);
+    p->hChat[h] = p->Ph;
+    p->hAnnz[h] = p->nAh;
+    p->batches.assign(1, {0, h});
+  } else {
+    // Batch cuts need every heavy row's product prefix on the host.
+    int64_t* pref = alloc_n<int64_t>(p, h + 1, s);
+    p->hChat.assign(h + 1, 0);
+    p->hAnnz.assign(h + 1, 0);
+    launch_gather_i64(p->rowP, p->xheavy, h, hv, s);
+    launch_scan_i64(hv, h, pref, tmp, s);
+    HIP_CHECK(hipMemcpyAsync(p->hChat.data(), pref, sizeof(int64_t) * (h + 1),
+                             hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(p->hAnnz.data(), p->dAnnz, sizeof(int64_t) * (h + 1),
+                             hipMemcpyDeviceToHost, s));
+    check_launch("heavy batch cuts");
+    HIP_CHECK(hipStreamSynchronize(s));
+    maxNum = cut_batches(p, cap, &p->batches);
+  }
   const int64_t bytes = (int64_t)heavy_buf_bytes(p, maxNum, true);
   p->symVals = p->batches.size() == 1;
   p->st.batches = (int64_t)p->batches.size();
@@ -797,14 +812,18 @@ void heavy_prepare(spgemm_plan_t p) {
   if (structCounts) {
     const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, s);
     p->CH = alloc_n<int32_t>(p, h * nreq, s);
-    const WsMark mk = ws_mark(p);
     const int64_t nnzB = p->nnzB;
-    int32_t* flags = alloc_n<int32_t>(p, nnzB, s);
-    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, s);
-    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
+    // B's runs stay for the dense chunks taken straight from A and B.
     int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, s);
     int32_t* runChunk = alloc_n<int32_t>(p, nnzB, s);
     int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, s);
+    p->runPtr = runPtr;
+    p->runChunk = runChunk;
+    p->runStart = runStart;
+    const WsMark mk = ws_mark(p);
+    int32_t* flags = alloc_n<int32_t>(p, nnzB, s);
+    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, s);
+    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
     launch_b_runs(p->k, nnzB, p->brp, p->bcol, log2_exact(p->params.dense_width), flags, runIdx,
                   stmp, runPtr, runChunk, runStart, s);
     launch_chunk_hist_rows(h, p->xheavy, p->arp, p->acol, runPtr, runChunk, runStart,
@@ -972,15 +991,13 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
       ph_end(p, phM, s);
     }
     check_launch("multisplit level");
-    HIP_CHECK(hipMemcpyAsync(p->hBins + 100, ctr, 8, hipMemcpyDeviceToHost, s));
+    // nH, nL and the heavy chunks' element total newOff[nH], in one readback
+    int64_t* tail = alloc_n<int64_t>(p, 3, s);
+    launch_level_tail(ctr, newOff, tail, s);
+    HIP_CHECK(hipMemcpyAsync(p->hStats + 16, tail, 24, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
-    const int64_t nH = p->hBins[100], nL = p->hBins[101];
-    int64_t nextE = 0;
-    if (nH > 0) {
-      HIP_CHECK(hipMemcpyAsync(p->hStats + 16, newOff + nH, 8, hipMemcpyDeviceToHost, s));
-      HIP_CHECK(hipStreamSynchronize(s));
-      nextE = p->hStats[16];
-    }
+    const int64_t nH = p->hStats[16], nL = p->hStats[17];
+    const int64_t nextE = nH > 0 ? p->hStats[18] : 0;
     pieces.push_back(Piece{Q - nL, nL, newOff, newCnt, newRow, newSlot, (int8_t)out,
                            (int8_t)log2_exact(w / W)});
     if (last) completed = true;
@@ -1019,13 +1036,38 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     }
     B->lastFirst = completed ? nfc - pieces.back().n : nfc;
   }
+  // Numeric bins: W-wide chunks with more than W/8 elements (or tau, if
+  // smaller) go to the dense accumulator, at that density zeroing and
+  // scanning W columns is cheaper than hashing; the rest by element count.
+  uint8_t* key = alloc_n<uint8_t>(p, nfc, s);
+  B->fcOrder = alloc_n<int32_t>(p, nfc, s);
+  int32_t* bc = alloc_n<int32_t>(p, 64, s);
+  int32_t* bf = alloc_n<int32_t>(p, 64, s);
+  int32_t* bs = alloc_n<int32_t>(p, 65, s);
+  const int64_t denseMin = std::min<int64_t>(p->tau, W / 8);
+  launch_chunk_bins(nfc, B->fcCnt, B->lastFirst, denseMin, p->dSymCaps, p->NS, p->NS, key,
+                    countStats ? p->stats + kStatDenseElems : nullptr, s);
+  launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, B->fcOrder, s);
+  HIP_CHECK(hipMemcpyAsync(p->hBins + 64, bs, sizeof(int32_t) * (p->NS + 2), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipStreamSynchronize(s));
+  B->fcBinStart.assign(p->hBins + 64, p->hBins + 64 + p->NS + 2);
+  B->denseChunks = B->fcBinStart[p->NS + 1] - B->fcBinStart[p->NS];
   if (p->direct) {
     // Final chunks back to back in buffer 0, in list order; every product
     // goes straight to the final chunk covering its column.
     const int phX = ph_begin(p, vals ? SPGEMM_PH_EXPAND_FINAL : SPGEMM_PH_SYM_HEAVY, s);
+    // With values, dense chunks are accumulated straight from A and B: the
+    // expansion skips their products and they take no space.
+    B->denseDirect = vals && p->opts.dense_direct;
+    const int32_t* stored = B->fcCnt;
+    if (B->denseDirect) {
+      int32_t* sc = alloc_n<int32_t>(p, nfc, s);
+      launch_stored_counts(nfc, B->fcCnt, key, p->NS, sc, s);
+      stored = sc;
+    }
     int64_t* fcOff = alloc_n<int64_t>(p, nfc + 1, s);
     int64_t* ftmp = alloc_n<int64_t>(p, scan_tmp_elems(nfc) + 1, s);
-    launch_scan_i32(B->fcCnt, nfc, fcOff, ftmp, s);
+    launch_scan_i32(stored, nfc, fcOff, ftmp, s);
     B->fcOff = fcOff;
     launch_fill_i8(B->fcBuf, 0, nfc, s);
     const int64_t nslot = hb * p->nreq;
@@ -1033,7 +1075,8 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     int8_t* spanOf = alloc_n<int8_t>(p, nslot, s);
     launch_fill_i32(finalOf, -1, nslot, s);
     launch_fill_i8(spanOf, 0, nslot, s);
-    launch_final_map(nfc, B->fcRow, B->fcSlot, B->fcSpan, p->nreq, finalOf, spanOf, s);
+    launch_final_map(nfc, B->fcRow, B->fcSlot, B->fcSpan, p->nreq,
+                     B->denseDirect ? key : nullptr, p->NS, finalOf, spanOf, s);
     int64_t* fcCursor = alloc_n<int64_t>(p, nfc, s);
     launch_copy_i64(fcCursor, fcOff, nfc, s);
     int32_t blockElems = 0;
@@ -1053,22 +1096,6 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     ph_end(p, phX, s);
     check_launch("direct expansion");
   }
-  // Numeric bins: W-wide chunks with more than W/8 elements (or tau, if
-  // smaller) go to the dense accumulator, at that density zeroing and
-  // scanning W columns is cheaper than hashing; the rest by element count.
-  uint8_t* key = alloc_n<uint8_t>(p, nfc, s);
-  B->fcOrder = alloc_n<int32_t>(p, nfc, s);
-  int32_t* bc = alloc_n<int32_t>(p, 64, s);
-  int32_t* bf = alloc_n<int32_t>(p, 64, s);
-  int32_t* bs = alloc_n<int32_t>(p, 65, s);
-  const int64_t denseMin = std::min<int64_t>(p->tau, W / 8);
-  launch_chunk_bins(nfc, B->fcCnt, B->lastFirst, denseMin, p->dSymCaps, p->NS, p->NS, key,
-                    countStats ? p->stats + kStatDenseElems : nullptr, s);
-  launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, B->fcOrder, s);
-  HIP_CHECK(hipMemcpyAsync(p->hBins + 64, bs, sizeof(int32_t) * (p->NS + 2), hipMemcpyDeviceToHost, s));
-  HIP_CHECK(hipStreamSynchronize(s));
-  B->fcBinStart.assign(p->hBins + 64, p->hBins + 64 + p->NS + 2);
-  B->denseChunks = B->fcBinStart[p->NS + 1] - B->fcBinStart[p->NS];
 }
 
 ChunkList chunk_list(spgemm_plan_t p, const Batch& B) {
@@ -1142,7 +1169,12 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
   ph_end(p, ph, s);
   const int64_t st = B.fcBinStart[p->NS], en = B.fcBinStart[p->NS + 1];
   const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
-  launch_dense_num(p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, p->numCUs, s);
+  if (B.denseDirect)
+    launch_dense_num_direct(p->f64, desc + st, en - st, p->params.dense_width, row_args(p),
+                            BRuns{p->runPtr, p->runChunk, p->runStart}, ccol, cval, p->errWord,
+                            p->numCUs, s);
+  else
+    launch_dense_num(p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, p->numCUs, s);
   ph_end(p, phD, s);
   check_launch("chunk numeric");
 }
@@ -1164,7 +1196,9 @@ void heavy_symbolic(spgemm_plan_t p) {
   }
   p->st.final_chunks = 0;
   p->st.dense_chunks = 0;
-  if (p->symVals) {
+  if (p->symVals && !(p->direct && p->opts.dense_direct)) {
+    // One batch (gMAGNUS Algorithm 3): expand with values, count every final
+    // chunk, keep the chunks for numeric.
     Batch B;
     expand_batch(p, p->batches[0].first, p->batches[0].second, true, true, &B);
     symbolic_batch(p, B);
@@ -1176,12 +1210,26 @@ void heavy_symbolic(spgemm_plan_t p) {
     // numeric's descriptors, reserved now so that numeric allocates nothing
     p->keptDesc = alloc_n<ChunkDesc>(p, B.nfc, s);
   } else {
+    // Every heavy row's W-wide slots counted straight from A and B.
     const int ph = ph_begin(p, SPGEMM_PH_SYM_HEAVY, s);
     int32_t* next = alloc_n<int32_t>(p, 1, s);
     launch_fill_i32(next, 0, 1, s);
     launch_sym_heavy_rows(h, p->nreq, log2_exact(W), p->xheavy, row_args(p), p->nnzB,
                           p->slotNnz, next, p->numCUs, (size_t)p->lds, s);
     ph_end(p, ph, s);
+    if (p->symVals) {
+      // One batch with dense_direct: the light chunks' products are expanded
+      // now and kept for numeric (dense chunks are taken straight from A and
+      // B there), so numeric allocates nothing.
+      Batch B;
+      expand_batch(p, p->batches[0].first, p->batches[0].second, true, true, &B);
+      p->st.final_chunks += B.nfc;
+      p->st.dense_chunks += B.denseChunks;
+      for (int l = 0; l < 8; ++l) p->st.level_elems[l] += B.levelElems[l];
+      p->kept = B;
+      p->haveKept = true;
+      p->keptDesc = alloc_n<ChunkDesc>(p, B.nfc, s);
+    }
   }
   launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
   check_launch("heavy symbolic");

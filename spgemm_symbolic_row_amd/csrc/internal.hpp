@@ -113,6 +113,16 @@ struct ChunkDesc {
   int32_t want;     // distinct columns (from symbolic)
   int32_t colBase;  // global column of local column 0
   int32_t buf;      // buffer holding the elements (0 or 1)
+  int32_t row;      // row of C (and of A) the chunk belongs to
+};
+
+// Runs of B's rows in W-wide column slots (launch_b_runs): run q covers B
+// positions [start[q], start[q+1]), all in slot chunk[q]; the runs of B row
+// k are ptr[k] .. ptr[k+1]-1, in rising slot order.
+struct BRuns {
+  const int32_t* ptr;
+  const int32_t* chunk;
+  const int32_t* start;
 };
 
 // What a multisplit work group needs to know about its tile of elements.
@@ -123,6 +133,10 @@ struct TileInfo {
 };
 
 // ---- k_util.hip ----
+// dst[0..n) = vals[0..n) for n <= 64, the values passed as kernel arguments.
+void launch_set_small_i32(int32_t* dst, const int32_t* vals, int n, hipStream_t s);
+// tail[0..3) = (ctr[0], ctr[1], newOff[ctr[0]]).
+void launch_level_tail(const int32_t* ctr, const int64_t* newOff, int64_t* tail, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 void launch_fill_i64(int64_t* p, int64_t v, int64_t n, hipStream_t s);
 void launch_fill_i8(int8_t* p, int8_t v, int64_t n, hipStream_t s);
@@ -254,11 +268,16 @@ void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,
                             const int32_t* acol, const int32_t* runPtr, const int32_t* runChunk,
                             const int32_t* runStart, int32_t nreq, int32_t* CH, hipStream_t s);
 // finalOf[row * nreq + slot] = the final chunk covering W-wide slot `slot`
-// of batch row `row`, spanOf[...] = that chunk's width as log2 of W-wide
+// of batch row `row`, or -(chunk + 2) when key[chunk] == denseKey (a chunk
+// accumulated straight from A and B, whose products the expansion skips;
+// key may be null), spanOf[...] = that chunk's width as log2 of W-wide
 // slots (slots of no chunk are left as they are).
 void launch_final_map(int64_t nfc, const int32_t* fcRow, const int32_t* fcSlot,
-                      const int8_t* fcSpan, int64_t nreq, int32_t* finalOf, int8_t* spanOf,
-                      hipStream_t s);
+                      const int8_t* fcSpan, int64_t nreq, const uint8_t* key, int denseKey,
+                      int32_t* finalOf, int8_t* spanOf, hipStream_t s);
+// out[c] = key[c] == denseKey ? 0 : cnt[c].
+void launch_stored_counts(int64_t nfc, const int32_t* cnt, const uint8_t* key, int denseKey,
+                          int32_t* out, hipStream_t s);
 // One level's (row, chunk) counts as sums of `span` W-wide counts.
 void launch_level_counts(int64_t Q, int v, int32_t span, int32_t nreq, const int32_t* inRow,
                          const int32_t* inSlot, const int32_t* CH, int32_t* counts,
@@ -329,6 +348,11 @@ void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkLis
 void launch_chunk_desc(int64_t n, const int32_t* order, const ChunkList& cl,
                        const int64_t* cRowOff, ChunkDesc* desc, hipStream_t s);
 size_t dense_num_lds(bool f64, int64_t W);
+// Dense chunks (W-wide, one column slot of a heavy row each) accumulated
+// straight from A and B through B's slot runs; desc as for launch_dense_num.
+void launch_dense_num_direct(bool f64, const ChunkDesc* desc, int64_t n, int64_t W,
+                             const RowArgs& a, const BRuns& br, int32_t* ccol, void* cval,
+                             int32_t* err, int numCUs, hipStream_t s);
 // Per heavy row: exclusive scan of its nreq slot counts -> slotOff, and the
 // row total -> cnt[xheavy[r]].
 void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,

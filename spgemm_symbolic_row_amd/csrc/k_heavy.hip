@@ -192,6 +192,79 @@ __device__ __forceinline__ void dense_add_batch(V* vals, void* marks, const int3
   }
 }
 
+// Write-out of a dense chunk in column order, then the accumulator cleared
+// for the next chunk.  Wave w owns columns [w*W/16, (w+1)*W/16), lane l a
+// run of cpl of them; a wave scan of the lanes' popcounts gives every lane
+// its output offset, and each lane then writes its own entries in column
+// order, one per step (the wave's stores of a step fall in a short stretch
+// of the output).  A slot's value is cleared as it is read.  Called by the
+// whole work group after a barrier that ends the accumulation.
+template <typename V, bool kBytes>
+__device__ __forceinline__ void dense_write_out(V* vals, uint32_t* bm, int32_t* wtot, int W,
+                                                int32_t want, int64_t base, int32_t colBase,
+                                                int32_t* __restrict__ ccol, V* __restrict__ cval,
+                                                int32_t* __restrict__ err) {
+  constexpr int kWaves = kDenseNT / kWave;
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int nwords = (W + 31) / 32;
+  const int cpw = (W + kWaves - 1) / kWaves;        // columns per wave
+  const int cpl = cpw >= kWave ? cpw / kWave : 1;   // columns per lane, <= 32
+  const int lc0 = w * cpw + lane * cpl;             // this lane's first column
+  uint32_t mask = 0;
+  if (lc0 < W && lane * cpl < cpw) {
+    if constexpr (kBytes) {
+      // cpl is a power of two; from 4 on, lc0 is a multiple of 4.
+      const unsigned char* mk = (const unsigned char*)bm;
+      if (cpl >= 4) {
+        for (int k = 0; k < cpl; k += 4) {
+          const uint32_t wd = *(const uint32_t*)(mk + lc0 + k);
+          mask |= ((wd & 1u) | ((wd >> 7) & 2u) | ((wd >> 14) & 4u) | ((wd >> 21) & 8u)) << k;
+        }
+      } else {
+        for (int k = 0; k < cpl; ++k) mask |= (uint32_t)mk[lc0 + k] << k;
+      }
+    } else {
+      const uint32_t word = bm[lc0 >> 5];
+      mask = cpl >= 32 ? word : (word >> (lc0 & 31)) & ((1u << cpl) - 1u);
+    }
+  }
+  const int32_t cntL = __popc(mask);
+  const int32_t incL = wave_incl_scan(cntL);
+  const int32_t exclL = incL - cntL;
+  const int32_t nw = __shfl(incL, kWave - 1);
+  if (lane == 0) wtot[w] = nw;
+  __syncthreads();
+  int32_t wbase = 0, total = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    const int32_t t = wtot[i];
+    if (i < w) wbase += t;
+    total += t;
+  }
+  if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
+  uint32_t m = mask;
+  int32_t p = wbase + exclL;
+  while (__ballot(m != 0)) {
+    if (m) {
+      const int c = lc0 + __ffs(m) - 1;
+      m &= m - 1;
+      const V x = vals[c];
+      vals[c] = V(0);
+      if (p < want) {
+        ccol[base + p] = colBase + c;
+        cval[base + p] = x;
+      }
+      ++p;
+    }
+  }
+  __syncthreads();
+  if constexpr (kBytes) {
+    for (int i = threadIdx.x; i < W / 16; i += kDenseNT) ((uint4*)bm)[i] = uint4{0, 0, 0, 0};
+  } else {
+    for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
+  }
+  __syncthreads();
+}
+
 template <typename V, typename C, bool kBytes>
 __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restrict__ desc, int64_t n,
                                                         ChunkList cl,
@@ -199,7 +272,6 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
                                                         V* __restrict__ cval,
                                                         int32_t* __restrict__ err) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kWaves = kDenseNT / kWave;
   const int W = (int)cl.W;
   const int nwords = (W + 31) / 32;
   // kBytes: W is a power of two from 16 on and the marks take W bytes.
@@ -209,7 +281,6 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
   int32_t* wtot = (int32_t*)(bm + markWords);
   for (int i = threadIdx.x; i < W; i += kDenseNT) vals[i] = V(0);
   for (int i = threadIdx.x; i < markWords; i += kDenseNT) bm[i] = 0;
-  const int w = threadIdx.x / kWave, lane = lane_id();
 
   int64_t ci = blockIdx.x;
   int32_t cc[kDenseB];
@@ -243,69 +314,116 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
       val = (const V*)(d.buf ? cl.val1 : cl.val0);
       dense_load_batch(col, val, d.off + threadIdx.x, d.off + d.cnt, cc, vv);
     }
-    // Write-out in column order.  Wave w owns columns [w*W/16, (w+1)*W/16),
-    // lane l a run of cpl of them; a wave scan of the lanes' popcounts gives
-    // every lane its output offset, and each lane then writes its own
-    // entries in column order, one per step (the wave's stores of a step
-    // fall in a short stretch of the output).  The slot's value is cleared
-    // as it is read.
-    const int cpw = (W + kWaves - 1) / kWaves;        // columns per wave
-    const int cpl = cpw >= kWave ? cpw / kWave : 1;   // columns per lane, <= 32
-    const int lc0 = w * cpw + lane * cpl;             // this lane's first column
-    uint32_t mask = 0;
-    if (lc0 < W && lane * cpl < cpw) {
-      if constexpr (kBytes) {
-        // cpl is a power of two; from 4 on, lc0 is a multiple of 4.
-        const unsigned char* mk = (const unsigned char*)bm;
-        if (cpl >= 4) {
-          for (int k = 0; k < cpl; k += 4) {
-            const uint32_t wd = *(const uint32_t*)(mk + lc0 + k);
-            mask |= ((wd & 1u) | ((wd >> 7) & 2u) | ((wd >> 14) & 4u) | ((wd >> 21) & 8u)) << k;
-          }
-        } else {
-          for (int k = 0; k < cpl; ++k) mask |= (uint32_t)mk[lc0 + k] << k;
-        }
-      } else {
-        const uint32_t word = bm[lc0 >> 5];
-        mask = cpl >= 32 ? word : (word >> (lc0 & 31)) & ((1u << cpl) - 1u);
-      }
-    }
-    const int32_t cntL = __popc(mask);
-    const int32_t incL = wave_incl_scan(cntL);
-    const int32_t exclL = incL - cntL;
-    const int32_t nw = __shfl(incL, kWave - 1);
-    if (lane == 0) wtot[w] = nw;
-    __syncthreads();
-    int32_t wbase = 0, total = 0;
-    for (int i = 0; i < kWaves; ++i) {
-      const int32_t t = wtot[i];
-      if (i < w) wbase += t;
-      total += t;
-    }
-    if (threadIdx.x == 0 && want != total) flag_error(err, kErrCountMismatch);
-    uint32_t m = mask;
-    int32_t p = wbase + exclL;
-    while (__ballot(m != 0)) {
-      if (m) {
-        const int c = lc0 + __ffs(m) - 1;
-        m &= m - 1;
-        const V x = vals[c];
-        vals[c] = V(0);
-        if (p < want) {
-          ccol[base + p] = colBase + c;
-          cval[base + p] = x;
-        }
-        ++p;
-      }
-    }
-    __syncthreads();
-    if constexpr (kBytes) {
-      for (int i = threadIdx.x; i < W / 16; i += kDenseNT) ((uint4*)bm)[i] = uint4{0, 0, 0, 0};
-    } else {
-      for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
-    }
-    __syncthreads();
+    dense_write_out<V, kBytes>(vals, bm, wtot, W, want, base, colBase, ccol, cval, err);
     ci = cn;
+  }
+}
+
+// Dense chunks accumulated straight from A and B.  A dense chunk is one
+// W-wide column slot s of a heavy row i; its elements are the products
+// A[i,k] * B[k,j] with j in the slot, i.e. for every entry k of A's row i
+// the run of B's row k inside the slot (B's rows are sorted, so the run is
+// contiguous; the runs of every B row in W-wide slots are listed once, in
+// rising slot order).  The waves of a work group share the row's entries
+// (each wave every 16th one); every lane finds its entry's run by a binary
+// search over its B row's runs, and the wave then streams the runs' products as one sequence, 64
+// lanes wide, each lane finding its run by a search across the lanes'
+// offsets, with four rounds of loads in flight before the LDS adds.  B's rows are read from the caches
+// instead of a materialised intermediate.  Persistent work groups, write-out
+// and clearing as in k_dense_num.
+constexpr int kDirectU = 4;  // runs of 64 products whose loads are in flight together
+template <typename V, bool kBytes>
+__global__ __launch_bounds__(kDenseNT) void k_dense_num_direct(const ChunkDesc* __restrict__ desc,
+                                                               int64_t n, RowArgs a, BRuns br,
+                                                               int log2W,
+                                                               int32_t* __restrict__ ccol,
+                                                               V* __restrict__ cval,
+                                                               int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kWaves = kDenseNT / kWave;
+  const int W = 1 << log2W;
+  const int nwords = (W + 31) / 32;
+  const int markWords = kBytes ? W / 4 : nwords;
+  V* vals = (V*)smem;
+  uint32_t* bm = (uint32_t*)(vals + W);
+  int32_t* wtot = (int32_t*)(bm + markWords);
+  for (int i = threadIdx.x; i < W; i += kDenseNT) vals[i] = V(0);
+  for (int i = threadIdx.x; i < markWords; i += kDenseNT) bm[i] = 0;
+  __syncthreads();
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const V* __restrict__ aval = (const V*)a.aval;
+  const V* __restrict__ bval = (const V*)a.bval;
+  const int32_t* __restrict__ bcol = a.bcol;
+  for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
+    const ChunkDesc d = desc[ci];
+    const int32_t slot = d.colBase >> log2W;
+    const int64_t rs = a.arp[d.row], re = a.arp[d.row + 1];
+    // Rounds of kWaves * 64 entries; wave w takes every kWaves-th entry of a
+    // round, so the waves share the row's runs evenly even when the row has
+    // few entries.
+    for (int64_t e0 = rs; e0 < re; e0 += (int64_t)kWaves * kWave) {
+      const int64_t e = e0 + (int64_t)lane * kWaves + w;
+      int32_t b0 = 0, len = 0;
+      V av = V(0);
+      if (e < re) {
+        const int32_t k = a.acol[e];
+        av = aval[e];
+        const int32_t q1 = br.ptr[k + 1];
+        int32_t lo = br.ptr[k], hi = q1;
+        while (lo < hi) {
+          const int32_t mid = (lo + hi) >> 1;
+          if (br.chunk[mid] < slot) lo = mid + 1;
+          else hi = mid;
+        }
+        if (lo < q1 && br.chunk[lo] == slot) {
+          b0 = br.start[lo];
+          len = br.start[lo + 1] - b0;
+        }
+      }
+      // The 64 runs' products as one sequence: product q belongs to the
+      // last lane whose exclusive offset is <= q (lanes with empty runs
+      // share the next lane's offset, so the last one has products).
+      const int32_t inc = wave_incl_scan(len);
+      const int32_t off = inc - len;
+      const int32_t total = __shfl(inc, kWave - 1);
+      for (int32_t p = 0; p < total; p += kWave * kDirectU) {
+        int32_t cc[kDirectU];
+        V vv[kDirectU];
+#pragma unroll
+        for (int u = 0; u < kDirectU; ++u) {
+          const int32_t q = p + u * kWave + lane;
+          cc[u] = -1;
+          vv[u] = V(0);
+          if (p + u * kWave < total) {  // the same for every lane
+            int s = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1)
+              if (__shfl(off, s + step) <= q) s += step;
+            const int32_t bi = __shfl(b0, s) + (q - __shfl(off, s));
+            const V at = __shfl(av, s);
+            if (q < total) {
+              cc[u] = bcol[bi] - (slot << log2W);
+              vv[u] = at * bval[bi];
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kDirectU; ++u) {
+          const int32_t c = cc[u];
+          if (c >= 0) {
+            atomicAdd(&vals[c], vv[u]);
+            if constexpr (kBytes) {
+              ((unsigned char*)bm)[c] = 1;
+            } else {
+              const uint32_t bit = 1u << (c & 31);
+              if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    dense_write_out<V, kBytes>(vals, bm, wtot, W, d.want, d.base, d.colBase, ccol, cval, err);
   }
 }
 
@@ -330,6 +448,7 @@ __global__ __launch_bounds__(kNT) void k_chunk_desc(int64_t n, const int32_t* __
   }
   d.want = want;
   d.colBase = (int32_t)((int64_t)cl.slot[item] * cl.W);
+  d.row = cl.xheavy[hr];
   d.buf = cl.buf[item];
   desc[i] = d;
 }
@@ -354,19 +473,32 @@ __global__ __launch_bounds__(kNT) void k_slot_scan(int64_t h, int64_t nreq,
 }
 
 // finalOf / spanOf over the W-wide slots of every final chunk.
+// finalOf of a chunk accumulated straight from A and B (key == denseKey)
+// is -(c + 2): the expansion skips its products.
 __global__ __launch_bounds__(kNT) void k_final_map(int64_t nfc, const int32_t* __restrict__ fcRow,
                                                    const int32_t* __restrict__ fcSlot,
                                                    const int8_t* __restrict__ fcSpan, int64_t nreq,
+                                                   const uint8_t* __restrict__ key, int denseKey,
                                                    int32_t* __restrict__ finalOf,
                                                    int8_t* __restrict__ spanOf) {
   const int64_t c = (int64_t)blockIdx.x * kNT + threadIdx.x;
   if (c >= nfc) return;
   const int64_t q = (int64_t)fcRow[c] * nreq + fcSlot[c];
   const int8_t sp = fcSpan[c];
+  const int32_t f = (key && key[c] == denseKey) ? -(int32_t)c - 2 : (int32_t)c;
   for (int s = 0; s < (1 << sp); ++s) {
-    finalOf[q + s] = (int32_t)c;
+    finalOf[q + s] = f;
     spanOf[q + s] = sp;
   }
+}
+
+// Element counts of the chunks the expansion writes: 0 for the chunks taken
+// straight from A and B.
+__global__ __launch_bounds__(kNT) void k_stored_counts(int64_t nfc, const int32_t* __restrict__ cnt,
+                                                       const uint8_t* __restrict__ key,
+                                                       int denseKey, int32_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (c < nfc) out[c] = key[c] == denseKey ? 0 : cnt[c];
 }
 
 }  // namespace
@@ -381,6 +513,10 @@ void heavy_set_attributes() {
   SG_ATTR((k_dense_num<double, int32_t, true>));
   SG_ATTR((k_dense_num<float, uint16_t, true>));
   SG_ATTR((k_dense_num<double, uint16_t, true>));
+  SG_ATTR((k_dense_num_direct<double, true>));
+  SG_ATTR((k_dense_num_direct<double, false>));
+  SG_ATTR((k_dense_num_direct<float, true>));
+  SG_ATTR((k_dense_num_direct<float, false>));
   SG_ATTR(k_dense_sym<int32_t>);
   SG_ATTR(k_dense_sym<uint16_t>);
 #undef SG_ATTR
@@ -396,11 +532,18 @@ void launch_partition(int64_t Q, const int32_t* counts, int64_t tau, bool last, 
 }
 
 void launch_final_map(int64_t nfc, const int32_t* fcRow, const int32_t* fcSlot,
-                      const int8_t* fcSpan, int64_t nreq, int32_t* finalOf, int8_t* spanOf,
-                      hipStream_t s) {
+                      const int8_t* fcSpan, int64_t nreq, const uint8_t* key, int denseKey,
+                      int32_t* finalOf, int8_t* spanOf, hipStream_t s) {
   if (nfc <= 0) return;
   hipLaunchKernelGGL(k_final_map, dim3(grid_for(nfc, kNT)), dim3(kNT), 0, s, nfc, fcRow, fcSlot,
-                     fcSpan, nreq, finalOf, spanOf);
+                     fcSpan, nreq, key, denseKey, finalOf, spanOf);
+}
+
+void launch_stored_counts(int64_t nfc, const int32_t* cnt, const uint8_t* key, int denseKey,
+                          int32_t* out, hipStream_t s) {
+  if (nfc <= 0) return;
+  hipLaunchKernelGGL(k_stored_counts, dim3(grid_for(nfc, kNT)), dim3(kNT), 0, s, nfc, cnt, key,
+                     denseKey, out);
 }
 
 void launch_final_from_level(int64_t first, int64_t n, const int64_t* newOff,
@@ -481,6 +624,26 @@ void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkLis
   else if (f64) L(double, int32_t);
   else if (cl.col16) L(float, uint16_t);
   else L(float, int32_t);
+#undef L
+}
+
+void launch_dense_num_direct(bool f64, const ChunkDesc* desc, int64_t n, int64_t W,
+                             const RowArgs& a, const BRuns& br, int32_t* ccol, void* cval,
+                             int32_t* err, int numCUs, hipStream_t s) {
+  if (n <= 0) return;
+  const size_t lds = dense_num_lds(f64, W);
+  const bool bytes = dense_byte_marks(f64, W);
+  const int64_t perCU = std::max<int64_t>(1, (int64_t)163840 / (int64_t)lds);
+  const unsigned g = (unsigned)std::min<int64_t>(n, std::max(numCUs, 1) * perCU);
+  int log2W = 0;
+  while ((int64_t(1) << log2W) < W) ++log2W;
+#define L(V, B)                                                                           \
+  hipLaunchKernelGGL((k_dense_num_direct<V, B>), dim3(g), dim3(kDenseNT), lds, s, desc, n, a, \
+                     br, log2W, ccol, (V*)cval, err)
+  if (f64 && bytes) L(double, true);
+  else if (f64) L(double, false);
+  else if (bytes) L(float, true);
+  else L(float, false);
 #undef L
 }
 

@@ -550,18 +550,18 @@ __global__ __launch_bounds__(kNT) void k_expand_final(int64_t E, int32_t blockEl
     int64_t g = 0;
     if (c) {
       const int32_t q = finS[b];
-      if (q < 0) {
+      if (q == -1) {
         flag_error(err, kErrCountMismatch);
-      } else {
+      } else if (q >= 0) {
         g = (int64_t)atomicAdd((unsigned long long*)&cursor[q], (unsigned long long)c);
-      }
+      }  // q <= -2: a chunk taken straight from A and B, nothing written
     }
     gbase[b] = g;
   }
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
-    if (bb[it] >= 0) {
+    if (bb[it] >= 0 && finS[bb[it]] >= 0) {
       const int64_t dest = gbase[bb[it]] + rank[it];
       if (dest < E) {
         outCol[dest] = (OC)cc[it];

@@ -538,7 +538,35 @@ __global__ __launch_bounds__(kNT) void k_numeric_row_bins(int64_t m, const int64
   key[i] = (uint8_t)b;
 }
 
+struct SmallI32 {
+  int32_t v[64];
+};
+__global__ void k_set_small(int32_t* __restrict__ dst, SmallI32 vals, int n) {
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = vals.v[threadIdx.x];
+}
+
+// tail = (ctr[0], ctr[1], newOff[ctr[0]]): a multisplit level's heavy and
+// light chunk counts and the heavy chunks' element total.
+__global__ void k_level_tail(const int32_t* __restrict__ ctr, const int64_t* __restrict__ newOff,
+                             int64_t* __restrict__ tail) {
+  if (threadIdx.x == 0) {
+    tail[0] = ctr[0];
+    tail[1] = ctr[1];
+    tail[2] = newOff[ctr[0]];
+  }
+}
+
 }  // namespace
+
+void launch_set_small_i32(int32_t* dst, const int32_t* vals, int n, hipStream_t s) {
+  if (n <= 0) return;
+  SmallI32 sv{};
+  for (int i = 0; i < n && i < 64; ++i) sv.v[i] = vals[i];
+  hipLaunchKernelGGL(k_set_small, dim3(1), dim3(64), 0, s, dst, sv, n < 64 ? n : 64);
+}
+void launch_level_tail(const int32_t* ctr, const int64_t* newOff, int64_t* tail, hipStream_t s) {
+  hipLaunchKernelGGL(k_level_tail, dim3(1), dim3(64), 0, s, ctr, newOff, tail);
+}
 
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return;

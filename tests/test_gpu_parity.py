@@ -205,14 +205,15 @@ def test_rmat14_default_parameters():
     assert st["params"]["tau"] == 6826
 
 
+@pytest.mark.parametrize("direct", [0, 1], ids=["expanded", "dense_direct"])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
-def test_default_width_dense_chunks(dtype):
+def test_default_width_dense_chunks(dtype, direct):
     # The default chunk width (16384 for fp64, 32768 for fp32) with chunks
     # above a lowered tau, so the dense chunk kernels run at full width:
     # fp64 marks columns with bytes, fp32 with bits (bytes would not fit
     # beside the 128 KiB accumulator).
     A = synth.rmat(15, 16, seed=12, dtype=dtype)
-    st = check_full(A, A, heavy_threshold=512)
+    st = check_full(A, A, heavy_threshold=512, dense_direct=direct)
     assert st["heavy_rows"] > 0
     assert st["params"]["dense_width"] == (16384 if dtype == np.float64 else 32768)
 
@@ -226,6 +227,9 @@ def test_options_do_not_change_the_result():
                  dict(heavy_threshold=100, dense_width=512, max_chunks_per_level=2),
                  dict(heavy_threshold=100, heavy_row_threshold=20, dense_width=512),
                  dict(heavy_row_threshold=1),
+                 dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, dense_direct=1),
+                 dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, dense_direct=1,
+                      mem_budget=100_000),
                  dict()):
         rp, col, val, _ = gpu_product(A, A, **opts)
         np.testing.assert_array_equal(rp, ref[0])
