@@ -331,6 +331,10 @@ def main():
     ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
+    ap.add_argument("--heavy-row-threshold", type=int, default=0,
+                    help="override the light/heavy row split (tuning)")
+    ap.add_argument("--mem-budget", type=int, default=0,
+                    help="bytes for the heavy intermediate (tuning; 0 = the library's)")
     ap.add_argument("--workflow", type=int, default=-1,
                     help="light-row size prediction: 0 symbolic, 1 upper bound, 2 HyperLogLog, "
                          "3 Table 1 choice (default: the library's)")
@@ -389,6 +393,10 @@ def main():
         opts["lds_budget"] = args.lds_budget
     if args.heavy_threshold:
         opts["heavy_threshold"] = args.heavy_threshold
+    if args.heavy_row_threshold:
+        opts["heavy_row_threshold"] = args.heavy_row_threshold
+    if args.mem_budget:
+        opts["mem_budget"] = args.mem_budget
     if args.expansion >= 0:
         opts["expansion"] = args.expansion
     if args.light_hash_only:
