@@ -139,7 +139,7 @@ void make_rank_bins(int64_t lds, bool f64, int32_t words, const std::vector<BinC
 // first use and kept for the life of the process: workspace freed on a side
 // stream is then reused by the next product's allocations on it.
 struct SideStreams {
-  hipStream_t sl = nullptr, sh = nullptr;
+  hipStream_t sl = nullptr, sh = nullptr, sd = nullptr;
 };
 SideStreams side_streams(int device) {
   static SideStreams pool[64];
@@ -147,6 +147,7 @@ SideStreams side_streams(int device) {
   if (!ss.sl) {
     HIP_CHECK(hipStreamCreateWithFlags(&ss.sl, hipStreamNonBlocking));
     HIP_CHECK(hipStreamCreateWithFlags(&ss.sh, hipStreamNonBlocking));
+    HIP_CHECK(hipStreamCreateWithFlags(&ss.sd, hipStreamNonBlocking));
   }
   return ss;
 }
@@ -236,7 +237,8 @@ struct spgemm_plan_s {
   bool f64 = true;
   spgemm_options opts{};
   hipStream_t stream = nullptr, sl = nullptr, sh = nullptr;
-  hipEvent_t evFork = nullptr, evL = nullptr, evH = nullptr;
+  hipStream_t sd = nullptr;  // dense chunks, beside the light chunks on sh
+  hipEvent_t evFork = nullptr, evL = nullptr, evH = nullptr, evD0 = nullptr, evD1 = nullptr;
   int device = 0;
   int64_t lds = 0, tau = 0, rowTau = 0;  // chunk and row heavy thresholds
   int numCUs = 0;
@@ -608,11 +610,14 @@ void do_plan(spgemm_plan_t p) {
   }
 
   if (p->opts.single_stream) {
-    p->sl = p->sh = p->stream;
+    p->sl = p->sh = p->sd = p->stream;
   } else {
     const SideStreams ss = side_streams(p->device);
     p->sl = ss.sl;
     p->sh = ss.sh;
+    p->sd = ss.sd;
+    HIP_CHECK(hipEventCreateWithFlags(&p->evD0, hipEventDisableTiming));
+    HIP_CHECK(hipEventCreateWithFlags(&p->evD1, hipEventDisableTiming));
     HIP_CHECK(hipEventCreateWithFlags(&p->evFork, hipEventDisableTiming));
     HIP_CHECK(hipEventCreateWithFlags(&p->evL, hipEventDisableTiming));
     HIP_CHECK(hipEventCreateWithFlags(&p->evH, hipEventDisableTiming));
@@ -1154,6 +1159,26 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
   // reserved by symbolic for the kept batch).
   if (!desc) desc = alloc_n<ChunkDesc>(p, B.nfc, s);
   launch_chunk_desc(B.nfc, B.fcOrder, cl, p->cRowOff, desc, s);
+  // Dense chunks on their own stream, launched first (one persistent work
+  // group per CU), while the light chunks' kernels fill the rest of the
+  // device from the heavy stream; the heavy stream waits for both.
+  hipStream_t sd = p->sd;
+  if (sd != s) {
+    HIP_CHECK(hipEventRecord(p->evD0, s));
+    HIP_CHECK(hipStreamWaitEvent(sd, p->evD0, 0));
+  }
+  {
+    const int64_t st = B.fcBinStart[p->NS], en = B.fcBinStart[p->NS + 1];
+    const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, sd);
+    if (B.denseDirect)
+      launch_dense_num_direct(p->f64, desc + st, en - st, p->params.dense_width, row_args(p),
+                              BRuns{p->runPtr, p->runChunk, p->runStart}, ccol, cval,
+                              p->errWord, p->numCUs, sd);
+    else
+      launch_dense_num(p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, p->numCUs, sd);
+    ph_end(p, phD, sd);
+    if (sd != s) HIP_CHECK(hipEventRecord(p->evD1, sd));
+  }
   const int ph = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = B.fcBinStart[b], en = B.fcBinStart[b + 1];
@@ -1167,15 +1192,7 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
       launch_num_chunks(p->numBins[b], p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, s);
   }
   ph_end(p, ph, s);
-  const int64_t st = B.fcBinStart[p->NS], en = B.fcBinStart[p->NS + 1];
-  const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, s);
-  if (B.denseDirect)
-    launch_dense_num_direct(p->f64, desc + st, en - st, p->params.dense_width, row_args(p),
-                            BRuns{p->runPtr, p->runChunk, p->runStart}, ccol, cval, p->errWord,
-                            p->numCUs, s);
-  else
-    launch_dense_num(p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, p->numCUs, s);
-  ph_end(p, phD, s);
+  if (s != p->sd) HIP_CHECK(hipStreamWaitEvent(s, p->evD1, 0));
   check_launch("chunk numeric");
 }
 
@@ -1553,6 +1570,8 @@ void destroy_plan(spgemm_plan_t p) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
   }
+  if (p->evD0) (void)hipEventDestroy(p->evD0);
+  if (p->evD1) (void)hipEventDestroy(p->evD1);
   if (p->evFork) (void)hipEventDestroy(p->evFork);
   if (p->evL) (void)hipEventDestroy(p->evL);
   if (p->evH) (void)hipEventDestroy(p->evH);
