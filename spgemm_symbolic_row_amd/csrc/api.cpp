@@ -280,6 +280,10 @@ struct spgemm_plan_s {
   size_t wsCur = 0;      // workspace bytes currently held
   int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
   const int32_t *runPtr = nullptr, *runChunk = nullptr, *runStart = nullptr;  // B's slot runs
+  // Dense chunks accumulated straight from A and B (option dense_direct),
+  // with B's slot table: (nreq + 1) run starts per B row.
+  bool useDD = false;
+  const int32_t* slotTab = nullptr;
   int64_t* dAnnz = nullptr; // scan of the heavy rows' A lengths (h + 1)
   bool fused = false;    // the first level is fed straight from A and B
   bool direct = false;   // one pass straight into the final chunks
@@ -835,6 +839,16 @@ void heavy_prepare(spgemm_plan_t p) {
                            (int32_t)nreq, p->CH, s);
     check_launch("chunk histogram");
     ws_reset(p, mk, s);
+    // The slot table for dense chunks taken straight from A and B, when it
+    // takes at most 1 GiB (else those chunks are expanded as usual).
+    const int64_t tabBytes = (p->k * (nreq + 1)) * 4;
+    if (p->opts.dense_direct && p->direct && tabBytes <= ((int64_t)1 << 30)) {
+      int32_t* tab = alloc_n<int32_t>(p, p->k * (nreq + 1), s);
+      launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, s);
+      check_launch("slot table");
+      p->slotTab = tab;
+      p->useDD = true;
+    }
     ph_end(p, ph, s);
   }
 }
@@ -1063,7 +1077,7 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     const int phX = ph_begin(p, vals ? SPGEMM_PH_EXPAND_FINAL : SPGEMM_PH_SYM_HEAVY, s);
     // With values, dense chunks are accumulated straight from A and B: the
     // expansion skips their products and they take no space.
-    B->denseDirect = vals && p->opts.dense_direct;
+    B->denseDirect = vals && p->useDD;
     const int32_t* stored = B->fcCnt;
     if (B->denseDirect) {
       int32_t* sc = alloc_n<int32_t>(p, nfc, s);
@@ -1172,7 +1186,7 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
     const int phD = ph_begin(p, SPGEMM_PH_NUM_CHUNK_DENSE, sd);
     if (B.denseDirect)
       launch_dense_num_direct(p->f64, desc + st, en - st, p->params.dense_width, row_args(p),
-                              BRuns{p->runPtr, p->runChunk, p->runStart}, ccol, cval,
+                              p->slotTab, p->nreq + 1, p->nnzB, ccol, cval,
                               p->errWord, p->numCUs, sd);
     else
       launch_dense_num(p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, p->numCUs, sd);
@@ -1213,7 +1227,7 @@ void heavy_symbolic(spgemm_plan_t p) {
   }
   p->st.final_chunks = 0;
   p->st.dense_chunks = 0;
-  if (p->symVals && !(p->direct && p->opts.dense_direct)) {
+  if (p->symVals && !p->useDD) {
     // One batch (gMAGNUS Algorithm 3): expand with values, count every final
     // chunk, keep the chunks for numeric.
     Batch B;

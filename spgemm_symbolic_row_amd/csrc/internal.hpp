@@ -116,14 +116,6 @@ struct ChunkDesc {
   int32_t row;      // row of C (and of A) the chunk belongs to
 };
 
-// Runs of B's rows in W-wide column slots (launch_b_runs): run q covers B
-// positions [start[q], start[q+1]), all in slot chunk[q]; the runs of B row
-// k are ptr[k] .. ptr[k+1]-1, in rising slot order.
-struct BRuns {
-  const int32_t* ptr;
-  const int32_t* chunk;
-  const int32_t* start;
-};
 
 // What a multisplit work group needs to know about its tile of elements.
 struct TileInfo {
@@ -264,6 +256,10 @@ void launch_b_runs(int64_t K, int64_t nnzB, const int32_t* brp, const int32_t* b
                    int32_t* flags, int64_t* runIdx, int64_t* scanTmp, int32_t* runPtr,
                    int32_t* runChunk, int32_t* runStart, hipStream_t s);
 // CH[i][f] = products of row rows[i] in W-wide chunk f (nreq <= 16384).
+// B's slot table (k_slot_table): (nreq + 1) run starts per B row.
+void launch_slot_table(int64_t K, int32_t nreq, const int32_t* brp, const int32_t* runPtr,
+                       const int32_t* runChunk, const int32_t* runStart, int32_t* tab,
+                       hipStream_t s);
 void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,
                             const int32_t* acol, const int32_t* runPtr, const int32_t* runChunk,
                             const int32_t* runStart, int32_t nreq, int32_t* CH, hipStream_t s);
@@ -351,8 +347,9 @@ size_t dense_num_lds(bool f64, int64_t W);
 // Dense chunks (W-wide, one column slot of a heavy row each) accumulated
 // straight from A and B through B's slot runs; desc as for launch_dense_num.
 void launch_dense_num_direct(bool f64, const ChunkDesc* desc, int64_t n, int64_t W,
-                             const RowArgs& a, const BRuns& br, int32_t* ccol, void* cval,
-                             int32_t* err, int numCUs, hipStream_t s);
+                             const RowArgs& a, const int32_t* slotTab, int64_t stride,
+                             int64_t nnzB, int32_t* ccol, void* cval, int32_t* err, int numCUs,
+                             hipStream_t s);
 // Per heavy row: exclusive scan of its nreq slot counts -> slotOff, and the
 // row total -> cnt[xheavy[r]].
 void launch_slot_scan(int64_t h, int64_t nreq, const int32_t* slotNnz, int64_t* slotOff,

@@ -68,6 +68,30 @@ __global__ __launch_bounds__(kNT) void k_run_row_ptr(int64_t K, int64_t nnz,
   if (k == K) runStart[runIdx[nnz]] = (int32_t)nnz;
 }
 
+// B's slot table from its runs: tab[k * (nreq + 1) + f] = first position of
+// B row k whose column lies in slot f or later (the row's end when none
+// does), for f in [0, nreq].  One thread per B row writes its nreq + 1
+// cells once each, in rising slot order.
+__global__ __launch_bounds__(kNT) void k_slot_table(int64_t K, int32_t nreq,
+                                                    const int32_t* __restrict__ rp,
+                                                    const int32_t* __restrict__ runPtr,
+                                                    const int32_t* __restrict__ runChunk,
+                                                    const int32_t* __restrict__ runStart,
+                                                    int32_t* __restrict__ tab) {
+  const int64_t k = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (k >= K) return;
+  int32_t* t = tab + k * (int64_t)(nreq + 1);
+  int32_t f = 0;
+  const int32_t q1 = runPtr[k + 1];
+  for (int32_t q = runPtr[k]; q < q1; ++q) {
+    const int32_t c = min(runChunk[q], nreq - 1);
+    const int32_t pos = runStart[q];
+    for (; f <= c; ++f) t[f] = pos;
+  }
+  const int32_t end = rp[k + 1];
+  for (; f <= nreq; ++f) t[f] = end;
+}
+
 // One work group per heavy row: LDS counters for the n_req chunks.
 __global__ __launch_bounds__(kNT) void k_chunk_hist_rows(const int32_t* __restrict__ rows,
                                                          const int32_t* __restrict__ arp,
@@ -134,6 +158,14 @@ void launch_b_runs(int64_t K, int64_t nnzB, const int32_t* brp, const int32_t* b
                        shift, flags, runIdx, runChunk, runStart);
   hipLaunchKernelGGL(k_run_row_ptr, dim3(grid_for(K + 1, kNT, 1u << 30)), dim3(kNT), 0, s, K,
                      nnzB, brp, runIdx, runPtr, runStart);
+}
+
+void launch_slot_table(int64_t K, int32_t nreq, const int32_t* brp, const int32_t* runPtr,
+                       const int32_t* runChunk, const int32_t* runStart, int32_t* tab,
+                       hipStream_t s) {
+  if (K <= 0) return;
+  hipLaunchKernelGGL(k_slot_table, dim3(grid_for(K, kNT, 1u << 30)), dim3(kNT), 0, s, K, nreq, brp,
+                     runPtr, runChunk, runStart, tab);
 }
 
 void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,

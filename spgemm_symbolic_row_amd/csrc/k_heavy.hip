@@ -323,18 +323,58 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
 // W-wide column slot s of a heavy row i; its elements are the products
 // A[i,k] * B[k,j] with j in the slot, i.e. for every entry k of A's row i
 // the run of B's row k inside the slot (B's rows are sorted, so the run is
-// contiguous; the runs of every B row in W-wide slots are listed once, in
-// rising slot order).  The waves of a work group share the row's entries
-// (each wave every 16th one); every lane finds its entry's run by a binary
-// search over its B row's runs, and the wave then streams the runs' products as one sequence, 64
-// lanes wide, each lane finding its run by a search across the lanes'
-// offsets, with four rounds of loads in flight before the LDS adds.  B's rows are read from the caches
-// instead of a materialised intermediate.  Persistent work groups, write-out
-// and clearing as in k_dense_num.
-constexpr int kDirectU = 4;  // runs of 64 products whose loads are in flight together
+// contiguous).  B's slot table gives the run at once: tab[k * stride + s] is
+// the first position of B row k whose column is at least s * W, so the run
+// is [tab[k*stride+s], tab[k*stride+s+1]).  The waves of a work group share
+// the row's entries (each wave every 16th one, a lane per entry).  Runs of
+// at least kLong products are streamed by the whole wave, 64 products a
+// piece, kLongU pieces in flight: the pieces of a round's long runs are
+// numbered by a scan of their counts, and a piece finds its run from one
+// ballot, with the run's start, length and a_ik read from that lane (no
+// per-product search).  The shorter runs of the round are streamed as one
+// sequence, each lane finding its run by a search across the lanes'
+// offsets.  B's rows are read from the caches instead of a materialised
+// intermediate.  Persistent work groups, write-out and clearing as in
+// k_dense_num.
+constexpr int kDirectU = 4;  // short-run pieces of 64 products in flight together
+constexpr int kLongU = 4;    // long-run pieces in flight together
+constexpr int kLong = 32;    // runs of at least this many products go whole-wave
+
+__device__ __forceinline__ int32_t lane_read(int32_t x, int j) {
+  return __builtin_amdgcn_readlane(x, j);
+}
+__device__ __forceinline__ double lane_read(double x, int j) {
+  const int64_t b = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)b, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(b >> 32), j);
+  return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float lane_read(float x, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+
+template <typename V, bool kBytes>
+__device__ __forceinline__ void direct_add(V* vals, uint32_t* bm, int32_t c, V v, int W,
+                                           int32_t* __restrict__ err) {
+  if (c < 0) return;
+  if (c >= W) {  // a column outside the slot: B is not canonical
+    flag_error(err, kErrCsr);
+    return;
+  }
+  atomicAdd(&vals[c], v);
+  if constexpr (kBytes) {
+    ((unsigned char*)bm)[c] = 1;
+  } else {
+    const uint32_t bit = 1u << (c & 31);
+    if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
+  }
+}
+
 template <typename V, bool kBytes>
 __global__ __launch_bounds__(kDenseNT) void k_dense_num_direct(const ChunkDesc* __restrict__ desc,
-                                                               int64_t n, RowArgs a, BRuns br,
+                                                               int64_t n, RowArgs a,
+                                                               const int32_t* __restrict__ tab,
+                                                               int64_t stride, int64_t nnzB,
                                                                int log2W,
                                                                int32_t* __restrict__ ccol,
                                                                V* __restrict__ cval,
@@ -357,10 +397,8 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num_direct(const ChunkDesc* 
   for (int64_t ci = blockIdx.x; ci < n; ci += gridDim.x) {
     const ChunkDesc d = desc[ci];
     const int32_t slot = d.colBase >> log2W;
+    const int32_t colBase = d.colBase;
     const int64_t rs = a.arp[d.row], re = a.arp[d.row + 1];
-    // Rounds of kWaves * 64 entries; wave w takes every kWaves-th entry of a
-    // round, so the waves share the row's runs evenly even when the row has
-    // few entries.
     for (int64_t e0 = rs; e0 < re; e0 += (int64_t)kWaves * kWave) {
       const int64_t e = e0 + (int64_t)lane * kWaves + w;
       int32_t b0 = 0, len = 0;
@@ -368,24 +406,50 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num_direct(const ChunkDesc* 
       if (e < re) {
         const int32_t k = a.acol[e];
         av = aval[e];
-        const int32_t q1 = br.ptr[k + 1];
-        int32_t lo = br.ptr[k], hi = q1;
-        while (lo < hi) {
-          const int32_t mid = (lo + hi) >> 1;
-          if (br.chunk[mid] < slot) lo = mid + 1;
-          else hi = mid;
-        }
-        if (lo < q1 && br.chunk[lo] == slot) {
-          b0 = br.start[lo];
-          len = br.start[lo + 1] - b0;
-        }
+        const int32_t* t = tab + (int64_t)k * stride + slot;
+        // Clamped into B, so that no table content can send a load outside it.
+        const int64_t t0 = min<int64_t>(max<int64_t>(t[0], 0), nnzB);
+        const int64_t t1 = min<int64_t>(max<int64_t>(t[1], t0), nnzB);
+        b0 = (int32_t)t0;
+        len = (int32_t)(t1 - t0);
       }
-      // The 64 runs' products as one sequence: product q belongs to the
-      // last lane whose exclusive offset is <= q (lanes with empty runs
-      // share the next lane's offset, so the last one has products).
-      const int32_t inc = wave_incl_scan(len);
-      const int32_t off = inc - len;
+      // Long runs: whole-wave pieces of 64 products.
+      const int32_t np = len >= kLong ? (len + kWave - 1) / kWave : 0;
+      const int32_t pinc = wave_incl_scan(np);
+      const int32_t ptot = __shfl(pinc, kWave - 1);
+      for (int32_t g0 = 0; g0 < ptot; g0 += kLongU) {
+        int32_t cc[kLongU];
+        V vv[kLongU];
+#pragma unroll
+        for (int u = 0; u < kLongU; ++u) {
+          cc[u] = -1;
+          vv[u] = V(0);
+          const int32_t g = g0 + u;
+          if (g < ptot) {  // the same for every lane
+            // The run holding piece g: the first lane whose inclusive piece
+            // count passes g.
+            const int j = ffs64(__ballot(pinc > g));
+            const int32_t rb0 = lane_read(b0, j), rlen = lane_read(len, j);
+            const int32_t first = lane_read(pinc, j) - lane_read(np, j);
+            const V rav = lane_read(av, j);
+            const int32_t t = (g - first) * kWave + lane;
+            if (t < rlen) {
+              cc[u] = bcol[rb0 + t] - colBase;
+              vv[u] = rav * bval[rb0 + t];
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kLongU; ++u) direct_add<V, kBytes>(vals, bm, cc[u], vv[u], W, err);
+      }
+      // Short runs as one sequence: product q belongs to the last lane whose
+      // exclusive offset is <= q (lanes with empty runs share the next
+      // lane's offset, so the last one has products).
+      const int32_t slen = len >= kLong ? 0 : len;
+      const int32_t inc = wave_incl_scan(slen);
+      const int32_t off = inc - slen;
       const int32_t total = __shfl(inc, kWave - 1);
+      const int32_t sdelta = b0 - off;  // B position of product q is q + sdelta of its lane
       for (int32_t p = 0; p < total; p += kWave * kDirectU) {
         int32_t cc[kDirectU];
         V vv[kDirectU];
@@ -399,27 +463,16 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num_direct(const ChunkDesc* 
 #pragma unroll
             for (int step = 32; step >= 1; step >>= 1)
               if (__shfl(off, s + step) <= q) s += step;
-            const int32_t bi = __shfl(b0, s) + (q - __shfl(off, s));
+            const int32_t bi = __shfl(sdelta, s) + q;
             const V at = __shfl(av, s);
             if (q < total) {
-              cc[u] = bcol[bi] - (slot << log2W);
+              cc[u] = bcol[bi] - colBase;
               vv[u] = at * bval[bi];
             }
           }
         }
 #pragma unroll
-        for (int u = 0; u < kDirectU; ++u) {
-          const int32_t c = cc[u];
-          if (c >= 0) {
-            atomicAdd(&vals[c], vv[u]);
-            if constexpr (kBytes) {
-              ((unsigned char*)bm)[c] = 1;
-            } else {
-              const uint32_t bit = 1u << (c & 31);
-              if (!(bm[c >> 5] & bit)) atomicOr(&bm[c >> 5], bit);
-            }
-          }
-        }
+        for (int u = 0; u < kDirectU; ++u) direct_add<V, kBytes>(vals, bm, cc[u], vv[u], W, err);
       }
     }
     __syncthreads();
@@ -628,8 +681,9 @@ void launch_dense_num(bool f64, const ChunkDesc* desc, int64_t n, const ChunkLis
 }
 
 void launch_dense_num_direct(bool f64, const ChunkDesc* desc, int64_t n, int64_t W,
-                             const RowArgs& a, const BRuns& br, int32_t* ccol, void* cval,
-                             int32_t* err, int numCUs, hipStream_t s) {
+                             const RowArgs& a, const int32_t* slotTab, int64_t stride,
+                             int64_t nnzB, int32_t* ccol, void* cval, int32_t* err, int numCUs,
+                             hipStream_t s) {
   if (n <= 0) return;
   const size_t lds = dense_num_lds(f64, W);
   const bool bytes = dense_byte_marks(f64, W);
@@ -639,7 +693,7 @@ void launch_dense_num_direct(bool f64, const ChunkDesc* desc, int64_t n, int64_t
   while ((int64_t(1) << log2W) < W) ++log2W;
 #define L(V, B)                                                                           \
   hipLaunchKernelGGL((k_dense_num_direct<V, B>), dim3(g), dim3(kDenseNT), lds, s, desc, n, a, \
-                     br, log2W, ccol, (V*)cval, err)
+                     slotTab, stride, nnzB, log2W, ccol, (V*)cval, err)
   if (f64 && bytes) L(double, true);
   else if (f64) L(double, false);
   else if (bytes) L(float, true);
