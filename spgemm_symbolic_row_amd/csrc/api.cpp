@@ -279,7 +279,6 @@ struct spgemm_plan_s {
   ChunkDesc* keptDesc = nullptr;  // numeric's chunk descriptors for `kept`
   size_t wsCur = 0;      // workspace bytes currently held
   int32_t* CH = nullptr; // per heavy row, elements per W-wide chunk (or null)
-  const int32_t *runPtr = nullptr, *runChunk = nullptr, *runStart = nullptr;  // B's slot runs
   // Dense chunks accumulated straight from A and B (option dense_direct),
   // with B's slot table: (nreq + 1) run starts per B row.
   bool useDD = false;
@@ -822,14 +821,16 @@ void heavy_prepare(spgemm_plan_t p) {
     const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, s);
     p->CH = alloc_n<int32_t>(p, h * nreq, s);
     const int64_t nnzB = p->nnzB;
-    // B's runs stay for the dense chunks taken straight from A and B.
+    // B's slot table ((nreq + 1) run starts per B row) for the dense chunks
+    // taken straight from A and B (option dense_direct), when it takes at
+    // most 1 GiB; else those chunks are expanded as usual.
+    const int64_t tabElems = p->k * (nreq + 1);
+    p->useDD = p->opts.dense_direct && p->direct && tabElems * 4 <= ((int64_t)1 << 30);
+    int32_t* tab = p->useDD ? alloc_n<int32_t>(p, tabElems, s) : nullptr;
+    const WsMark mk = ws_mark(p);
     int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, s);
     int32_t* runChunk = alloc_n<int32_t>(p, nnzB, s);
     int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, s);
-    p->runPtr = runPtr;
-    p->runChunk = runChunk;
-    p->runStart = runStart;
-    const WsMark mk = ws_mark(p);
     int32_t* flags = alloc_n<int32_t>(p, nnzB, s);
     int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, s);
     int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
@@ -837,18 +838,10 @@ void heavy_prepare(spgemm_plan_t p) {
                   stmp, runPtr, runChunk, runStart, s);
     launch_chunk_hist_rows(h, p->xheavy, p->arp, p->acol, runPtr, runChunk, runStart,
                            (int32_t)nreq, p->CH, s);
+    if (tab) launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, s);
     check_launch("chunk histogram");
     ws_reset(p, mk, s);
-    // The slot table for dense chunks taken straight from A and B, when it
-    // takes at most 1 GiB (else those chunks are expanded as usual).
-    const int64_t tabBytes = (p->k * (nreq + 1)) * 4;
-    if (p->opts.dense_direct && p->direct && tabBytes <= ((int64_t)1 << 30)) {
-      int32_t* tab = alloc_n<int32_t>(p, p->k * (nreq + 1), s);
-      launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, s);
-      check_launch("slot table");
-      p->slotTab = tab;
-      p->useDD = true;
-    }
+    p->slotTab = tab;
     ph_end(p, ph, s);
   }
 }
@@ -1202,7 +1195,8 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
         launch_num_chunks_rank(p->rankBins[b], p->f64, desc + st, en - st, p->chunkWords, cl, ccol,
                                cval, p->errWord, s);
     }
-    else
+    else if (!launch_num_chunks_esc(p->symBins[b].cap, p->f64, desc + st, en - st, cl, ccol,
+                                    cval, p->errWord, s))
       launch_num_chunks(p->numBins[b], p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, s);
   }
   ph_end(p, ph, s);

@@ -857,6 +857,82 @@ __global__ __launch_bounds__(kEscNT) void k_rows_esc(const int32_t* __restrict__
   }
 }
 
+// Light chunks of at most L elements (L = 32 or 64), expand-sort-compact
+// as for short rows: L lanes per chunk, one element per lane, a bitonic sort
+// of (chunk column, value) by lane exchanges, a segmented sum of equal
+// columns, and the last lane of every run writes it.  No LDS, no table to
+// clear.
+template <int L, int LD, typename V>
+__device__ __forceinline__ void esc_step_l(int k, int32_t& key, V& val) {
+  const int i = lane_id() % L;
+  const int32_t ok = lane_xor<LD>(key);
+  const V ov = lane_xor_v<LD>(val);
+  const bool up = (i & k) == 0;
+  const bool lower = (i & LD) == 0;
+  const bool take = (lower == up) ? (ok < key) : (ok > key);
+  if (take) {
+    key = ok;
+    val = ov;
+  }
+}
+
+template <int L, typename V, typename C>
+__global__ __launch_bounds__(kEscNT) void k_num_chunks_esc(const ChunkDesc* __restrict__ desc,
+                                                           int64_t n, ChunkList cl,
+                                                           int32_t* __restrict__ ccol,
+                                                           V* __restrict__ cval,
+                                                           int32_t* __restrict__ err) {
+  static_assert(L == 32 || L == 64, "a chunk takes half a wave or a wave");
+  const int64_t ci = ((int64_t)blockIdx.x * kEscNT + threadIdx.x) / L;
+  const int l = lane_id() % L;
+  const bool live = ci < n;
+  ChunkDesc d{};
+  if (live) d = desc[ci];
+  int32_t key = INT_MAX;
+  V val = V(0);
+  if (live && l < d.cnt) {
+    const int64_t e = d.off + l;
+    key = (int32_t)((const C*)(d.buf ? cl.col1 : cl.col0))[e];
+    val = ((const V*)(d.buf ? cl.val1 : cl.val0))[e];
+  }
+  if (live && l == 0 && d.cnt > L) flag_error(err, kErrHashFull);
+#pragma unroll
+  for (int k = 2; k <= L; k <<= 1) {
+    if (k >= 64) esc_step_l<L, 32, V>(k, key, val);
+    if (k >= 32) esc_step_l<L, 16, V>(k, key, val);
+    if (k >= 16) esc_step_l<L, 8, V>(k, key, val);
+    if (k >= 8) esc_step_l<L, 4, V>(k, key, val);
+    if (k >= 4) esc_step_l<L, 2, V>(k, key, val);
+    esc_step_l<L, 1, V>(k, key, val);
+  }
+  const int32_t prev = __shfl_up(key, 1, L);
+  const bool valid = key != INT_MAX;
+  const bool head = valid && (l == 0 || prev != key);
+  const uint64_t heads = __ballot(head);
+  const int half = (lane_id() / L) * L;
+  const uint64_t mine = L == 64 ? heads : (heads >> half) & 0xffffffffull;
+  const int32_t nnz = __popcll(mine);
+  bool f = head;
+#pragma unroll
+  for (int dd = 1; dd < L; dd <<= 1) {
+    const V y = __shfl_up(val, dd, L);
+    const bool fy = __shfl_up((int)f, dd, L) != 0;
+    if (l >= dd && !f) val += y;
+    if (l >= dd) f = f || fy;
+  }
+  const int32_t next = __shfl_down(key, 1, L);
+  const bool tail = valid && (l == L - 1 || next != key);
+  const uint64_t upto = l == 63 ? ~0ull : ((2ull << l) - 1ull);
+  const int32_t pos = __popcll(mine & upto) - 1;  // run index
+  if (live) {
+    if (l == 0 && d.want != nnz) flag_error(err, kErrCountMismatch);
+    if (tail && pos < d.want) {
+      ccol[d.base + pos] = d.colBase + key;
+      cval[d.base + pos] = val;
+    }
+  }
+}
+
 template <int TPR, int RPB, int E, typename V, typename C = int32_t>
 __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, int32_t spt,
@@ -1227,6 +1303,35 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
 #undef L
   }
   (void)flag_unsupported;  // make_bins rejects bins without an instance
+}
+
+bool launch_num_chunks_esc(int32_t cap, bool f64, const ChunkDesc* desc, int64_t n,
+                           const ChunkList& cl, int32_t* ccol, void* cval, int32_t* err,
+                           hipStream_t s) {
+  if (cap > 64) return false;
+  if (n <= 0) return true;
+  const int L = cap <= 32 ? 32 : 64;
+  const unsigned grid = (unsigned)((n * L + kEscNT - 1) / kEscNT);
+#define LE(LL, V, C)                                                                        \
+  hipLaunchKernelGGL((k_num_chunks_esc<LL, V, C>), dim3(grid), dim3(kEscNT), 0, s, desc, n, cl, \
+                     ccol, (V*)cval, err)
+#define LV(LL, V)              \
+  do {                         \
+    if (cl.col16)              \
+      LE(LL, V, uint16_t);     \
+    else                       \
+      LE(LL, V, int32_t);      \
+  } while (0)
+  if (L == 32) {
+    if (f64) LV(32, double);
+    else LV(32, float);
+  } else {
+    if (f64) LV(64, double);
+    else LV(64, float);
+  }
+#undef LV
+#undef LE
+  return true;
 }
 
 void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
