@@ -1189,15 +1189,19 @@ void numeric_batch(spgemm_plan_t p, const Batch& B, int32_t* ccol, void* cval,
   const int ph = ph_begin(p, SPGEMM_PH_NUM_CHUNK_HASH, s);
   for (int b = 0; b < p->NS; ++b) {
     const int64_t st = B.fcBinStart[b], en = B.fcBinStart[b + 1];
+    // Up to 256 elements: sorted in registers; then the bitmap-rank or the
+    // hash accumulators.
+    if (launch_num_chunks_esc(p->symBins[b].cap, p->f64, desc + st, en - st, cl, ccol, cval,
+                              p->errWord, s))
+      continue;
     if (num_bitmap(p, b)) {
       if (!launch_num_chunks_direct(p->symBins[b], p->f64, desc + st, en - st, p->chunkWords,
                                     (size_t)p->lds, cl, ccol, cval, p->errWord, s))
         launch_num_chunks_rank(p->rankBins[b], p->f64, desc + st, en - st, p->chunkWords, cl, ccol,
                                cval, p->errWord, s);
-    }
-    else if (!launch_num_chunks_esc(p->symBins[b].cap, p->f64, desc + st, en - st, cl, ccol,
-                                    cval, p->errWord, s))
+    } else {
       launch_num_chunks(p->numBins[b], p->f64, desc + st, en - st, cl, ccol, cval, p->errWord, s);
+    }
   }
   ph_end(p, ph, s);
   if (s != p->sd) HIP_CHECK(hipStreamWaitEvent(s, p->evD1, 0));

@@ -216,8 +216,8 @@ bool num_bin_supported(const BinCfg& b);
 void launch_num_chunks(const BinCfg& b, bool f64, const ChunkDesc* desc, int64_t n,
                        const ChunkList& cl, int32_t* ccol, void* cval, int32_t* err,
                        hipStream_t s);
-// Light chunks of at most 64 elements by expand-sort-compact (false, with
-// nothing launched, for a larger cap).
+// Light chunks of at most 256 elements by expand-sort-compact in registers
+// (false, with nothing launched, for a larger cap).
 bool launch_num_chunks_esc(int32_t cap, bool f64, const ChunkDesc* desc, int64_t n,
                            const ChunkList& cl, int32_t* ccol, void* cval, int32_t* err,
                            hipStream_t s);

@@ -933,6 +933,118 @@ __global__ __launch_bounds__(kEscNT) void k_num_chunks_esc(const ChunkDesc* __re
   }
 }
 
+// Light chunks of at most 64 * E elements (E = 2 or 4): one wave per chunk,
+// E elements per lane sorted by the bitonic network of sort_to_regs (lane
+// exchanges and register swaps), then a segmented sum: inside each lane,
+// across lanes for the run that continues from the lanes before, and a scan
+// of the lanes' run heads gives every run its output position.
+template <int E, typename V, typename C>
+__global__ __launch_bounds__(kEscNT) void k_num_chunks_esc_e(const ChunkDesc* __restrict__ desc,
+                                                             int64_t n, ChunkList cl,
+                                                             int32_t* __restrict__ ccol,
+                                                             V* __restrict__ cval,
+                                                             int32_t* __restrict__ err) {
+  constexpr int NP = kWave * E;
+  const int64_t ci = ((int64_t)blockIdx.x * kEscNT + threadIdx.x) / kWave;
+  const int l = lane_id();
+  const bool live = ci < n;
+  ChunkDesc d{};
+  if (live) d = desc[ci];
+  int32_t kk[E];
+  V vv[E];
+  {
+    const C* __restrict__ col = (const C*)(d.buf ? cl.col1 : cl.col0);
+    const V* __restrict__ val = (const V*)(d.buf ? cl.val1 : cl.val0);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = e * kWave + l;  // any order: the network sorts them all
+      const bool in = live && i < d.cnt;
+      kk[e] = in ? (int32_t)col[d.off + i] : INT_MAX;
+      vv[e] = in ? val[d.off + i] : V(0);
+    }
+  }
+  if (live && l == 0 && d.cnt > NP) flag_error(err, kErrHashFull);
+  // Bitonic network over element index l * E + e.
+  for (int k = 2; k <= NP; k <<= 1) {
+    for (int j = k >> 1; j >= E; j >>= 1) {
+      switch (j / E) {  // lane distance, below 64
+        case 1: bitonic_lane_step<1, kWave, E, V>(k, kk, vv); break;
+        case 2: bitonic_lane_step<2, kWave, E, V>(k, kk, vv); break;
+        case 4: bitonic_lane_step<4, kWave, E, V>(k, kk, vv); break;
+        case 8: bitonic_lane_step<8, kWave, E, V>(k, kk, vv); break;
+        case 16: bitonic_lane_step<16, kWave, E, V>(k, kk, vv); break;
+        default: bitonic_lane_step<32, kWave, E, V>(k, kk, vv); break;
+      }
+    }
+#pragma unroll
+    for (int jj = E / 2; jj >= 1; jj >>= 1) {
+      if (jj < k) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & jj) == 0) {
+            const bool up = ((l * E + e) & k) == 0;
+            if ((kk[e] > kk[e + jj]) == up) {
+              const int32_t tk = kk[e];
+              kk[e] = kk[e + jj];
+              kk[e + jj] = tk;
+              const V tv = vv[e];
+              vv[e] = vv[e + jj];
+              vv[e + jj] = tv;
+            }
+          }
+        }
+      }
+    }
+  }
+  // Run heads, in-lane segmented sums, and the lanes' run-head counts.
+  bool head[E];
+  const int32_t prevLast = __shfl_up(kk[E - 1], 1);
+  int32_t hc = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int32_t pk = e == 0 ? prevLast : kk[e - 1];
+    head[e] = kk[e] != INT_MAX && ((l == 0 && e == 0) || pk != kk[e]);
+    hc += head[e] ? 1 : 0;
+    if (e > 0 && !head[e]) vv[e] += vv[e - 1];
+  }
+  // Across lanes: the partial of each lane's last run, summed over the
+  // lanes before while no head separates them.
+  V x = vv[E - 1];
+  bool f = hc > 0;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const V y = __shfl_up(x, dd);
+    const bool fy = __shfl_up((int)f, dd) != 0;
+    if (l >= dd && !f) x += y;
+    if (l >= dd) f = f || fy;
+  }
+  V incoming = __shfl_up(x, 1);
+  if (l == 0) incoming = V(0);
+  bool seen = false;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    seen = seen || head[e];
+    if (!seen) vv[e] += incoming;
+  }
+  const int32_t nextFirst = __shfl_down(kk[0], 1);
+  const int32_t hinc = wave_incl_scan(hc);
+  const int32_t nnz = __shfl(hinc, kWave - 1);
+  int32_t r = hinc - hc;  // runs that start before this lane
+  if (live) {
+    if (l == 0 && d.want != nnz) flag_error(err, kErrCountMismatch);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      r += head[e] ? 1 : 0;
+      const int32_t nk = e < E - 1 ? kk[e + 1] : (l == kWave - 1 ? INT_MAX : nextFirst);
+      const bool tail = kk[e] != INT_MAX && nk != kk[e];
+      if (tail && r - 1 < d.want) {
+        ccol[d.base + r - 1] = d.colBase + kk[e];
+        cval[d.base + r - 1] = vv[e];
+      }
+    }
+  }
+}
+
 template <int TPR, int RPB, int E, typename V, typename C = int32_t>
 __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __restrict__ desc,
                                                          int64_t n, int32_t T, int32_t spt,
@@ -1308,8 +1420,31 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
 bool launch_num_chunks_esc(int32_t cap, bool f64, const ChunkDesc* desc, int64_t n,
                            const ChunkList& cl, int32_t* ccol, void* cval, int32_t* err,
                            hipStream_t s) {
-  if (cap > 64) return false;
+  if (cap > 256) return false;
   if (n <= 0) return true;
+  if (cap > 64) {
+    const unsigned g = (unsigned)((n * kWave + kEscNT - 1) / kEscNT);
+#define LE(E, V, C)                                                                        \
+  hipLaunchKernelGGL((k_num_chunks_esc_e<E, V, C>), dim3(g), dim3(kEscNT), 0, s, desc, n, cl, \
+                     ccol, (V*)cval, err)
+#define LV(E, V)              \
+  do {                        \
+    if (cl.col16)             \
+      LE(E, V, uint16_t);     \
+    else                      \
+      LE(E, V, int32_t);      \
+  } while (0)
+    if (cap <= 128) {
+      if (f64) LV(2, double);
+      else LV(2, float);
+    } else {
+      if (f64) LV(4, double);
+      else LV(4, float);
+    }
+#undef LV
+#undef LE
+    return true;
+  }
   const int L = cap <= 32 ? 32 : 64;
   const unsigned grid = (unsigned)((n * L + kEscNT - 1) / kEscNT);
 #define LE(LL, V, C)                                                                        \
