@@ -836,8 +836,11 @@ void heavy_prepare(spgemm_plan_t p) {
     int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
     launch_b_runs(p->k, nnzB, p->brp, p->bcol, log2_exact(p->params.dense_width), flags, runIdx,
                   stmp, runPtr, runChunk, runStart, s);
-    launch_chunk_hist_rows(h, p->xheavy, p->arp, p->acol, runPtr, runChunk, runStart,
-                           (int32_t)nreq, p->CH, s);
+    int64_t* parts = alloc_n<int64_t>(p, h, s);
+    int64_t* itemPtr = alloc_n<int64_t>(p, h + 1, s);
+    int64_t* htmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, s);
+    launch_chunk_hist_rows(h, p->nAh, p->dAnnz, p->xheavy, p->arp, p->acol, runPtr, runChunk,
+                           runStart, (int32_t)nreq, p->CH, parts, itemPtr, htmp, s);
     if (tab) launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, s);
     check_launch("chunk histogram");
     ws_reset(p, mk, s);

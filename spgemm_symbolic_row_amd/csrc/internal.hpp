@@ -265,9 +265,13 @@ void launch_b_runs(int64_t K, int64_t nnzB, const int32_t* brp, const int32_t* b
 void launch_slot_table(int64_t K, int32_t nreq, const int32_t* brp, const int32_t* runPtr,
                        const int32_t* runChunk, const int32_t* runStart, int32_t* tab,
                        hipStream_t s);
-void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,
-                            const int32_t* acol, const int32_t* runPtr, const int32_t* runChunk,
-                            const int32_t* runStart, int32_t nreq, int32_t* CH, hipStream_t s);
+// annz: scan of the heavy rows' A lengths (hb + 1), nAh its total; parts
+// (hb), itemPtr (hb + 1) and scanTmp (scan_tmp_elems(hb) + 1) are workspace.
+void launch_chunk_hist_rows(int64_t hb, int64_t nAh, const int64_t* annz, const int32_t* rows,
+                            const int32_t* arp, const int32_t* acol, const int32_t* runPtr,
+                            const int32_t* runChunk, const int32_t* runStart, int32_t nreq,
+                            int32_t* CH, int64_t* parts, int64_t* itemPtr, int64_t* scanTmp,
+                            hipStream_t s);
 // finalOf[row * nreq + slot] = the final chunk covering W-wide slot `slot`
 // of batch row `row`, or -(chunk + 2) when key[chunk] == denseKey (a chunk
 // accumulated straight from A and B, whose products the expansion skips;

@@ -92,8 +92,19 @@ __global__ __launch_bounds__(kNT) void k_slot_table(int64_t K, int32_t nreq,
   for (; f <= nreq; ++f) t[f] = end;
 }
 
-// One work group per heavy row: LDS counters for the n_req chunks.
-__global__ __launch_bounds__(kNT) void k_chunk_hist_rows(const int32_t* __restrict__ rows,
+// Chunk histogram of the heavy rows.  A work item is a part of at most
+// kHistPart consecutive A entries of one heavy row (a row of more entries
+// is cut into several parts, so one long row does not hold up the launch);
+// itemPtr[i] is the first item of heavy row i.  A work group keeps LDS
+// counters for the n_req chunks.  Its waves take the part's entries in turn,
+// kHistU at a time, and the lanes of a wave take the runs of one entry's B
+// row, which all lie in different chunks, so the LDS adds of one
+// instruction never meet at one counter.  A row of one part stores its
+// counts; the parts of a longer row add theirs into zeroed counts.
+constexpr int kHistU = 4;
+constexpr int kHistPart = 256;
+__global__ __launch_bounds__(kNT) void k_chunk_hist_rows(int64_t h, const int64_t* __restrict__ itemPtr,
+                                                         const int32_t* __restrict__ rows,
                                                          const int32_t* __restrict__ arp,
                                                          const int32_t* __restrict__ acol,
                                                          const int32_t* __restrict__ runPtr,
@@ -101,23 +112,70 @@ __global__ __launch_bounds__(kNT) void k_chunk_hist_rows(const int32_t* __restri
                                                          const int32_t* __restrict__ runStart,
                                                          int32_t nreq, int32_t* __restrict__ CH) {
   extern __shared__ int32_t ch[];
+  constexpr int NW = kNT / kWave;
+  const int64_t item = blockIdx.x;
+  if (item >= itemPtr[h]) return;  // the same for the whole work group
+  // The heavy row of this item: the last i with itemPtr[i] <= item.
+  const int64_t i = wave_last_le(itemPtr, 0, h + 1, item);
+  const int64_t part = item - itemPtr[i];
+  const bool whole = itemPtr[i + 1] - itemPtr[i] == 1;
   for (int f = threadIdx.x; f < nreq; f += kNT) ch[f] = 0;
   __syncthreads();
-  const int32_t r = rows[blockIdx.x];
-  const int32_t a1 = arp[r + 1];
-  for (int32_t e = arp[r] + threadIdx.x; e < a1; e += kNT) {
-    const int32_t k = acol[e];
-    const int32_t q1 = runPtr[k + 1];
-    int32_t s = runStart[runPtr[k]];
-    for (int32_t q = runPtr[k]; q < q1; ++q) {
-      const int32_t s1 = runStart[q + 1];
-      atomicAdd(&ch[runChunk[q]], s1 - s);
-      s = s1;
+  const int32_t r = rows[i];
+  const int32_t a0 = arp[r] + (int32_t)(part * kHistPart);
+  const int32_t a1 = min(arp[r + 1], a0 + kHistPart);
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  for (int32_t e0 = a0 + w; e0 < a1; e0 += NW * kHistU) {
+    int32_t q0[kHistU], nq[kHistU];
+#pragma unroll
+    for (int u = 0; u < kHistU; ++u) {
+      const int32_t e = e0 + u * NW;
+      q0[u] = 0;
+      nq[u] = 0;
+      if (e < a1) {  // the same for every lane
+        const int32_t k = acol[e];
+        q0[u] = runPtr[k];
+        nq[u] = runPtr[k + 1] - q0[u];
+      }
+    }
+    int32_t c[kHistU], d[kHistU];
+#pragma unroll
+    for (int u = 0; u < kHistU; ++u) {
+      c[u] = -1;
+      d[u] = 0;
+      if (lane < nq[u]) {
+        const int32_t q = q0[u] + lane;
+        c[u] = runChunk[q];
+        d[u] = runStart[q + 1] - runStart[q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kHistU; ++u)
+      if (c[u] >= 0) atomicAdd(&ch[c[u]], d[u]);
+    // B rows with more than 64 runs (more than 64 chunks per row)
+#pragma unroll
+    for (int u = 0; u < kHistU; ++u) {
+      for (int32_t j = kWave + lane; j < nq[u]; j += kWave) {
+        const int32_t q = q0[u] + j;
+        atomicAdd(&ch[runChunk[q]], runStart[q + 1] - runStart[q]);
+      }
     }
   }
   __syncthreads();
-  int32_t* out = CH + (int64_t)blockIdx.x * nreq;
-  for (int f = threadIdx.x; f < nreq; f += kNT) out[f] = ch[f];
+  int32_t* out = CH + i * nreq;
+  for (int f = threadIdx.x; f < nreq; f += kNT) {
+    if (whole) out[f] = ch[f];
+    else if (ch[f]) atomicAdd(&out[f], ch[f]);
+  }
+}
+
+// Items of every heavy row: ceil(entries / kHistPart), at least one.
+__global__ __launch_bounds__(kNT) void k_hist_parts(int64_t h, const int64_t* __restrict__ annz,
+                                                    int64_t* __restrict__ parts) {
+  const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (i >= h) return;
+  const int64_t e = annz[i + 1] - annz[i];
+  parts[i] = e <= kHistPart ? 1 : (e + kHistPart - 1) / kHistPart;
 }
 
 // counts[q*v + c] = elements of level row q in its sub-chunk c: the sum of
@@ -168,12 +226,20 @@ void launch_slot_table(int64_t K, int32_t nreq, const int32_t* brp, const int32_
                      runPtr, runChunk, runStart, tab);
 }
 
-void launch_chunk_hist_rows(int64_t hb, const int32_t* rows, const int32_t* arp,
-                            const int32_t* acol, const int32_t* runPtr, const int32_t* runChunk,
-                            const int32_t* runStart, int32_t nreq, int32_t* CH, hipStream_t s) {
+void launch_chunk_hist_rows(int64_t hb, int64_t nAh, const int64_t* annz, const int32_t* rows,
+                            const int32_t* arp, const int32_t* acol, const int32_t* runPtr,
+                            const int32_t* runChunk, const int32_t* runStart, int32_t nreq,
+                            int32_t* CH, int64_t* parts, int64_t* itemPtr, int64_t* scanTmp,
+                            hipStream_t s) {
   if (hb <= 0) return;
-  hipLaunchKernelGGL(k_chunk_hist_rows, dim3((unsigned)hb), dim3(kNT), (size_t)nreq * 4, s, rows,
-                     arp, acol, runPtr, runChunk, runStart, nreq, CH);
+  hipLaunchKernelGGL(k_hist_parts, dim3(grid_for(hb, kNT, 1u << 30)), dim3(kNT), 0, s, hb, annz,
+                     parts);
+  launch_scan_i64(parts, hb, itemPtr, scanTmp, s);
+  launch_fill_i32(CH, 0, hb * nreq, s);
+  // Items: one per row plus one per kHistPart entries, at most.
+  const int64_t maxItems = hb + nAh / kHistPart + 1;
+  hipLaunchKernelGGL(k_chunk_hist_rows, dim3((unsigned)maxItems), dim3(kNT), (size_t)nreq * 4, s,
+                     hb, itemPtr, rows, arp, acol, runPtr, runChunk, runStart, nreq, CH);
 }
 
 void launch_level_counts(int64_t Q, int v, int32_t span, int32_t nreq, const int32_t* inRow,
