@@ -28,19 +28,38 @@ __global__ __launch_bounds__(kNT) void k_partition(int64_t Q, const int32_t* __r
                                                    int32_t* __restrict__ newRow,
                                                    int32_t* __restrict__ newSlot,
                                                    int32_t* __restrict__ ctr) {
+  // One pair of global atomics per work group (the waves' counts added in
+  // LDS first), so that a level of millions of chunks does not queue on
+  // two counters.
+  constexpr int NW = kNT / kWave;
+  __shared__ int32_t wh[NW], wl[NW], gb[2];
   const int64_t q = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  const int w = threadIdx.x / kWave;
   const bool act = q < Q;
   const int32_t cnt = act ? counts[q] : 0;
   const bool heavy = act && !last && cnt > tau;
   const bool light = act && !heavy && cnt > 0;
   const uint64_t mh = __ballot(heavy), ml = __ballot(light);
-  int32_t bh = 0, bl = 0;
   if (lane_id() == 0) {
-    if (mh) bh = atomicAdd(&ctr[0], __popcll(mh));
-    if (ml) bl = atomicAdd(&ctr[1], __popcll(ml));
+    wh[w] = __popcll(mh);
+    wl[w] = __popcll(ml);
   }
-  bh = __shfl(bh, 0);
-  bl = __shfl(bl, 0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t th = 0, tl = 0;
+    for (int i = 0; i < NW; ++i) {
+      th += wh[i];
+      tl += wl[i];
+    }
+    gb[0] = th ? atomicAdd(&ctr[0], th) : 0;
+    gb[1] = tl ? atomicAdd(&ctr[1], tl) : 0;
+  }
+  __syncthreads();
+  int32_t bh = gb[0], bl = gb[1];
+  for (int i = 0; i < w; ++i) {
+    bh += wh[i];
+    bl += wl[i];
+  }
   int64_t pos = -1;
   if (heavy) pos = bh + __popcll(mh & lanemask_lt());
   if (light) pos = Q - 1 - (bl + __popcll(ml & lanemask_lt()));
