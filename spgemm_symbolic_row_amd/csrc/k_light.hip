@@ -1118,10 +1118,36 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_chunks(const ChunkDesc* __rest
 // lane broadcasts.
 constexpr int kSymHeavyNT = 1024;
 constexpr int kSymHeavyU = 2;  // 16-byte loads per lane in flight per step
+constexpr int kSymHeavyG = 4;  // entries whose first loads are in flight together
 
 __device__ __forceinline__ void mark_col(uint32_t* bm, int32_t col, int32_t w0, uint32_t wlen) {
   const uint32_t c = (uint32_t)(col - w0);
   if (c < wlen) atomicOr(&bm[c >> 5], 1u << (c & 31));
+}
+// Columns idx .. idx+3 of B that lie in [x0, x1) (others -1): one 16-byte
+// load at a 16-byte aligned idx where the whole vector lies in B, else the
+// elements one by one.
+__device__ __forceinline__ int4 sym_heavy_load4(const int32_t* __restrict__ bcol, int64_t idx,
+                                                int64_t x0, int64_t x1, int64_t nnzB) {
+  int4 v = make_int4(-1, -1, -1, -1);
+  if (idx < x1) {
+    if (idx >= 0 && idx + 4 <= nnzB) {
+      v = *(const int4*)(bcol + idx);
+    } else {
+      if (idx >= x0) v.x = bcol[idx];
+      if (idx + 1 >= x0 && idx + 1 < x1) v.y = bcol[idx + 1];
+      if (idx + 2 >= x0 && idx + 2 < x1) v.z = bcol[idx + 2];
+      if (idx + 3 >= x0 && idx + 3 < x1) v.w = bcol[idx + 3];
+    }
+  }
+  return v;
+}
+__device__ __forceinline__ void sym_heavy_mark4(uint32_t* bm, int4 v, int64_t idx, int64_t x0,
+                                                int64_t x1, int32_t w0, uint32_t wlen) {
+  if (idx >= x0 && idx < x1) mark_col(bm, v.x, w0, wlen);
+  if (idx + 1 >= x0 && idx + 1 < x1) mark_col(bm, v.y, w0, wlen);
+  if (idx + 2 >= x0 && idx + 2 < x1) mark_col(bm, v.z, w0, wlen);
+  if (idx + 3 >= x0 && idx + 3 < x1) mark_col(bm, v.w, w0, wlen);
 }
 
 __global__ __launch_bounds__(kSymHeavyNT) void k_sym_heavy_rows(
@@ -1155,53 +1181,54 @@ __global__ __launch_bounds__(kSymHeavyNT) void k_sym_heavy_rows(
     const int32_t p0 = (int32_t)((int64_t)P * w / NW);
     const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / NW);
     if (p0 < p1) {
-      int64_t j = wave_last_le(a.scanA, rs, re, p0);  // the entry holding product p0
-      int32_t p = p0;
-      while (p < p1) {
-        // offsets, B row starts and ends of entries j .. j+63
+      // Entries from the one holding product p0, 64 at a time: their
+      // offsets, B row starts and ends are loaded lane-parallel and read
+      // back by lane broadcasts.  Each group of kSymHeavyG entries issues the
+      // first 16-byte load of every entry's run before marking any (runs are
+      // mostly short), then walks what is left of each run.
+      for (int64_t j = wave_last_le(a.scanA, rs, re, p0); j < re; j += kWave) {
         const int64_t e = j + lane;
         const bool ev = e < re;
         const int32_t o = ev ? a.scanA[e] : P;
         const int32_t bs = ev ? a.brp[a.acol[e]] : 0;
         int32_t on = __shfl_down(o, 1);
         if (lane == kWave - 1) on = (j + kWave < re) ? a.scanA[j + kWave] : P;
-        for (int q = 0; q < kWave && p < p1; ++q) {
-          const int32_t oe = __shfl(o, q), one = __shfl(on, q), be = __shfl(bs, q);
-          if (one <= p) continue;  // no products, or before this wave's share
-          const int64_t x0 = (int64_t)be + (p - oe);
-          const int64_t x1 = (int64_t)be + ((one < p1 ? one : p1) - oe);
-          // 16-byte loads at 16-byte aligned addresses; elements outside
-          // [x0, x1) are loaded only where the whole vector lies in B.
-          for (int64_t base = ((x0 + mis) & ~(int64_t)3) - mis; base < x1;
-               base += 4 * kWave * kSymHeavyU) {
-            int4 v[kSymHeavyU];
+        if (__builtin_amdgcn_readlane(o, 0) >= p1) break;  // past this wave's share
+        for (int q0 = 0; q0 < kWave; q0 += kSymHeavyG) {
+          if (__builtin_amdgcn_readlane(o, q0) >= p1) break;
+          int64_t xs[kSymHeavyG], xe[kSymHeavyG];
+          int4 v[kSymHeavyG];
 #pragma unroll
-            for (int u = 0; u < kSymHeavyU; ++u) {
-              const int64_t idx = base + 4 * (u * kWave + lane);
-              v[u] = make_int4(-1, -1, -1, -1);
-              if (idx < x1) {
-                if (idx >= 0 && idx + 4 <= nnzB) {
-                  v[u] = *(const int4*)(bcol + idx);
-                } else {
-                  if (idx >= x0) v[u].x = bcol[idx];
-                  if (idx + 1 >= x0 && idx + 1 < x1) v[u].y = bcol[idx + 1];
-                  if (idx + 2 >= x0 && idx + 2 < x1) v[u].z = bcol[idx + 2];
-                  if (idx + 3 >= x0 && idx + 3 < x1) v[u].w = bcol[idx + 3];
-                }
-              }
-            }
+          for (int g = 0; g < kSymHeavyG; ++g) {
+            const int q = q0 + g;
+            const int32_t oe = __builtin_amdgcn_readlane(o, q);
+            const int32_t one = __builtin_amdgcn_readlane(on, q);
+            const int32_t be = __builtin_amdgcn_readlane(bs, q);
+            // this entry's products inside [p0, p1)
+            const int32_t st = oe > p0 ? oe : p0, en = one < p1 ? one : p1;
+            xs[g] = en > st ? (int64_t)be + (st - oe) : 0;
+            xe[g] = en > st ? (int64_t)be + (en - oe) : 0;
+            v[g] = sym_heavy_load4(bcol, ((xs[g] + mis) & ~(int64_t)3) - mis + 4 * lane, xs[g],
+                                   xe[g], nnzB);
+          }
 #pragma unroll
-            for (int u = 0; u < kSymHeavyU; ++u) {
-              const int64_t idx = base + 4 * (u * kWave + lane);
-              if (idx >= x0 && idx < x1) mark_col(bm, v[u].x, w0, wlen);
-              if (idx + 1 >= x0 && idx + 1 < x1) mark_col(bm, v[u].y, w0, wlen);
-              if (idx + 2 >= x0 && idx + 2 < x1) mark_col(bm, v[u].z, w0, wlen);
-              if (idx + 3 >= x0 && idx + 3 < x1) mark_col(bm, v[u].w, w0, wlen);
+          for (int g = 0; g < kSymHeavyG; ++g)
+            sym_heavy_mark4(bm, v[g], ((xs[g] + mis) & ~(int64_t)3) - mis + 4 * lane, xs[g],
+                            xe[g], w0, wlen);
+          // the rest of each run, 4 * 64 * kSymHeavyU columns a step
+          for (int g = 0; g < kSymHeavyG; ++g) {
+            for (int64_t base = ((xs[g] + mis) & ~(int64_t)3) - mis + 4 * kWave; base < xe[g];
+                 base += 4 * kWave * kSymHeavyU) {
+              int4 r[kSymHeavyU];
+#pragma unroll
+              for (int u = 0; u < kSymHeavyU; ++u)
+                r[u] = sym_heavy_load4(bcol, base + 4 * (u * kWave + lane), xs[g], xe[g], nnzB);
+#pragma unroll
+              for (int u = 0; u < kSymHeavyU; ++u)
+                sym_heavy_mark4(bm, r[u], base + 4 * (u * kWave + lane), xs[g], xe[g], w0, wlen);
             }
           }
-          p = one < p1 ? one : p1;
         }
-        j += kWave;
       }
     }
     __syncthreads();
