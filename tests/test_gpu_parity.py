@@ -257,6 +257,38 @@ def test_heavy_rows_in_batches(budget):
     assert st["final_chunks"] == one[3]["final_chunks"]
 
 
+def _light_chunk_edges(dtype):
+    # Every row is heavy; its first-level chunks (2048 columns wide) are
+    # light and hold exactly E elements, E around the sizes where the chunk
+    # kernels change (32, 64, 128, 256 elements sorted in registers, larger
+    # ones by the bitmap rank): B row k has column k mod 7 (chunk 0: E
+    # elements over at most 7 columns, so long runs of equal columns are
+    # summed) and column 2048 + k (chunk 1: E distinct columns).
+    sizes = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300]
+    K = max(sizes)
+    rp = np.zeros(len(sizes) + 1, np.int64)
+    rp[1:] = np.cumsum(sizes)
+    acol = np.concatenate([np.arange(e) for e in sizes]).astype(np.int32)
+    rng = np.random.default_rng(5)
+    aval = rng.integers(-3, 4, acol.size).astype(dtype)
+    A = synth.CSR(rp.astype(np.int32), acol, aval, len(sizes), K)
+    bcol = np.stack([np.arange(K) % 7, 2048 + np.arange(K)], axis=1).reshape(-1).astype(np.int32)
+    bval = rng.integers(-3, 4, bcol.size).astype(dtype)
+    B = synth.CSR((2 * np.arange(K + 1)).astype(np.int32), bcol, bval, K, 4096)
+    A.check_canonical()
+    B.check_canonical()
+    return A, B
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_light_chunks_at_kernel_boundaries(dtype):
+    A, B = _light_chunk_edges(dtype)
+    st = check_full(A, B, exact=True, heavy_threshold=512, heavy_row_threshold=1, dense_width=256,
+                    max_chunks_per_level=2)
+    assert st["heavy_rows"] == A.m
+    assert st["dense_chunks"] == 0
+
+
 @pytest.mark.parametrize("W,nmax,budget", [(256, 4, 0), (128, 2, 0), (256, 32, 0), (256, 4, 150_000)])
 def test_chunk_counts_from_structure_match_data_pass(W, nmax, budget):
     # The level histograms derived from A's structure and B's chunk runs must
