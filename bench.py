@@ -329,6 +329,8 @@ def main():
                     help="first run one device-to-device copy of this many GiB, so "
                          "hardware byte counters can be scaled against a known size")
     ap.add_argument("--dense-width", type=int, default=0, help="override W (tuning)")
+    ap.add_argument("--max-chunks", type=int, default=0,
+                    help="override the chunks per multisplit level (tuning)")
     ap.add_argument("--lds-budget", type=int, default=0, help="override s_LM (tuning)")
     ap.add_argument("--heavy-threshold", type=int, default=0, help="override tau (tuning)")
     ap.add_argument("--heavy-row-threshold", type=int, default=0,
@@ -389,6 +391,8 @@ def main():
         opts["single_stream"] = 1
     if args.dense_width:
         opts["dense_width"] = args.dense_width
+    if args.max_chunks:
+        opts["max_chunks_per_level"] = args.max_chunks
     if args.lds_budget:
         opts["lds_budget"] = args.lds_budget
     if args.heavy_threshold:
