@@ -345,12 +345,13 @@ __global__ __launch_bounds__(kDenseNT) void k_dense_num(const ChunkDesc* __restr
 // contiguous).  B's slot table gives the run at once: tab[k * stride + s] is
 // the first position of B row k whose column is at least s * W, so the run
 // is [tab[k*stride+s], tab[k*stride+s+1]).  The waves of a work group share
-// the row's entries (each wave every 16th one, a lane per entry).  Runs of
+// the row's entries (each wave every 16th one, a lane per entry, 1024
+// entries a pass).  Runs of
 // at least kLong products are streamed by the whole wave, 64 products a
-// piece, kLongU pieces in flight: the pieces of a round's long runs are
+// piece, kLongU pieces in flight: the pieces of one pass's long runs are
 // numbered by a scan of their counts, and a piece finds its run from one
 // ballot, with the run's start, length and a_ik read from that lane (no
-// per-product search).  The shorter runs of the round are streamed as one
+// per-product search).  The shorter runs of the pass are streamed as one
 // sequence, each lane finding its run by a search across the lanes'
 // offsets.  B's rows are read from the caches instead of a materialised
 // intermediate.  Persistent work groups, write-out and clearing as in
