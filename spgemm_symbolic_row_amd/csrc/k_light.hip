@@ -17,16 +17,30 @@ namespace {
 
 constexpr int kMaxSpt = 24;  // slots per thread held in registers by the compaction
 
+// Value of lane j (j the same for every lane), without the LDS crossbar.
+__device__ __forceinline__ float lane_read(float x, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+}
+__device__ __forceinline__ double lane_read(double x, int j) {
+  const int64_t b = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)b, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int32_t)(uint32_t)(b >> 32), j);
+  return __longlong_as_double((int64_t)(((uint64_t)hi << 32) | lo));
+}
+
 // Products [p0, p1) of one row of A*B in Gustavson order (entry-major): the
 // flattened product index q of entry e starts at scanA[e] (row-local
-// exclusive offset).  The wave keeps 64 consecutive A entries in registers,
-// finds for each of 64 consecutive products the entry that owns it with a
-// 6-step binary search across lanes, and loads the B element's column (and
-// value).  kStreamU runs of 64 products are located and their loads issued
+// exclusive offset).  The wave keeps 64 consecutive A entries in registers
+// and finds, for each of 64 consecutive products, the entry that owns it:
+// when those products span at most kStreamWalk entries (two ballots tell),
+// by walking these entries with lane broadcasts, else by a 6-step binary
+// search across lanes (permutes through the LDS crossbar); then it loads the
+// B element's column (and value).  kStreamU runs of 64 products are located and their loads issued
 // before any is used, so a wave waits on one memory round trip per 256
 // products, not per 64.  f(act, col, a, b, q) gets the column, the A value,
 // the B value and the product index q.  Every lane runs the same iterations.
 constexpr int kStreamU = 4;
+constexpr int kStreamWalk = 8;  // entries a piece may span for the walk
 template <bool VAL, typename V, typename F>
 __device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
                                            const int32_t* __restrict__ acol,
@@ -64,15 +78,36 @@ __device__ __forceinline__ void stream_row(const int32_t* __restrict__ scanA,
         sa[u] = V(0);
         bv[u] = V(0);
         if (p + u * kWave < bend) {  // the same for every lane
-          int s = 0;
+          const int32_t pu = p + u * kWave;
+          // entries owning the first and the last product of this piece
+          const int lo = last_set64(__ballot(off <= pu));
+          const int hi = last_set64(__ballot(off <= pu + kWave - 1));
+          int32_t so, sb;
+          if (hi - lo < kStreamWalk) {
+            so = __builtin_amdgcn_readlane(off, lo);
+            sb = __builtin_amdgcn_readlane(bs, lo);
+            if (VAL) sa[u] = lane_read(a, lo);
+            for (int s = lo + 1; s <= hi; ++s) {
+              const int32_t os = __builtin_amdgcn_readlane(off, s);
+              const int32_t bss = __builtin_amdgcn_readlane(bs, s);
+              const V as = VAL ? lane_read(a, s) : V(0);
+              if (os <= q) {
+                so = os;
+                sb = bss;
+                if (VAL) sa[u] = as;
+              }
+            }
+          } else {
+            int s = 0;
 #pragma unroll
-          for (int step = 32; step >= 1; step >>= 1) {
-            const int32_t o = __shfl(off, s + step);
-            if (o <= q) s += step;
+            for (int step = 32; step >= 1; step >>= 1) {
+              const int32_t o = __shfl(off, s + step);
+              if (o <= q) s += step;
+            }
+            so = __shfl(off, s);
+            sb = __shfl(bs, s);
+            if (VAL) sa[u] = __shfl(a, s);
           }
-          const int32_t so = __shfl(off, s);
-          const int32_t sb = __shfl(bs, s);
-          if (VAL) sa[u] = __shfl(a, s);
           if (act[u]) {
             const int32_t bi = sb + (q - so);
             cc[u] = bcol[bi];
