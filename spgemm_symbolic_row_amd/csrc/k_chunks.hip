@@ -397,6 +397,8 @@ void chunks_set_attributes() {
   SG_ATTR((k_num_chunks_direct<128, 2, 4, V>)); \
   SG_ATTR((k_num_chunks_direct<256, 1, 4, V>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 4, V>)); \
+  SG_ATTR((k_num_chunks_direct<512, 1, 8, V>)); \
+  SG_ATTR((k_num_chunks_direct<512, 1, 16, V>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 4, V>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 8, V>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 16, V>))
@@ -410,6 +412,8 @@ void chunks_set_attributes() {
   SG_ATTR((k_num_chunks_direct<128, 2, 4, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<256, 1, 4, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 4, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<512, 1, 8, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<512, 1, 16, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 4, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 8, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<1024, 1, 16, V, uint16_t>))
@@ -450,11 +454,13 @@ bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, 
     case 128: L(128, 2, 4); break;
     case 256: L(256, 1, 4); break;
     case 512: L(512, 1, 4); break;
-    default:
-      if (kb <= 4) L(1024, 1, 4);
-      else if (kb <= 8) L(1024, 1, 8);
-      else L(1024, 1, 16);
+    default: {
+      // 512 threads with more elements each: more chunks in flight per CU.
+      const int kb2 = (int)((b.cap + 511) / 512);
+      if (kb2 <= 8) L(512, 1, 8);
+      else L(512, 1, 16);
       break;
+    }
   }
 #undef L
 #undef L1
