@@ -396,6 +396,7 @@ void chunks_set_attributes() {
   SG_ATTR((k_num_chunks_direct<64, 4, 4, V>));  \
   SG_ATTR((k_num_chunks_direct<128, 2, 4, V>)); \
   SG_ATTR((k_num_chunks_direct<256, 1, 4, V>)); \
+  SG_ATTR((k_num_chunks_direct<256, 1, 8, V>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 4, V>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 8, V>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 16, V>)); \
@@ -411,6 +412,7 @@ void chunks_set_attributes() {
   SG_ATTR((k_num_chunks_direct<64, 4, 4, V, uint16_t>));  \
   SG_ATTR((k_num_chunks_direct<128, 2, 4, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<256, 1, 4, V, uint16_t>)); \
+  SG_ATTR((k_num_chunks_direct<256, 1, 8, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 4, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 8, V, uint16_t>)); \
   SG_ATTR((k_num_chunks_direct<512, 1, 16, V, uint16_t>)); \
@@ -453,7 +455,7 @@ bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, 
       break;
     case 128: L(128, 2, 4); break;
     case 256: L(256, 1, 4); break;
-    case 512: L(512, 1, 4); break;
+    case 512: L(256, 1, 8); break;
     default: {
       // 512 threads with more elements each: more chunks in flight per CU.
       const int kb2 = (int)((b.cap + 511) / 512);
