@@ -436,10 +436,17 @@ bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, 
   const size_t lds = direct_chunk_lds(f64, b.cap, words, b.rpb);
   if (kb > 16 || (b.tpr < 1024 && b.tpr * 4 < b.cap) || lds > ldsMax) return false;
   if (n <= 0) return true;
-  const unsigned grid = (unsigned)((n + b.rpb - 1) / b.rpb);
+  // Grid and LDS follow the instance's chunks per block (CPB), which may
+  // differ from the bin's rows per block; an instance whose LDS would not
+  // fit is not launched.
 #define L1(TPC, CPB, KB, V, C)                                                                 \
-  hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, V, C>), dim3(grid), dim3(TPC * CPB),    \
-                     lds, s, desc, n, b.cap, words, cl, ccol, (V*)cval, err)
+  do {                                                                                         \
+    const size_t ldsI = direct_chunk_lds(f64, b.cap, words, CPB);                              \
+    if (ldsI > ldsMax || (int64_t)(TPC) * (KB) < b.cap) return false;                          \
+    hipLaunchKernelGGL((k_num_chunks_direct<TPC, CPB, KB, V, C>),                              \
+                       dim3((unsigned)((n + (CPB) - 1) / (CPB))), dim3((TPC) * (CPB)), ldsI, s, \
+                       desc, n, b.cap, words, cl, ccol, (V*)cval, err);                         \
+  } while (0)
 #define L(TPC, CPB, KB)                                                                        \
   do {                                                                                         \
     if (f64 && cl.col16) L1(TPC, CPB, KB, double, uint16_t);                                   \
@@ -460,7 +467,8 @@ bool launch_num_chunks_direct(const BinCfg& b, bool f64, const ChunkDesc* desc, 
       // 512 threads with more elements each: more chunks in flight per CU.
       const int kb2 = (int)((b.cap + 511) / 512);
       if (kb2 <= 8) L(512, 1, 8);
-      else L(512, 1, 16);
+      else if (kb2 <= 16) L(512, 1, 16);
+      else L(1024, 1, 16);
       break;
     }
   }
