@@ -232,15 +232,21 @@ __device__ __forceinline__ void dense_write_out(V* vals, uint32_t* bm, int32_t* 
   uint32_t mask = 0;
   if (lc0 < W && lane * cpl < cpw) {
     if constexpr (kBytes) {
-      // cpl is a power of two; from 4 on, lc0 is a multiple of 4.
-      const unsigned char* mk = (const unsigned char*)bm;
+      // cpl is a power of two; from 4 on, lc0 is a multiple of 4.  Each
+      // lane owns its mark bytes, so it clears them as it reads them.
+      unsigned char* mk = (unsigned char*)bm;
       if (cpl >= 4) {
         for (int k = 0; k < cpl; k += 4) {
-          const uint32_t wd = *(const uint32_t*)(mk + lc0 + k);
+          uint32_t* wp = (uint32_t*)(mk + lc0 + k);
+          const uint32_t wd = *wp;
+          *wp = 0u;
           mask |= ((wd & 1u) | ((wd >> 7) & 2u) | ((wd >> 14) & 4u) | ((wd >> 21) & 8u)) << k;
         }
       } else {
-        for (int k = 0; k < cpl; ++k) mask |= (uint32_t)mk[lc0 + k] << k;
+        for (int k = 0; k < cpl; ++k) {
+          mask |= (uint32_t)mk[lc0 + k] << k;
+          mk[lc0 + k] = 0;
+        }
       }
     } else {
       const uint32_t word = bm[lc0 >> 5];
@@ -276,12 +282,12 @@ __device__ __forceinline__ void dense_write_out(V* vals, uint32_t* bm, int32_t* 
     }
   }
   __syncthreads();
-  if constexpr (kBytes) {
-    for (int i = threadIdx.x; i < W / 16; i += kDenseNT) ((uint4*)bm)[i] = uint4{0, 0, 0, 0};
-  } else {
+  // Byte marks were cleared as they were read; bit marks, which lanes may
+  // share, are cleared here.
+  if constexpr (!kBytes) {
     for (int i = threadIdx.x; i < nwords; i += kDenseNT) bm[i] = 0;
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 template <typename V, typename C, bool kBytes>
