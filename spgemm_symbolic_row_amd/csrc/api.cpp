@@ -505,8 +505,10 @@ void join(spgemm_plan_t p) {
   if (p->sl == p->stream) return;
   HIP_CHECK(hipEventRecord(p->evL, p->sl));
   HIP_CHECK(hipEventRecord(p->evH, p->sh));
+  HIP_CHECK(hipEventRecord(p->evD1, p->sd));
   HIP_CHECK(hipStreamWaitEvent(p->stream, p->evL, 0));
   HIP_CHECK(hipStreamWaitEvent(p->stream, p->evH, 0));
+  HIP_CHECK(hipStreamWaitEvent(p->stream, p->evD1, 0));
 }
 
 void check_device_errors(spgemm_plan_t p, int32_t word) {
@@ -818,7 +820,6 @@ void heavy_prepare(spgemm_plan_t p) {
   // Chunk counts of every heavy row from the structure, for all levels.
   const int64_t nreq = p->nreq;
   if (structCounts) {
-    const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, s);
     p->CH = alloc_n<int32_t>(p, h * nreq, s);
     const int64_t nnzB = p->nnzB;
     // B's slot table ((nreq + 1) run starts per B row) for the dense chunks
@@ -827,25 +828,36 @@ void heavy_prepare(spgemm_plan_t p) {
     const int64_t tabElems = p->k * (nreq + 1);
     p->useDD = p->opts.dense_direct && p->direct && tabElems * 4 <= ((int64_t)1 << 30);
     int32_t* tab = p->useDD ? alloc_n<int32_t>(p, tabElems, s) : nullptr;
+    // With several batches the counts are first needed in numeric, so they
+    // are taken on the dense chunks' stream (idle until then), beside the
+    // heavy-row symbolic; symbolic ends by joining that stream.  Their
+    // workspace is then kept until the plan ends.
+    const bool aside = !p->symVals && p->sd != s;
+    hipStream_t sc = aside ? p->sd : s;
+    if (aside) {
+      HIP_CHECK(hipEventRecord(p->evD0, s));
+      HIP_CHECK(hipStreamWaitEvent(sc, p->evD0, 0));
+    }
+    const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, sc);
     const WsMark mk = ws_mark(p);
-    int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, s);
-    int32_t* runChunk = alloc_n<int32_t>(p, nnzB, s);
-    int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, s);
-    int32_t* flags = alloc_n<int32_t>(p, nnzB, s);
-    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, s);
-    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
+    int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, sc);
+    int32_t* runChunk = alloc_n<int32_t>(p, nnzB, sc);
+    int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, sc);
+    int32_t* flags = alloc_n<int32_t>(p, nnzB, sc);
+    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, sc);
+    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, sc);
     launch_b_runs(p->k, nnzB, p->brp, p->bcol, log2_exact(p->params.dense_width), flags, runIdx,
-                  stmp, runPtr, runChunk, runStart, s);
-    int64_t* parts = alloc_n<int64_t>(p, h, s);
-    int64_t* itemPtr = alloc_n<int64_t>(p, h + 1, s);
-    int64_t* htmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, s);
+                  stmp, runPtr, runChunk, runStart, sc);
+    int64_t* parts = alloc_n<int64_t>(p, h, sc);
+    int64_t* itemPtr = alloc_n<int64_t>(p, h + 1, sc);
+    int64_t* htmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, sc);
     launch_chunk_hist_rows(h, p->nAh, p->dAnnz, p->xheavy, p->arp, p->acol, runPtr, runChunk,
-                           runStart, (int32_t)nreq, p->CH, parts, itemPtr, htmp, s);
-    if (tab) launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, s);
+                           runStart, (int32_t)nreq, p->CH, parts, itemPtr, htmp, sc);
+    if (tab) launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, sc);
     check_launch("chunk histogram");
-    ws_reset(p, mk, s);
+    if (!aside) ws_reset(p, mk, s);
     p->slotTab = tab;
-    ph_end(p, ph, s);
+    ph_end(p, ph, sc);
   }
 }
 
@@ -1569,12 +1581,19 @@ void destroy_plan(spgemm_plan_t p) {
     // free on one stream never overtakes a use on another.
     (void)hipEventRecord(p->evL, p->sl);
     (void)hipEventRecord(p->evH, p->sh);
+    (void)hipEventRecord(p->evD1, p->sd);
     (void)hipEventRecord(p->evFork, p->stream);
     (void)hipStreamWaitEvent(p->stream, p->evL, 0);
     (void)hipStreamWaitEvent(p->stream, p->evH, 0);
+    (void)hipStreamWaitEvent(p->stream, p->evD1, 0);
+    (void)hipStreamWaitEvent(p->sd, p->evL, 0);
+    (void)hipStreamWaitEvent(p->sd, p->evH, 0);
+    (void)hipStreamWaitEvent(p->sd, p->evFork, 0);
     (void)hipStreamWaitEvent(p->sl, p->evH, 0);
+    (void)hipStreamWaitEvent(p->sl, p->evD1, 0);
     (void)hipStreamWaitEvent(p->sl, p->evFork, 0);
     (void)hipStreamWaitEvent(p->sh, p->evL, 0);
+    (void)hipStreamWaitEvent(p->sh, p->evD1, 0);
     (void)hipStreamWaitEvent(p->sh, p->evFork, 0);
   }
   arena_release(p);
