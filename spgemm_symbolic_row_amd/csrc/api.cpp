@@ -828,36 +828,26 @@ void heavy_prepare(spgemm_plan_t p) {
     const int64_t tabElems = p->k * (nreq + 1);
     p->useDD = p->opts.dense_direct && p->direct && tabElems * 4 <= ((int64_t)1 << 30);
     int32_t* tab = p->useDD ? alloc_n<int32_t>(p, tabElems, s) : nullptr;
-    // With several batches the counts are first needed in numeric, so they
-    // are taken on the dense chunks' stream (idle until then), beside the
-    // heavy-row symbolic; symbolic ends by joining that stream.  Their
-    // workspace is then kept until the plan ends.
-    const bool aside = !p->symVals && p->sd != s;
-    hipStream_t sc = aside ? p->sd : s;
-    if (aside) {
-      HIP_CHECK(hipEventRecord(p->evD0, s));
-      HIP_CHECK(hipStreamWaitEvent(sc, p->evD0, 0));
-    }
-    const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, sc);
+    const int ph = ph_begin(p, SPGEMM_PH_CHUNK_HIST, s);
     const WsMark mk = ws_mark(p);
-    int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, sc);
-    int32_t* runChunk = alloc_n<int32_t>(p, nnzB, sc);
-    int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, sc);
-    int32_t* flags = alloc_n<int32_t>(p, nnzB, sc);
-    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, sc);
-    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, sc);
+    int32_t* runPtr = alloc_n<int32_t>(p, p->k + 1, s);
+    int32_t* runChunk = alloc_n<int32_t>(p, nnzB, s);
+    int32_t* runStart = alloc_n<int32_t>(p, nnzB + 1, s);
+    int32_t* flags = alloc_n<int32_t>(p, nnzB, s);
+    int64_t* runIdx = alloc_n<int64_t>(p, nnzB + 1, s);
+    int64_t* stmp = alloc_n<int64_t>(p, scan_tmp_elems(nnzB) + 1, s);
     launch_b_runs(p->k, nnzB, p->brp, p->bcol, log2_exact(p->params.dense_width), flags, runIdx,
-                  stmp, runPtr, runChunk, runStart, sc);
-    int64_t* parts = alloc_n<int64_t>(p, h, sc);
-    int64_t* itemPtr = alloc_n<int64_t>(p, h + 1, sc);
-    int64_t* htmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, sc);
+                  stmp, runPtr, runChunk, runStart, s);
+    int64_t* parts = alloc_n<int64_t>(p, h, s);
+    int64_t* itemPtr = alloc_n<int64_t>(p, h + 1, s);
+    int64_t* htmp = alloc_n<int64_t>(p, scan_tmp_elems(h) + 1, s);
     launch_chunk_hist_rows(h, p->nAh, p->dAnnz, p->xheavy, p->arp, p->acol, runPtr, runChunk,
-                           runStart, (int32_t)nreq, p->CH, parts, itemPtr, htmp, sc);
-    if (tab) launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, sc);
+                           runStart, (int32_t)nreq, p->CH, parts, itemPtr, htmp, s);
+    if (tab) launch_slot_table(p->k, (int32_t)nreq, p->brp, runPtr, runChunk, runStart, tab, s);
     check_launch("chunk histogram");
-    if (!aside) ws_reset(p, mk, s);
+    ws_reset(p, mk, s);
     p->slotTab = tab;
-    ph_end(p, ph, sc);
+    ph_end(p, ph, s);
   }
 }
 
@@ -1253,38 +1243,43 @@ void heavy_symbolic(spgemm_plan_t p) {
     p->haveKept = true;
     // numeric's descriptors, reserved now so that numeric allocates nothing
     p->keptDesc = alloc_n<ChunkDesc>(p, B.nfc, s);
+    launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
   } else {
-    // Every heavy row's W-wide slots counted straight from A and B.
-    const int ph = ph_begin(p, SPGEMM_PH_SYM_HEAVY, s);
-    int32_t* next = alloc_n<int32_t>(p, 1, s);
-    launch_fill_i32(next, 0, 1, s);
-    launch_sym_heavy_rows(h, p->nreq, log2_exact(W), p->xheavy, row_args(p), p->nnzB,
-                          p->slotNnz, next, p->numCUs, (size_t)p->lds, s);
-    ph_end(p, ph, s);
-    if (p->symVals) {
-      // One batch with dense_direct: the light chunks' products are expanded
-      // now and kept for numeric (dense chunks are taken straight from A and
-      // B there), so numeric allocates nothing.
-      Batch B;
-      expand_batch(p, p->batches[0].first, p->batches[0].second, true, true, &B);
-      p->st.final_chunks += B.nfc;
-      p->st.dense_chunks += B.denseChunks;
-      for (int l = 0; l < 8; ++l) p->st.level_elems[l] += B.levelElems[l];
-      p->kept = B;
-      p->haveKept = true;
-      p->keptDesc = alloc_n<ChunkDesc>(p, B.nfc, s);
+    // Every heavy row's W-wide slots counted straight from A and B, on the
+    // dense chunks' stream (idle until numeric); meanwhile the heavy stream
+    // expands the first batch with values (only its light chunks with
+    // dense_direct), which numeric takes as it is.  Symbolic ends by joining
+    // both streams.
+    hipStream_t sy = p->sd;
+    if (sy != s) {
+      HIP_CHECK(hipEventRecord(p->evD0, s));
+      HIP_CHECK(hipStreamWaitEvent(sy, p->evD0, 0));
     }
+    const int ph = ph_begin(p, SPGEMM_PH_SYM_HEAVY, sy);
+    int32_t* next = alloc_n<int32_t>(p, 1, sy);
+    launch_fill_i32(next, 0, 1, sy);
+    launch_sym_heavy_rows(h, p->nreq, log2_exact(W), p->xheavy, row_args(p), p->nnzB,
+                          p->slotNnz, next, p->numCUs, (size_t)p->lds, sy);
+    ph_end(p, ph, sy);
+    launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, sy);
+    Batch B;
+    expand_batch(p, p->batches[0].first, p->batches[0].second, true, true, &B);
+    p->st.final_chunks += B.nfc;
+    p->st.dense_chunks += B.denseChunks;
+    for (int l = 0; l < 8; ++l) p->st.level_elems[l] += B.levelElems[l];
+    p->kept = B;
+    p->haveKept = true;
+    p->keptDesc = alloc_n<ChunkDesc>(p, B.nfc, s);
   }
-  launch_slot_scan(h, p->nreq, p->slotNnz, p->slotOff, p->xheavy, p->cnt, s);
   check_launch("heavy symbolic");
 }
 
 void heavy_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
-  if (p->haveKept) {
-    numeric_batch(p, p->kept, ccol, cval, p->keptDesc);
-    return;
-  }
-  for (const auto& bt : p->batches) {
+  // The first batch was expanded in symbolic; the others are expanded here,
+  // one after another, each into the same memory.
+  if (p->haveKept) numeric_batch(p, p->kept, ccol, cval, p->keptDesc);
+  for (size_t i = p->haveKept ? 1 : 0; i < p->batches.size(); ++i) {
+    const auto& bt = p->batches[i];
     const WsMark mk = ws_mark(p);
     Batch B;
     expand_batch(p, bt.first, bt.second, true, true, &B);
@@ -1728,7 +1723,7 @@ spgemm_status spgemm_get_stats(spgemm_plan_t p, spgemm_stats* out) {
       const int32_t word = read_err(p, p->stream);
       p->st.device_errors = word;
       if (p->opts.profile) ph_collect(p);
-      if (p->state >= 2 && p->h > 0 && !p->haveKept) {
+      if (p->state >= 2 && p->h > 0 && !p->symVals) {
         // the batched schedule bins the chunks (and counts the dense
         // accumulators' products) in numeric
         HIP_CHECK(hipMemcpyAsync(p->hStats + 24, p->stats + kStatDenseElems, 8,
