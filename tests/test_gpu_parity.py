@@ -237,14 +237,17 @@ def test_options_do_not_change_the_result():
         np.testing.assert_array_equal(val, ref[2])
 
 
+@pytest.mark.parametrize("direct", [0, 1], ids=["expanded", "dense_direct"])
 @pytest.mark.parametrize("budget", [1, 200_000])
-def test_heavy_rows_in_batches(budget):
+def test_heavy_rows_in_batches(budget, direct):
     # A memory budget far below the intermediate's size splits the heavy rows
-    # into batches (one row each at budget 1); symbolic keeps only chunk
-    # counts and numeric expands every batch again.
+    # into batches (one row each at budget 1); symbolic counts every heavy
+    # row's slots from A and B and expands the first batch, numeric expands
+    # the others (with dense_direct: their light chunks only, the dense ones
+    # from run lists).
     A = synth.rmat(11 if budget == 1 else 12, 16, seed=5)
     A.val = np.round(A.val * 6 - 3)
-    opts = dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4)
+    opts = dict(heavy_threshold=64, dense_width=256, max_chunks_per_level=4, dense_direct=direct)
     st = check_full(A, A, exact=True, mem_budget=budget, **opts)
     assert st["batches"] > 1
     if budget == 1:
