@@ -1774,6 +1774,7 @@ struct spgemm_prune_s {
   hipStream_t stream = nullptr;
   int64_t *keep = nullptr, *off = nullptr, *tmp = nullptr;
   double* colsum = nullptr;
+  void* buckets = nullptr;  // column buckets of the count (fill, columns, values)
   int64_t nnzOut = 0;
   int state = 0;
   std::string err;
@@ -1783,7 +1784,7 @@ struct spgemm_prune_s {
 namespace {
 void prune_free(spgemm_prune_t p) {
   if (!p) return;
-  for (void* ptr : {(void*)p->keep, (void*)p->off, (void*)p->tmp, (void*)p->colsum})
+  for (void* ptr : {(void*)p->keep, (void*)p->off, (void*)p->tmp, (void*)p->colsum, p->buckets})
     if (ptr) (void)hipFreeAsync(ptr, p->stream);
   if (p->hbuf) {
     (void)hipStreamSynchronize(p->stream);
@@ -1824,20 +1825,54 @@ spgemm_status prune_count(bool mcl, spgemm_prune_t* out, int64_t m, int64_t n,
     HIP_CHECK(hipMallocAsync((void**)&p->tmp, sizeof(int64_t) * (scan_tmp_elems(m) + 1), s));
     HIP_CHECK(hipMallocAsync((void**)&p->colsum, sizeof(double) * std::max<int64_t>(n, 1), s));
     launch_fill_i64((int64_t*)p->colsum, 0, n, s);  // +0.0 has an all-zero bit pattern
+    // Column buckets for the count's column sums (each work group's LDS
+    // table and the entries it misses): room for min(nnz(C), 2^29) entries
+    // spread evenly (full buckets fall back to global adds).
+    int log2Cols = 0;
+    int32_t nb = 0;
+    int64_t cap = 0;
+    unsigned long long* fill = nullptr;
+    int32_t* bcol = nullptr;
+    double* bval = nullptr;
+    if (m > 0 && prune_buckets_fit(n, &log2Cols, &nb)) {
+      HIP_CHECK(hipMemcpyAsync(p->hbuf, (const char*)p->rp + m * (p->rp64 ? 8 : 4),
+                               p->rp64 ? 8 : 4, hipMemcpyDeviceToHost, s));
+      HIP_CHECK(hipStreamSynchronize(s));
+      const int64_t nnzC = p->rp64 ? p->hbuf[0] : (int64_t)((const int32_t*)p->hbuf)[0];
+      cap = (std::min<int64_t>(nnzC, (int64_t)1 << 29) + nb - 1) / nb;
+      if (cap > 0) {
+        const size_t bytes = 8 * (size_t)nb + (size_t)nb * cap * 12;
+        HIP_CHECK(hipMallocAsync(&p->buckets, bytes, s));
+        fill = (unsigned long long*)p->buckets;
+        bval = (double*)(fill + nb);
+        bcol = (int32_t*)(bval + (size_t)nb * cap);
+        launch_fill_i64((int64_t*)fill, 0, nb, s);
+      }
+    }
+    auto count = [&](double thr) {
+      if (fill)
+        launch_prune_count_b(m, n, p->rp, p->rp64, p->col, p->val, p->f64, thr, p->keep,
+                             p->colsum, nb, log2Cols, cap, fill, bcol, bval, s);
+      else
+        launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, thr, p->keep, p->colsum,
+                           s);
+    };
     if (mcl) {
       // Column sums of every entry, then the kept count of every row.
-      launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, -INFINITY, p->keep,
-                         p->colsum, s);
+      count(-INFINITY);
       launch_mcl_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->colsum, p->keep, s);
     } else {
-      launch_prune_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->keep, p->colsum,
-                         s);
+      count(p->thr);
     }
     launch_scan_i64(p->keep, m, p->off, p->tmp, s);
     check_launch("prune count");
     HIP_CHECK(hipMemcpyAsync(p->hbuf, p->off + m, 8, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
     p->nnzOut = p->hbuf[0];
+    if (p->buckets) {  // only the count uses them
+      HIP_CHECK(hipFreeAsync(p->buckets, s));
+      p->buckets = nullptr;
+    }
     if (!out_rowptr64 && p->nnzOut > INT32_MAX)
       throw Error{SPGEMM_ERR_INDEX_OVERFLOW, "kept entries exceed INT32_MAX"};
     launch_write_rowptr(p->off, m + 1, dOut_row_ptr, out_rowptr64 ? 1 : 0, s);

@@ -34,8 +34,9 @@ constexpr int kPruneSlots = 4096;
 constexpr int kPruneProbes = 4;
 constexpr int kPruneU = 4;
 
+template <int SLOTS = kPruneSlots>
 __device__ __forceinline__ bool colsum_add_lds(int32_t* keys, double* vals, int32_t key, double v) {
-  uint32_t s = hash_slot(key, kPruneSlots);
+  uint32_t s = hash_slot(key, SLOTS);
   for (int probe = 0; probe < kPruneProbes; ++probe) {
     const int32_t cur = lds_load_relaxed(&keys[s]);
     if (cur == key) {
@@ -49,7 +50,7 @@ __device__ __forceinline__ bool colsum_add_lds(int32_t* keys, double* vals, int3
         return true;
       }
     }
-    s = (s + 1 == kPruneSlots) ? 0 : s + 1;
+    s = (s + 1 == SLOTS) ? 0 : s + 1;
   }
   return false;
 }
@@ -97,6 +98,148 @@ __global__ __launch_bounds__(kPruneNT) void k_prune_count(int64_t m, const void*
   for (int i = threadIdx.x; i < kPruneSlots; i += kPruneNT) {
     const int32_t c = keys[i];
     if (c != kEmptyKey) unsafeAtomicAdd(&colsum[c], vals[i]);
+  }
+}
+
+// The same count with no global add per column: the LDS table's misses
+// (mostly columns met once by the work group, such as entries between
+// clusters) are kept in an LDS list, and at the end the work group counts
+// the list and its table's columns per bucket of 2^log2Cols columns,
+// reserves each bucket's range with one global add, and writes them there as
+// (column, fp64 value); k_colsum_buckets then adds each bucket up in LDS.  A
+// full list or bucket falls back to the global add.
+constexpr int kPruneBNT = 1024;
+constexpr int kPruneBRows = 40;
+constexpr int kPruneBSlots = 4096;
+constexpr int kMissCap = 8192;
+constexpr int kMaxBuckets = 1024;
+constexpr int kBucketSplit = 4;  // work groups per bucket in k_colsum_buckets
+
+template <typename V, typename RP>
+__global__ __launch_bounds__(kPruneBNT) void k_prune_count_b(int64_t m, const void* __restrict__ rp,
+                                                             const int32_t* __restrict__ col,
+                                                             const V* __restrict__ val, V thr,
+                                                             int64_t* __restrict__ keep,
+                                                             double* __restrict__ colsum,
+                                                             int32_t nb, int log2Cols, int64_t cap,
+                                                             unsigned long long* __restrict__ fill,
+                                                             int32_t* __restrict__ bcol,
+                                                             double* __restrict__ bval) {
+  __shared__ int32_t keys[kPruneBSlots];
+  __shared__ double vals[kPruneBSlots];
+  __shared__ int32_t missCol[kMissCap];
+  __shared__ V missVal[kMissCap];
+  __shared__ int32_t hist[kMaxBuckets];
+  __shared__ int64_t base[kMaxBuckets];
+  __shared__ int32_t nMiss;
+  for (int i = threadIdx.x; i < kPruneBSlots; i += kPruneBNT) {
+    keys[i] = kEmptyKey;
+    vals[i] = 0.0;
+  }
+  for (int i = threadIdx.x; i < nb; i += kPruneBNT) hist[i] = 0;
+  if (threadIdx.x == 0) nMiss = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * kPruneBRows;
+  const int w = threadIdx.x / kWave;
+  for (int64_t r = r0 + w; r < r0 + kPruneBRows && r < m; r += kPruneBNT / kWave) {
+    const int64_t a = rp_at<RP>(rp, r), b = rp_at<RP>(rp, r + 1);
+    int64_t kept = 0;
+    for (int64_t e0 = a; e0 < b; e0 += kWave * kPruneU) {
+      V x[kPruneU];
+      int32_t c[kPruneU];
+      bool act[kPruneU];
+#pragma unroll
+      for (int u = 0; u < kPruneU; ++u) {
+        const int64_t e = e0 + u * kWave + lane_id();
+        act[u] = e < b;
+        x[u] = act[u] ? val[e] : V(0);
+        c[u] = act[u] ? col[e] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kPruneU; ++u) {
+        const bool k = act[u] && x[u] >= thr;
+        if (k && !colsum_add_lds<kPruneBSlots>(keys, vals, c[u], (double)x[u])) {
+          const int at = atomicAdd(&nMiss, 1);
+          if (at < kMissCap) {
+            missCol[at] = c[u];
+            missVal[at] = x[u];
+          } else {
+            unsafeAtomicAdd(&colsum[c[u]], (double)x[u]);
+          }
+        }
+        kept += __popcll(__ballot(k));
+      }
+    }
+    if (lane_id() == 0) keep[r] = kept;
+  }
+  __syncthreads();
+  // Bucket counts of the table's columns and of the list, one reservation
+  // per bucket, then both written out.
+  const int nm = min(nMiss, kMissCap);
+  for (int i = threadIdx.x; i < kPruneBSlots + nm; i += kPruneBNT) {
+    const int32_t c = i < kPruneBSlots ? keys[i] : missCol[i - kPruneBSlots];
+    if (c == kEmptyKey) continue;
+    const uint32_t bk = (uint32_t)c >> log2Cols;
+    if (bk < (uint32_t)nb) atomicAdd(&hist[bk], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += kPruneBNT) {
+    const int32_t h = hist[i];
+    base[i] = h ? (int64_t)atomicAdd(&fill[i], (unsigned long long)h) : 0;
+    hist[i] = 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPruneBSlots + nm; i += kPruneBNT) {
+    int32_t c;
+    double v;
+    if (i < kPruneBSlots) {
+      c = keys[i];
+      v = vals[i];
+    } else {
+      c = missCol[i - kPruneBSlots];
+      v = (double)missVal[i - kPruneBSlots];
+    }
+    if (c == kEmptyKey) continue;
+    const uint32_t bk = (uint32_t)c >> log2Cols;
+    const int64_t p = bk < (uint32_t)nb ? base[bk] + atomicAdd(&hist[bk], 1) : cap;
+    if (p < cap) {
+      bcol[bk * cap + p] = c;
+      bval[bk * cap + p] = v;
+    } else {
+      unsafeAtomicAdd(&colsum[c], v);
+    }
+  }
+}
+
+// kBucketSplit work groups per bucket, each adding its share of the
+// bucket's entries up in LDS (fp64) and each column's partial sum into
+// colsum.
+constexpr int kSumNT = 1024;
+__global__ __launch_bounds__(kSumNT) void k_colsum_buckets(int64_t n, int log2Cols, int64_t cap,
+                                                              const unsigned long long* __restrict__ fill,
+                                                              const int32_t* __restrict__ bcol,
+                                                              const double* __restrict__ bval,
+                                                              double* __restrict__ colsum) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  double* sums = (double*)smem;
+  const int cols = 1 << log2Cols;
+  const int64_t bk = blockIdx.x / kBucketSplit;
+  const int part = blockIdx.x % kBucketSplit;
+  const int64_t c0 = bk << log2Cols;
+  for (int j = threadIdx.x; j < cols; j += kSumNT) sums[j] = 0.0;
+  __syncthreads();
+  const int64_t cnt = min<int64_t>((int64_t)fill[bk], cap);
+  const int64_t i0 = cnt * part / kBucketSplit, i1 = cnt * (part + 1) / kBucketSplit;
+  const int32_t* bc = bcol + bk * cap;
+  const double* bv = bval + bk * cap;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += kSumNT) {
+    const int64_t j = (int64_t)bc[i] - c0;
+    if (j >= 0 && j < cols) atomicAdd(&sums[j], bv[i]);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < cols; j += kSumNT) {
+    const int64_t c = c0 + j;
+    if (c < n && sums[j] != 0.0) unsafeAtomicAdd(&colsum[c], sums[j]);
   }
 }
 
@@ -253,6 +396,35 @@ void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col,
       hipLaunchKernelGGL((k_prune_count<float, int32_t>), g, b, 0, s, m, rp, col,
                          (const float*)val, (float)thr, keepCnt, colsum);
   }
+}
+
+bool prune_buckets_fit(int64_t n, int* log2Cols, int32_t* nb) {
+  int lg = 11;
+  while (lg < 14 && ((n + ((int64_t)1 << lg) - 1) >> lg) > kMaxBuckets) ++lg;
+  const int64_t b = (n + ((int64_t)1 << lg) - 1) >> lg;
+  if (n <= 0 || b > kMaxBuckets) return false;
+  *log2Cols = lg;
+  *nb = (int32_t)b;
+  return true;
+}
+
+void launch_prune_count_b(int64_t m, int64_t n, const void* rp, int rp64, const int32_t* col,
+                          const void* val, bool f64, double thr, int64_t* keepCnt, double* colsum,
+                          int32_t nb, int log2Cols, int64_t cap, unsigned long long* fill,
+                          int32_t* bcol, double* bval, hipStream_t s) {
+  if (m <= 0) return;
+  const dim3 g((unsigned)((m + kPruneBRows - 1) / kPruneBRows)), b(kPruneBNT);
+#define L(V, RP)                                                                               \
+  hipLaunchKernelGGL((k_prune_count_b<V, RP>), g, b, 0, s, m, rp, col, (const V*)val, (V)thr,   \
+                     keepCnt, colsum, nb, log2Cols, cap, fill, bcol, bval)
+  if (f64 && rp64) L(double, int64_t);
+  else if (f64) L(double, int32_t);
+  else if (rp64) L(float, int64_t);
+  else L(float, int32_t);
+#undef L
+  const size_t lds = sizeof(double) << log2Cols;
+  hipLaunchKernelGGL(k_colsum_buckets, dim3((unsigned)nb * kBucketSplit), dim3(kSumNT), lds, s,
+                     n, log2Cols, cap, fill, bcol, bval, colsum);
 }
 
 void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,

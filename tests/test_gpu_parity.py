@@ -439,6 +439,37 @@ def test_planted_partition_small_with_prune():
     assert ecol.size == int(((ref32 >= np.float32(1e-4)) & ~band).sum() + (keep[band] == 1).sum())
 
 
+def _random_csr(m, n, per_row, col_hi, seed, dtype):
+    """m x n CSR, per_row distinct columns per row drawn from [0, col_hi),
+    values multiples of 1/64 in (0, 1] (no value meets a threshold of 0.3)."""
+    rng = np.random.default_rng(seed)
+    cols = [np.sort(rng.choice(col_hi, per_row, replace=False)) for _ in range(m)]
+    col = np.concatenate(cols).astype(np.int32)
+    val = (rng.integers(1, 65, col.size) / 64.0).astype(dtype)
+    rp = np.arange(0, m * per_row + 1, per_row, dtype=np.int32)
+    return synth.CSR(rp, col, val, m, n)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("case", ["one_bucket", "scattered"])
+def test_prune_column_sums_past_their_buckets(case, dtype):
+    # The prune's column sums go through column buckets sized for nnz(C)
+    # spread evenly; entries that do not fit fall back to global adds.
+    # one_bucket: every column lies in the first of four buckets, so three
+    # quarters of its entries overflow.  scattered: a work group's 40 rows
+    # hold 32,000 nearly distinct columns, past its LDS table and its list.
+    if case == "one_bucket":
+        C = _random_csr(3000, 8192, 50, 2048, 7, dtype)
+    else:
+        C = _random_csr(400, 200_000, 800, 200_000, 8, dtype)
+    dC = sg.to_device(C)
+    orp, ocol, oval = sg.prune_colnorm(dC.row_ptr, dC.col, dC.val, C.m, C.n, 0.3)
+    erp, ecol, evals = oracle.prune_colnorm(C.m, C.n, C.row_ptr, C.col, C.val.astype(np.float64), 0.3)
+    assert_csr_equal_structure(_to_np(orp, np.int64), _to_np(ocol), erp, ecol, "pruned")
+    np.testing.assert_allclose(_to_np(oval).astype(np.float64), evals,
+                               rtol=1e-5 if dtype == np.float32 else 1e-12, atol=0)
+
+
 def _check_mcl_inflate(rp, col, val, m, n, thr, dtype):
     """GPU MCL inflation of C (device CSR) against the oracle on the same C;
     normalised values within 1e-6 relative of the threshold may go either
