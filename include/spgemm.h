@@ -242,6 +242,8 @@ typedef struct spgemm_stats {
   int64_t light_capacity;     /* output slots reserved for light rows (1, 2)   */
   int64_t overflow_rows;      /* light rows computed again with P_i slots      */
   double sampled_cr;          /* compression ratio of the row sample (mode 3)  */
+  double phase_min_ms[16];    /* shortest window of each phase (with profile;
+                                 0 for a phase with no window)              */
 } spgemm_stats;
 
 typedef struct spgemm_plan_s *spgemm_plan_t;

@@ -69,15 +69,18 @@ class Stats(ctypes.Structure):
         ("heavy_row_threshold", c_i64), ("chunk_col_bytes", c_i64),
         ("workflow", c_i32), ("hll_registers", c_i32), ("light_capacity", c_i64),
         ("overflow_rows", c_i64), ("sampled_cr", ctypes.c_double),
+        ("phase_min_ms", ctypes.c_double * 16),
     ]
 
     def as_dict(self):
         d = {name: getattr(self, name) for name, _ in self._fields_
-             if name not in ("params", "level_elems", "phase_ms", "phase_windows")}
+             if name not in ("params", "level_elems", "phase_ms", "phase_windows",
+                             "phase_min_ms")}
         d["params"] = self.params.as_dict()
         d["level_elems"] = list(self.level_elems[:self.params.levels])
         d["phase_ms"] = {PHASES[i]: self.phase_ms[i] for i in range(len(PHASES))}
         d["phase_windows"] = {PHASES[i]: self.phase_windows[i] for i in range(len(PHASES))}
+        d["phase_min_ms"] = {PHASES[i]: self.phase_min_ms[i] for i in range(len(PHASES))}
         return d
 
 

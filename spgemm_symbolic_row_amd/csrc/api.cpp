@@ -398,12 +398,15 @@ void ph_collect(spgemm_plan_t p) {
   for (int i = 0; i < 16; ++i) {
     p->st.phase_ms[i] = 0;
     p->st.phase_windows[i] = 0;
+    p->st.phase_min_ms[i] = 0;
   }
   for (auto& r : p->phases) {
     HIP_CHECK(hipEventSynchronize(r.b));
     float ms = 0;
     HIP_CHECK(hipEventElapsedTime(&ms, r.a, r.b));
     p->st.phase_ms[r.id] += ms;
+    if (p->st.phase_windows[r.id] == 0 || ms < p->st.phase_min_ms[r.id])
+      p->st.phase_min_ms[r.id] = ms;
     p->st.phase_windows[r.id] += 1;
   }
 }
