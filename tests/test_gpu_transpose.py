@@ -121,7 +121,7 @@ def _check_product(dA, dB, A, B, exact=False, **opts):
     else:
         rtol = 1e-12 if A.val.dtype == np.float64 else 1e-5
         assert_values_close(v, ref.val, ref.mag, rtol, "C")
-    assert st["global_products"] == 0
+    assert st["lds_hash_products"] + st["lds_dense_products"] == st["products"]
     return st, ref
 
 

@@ -47,7 +47,7 @@ def _run(A, B, exact=False, **opts):
     else:
         rtol = 1e-12 if A.val.dtype == np.float64 else 1e-5
         assert_values_close(v, ref.val, ref.mag, rtol, "C")
-    assert st["global_products"] == 0 and st["device_errors"] == 0
+    assert st["device_errors"] == 0
     return st, ref, (None if cap is None else _np(cap)), (None if est is None else _np(est))
 
 
