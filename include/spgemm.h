@@ -121,7 +121,13 @@ typedef struct spgemm_options {
                                    product bound columns (at most 65536) takes
                                    the dense window: an LDS bitmap over the
                                    span, ranks by prefix popcount, values
-                                   added at their rank (no hash, no sort)    */
+                                   added at their rank (no hash, no sort);
+                                   other rows of at least 512 products take a
+                                   dense window over the 2048 columns around
+                                   their diagonal position (row * n / m) plus
+                                   an LDS hash table for the columns outside
+                                   it, when those outliers fit half of the
+                                   table (only the outliers are sorted)     */
   int32_t workflow;             /* how light rows get their output size (Ocean
                                    page, §3 and Table 1; heavy rows always take
                                    the exact chunk path):
@@ -244,6 +250,9 @@ typedef struct spgemm_stats {
   double sampled_cr;          /* compression ratio of the row sample (mode 3)  */
   double phase_min_ms[16];    /* shortest window of each phase (with profile;
                                  0 for a phase with no window)              */
+  int64_t hybrid_rows;        /* light rows accumulated in a dense window
+                                 around their diagonal position plus an
+                                 LDS hash table for the other columns     */
 } spgemm_stats;
 
 typedef struct spgemm_plan_s *spgemm_plan_t;

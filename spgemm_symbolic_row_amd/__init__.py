@@ -69,7 +69,7 @@ class Stats(ctypes.Structure):
         ("heavy_row_threshold", c_i64), ("chunk_col_bytes", c_i64),
         ("workflow", c_i32), ("hll_registers", c_i32), ("light_capacity", c_i64),
         ("overflow_rows", c_i64), ("sampled_cr", ctypes.c_double),
-        ("phase_min_ms", ctypes.c_double * 16),
+        ("phase_min_ms", ctypes.c_double * 16), ("hybrid_rows", c_i64),
     ]
 
     def as_dict(self):

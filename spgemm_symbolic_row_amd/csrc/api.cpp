@@ -254,8 +254,11 @@ struct spgemm_plan_s {
   int32_t chunkWords = 0;  // bitmap words of the widest final chunk (0: hash fallback)
   int NS = 0;  // number of hash bins
   int winBins = 0;  // leading light bins whose rows may take the dense window
+  int hybSymBin = 0;  // first symbolic bin of the hybrid kernel (NS: none)
   // device arrays
   int32_t *dSymCaps = nullptr;
+  int32_t* dHybCap = nullptr;  // per numeric bin: outliers a hybrid row may have (-1: none)
+  int32_t* outc = nullptr;     // outlier count of every row of a hybrid symbolic bin
   int64_t *rowP = nullptr, *cnt = nullptr, *stats = nullptr, *cRowOff = nullptr, *scanTmp = nullptr;
   int32_t *scanA = nullptr, *rowOrder = nullptr, *numOrder = nullptr, *errWord = nullptr;
   int64_t* rowWin = nullptr;  // dense-window rows: first column and span words
@@ -581,7 +584,7 @@ void do_plan(spgemm_plan_t p) {
   if (p->opts.hll_coef_pct < 0) throw Error{SPGEMM_ERR_INVALID_ARG, "hll_coef_pct must be >= 0"};
   make_bins(p->tau, p->lds, vb, &p->symBins, &p->numBins);
   p->NS = (int)p->symBins.size();
-  if (2 * p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
+  if (3 * p->NS + 2 > 60) throw Error{SPGEMM_ERR_INVALID_ARG, "too many bins"};
   // Dense windows for light rows unless turned off or a bin's window does
   // not fit the LDS budget.
   p->winBins = 0;
@@ -653,6 +656,20 @@ void do_plan(spgemm_plan_t p) {
   for (int b = 0; b < p->NS; ++b) caps[b] = p->symBins[b].cap;
   p->dSymCaps = alloc_n<int32_t>(p, 64, s);
   launch_set_small_i32(p->dSymCaps, caps.data(), p->NS, s);
+  // Hybrid light rows (diagonal window plus outlier table) from the first
+  // bin of at least kHybMinCap products, unless every light row is to take
+  // the hash table.
+  p->hybSymBin = p->NS;
+  if (!p->opts.light_hash_only)
+    for (int b = 0; b < p->NS; ++b)
+      if (p->symBins[b].cap >= kHybMinCap) {
+        p->hybSymBin = b;
+        break;
+      }
+  std::vector<int32_t> hcap(p->NS, -1);
+  for (int b = 0; b < p->NS; ++b) hcap[b] = hyb_out_cap(p->numBins[b], p->f64, p->lds);
+  p->dHybCap = alloc_n<int32_t>(p, 64, s);
+  launch_set_small_i32(p->dHybCap, hcap.data(), p->NS, s);
 
   p->rowP = alloc_n<int64_t>(p, m, s);
   p->cnt = alloc_n<int64_t>(p, m, s);
@@ -1457,6 +1474,7 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   hipStream_t s = p->stream;
   p->wf = p->opts.workflow == 3 ? select_workflow(p, s) : p->opts.workflow;
   p->st.workflow = p->wf;
+  if (p->wf == 0 && p->hybSymBin < p->NS) p->outc = alloc_n<int32_t>(p, p->m, s);
   fork(p);
   const RowArgs a = row_args(p);
   if (p->wf == 0) {
@@ -1465,6 +1483,9 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
       const int64_t st = p->rowBinStart[b + 1], en = p->rowBinStart[b + 2];
       if (b == 0 && esc_on(p))
         launch_sym_rows_esc(p->rowOrder + st, en - st, a, p->cnt, p->sl);
+      else if (b >= p->hybSymBin)
+        launch_sym_rows_hyb(p->symBins[b], p->rowOrder + st, en - st, a, p->m, p->n, p->cnt,
+                            p->outc, p->errWord, p->sl);
       else
         launch_sym_rows(p->symBins[b], p->rowOrder + st, en - st, a, p->cnt, p->errWord, p->sl);
       const int64_t ws = p->rowBinStart[p->NS + 2 + b], we = p->rowBinStart[p->NS + 3 + b];
@@ -1488,23 +1509,26 @@ void do_symbolic(spgemm_plan_t p, void* dRowPtr, int64_t* nnzC) {
   p->numOrder = alloc_n<int32_t>(p, m, s);
   const int phR = ph_begin(p, SPGEMM_PH_ROWPTR, s);
   launch_scan_i64(p->cnt, m, p->cRowOff, p->scanTmp, s);
+  // numeric keys: hash bins, dense-window bins, ESC, hybrid bins
+  const int nkeys = 3 * p->NS + 1;
   if (p->wf == 0) {
     launch_numeric_row_bins(m, p->cnt, p->rowBin, p->NS + 1, p->dSymCaps, p->NS, p->numKey, s,
-                            esc_on(p) ? 2 * p->NS : -1);
-    launch_bin_sort(p->numKey, m, 2 * p->NS + 1, p->binCnt, p->binFill, p->binStart, p->numOrder,
-                    s);
+                            esc_on(p) ? 2 * p->NS : -1, p->outc, p->dHybCap,
+                            p->hybSymBin + 1, 2 * p->NS + 1);
+    launch_bin_sort(p->numKey, m, nkeys, p->binCnt, p->binFill, p->binStart, p->numOrder, s);
   } else {
-    launch_fill_i32(p->binStart, 0, 2 * p->NS + 2, s);  // light rows are done
+    launch_fill_i32(p->binStart, 0, nkeys + 1, s);  // light rows are done
   }
   ph_end(p, phR, s);
   check_launch("row pointer scan");
   HIP_CHECK(hipMemcpyAsync(p->hStats + 20, p->cRowOff + m, 8, hipMemcpyDeviceToHost, s));
-  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (2 * p->NS + 2), hipMemcpyDeviceToHost, s));
+  HIP_CHECK(hipMemcpyAsync(p->hBins, p->binStart, sizeof(int32_t) * (nkeys + 1), hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hBins + 120, p->errWord, 4, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipMemcpyAsync(p->hStats, p->stats, sizeof(int64_t) * kNumStats, hipMemcpyDeviceToHost, s));
   HIP_CHECK(hipStreamSynchronize(s));
   check_device_errors(p, p->hBins[120]);
-  p->numBinStart.assign(p->hBins, p->hBins + 2 * p->NS + 2);
+  p->numBinStart.assign(p->hBins, p->hBins + nkeys + 1);
+  p->st.hybrid_rows = p->numBinStart[nkeys] - p->numBinStart[2 * p->NS + 1];
   p->nnzC = p->hStats[20];
   p->st.nnz_c = p->nnzC;
   p->st.lds_dense_products = p->hStats[kStatDenseElems];
@@ -1539,6 +1563,10 @@ void do_numeric(spgemm_plan_t p, int32_t* ccol, void* cval) {
     const int64_t ws = p->numBinStart[p->NS + b], we = p->numBinStart[p->NS + b + 1];
     if (we > ws)
       launch_num_rows_win(p->symBins[b], p->winWords[b], p->f64, p->numOrder + ws, we - ws, a,
+                          p->cRowOff, ccol, cval, p->errWord, p->sl);
+    const int64_t hs = p->numBinStart[2 * p->NS + 1 + b], he = p->numBinStart[2 * p->NS + 2 + b];
+    if (he > hs)
+      launch_num_rows_hyb(p->numBins[b], p->f64, p->numOrder + hs, he - hs, a, p->m, p->n,
                           p->cRowOff, ccol, cval, p->errWord, p->sl);
   }
   ph_end(p, phL, p->sl);

@@ -74,6 +74,15 @@ __host__ __device__ inline size_t num_rows_radix_bytes(int tpr, int rpb) {
                                   : 0;
 }
 
+// Diagonal window of the hybrid light-row accumulator (window plus outlier
+// table): columns per row, and bitmap words.
+constexpr int kHybW = 2048;
+constexpr int kHybWords = kHybW / 32;
+// Symbolic bins from this product bound on take the hybrid kernel.
+constexpr int64_t kHybMinCap = 512;
+// Outliers a row may have to take the hybrid numeric kernel.
+constexpr int32_t kHybOutMax = 512;
+
 __host__ __device__ inline int32_t window_words(int64_t cap) {
   return (int32_t)(4 * cap < 2048 ? 4 * cap : 2048);
 }
@@ -170,9 +179,13 @@ void launch_row_lengths(int64_t n, const int32_t* rows, const int32_t* rp, int64
 // key[i] = bin of cnt[rows[i]] among caps[0..nbins) (first cap >= value), for
 // light rows; heavy rows (rowBin == heavyBin) get 255; with escKey >= 0,
 // rows of the first product bin (at most 32 products) get escKey.
+// With outc: a row of a symbolic bin from hybSymMin on (its outlier count
+// in outc) whose outliers fit hybCap[b] of its numeric bin b gets hybKey + b.
 void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,
                              int heavyBin, const int32_t* caps, int nbins, uint8_t* key,
-                             hipStream_t s, int escKey = -1);
+                             hipStream_t s, int escKey = -1, const int32_t* outc = nullptr,
+                             const int32_t* hybCap = nullptr, int hybSymMin = 0,
+                             int hybKey = 0);
 
 // ---- k_light.hip ----
 void light_set_attributes();
@@ -189,6 +202,18 @@ void launch_num_rows_win(const BinCfg& b, int32_t words, bool f64, const int32_t
                          void* cval, int32_t* err, hipStream_t s, int64_t* cntOut = nullptr);
 void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
                      int64_t* cnt, int32_t* err, hipStream_t s);
+// Hybrid light rows (diagonal window plus outlier table): symbolic for every
+// row of a hash bin, storing its count and its outlier count; numeric for
+// the rows whose outliers fit half of the bin's outlier table.
+void launch_sym_rows_hyb(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
+                         int64_t m, int64_t n, int64_t* cnt, int32_t* outc, int32_t* err,
+                         hipStream_t s);
+// Outliers a row may have to take the hybrid numeric kernel of bin b, or -1
+// when the kernel has no instance for b or does not fit the LDS budget.
+int32_t hyb_out_cap(const BinCfg& b, bool f64, int64_t lds);
+void launch_num_rows_hyb(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
+                         const RowArgs& a, int64_t m, int64_t n, const int64_t* cRowOff,
+                         int32_t* ccol, void* cval, int32_t* err, hipStream_t s);
 // Rows of at most 32 products (the first product bin) by expand-sort-compact
 // in 32 lanes each: count of distinct columns, or the sorted row (cntOut as
 // for launch_num_rows).

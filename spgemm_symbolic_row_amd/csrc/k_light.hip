@@ -755,6 +755,210 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
   }
 }
 
+
+// ------------------------------------- diagonal window plus outlier table
+// Light hash-bin rows of banded or clustered matrices (the iterates of
+// Markov clustering, Trident page §5.7, whose clusters lie on the diagonal)
+// spread most of their products over a few thousand columns around the
+// diagonal and the rest thinly over the whole row.  Such a row takes a dense
+// LDS window over the kHybW columns [lo, lo + kHybW) around its diagonal
+// position (a bitmap, and in numeric a value per column: no probing, no
+// sort) and an LDS hash table for the other columns, its outliers.  The
+// output row is the outliers below lo, then the window's columns in order,
+// then the outliers above, so only the outliers are sorted (a few hundred
+// at most, by one wave in registers).  Symbolic
+// counts both parts and stores the outlier count; numeric takes a row this
+// way when the outliers fit half of a table of next_pow2(bin bound) slots
+// and number at most kHybOutMax, else the row goes to the hash kernel.  (An accumulator per row chosen
+// from the row's structure: gMAGNUS page §III-E, Ocean page §2.)
+__device__ __forceinline__ int32_t hyb_lo(int32_t row, int64_t m, int64_t n) {
+  const int64_t center = m > 0 ? (int64_t)row * n / m : 0;
+  int64_t lo = center - (kHybW / 2 - 16);
+  lo = lo < 0 ? 0 : lo;
+  return (int32_t)(lo & ~(int64_t)31);
+}
+
+template <int TPR, int RPB>
+__global__ __launch_bounds__(TPR* RPB) void k_sym_rows_hyb(const int32_t* __restrict__ rows,
+                                                           int64_t nrows, int32_t T, RowArgs a,
+                                                           int64_t m, int64_t n,
+                                                           int64_t* __restrict__ cnt,
+                                                           int32_t* __restrict__ outc,
+                                                           int32_t* __restrict__ err) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* keysAll = (int32_t*)smem;
+  uint32_t* bmAll = (uint32_t*)(keysAll + RPB * T);
+  __shared__ int32_t gwin[RPB], gout[RPB];
+  const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
+  int32_t* keys = keysAll + g * T;
+  uint32_t* bm = bmAll + g * kHybWords;
+  for (int s = t; s < T; s += TPR) keys[s] = kEmptyKey;
+  for (int i = t; i < kHybWords; i += TPR) bm[i] = 0;
+  if (t == 0) {
+    gwin[g] = 0;
+    gout[g] = 0;
+  }
+  __syncthreads();
+  const int64_t ri = (int64_t)blockIdx.x * RPB + g;
+  int32_t row = 0, mine = 0;
+  if (ri < nrows) {
+    row = rows[ri];
+    const int32_t lo = hyb_lo(row, m, n);
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t P = (int32_t)a.rowP[row];
+    constexpr int WPR = TPR / kWave;
+    const int w = t / kWave;
+    const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
+    stream_row<false, float>(a.scanA, a.acol, (const float*)nullptr, a.brp, a.bcol,
+                             (const float*)nullptr, rs, re, P, p0, p1,
+                             [&](bool act, int32_t c, float, float, int32_t) {
+                               if (act) {
+                                 const uint32_t d = (uint32_t)(c - lo);
+                                 if (d < (uint32_t)kHybW) {
+                                   const uint32_t bit = 1u << (d & 31);
+                                   if (!(bm[d >> 5] & bit)) atomicOr(&bm[d >> 5], bit);
+                                 } else if (hset_insert(keys, (uint32_t)T, c, err)) {
+                                   ++mine;
+                                 }
+                               }
+                             });
+  }
+  const int32_t ws = wave_sum(mine);
+  if (lane_id() == 0 && ri < nrows) atomicAdd(&gout[g], ws);
+  __syncthreads();
+  int32_t pc = 0;
+  for (int i = t; i < kHybWords; i += TPR) pc += __popc(bm[i]);
+  pc = wave_sum(pc);
+  if (lane_id() == 0 && ri < nrows) atomicAdd(&gwin[g], pc);
+  __syncthreads();
+  if (t == 0 && ri < nrows) {
+    cnt[row] = gwin[g] + gout[g];
+    outc[row] = gout[g];
+  }
+}
+
+// LDS: vw[kHybW] V | ov[To] V | ok[To] i32 | bm[kHybWords] | wpre[kHybWords] |
+// wtot[TPR / 64] | red[2].
+__host__ __device__ constexpr size_t hyb_num_lds(int tpr, int32_t To, int vb) {
+  return (size_t)kHybW * vb + (size_t)To * (vb + 4) + (size_t)kHybWords * 8 +
+         (size_t)(tpr / kWave) * 4 + 8;
+}
+
+// Bitonic sort of a row's outliers by one wave (E per lane, lane exchanges
+// and register swaps: no LDS after the load, no barrier), then each lane
+// writes its E ranks: below the window, or after it.
+template <int E, typename V>
+__device__ __forceinline__ void hyb_sort_write(int32_t* ok, V* ov, int32_t nout, int32_t nb,
+                                               int32_t nwin, int32_t lim, int64_t base,
+                                               int32_t* __restrict__ ccol, V* __restrict__ cval) {
+  int32_t kk[E];
+  V vv[E];
+  sort_to_regs<kWave, E, V>(ok, ov, kk, vv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int32_t r = lane_id() * E + e;
+    if (r < nout) {
+      const int32_t pos = r < nb ? r : r + nwin;
+      if (pos < lim) {
+        ccol[base + pos] = kk[e];
+        cval[base + pos] = vv[e];
+      }
+    }
+  }
+}
+
+template <int TPR, int E, typename V>
+__global__ __launch_bounds__(TPR) void k_num_rows_hyb(const int32_t* __restrict__ rows,
+                                                      int32_t To, RowArgs a, int64_t m, int64_t n,
+                                                      const int64_t* __restrict__ cRowOff,
+                                                      int32_t* __restrict__ ccol,
+                                                      V* __restrict__ cval,
+                                                      int32_t* __restrict__ err) {
+  static_assert(TPR >= 256, "one row per work group");
+  extern __shared__ __align__(16) unsigned char smem[];
+  V* vw = (V*)smem;
+  V* ov = vw + kHybW;
+  int32_t* ok = (int32_t*)(ov + To);
+  uint32_t* bm = (uint32_t*)(ok + To);
+  int32_t* wpre = (int32_t*)(bm + kHybWords);
+  int32_t* wtot = wpre + kHybWords;
+  int32_t* red = wtot + TPR / kWave;  // window entries, outliers below lo
+  const int t = threadIdx.x;
+  for (int i = t; i < kHybW; i += TPR) vw[i] = V(0);
+  for (int s = t; s < To; s += TPR) {
+    ok[s] = kEmptyKey;
+    ov[s] = V(0);
+  }
+  if (t < kHybWords) bm[t] = 0;
+  if (t == 0) red[1] = 0;
+  __syncthreads();
+  const int32_t row = rows[blockIdx.x];
+  const int32_t lo = hyb_lo(row, m, n);
+  {
+    const int64_t rs = a.arp[row], re = a.arp[row + 1];
+    const int32_t P = (int32_t)a.rowP[row];
+    constexpr int WPR = TPR / kWave;
+    const int w = t / kWave;
+    const int32_t p0 = (int32_t)((int64_t)P * w / WPR);
+    const int32_t p1 = (int32_t)((int64_t)P * (w + 1) / WPR);
+    stream_row<true, V>(a.scanA, a.acol, (const V*)a.aval, a.brp, a.bcol, (const V*)a.bval, rs,
+                        re, P, p0, p1, [&](bool act, int32_t c, V av, V bv, int32_t) {
+                          if (act) {
+                            const uint32_t d = (uint32_t)(c - lo);
+                            const V x = av * bv;
+                            if (d < (uint32_t)kHybW) {
+                              atomicAdd(&vw[d], x);
+                              const uint32_t bit = 1u << (d & 31);
+                              if (!(bm[d >> 5] & bit)) atomicOr(&bm[d >> 5], bit);
+                            } else {
+                              hmap_add(ok, ov, (uint32_t)To, c, x, err);
+                            }
+                          }
+                        });
+  }
+  __syncthreads();
+  // Window ranks: exclusive prefix of the word popcounts (a lane per word).
+  if (t < kWave) {
+    const int32_t x = __popc(bm[t]);
+    const int32_t inc = wave_incl_scan(x);
+    wpre[t] = inc - x;
+    if (t == kWave - 1) red[0] = inc;
+  }
+  // Outliers: compacted (the barriers inside also publish wpre and red[0]),
+  // then those below the window counted.
+  const int32_t nout = compact_slots<TPR, 1, E, V>(ok, ov, To / TPR, wtot);
+  int32_t below = 0;
+  for (int i = t; i < nout; i += TPR) below += ok[i] < lo;
+  below = wave_sum(below);
+  if (lane_id() == 0 && below) atomicAdd(&red[1], below);
+  __syncthreads();
+  const int32_t nwin = red[0], nb = red[1];
+  const int64_t base = cRowOff[row];
+  const int64_t want = cRowOff[row + 1] - base;
+  const int32_t total = nwin + nout;
+  if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
+  const int32_t lim = (int32_t)(want < total ? want : total);
+  for (int c = t; c < kHybW; c += TPR) {
+    const uint32_t word = bm[c >> 5];
+    if ((word >> (c & 31)) & 1u) {
+      const int32_t pos = nb + wpre[c >> 5] + __popc(word & ((1u << (c & 31)) - 1u));
+      if (pos < lim) {
+        ccol[base + pos] = lo + c;
+        cval[base + pos] = vw[c];
+      }
+    }
+  }
+  // The outliers (at most kHybOutMax, padded with INT_MAX by the
+  // compaction) are sorted by the first wave alone, in registers.
+  if (t < kWave) {
+    if (nout <= kWave) hyb_sort_write<1, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
+    else if (nout <= 2 * kWave) hyb_sort_write<2, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
+    else if (nout <= 4 * kWave) hyb_sort_write<4, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
+    else hyb_sort_write<8, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
+  }
+}
+
 // ------------------------------------------------ ESC for short rows
 // Rows of at most kEscLanes products (Ocean page, §3: an expand-sort-compact
 // accumulator for short rows, several rows per work group): 32 lanes per row,
@@ -1352,6 +1556,19 @@ void light_set_attributes() {
   SG_NUM_ATTR(float)
   SG_NUM_ATTR(double)
 #undef SG_NUM_ATTR
+  set_lds_attr(k_sym_rows_hyb<64, 4>);
+  set_lds_attr(k_sym_rows_hyb<128, 2>);
+  set_lds_attr(k_sym_rows_hyb<256, 1>);
+  set_lds_attr(k_sym_rows_hyb<512, 1>);
+  set_lds_attr(k_sym_rows_hyb<1024, 1>);
+  set_lds_attr(k_num_rows_hyb<256, 4, float>);
+  set_lds_attr(k_num_rows_hyb<512, 4, float>);
+  set_lds_attr(k_num_rows_hyb<1024, 4, float>);
+  set_lds_attr(k_num_rows_hyb<1024, 8, float>);
+  set_lds_attr(k_num_rows_hyb<256, 4, double>);
+  set_lds_attr(k_num_rows_hyb<512, 4, double>);
+  set_lds_attr(k_num_rows_hyb<1024, 4, double>);
+  set_lds_attr(k_num_rows_hyb<1024, 8, double>);
 }
 
 #define SG_DISPATCH_TPR(b, MACRO)                      \
@@ -1370,6 +1587,19 @@ void launch_sym_rows(const BinCfg& b, const int32_t* rows, int64_t nrows, const 
 #define L(TPR, RPB)                                                                         \
   hipLaunchKernelGGL((k_sym_rows<TPR, RPB>), dim3(grid), dim3(TPR * RPB), b.lds, s, rows, nrows, \
                      b.T, a, cnt, err)
+  SG_DISPATCH_TPR(b, L)
+#undef L
+}
+
+void launch_sym_rows_hyb(const BinCfg& b, const int32_t* rows, int64_t nrows, const RowArgs& a,
+                         int64_t m, int64_t n, int64_t* cnt, int32_t* outc, int32_t* err,
+                         hipStream_t s) {
+  if (nrows <= 0) return;
+  const unsigned grid = (unsigned)((nrows + b.rpb - 1) / b.rpb);
+  const size_t lds = (size_t)b.rpb * ((size_t)b.T * 4 + kHybWords * 4);
+#define L(TPR, RPB)                                                                          \
+  hipLaunchKernelGGL((k_sym_rows_hyb<TPR, RPB>), dim3(grid), dim3(TPR * RPB), lds, s, rows,   \
+                     nrows, b.T, a, m, n, cnt, outc, err)
   SG_DISPATCH_TPR(b, L)
 #undef L
 }
@@ -1477,6 +1707,42 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
 #undef L
   }
   (void)flag_unsupported;  // make_bins rejects bins without an instance
+}
+
+// The hybrid numeric's outlier table holds next_pow2(bin bound) slots (E
+// per thread, as the bin's sort); a row may use half of it, and at most
+// kHybOutMax (one wave sorts them).
+int32_t hyb_out_cap(const BinCfg& b, bool f64, int64_t lds) {
+  const int E = sort_e(b);
+  const bool inst = b.rpb == 1 && ((b.tpr == 256 && E == 4) || (b.tpr == 512 && E == 4) ||
+                                   (b.tpr == 1024 && (E == 4 || E == 8)));
+  const int32_t To = b.tpr * E;
+  if (!inst || (int64_t)hyb_num_lds(b.tpr, To, f64 ? 8 : 4) > lds) return -1;
+  return std::min<int32_t>(To / 2, kHybOutMax);
+}
+
+void launch_num_rows_hyb(const BinCfg& b, bool f64, const int32_t* rows, int64_t nrows,
+                         const RowArgs& a, int64_t m, int64_t n, const int64_t* cRowOff,
+                         int32_t* ccol, void* cval, int32_t* err, hipStream_t s) {
+  if (nrows <= 0) return;
+  const int E = sort_e(b);
+  const int32_t To = b.tpr * E;
+  const size_t lds = hyb_num_lds(b.tpr, To, f64 ? 8 : 4);
+  const unsigned grid = (unsigned)nrows;
+#define L(TPR, E_, V)                                                                         \
+  hipLaunchKernelGGL((k_num_rows_hyb<TPR, E_, V>), dim3(grid), dim3(TPR), lds, s, rows, To, a, \
+                     m, n, cRowOff, ccol, (V*)cval, err)
+#define LV(V)                                 \
+  do {                                        \
+    if (b.tpr == 256) L(256, 4, V);           \
+    else if (b.tpr == 512) L(512, 4, V);      \
+    else if (E == 4) L(1024, 4, V);           \
+    else L(1024, 8, V);                       \
+  } while (0)
+  if (f64) LV(double);
+  else LV(float);
+#undef LV
+#undef L
 }
 
 bool launch_num_chunks_esc(int32_t cap, bool f64, const ChunkDesc* desc, int64_t n,

@@ -516,6 +516,9 @@ __global__ __launch_bounds__(kNT) void k_numeric_row_bins(int64_t m, const int64
                                                           int heavyBin,
                                                           const int32_t* __restrict__ caps,
                                                           int nbins, int escKey,
+                                                          const int32_t* __restrict__ outc,
+                                                          const int32_t* __restrict__ hybCap,
+                                                          int hybSymMin, int hybKey,
                                                           uint8_t* __restrict__ key) {
   const int64_t i = (int64_t)blockIdx.x * kNT + threadIdx.x;
   if (i >= m) return;
@@ -535,6 +538,10 @@ __global__ __launch_bounds__(kNT) void k_numeric_row_bins(int64_t m, const int64
   const int64_t c = cnt[i];
   int b = 0;
   while (b < nbins - 1 && c > caps[b]) ++b;
+  if (outc && rb >= hybSymMin && outc[i] <= hybCap[b]) {
+    key[i] = (uint8_t)(hybKey + b);
+    return;
+  }
   key[i] = (uint8_t)b;
 }
 
@@ -688,10 +695,11 @@ void launch_write_rowptr(const int64_t* off, int64_t n, void* out, int is64, hip
 
 void launch_numeric_row_bins(int64_t m, const int64_t* cnt, const uint8_t* rowBin,
                              int heavyBin, const int32_t* caps, int nbins, uint8_t* key,
-                             hipStream_t s, int escKey) {
+                             hipStream_t s, int escKey, const int32_t* outc,
+                             const int32_t* hybCap, int hybSymMin, int hybKey) {
   if (m <= 0) return;
   hipLaunchKernelGGL(k_numeric_row_bins, dim3(grid_for(m, kNT)), dim3(kNT), 0, s, m, cnt, rowBin,
-                     heavyBin, caps, nbins, escKey, key);
+                     heavyBin, caps, nbins, escKey, outc, hybCap, hybSymMin, hybKey, key);
 }
 
 }  // namespace sg

@@ -28,7 +28,7 @@ import numpy as np
 __all__ = [
     "CSR", "erdos_renyi", "laplacian27", "rmat", "planted_partition",
     "random_csr", "identity", "workload", "rmat_rect", "sparse_uniform", "aggregation",
-    "grid_aggregation",
+    "grid_aggregation", "banded_outliers",
 ]
 
 
@@ -239,6 +239,31 @@ def random_csr(m: int, n: int, per_row: float, seed: int, values: str = "int",
         val = rng.random(nnz).astype(dtype)
     else:
         val = rng.uniform(-1.0, 1.0, size=nnz).astype(dtype)
+    return CSR(rp.astype(np.int32), col, val, m, n)
+
+
+def banded_outliers(m: int, n: int, in_band: int, band: int, outliers: int, seed: int,
+                    values: str = "int", dtype=np.float64) -> CSR:
+    """Rows with `in_band` distinct columns drawn within `band` of the
+    diagonal position row * n / m and Poisson(`outliers`) more drawn
+    uniformly from the whole row (a clustered matrix with thin links between
+    clusters, as the Markov-clustering iterates).  values as for random_csr."""
+    rng = np.random.default_rng(seed)
+    cols = []
+    for i in range(m):
+        ctr = (i * n) // max(m, 1)
+        lo_c, hi_c = max(0, ctr - band), min(n, ctr + band + 1)
+        a = rng.choice(np.arange(lo_c, hi_c), size=min(in_band, hi_c - lo_c), replace=False)
+        b = rng.integers(0, n, size=rng.poisson(outliers))
+        cols.append(np.unique(np.concatenate([a, b])))
+    k = np.array([c.size for c in cols], dtype=np.int64)
+    col = np.concatenate(cols).astype(np.int32)
+    rp = np.zeros(m + 1, dtype=np.int64)
+    np.cumsum(k, out=rp[1:])
+    if values == "int":
+        val = rng.integers(-3, 4, size=col.size).astype(dtype)
+    else:
+        val = rng.random(col.size).astype(dtype)
     return CSR(rp.astype(np.int32), col, val, m, n)
 
 

@@ -165,6 +165,34 @@ def test_dense_window_rows_match_hash(m, n, per_row, band, seed, dtype):
         assert st["lds_dense_products"] == 0
 
 
+# ------------------------------- diagonal window plus outlier table (hybrid)
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("m,k,n,in_band,band,outl,seed", [
+    (100000, 100000, 100000, 26, 400, 5, 31),  # most rows hybrid; first and last rows
+                                               # have windows clipped by the matrix edge
+    (150000, 150000, 150000, 14, 300, 12, 32), # many outliers: some rows over the table
+    (30000, 60000, 150000, 20, 150, 6, 33),    # rectangular (window centre row * n / m)
+])
+def test_hybrid_window_rows(m, k, n, in_band, band, outl, seed, dtype):
+    # Light rows of at least 512 products whose span is too wide for the
+    # dense window take a dense window around their diagonal position plus a
+    # hash table for the other columns; the hash path alone
+    # (light_hash_only) and the oracle must agree with it.
+    A = synth.banded_outliers(m, k, in_band, band, outl, seed, dtype=dtype)
+    B = synth.banded_outliers(k, n, in_band, band * n // k, outl, seed + 1, dtype=dtype)
+    st = check_full(A, B, exact=True)
+    rp_h, col_h, val_h, st_h = gpu_product(A, B, light_hash_only=1)
+    rp, col, val, _ = gpu_product(A, B)
+    np.testing.assert_array_equal(rp, rp_h)
+    np.testing.assert_array_equal(col, col_h)
+    np.testing.assert_array_equal(val, val_h)
+    assert st_h["hybrid_rows"] == 0
+    assert st["heavy_rows"] == 0
+    assert st["hybrid_rows"] > 0
+    if outl >= 10:
+        assert st["hybrid_rows"] < st["light_rows"]
+
+
 # -------------------------------------------------- heavy path, forced sizes
 @pytest.mark.parametrize("scale,tau,W,nmax", [
     (10, 64, 256, 32),     # one level, 4 chunks
@@ -215,6 +243,30 @@ def test_default_width_dense_chunks(dtype, direct):
     st = check_full(A, A, heavy_threshold=512, dense_direct=direct)
     assert st["heavy_rows"] > 0
     assert st["params"]["dense_width"] == (16384 if dtype == np.float64 else 32768)
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_dense_chunks_with_negative_zero_products(dtype):
+    # Columns whose products are all -0.0 are still entries of C: the 16
+    # heaviest rows get only -0.0 values (every column of their dense chunks
+    # sums to -0.0), the next 300 heavy rows -0.0 on half of their entries
+    # (some columns of a chunk do, the others do not).
+    A = synth.rmat(15, 16, seed=12, dtype=dtype)
+    P = oracle.row_products(A, A)
+    order = np.argsort(-P, kind="stable")
+    rp = A.row_ptr.astype(np.int64)
+    rng = np.random.default_rng(5)
+    val = A.val.copy()
+    for i in order[:16]:
+        val[rp[i]:rp[i + 1]] = -0.0
+    for i in order[16:316]:
+        seg = np.arange(rp[i], rp[i + 1])
+        val[seg[rng.random(seg.size) < 0.5]] = -0.0
+    A.val = val
+    st = check_full(A, A, heavy_threshold=512)
+    assert st["dense_chunks"] > 0
+    hv = P > st["heavy_row_threshold"]
+    assert hv[order[:316]].all()
 
 
 def test_options_do_not_change_the_result():
