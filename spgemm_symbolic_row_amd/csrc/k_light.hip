@@ -765,8 +765,8 @@ __global__ __launch_bounds__(TPR* RPB) void k_num_rows(const int32_t* __restrict
 // position (a bitmap, and in numeric a value per column: no probing, no
 // sort) and an LDS hash table for the other columns, its outliers.  The
 // output row is the outliers below lo, then the window's columns in order,
-// then the outliers above, so only the outliers are sorted (a few hundred
-// at most, by one wave in registers).  Symbolic
+// then the outliers above, so only the outliers are ordered (a few hundred
+// at most, ranked through buckets of equal column ranges).  Symbolic
 // counts both parts and stores the outlier count; numeric takes a row this
 // way when the outliers fit half of a table of next_pow2(bin bound) slots
 // and number at most kHybOutMax, else the row goes to the hash kernel.  (An accumulator per row chosen
@@ -839,33 +839,10 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows_hyb(const int32_t* __rest
 }
 
 // LDS: vw[kHybW] V | ov[To] V | ok[To] i32 | bm[kHybWords] | wpre[kHybWords] |
-// wtot[TPR / 64] | red[2].
+// wtot[TPR / 64] | red[2] | bcnt[kHybOutMax] | bfirst[kHybOutMax].
 __host__ __device__ constexpr size_t hyb_num_lds(int tpr, int32_t To, int vb) {
   return (size_t)kHybW * vb + (size_t)To * (vb + 4) + (size_t)kHybWords * 8 +
-         (size_t)(tpr / kWave) * 4 + 8;
-}
-
-// Bitonic sort of a row's outliers by one wave (E per lane, lane exchanges
-// and register swaps: no LDS after the load, no barrier), then each lane
-// writes its E ranks: below the window, or after it.
-template <int E, typename V>
-__device__ __forceinline__ void hyb_sort_write(int32_t* ok, V* ov, int32_t nout, int32_t nb,
-                                               int32_t nwin, int32_t lim, int64_t base,
-                                               int32_t* __restrict__ ccol, V* __restrict__ cval) {
-  int32_t kk[E];
-  V vv[E];
-  sort_to_regs<kWave, E, V>(ok, ov, kk, vv);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int32_t r = lane_id() * E + e;
-    if (r < nout) {
-      const int32_t pos = r < nb ? r : r + nwin;
-      if (pos < lim) {
-        ccol[base + pos] = kk[e];
-        cval[base + pos] = vv[e];
-      }
-    }
-  }
+         (size_t)(tpr / kWave) * 4 + 8 + (size_t)kHybOutMax * 8;
 }
 
 template <int TPR, int E, typename V>
@@ -884,8 +861,12 @@ __global__ __launch_bounds__(TPR) void k_num_rows_hyb(const int32_t* __restrict_
   int32_t* wpre = (int32_t*)(bm + kHybWords);
   int32_t* wtot = wpre + kHybWords;
   int32_t* red = wtot + TPR / kWave;  // window entries, outliers below lo
+  int32_t* bcnt = red + 2;               // outliers per bucket
+  int32_t* bfirst = bcnt + kHybOutMax;   // first rank of each bucket
+  int32_t* bkey = ok + To / 2;           // outlier columns gathered by bucket
   const int t = threadIdx.x;
   for (int i = t; i < kHybW; i += TPR) vw[i] = V(0);
+  for (int i = t; i < kHybOutMax; i += TPR) bcnt[i] = 0;
   for (int s = t; s < To; s += TPR) {
     ok[s] = kEmptyKey;
     ov[s] = V(0);
@@ -926,18 +907,63 @@ __global__ __launch_bounds__(TPR) void k_num_rows_hyb(const int32_t* __restrict_
     if (t == kWave - 1) red[0] = inc;
   }
   // Outliers: compacted (the barriers inside also publish wpre and red[0]),
-  // then those below the window counted.
+  // then ranked through kHybOutMax buckets of equal column ranges (the
+  // bucket of a column is monotone in it): each outlier takes a slot in its
+  // bucket, a scan of the bucket counts gives each bucket its first rank,
+  // the buckets' columns are gathered there, and an outlier's rank is its
+  // bucket's first rank plus the columns of its bucket below its own.
+  // Routing keeps a row's outliers to kHybOutMax; a row with more (a count
+  // that disagrees with symbolic) writes none and is reported by the size
+  // check below.
   const int32_t nout = compact_slots<TPR, 1, E, V>(ok, ov, To / TPR, wtot);
+  const bool fits = nout <= kHybOutMax;
+  constexpr int kPer = (kHybOutMax + TPR - 1) / TPR;
+  int32_t key[kPer], bk[kPer], slot[kPer];
+  V xv[kPer];
   int32_t below = 0;
-  for (int i = t; i < nout; i += TPR) below += ok[i] < lo;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t + j * TPR;
+    bk[j] = -1;
+    if (fits && i < nout) {
+      key[j] = ok[i];
+      xv[j] = ov[i];
+      bk[j] = (int32_t)((int64_t)key[j] * kHybOutMax / n);
+      slot[j] = atomicAdd(&bcnt[bk[j]], 1);
+      below += key[j] < lo;
+    }
+  }
   below = wave_sum(below);
   if (lane_id() == 0 && below) atomicAdd(&red[1], below);
+  __syncthreads();
+  {
+    constexpr int kCpt = (kHybOutMax + TPR - 1) / TPR;  // bucket counters per thread
+    int32_t c[kCpt], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      const int b = t * kCpt + j;
+      c[j] = b < kHybOutMax ? bcnt[b] : 0;
+      sum += c[j];
+    }
+    int32_t all;
+    int32_t run = block_excl_scan<TPR>(sum, wtot, &all);
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      const int b = t * kCpt + j;
+      if (b < kHybOutMax) bfirst[b] = run;
+      run += c[j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (bk[j] >= 0) bkey[bfirst[bk[j]] + slot[j]] = key[j];
   __syncthreads();
   const int32_t nwin = red[0], nb = red[1];
   const int64_t base = cRowOff[row];
   const int64_t want = cRowOff[row + 1] - base;
   const int32_t total = nwin + nout;
-  if (t == 0 && want != total) flag_error(err, kErrCountMismatch);
+  if (t == 0 && (want != total || !fits)) flag_error(err, kErrCountMismatch);
   const int32_t lim = (int32_t)(want < total ? want : total);
   for (int c = t; c < kHybW; c += TPR) {
     const uint32_t word = bm[c >> 5];
@@ -949,13 +975,18 @@ __global__ __launch_bounds__(TPR) void k_num_rows_hyb(const int32_t* __restrict_
       }
     }
   }
-  // The outliers (at most kHybOutMax, padded with INT_MAX by the
-  // compaction) are sorted by the first wave alone, in registers.
-  if (t < kWave) {
-    if (nout <= kWave) hyb_sort_write<1, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
-    else if (nout <= 2 * kWave) hyb_sort_write<2, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
-    else if (nout <= 4 * kWave) hyb_sort_write<4, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
-    else hyb_sort_write<8, V>(ok, ov, nout, nb, nwin, lim, base, ccol, cval);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (bk[j] >= 0) {
+      const int32_t f = bfirst[bk[j]], e = f + bcnt[bk[j]];
+      int32_t r = f;
+      for (int q = f; q < e; ++q) r += bkey[q] < key[j];
+      const int32_t pos = key[j] < lo ? r : r + nwin;
+      if (pos < lim) {
+        ccol[base + pos] = key[j];
+        cval[base + pos] = xv[j];
+      }
+    }
   }
 }
 
@@ -1711,7 +1742,7 @@ void launch_num_rows(const BinCfg& b, bool f64, const int32_t* rows, int64_t nro
 
 // The hybrid numeric's outlier table holds next_pow2(bin bound) slots (E
 // per thread, as the bin's sort); a row may use half of it, and at most
-// kHybOutMax (one wave sorts them).
+// kHybOutMax (the bucket ranking's bound).
 int32_t hyb_out_cap(const BinCfg& b, bool f64, int64_t lds) {
   const int E = sort_e(b);
   const bool inst = b.rpb == 1 && ((b.tpr == 256 && E == 4) || (b.tpr == 512 && E == 4) ||
