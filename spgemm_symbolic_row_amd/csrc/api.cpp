@@ -1805,6 +1805,7 @@ struct spgemm_prune_s {
   hipStream_t stream = nullptr;
   int64_t *keep = nullptr, *off = nullptr, *tmp = nullptr;
   double* colsum = nullptr;
+  float* inv = nullptr;     // fp32 values: reciprocals of the column sums
   void* buckets = nullptr;  // column buckets of the count (fill, columns, values)
   int64_t nnzOut = 0;
   int state = 0;
@@ -1854,7 +1855,12 @@ spgemm_status prune_count(bool mcl, spgemm_prune_t* out, int64_t m, int64_t n,
     HIP_CHECK(hipMallocAsync((void**)&p->keep, sizeof(int64_t) * std::max<int64_t>(m, 1), s));
     HIP_CHECK(hipMallocAsync((void**)&p->off, sizeof(int64_t) * (m + 1), s));
     HIP_CHECK(hipMallocAsync((void**)&p->tmp, sizeof(int64_t) * (scan_tmp_elems(m) + 1), s));
-    HIP_CHECK(hipMallocAsync((void**)&p->colsum, sizeof(double) * std::max<int64_t>(n, 1), s));
+    // column sums (fp64), then for fp32 values their reciprocals (fp32)
+    HIP_CHECK(hipMallocAsync((void**)&p->colsum,
+                             (sizeof(double) + (p->f64 ? 0 : sizeof(float))) *
+                                 std::max<int64_t>(n, 1),
+                             s));
+    if (!p->f64) p->inv = (float*)(p->colsum + std::max<int64_t>(n, 1));
     launch_fill_i64((int64_t*)p->colsum, 0, n, s);  // +0.0 has an all-zero bit pattern
     // Column buckets for the count's column sums (each work group's LDS
     // table and the entries it misses): room for min(nnz(C), 2^29) entries
@@ -1894,6 +1900,7 @@ spgemm_status prune_count(bool mcl, spgemm_prune_t* out, int64_t m, int64_t n,
       launch_mcl_count(m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->colsum, p->keep, s);
     } else {
       count(p->thr);
+      if (p->inv) launch_colsum_recip(n, p->colsum, p->inv, s);
     }
     launch_scan_i64(p->keep, m, p->off, p->tmp, s);
     check_launch("prune count");
@@ -1948,7 +1955,7 @@ spgemm_status prune_fill(bool mcl, spgemm_prune_t p, int32_t* dOut_col, void* dO
                       dOut_col, dOut_val, p->stream);
     else
       launch_prune_fill(p->m, p->rp, p->rp64, p->col, p->val, p->f64, p->thr, p->off,
-                        p->colsum, dOut_col, dOut_val, p->stream);
+                        p->colsum, p->inv, dOut_col, dOut_val, p->stream);
     check_launch("prune fill");
   } catch (const Error& e) {
     p->err = e.msg;

@@ -423,9 +423,12 @@ void launch_prune_count_b(int64_t m, int64_t n, const void* rp, int rp64, const 
                           const void* val, bool f64, double thr, int64_t* keepCnt, double* colsum,
                           int32_t nb, int log2Cols, int64_t cap, unsigned long long* fill,
                           int32_t* bcol, double* bval, hipStream_t s);
+// inv[j] = fp32 reciprocal of colsum[j] (0 for a zero sum).
+void launch_colsum_recip(int64_t n, const double* colsum, float* inv, hipStream_t s);
+// fp64 values are divided by colsum, fp32 ones multiplied by inv.
 void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
                        bool f64, double thr, const int64_t* outOff, const double* colsum,
-                       int32_t* ocol, void* oval, hipStream_t s);
+                       const float* inv, int32_t* ocol, void* oval, hipStream_t s);
 // MCL inflation (normalise, drop below the threshold, square); column sums
 // of all entries from launch_prune_count with threshold -inf.
 void launch_mcl_count(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,

@@ -2,7 +2,9 @@
 // "Communication-Avoiding SpGEMM via Trident Partitioning", §5.7): entries
 // below the threshold are dropped, then every column is divided by the sum
 // of its kept entries.  The comparison is made in the value type; column
-// sums are accumulated in fp64 and each kept value is rounded once.
+// sums are accumulated in fp64; an fp64 kept value is divided by its column
+// sum and rounded once, an fp32 one multiplied by the fp32-rounded
+// reciprocal of the sum (relative error below 2^-22).
 #include "device_common.hpp"
 
 namespace sg {
@@ -243,15 +245,31 @@ __global__ __launch_bounds__(kSumNT) void k_colsum_buckets(int64_t n, int log2Co
   }
 }
 
+// fp32 values: the reciprocal of every column sum, rounded to fp32 (0 for
+// an empty column), so that the fill gathers 4 bytes per kept entry from a
+// table half the size of the sums.
+__global__ __launch_bounds__(kNT) void k_colsum_recip(int64_t n, const double* __restrict__ colsum,
+                                                      float* __restrict__ inv) {
+  const int64_t j = (int64_t)blockIdx.x * kNT + threadIdx.x;
+  if (j < n) inv[j] = colsum[j] != 0.0 ? (float)(1.0 / colsum[j]) : 0.0f;
+}
+
+template <typename V>
+__device__ __forceinline__ V prune_scaled(V x, double cs) {
+  return (V)((double)x / cs);
+}
+__device__ __forceinline__ float prune_scaled(float x, float inv) { return x * inv; }
+
 // One wave per row: order-preserving compaction of the kept entries.  As in
 // the count, a wave loads kPruneU runs of 64 entries, then gathers their
-// column sums, then writes.
-template <typename V, typename RP>
+// column scales (fp64 sums, or fp32 reciprocals of them for fp32 values),
+// then writes.
+template <typename V, typename RP, typename S>
 __global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __restrict__ rp,
                                                     const int32_t* __restrict__ col,
                                                     const V* __restrict__ val, V thr,
                                                     const int64_t* __restrict__ outOff,
-                                                    const double* __restrict__ colsum,
+                                                    const S* __restrict__ colsum,
                                                     int32_t* __restrict__ ocol,
                                                     V* __restrict__ oval) {
   const int64_t r = ((int64_t)blockIdx.x * kNT + threadIdx.x) / kWave;
@@ -262,7 +280,7 @@ __global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __res
     V x[kPruneU];
     int32_t c[kPruneU];
     bool k[kPruneU];
-    double cs[kPruneU];
+    S cs[kPruneU];
 #pragma unroll
     for (int u = 0; u < kPruneU; ++u) {
       const int64_t e = base + u * kWave + lane_id();
@@ -272,14 +290,14 @@ __global__ __launch_bounds__(kNT) void k_prune_fill(int64_t m, const void* __res
       k[u] = act && x[u] >= thr;
     }
 #pragma unroll
-    for (int u = 0; u < kPruneU; ++u) cs[u] = k[u] ? colsum[c[u]] : 1.0;
+    for (int u = 0; u < kPruneU; ++u) cs[u] = k[u] ? colsum[c[u]] : S(1);
 #pragma unroll
     for (int u = 0; u < kPruneU; ++u) {
       const uint64_t mk = __ballot(k[u]);
       if (k[u]) {
         const int64_t pos = w + __popcll(mk & lanemask_lt());
         ocol[pos] = c[u];
-        oval[pos] = (V)((double)x[u] / cs[u]);
+        oval[pos] = prune_scaled(x[u], cs[u]);
       }
       w += __popcll(mk);
     }
@@ -427,25 +445,31 @@ void launch_prune_count_b(int64_t m, int64_t n, const void* rp, int rp64, const 
                      n, log2Cols, cap, fill, bcol, bval, colsum);
 }
 
+void launch_colsum_recip(int64_t n, const double* colsum, float* inv, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_colsum_recip, dim3((unsigned)((n + kNT - 1) / kNT)), dim3(kNT), 0, s, n,
+                     colsum, inv);
+}
+
 void launch_prune_fill(int64_t m, const void* rp, int rp64, const int32_t* col, const void* val,
                        bool f64, double thr, const int64_t* outOff, const double* colsum,
-                       int32_t* ocol, void* oval, hipStream_t s) {
+                       const float* inv, int32_t* ocol, void* oval, hipStream_t s) {
   if (m <= 0) return;
   const dim3 g(grid_rows(m)), b(kNT);
   if (f64) {
     if (rp64)
-      hipLaunchKernelGGL((k_prune_fill<double, int64_t>), g, b, 0, s, m, rp, col,
+      hipLaunchKernelGGL((k_prune_fill<double, int64_t, double>), g, b, 0, s, m, rp, col,
                          (const double*)val, thr, outOff, colsum, ocol, (double*)oval);
     else
-      hipLaunchKernelGGL((k_prune_fill<double, int32_t>), g, b, 0, s, m, rp, col,
+      hipLaunchKernelGGL((k_prune_fill<double, int32_t, double>), g, b, 0, s, m, rp, col,
                          (const double*)val, thr, outOff, colsum, ocol, (double*)oval);
   } else {
     if (rp64)
-      hipLaunchKernelGGL((k_prune_fill<float, int64_t>), g, b, 0, s, m, rp, col,
-                         (const float*)val, (float)thr, outOff, colsum, ocol, (float*)oval);
+      hipLaunchKernelGGL((k_prune_fill<float, int64_t, float>), g, b, 0, s, m, rp, col,
+                         (const float*)val, (float)thr, outOff, inv, ocol, (float*)oval);
     else
-      hipLaunchKernelGGL((k_prune_fill<float, int32_t>), g, b, 0, s, m, rp, col,
-                         (const float*)val, (float)thr, outOff, colsum, ocol, (float*)oval);
+      hipLaunchKernelGGL((k_prune_fill<float, int32_t, float>), g, b, 0, s, m, rp, col,
+                         (const float*)val, (float)thr, outOff, inv, ocol, (float*)oval);
   }
 }
 
