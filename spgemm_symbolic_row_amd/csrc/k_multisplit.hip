@@ -22,8 +22,10 @@ constexpr int kMsNBMax = 1024;  // LDS buckets per work group
 constexpr int kMsRowsMax = 512;
 constexpr int kMsItemsF64 = 4;   // elements per thread held in registers
 constexpr int kMsItemsF32 = 8;
-// Straight into final chunks: no LDS staging, so larger tiles.
-constexpr int kXfItemsF64 = 8;
+// Straight into final chunks: no LDS staging, so larger tiles.  fp64: six
+// elements per thread keep the kernel at 66 VGPRs, seven waves per SIMD
+// (eight elements take 84, five waves: 4% slower on R-MAT 18 and 20).
+constexpr int kXfItemsF64 = 6;
 constexpr int kXfItemsF32 = 8;
 constexpr int kXfNBMax = 8192;   // (row, chunk) buckets per work group
 constexpr int kXfEnt = 256;      // entries per tile staged in LDS
