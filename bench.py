@@ -486,10 +486,9 @@ def main():
                     "per_unit": unit_desc}
             if kern in phase_min:
                 # The shortest launch (with several heavy batches the first
-                # one runs beside the heavy-row slot counts and takes longer).
+                # one runs beside the heavy-row slot counts and takes longer;
+                # the batches differ in size, so no rate is derived from it).
                 roof["min_launch_ms"] = round(phase_min[kern], 4)
-                roof["frac_min_launch"] = round(byt / (phase_min[kern] / 1e3) / 1e9
-                                                / HBM_PEAK_GBPS, 4)
             if not args.no_copy_rate:
                 roof["copy_gbps"] = copy_bandwidth()
                 roof["frac_of_copy"] = round(achieved / roof["copy_gbps"], 4)
