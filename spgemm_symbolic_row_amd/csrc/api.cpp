@@ -1878,12 +1878,12 @@ spgemm_status prune_count(bool mcl, spgemm_prune_t* out, int64_t m, int64_t n,
       const int64_t nnzC = p->rp64 ? p->hbuf[0] : (int64_t)((const int32_t*)p->hbuf)[0];
       cap = (std::min<int64_t>(nnzC, (int64_t)1 << 29) + nb - 1) / nb;
       if (cap > 0) {
-        const size_t bytes = 8 * (size_t)nb + (size_t)nb * cap * 12;
+        const size_t bytes = 8 * kFillStride * (size_t)nb + (size_t)nb * cap * 12;
         HIP_CHECK(hipMallocAsync(&p->buckets, bytes, s));
         fill = (unsigned long long*)p->buckets;
-        bval = (double*)(fill + nb);
+        bval = (double*)(fill + kFillStride * (size_t)nb);
         bcol = (int32_t*)(bval + (size_t)nb * cap);
-        launch_fill_i64((int64_t*)fill, 0, nb, s);
+        launch_fill_i64((int64_t*)fill, 0, kFillStride * nb, s);
       }
     }
     auto count = [&](double thr) {

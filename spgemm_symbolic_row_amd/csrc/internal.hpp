@@ -414,11 +414,14 @@ void launch_prune_count(int64_t m, const void* rp, int rp64, const int32_t* col,
                         bool f64, double thr, int64_t* keepCnt, double* colsum,
                         hipStream_t s);
 // The count with its column sums sent through nb column buckets of
-// 2^log2Cols columns (cap entries each: fill[nb] zeroed, bcol and bval
+// 2^log2Cols columns (cap entries each: fill[nb * kFillStride] zeroed, bcol and bval
 // nb * cap), then the buckets' sums added into colsum.  prune_buckets_fit
 // gives the bucket geometry for n columns (false: too many columns, use
 // launch_prune_count).
 bool prune_buckets_fit(int64_t n, int* log2Cols, int32_t* nb);
+// Bucket fill counters sit kFillStride apart (one 128-byte line each), so
+// the reservations of different buckets do not contend for one line.
+constexpr int kFillStride = 16;
 void launch_prune_count_b(int64_t m, int64_t n, const void* rp, int rp64, const int32_t* col,
                           const void* val, bool f64, double thr, int64_t* keepCnt, double* colsum,
                           int32_t nb, int log2Cols, int64_t cap, unsigned long long* fill,

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kPruneBNT) void k_prune_count_b(int64_t m, const vo
   __syncthreads();
   for (int i = threadIdx.x; i < nb; i += kPruneBNT) {
     const int32_t h = hist[i];
-    base[i] = h ? (int64_t)atomicAdd(&fill[i], (unsigned long long)h) : 0;
+    base[i] = h ? (int64_t)atomicAdd(&fill[i * kFillStride], (unsigned long long)h) : 0;
     hist[i] = 0;
   }
   __syncthreads();
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kSumNT) void k_colsum_buckets(int64_t n, int log2Co
   const int64_t c0 = bk << log2Cols;
   for (int j = threadIdx.x; j < cols; j += kSumNT) sums[j] = 0.0;
   __syncthreads();
-  const int64_t cnt = min<int64_t>((int64_t)fill[bk], cap);
+  const int64_t cnt = min<int64_t>((int64_t)fill[bk * kFillStride], cap);
   const int64_t i0 = cnt * part / kBucketSplit, i1 = cnt * (part + 1) / kBucketSplit;
   const int32_t* bc = bcol + bk * cap;
   const double* bv = bval + bk * cap;
