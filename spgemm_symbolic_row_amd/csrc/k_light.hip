@@ -792,7 +792,9 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows_hyb(const int32_t* __rest
   const int g = threadIdx.x / TPR, t = threadIdx.x % TPR;
   int32_t* keys = keysAll + g * T;
   uint32_t* bm = bmAll + g * kHybWords;
-  for (int s = t; s < T; s += TPR) keys[s] = kEmptyKey;
+  // T is a power of two from 64 on: the keys are cleared 16 bytes a store.
+  for (int s = t; s < T / 4; s += TPR)
+    ((int4*)keys)[s] = make_int4(kEmptyKey, kEmptyKey, kEmptyKey, kEmptyKey);
   for (int i = t; i < kHybWords; i += TPR) bm[i] = 0;
   if (t == 0) {
     gwin[g] = 0;
@@ -839,10 +841,10 @@ __global__ __launch_bounds__(TPR* RPB) void k_sym_rows_hyb(const int32_t* __rest
 }
 
 // LDS: vw[kHybW] V | ov[To] V | ok[To] i32 | bm[kHybWords] | wpre[kHybWords] |
-// wtot[TPR / 64] | red[2] | bcnt[kHybOutMax] | bfirst[kHybOutMax].
+// wtot[TPR / 64] | red[4] | bcnt[kHybOutMax] | bfirst[kHybOutMax].
 __host__ __device__ constexpr size_t hyb_num_lds(int tpr, int32_t To, int vb) {
   return (size_t)kHybW * vb + (size_t)To * (vb + 4) + (size_t)kHybWords * 8 +
-         (size_t)(tpr / kWave) * 4 + 8 + (size_t)kHybOutMax * 8;
+         (size_t)(tpr / kWave) * 4 + 16 + (size_t)kHybOutMax * 8;
 }
 
 template <int TPR, int E, typename V>
@@ -861,15 +863,20 @@ __global__ __launch_bounds__(TPR) void k_num_rows_hyb(const int32_t* __restrict_
   int32_t* wpre = (int32_t*)(bm + kHybWords);
   int32_t* wtot = wpre + kHybWords;
   int32_t* red = wtot + TPR / kWave;  // window entries, outliers below lo
-  int32_t* bcnt = red + 2;               // outliers per bucket
+  int32_t* bcnt = red + 4;               // outliers per bucket (16-byte aligned)
   int32_t* bfirst = bcnt + kHybOutMax;   // first rank of each bucket
   int32_t* bkey = ok + To / 2;           // outlier columns gathered by bucket
   const int t = threadIdx.x;
-  for (int i = t; i < kHybW; i += TPR) vw[i] = V(0);
-  for (int i = t; i < kHybOutMax; i += TPR) bcnt[i] = 0;
-  for (int s = t; s < To; s += TPR) {
-    ok[s] = kEmptyKey;
-    ov[s] = V(0);
+  // Cleared 16 bytes a store: the window and the outlier values (adjacent,
+  // all-zero bits), the outlier keys (kEmptyKey), the bucket counts.
+  {
+    float4* z = (float4*)smem;
+    const int nz = (int)(((size_t)kHybW + To) * sizeof(V) / 16);
+    for (int i = t; i < nz; i += TPR) z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int4* k4 = (int4*)ok;
+    for (int i = t; i < To / 4; i += TPR) k4[i] = make_int4(kEmptyKey, kEmptyKey, kEmptyKey, kEmptyKey);
+    int4* b4 = (int4*)bcnt;
+    for (int i = t; i < kHybOutMax / 4; i += TPR) b4[i] = make_int4(0, 0, 0, 0);
   }
   if (t < kHybWords) bm[t] = 0;
   if (t == 0) red[1] = 0;
