@@ -193,6 +193,25 @@ def test_hybrid_window_rows(m, k, n, in_band, band, outl, seed, dtype):
         assert st["hybrid_rows"] < st["light_rows"]
 
 
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_hybrid_window_rows_largest_bin(dtype):
+    # Light rows of up to tau products (heavy_row_threshold = tau): rows of
+    # more than 2,048 entries, nearly all of the window's columns set plus a
+    # few hundred outliers, take the 1024-thread hybrid kernel; the few rows
+    # above tau products take the heavy path.
+    A = synth.banded_outliers(100000, 100000, 80, 500, 2, 41, dtype=dtype)
+    B = synth.banded_outliers(100000, 100000, 80, 500, 2, 42, dtype=dtype)
+    st = check_full(A, B, exact=True, heavy_row_threshold=6826)
+    rp_h, col_h, val_h, st_h = gpu_product(A, B, light_hash_only=1, heavy_row_threshold=6826)
+    rp, col, val, _ = gpu_product(A, B, heavy_row_threshold=6826)
+    np.testing.assert_array_equal(rp, rp_h)
+    np.testing.assert_array_equal(col, col_h)
+    np.testing.assert_array_equal(val, val_h)
+    nnz = np.diff(rp)
+    assert st["hybrid_rows"] > 0 and st_h["hybrid_rows"] == 0
+    assert (nnz > 2048).sum() > 10000
+
+
 # -------------------------------------------------- heavy path, forced sizes
 @pytest.mark.parametrize("scale,tau,W,nmax", [
     (10, 64, 256, 32),     # one level, 4 chunks
