@@ -67,6 +67,11 @@ def algorithmic_bytes(st, phase, sv, si=4):
         return E * si, f"{si} B read per element per level"
     if phase == "num_chunk_dense":
         return st["lds_dense_products"] * (si + sv), f"{si + sv} B read per dense-chunk element"
+    if phase == "num_chunk_hash":
+        return ((st["heavy_products"] - st["lds_dense_products"]) * (si + sv),
+                f"{si + sv} B read per light-chunk element")
+    if phase == "sym_chunk_dense":
+        return st["lds_dense_products"] * si, f"{si} B read per dense-chunk element"
     if phase == "num_light":
         return ((st["products"] - st["heavy_products"]) * (si + sv),
                 f"{si + sv} B of B read per light-row product")
@@ -489,6 +494,26 @@ def main():
                 # one runs beside the heavy-row slot counts and takes longer;
                 # the batches differ in size, so no rate is derived from it).
                 roof["min_launch_ms"] = round(phase_min[kern], 4)
+            # The other heavy kernels with an algorithmic byte count, as the
+            # pages report a fraction of speed of light per core kernel.
+            others = []
+            # (The histogram phase is left out: by default it derives the
+            # level counts from the structure and reads no element.)
+            for k in ("expand_final", "num_chunk_dense", "num_chunk_hash", "sym_chunk_dense",
+                      "multisplit", "expand_split", "outer_product"):
+                if k == kern or phase_tot.get(k, 0) <= 0:
+                    continue
+                kb, kunit = algorithmic_bytes(st, k, sv)
+                if not kb:
+                    continue
+                kw = st["phase_windows"][k]
+                kms = phase_tot[k] / (kw * K)
+                others.append({"kernel": k, "avg_launch_ms": round(kms, 4),
+                               "bytes_per_launch": int(kb / kw),
+                               "frac": round(kb / kw / (kms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                               "per_unit": kunit})
+            if others:
+                roof["other_kernels"] = others
             if not args.no_copy_rate:
                 roof["copy_gbps"] = copy_bandwidth()
                 roof["frac_of_copy"] = round(achieved / roof["copy_gbps"], 4)
