@@ -185,15 +185,19 @@ def cpu_model():
 
 def traffic_for(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current sources (the kernel's, and the host code that
+    decides which elements it moves: the SHA-256 of their contents in the
+    listed order); else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, rec["source"])
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if digest != rec["source_sha256"]:
+    srcs = rec.get("sources") or [rec["source"]]
+    h = hashlib.sha256()
+    for src in srcs:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec["bytes_per_launch"]
 

@@ -170,7 +170,7 @@ typedef struct spgemm_options {
                                    exercised from the host               */
   int64_t dense_direct;         /* 1: with expansion 0, dense chunks (W-wide
                                    slots of a heavy row holding more than
-                                   min(tau, W/8) products) are accumulated
+                                   min(tau, W/2) products) are accumulated
                                    straight from A and B (each entry's run of
                                    its B row inside the slot, found among B's
                                    per-slot runs) instead of from the expanded

@@ -1073,15 +1073,17 @@ void expand_batch(spgemm_plan_t p, int64_t hb0, int64_t hb1, bool countStats, bo
     }
     B->lastFirst = completed ? nfc - pieces.back().n : nfc;
   }
-  // Numeric bins: W-wide chunks with more than W/8 elements (or tau, if
-  // smaller) go to the dense accumulator, at that density zeroing and
-  // scanning W columns is cheaper than hashing; the rest by element count.
+  // Numeric bins: W-wide chunks with more than tau elements (or W/2, if
+  // smaller) go to the dense accumulator; the rest by element count.  Below
+  // that the light chunk kernels (register sort, bitmap rank) beat zeroing
+  // and scanning W columns: with W/8 in place of tau, 9% more time per
+  // product at R-MAT 18 (fp64, W = 16384) and 5% at R-MAT 20.
   uint8_t* key = alloc_n<uint8_t>(p, nfc, s);
   B->fcOrder = alloc_n<int32_t>(p, nfc, s);
   int32_t* bc = alloc_n<int32_t>(p, 64, s);
   int32_t* bf = alloc_n<int32_t>(p, 64, s);
   int32_t* bs = alloc_n<int32_t>(p, 65, s);
-  const int64_t denseMin = std::min<int64_t>(p->tau, W / 8);
+  const int64_t denseMin = std::min<int64_t>(p->tau, W / 2);
   launch_chunk_bins(nfc, B->fcCnt, B->lastFirst, denseMin, p->dSymCaps, p->NS, p->NS, key,
                     countStats ? p->stats + kStatDenseElems : nullptr, s);
   launch_bin_sort(key, nfc, p->NS + 1, bc, bf, bs, B->fcOrder, s);
